@@ -1,0 +1,206 @@
+/*
+ * swimba.h - C ABI of the Swimba (Switch Mamba) mixer forward pass on MI355X.
+ *
+ * The method: arXiv 2603.06938, "Swimba: Switch Mamba Model Scales State
+ * Space Models". Per token a router gives softmax weights over E experts and
+ * keeps the top-k; each selected expert's linear projection emits its own
+ * B, C and X streams; these are mixed in parameter space into one injection
+ * U~_t = sum_j pi_{t,j} B_{t,j} X_{t,j}^T and one readout C~_t; one state per
+ * head then runs h_t = a_h h_{t-1} + U~_t, y_t = C~_t^T h_t with a scalar,
+ * contractive a_h shared by all experts and all steps.
+ * (papernotes.org notes on the paper, Method, key designs 1 and 2; gist.science
+ *  English summary, Technical Summary section 2, Architecture Details.)
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless a comment says otherwise. Tensors are
+ *    dense, row-major, with the shapes given below. Every device pointer must be
+ *    16-byte aligned.
+ *  - Token index m = b * seqlen + t.
+ *  - The caller owns every buffer, including the workspace, whose size comes
+ *    from swimba_workspace_size(). The library never allocates or frees device
+ *    memory and keeps no device state between calls.
+ *  - Work is enqueued on the given stream only (never the null stream, unless
+ *    the caller passes it); no call synchronises.
+ *  - Errors: a call validates every argument before it launches anything. On
+ *    an error it returns a negative swimba_status, launches nothing, leaves
+ *    every output untouched and records a message for swimba_last_error().
+ *    A failed kernel launch returns SWIMBA_ERR_HIP. No C++ exception crosses
+ *    this boundary.
+ *  - Same inputs give bitwise-identical outputs (no order-dependent atomics).
+ *  - Calls that share a workspace, or write the same outputs, must not run
+ *    concurrently.
+ */
+#ifndef SWIMBA_H
+#define SWIMBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWIMBA_ABI_VERSION 1
+
+typedef enum swimba_dtype {
+  SWIMBA_F32 = 0,  /* every stream tensor is float32 */
+  SWIMBA_BF16 = 1  /* u, weights, B_hat, X_hat, C_mix and y are bfloat16 */
+} swimba_dtype;
+
+typedef enum swimba_status {
+  SWIMBA_OK = 0,
+  SWIMBA_ERR_NULL = -1,        /* a required pointer is NULL */
+  SWIMBA_ERR_DIMS = -2,        /* a dimension is out of range or inconsistent */
+  SWIMBA_ERR_UNSUPPORTED = -3, /* valid, but no kernel exists for this shape */
+  SWIMBA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  SWIMBA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+  SWIMBA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+} swimba_status;
+
+typedef enum swimba_call {
+  SWIMBA_CALL_ROUTE = 0,
+  SWIMBA_CALL_PROJECT = 1,
+  SWIMBA_CALL_SCAN = 2,
+  SWIMBA_CALL_DECODE = 3
+} swimba_call;
+
+/*
+ * Dimensions. Constraints checked by every call:
+ *   batch >= 0, seqlen >= 0 (M = batch*seqlen may be 0), d_model >= 1,
+ *   nheads >= 1, headdim >= 1, dstate >= 1, ngroups >= 1 and divides nheads,
+ *   n_experts >= 1, 1 <= top_k <= n_experts, chunk >= 1, dtype in swimba_dtype.
+ * Shapes with a kernel (else SWIMBA_ERR_UNSUPPORTED):
+ *   headdim == 64; dstate in {16, 32, 64, 128}; d_model % 32 == 0;
+ *   n_experts <= 256; top_k <= 8 (the prefill scan: top_k <= 2);
+ *   chunk in {32, 64, 128, 256} for the scan.
+ */
+typedef struct swimba_dims {
+  int32_t batch;      /* Bt: independent sequences */
+  int32_t seqlen;     /* T: tokens per sequence (1 for a decode step) */
+  int32_t d_model;    /* D: width of the mixer input u_t */
+  int32_t nheads;     /* H */
+  int32_t headdim;    /* P: X and y width per head */
+  int32_t dstate;     /* N: state rows per head (state is N x P) */
+  int32_t ngroups;    /* G: B and C groups; head h uses group h / (H/G) */
+  int32_t n_experts;  /* E */
+  int32_t top_k;      /* k: selected experts per token */
+  int32_t chunk;      /* L: SSD chunk length (scan only) */
+  int32_t dtype;      /* swimba_dtype */
+  int32_t reserved;   /* must be 0 */
+} swimba_dims;
+
+int32_t swimba_abi_version(void);
+
+/* Message of the last failed call on this host thread (host memory, owned by
+ * the library, valid until the next call on this thread). */
+const char* swimba_last_error(void);
+
+/* Workspace bytes that call `call` needs for `dims` (0 if none). Returns 0
+ * for invalid dims as well; the call itself then reports the error. */
+size_t swimba_workspace_size(const swimba_dims* dims, int32_t call);
+
+/*
+ * Router and top-k active set.
+ * (papernotes.org notes, Method, key design 1: pi_t = softmax(g_t), K_t a
+ *  top-k set; gist.science English summary, section 2, Expert Routing.)
+ * g_t = W_r u_t accumulated in fp32 (never rounded to bf16); pi_t = softmax
+ * over all E logits in fp32; K_t = the k largest logits, descending, exact
+ * ties to the lower expert index; topk_w[m, j] = pi_{m, K_t[j]} (not
+ * renormalised).
+ *   u         [M, D]   dtype
+ *   w_router  [E, D]   dtype
+ *   topk_idx  [M, k]   int32 out
+ *   topk_w    [M, k]   float32 out
+ *   logits    [M, E]   float32 out, or NULL
+ */
+swimba_status swimba_route_topk(const swimba_dims* dims, const void* u, const void* w_router,
+                                int32_t* topk_idx, float* topk_w, float* logits,
+                                hipStream_t stream);
+
+/*
+ * Expert projections with the parameter-space mix in the epilogue.
+ * (papernotes.org notes, Method, key design 1: each expert's linear
+ *  projection of the token gives B^(e), C^(e), X^(e); mixing equation for
+ *  U~_t and C~_t. gist.science English summary, section 2, Parameter Mixing.)
+ * For slot j of token m with expert e = topk_idx[m, j] and weight w:
+ *   z = W_e u_m (fp32 accumulation), W_e = w_experts[e], rows X | B | C;
+ *   X_hat[m, j] = z[0 : H*P]                          (as [H, P])
+ *   B_hat[m, j] = w * z[H*P : H*P + G*N]              (as [G, N])
+ *   C_mix[m]    = sum_j w * z[H*P + G*N : H*P + 2*G*N] (as [G, N]), summed in
+ *                 slot order j = 0..k-1 in fp32, then stored in dtype.
+ * U~_m = sum_j B_hat[m, j] X_hat[m, j]^T is never formed.
+ *   u          [M, D]              dtype
+ *   w_experts  [E, H*P + 2*G*N, D] dtype
+ *   topk_idx   [M, k] int32 (values in [0, E); validated on the device: an
+ *              out-of-range index makes its slot contribute zeros)
+ *   topk_w     [M, k] float32
+ *   B_hat      [M, k, G, N] dtype out
+ *   X_hat      [M, k, H, P] dtype out
+ *   C_mix      [M, G, N]    dtype out
+ *   ws         workspace of swimba_workspace_size(dims, SWIMBA_CALL_PROJECT)
+ */
+swimba_status swimba_expert_project_mix(const swimba_dims* dims, const void* u,
+                                        const void* w_experts, const int32_t* topk_idx,
+                                        const float* topk_w, void* B_hat, void* X_hat,
+                                        void* C_mix, void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
+
+/*
+ * Single-trajectory scan, solved in chunks of L tokens (SSD).
+ * (papernotes.org notes, Method, key design 1 state equation and the reuse of
+ *  the chunked SSD solver; key design 2: A shared over experts and steps.)
+ * For every sequence b and head h (group g = h / (H/G)), with h_{-1} = h_init:
+ *   h_t = a_h h_{t-1} + sum_j B_hat[t, j, g] X_hat[t, j, h]^T      (N x P)
+ *   y[t, h] = C_mix[t, g]^T h_t                                     (P)
+ * computed as, per chunk: a masked quadratic form over the chunk's
+ * k-concatenated (token, slot) pairs, plus the decayed readout of the state
+ * entering the chunk; states are carried across chunks in fp32.
+ *   B_hat    [M, k, G, N] dtype;  X_hat [M, k, H, P] dtype;  C_mix [M, G, N] dtype
+ *   a        [H] float32, each in [0, 1)
+ *   h_init   [Bt, H, N, P] float32, or NULL for zeros
+ *   y        [M, H, P] dtype out
+ *   h_final  [Bt, H, N, P] float32 out, or NULL (may alias h_init)
+ *   ws       workspace of swimba_workspace_size(dims, SWIMBA_CALL_SCAN)
+ */
+swimba_status swimba_ssd_chunk_scan(const swimba_dims* dims, const void* B_hat,
+                                    const void* X_hat, const void* C_mix, const float* a,
+                                    const float* h_init, void* y, float* h_final, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One recurrent decode step for `batch` sequences (dims->seqlen must be 1).
+ * (papernotes.org notes, Method, key design 1, the recurrent form; key
+ *  findings: token-by-token decoding.)
+ * Routes u, projects the k selected experts, updates the state in place,
+ *   h <- a_h h + sum_j B_hat_j X_hat_j^T  (fp32),   y = C_mix^T h,
+ * and reads out y.
+ *   u         [Bt, D] dtype;  w_router [E, D] dtype;  w_experts as above
+ *   a         [H] float32
+ *   h         [Bt, H, N, P] float32, in/out
+ *   y         [Bt, H, P] dtype out
+ *   topk_idx  [Bt, k] int32 out, or NULL
+ *   ws        workspace of swimba_workspace_size(dims, SWIMBA_CALL_DECODE)
+ */
+swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const void* w_router,
+                                 const void* w_experts, const float* a, float* h, void* y,
+                                 int32_t* topk_idx, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Per-kernel timing with HIP events, for measurement only. While enabled,
+ * every kernel the library launches is bracketed by two events recorded on
+ * its stream. swimba_profile_report() waits for the recorded events, writes a
+ * NUL-terminated JSON object {"kernel": {"launches": n, "ms": total}, ...}
+ * into `buf` (host memory, `cap` bytes) and clears the records. It returns the
+ * length written, or a negative swimba_status.
+ */
+swimba_status swimba_profile_enable(int32_t on);
+int32_t swimba_profile_report(char* buf, size_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIMBA_H */

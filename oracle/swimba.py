@@ -84,13 +84,15 @@ def route(u: np.ndarray, w_router: np.ndarray, top_k: int) -> Routing:
 
 
 def expert_streams(u: np.ndarray, w_experts: np.ndarray, idx: np.ndarray,
-                   nheads: int, headdim: int, ngroups: int, dstate: int) -> Streams:
+                   nheads: int, headdim: int, ngroups: int, dstate: int,
+                   heads=None) -> Streams:
     """Expert-specific linear projections of the same token.
 
     [notes] Method, key design 1: each expert e maps X_t to its candidate
     streams B_t^(e), C_t^(e), X_t^(e); [gist-en] Technical Summary 2,
     "Parameter Mixing", first bullet. Only selected experts are evaluated.
-    w_experts: [E, W, D] with rows X | B | C.
+    w_experts: [E, W, D] with rows X | B | C. ``heads`` keeps only the X rows
+    of those heads (X is then [M, k, len(heads), P]); B and C are always whole.
     """
     u = np.asarray(u, dtype=np.float64)
     M, k = idx.shape
@@ -98,14 +100,19 @@ def expert_streams(u: np.ndarray, w_experts: np.ndarray, idx: np.ndarray,
     W = w_experts.shape[1]
     if W != HP + 2 * GN:
         raise ValueError("expert width must be H*P + 2*G*N")
-    z = np.zeros((M, k, W))
+    hs = np.arange(nheads) if heads is None else np.asarray(heads)
+    rows_x = (hs[:, None] * headdim + np.arange(headdim)[None, :]).ravel()
+    keep = np.concatenate([rows_x, np.arange(HP, W)])
+    nx = rows_x.size
+    z = np.zeros((M, k, keep.size))
     for e in range(w_experts.shape[0]):
         rows, slots = np.nonzero(idx == e)
         if rows.size:
-            z[rows, slots] = u[rows] @ np.asarray(w_experts[e], dtype=np.float64).T
-    X = z[..., :HP].reshape(M, k, nheads, headdim)
-    B = z[..., HP:HP + GN].reshape(M, k, ngroups, dstate)
-    C = z[..., HP + GN:].reshape(M, k, ngroups, dstate)
+            we = np.asarray(w_experts[e][keep], dtype=np.float64)
+            z[rows, slots] = u[rows] @ we.T
+    X = z[..., :nx].reshape(M, k, hs.size, headdim)
+    B = z[..., nx:nx + GN].reshape(M, k, ngroups, dstate)
+    C = z[..., nx + GN:].reshape(M, k, ngroups, dstate)
     return Streams(X=X, B=B, C=C)
 
 
@@ -165,17 +172,16 @@ def forward(u: np.ndarray, w_router: np.ndarray, w_experts: np.ndarray, a: np.nd
     """The whole mixer: route, project, mix, recur, read out.
 
     u: [Bt, T, D]. ``heads`` restricts X, y and the state to those heads (the
-    routing, B and C never depend on the head). ``routing`` lets a caller pass
+    routing, B and C never depend on the head); "X" is then over those heads. ``routing`` lets a caller pass
     a routing the oracle itself produced (for example a different top-k
     choice at a flagged near-tie).
     """
     Bt, T, D = u.shape
     uf = u.reshape(Bt * T, D)
     r = routing if routing is not None else route(uf, w_router, top_k)
-    s = expert_streams(uf, w_experts, r.idx, nheads, headdim, ngroups, dstate)
+    s = expert_streams(uf, w_experts, r.idx, nheads, headdim, ngroups, dstate, heads=heads)
     B_hat, X, C_mix = mix_streams(s, r.w)
-    Xs = X if heads is None else X[:, :, np.asarray(heads)]
-    y, hT = recurrence(B_hat, Xs, C_mix, a, h_init, Bt, T, heads=heads)
+    y, hT = recurrence(B_hat, X, C_mix, a, h_init, Bt, T, heads=heads)
     return {"y": y, "h_final": hT, "routing": r, "B_hat": B_hat, "X": X, "C_mix": C_mix}
 
 

@@ -1,0 +1,226 @@
+"""Python binding of the Swimba C ABI (``include/swimba.h``).
+
+Argument marshalling only: every step of the mixer runs in the HIP kernels of
+``libswimba.so``. PyTorch provides device memory and the current stream. The
+library must have been built (``python -m selective_ssm_parameter_amd.build``);
+there is no fallback of any kind: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswimba.so")
+
+F32, BF16 = 0, 1
+CALL_ROUTE, CALL_PROJECT, CALL_SCAN, CALL_DECODE = 0, 1, 2, 3
+
+STATUS = {
+    0: "SWIMBA_OK", -1: "SWIMBA_ERR_NULL", -2: "SWIMBA_ERR_DIMS", -3: "SWIMBA_ERR_UNSUPPORTED",
+    -4: "SWIMBA_ERR_WORKSPACE", -5: "SWIMBA_ERR_ALIGN", -6: "SWIMBA_ERR_HIP",
+}
+
+EXPORTS = (
+    "swimba_abi_version", "swimba_last_error", "swimba_workspace_size", "swimba_route_topk",
+    "swimba_expert_project_mix", "swimba_ssd_chunk_scan", "swimba_decode_step",
+    "swimba_profile_enable", "swimba_profile_report",
+)
+
+
+class SwimbaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "seqlen", "d_model", "nheads", "headdim", "dstate", "ngroups", "n_experts",
+        "top_k", "chunk", "dtype", "reserved")]
+
+    def __repr__(self):
+        return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libswimba.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m selective_ssm_parameter_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I32, SZ = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(Dims)
+    L.swimba_abi_version.restype = I32
+    L.swimba_abi_version.argtypes = []
+    L.swimba_last_error.restype = ctypes.c_char_p
+    L.swimba_last_error.argtypes = []
+    L.swimba_workspace_size.restype = SZ
+    L.swimba_workspace_size.argtypes = [D, I32]
+    L.swimba_route_topk.restype = I32
+    L.swimba_route_topk.argtypes = [D, P, P, P, P, P, S]
+    L.swimba_expert_project_mix.restype = I32
+    L.swimba_expert_project_mix.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
+    L.swimba_ssd_chunk_scan.restype = I32
+    L.swimba_ssd_chunk_scan.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
+    L.swimba_decode_step.restype = I32
+    L.swimba_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
+    L.swimba_profile_enable.restype = I32
+    L.swimba_profile_enable.argtypes = [I32]
+    L.swimba_profile_report.restype = I32
+    L.swimba_profile_report.argtypes = [ctypes.c_char_p, SZ]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise SwimbaError(status, lib().swimba_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the Swimba library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def make_dims(batch, seqlen, d_model, nheads, headdim, dstate, ngroups, n_experts, top_k,
+              chunk, dtype) -> Dims:
+    dt = {"f32": F32, "bf16": BF16, F32: F32, BF16: BF16}[dtype]
+    return Dims(batch, seqlen, d_model, nheads, headdim, dstate, ngroups, n_experts, top_k,
+                chunk, dt, 0)
+
+
+def dims_of(wl, batch=None, seqlen=None) -> Dims:
+    """Dims of a ``synth.Workload`` (optionally with another batch or seqlen)."""
+    return make_dims(wl.batch if batch is None else batch, wl.seqlen if seqlen is None else seqlen,
+                     wl.d_model, wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.n_experts,
+                     wl.top_k, wl.chunk, wl.dtype)
+
+
+def torch_dtype(dims: Dims):
+    return torch.bfloat16 if dims.dtype == BF16 else torch.float32
+
+
+def abi_version() -> int:
+    return lib().swimba_abi_version()
+
+
+def swimba_workspace_size(dims: Dims, call: int) -> int:
+    return lib().swimba_workspace_size(ctypes.byref(dims), call)
+
+
+def workspace(dims: Dims, call: int, device="cuda"):
+    n = swimba_workspace_size(dims, call)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device), n
+
+
+# ----------------------------------------------------------------- raw calls
+
+def swimba_route_topk(dims, u, w_router, topk_idx, topk_w, logits=None, stream=None):
+    _check(lib().swimba_route_topk(ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(topk_idx),
+                                   _ptr(topk_w), _ptr(logits), _stream(stream)))
+
+
+def swimba_expert_project_mix(dims, u, w_experts, topk_idx, topk_w, B_hat, X_hat, C_mix, ws,
+                              ws_bytes=None, stream=None):
+    nb = ws.numel() if ws_bytes is None else ws_bytes
+    _check(lib().swimba_expert_project_mix(
+        ctypes.byref(dims), _ptr(u), _ptr(w_experts), _ptr(topk_idx), _ptr(topk_w), _ptr(B_hat),
+        _ptr(X_hat), _ptr(C_mix), _ptr(ws), nb, _stream(stream)))
+
+
+def swimba_ssd_chunk_scan(dims, B_hat, X_hat, C_mix, a, h_init, y, h_final, ws, ws_bytes=None,
+                          stream=None):
+    nb = (ws.numel() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check(lib().swimba_ssd_chunk_scan(
+        ctypes.byref(dims), _ptr(B_hat), _ptr(X_hat), _ptr(C_mix), _ptr(a), _ptr(h_init), _ptr(y),
+        _ptr(h_final), _ptr(ws), nb, _stream(stream)))
+
+
+def swimba_decode_step(dims, u, w_router, w_experts, a, h, y, topk_idx, ws, ws_bytes=None,
+                       stream=None):
+    nb = ws.numel() if ws_bytes is None else ws_bytes
+    _check(lib().swimba_decode_step(
+        ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(a), _ptr(h), _ptr(y),
+        _ptr(topk_idx), _ptr(ws), nb, _stream(stream)))
+
+
+def profile_enable(on: bool):
+    _check(lib().swimba_profile_enable(1 if on else 0))
+
+
+def profile_report() -> str:
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().swimba_profile_report(buf, len(buf))
+    if n < 0:
+        _check(n)
+    return buf.value.decode()
+
+
+# ----------------------------------------------------------------- helpers
+
+@dataclasses.dataclass
+class Buffers:
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    B_hat: torch.Tensor
+    X_hat: torch.Tensor
+    C_mix: torch.Tensor
+    y: torch.Tensor
+    h_final: torch.Tensor
+    ws_project: torch.Tensor
+    ws_scan: torch.Tensor
+    logits: torch.Tensor | None = None
+
+
+def alloc_buffers(dims: Dims, device="cuda", logits=False) -> Buffers:
+    """Every output and workspace of one prefill forward, allocated by torch."""
+    M = dims.batch * dims.seqlen
+    k, H, P, G, N = dims.top_k, dims.nheads, dims.headdim, dims.ngroups, dims.dstate
+    dt = torch_dtype(dims)
+    ws_p, _ = workspace(dims, CALL_PROJECT, device)
+    ws_s, _ = workspace(dims, CALL_SCAN, device)
+    return Buffers(
+        topk_idx=torch.empty(M, k, dtype=torch.int32, device=device),
+        topk_w=torch.empty(M, k, dtype=torch.float32, device=device),
+        B_hat=torch.empty(M, k, G, N, dtype=dt, device=device),
+        X_hat=torch.empty(M, k, H, P, dtype=dt, device=device),
+        C_mix=torch.empty(M, G, N, dtype=dt, device=device),
+        y=torch.empty(M, H, P, dtype=dt, device=device),
+        h_final=torch.empty(dims.batch, H, N, P, dtype=torch.float32, device=device),
+        ws_project=ws_p, ws_scan=ws_s,
+        logits=torch.empty(M, dims.n_experts, dtype=torch.float32, device=device) if logits else None,
+    )
+
+
+def forward(dims: Dims, u, w_router, w_experts, a, h_init=None, buf: Buffers | None = None,
+            stream=None) -> Buffers:
+    """Route -> project + mix -> chunked scan, on the current stream."""
+    if buf is None:
+        buf = alloc_buffers(dims, u.device)
+    swimba_route_topk(dims, u, w_router, buf.topk_idx, buf.topk_w, buf.logits, stream=stream)
+    swimba_expert_project_mix(dims, u, w_experts, buf.topk_idx, buf.topk_w, buf.B_hat, buf.X_hat,
+                              buf.C_mix, buf.ws_project, stream=stream)
+    swimba_ssd_chunk_scan(dims, buf.B_hat, buf.X_hat, buf.C_mix, a, h_init, buf.y, buf.h_final,
+                          buf.ws_scan, stream=stream)
+    return buf

@@ -1,0 +1,399 @@
+// C ABI of the Swimba mixer: argument validation, workspace carving, dispatch.
+// Every check runs before the first launch; no HIP call is made on an invalid
+// argument, so outputs stay untouched and the call is safe without a device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "swimba.h"
+
+using namespace swimba;
+
+namespace {
+
+thread_local std::string g_err;
+
+swimba_status fail(swimba_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+swimba_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SWIMBA_OK;
+  return fail(SWIMBA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------- dims
+
+struct Dims {
+  int64_t Bt, T, D, H, P, N, G, E, k, L, M, W, HP, GN;
+  bool bf16;
+  size_t esize;
+};
+
+swimba_status read_dims(const swimba_dims* d, Dims& o) {
+  if (!d) return fail(SWIMBA_ERR_NULL, "dims is NULL");
+  if (d->reserved != 0) return fail(SWIMBA_ERR_DIMS, "dims.reserved must be 0");
+  if (d->dtype != SWIMBA_F32 && d->dtype != SWIMBA_BF16)
+    return fail(SWIMBA_ERR_DIMS, "dims.dtype %d is not a swimba_dtype", d->dtype);
+  if (d->batch < 0 || d->seqlen < 0) return fail(SWIMBA_ERR_DIMS, "batch and seqlen must be >= 0");
+  if (d->d_model < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 || d->ngroups < 1 ||
+      d->n_experts < 1 || d->chunk < 1)
+    return fail(SWIMBA_ERR_DIMS, "d_model, nheads, headdim, dstate, ngroups, n_experts and chunk must be >= 1");
+  if (d->nheads % d->ngroups != 0) return fail(SWIMBA_ERR_DIMS, "ngroups must divide nheads");
+  if (d->top_k < 1 || d->top_k > d->n_experts)
+    return fail(SWIMBA_ERR_DIMS, "top_k must lie in [1, n_experts]");
+  o.Bt = d->batch; o.T = d->seqlen; o.D = d->d_model; o.H = d->nheads; o.P = d->headdim;
+  o.N = d->dstate; o.G = d->ngroups; o.E = d->n_experts; o.k = d->top_k; o.L = d->chunk;
+  o.M = o.Bt * o.T;
+  o.HP = o.H * o.P;
+  o.GN = o.G * o.N;
+  o.W = o.HP + 2 * o.GN;
+  o.bf16 = d->dtype == SWIMBA_BF16;
+  o.esize = o.bf16 ? 2 : 4;
+  if (o.M * o.k >= (int64_t(1) << 30) || o.W * o.D >= (int64_t(1) << 31) ||
+      o.HP > (1 << 20))
+    return fail(SWIMBA_ERR_DIMS, "problem too large for 32-bit pair indexing");
+  return SWIMBA_OK;
+}
+
+swimba_status check_kernel_shape(const Dims& d) {
+  if (d.P != 64) return fail(SWIMBA_ERR_UNSUPPORTED, "headdim %lld: only 64 has a kernel", (long long)d.P);
+  if (d.N != 16 && d.N != 32 && d.N != 64 && d.N != 128)
+    return fail(SWIMBA_ERR_UNSUPPORTED, "dstate %lld: supported 16, 32, 64, 128", (long long)d.N);
+  if (d.D % 32 != 0) return fail(SWIMBA_ERR_UNSUPPORTED, "d_model must be a multiple of 32");
+  if (d.E > 256) return fail(SWIMBA_ERR_UNSUPPORTED, "n_experts must be <= 256");
+  if (d.k > 8) return fail(SWIMBA_ERR_UNSUPPORTED, "top_k must be <= 8");
+  return SWIMBA_OK;
+}
+
+swimba_status check_scan_shape(const Dims& d) {
+  if (d.k > 2) return fail(SWIMBA_ERR_UNSUPPORTED, "the prefill scan supports top_k <= 2");
+  if (d.L != 32 && d.L != 64 && d.L != 128 && d.L != 256)
+    return fail(SWIMBA_ERR_UNSUPPORTED, "chunk must be 32, 64, 128 or 256");
+  return SWIMBA_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct ProjWs {
+  size_t counts, bases, offsets, tiles, sorted, cpart, total;
+};
+
+ProjWs proj_ws(const Dims& d) {
+  const int64_t pairs = d.M * d.k;
+  const int64_t nblk = bucket_blocks((int)pairs);
+  ProjWs w{};
+  size_t off = 0;
+  w.counts = off; off += align256(sizeof(int32_t) * nblk * (d.E + 1));
+  w.bases = off; off += align256(sizeof(int32_t) * nblk * (d.E + 1));
+  w.offsets = off; off += align256(sizeof(int32_t) * (d.E + 2));
+  w.tiles = off; off += align256(sizeof(int32_t) * (d.E + 1));
+  w.sorted = off; off += align256(sizeof(int32_t) * pairs);
+  w.cpart = off; off += align256(sizeof(float) * pairs * d.GN);
+  w.total = off;
+  return w;
+}
+
+struct DecWs {
+  size_t idx, w, bhat, xhat, cmix, proj, total;
+};
+
+DecWs dec_ws(const Dims& d) {
+  DecWs w{};
+  size_t off = 0;
+  const int64_t pairs = d.Bt * d.k;
+  w.idx = off; off += align256(sizeof(int32_t) * pairs);
+  w.w = off; off += align256(sizeof(float) * pairs);
+  w.bhat = off; off += align256(d.esize * pairs * d.GN);
+  w.xhat = off; off += align256(d.esize * pairs * d.HP);
+  w.cmix = off; off += align256(d.esize * d.Bt * d.GN);
+  w.proj = off;
+  Dims one = d;
+  one.T = 1;
+  one.M = d.Bt;
+  off += proj_ws(one).total;
+  w.total = off;
+  return w;
+}
+
+size_t scan_bytes(const Dims& d) {
+  return scan_ws_bytes(scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
+                                 (int)d.k, (int)d.L));
+}
+
+swimba_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return SWIMBA_OK;
+  if (!ws) return fail(SWIMBA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (have < need) return fail(SWIMBA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, have);
+  if (!aligned16(ws)) return fail(SWIMBA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  return SWIMBA_OK;
+}
+
+#define REQUIRE_PTR(p)                                                  \
+  do {                                                                  \
+    if (!(p)) return fail(SWIMBA_ERR_NULL, "%s is NULL", #p);           \
+    if (!aligned16(p)) return fail(SWIMBA_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define OPTIONAL_PTR(p)                                                 \
+  do {                                                                  \
+    if ((p) && !aligned16(p)) return fail(SWIMBA_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+ProjGeom proj_geom(const Dims& d, int64_t M) {
+  ProjGeom g;
+  g.M = (int)M; g.D = (int)d.D; g.H = (int)d.H; g.P = (int)d.P; g.G = (int)d.G; g.N = (int)d.N;
+  g.E = (int)d.E; g.k = (int)d.k; g.W = (int)d.W;
+  return g;
+}
+
+// Runs bucketing, the grouped projection and the slot-ordered C sum for M tokens.
+hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_experts,
+                       const int32_t* idx, const float* w, void* B_hat, void* X_hat, void* C_mix,
+                       unsigned char* ws, hipStream_t s) {
+  Dims dm = d;
+  dm.M = M;
+  const ProjWs lay = proj_ws(dm);
+  const int pairs = (int)(M * d.k);
+  const int bm = proj_bm(pairs, (int)d.E);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
+  int32_t* bases = reinterpret_cast<int32_t*>(ws + lay.bases);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + lay.offsets);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + lay.sorted);
+  float* cpart = reinterpret_cast<float*>(ws + lay.cpart);
+  hipError_t e = launch_bucket(d.bf16, idx, pairs, (int)d.E, bm, counts, bases, offsets, tiles,
+                               sorted, X_hat, (int)d.HP, B_hat, (int)d.GN, cpart, s);
+  if (e != hipSuccess) return e;
+  return launch_project(d.bf16, proj_geom(d, M), u, w_experts, sorted, offsets, tiles, idx, w, bm,
+                        B_hat, X_hat, cpart, C_mix, s);
+}
+
+// ---------------------------------------------------------------- profiling
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t ev = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return ev;
+  }
+  hipEvent_t ev = nullptr;
+  if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+  return ev;
+}
+
+}  // namespace
+
+namespace swimba {
+
+void prof_begin(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  ProfRec r{name, prof_event(), prof_event()};
+  if (!r.start || !r.stop) return;
+  hipEventRecord(r.start, s);
+  g_prof_recs.push_back(r);
+}
+
+void prof_end(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || g_prof_recs.empty()) return;
+  hipEventRecord(g_prof_recs.back().stop, s);
+}
+
+}  // namespace swimba
+
+// ---------------------------------------------------------------- C ABI
+
+extern "C" {
+
+int32_t swimba_abi_version(void) { return SWIMBA_ABI_VERSION; }
+
+const char* swimba_last_error(void) { return g_err.c_str(); }
+
+size_t swimba_workspace_size(const swimba_dims* dims, int32_t call) {
+  Dims d;
+  std::string saved = g_err;
+  const swimba_status st = read_dims(dims, d);
+  g_err = saved;
+  if (st != SWIMBA_OK) return 0;
+  switch (call) {
+    case SWIMBA_CALL_ROUTE: return 0;
+    case SWIMBA_CALL_PROJECT: return d.M == 0 ? 0 : proj_ws(d).total;
+    case SWIMBA_CALL_SCAN: return scan_bytes(d);
+    case SWIMBA_CALL_DECODE: return d.Bt == 0 ? 0 : dec_ws(d).total;
+    default: return 0;
+  }
+}
+
+swimba_status swimba_route_topk(const swimba_dims* dims, const void* u, const void* w_router,
+                                int32_t* topk_idx, float* topk_w, float* logits,
+                                hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if (d.M == 0) return SWIMBA_OK;
+  REQUIRE_PTR(u);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  OPTIONAL_PTR(logits);
+  return hip_status(launch_route(d.bf16, u, w_router, (int)d.M, (int)d.D, (int)d.E, (int)d.k,
+                                 topk_idx, topk_w, logits, stream),
+                    "route_topk launch");
+}
+
+swimba_status swimba_expert_project_mix(const swimba_dims* dims, const void* u,
+                                        const void* w_experts, const int32_t* topk_idx,
+                                        const float* topk_w, void* B_hat, void* X_hat,
+                                        void* C_mix, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if (d.M == 0) return SWIMBA_OK;
+  REQUIRE_PTR(u);
+  REQUIRE_PTR(w_experts);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(B_hat);
+  REQUIRE_PTR(X_hat);
+  REQUIRE_PTR(C_mix);
+  if ((st = check_ws(ws, ws_bytes, proj_ws(d).total)) != SWIMBA_OK) return st;
+  return hip_status(run_project(d, d.M, u, w_experts, topk_idx, topk_w, B_hat, X_hat, C_mix,
+                                static_cast<unsigned char*>(ws), stream),
+                    "expert_project_mix launch");
+}
+
+swimba_status swimba_ssd_chunk_scan(const swimba_dims* dims, const void* B_hat,
+                                    const void* X_hat, const void* C_mix, const float* a,
+                                    const float* h_init, void* y, float* h_final, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_scan_shape(d)) != SWIMBA_OK) return st;
+  if (d.Bt == 0) return SWIMBA_OK;
+  REQUIRE_PTR(a);
+  OPTIONAL_PTR(h_init);
+  OPTIONAL_PTR(h_final);
+  if (d.M > 0) {
+    REQUIRE_PTR(B_hat);
+    REQUIRE_PTR(X_hat);
+    REQUIRE_PTR(C_mix);
+    REQUIRE_PTR(y);
+  }
+  if ((st = check_ws(ws, ws_bytes, scan_bytes(d))) != SWIMBA_OK) return st;
+  const ScanGeom g = scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
+                               (int)d.k, (int)d.L);
+  return hip_status(launch_scan(d.bf16, g, B_hat, X_hat, C_mix, a, h_init, y, h_final,
+                                static_cast<float*>(ws), stream),
+                    "ssd_chunk_scan launch");
+}
+
+swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const void* w_router,
+                                 const void* w_experts, const float* a, float* h, void* y,
+                                 int32_t* topk_idx, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if (d.T != 1) return fail(SWIMBA_ERR_DIMS, "decode_step needs seqlen == 1");
+  if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if (d.Bt == 0) return SWIMBA_OK;
+  REQUIRE_PTR(u);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(w_experts);
+  REQUIRE_PTR(a);
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(y);
+  OPTIONAL_PTR(topk_idx);
+  const DecWs lay = dec_ws(d);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != SWIMBA_OK) return st;
+  unsigned char* w8 = static_cast<unsigned char*>(ws);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w8 + lay.idx);
+  float* tw = reinterpret_cast<float*>(w8 + lay.w);
+  void* bhat = w8 + lay.bhat;
+  void* xhat = w8 + lay.xhat;
+  void* cmix = w8 + lay.cmix;
+  hipError_t e = launch_route(d.bf16, u, w_router, (int)d.Bt, (int)d.D, (int)d.E, (int)d.k, idx,
+                              tw, nullptr, stream);
+  if (e != hipSuccess) return hip_status(e, "decode_step route launch");
+  e = run_project(d, d.Bt, u, w_experts, idx, tw, bhat, xhat, cmix, w8 + lay.proj, stream);
+  if (e != hipSuccess) return hip_status(e, "decode_step projection launch");
+  e = launch_decode_state(d.bf16, (int)d.Bt, (int)d.H, (int)d.G, (int)d.N, (int)d.P, (int)d.k,
+                          bhat, xhat, cmix, a, h, y, stream);
+  return hip_status(e, "decode_step state launch");
+}
+
+swimba_status swimba_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return SWIMBA_OK;
+}
+
+int32_t swimba_profile_report(char* buf, size_t cap) {
+  if (!buf || cap == 0) return fail(SWIMBA_ERR_NULL, "report buffer is NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<std::string> names;
+  std::vector<double> ms;
+  std::vector<int> cnt;
+  for (const ProfRec& r : g_prof_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess)
+      t = -1.f;
+    size_t i = 0;
+    while (i < names.size() && names[i] != r.name) ++i;
+    if (i == names.size()) {
+      names.emplace_back(r.name);
+      ms.push_back(0.0);
+      cnt.push_back(0);
+    }
+    ms[i] += t;
+    cnt[i] += 1;
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_recs.clear();
+  std::string out = "{";
+  for (size_t i = 0; i < names.size(); ++i) {
+    char item[256];
+    snprintf(item, sizeof(item), "%s\"%s\": {\"launches\": %d, \"ms\": %.6f}", i ? ", " : "",
+             names[i].c_str(), cnt[i], ms[i]);
+    out += item;
+  }
+  out += "}";
+  if (out.size() + 1 > cap) return fail(SWIMBA_ERR_DIMS, "report buffer too small");
+  snprintf(buf, cap, "%s", out.c_str());
+  return (int32_t)out.size();
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Host-side launchers of the Swimba kernels. Each returns the hipError_t of
+// its launch(es); arguments are validated by the API layer before any call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swimba {
+
+// Optional per-kernel timing (see swimba_profile_enable in the public header).
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+struct ProjGeom {
+  int M, D, H, P, G, N, E, k, W;
+  int HP() const { return H * P; }
+  int GN() const { return G * N; }
+};
+
+// Router: logits (fp32), softmax, top-k.
+hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M, int D, int E, int k,
+                        int32_t* idx, float* w, float* logits, hipStream_t s);
+
+// Bucketing of (token, slot) pairs by expert.
+constexpr int kBucketPairs = 1024;  // pairs per bucketing block
+int bucket_blocks(int pairs);
+hipError_t launch_bucket(bool is_bf16, const int32_t* idx, int pairs, int E, int bm,
+                         int32_t* counts, int32_t* bases, int32_t* offsets, int32_t* tile_offsets,
+                         int32_t* sorted, void* X_hat, int HP, void* B_hat, int GN,
+                         float* c_part, hipStream_t s);
+
+// Grouped expert projection with the mix epilogue, then the slot-ordered C sum.
+int proj_row_tiles_max(int pairs, int E, int bm);
+int proj_bm(int pairs, int E);
+hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const void* w_experts,
+                          const int32_t* sorted, const int32_t* offsets,
+                          const int32_t* tile_offsets, const int32_t* idx, const float* w,
+                          int bm, void* B_hat, void* X_hat, float* c_part, void* C_mix,
+                          hipStream_t s);
+
+// Chunked scan.
+struct ScanGeom {
+  int Bt, T, H, G, N, P, k, L;
+  int segs;          // segments per sequence
+  int seg_chunks;    // chunks per segment
+};
+ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L);
+size_t scan_ws_bytes(const ScanGeom& g);
+hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
+                       const void* C_mix, const float* a, const float* h_init, void* y,
+                       float* h_final, float* ws, hipStream_t s);
+hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t s);
+
+// Decode: in-place state update and readout for one token per sequence.
+hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
+                               const void* B_hat, const void* X_hat, const void* C_mix,
+                               const float* a, float* h, void* y, hipStream_t s);
+
+}  // namespace swimba

@@ -1,0 +1,120 @@
+// Router and top-k active set (papernotes.org notes on "Swimba: Switch Mamba
+// Model Scales State Space Models", Method, key design 1: pi_t = softmax(g_t)
+// with a top-k sparse active set; gist.science English summary, Technical
+// Summary section 2, Expert Routing).
+//
+// One workgroup routes 64 tokens. Wave w computes the logits of tokens
+// [16w, 16w + 16) against every expert with 16x16 matrix-core tiles: the A
+// operand is the token rows of u, the B operand the router rows (both are
+// contiguous along d_model, so every lane loads 16 bytes). Products of bf16
+// values are exact in fp32 and accumulate in fp32, so the logits are never
+// rounded to bf16. The logits go through LDS; one thread per token then picks
+// the top-k (strictly greater wins, so equal logits keep the lower index) and
+// evaluates the softmax over all E experts in fp32.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace swimba {
+
+constexpr int kRouteTok = 64;
+
+template <typename T>
+__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
+                                                    const T* __restrict__ wr, int M, int D,
+                                                    int E, int k, int32_t* __restrict__ idx,
+                                                    float* __restrict__ wout,
+                                                    float* __restrict__ logits) {
+  extern __shared__ float lg[];  // [64][E + 1]
+  typedef typename Vec<T>::x8 F;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int tok0 = blockIdx.x * kRouteTok;
+  const int ET = (E + 15) / 16;
+  const int ldl = E + 1;
+
+  const int row = tok0 + wave * 16 + c;
+  const bool row_ok = row < M;
+  const T* urow = u + (size_t)(row_ok ? row : 0) * D + 8 * g;
+
+  // Expert tiles are processed 4 at a time (16 accumulators per lane).
+  for (int et0 = 0; et0 < ET; et0 += 4) {
+    floatx4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < D; k0 += 32) {
+      F a = row_ok ? load8<T>(urow + k0) : zero8<T>();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (et0 + i) * 16 + c;
+        if (et0 + i < ET) {
+          F b = e < E ? load8<T>(wr + (size_t)e * D + k0 + 8 * g) : zero8<T>();
+          acc[i] = mma16(a, b, acc[i]);
+        }
+      }
+    }
+    // acc[i][q] = logit of token (16*wave + 4g + q) for expert (16*(et0+i) + c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = (et0 + i) * 16 + c;
+      if (et0 + i < ET && e < E) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lg[(wave * 16 + 4 * g + q) * ldl + e] = acc[i][q];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  if (t >= kRouteTok || tok0 + t >= M) return;
+  const int m = tok0 + t;
+  const float* l = lg + t * ldl;
+  if (logits) {
+    for (int e = 0; e < E; ++e) logits[(size_t)m * E + e] = l[e];
+  }
+  int chosen[8];
+  for (int j = 0; j < k; ++j) {
+    int bi = -1;
+    float best = 0.f;
+    for (int e = 0; e < E; ++e) {
+      bool taken = false;
+      for (int q = 0; q < j; ++q) taken |= (chosen[q] == e);
+      if (taken) continue;
+      if (bi < 0 || l[e] > best) {
+        bi = e;
+        best = l[e];
+      }
+    }
+    chosen[j] = bi;
+  }
+  const float mx = l[chosen[0]];
+  float sum = 0.f;
+  for (int e = 0; e < E; ++e) sum += expf(l[e] - mx);
+  const float inv = 1.f / sum;
+  for (int j = 0; j < k; ++j) {
+    idx[(size_t)m * k + j] = chosen[j];
+    wout[(size_t)m * k + j] = expf(l[chosen[j]] - mx) * inv;
+  }
+}
+
+hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M, int D, int E, int k,
+                        int32_t* idx, float* w, float* logits, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  dim3 grid((M + kRouteTok - 1) / kRouteTok), block(256);
+  size_t lds = (size_t)kRouteTok * (E + 1) * sizeof(float);
+  hipError_t err = hipFuncSetAttribute(
+      is_bf16 ? (const void*)route_kernel<bf16> : (const void*)route_kernel<float>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  prof_begin("route_topk", s);
+  if (is_bf16)
+    hipLaunchKernelGGL(route_kernel<bf16>, grid, block, lds, s, (const bf16*)u,
+                       (const bf16*)w_router, M, D, E, k, idx, w, logits);
+  else
+    hipLaunchKernelGGL(route_kernel<float>, grid, block, lds, s, (const float*)u,
+                       (const float*)w_router, M, D, E, k, idx, w, logits);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace swimba

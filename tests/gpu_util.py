@@ -1,0 +1,131 @@
+"""Helpers shared by the GPU parity tests: upload, download, comparison.
+
+Inputs come from ``selective_ssm_parameter_amd.synth``; expected values come
+from the fp64 oracle only.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import swimba as osw
+from selective_ssm_parameter_amd import binding as sb
+from selective_ssm_parameter_amd import synth
+
+TOL = {synth.F32: 1e-4, synth.BF16: 2e-2}
+# Intermediate streams (one rounding of an fp32-accumulated dot product).
+STREAM_TOL = {synth.F32: 1e-5, synth.BF16: 8e-3}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, dtype, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device=device, dtype=dtype)
+
+
+def host(t) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def tdt(wl):
+    return torch.bfloat16 if wl.dtype == synth.BF16 else torch.float32
+
+
+def upload(wl, inp, device="cuda"):
+    dt = tdt(wl)
+    return {
+        "u": dev(inp["u"].reshape(-1, wl.d_model), dt, device),
+        "w_router": dev(inp["w_router"], dt, device),
+        "w_experts": dev(inp["w_experts"], dt, device),
+        "a": dev(inp["a"], torch.float32, device),
+        "h_init": None if inp["h_init"] is None else dev(inp["h_init"], torch.float32, device),
+    }
+
+
+def round_store(x, wl):
+    """What the library stores for a dtype-typed output, as fp64."""
+    x = np.asarray(x, dtype=np.float32)
+    if wl.dtype == synth.BF16:
+        x = synth.round_bf16(x)
+    return x.astype(np.float64)
+
+
+def slice_err(got, ref, axes_slice=(0, 2)):
+    """max over (batch, head) slices of max_i |d_i| / max(|ref_i|, rms(ref slice)).
+
+    got/ref: [Bt, T, H, P] (y) or [Bt, H, N, P] (states, use axes (0, 1))."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    worst = 0.0
+    a0, a1 = axes_slice
+    for i in range(ref.shape[a0]):
+        for j in range(ref.shape[a1]):
+            r = np.take(np.take(ref, i, axis=a0), j, axis=a1 - 1)
+            g = np.take(np.take(got, i, axis=a0), j, axis=a1 - 1)
+            if r.size == 0:
+                continue
+            rms = np.sqrt(np.mean(r * r))
+            den = np.maximum(np.abs(r), rms)
+            den = np.where(den > 0, den, 1.0)
+            worst = max(worst, float(np.max(np.abs(g - r) / den)))
+    return worst
+
+
+def rel_err(got, ref):
+    """max_i |d_i| / max(|ref_i|, rms(ref)) over the whole tensor."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(ref * ref))
+    den = np.maximum(np.abs(ref), rms)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(got - ref) / den))
+
+
+def check_routing(idx_gpu, w_gpu, r: osw.Routing, wl):
+    """Index parity, bit-exact except at flagged near-ties; returns the tokens
+    (flat indices) where the GPU picked a different, equally valid, order."""
+    idx_gpu = np.asarray(idx_gpu)
+    diff = np.any(idx_gpu != r.idx, axis=1)
+    bad = diff & ~r.flagged
+    assert not bad.any(), f"top-k mismatch at unflagged tokens {np.nonzero(bad)[0][:10]}"
+    for m in np.nonzero(diff)[0]:
+        # At a near-tie the GPU's choice must still be a valid top-k: distinct
+        # experts whose logits match the oracle's ranks within the margin.
+        sel = idx_gpu[m]
+        assert len(set(sel.tolist())) == len(sel)
+        assert np.all(np.abs(r.logits[m, sel] - r.logits[m, r.idx[m]]) < osw.TIE_MARGIN)
+    ok = ~diff
+    werr = np.max(np.abs(np.asarray(w_gpu)[ok] - r.w[ok]) / np.maximum(r.w[ok], 1e-30)) if ok.any() else 0.0
+    assert werr < 1e-5, f"top-k weight relative error {werr}"
+    return np.nonzero(diff)[0]
+
+
+def valid_prefix(flips, batch, seqlen):
+    """Per batch row, the number of leading tokens unaffected by a near-tie flip."""
+    lim = np.full(batch, seqlen)
+    for m in flips:
+        b, t = divmod(int(m), seqlen)
+        lim[b] = min(lim[b], t)
+    return lim
+
+
+def oracle_forward(wl, inp, heads=None, routing=None):
+    return osw.forward(inp["u"], inp["w_router"], inp["w_experts"], inp["a"], inp["h_init"],
+                       nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
+                       dstate=wl.dstate, top_k=wl.top_k, heads=heads, routing=routing)
+
+
+def run_forward(wl, d, logits=False):
+    dims = sb.dims_of(wl)
+    buf = sb.alloc_buffers(dims, "cuda", logits=logits)
+    sb.forward(dims, d["u"], d["w_router"], d["w_experts"], d["a"], d["h_init"], buf)
+    torch.cuda.synchronize()
+    return buf

@@ -78,13 +78,13 @@ def rec_wrong_group(B_hat, X, C_mix, a, h_init, batch, seqlen, heads=None):
     return np.concatenate(ys, axis=2), np.concatenate(hs, axis=1)
 
 
-def streams_b_c_swapped(u, w_experts, idx, nheads, headdim, ngroups, dstate):
-    s = _orig_streams(u, w_experts, idx, nheads, headdim, ngroups, dstate)
+def streams_b_c_swapped(u, w_experts, idx, nheads, headdim, ngroups, dstate, heads=None):
+    s = _orig_streams(u, w_experts, idx, nheads, headdim, ngroups, dstate, heads)
     return osw.Streams(X=s.X, B=s.C, C=s.B)
 
 
-def streams_transposed_x(u, w_experts, idx, nheads, headdim, ngroups, dstate):
-    s = _orig_streams(u, w_experts, idx, nheads, headdim, ngroups, dstate)
+def streams_transposed_x(u, w_experts, idx, nheads, headdim, ngroups, dstate, heads=None):
+    s = _orig_streams(u, w_experts, idx, nheads, headdim, ngroups, dstate, heads)
     M, k, H, P = s.X.shape
     return osw.Streams(X=s.X.reshape(M, k, P, H).transpose(0, 1, 3, 2).copy(), B=s.B, C=s.C)
 
