@@ -44,9 +44,19 @@ extern "C" {
 
 #define SWIMBA_ABI_VERSION 1
 
+/*
+ * Element types. "stream" below names the element type of the intermediate
+ * streams B_hat, X_hat and C_mix:
+ *   SWIMBA_F32:  u, weights, streams and y are float32.
+ *   SWIMBA_BF16: u, weights and y are bfloat16; the streams are float16 (the
+ *                same bytes with 8x finer spacing, so three roundings of the
+ *                streams do not dominate the error of y; their magnitudes, and
+ *                those of C_mix . B_hat dot products, must stay below 65504).
+ * States and a are float32 in both cases.
+ */
 typedef enum swimba_dtype {
-  SWIMBA_F32 = 0,  /* every stream tensor is float32 */
-  SWIMBA_BF16 = 1  /* u, weights, B_hat, X_hat, C_mix and y are bfloat16 */
+  SWIMBA_F32 = 0,
+  SWIMBA_BF16 = 1
 } swimba_dtype;
 
 typedef enum swimba_status {
@@ -129,16 +139,16 @@ swimba_status swimba_route_topk(const swimba_dims* dims, const void* u, const vo
  *   X_hat[m, j] = z[0 : H*P]                          (as [H, P])
  *   B_hat[m, j] = w * z[H*P : H*P + G*N]              (as [G, N])
  *   C_mix[m]    = sum_j w * z[H*P + G*N : H*P + 2*G*N] (as [G, N]), summed in
- *                 slot order j = 0..k-1 in fp32, then stored in dtype.
+ *                 slot order j = 0..k-1 in fp32, then stored as stream.
  * U~_m = sum_j B_hat[m, j] X_hat[m, j]^T is never formed.
  *   u          [M, D]              dtype
  *   w_experts  [E, H*P + 2*G*N, D] dtype
  *   topk_idx   [M, k] int32 (values in [0, E); validated on the device: an
  *              out-of-range index makes its slot contribute zeros)
  *   topk_w     [M, k] float32
- *   B_hat      [M, k, G, N] dtype out
- *   X_hat      [M, k, H, P] dtype out
- *   C_mix      [M, G, N]    dtype out
+ *   B_hat      [M, k, G, N] stream out
+ *   X_hat      [M, k, H, P] stream out
+ *   C_mix      [M, G, N]    stream out
  *   ws         workspace of swimba_workspace_size(dims, SWIMBA_CALL_PROJECT)
  */
 swimba_status swimba_expert_project_mix(const swimba_dims* dims, const void* u,
@@ -156,8 +166,9 @@ swimba_status swimba_expert_project_mix(const swimba_dims* dims, const void* u,
  *   y[t, h] = C_mix[t, g]^T h_t                                     (P)
  * computed as, per chunk: a masked quadratic form over the chunk's
  * k-concatenated (token, slot) pairs, plus the decayed readout of the state
- * entering the chunk; states are carried across chunks in fp32.
- *   B_hat    [M, k, G, N] dtype;  X_hat [M, k, H, P] dtype;  C_mix [M, G, N] dtype
+ * entering the chunk; states are carried across chunks in fp32. Matrix-core
+ * operands are of the stream type, accumulation is fp32.
+ *   B_hat    [M, k, G, N] stream;  X_hat [M, k, H, P] stream;  C_mix [M, G, N] stream
  *   a        [H] float32, each in [0, 1)
  *   h_init   [Bt, H, N, P] float32, or NULL for zeros
  *   y        [M, H, P] dtype out

@@ -118,7 +118,13 @@ def dims_of(wl, batch=None, seqlen=None) -> Dims:
 
 
 def torch_dtype(dims: Dims):
+    """Element type of u, the weights and y."""
     return torch.bfloat16 if dims.dtype == BF16 else torch.float32
+
+
+def stream_dtype(dims: Dims):
+    """Element type of B_hat, X_hat and C_mix (fp16 when the inputs are bf16)."""
+    return torch.float16 if dims.dtype == BF16 else torch.float32
 
 
 def abi_version() -> int:
@@ -198,14 +204,15 @@ def alloc_buffers(dims: Dims, device="cuda", logits=False) -> Buffers:
     M = dims.batch * dims.seqlen
     k, H, P, G, N = dims.top_k, dims.nheads, dims.headdim, dims.ngroups, dims.dstate
     dt = torch_dtype(dims)
+    st = stream_dtype(dims)
     ws_p, _ = workspace(dims, CALL_PROJECT, device)
     ws_s, _ = workspace(dims, CALL_SCAN, device)
     return Buffers(
         topk_idx=torch.empty(M, k, dtype=torch.int32, device=device),
         topk_w=torch.empty(M, k, dtype=torch.float32, device=device),
-        B_hat=torch.empty(M, k, G, N, dtype=dt, device=device),
-        X_hat=torch.empty(M, k, H, P, dtype=dt, device=device),
-        C_mix=torch.empty(M, G, N, dtype=dt, device=device),
+        B_hat=torch.empty(M, k, G, N, dtype=st, device=device),
+        X_hat=torch.empty(M, k, H, P, dtype=st, device=device),
+        C_mix=torch.empty(M, G, N, dtype=st, device=device),
         y=torch.empty(M, H, P, dtype=dt, device=device),
         h_final=torch.empty(dims.batch, H, N, P, dtype=torch.float32, device=device),
         ws_project=ws_p, ws_scan=ws_s,

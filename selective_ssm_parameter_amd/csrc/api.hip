@@ -62,7 +62,7 @@ swimba_status read_dims(const swimba_dims* d, Dims& o) {
   o.GN = o.G * o.N;
   o.W = o.HP + 2 * o.GN;
   o.bf16 = d->dtype == SWIMBA_BF16;
-  o.esize = o.bf16 ? 2 : 4;
+  o.esize = o.bf16 ? 2 : 4;  // stream element: fp16 for bf16 inputs, else fp32
   if (o.M * o.k >= (int64_t(1) << 30) || o.W * o.D >= (int64_t(1) << 31) ||
       o.HP > (1 << 20))
     return fail(SWIMBA_ERR_DIMS, "problem too large for 32-bit pair indexing");
@@ -186,12 +186,13 @@ hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_ex
 // ---------------------------------------------------------------- profiling
 
 struct ProfRec {
-  const char* name;
+  std::string name;
   hipEvent_t start, stop;
 };
 
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+thread_local const char* g_prof_prefix = "";  // "decode_" inside swimba_decode_step
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -213,7 +214,7 @@ namespace swimba {
 void prof_begin(const char* name, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
-  ProfRec r{name, prof_event(), prof_event()};
+  ProfRec r{std::string(g_prof_prefix) + name, prof_event(), prof_event()};
   if (!r.start || !r.stop) return;
   hipEventRecord(r.start, s);
   g_prof_recs.push_back(r);
@@ -337,6 +338,10 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
   OPTIONAL_PTR(topk_idx);
   const DecWs lay = dec_ws(d);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != SWIMBA_OK) return st;
+  struct PrefixGuard {
+    PrefixGuard() { g_prof_prefix = "decode_"; }
+    ~PrefixGuard() { g_prof_prefix = ""; }
+  } prefix_guard;
   unsigned char* w8 = static_cast<unsigned char*>(ws);
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w8 + lay.idx);
   float* tw = reinterpret_cast<float*>(w8 + lay.w);

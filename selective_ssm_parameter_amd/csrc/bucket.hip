@@ -151,8 +151,8 @@ hipError_t launch_bucket(bool is_bf16, const int32_t* idx, int pairs, int E, int
   if (nblk > 0) {
     prof_begin("bucket_scatter", s);
     if (is_bf16)
-      hipLaunchKernelGGL(bucket_scatter_kernel<bf16>, dim3(nblk), dim3(256), 5 * hl, s, idx,
-                         pairs, E, bases, sorted, (bf16*)X_hat, HP, (bf16*)B_hat, GN, c_part);
+      hipLaunchKernelGGL(bucket_scatter_kernel<f16>, dim3(nblk), dim3(256), 5 * hl, s, idx,
+                         pairs, E, bases, sorted, (f16*)X_hat, HP, (f16*)B_hat, GN, c_part);
     else
       hipLaunchKernelGGL(bucket_scatter_kernel<float>, dim3(nblk), dim3(256), 5 * hl, s, idx,
                          pairs, E, bases, sorted, (float*)X_hat, HP, (float*)B_hat, GN, c_part);

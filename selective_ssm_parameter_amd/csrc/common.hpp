@@ -18,6 +18,9 @@ namespace swimba {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -27,6 +30,10 @@ template <> struct Vec<bf16> {
   typedef bf16x8 x8;
   typedef bf16x4 x4;
 };
+template <> struct Vec<f16> {
+  typedef f16x8 x8;
+  typedef f16x4 x4;
+};
 template <> struct Vec<float> {
   typedef floatx8 x8;
   typedef floatx4 x4;
@@ -35,6 +42,10 @@ template <> struct Vec<float> {
 // One K=32 step of a 16x16 tile: bf16 inputs, fp32 accumulation.
 __device__ __forceinline__ floatx4 mma16(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mma16(f16x8 a, f16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // The same contraction in fp32: eight 16x16x4 fp32 matrix-core ops. In op i,
@@ -48,15 +59,20 @@ __device__ __forceinline__ floatx4 mma16(floatx8 a, floatx8 b, floatx4 c) {
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
 
 // 16-byte global/LDS vector helpers.
 template <typename T> __device__ __forceinline__ typename Vec<T>::x8 load8(const T* p);
 template <> __device__ __forceinline__ bf16x8 load8<bf16>(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+template <> __device__ __forceinline__ f16x8 load8<f16>(const f16* p) {
+  return *reinterpret_cast<const f16x8*>(p);
 }
 template <> __device__ __forceinline__ floatx8 load8<float>(const float* p) {
   floatx4 lo = *reinterpret_cast<const floatx4*>(p);
@@ -70,6 +86,9 @@ template <> __device__ __forceinline__ floatx8 load8<float>(const float* p) {
 template <typename T> __device__ __forceinline__ void store8(T* p, typename Vec<T>::x8 v);
 template <> __device__ __forceinline__ void store8<bf16>(bf16* p, bf16x8 v) {
   *reinterpret_cast<bf16x8*>(p) = v;
+}
+template <> __device__ __forceinline__ void store8<f16>(f16* p, f16x8 v) {
+  *reinterpret_cast<f16x8*>(p) = v;
 }
 template <> __device__ __forceinline__ void store8<float>(float* p, floatx8 v) {
   floatx4 lo = {v[0], v[1], v[2], v[3]};
@@ -97,6 +116,22 @@ __device__ __forceinline__ typename Vec<T>::x8 load4x2(const T* p0, const T* p1)
     r[i] = lo[i];
     r[4 + i] = hi[i];
   }
+  return r;
+}
+
+// Element type of the intermediate streams (B_hat, X_hat, C_mix) and of every
+// matrix-core operand inside the scan, per input type: bf16 inputs keep their
+// streams in fp16 (same bytes, 8x finer spacing; range +-65504), fp32 stays fp32.
+template <typename TI> struct StreamOf;
+template <> struct StreamOf<bf16> { typedef f16 type; };
+template <> struct StreamOf<float> { typedef float type; };
+
+// Convert 8 values between element types.
+template <typename TO, typename TI>
+__device__ __forceinline__ typename Vec<TO>::x8 convert8(typename Vec<TI>::x8 v) {
+  typename Vec<TO>::x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = from_f32<TO>(to_f32(v[i]));
   return r;
 }
 

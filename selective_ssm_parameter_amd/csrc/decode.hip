@@ -19,10 +19,10 @@ namespace swimba {
 constexpr int kDecMaxK = 8;
 constexpr int kDecMaxN = 128;
 
-template <typename T>
+template <typename S, typename TY>
 __global__ __launch_bounds__(256) void decode_state_kernel(
-    const T* __restrict__ B_hat, const T* __restrict__ X_hat, const T* __restrict__ C_mix,
-    const float* __restrict__ a, float* __restrict__ hstate, T* __restrict__ y, int H, int G,
+    const S* __restrict__ B_hat, const S* __restrict__ X_hat, const S* __restrict__ C_mix,
+    const float* __restrict__ a, float* __restrict__ hstate, TY* __restrict__ y, int H, int G,
     int N, int k) {
   constexpr int P = 64;
   __shared__ float sB[kDecMaxK][kDecMaxN];
@@ -63,9 +63,9 @@ __global__ __launch_bounds__(256) void decode_state_kernel(
   if (threadIdx.x < 16) {
     floatx4 s = red[0][threadIdx.x];
     for (int r = 1; r < 16; ++r) s += red[r][threadIdx.x];
-    T* yo = y + ((size_t)b * H + h) * P + 4 * threadIdx.x;
+    TY* yo = y + ((size_t)b * H + h) * P + 4 * threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) yo[i] = from_f32<T>(s[i]);
+    for (int i = 0; i < 4; ++i) yo[i] = from_f32<TY>(s[i]);
   }
 }
 
@@ -76,11 +76,11 @@ hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P,
   if (Bt == 0) return hipSuccess;
   prof_begin("decode_state", s);
   if (is_bf16)
-    hipLaunchKernelGGL(decode_state_kernel<bf16>, dim3(H, Bt), dim3(256), 0, s,
-                       (const bf16*)B_hat, (const bf16*)X_hat, (const bf16*)C_mix, a, h, (bf16*)y,
+    hipLaunchKernelGGL((decode_state_kernel<f16, bf16>), dim3(H, Bt), dim3(256), 0, s,
+                       (const f16*)B_hat, (const f16*)X_hat, (const f16*)C_mix, a, h, (bf16*)y,
                        H, G, N, k);
   else
-    hipLaunchKernelGGL(decode_state_kernel<float>, dim3(H, Bt), dim3(256), 0, s,
+    hipLaunchKernelGGL((decode_state_kernel<float, float>), dim3(H, Bt), dim3(256), 0, s,
                        (const float*)B_hat, (const float*)X_hat, (const float*)C_mix, a, h,
                        (float*)y, H, G, N, k);
   prof_end(s);

@@ -12,9 +12,9 @@
 // Both operands are contiguous along d, so global loads are 16 bytes per lane
 // and the tiles sit in LDS in [row][d] order, which is exactly the fragment
 // order of the matrix cores (8 consecutive d per lane). Accumulation is fp32.
-// Epilogue, by column region:
-//     c <  H*P          -> X_hat[token, slot, c]            (dtype)
-//     c <  H*P + G*N    -> B_hat[token, slot, .] = w * Z     (dtype, w folded)
+// Epilogue, by column region (S = stream type: fp16 for bf16 inputs, else fp32):
+//     c <  H*P          -> X_hat[token, slot, c]            (S)
+//     c <  H*P + G*N    -> B_hat[token, slot, .] = w * Z     (S, w folded)
 //     otherwise         -> c_part[token, slot, .] = w * Z    (fp32)
 // and a last small kernel sums c_part over the slots in slot order
 // (0..k-1, fp32) into C_mix, so C~ never depends on which workgroup ran first.
@@ -36,7 +36,9 @@ __global__ __launch_bounds__(256) void proj_kernel(
     const T* __restrict__ u, const T* __restrict__ wexp, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_offsets,
     const float* __restrict__ topk_w, int D, int W, int HP, int GN, int E, int k,
-    T* __restrict__ X_hat, T* __restrict__ B_hat, float* __restrict__ c_part) {
+    typename StreamOf<T>::type* __restrict__ X_hat, typename StreamOf<T>::type* __restrict__ B_hat,
+    float* __restrict__ c_part) {
+  typedef typename StreamOf<T>::type S;
   constexpr int WAVES_M = BM / 64;          // 2 (BM=128) or 1 (BM=64)
   constexpr int WAVES_N = 4 / WAVES_M;      // 2 or 4
   constexpr int WN = kBN / WAVES_N;         // 64 or 32
@@ -138,9 +140,9 @@ __global__ __launch_bounds__(256) void proj_kernel(
         const int col = col0 + wn * WN + j * 16 + c;
         const float z = acc[i][j][q];
         if (col < HP) {
-          X_hat[pair * HP + col] = from_f32<T>(z);
+          X_hat[pair * HP + col] = from_f32<S>(z);
         } else if (col < HP + GN) {
-          B_hat[pair * GN + (col - HP)] = from_f32<T>(w * z);
+          B_hat[pair * GN + (col - HP)] = from_f32<S>(w * z);
         } else if (col < W) {
           c_part[pair * GN + (col - HP - GN)] = w * z;
         }
@@ -170,7 +172,10 @@ template <typename T>
 static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
                                    const int32_t* sorted, const int32_t* offsets,
                                    const int32_t* tile_offsets, const float* w, int bm,
-                                   T* B_hat, T* X_hat, float* c_part, T* C_mix, hipStream_t s) {
+                                   typename StreamOf<T>::type* B_hat,
+                                   typename StreamOf<T>::type* X_hat, float* c_part,
+                                   typename StreamOf<T>::type* C_mix, hipStream_t s) {
+  typedef typename StreamOf<T>::type S;
   const int pairs = g.M * g.k;
   const dim3 grid(proj_row_tiles_max(pairs, g.E, bm), (g.W + kBN - 1) / kBN);
   prof_begin("expert_project", s);
@@ -183,7 +188,7 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
   prof_end(s);
   const size_t n4 = (size_t)g.M * g.GN() / 4;
   prof_begin("mix_c", s);
-  hipLaunchKernelGGL(mix_c_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, c_part,
+  hipLaunchKernelGGL(mix_c_kernel<S>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, c_part,
                      g.M, g.k, g.GN(), C_mix);
   prof_end(s);
   return hipGetLastError();
@@ -197,8 +202,8 @@ hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const 
   if (g.M == 0) return hipSuccess;
   if (is_bf16)
     return launch_project_t<bf16>(g, (const bf16*)u, (const bf16*)w_experts, sorted, offsets,
-                                  tile_offsets, w, bm, (bf16*)B_hat, (bf16*)X_hat, c_part,
-                                  (bf16*)C_mix, s);
+                                  tile_offsets, w, bm, (f16*)B_hat, (f16*)X_hat, c_part,
+                                  (f16*)C_mix, s);
   return launch_project_t<float>(g, (const float*)u, (const float*)w_experts, sorted, offsets,
                                  tile_offsets, w, bm, (float*)B_hat, (float*)X_hat, c_part,
                                  (float*)C_mix, s);

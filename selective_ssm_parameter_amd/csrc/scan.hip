@@ -66,7 +66,7 @@ struct ScanLds {
   static size_t bytes(int L) { return (size_t)ELEMS * sizeof(T) + (size_t)(L + 1) * sizeof(float); }
 };
 
-template <typename T, int NP, int KS, int BT, bool WITH_Y>
+template <typename T, typename TY, int NP, int KS, int BT, bool WITH_Y>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A, int pass) {
   typedef ScanLds<T, NP, KS, BT, WITH_Y> Lay;
   constexpr int R = Lay::R, LDN = Lay::LDN, LDR = Lay::LDR;
@@ -131,14 +131,32 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A, int pass) {
     const int Lc = min(L, Tlen - c0);
     const int nb = (Lc + BT - 1) / BT;
 
+    // The entering state as a matrix-core operand. In fp16 it is first scaled
+    // by 2^-e (per wave, e >= 0 chosen from the wave's max |H|) so that it stays
+    // below 2^14; the readout is multiplied back by 2^e in fp32.
     F hfrag[NT / 2];
+    float hscale = 1.f;
     if (WITH_Y) {
+      float hin = 1.f;
+      if (sizeof(T) == 2) {
+        float m = 0.f;
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(Hr[ni][i]));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        int e = 0;
+        if (m > 16384.f) e = (int)ceilf(log2f(m * (1.f / 16384.f)));
+        hin = ldexpf(1.f, -e);
+        hscale = ldexpf(1.f, e);
+      }
 #pragma unroll
       for (int q = 0; q < NT / 2; ++q) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          hfrag[q][i] = from_f32<T>(Hr[2 * q][i]);
-          hfrag[q][4 + i] = from_f32<T>(Hr[2 * q + 1][i]);
+          hfrag[q][i] = from_f32<T>(Hr[2 * q][i] * hin);
+          hfrag[q][4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
         }
       }
     }
@@ -215,7 +233,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A, int pass) {
                 F bf = load4x2<T>(crow + 32 * q + 4 * g4, crow + 32 * q + 16 + 4 * g4);
                 acc = mma16(hfrag[q], bf, acc);
               }
-              const float alpha = pw[min(tau * BT + 16 * tt + c + 1, L)];
+              const float alpha = pw[min(tau * BT + 16 * tt + c + 1, L)] * hscale;
               accY[tt] = acc * alpha;
             }
           }
@@ -275,15 +293,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A, int pass) {
       }
       if (WITH_Y) {
         // ---- store y for block tau: lane holds y[t = 16tt + c][p = 16w + 4g + i]
-        T* y = reinterpret_cast<T*>(A.y);
+        typedef typename Vec<TY>::x4 Y4;
+        TY* y = reinterpret_cast<TY*>(A.y);
 #pragma unroll
         for (int tt = 0; tt < BT / 16; ++tt) {
           const int tl = tau * BT + 16 * tt + c;
           if (tl < Lc) {
-            F4 o;
+            Y4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(accY[tt][i]);
-            *reinterpret_cast<F4*>(y + (tok_base + c0 + tl) * (size_t)H * kP + (size_t)h * kP +
+            for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[tt][i]);
+            *reinterpret_cast<Y4*>(y + (tok_base + c0 + tl) * (size_t)H * kP + (size_t)h * kP +
                                    16 * wave + 4 * g4) = o;
           }
         }
@@ -376,10 +395,10 @@ size_t scan_ws_bytes(const ScanGeom& g) {
   return (size_t)g.Bt * g.segs * g.H * g.N * g.P * sizeof(float);
 }
 
-template <typename T, int NP, int KS, int BT>
+template <typename T, typename TY, int NP, int KS, int BT>
 static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStream_t s) {
-  auto k3 = scan_kernel<T, NP, KS, BT, true>;
-  auto k1 = scan_kernel<T, NP, KS, BT, false>;
+  auto k3 = scan_kernel<T, TY, NP, KS, BT, true>;
+  auto k1 = scan_kernel<T, TY, NP, KS, BT, false>;
   const size_t l3 = ScanLds<T, NP, KS, BT, true>::bytes(g.L);
   const size_t l1 = ScanLds<T, NP, KS, BT, false>::bytes(g.L);
   hipError_t err = hipFuncSetAttribute((const void*)k3, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -403,18 +422,19 @@ static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStre
   return hipGetLastError();
 }
 
-template <typename T, int NP>
+template <typename T, typename TY, int NP>
 static hipError_t dispatch_ks(const ScanGeom& g, const ScanArgs& a, hipStream_t s, bool bt32) {
-  if (g.k == 1) return bt32 ? launch_scan_t<T, NP, 1, 32>(g, a, s) : launch_scan_t<T, NP, 1, 64>(g, a, s);
-  return bt32 ? launch_scan_t<T, NP, 2, 32>(g, a, s) : launch_scan_t<T, NP, 2, 64>(g, a, s);
+  if (g.k == 1)
+    return bt32 ? launch_scan_t<T, TY, NP, 1, 32>(g, a, s) : launch_scan_t<T, TY, NP, 1, 64>(g, a, s);
+  return bt32 ? launch_scan_t<T, TY, NP, 2, 32>(g, a, s) : launch_scan_t<T, TY, NP, 2, 64>(g, a, s);
 }
 
-template <typename T>
+template <typename T, typename TY>
 static hipError_t dispatch_np(const ScanGeom& g, const ScanArgs& a, hipStream_t s, bool bt32) {
   const int np = g.N <= 32 ? 32 : (g.N <= 64 ? 64 : 128);
-  if (np == 32) return dispatch_ks<T, 32>(g, a, s, bt32);
-  if (np == 64) return dispatch_ks<T, 64>(g, a, s, bt32);
-  return dispatch_ks<T, 128>(g, a, s, bt32);
+  if (np == 32) return dispatch_ks<T, TY, 32>(g, a, s, bt32);
+  if (np == 64) return dispatch_ks<T, TY, 64>(g, a, s, bt32);
+  return dispatch_ks<T, TY, 128>(g, a, s, bt32);
 }
 
 hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
@@ -427,10 +447,11 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
   }
   ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws,
                 g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks};
-  // bf16 uses 64-token blocks (32 when the chunk is 32); fp32 always 32.
+  // bf16 inputs (fp16 streams) use 64-token blocks (32 when the chunk is 32);
+  // fp32 always 32, to fit LDS.
   const bool bt32 = !is_bf16 || g.L == 32;
-  if (is_bf16) return dispatch_np<bf16>(g, args, s, bt32);
-  return dispatch_np<float>(g, args, s, bt32);
+  if (is_bf16) return dispatch_np<f16, bf16>(g, args, s, bt32);
+  return dispatch_np<float, float>(g, args, s, bt32);
 }
 
 }  // namespace swimba
