@@ -137,6 +137,36 @@ __device__ __forceinline__ typename Vec<TO>::x8 convert8(typename Vec<TI>::x8 v)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Raw buffer resources: loads at a byte offset at or beyond the resource's
+// size return zeros, so bounds handling is a select of the offset, not a
+// branch. kOOB is an offset that is always out of range.
+constexpr uint32_t kOOB = 0x80000000u;
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+__device__ __forceinline__ BufRes make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes >= 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// 8 elements (16 bytes for 2-byte types, 32 for fp32) at byte offset `off`.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x8 load8_buf(BufRes r, uint32_t off) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(typename Vec<T>::x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  } else {
+    int4v lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    int4v hi = __builtin_amdgcn_raw_buffer_load_b128(r, off >= kOOB ? kOOB : off + 16u, 0, 0);
+    floatx4 a = __builtin_bit_cast(floatx4, lo), b = __builtin_bit_cast(floatx4, hi);
+    floatx8 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+    return v;
+  }
+}
+
 // a^n for a in [0, 1) and integer n >= 0, computed as exp2(n * log2(a)).
 // a == 0 gives 1 for n == 0 and 0 otherwise.
 __device__ __forceinline__ float pow_int(float a, int n) {

@@ -46,6 +46,7 @@ struct ScanGeom {
   int seg_chunks;    // chunks per segment
 };
 ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L);
+int scan_block_tokens();
 size_t scan_ws_bytes(const ScanGeom& g);
 hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
                        const void* C_mix, const float* a, const float* h_init, void* y,

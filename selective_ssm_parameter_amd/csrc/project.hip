@@ -12,6 +12,9 @@
 // Both operands are contiguous along d, so global loads are 16 bytes per lane
 // and the tiles sit in LDS in [row][d] order, which is exactly the fragment
 // order of the matrix cores (8 consecutive d per lane). Accumulation is fp32.
+// The K loop double-buffers LDS and keeps the next K tile's global loads in
+// flight (in registers) while the current tile is multiplied, so there is one
+// barrier per K tile and memory latency overlaps the matrix-core work.
 // Epilogue, by column region (S = stream type: fp16 for bf16 inputs, else fp32):
 //     c <  H*P          -> X_hat[token, slot, c]            (S)
 //     c <  H*P + G*N    -> B_hat[token, slot, .] = w * Z     (S, w folded)
@@ -24,29 +27,42 @@
 namespace swimba {
 
 constexpr int kBN = 128;
-constexpr int kBK = 32;
-constexpr int kPadK = kBK + 8;  // LDS row stride in elements
 
 int proj_bm(int pairs, int E) { return (pairs / (E > 0 ? E : 1)) >= 96 ? 128 : 64; }
 
 int proj_row_tiles_max(int pairs, int E, int bm) { return (pairs + bm - 1) / bm + E; }
 
+// K-tile depth: 64 for 2-byte inputs, 32 for fp32 (same bytes per row).
+template <typename T> struct ProjK { static constexpr int BK = sizeof(T) == 2 ? 64 : 32; };
+
+template <typename T, int BM>
+struct ProjLds {
+  static constexpr int BK = ProjK<T>::BK;
+  static constexpr int LDK = BK + 8;  // LDS row stride in elements
+  static constexpr size_t bytes = (size_t)2 * (BM + kBN) * LDK * sizeof(T);
+};
+
 template <typename T, int BM>
 __global__ __launch_bounds__(256) void proj_kernel(
     const T* __restrict__ u, const T* __restrict__ wexp, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_offsets,
-    const float* __restrict__ topk_w, int D, int W, int HP, int GN, int E, int k,
+    const float* __restrict__ topk_w, int M, int D, int W, int HP, int GN, int E, int k,
     typename StreamOf<T>::type* __restrict__ X_hat, typename StreamOf<T>::type* __restrict__ B_hat,
     float* __restrict__ c_part) {
   typedef typename StreamOf<T>::type S;
-  constexpr int WAVES_M = BM / 64;          // 2 (BM=128) or 1 (BM=64)
-  constexpr int WAVES_N = 4 / WAVES_M;      // 2 or 4
-  constexpr int WN = kBN / WAVES_N;         // 64 or 32
-  constexpr int TM = 4, TN = WN / 16;       // 16x16 tiles per wave
+  constexpr int BK = ProjK<T>::BK, LDK = ProjLds<T, BM>::LDK;
+  constexpr int CH = BK / 8;                 // 8-element chunks per row and K tile
+  constexpr int WAVES_M = BM / 64;           // 2 (BM=128) or 1 (BM=64)
+  constexpr int WAVES_N = 4 / WAVES_M;       // 2 or 4
+  constexpr int WN = kBN / WAVES_N;          // 64 or 32
+  constexpr int TM = 4, TN = WN / 16;        // 16x16 tiles per wave
+  constexpr int AU = BM * CH / 256;          // A chunks per thread per K tile
+  constexpr int BU = kBN * CH / 256;         // B chunks per thread per K tile
   typedef typename Vec<T>::x8 F;
 
-  __shared__ T As[BM * kPadK];
-  __shared__ T Bs[kBN * kPadK];
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  T* As = reinterpret_cast<T*>(lds_raw);              // [2][BM][LDK]
+  T* Bs = As + 2 * BM * LDK;                          // [2][kBN][LDK]
   __shared__ int rtok[BM];
   __shared__ int rslot[BM];
   __shared__ float rw[BM];
@@ -92,37 +108,78 @@ __global__ __launch_bounds__(256) void proj_kernel(
   const int g = lane >> 4, c = lane & 15;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
+  // Per-thread byte offsets of the A (gathered tokens) and B (weight) chunks;
+  // out-of-range chunks read zeros through the buffer resources.
+  constexpr uint32_t ES = sizeof(T);
+  const BufRes rA = make_rsrc(u, (uint64_t)M * D * ES);
+  const BufRes rW = make_rsrc(We, (uint64_t)W * D * ES);
+  uint32_t aoff[AU], boff[BU];
+  int ach[AU], bch[BU];
+#pragma unroll
+  for (int i = 0; i < AU; ++i) {
+    const int q = threadIdx.x + 256 * i, r = q / CH;
+    ach[i] = q % CH;
+    const int tok = rtok[r];
+    aoff[i] = tok >= 0 ? ((uint32_t)tok * D + 8 * ach[i]) * ES : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < BU; ++i) {
+    const int q = threadIdx.x + 256 * i, r = q / CH;
+    bch[i] = q % CH;
+    const int col = col0 + r;
+    boff[i] = col < W ? ((uint32_t)col * D + 8 * bch[i]) * ES : kOOB;
+  }
+  F areg[AU], breg[BU];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AU; ++i)
+      areg[i] = load8_buf<T>(rA, (aoff[i] != kOOB && k0 + 8 * ach[i] < D) ? aoff[i] + k0 * ES : kOOB);
+#pragma unroll
+    for (int i = 0; i < BU; ++i)
+      breg[i] = load8_buf<T>(rW, (boff[i] != kOOB && k0 + 8 * bch[i] < D) ? boff[i] + k0 * ES : kOOB);
+  };
+  auto store_tile = [&](int buf) {
+    T* a = As + buf * BM * LDK;
+    T* bb = Bs + buf * kBN * LDK;
+#pragma unroll
+    for (int i = 0; i < AU; ++i) {
+      const int q = threadIdx.x + 256 * i, r = q / CH, ch = q % CH;
+      store8<T>(&a[r * LDK + 8 * ch], areg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < BU; ++i) {
+      const int q = threadIdx.x + 256 * i, r = q / CH, ch = q % CH;
+      store8<T>(&bb[r * LDK + 8 * ch], breg[i]);
+    }
+  };
+
   floatx4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < D; k0 += kBK) {
-    // A tile: BM rows x 32 d, as 4 chunks of 8 per row.
-    for (int q = threadIdx.x; q < BM * 4; q += 256) {
-      const int r = q >> 2, ch = q & 3;
-      const int tok = rtok[r];
-      F v = tok >= 0 ? load8<T>(u + (size_t)tok * D + k0 + 8 * ch) : zero8<T>();
-      store8<T>(&As[r * kPadK + 8 * ch], v);
+  const int nk = (D + BK - 1) / BK;
+  load_tile(0);
+  store_tile(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_tile((kt + 1) * BK);  // next tile in flight during compute
+    __syncthreads();  // tile kt is in LDS; everyone is done with tile kt - 1
+    const T* a = As + (kt & 1) * BM * LDK;
+    const T* bb = Bs + (kt & 1) * kBN * LDK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      F af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = load8<T>(&a[(wm * 64 + i * 16 + c) * LDK + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = load8<T>(&bb[(wn * WN + j * 16 + c) * LDK + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mma16(af[i], bfr[j], acc[i][j]);
     }
-    for (int q = threadIdx.x; q < kBN * 4; q += 256) {
-      const int r = q >> 2, ch = q & 3;
-      const int col = col0 + r;
-      F v = col < W ? load8<T>(We + (size_t)col * D + k0 + 8 * ch) : zero8<T>();
-      store8<T>(&Bs[r * kPadK + 8 * ch], v);
-    }
-    __syncthreads();
-    F af[TM], bfr[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = load8<T>(&As[(wm * 64 + i * 16 + c) * kPadK + 8 * g]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[j] = load8<T>(&Bs[(wn * WN + j * 16 + c) * kPadK + 8 * g]);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mma16(af[i], bfr[j], acc[i][j]);
-    __syncthreads();
+    if (kt + 1 < nk) store_tile((kt + 1) & 1);
   }
 
   // Epilogue: lane holds Z[4g + q][c] of every 16x16 tile.
@@ -178,13 +235,17 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
   typedef typename StreamOf<T>::type S;
   const int pairs = g.M * g.k;
   const dim3 grid(proj_row_tiles_max(pairs, g.E, bm), (g.W + kBN - 1) / kBN);
+  const size_t lds = bm == 128 ? ProjLds<T, 128>::bytes : ProjLds<T, 64>::bytes;
+  const void* kfn = bm == 128 ? (const void*)proj_kernel<T, 128> : (const void*)proj_kernel<T, 64>;
+  hipError_t err = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
   prof_begin("expert_project", s);
   if (bm == 128)
-    hipLaunchKernelGGL((proj_kernel<T, 128>), grid, dim3(256), 0, s, u, wexp, sorted, offsets,
-                       tile_offsets, w, g.D, g.W, g.HP(), g.GN(), g.E, g.k, X_hat, B_hat, c_part);
+    hipLaunchKernelGGL((proj_kernel<T, 128>), grid, dim3(256), lds, s, u, wexp, sorted, offsets,
+                       tile_offsets, w, g.M, g.D, g.W, g.HP(), g.GN(), g.E, g.k, X_hat, B_hat, c_part);
   else
-    hipLaunchKernelGGL((proj_kernel<T, 64>), grid, dim3(256), 0, s, u, wexp, sorted, offsets,
-                       tile_offsets, w, g.D, g.W, g.HP(), g.GN(), g.E, g.k, X_hat, B_hat, c_part);
+    hipLaunchKernelGGL((proj_kernel<T, 64>), grid, dim3(256), lds, s, u, wexp, sorted, offsets,
+                       tile_offsets, w, g.M, g.D, g.W, g.HP(), g.GN(), g.E, g.k, X_hat, B_hat, c_part);
   prof_end(s);
   const size_t n4 = (size_t)g.M * g.GN() / 4;
   prof_begin("mix_c", s);

@@ -33,6 +33,8 @@
 //   Gm[t, r]     = Gram^T[r, t] a^{t-s}, zero above the diagonal (LDS table)
 //   y^T         += X^T Gm^T                 (K = pairs)
 //   carry       += B_hat^T (decay * X)      (K = pairs, diagonal block only)
+#include <cstdlib>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -63,14 +65,49 @@ struct ScanLds {
   static constexpr int XST = kP * LDR;
   static constexpr int GM = WITH_Y ? BT * LDR : 0;
   static constexpr int ELEMS = CS + BS + BST + XST + GM;
-  static size_t bytes(int L) { return (size_t)ELEMS * sizeof(T) + (size_t)(L + 1) * sizeof(float); }
+  static constexpr size_t bytes = (size_t)ELEMS * sizeof(T);
+};
+
+// Transposed [row][r] buffers store 8-element column chunks XOR-swizzled by the
+// row's 8-row group, so the 4-element column writes of the staging (rows 8
+// apart) land in different banks; readers apply the same swizzle.
+template <int R>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ ((row >> 3) & (R / 8 - 1) & 7);
+}
+
+// a^d for integer d >= 0 from la = log2(a) (la = -1e30 encodes a = 0).
+__device__ __forceinline__ float apow(float la, int d) {
+  return d == 0 ? 1.f : exp2f((float)d * la);
+}
+
+// One step of the walk over a segment: chunk ch, output block tau, source
+// block sig (sig <= tau). Pass 1 (no output) visits (ch, sig) with tau = sig.
+struct ScanStep {
+  int ch, tau, sig;
+};
+
+template <typename T, int NP, int KS, int BT, bool WITH_Y>
+struct ScanStage {
+  static constexpr int R = KS * BT;
+  static constexpr int CUN = (BT * (NP / 8) + 255) / 256;        // C~ chunks per thread
+  static constexpr int BUN = ((R / 4) * (NP / 8) + 255) / 256;   // B_hat 4x8 units per thread
+  static constexpr int XUN = ((R / 4) * (kP / 8) + 255) / 256;   // X 4x8 units per thread
+  typedef typename Vec<T>::x8 F;
+  F cv[WITH_Y ? CUN : 1];
+  F bv[BUN][4];
+  F xv[XUN][4];
 };
 
 template <typename T, typename TY, int NP, int KS, int BT, bool WITH_Y>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs A, int pass) {
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
   typedef ScanLds<T, NP, KS, BT, WITH_Y> Lay;
+  typedef ScanStage<T, NP, KS, BT, WITH_Y> Stage;
   constexpr int R = Lay::R, LDN = Lay::LDN, LDR = Lay::LDR;
-  constexpr int NT = NP / 16;  // 16-row tiles of the state
+  constexpr int NT = NP / 16;               // 16-row tiles of the state
+  constexpr int RT = R / 16, TT = BT / 16;  // Gram tiles
+  constexpr int MT = (RT * TT + 3) / 4;     // Gram tiles per wave
+  constexpr int RQ = R / 32;                // 32-pair contraction steps per block
   typedef typename Vec<T>::x8 F;
   typedef typename Vec<T>::x4 F4;
 
@@ -80,241 +117,333 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A, int pass) {
   T* BsT = Bs + Lay::BS;
   T* XsT = BsT + Lay::BST;
   T* Gm = XsT + Lay::XST;
-  float* pw = reinterpret_cast<float*>(Gm + Lay::GM);
 
   const int h = blockIdx.x, seg = blockIdx.y, b = blockIdx.z;
   const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
   const int grp = h / (H / G);
   const int GN = G * N;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = tid >> 6;
   const int g4 = lane >> 4, c = lane & 15;
   const int pcol = 16 * wave + c;  // this lane's state column
-
-  const T* Bh = reinterpret_cast<const T*>(A.B_hat);
-  const T* Xh = reinterpret_cast<const T*>(A.X_hat);
-  const T* Cm = reinterpret_cast<const T*>(A.C_mix);
-  const size_t tok_base = (size_t)b * Tlen;
   const size_t NPsz = (size_t)N * kP;
+  const size_t HPsz = (size_t)H * kP;
 
   const float ah = A.a[h];
-  for (int j = threadIdx.x; j <= L; j += 256) pw[j] = pow_int(ah, j);
+  const float la = ah > 0.f ? log2f(ah) : -1e30f;
 
-  // Entering state of this segment.
-  floatx4 Hr[NT], Sn[NT];
-  {
-    const float* src = nullptr;
-    if (!WITH_Y) {
-      src = nullptr;  // pass 1 starts from zero
-    } else if (A.segs == 1) {
-      src = A.h_init;
-      if (src) src += ((size_t)b * H + h) * NPsz;
-    } else {
-      src = A.ws + (((size_t)b * A.segs + seg) * H + h) * NPsz;
+  // ---- buffer resources over this sequence's streams (out of range -> 0)
+  constexpr uint32_t ES = sizeof(T);
+  const BufRes rB = make_rsrc(reinterpret_cast<const T*>(A.B_hat) + (size_t)b * Tlen * KS * GN,
+                              (uint64_t)Tlen * KS * GN * ES);
+  const BufRes rX = make_rsrc(reinterpret_cast<const T*>(A.X_hat) + (size_t)b * Tlen * KS * HPsz,
+                              (uint64_t)Tlen * KS * HPsz * ES);
+  const BufRes rC = make_rsrc(reinterpret_cast<const T*>(A.C_mix) + (size_t)b * Tlen * GN,
+                              (uint64_t)Tlen * GN * ES);
+
+  // ---- per-lane decay tables for full chunks (Lc == L)
+  // carry: a^{BT-1-s} for the pair rows r = 32q + 8g + e this lane contracts
+  float cd[RQ][8];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cd[q][e] = apow(la, BT - 1 - (32 * q + 8 * g4 + e) / KS);
+  // Gram mask of a diagonal block: a^{t-s} for t >= s, else 0
+  float gmk[MT][4];
+  float al[BT / 16];  // readout decay a^{t+1} for the lane's t in block 0
+  if (WITH_Y) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int tix = wave + 4 * m;
+      const int rt = tix / TT, tt = tix % TT;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = (16 * tt + c) - (16 * rt + 4 * g4 + i) / KS;
+        gmk[m][i] = (tix < RT * TT && d >= 0) ? apow(la, d) : 0.f;
+      }
     }
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) {
+    for (int tt = 0; tt < BT / 16; ++tt) al[tt] = apow(la, 16 * tt + c + 1);
+  }
+
+  // ---- entering state of this segment
+  floatx4 Hr[NT];
+  {
+    const float* src = nullptr;
+    if (WITH_Y) {
+      if (A.segs == 1) {
+        src = A.h_init;
+        if (src) src += ((size_t)b * H + h) * NPsz;
+      } else {
+        src = A.ws + (((size_t)b * A.segs + seg) * H + h) * NPsz;
+      }
+    }
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = 16 * ni + 4 * g4 + i;
         Hr[ni][i] = (src && n < N) ? src[(size_t)n * kP + pcol] : 0.f;
       }
-      Sn[ni] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
   }
 
   const int nc = (Tlen + L - 1) / L;
   const int ch0 = seg * A.seg_chunks;
   const int ch1 = min(nc, ch0 + A.seg_chunks);
-
-  for (int ch = ch0; ch < ch1; ++ch) {
-    const int c0 = ch * L;
-    const int Lc = min(L, Tlen - c0);
-    const int nb = (Lc + BT - 1) / BT;
-
-    // The entering state as a matrix-core operand. In fp16 it is first scaled
-    // by 2^-e (per wave, e >= 0 chosen from the wave's max |H|) so that it stays
-    // below 2^14; the readout is multiplied back by 2^e in fp32.
-    F hfrag[NT / 2];
-    float hscale = 1.f;
+  if (ch0 >= ch1) return;
+  auto nblocks = [&](int ch) { return (min(L, Tlen - ch * L) + BT - 1) / BT; };
+  auto advance = [&](ScanStep s) {
     if (WITH_Y) {
-      float hin = 1.f;
-      if (sizeof(T) == 2) {
-        float m = 0.f;
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(Hr[ni][i]));
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        int e = 0;
-        if (m > 16384.f) e = (int)ceilf(log2f(m * (1.f / 16384.f)));
-        hin = ldexpf(1.f, -e);
-        hscale = ldexpf(1.f, e);
+      if (++s.sig > s.tau) {
+        s.sig = 0;
+        if (++s.tau == nblocks(s.ch)) { s.tau = 0; ++s.ch; }
       }
+    } else {
+      if (++s.sig == nblocks(s.ch)) { s.sig = 0; ++s.ch; }
+      s.tau = s.sig;
+    }
+    return s;
+  };
+
+  // ---- global -> registers for one step (issued one step ahead). Full
+  // blocks take the unguarded path; only a sequence's last block is partial.
+  auto load = [&](Stage& st, ScanStep s) {
+    const int c0 = s.ch * L;
+    const int Lc = min(L, Tlen - c0);
+    const uint32_t prow = (uint32_t)(c0 + s.sig * BT) * KS;  // first pair row of block sig
+    const int rlim = (Lc - s.sig * BT) * KS;                  // valid pair rows in the block
+    if (WITH_Y && s.sig == 0) {
+      const int tlim = Lc - s.tau * BT;
+      const uint32_t trow = (uint32_t)(c0 + s.tau * BT);
 #pragma unroll
-      for (int q = 0; q < NT / 2; ++q) {
+      for (int u = 0; u < Stage::CUN; ++u) {
+        const int q = tid + 256 * u;
+        const int t = q / (NP / 8), n0 = 8 * (q % (NP / 8));
+        const bool ok = q < BT * (NP / 8) && n0 < N && t < tlim;
+        const uint32_t off = ((trow + t) * GN + grp * N + n0) * ES;
+        st.cv[u] = load8_buf<T>(rC, ok ? off : kOOB);
+      }
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hfrag[q][i] = from_f32<T>(Hr[2 * q][i] * hin);
-          hfrag[q][4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
+    for (int u = 0; u < Stage::BUN; ++u) {
+      const int q = tid + 256 * u;
+      const int r0 = 4 * (q / (NP / 8)), n0 = 8 * (q % (NP / 8));
+      const bool uok = q < (R / 4) * (NP / 8) && n0 < N;
+      const uint32_t off = ((prow + r0) * GN + grp * N + n0) * ES;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st.bv[u][i] = load8_buf<T>(rB, (uok && r0 + i < rlim) ? off + i * GN * ES : kOOB);
+    }
+#pragma unroll
+    for (int u = 0; u < Stage::XUN; ++u) {
+      const int q = tid + 256 * u;
+      const int r0 = 4 * (q / (kP / 8)), p0 = 8 * (q % (kP / 8));
+      const bool uok = q < (R / 4) * (kP / 8);
+      const uint32_t off = ((prow + r0) * (uint32_t)HPsz + h * kP + p0) * ES;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st.xv[u][i] = load8_buf<T>(rX, (uok && r0 + i < rlim) ? off + i * (uint32_t)HPsz * ES : kOOB);
+    }
+  };
+
+  // ---- registers -> LDS
+  auto store = [&](const Stage& st, ScanStep s) {
+    const bool diag = s.sig == s.tau;
+    if (WITH_Y && s.sig == 0) {
+#pragma unroll
+      for (int u = 0; u < Stage::CUN; ++u) {
+        const int q = tid + 256 * u;
+        if (q < BT * (NP / 8)) {
+          const int t = q / (NP / 8), n0 = 8 * (q % (NP / 8));
+          store8<T>(&Cs[t * LDN + n0], st.cv[u]);
         }
       }
     }
-
-    for (int tau = WITH_Y ? 0 : nb - 1; tau < nb; ++tau) {
-      floatx4 accY[BT / 16];
-      const int sig0 = WITH_Y ? 0 : 0;
-      const int sig1 = WITH_Y ? tau : nb - 1;
-      for (int sig = sig0; sig <= sig1; ++sig) {
-        const bool diag = WITH_Y ? (sig == tau) : true;
-        __syncthreads();  // previous users of the LDS buffers are done
-        // ---- stage C~ of block tau (first sigma only)
-        if (WITH_Y && sig == 0) {
-          for (int q = threadIdx.x; q < BT * (NP / 8); q += 256) {
-            const int t = q / (NP / 8), n0 = 8 * (q % (NP / 8));
-            const int tl = tau * BT + t;
-            F v = zero8<T>();
-            if (tl < Lc && n0 < N) v = load8<T>(Cm + (tok_base + c0 + tl) * GN + grp * N + n0);
-            store8<T>(&Cs[t * LDN + n0], v);
-          }
-        }
-        // ---- stage B_hat (rows and/or transposed) and X^T of block sigma
-        for (int q = threadIdx.x; q < (R / 4) * (NP / 8); q += 256) {
-          const int r0 = 4 * (q / (NP / 8)), n0 = 8 * (q % (NP / 8));
-          F v[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = r0 + i, s = r / KS, j = r - s * KS;
-            const int sl = sig * BT + s;
-            v[i] = zero8<T>();
-            if (sl < Lc && n0 < N)
-              v[i] = load8<T>(Bh + ((tok_base + c0 + sl) * KS + j) * GN + grp * N + n0);
-          }
-          if (WITH_Y) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) store8<T>(&Bs[(r0 + i) * LDN + n0], v[i]);
-          }
-          if (diag) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              F4 col = {v[0][e], v[1][e], v[2][e], v[3][e]};
-              *reinterpret_cast<F4*>(&BsT[(n0 + e) * LDR + r0]) = col;
-            }
-          }
-        }
-        for (int q = threadIdx.x; q < (R / 4) * (kP / 8); q += 256) {
-          const int r0 = 4 * (q / (kP / 8)), p0 = 8 * (q % (kP / 8));
-          F v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = r0 + i, s = r / KS, j = r - s * KS;
-            const int sl = sig * BT + s;
-            v[i] = zero8<T>();
-            if (sl < Lc) v[i] = load8<T>(Xh + ((tok_base + c0 + sl) * KS + j) * (size_t)H * kP +
-                                         (size_t)h * kP + p0);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            F4 col = {v[0][e], v[1][e], v[2][e], v[3][e]};
-            *reinterpret_cast<F4*>(&XsT[(p0 + e) * LDR + r0]) = col;
-          }
-        }
-        __syncthreads();
-
+    for (int u = 0; u < Stage::BUN; ++u) {
+      const int q = tid + 256 * u;
+      if (q < (R / 4) * (NP / 8)) {
+        const int r0 = 4 * (q / (NP / 8)), n0 = 8 * (q % (NP / 8));
         if (WITH_Y) {
-          // ---- readout of the entering state, once per tau
-          if (sig == 0) {
 #pragma unroll
-            for (int tt = 0; tt < BT / 16; ++tt) {
-              floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-              const T* crow = &Cs[(16 * tt + c) * LDN];
-#pragma unroll
-              for (int q = 0; q < NT / 2; ++q) {
-                F bf = load4x2<T>(crow + 32 * q + 4 * g4, crow + 32 * q + 16 + 4 * g4);
-                acc = mma16(hfrag[q], bf, acc);
-              }
-              const float alpha = pw[min(tau * BT + 16 * tt + c + 1, L)] * hscale;
-              accY[tt] = acc * alpha;
-            }
-          }
-          // ---- masked Gram^T tiles -> Gm[t][r]
-          constexpr int RT = R / 16, TT = BT / 16;
-          for (int tix = wave; tix < RT * TT; tix += 4) {
-            const int rt = tix / TT, tt = tix % TT;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < NP / 32; ++q) {
-              F af = load8<T>(&Bs[(16 * rt + c) * LDN + 32 * q + 8 * g4]);
-              F bf = load8<T>(&Cs[(16 * tt + c) * LDN + 32 * q + 8 * g4]);
-              acc = mma16(af, bf, acc);
-            }
-            const int t = 16 * tt + c;
-            const int tpos = tau * BT + t;
-            F4 out;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 16 * rt + 4 * g4 + i;
-              const int spos = sig * BT + r / KS;
-              const int d = tpos - spos;
-              out[i] = from_f32<T>(d >= 0 ? acc[i] * pw[d] : 0.f);
-            }
-            *reinterpret_cast<F4*>(&Gm[t * LDR + 16 * rt + 4 * g4]) = out;
-          }
-          __syncthreads();
-          // ---- y^T[p, t] += X^T[p, r] Gm[t, r]
-#pragma unroll
-          for (int tt = 0; tt < BT / 16; ++tt) {
-#pragma unroll
-            for (int q = 0; q < R / 32; ++q) {
-              F af = load8<T>(&XsT[pcol * LDR + 32 * q + 8 * g4]);
-              F bf = load8<T>(&Gm[(16 * tt + c) * LDR + 32 * q + 8 * g4]);
-              accY[tt] = mma16(af, bf, accY[tt]);
-            }
-          }
+          for (int i = 0; i < 4; ++i) store8<T>(&Bs[(r0 + i) * LDN + n0], st.bv[u][i]);
         }
-        // ---- carry: Sn[n, p] += sum_r B_hat[r, n] a^{Lc-1-s} X[r, p]
         if (diag) {
 #pragma unroll
-          for (int q = 0; q < R / 32; ++q) {
-            F xf = load8<T>(&XsT[pcol * LDR + 32 * q + 8 * g4]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 32 * q + 8 * g4 + e;
-              const int d = Lc - 1 - (sig * BT + r / KS);
-              xf[e] = from_f32<T>(d >= 0 ? to_f32(xf[e]) * pw[d] : 0.f);
-            }
-#pragma unroll
-            for (int ni = 0; ni < NT; ++ni) {
-              F af = load8<T>(&BsT[(16 * ni + c) * LDR + 32 * q + 8 * g4]);
-              Sn[ni] = mma16(af, xf, Sn[ni]);
-            }
+          for (int e = 0; e < 8; ++e) {
+            const int row = n0 + e;
+            F4 col = {st.bv[u][0][e], st.bv[u][1][e], st.bv[u][2][e], st.bv[u][3][e]};
+            *reinterpret_cast<F4*>(&BsT[row * LDR + 8 * swz<R>(row, r0 >> 3) + (r0 & 7)]) = col;
           }
         }
       }
+    }
+#pragma unroll
+    for (int u = 0; u < Stage::XUN; ++u) {
+      const int q = tid + 256 * u;
+      if (q < (R / 4) * (kP / 8)) {
+        const int r0 = 4 * (q / (kP / 8)), p0 = 8 * (q % (kP / 8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int row = p0 + e;
+          F4 col = {st.xv[u][0][e], st.xv[u][1][e], st.xv[u][2][e], st.xv[u][3][e]};
+          *reinterpret_cast<F4*>(&XsT[row * LDR + 8 * swz<R>(row, r0 >> 3) + (r0 & 7)]) = col;
+        }
+      }
+    }
+  };
+
+  ScanStep cur{ch0, 0, 0};
+  Stage st;
+  load(st, cur);
+
+  F hfrag[NT / 2];
+  float hscale = 1.f;
+  floatx4 accY[BT / 16];
+
+  while (cur.ch < ch1) {
+    const int c0 = cur.ch * L;
+    const int Lc = min(L, Tlen - c0);
+    const int nb = (Lc + BT - 1) / BT;
+    const bool full_chunk = Lc == L;
+    const bool diag = cur.sig == cur.tau;
+
+    __syncthreads();  // every reader of the previous step's LDS data is done
+    store(st, cur);
+    const ScanStep nxt = advance(cur);
+    if (nxt.ch < ch1) load(st, nxt);  // in flight during this step's compute
+    __syncthreads();
+
+    if (cur.tau == 0 && cur.sig == 0) {
       if (WITH_Y) {
-        // ---- store y for block tau: lane holds y[t = 16tt + c][p = 16w + 4g + i]
-        typedef typename Vec<TY>::x4 Y4;
-        TY* y = reinterpret_cast<TY*>(A.y);
+        // The entering state as a matrix-core operand. In fp16 it is first
+        // scaled by 2^-e (per wave, e >= 0 chosen from the wave's max |H|) so
+        // it stays below 2^14; the readout is multiplied back by 2^e in fp32.
+        float hin = 1.f;
+        hscale = 1.f;
+        if (sizeof(T) == 2) {
+          float mx = 0.f;
+#pragma unroll
+          for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[ni][i]));
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+          if (mx > 16384.f) {
+            const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
+            hin = ldexpf(1.f, -e);
+            hscale = ldexpf(1.f, e);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < NT / 2; ++q) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hfrag[q][i] = from_f32<T>(Hr[2 * q][i] * hin);
+            hfrag[q][4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
+          }
+        }
+      }
+      // The carry accumulates straight into the state: H <- a^{Lc} H first.
+      const float aL = apow(la, Lc);
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) Hr[ni] = Hr[ni] * aL;
+    }
+
+    if (WITH_Y) {
+      if (cur.sig == 0) {
+        // ---- readout of the entering state for block tau
+        const float ablk = (cur.tau == 0 ? 1.f : apow(la, cur.tau * BT)) * hscale;
 #pragma unroll
         for (int tt = 0; tt < BT / 16; ++tt) {
-          const int tl = tau * BT + 16 * tt + c;
-          if (tl < Lc) {
-            Y4 o;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          const T* crow = &Cs[(16 * tt + c) * LDN];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[tt][i]);
-            *reinterpret_cast<Y4*>(y + (tok_base + c0 + tl) * (size_t)H * kP + (size_t)h * kP +
-                                   16 * wave + 4 * g4) = o;
+          for (int q = 0; q < NT / 2; ++q) {
+            F bf = load4x2<T>(crow + 32 * q + 4 * g4, crow + 32 * q + 16 + 4 * g4);
+            acc = mma16(hfrag[q], bf, acc);
           }
+          accY[tt] = acc * (al[tt] * ablk);
+        }
+      }
+      // ---- masked Gram^T tiles -> Gm[t][r]
+      const int dblk = (cur.tau - cur.sig) * BT;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int tix = wave + 4 * m;
+        if (tix < RT * TT) {
+          const int rt = tix / TT, tt = tix % TT;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          const T* brow = &Bs[(16 * rt + c) * LDN + 8 * g4];
+          const T* crow = &Cs[(16 * tt + c) * LDN + 8 * g4];
+#pragma unroll
+          for (int q = 0; q < NP / 32; ++q) acc = mma16(load8<T>(brow + 32 * q), load8<T>(crow + 32 * q), acc);
+          F4 out;
+          if (dblk == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = from_f32<T>(acc[i] * gmk[m][i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              out[i] = from_f32<T>(acc[i] * apow(la, dblk + (16 * tt + c) - (16 * rt + 4 * g4 + i) / KS));
+          }
+          *reinterpret_cast<F4*>(&Gm[(16 * tt + c) * LDR + 16 * rt + 4 * g4]) = out;
+        }
+      }
+      __syncthreads();
+      // ---- y^T[p, t] += X^T[p, r] Gm[t, r]
+      F xa[RQ];
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) xa[q] = load8<T>(&XsT[pcol * LDR + 8 * swz<R>(pcol, 4 * q + g4)]);
+#pragma unroll
+      for (int tt = 0; tt < BT / 16; ++tt) {
+        const T* grow = &Gm[(16 * tt + c) * LDR + 8 * g4];
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) accY[tt] = mma16(xa[q], load8<T>(grow + 32 * q), accY[tt]);
+      }
+    }
+    // ---- carry: H[n, p] += sum_r B_hat[r, n] a^{Lc-1-s} X[r, p]
+    if (diag) {
+      // decay of block sig relative to the chunk end
+      const bool tab = full_chunk;
+      const float blk = tab ? apow(la, (nb - 1 - cur.sig) * BT) : 0.f;
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        F xf = load8<T>(&XsT[pcol * LDR + 8 * swz<R>(pcol, 4 * q + g4)]);
+        if (tab) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xf[e] = from_f32<T>(to_f32(xf[e]) * (cd[q][e] * blk));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = Lc - 1 - (cur.sig * BT + (32 * q + 8 * g4 + e) / KS);
+            xf[e] = from_f32<T>(d >= 0 ? to_f32(xf[e]) * apow(la, d) : 0.f);
+          }
+        }
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) {
+          const int row = 16 * ni + c;
+          Hr[ni] = mma16(load8<T>(&BsT[row * LDR + 8 * swz<R>(row, 4 * q + g4)]), xf, Hr[ni]);
         }
       }
     }
-    // ---- chunk end: H <- a^{Lc} H + carry
-    const float aL = pw[Lc];
+    if (WITH_Y && diag) {
+      // ---- store y for block tau: lane holds y[t = 16tt + c][p = 16w + 4g + i]
+      typedef typename Vec<TY>::x4 Y4;
+      TY* yb = reinterpret_cast<TY*>(A.y) + ((size_t)b * Tlen + c0) * HPsz + (size_t)h * kP +
+               16 * wave + 4 * g4;
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) {
-      Hr[ni] = Hr[ni] * aL + Sn[ni];
-      Sn[ni] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < BT / 16; ++tt) {
+        const int tl = cur.tau * BT + 16 * tt + c;
+        if (tl < Lc) {
+          Y4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[tt][i]);
+          *reinterpret_cast<Y4*>(yb + (size_t)tl * HPsz) = o;
+        }
+      }
     }
+    cur = nxt;
   }
 
   // ---- write the end state
@@ -333,7 +462,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A, int pass) {
         if (n < N) dst[(size_t)n * kP + pcol] = Hr[ni][i];
       }
   }
-  (void)pass;
 }
 
 // Pass 2: Hin_0 = h_init (or 0), Hin_{s+1} = a^{len_s} Hin_s + S_s, for every
@@ -377,12 +505,28 @@ hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t
   return hipGetLastError();
 }
 
+// Tuning knobs (environment, read once): SWIMBA_SCAN_BT = 32 or 64 tokens per
+// block for fp16 streams (default 64); SWIMBA_SCAN_WGS = target number of
+// workgroups of the output pass (default 1024), which sets the segment count.
+static int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : dflt;
+}
+int scan_block_tokens() {
+  static const int bt = env_int("SWIMBA_SCAN_BT", 64);
+  return bt;
+}
+static int scan_target_wgs() {
+  static const int w = env_int("SWIMBA_SCAN_WGS", 1024);
+  return w > 0 ? w : 1024;
+}
+
 ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L) {
   ScanGeom g{Bt, T, H, G, N, P, k, L, 1, 1};
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
   const int units = Bt * H;
-  int want = (1024 + units - 1) / units;
+  int want = (scan_target_wgs() + units - 1) / units;
   if (want > nc) want = nc;
   if (want < 1) want = 1;
   g.seg_chunks = (nc + want - 1) / want;
@@ -399,8 +543,8 @@ template <typename T, typename TY, int NP, int KS, int BT>
 static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStream_t s) {
   auto k3 = scan_kernel<T, TY, NP, KS, BT, true>;
   auto k1 = scan_kernel<T, TY, NP, KS, BT, false>;
-  const size_t l3 = ScanLds<T, NP, KS, BT, true>::bytes(g.L);
-  const size_t l1 = ScanLds<T, NP, KS, BT, false>::bytes(g.L);
+  const size_t l3 = ScanLds<T, NP, KS, BT, true>::bytes;
+  const size_t l1 = ScanLds<T, NP, KS, BT, false>::bytes;
   hipError_t err = hipFuncSetAttribute((const void*)k3, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)l3);
   if (err != hipSuccess) return err;
@@ -408,7 +552,7 @@ static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStre
   if (err != hipSuccess) return err;
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
-    hipLaunchKernelGGL(k1, dim3(g.H, g.segs - 1, g.Bt), dim3(256), l1, s, args, 1);
+    hipLaunchKernelGGL(k1, dim3(g.H, g.segs - 1, g.Bt), dim3(256), l1, s, args);
     prof_end(s);
     const int NPsz = g.N * g.P;
     prof_begin("scan_state_pass", s);
@@ -417,7 +561,7 @@ static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStre
     prof_end(s);
   }
   prof_begin("scan_chunk_output", s);
-  hipLaunchKernelGGL(k3, dim3(g.H, g.segs, g.Bt), dim3(256), l3, s, args, 3);
+  hipLaunchKernelGGL(k3, dim3(g.H, g.segs, g.Bt), dim3(256), l3, s, args);
   prof_end(s);
   return hipGetLastError();
 }
@@ -449,7 +593,7 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
                 g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks};
   // bf16 inputs (fp16 streams) use 64-token blocks (32 when the chunk is 32);
   // fp32 always 32, to fit LDS.
-  const bool bt32 = !is_bf16 || g.L == 32;
+  const bool bt32 = !is_bf16 || g.L == 32 || scan_block_tokens() == 32;
   if (is_bf16) return dispatch_np<f16, bf16>(g, args, s, bt32);
   return dispatch_np<float, float>(g, args, s, bt32);
 }
