@@ -1,0 +1,105 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times (``binding.forward`` over the whole batch, ``swimba_decode_step`` over
+all sequences).
+
+The oracle cannot run every head of every sequence at these sizes in seconds,
+so it checks, bit-exactly, the top-k indices of every token, and, to the bf16
+tolerance, y and the final state of sampled (sequence, head) pairs, computed
+one head at a time over the whole sequence. The long-sequence workload (65536
+tokens) checks the first 16384 tokens of y (causality makes that prefix
+independent of what follows) and the final state at a smaller model width.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (TOL, check_routing, host, oracle_forward, run_forward, say, slice_err, tdt,
+                      upload, valid_prefix, dev)
+from oracle import swimba as osw
+from selective_ssm_parameter_amd import binding as sb
+from selective_ssm_parameter_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def sampled_parity(wl, inp, buf, samples, prefix=None):
+    M = wl.tokens
+    r = osw.route(inp["u"].reshape(M, -1), inp["w_router"], wl.top_k)
+    flips = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), r, wl)
+    lim = valid_prefix(flips, wl.batch, wl.seqlen)
+    y = buf.y.view(wl.batch, wl.seqlen, wl.nheads, 64)
+    worst_y = worst_h = 0.0
+    for b, heads in samples:
+        T = wl.seqlen if prefix is None else prefix
+        T = min(T, int(lim[b]))
+        sub = dict(inp, u=inp["u"][b:b + 1, :T],
+                   h_init=None if inp["h_init"] is None else inp["h_init"][b:b + 1])
+        ref = oracle_forward(wl.replace(batch=1, seqlen=T), sub, heads=heads)
+        got = host(y[b:b + 1, :T][:, :, heads])
+        e = slice_err(got, ref["y"])
+        worst_y = max(worst_y, e)
+        if T == wl.seqlen:
+            eh = slice_err(host(buf.h_final[b:b + 1, heads]), ref["h_final"], (0, 1))
+            worst_h = max(worst_h, eh)
+        say(f"  b={b} heads={heads} T={T}: y err {e:.3e}")
+    return worst_y, worst_h
+
+
+@pytest.mark.parametrize("name,samples,prefix", [
+    ("c2", [(0, [0, 13]), (7, [23])], None),
+    ("c3", [(0, [0]), (3, [63])], None),
+    ("c4", [(0, [0, 31])], 16384),
+])
+def test_prefill_full_size(name, samples, prefix):
+    wl = synth.WORKLOADS[name]
+    say(f"[fullsize] {name}: M={wl.tokens} D={wl.d_model} H={wl.nheads} E={wl.n_experts}")
+    inp = synth.make_inputs(wl)
+    buf = run_forward(wl, upload(wl, inp))
+    wy, wh = sampled_parity(wl, inp, buf, samples, prefix)
+    say(f"  worst y {wy:.3e}  worst h_final {wh:.3e}")
+    assert wy < TOL[wl.dtype]
+    assert wh < TOL[wl.dtype]
+
+
+def test_long_sequence_final_state():
+    # 65536 tokens with the slow decay of the long-sequence workload, at a
+    # width the oracle runs in seconds: exercises the cross-segment state pass.
+    wl = synth.WORKLOADS["c4"].replace(name="c4_narrow", seed=44, d_model=128, nheads=2,
+                                       n_experts=4)
+    say(f"[fullsize] long sequence T={wl.seqlen} a in [{wl.a_lo}, {wl.a_hi}]")
+    inp = synth.make_inputs(wl)
+    buf = run_forward(wl, upload(wl, inp))
+    wy, wh = sampled_parity(wl, inp, buf, [(0, [0, 1])])
+    say(f"  worst y {wy:.3e}  worst h_final {wh:.3e}")
+    assert wy < TOL[wl.dtype] and wh < TOL[wl.dtype]
+
+
+def test_decode_full_size():
+    wl = synth.WORKLOADS["c5"]
+    steps, rows = 4, [0, 101, 255]
+    say(f"[fullsize] c5 decode: batch {wl.batch}, {steps} steps, rows {rows}")
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    dims = sb.dims_of(wl)
+    dt = tdt(wl)
+    h = d["h_init"].clone()
+    y = torch.empty(wl.batch, wl.nheads, 64, dtype=dt, device="cuda")
+    idx = torch.empty(wl.batch, wl.top_k, dtype=torch.int32, device="cuda")
+    ws, _ = sb.workspace(dims, sb.CALL_DECODE)
+    h_ref = inp["h_init"][rows].astype(np.float64)
+    for step in range(steps):
+        ut = synth.decode_token(wl, step)
+        sb.swimba_decode_step(dims, dev(ut, dt), d["w_router"], d["w_experts"], d["a"], h, y, idx, ws)
+        torch.cuda.synchronize()
+        r = osw.route(ut, inp["w_router"], wl.top_k)
+        check_routing(host(idx).astype(np.int64), None, r, wl)
+        ref = osw.decode_step(ut[rows], inp["w_router"], inp["w_experts"], inp["a"], h_ref,
+                              nheads=wl.nheads, headdim=64, ngroups=1, dstate=wl.dstate,
+                              top_k=wl.top_k)
+        ey = slice_err(host(y)[rows][:, None], ref["y"][:, None])
+        eh = slice_err(host(h)[rows], ref["h"], (0, 1))
+        say(f"  step {step}: y err {ey:.3e} h err {eh:.3e}")
+        assert ey < TOL[wl.dtype] and eh < TOL[wl.dtype]
+        h_ref = ref["h"]
