@@ -7,8 +7,9 @@ the prefill's final state. Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line. ``value`` is tokens per second (prefill tokens plus the
 decoded tokens) over the timed steps. ``roofline`` describes the kernel with
-the largest share of the step, timed with HIP events recorded by the library
-around each of its launches, over the same steps re-run with the events on.
+the largest share of the step (found in an untimed pass with events around
+every kernel); inside the timed region the library records a HIP event pair
+around each launch of that kernel only, on the stream it runs on.
 ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
 workload on this host's cores.
 """
@@ -88,27 +89,42 @@ def run_gpu(args):
     ddims = sb.dims_of(wl, seqlen=1)
     dws, _ = sb.workspace(ddims, sb.CALL_DECODE, dev)
     u_dec = up(synth.decode_token(wl, 0))
-    h_dec = torch.empty(wl.batch, wl.nheads, wl.dstate, wl.headdim, device=dev)
     y_dec = torch.empty(wl.batch, wl.nheads, wl.headdim, dtype=dt, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
+        # prefill the batch, then decode one more token of every sequence,
+        # updating the prefill's final state in place
         sb.forward(dims, u, wr, we, a, None, buf)
-        h_dec.copy_(buf.h_final)
-        sb.swimba_decode_step(ddims, u_dec, wr, we, a, h_dec, y_dec, None, dws)
+        sb.swimba_decode_step(ddims, u_dec, wr, we, a, buf.h_final, y_dec, None, dws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Reference timing without per-kernel events (reported, not the value).
+    # Per-kernel breakdown (events around every kernel), outside the timed region.
+    sb.profile_select(None)
+    sb.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    report = json.loads(sb.profile_report())
+    sb.profile_enable(False)
+    models = kernel_models(wl)
+    kernels = {n: {"launches": r["launches"], "avg_us": 1e3 * r["ms"] / r["launches"]}
+               for n, r in report.items()}
+    dom = max((n for n in models if n in report), key=lambda n: report[n]["ms"])
+
+    # Reference timing without any events (reported beside the value).
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed_plain = time.perf_counter() - t0
 
-    # The timed region: every library kernel is bracketed by HIP events
-    # recorded on the stream it runs on.
+    # The timed region: the dominant kernel is bracketed by HIP events recorded
+    # on the stream it runs on.
+    sb.profile_select(dom)
     sb.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -116,17 +132,14 @@ def run_gpu(args):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    report = json.loads(sb.profile_report())
+    rep_dom = json.loads(sb.profile_report())
     sb.profile_enable(False)
+    sb.profile_select(None)
 
     tokens = wl.tokens + wl.batch
     value = tokens * args.steps / elapsed
-    models = kernel_models(wl)
-    kernels = {n: {"launches": r["launches"], "avg_us": 1e3 * r["ms"] / r["launches"]}
-               for n, r in report.items()}
-    dom = max((n for n in models if n in report), key=lambda n: report[n]["ms"])
     bound, flops, nbytes = models[dom]
-    avg_s = report[dom]["ms"] / report[dom]["launches"] / 1e3
+    avg_s = rep_dom[dom]["ms"] / rep_dom[dom]["launches"] / 1e3
     if bound == "mfma":
         achieved = flops / avg_s / 1e12
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS

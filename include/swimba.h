@@ -209,6 +209,9 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
  */
 swimba_status swimba_profile_enable(int32_t on);
 int32_t swimba_profile_report(char* buf, size_t cap);
+/* Restrict the timing to kernels of this name (host string, copied); NULL or
+ * "" records every kernel. Decode-step kernels carry the prefix "decode_". */
+swimba_status swimba_profile_select(const char* kernel);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ STATUS = {
 EXPORTS = (
     "swimba_abi_version", "swimba_last_error", "swimba_workspace_size", "swimba_route_topk",
     "swimba_expert_project_mix", "swimba_ssd_chunk_scan", "swimba_decode_step",
-    "swimba_profile_enable", "swimba_profile_report",
+    "swimba_profile_enable", "swimba_profile_report", "swimba_profile_select",
 )
 
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.swimba_profile_enable.argtypes = [I32]
     L.swimba_profile_report.restype = I32
     L.swimba_profile_report.argtypes = [ctypes.c_char_p, SZ]
+    L.swimba_profile_select.restype = I32
+    L.swimba_profile_select.argtypes = [ctypes.c_char_p]
     _lib = L
     return L
 
@@ -173,6 +175,11 @@ def swimba_decode_step(dims, u, w_router, w_experts, a, h, y, topk_idx, ws, ws_b
 
 def profile_enable(on: bool):
     _check(lib().swimba_profile_enable(1 if on else 0))
+
+
+def profile_select(kernel: str | None):
+    """Time only kernels of this name (None: every kernel)."""
+    _check(lib().swimba_profile_select(kernel.encode() if kernel else None))
 
 
 def profile_report() -> str:

@@ -3,6 +3,7 @@
 // argument, so outputs stay untouched and the call is safe without a device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -91,16 +92,17 @@ swimba_status check_scan_shape(const Dims& d) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct ProjWs {
-  size_t counts, bases, offsets, tiles, sorted, cpart, total;
+  size_t counts, offsets, tiles, sorted, cpart, total;
 };
 
 ProjWs proj_ws(const Dims& d) {
   const int64_t pairs = d.M * d.k;
-  const int64_t nblk = bucket_blocks((int)pairs);
+  // histograms: blocks of kBucketPairs pairs, or of kRouteTok tokens when the
+  // router wrote them (decode); the latter is never fewer blocks (k <= 8).
+  const int64_t nblk = std::max<int64_t>(bucket_blocks((int)pairs), (d.M + kRouteTok - 1) / kRouteTok);
   ProjWs w{};
   size_t off = 0;
   w.counts = off; off += align256(sizeof(int32_t) * nblk * (d.E + 1));
-  w.bases = off; off += align256(sizeof(int32_t) * nblk * (d.E + 1));
   w.offsets = off; off += align256(sizeof(int32_t) * (d.E + 2));
   w.tiles = off; off += align256(sizeof(int32_t) * (d.E + 1));
   w.sorted = off; off += align256(sizeof(int32_t) * pairs);
@@ -110,7 +112,7 @@ ProjWs proj_ws(const Dims& d) {
 }
 
 struct DecWs {
-  size_t idx, w, bhat, xhat, cmix, proj, total;
+  size_t idx, w, bhat, xhat, proj, total;
 };
 
 DecWs dec_ws(const Dims& d) {
@@ -121,7 +123,6 @@ DecWs dec_ws(const Dims& d) {
   w.w = off; off += align256(sizeof(float) * pairs);
   w.bhat = off; off += align256(d.esize * pairs * d.GN);
   w.xhat = off; off += align256(d.esize * pairs * d.HP);
-  w.cmix = off; off += align256(d.esize * d.Bt * d.GN);
   w.proj = off;
   Dims one = d;
   one.T = 1;
@@ -161,23 +162,25 @@ ProjGeom proj_geom(const Dims& d, int64_t M) {
   return g;
 }
 
-// Runs bucketing, the grouped projection and the slot-ordered C sum for M tokens.
+// Runs bucketing, the grouped projection and (with C_mix non-null) the
+// slot-ordered C sum for M tokens. routed: the router already wrote the
+// per-kRouteTok-token expert histograms into the workspace.
 hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_experts,
                        const int32_t* idx, const float* w, void* B_hat, void* X_hat, void* C_mix,
-                       unsigned char* ws, hipStream_t s) {
+                       unsigned char* ws, hipStream_t s, bool routed = false) {
   Dims dm = d;
   dm.M = M;
   const ProjWs lay = proj_ws(dm);
   const int pairs = (int)(M * d.k);
   const int bm = proj_bm(pairs, (int)d.E);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
-  int32_t* bases = reinterpret_cast<int32_t*>(ws + lay.bases);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + lay.offsets);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + lay.sorted);
   float* cpart = reinterpret_cast<float*>(ws + lay.cpart);
-  hipError_t e = launch_bucket(d.bf16, idx, pairs, (int)d.E, bm, counts, bases, offsets, tiles,
-                               sorted, X_hat, (int)d.HP, B_hat, (int)d.GN, cpart, s);
+  hipError_t e = launch_bucket(d.bf16, idx, pairs, (int)d.E, bm, counts, nullptr, offsets, tiles,
+                               sorted, X_hat, (int)d.HP, B_hat, (int)d.GN, cpart, s,
+                               routed ? kRouteTok * (int)d.k : 0, routed);
   if (e != hipSuccess) return e;
   return launch_project(d.bf16, proj_geom(d, M), u, w_experts, sorted, offsets, tiles, idx, w, bm,
                         B_hat, X_hat, cpart, C_mix, s);
@@ -192,7 +195,9 @@ struct ProfRec {
 
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;  // record only this kernel name (empty: all)
 thread_local const char* g_prof_prefix = "";  // "decode_" inside swimba_decode_step
+bool g_prof_open = false;                      // a begin without its end yet
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -214,15 +219,19 @@ namespace swimba {
 void prof_begin(const char* name, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
-  ProfRec r{std::string(g_prof_prefix) + name, prof_event(), prof_event()};
+  std::string full = std::string(g_prof_prefix) + name;
+  if (!g_prof_only.empty() && full != g_prof_only) return;
+  ProfRec r{full, prof_event(), prof_event()};
   if (!r.start || !r.stop) return;
+  g_prof_open = true;
   hipEventRecord(r.start, s);
   g_prof_recs.push_back(r);
 }
 
 void prof_end(hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on || g_prof_recs.empty()) return;
+  if (!g_prof_on || !g_prof_open || g_prof_recs.empty()) return;
+  g_prof_open = false;
   hipEventRecord(g_prof_recs.back().stop, s);
 }
 
@@ -347,20 +356,30 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
   float* tw = reinterpret_cast<float*>(w8 + lay.w);
   void* bhat = w8 + lay.bhat;
   void* xhat = w8 + lay.xhat;
-  void* cmix = w8 + lay.cmix;
+  Dims d1 = d;
+  d1.M = d.Bt;
+  const ProjWs play = proj_ws(d1);
+  unsigned char* pws = w8 + lay.proj;
   hipError_t e = launch_route(d.bf16, u, w_router, (int)d.Bt, (int)d.D, (int)d.E, (int)d.k, idx,
-                              tw, nullptr, stream);
+                              tw, nullptr, stream, reinterpret_cast<int32_t*>(pws + play.counts));
   if (e != hipSuccess) return hip_status(e, "decode_step route launch");
-  e = run_project(d, d.Bt, u, w_experts, idx, tw, bhat, xhat, cmix, w8 + lay.proj, stream);
+  e = run_project(d, d.Bt, u, w_experts, idx, tw, bhat, xhat, nullptr, pws, stream, true);
   if (e != hipSuccess) return hip_status(e, "decode_step projection launch");
   e = launch_decode_state(d.bf16, (int)d.Bt, (int)d.H, (int)d.G, (int)d.N, (int)d.P, (int)d.k,
-                          bhat, xhat, cmix, a, h, y, stream);
+                          bhat, xhat, reinterpret_cast<const float*>(pws + play.cpart), a, h, y,
+                          stream);
   return hip_status(e, "decode_step state launch");
 }
 
 swimba_status swimba_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
+  return SWIMBA_OK;
+}
+
+swimba_status swimba_profile_select(const char* kernel) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = kernel ? kernel : "";
   return SWIMBA_OK;
 }
 

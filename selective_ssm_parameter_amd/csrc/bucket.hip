@@ -3,17 +3,17 @@
 // contiguous row list per expert, so that the projection can run as a grouped
 // GEMM over active pairs only.
 //
-// Three launches, all integer work and all deterministic:
-//   count   - per block of 1024 pairs, a histogram over E experts plus one
-//             extra bucket for out-of-range indices (LDS integer atomics:
-//             the counts do not depend on their order);
-//   scan    - one workgroup: expert offsets, per-block bases, and the number
-//             of BM-row tiles per expert with their prefix (the GEMM's tile
-//             schedule);
-//   scatter - per block, the stable rank of every pair among the block's
-//             pairs of the same expert (wave ballots, then wave order), so
-//             every expert's list is sorted by pair id m*k + j. A pair whose
-//             expert index is out of range gets zero outputs here.
+// Two launches, all integer work and all deterministic:
+//   count - per block of pairs, a histogram over E experts plus one extra
+//           bucket for out-of-range indices (LDS integer atomics: the counts
+//           do not depend on their order). The decode path gets these from
+//           the router instead.
+//   place - per block: bucket starts and earlier blocks' counts from the
+//           histograms, then the stable rank of every pair among the block's
+//           pairs of the same expert (wave ballots, then wave order), so
+//           every expert's list is sorted by pair id m*k + j. Block 0 also
+//           writes the GEMM's tile schedule. A pair whose expert index is out
+//           of range gets zero outputs here.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -39,83 +39,117 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
     counts[(size_t)blockIdx.x * (E + 1) + e] = hist[e];
 }
 
-// offsets[0..E+1]: start of each bucket (bucket E = invalid pairs) and the end.
-// tile_offsets[0..E]: prefix of ceil(count_e / bm) over real experts.
-__global__ __launch_bounds__(256) void bucket_scan_kernel(const int32_t* __restrict__ counts,
-                                                          int nblk, int E, int bm,
-                                                          int32_t* __restrict__ bases,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ tile_offsets) {
-  extern __shared__ int tot[];  // [E + 1]
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
-    int s = 0;
-    for (int b = 0; b < nblk; ++b) s += counts[(size_t)b * (E + 1) + e];
-    tot[e] = s;
+// Merged scan + scatter. Every workgroup owns one block of `bp` pairs; it
+// derives, from the per-block histograms, the start of every bucket (bucket E
+// = out-of-range indices) and the number of pairs of each bucket in the
+// blocks before its own, then places its pairs in stable order (pair id).
+// Workgroup 0 also writes the bucket offsets and the GEMM tile schedule:
+//   offsets[0..E+1]: start of each bucket and the end;
+//   tile_offsets[0..E]: prefix of ceil(count_e / bm) over real experts.
+template <typename T>
+__global__ __launch_bounds__(256) void bucket_place_kernel(
+    const int32_t* __restrict__ idx, int pairs, int E, int bp, int nblk,
+    const int32_t* __restrict__ counts, int bm, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tile_offsets, int32_t* __restrict__ sorted, T* __restrict__ X_hat,
+    int HP, T* __restrict__ B_hat, int GN, float* __restrict__ c_part) {
+  extern __shared__ int sh[];
+  const int EP = E + 1;
+  int* before = sh;            // [EP] pairs of each bucket in earlier blocks (then: running base)
+  int* total = sh + EP;        // [EP]
+  int* wcnt = sh + 2 * EP;     // [4][EP] per-wave counts of the current round
+  int* scan = sh + 6 * EP;     // [256] scan scratch
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int blk = blockIdx.x;
+
+  // ---- per-bucket sums over blocks, split over threads
+  const int nparts = EP <= 256 ? 256 / EP : 1;
+  for (int e = threadIdx.x; e < EP; e += blockDim.x) { before[e] = 0; total[e] = 0; }
+  for (int e = threadIdx.x; e < 4 * EP; e += blockDim.x) wcnt[e] = 0;
+  __syncthreads();
+  {
+    const int part = threadIdx.x / EP, e = threadIdx.x % EP;
+    if (part < nparts) {
+      int sb = 0, st = 0;
+      for (int b = part; b < nblk; b += nparts) {
+        const int v = counts[(size_t)b * EP + e];
+        st += v;
+        sb += b < blk ? v : 0;
+      }
+      atomicAdd(&before[e], sb);
+      atomicAdd(&total[e], st);
+    }
+    if (EP > 256) {  // one thread per bucket when buckets outnumber threads
+      for (int e2 = threadIdx.x; e2 < EP; e2 += blockDim.x) {
+        if (e2 < 256) continue;
+        int sb = 0, st = 0;
+        for (int b = 0; b < nblk; ++b) {
+          const int v = counts[(size_t)b * EP + e2];
+          st += v;
+          sb += b < blk ? v : 0;
+        }
+        before[e2] = sb;
+        total[e2] = st;
+      }
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0, tiles = 0;
-    for (int e = 0; e <= E; ++e) {
-      offsets[e] = run;
-      if (e < E) {
-        tile_offsets[e] = tiles;
-        tiles += (tot[e] + bm - 1) / bm;
-      }
-      run += tot[e];
+  // ---- exclusive scan of the totals (one bucket per thread, EP <= 257)
+  int tv = threadIdx.x < EP ? total[threadIdx.x] : 0;
+  scan[threadIdx.x] = tv;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+    __syncthreads();
+    scan[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const int excl = scan[threadIdx.x] - tv;
+  const int last_total = EP > 256 ? total[256] : 0;  // E = 256: bucket 256 is the invalid one
+  if (blk == 0) {
+    if (threadIdx.x < EP) offsets[threadIdx.x] = excl;
+    if (threadIdx.x == 0) {
+      if (EP > 256) offsets[256] = scan[255];
+      offsets[EP] = scan[255] + last_total;
     }
-    offsets[E + 1] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x < EP) before[threadIdx.x] += excl;  // becomes the running base of this block
+  if (EP > 256 && threadIdx.x == 0) before[256] += scan[255];
+  __syncthreads();
+  if (blk == 0 && threadIdx.x == 0) {
+    int tiles = 0;
+    for (int e = 0; e < E; ++e) {
+      tile_offsets[e] = tiles;
+      tiles += (total[e] + bm - 1) / bm;
+    }
     tile_offsets[E] = tiles;
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
-    int run = offsets[e];
-    for (int b = 0; b < nblk; ++b) {
-      bases[(size_t)b * (E + 1) + e] = run;
-      run += counts[(size_t)b * (E + 1) + e];
-    }
-  }
-}
 
-template <typename T>
-__global__ __launch_bounds__(256) void bucket_scatter_kernel(const int32_t* __restrict__ idx,
-                                                             int pairs, int E,
-                                                             const int32_t* __restrict__ bases,
-                                                             int32_t* __restrict__ sorted,
-                                                             T* __restrict__ X_hat, int HP,
-                                                             T* __restrict__ B_hat, int GN,
-                                                             float* __restrict__ c_part) {
-  extern __shared__ int sh[];
-  int* run = sh;                // [E + 1] running count of this block per bucket
-  int* wcnt = sh + (E + 1);     // [4][E + 1] per-wave counts of the current round
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) run[e] = 0;
-  for (int e = threadIdx.x; e < 4 * (E + 1); e += blockDim.x) wcnt[e] = 0;
-  __syncthreads();
-  const int p0 = blockIdx.x * kBucketPairs;
-  for (int r0 = 0; r0 < kBucketPairs; r0 += 256) {
+  // ---- stable placement of this block's pairs
+  const int p0 = blk * bp;
+  for (int r0 = 0; r0 < bp; r0 += 256) {
     const int p = p0 + r0 + threadIdx.x;
-    const bool ok = p < pairs;
-    const int b = ok ? bucket_of(idx[p], E) : -1;
-    // Rank among earlier lanes of this wave with the same bucket.
+    const bool ok = r0 + threadIdx.x < bp && p < pairs;
+    const int bkt = ok ? bucket_of(idx[p], E) : -1;
     int rank = 0;
     uint64_t todo = __ballot(ok);
     while (todo) {
       const int leader = __ffsll((long long)todo) - 1;
-      const int lb = __shfl(b, leader);
-      const uint64_t same = __ballot(ok && b == lb);
-      if (ok && b == lb) {
+      const int lb = __shfl(bkt, leader);
+      const uint64_t same = __ballot(ok && bkt == lb);
+      if (ok && bkt == lb) {
         const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         rank = __popcll(same & below);
       }
-      if (lane == leader) wcnt[wave * (E + 1) + lb] = __popcll(same);
+      if (lane == leader) wcnt[wave * EP + lb] = __popcll(same);
       todo &= ~same;
     }
     __syncthreads();
     if (ok) {
-      int pos = bases[(size_t)blockIdx.x * (E + 1) + b] + run[b] + rank;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w * (E + 1) + b];
+      int pos = before[bkt] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w * EP + bkt];
       sorted[pos] = p;
-      if (b == E) {
+      if (bkt == E) {
         // An out-of-range expert index: this slot contributes nothing.
         for (int i = 0; i < HP; ++i) X_hat[(size_t)p * HP + i] = from_f32<T>(0.f);
         for (int i = 0; i < GN; ++i) {
@@ -125,9 +159,9 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(const int32_t* __re
       }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
-      run[e] += wcnt[e] + wcnt[(E + 1) + e] + wcnt[2 * (E + 1) + e] + wcnt[3 * (E + 1) + e];
-      wcnt[e] = wcnt[(E + 1) + e] = wcnt[2 * (E + 1) + e] = wcnt[3 * (E + 1) + e] = 0;
+    for (int e = threadIdx.x; e < EP; e += blockDim.x) {
+      before[e] += wcnt[e] + wcnt[EP + e] + wcnt[2 * EP + e] + wcnt[3 * EP + e];
+      wcnt[e] = wcnt[EP + e] = wcnt[2 * EP + e] = wcnt[3 * EP + e] = 0;
     }
     __syncthreads();
   }
@@ -136,28 +170,28 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(const int32_t* __re
 hipError_t launch_bucket(bool is_bf16, const int32_t* idx, int pairs, int E, int bm,
                          int32_t* counts, int32_t* bases, int32_t* offsets, int32_t* tile_offsets,
                          int32_t* sorted, void* X_hat, int HP, void* B_hat, int GN,
-                         float* c_part, hipStream_t s) {
-  const int nblk = bucket_blocks(pairs);
+                         float* c_part, hipStream_t s, int block_pairs, bool counted) {
+  (void)bases;
+  const int bp = block_pairs > 0 ? block_pairs : kBucketPairs;
+  const int nblk = (pairs + bp - 1) / bp;
   const size_t hl = (size_t)(E + 1) * sizeof(int);
-  if (nblk > 0) {
+  if (nblk > 0 && !counted) {
     prof_begin("bucket_count", s);
     hipLaunchKernelGGL(bucket_count_kernel, dim3(nblk), dim3(256), hl, s, idx, pairs, E, counts);
     prof_end(s);
   }
-  prof_begin("bucket_scan", s);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(256), hl, s, counts, nblk, E, bm, bases,
-                     offsets, tile_offsets);
+  const size_t pl = (size_t)(6 * (E + 1) + 256) * sizeof(int);
+  prof_begin("bucket_place", s);
+  const dim3 grid(nblk > 0 ? nblk : 1);
+  if (is_bf16)
+    hipLaunchKernelGGL(bucket_place_kernel<f16>, grid, dim3(256), pl, s, idx, pairs, E, bp, nblk,
+                       counts, bm, offsets, tile_offsets, sorted, (f16*)X_hat, HP, (f16*)B_hat,
+                       GN, c_part);
+  else
+    hipLaunchKernelGGL(bucket_place_kernel<float>, grid, dim3(256), pl, s, idx, pairs, E, bp,
+                       nblk, counts, bm, offsets, tile_offsets, sorted, (float*)X_hat, HP,
+                       (float*)B_hat, GN, c_part);
   prof_end(s);
-  if (nblk > 0) {
-    prof_begin("bucket_scatter", s);
-    if (is_bf16)
-      hipLaunchKernelGGL(bucket_scatter_kernel<f16>, dim3(nblk), dim3(256), 5 * hl, s, idx,
-                         pairs, E, bases, sorted, (f16*)X_hat, HP, (f16*)B_hat, GN, c_part);
-    else
-      hipLaunchKernelGGL(bucket_scatter_kernel<float>, dim3(nblk), dim3(256), 5 * hl, s, idx,
-                         pairs, E, bases, sorted, (float*)X_hat, HP, (float*)B_hat, GN, c_part);
-    prof_end(s);
-  }
   return hipGetLastError();
 }
 

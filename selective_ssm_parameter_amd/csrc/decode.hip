@@ -4,7 +4,8 @@
 // key findings: token-by-token decoding).
 //
 // One workgroup per (sequence, head) streams that head's fp32 N x P state from
-// HBM once and writes it back once:
+// HBM once and writes it back once (C~ is summed here from the projection's
+// per-slot fp32 parts, in slot order):
 //     h[n, p] <- a_h h[n, p] + sum_j B_hat[j, n] X[j, p]      (fp32)
 //     y[p]     = sum_n C~[n] h[n, p]
 // Thread t handles columns p = 4(t % 16) .. +3 and rows n = t/16 + 16 i, so
@@ -21,7 +22,7 @@ constexpr int kDecMaxN = 128;
 
 template <typename S, typename TY>
 __global__ __launch_bounds__(256) void decode_state_kernel(
-    const S* __restrict__ B_hat, const S* __restrict__ X_hat, const S* __restrict__ C_mix,
+    const S* __restrict__ B_hat, const S* __restrict__ X_hat, const float* __restrict__ c_part,
     const float* __restrict__ a, float* __restrict__ hstate, TY* __restrict__ y, int H, int G,
     int N, int k) {
   constexpr int P = 64;
@@ -41,7 +42,12 @@ __global__ __launch_bounds__(256) void decode_state_kernel(
     const int j = q / P, p = q % P;
     sX[j][p] = to_f32(X_hat[((size_t)b * k + j) * H * P + (size_t)h * P + p]);
   }
-  for (int n = threadIdx.x; n < N; n += 256) sC[n] = to_f32(C_mix[(size_t)b * GN + grp * N + n]);
+  // C~ = sum_j c_part[b, j] in slot order (fp32), rounded to the stream type
+  for (int n = threadIdx.x; n < N; n += 256) {
+    float cs = 0.f;
+    for (int j = 0; j < k; ++j) cs += c_part[((size_t)b * k + j) * GN + grp * N + n];
+    sC[n] = to_f32(from_f32<S>(cs));
+  }
   __syncthreads();
 
   const float ah = a[h];
@@ -70,18 +76,18 @@ __global__ __launch_bounds__(256) void decode_state_kernel(
 }
 
 hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
-                               const void* B_hat, const void* X_hat, const void* C_mix,
+                               const void* B_hat, const void* X_hat, const float* c_part,
                                const float* a, float* h, void* y, hipStream_t s) {
   (void)P;
   if (Bt == 0) return hipSuccess;
   prof_begin("decode_state", s);
   if (is_bf16)
     hipLaunchKernelGGL((decode_state_kernel<f16, bf16>), dim3(H, Bt), dim3(256), 0, s,
-                       (const f16*)B_hat, (const f16*)X_hat, (const f16*)C_mix, a, h, (bf16*)y,
+                       (const f16*)B_hat, (const f16*)X_hat, c_part, a, h, (bf16*)y,
                        H, G, N, k);
   else
     hipLaunchKernelGGL((decode_state_kernel<float, float>), dim3(H, Bt), dim3(256), 0, s,
-                       (const float*)B_hat, (const float*)X_hat, (const float*)C_mix, a, h,
+                       (const float*)B_hat, (const float*)X_hat, c_part, a, h,
                        (float*)y, H, G, N, k);
   prof_end(s);
   return hipGetLastError();

@@ -9,7 +9,7 @@
 namespace swimba {
 
 // Optional per-kernel timing (see swimba_profile_enable in the public header).
-void prof_begin(const char* name, hipStream_t s);
+void prof_begin(const char* name, hipStream_t s);  // no-op unless profiling is on
 void prof_end(hipStream_t s);
 
 struct ProjGeom {
@@ -18,21 +18,27 @@ struct ProjGeom {
   int GN() const { return G * N; }
 };
 
-// Router: logits (fp32), softmax, top-k.
+// Router: logits (fp32), softmax, top-k. With `hist` non-null it also writes
+// the expert histogram of each workgroup's kRouteTok tokens ([nblk][E+1]).
+constexpr int kRouteTok = 64;
 hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M, int D, int E, int k,
-                        int32_t* idx, float* w, float* logits, hipStream_t s);
+                        int32_t* idx, float* w, float* logits, hipStream_t s,
+                        int32_t* hist = nullptr);
 
 // Bucketing of (token, slot) pairs by expert.
 constexpr int kBucketPairs = 1024;  // pairs per bucketing block
 int bucket_blocks(int pairs);
+// block_pairs: pairs per bucketing block (0 = kBucketPairs); counted: the
+// histograms [nblk][E+1] are already in `counts` (written by the router).
 hipError_t launch_bucket(bool is_bf16, const int32_t* idx, int pairs, int E, int bm,
                          int32_t* counts, int32_t* bases, int32_t* offsets, int32_t* tile_offsets,
                          int32_t* sorted, void* X_hat, int HP, void* B_hat, int GN,
-                         float* c_part, hipStream_t s);
+                         float* c_part, hipStream_t s, int block_pairs = 0, bool counted = false);
 
 // Grouped expert projection with the mix epilogue, then the slot-ordered C sum.
 int proj_row_tiles_max(int pairs, int E, int bm);
 int proj_bm(int pairs, int E);
+// C_mix == nullptr skips the slot sum (the caller consumes c_part itself).
 hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const void* w_experts,
                           const int32_t* sorted, const int32_t* offsets,
                           const int32_t* tile_offsets, const int32_t* idx, const float* w,
@@ -54,8 +60,9 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
 hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t s);
 
 // Decode: in-place state update and readout for one token per sequence.
+// C~ is summed here from the per-slot fp32 parts c_part [Bt, k, G*N], in slot order.
 hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
-                               const void* B_hat, const void* X_hat, const void* C_mix,
+                               const void* B_hat, const void* X_hat, const float* c_part,
                                const float* a, float* h, void* y, hipStream_t s);
 
 }  // namespace swimba

@@ -247,6 +247,7 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
     hipLaunchKernelGGL((proj_kernel<T, 64>), grid, dim3(256), lds, s, u, wexp, sorted, offsets,
                        tile_offsets, w, g.M, g.D, g.W, g.HP(), g.GN(), g.E, g.k, X_hat, B_hat, c_part);
   prof_end(s);
+  if (!C_mix) return hipGetLastError();
   const size_t n4 = (size_t)g.M * g.GN() / 4;
   prof_begin("mix_c", s);
   hipLaunchKernelGGL(mix_c_kernel<S>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, c_part,

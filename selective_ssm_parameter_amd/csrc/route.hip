@@ -16,14 +16,16 @@
 
 namespace swimba {
 
-constexpr int kRouteTok = 64;
+__device__ void route_token(const float* l, int m, int E, int k, int32_t* __restrict__ idx,
+                            float* __restrict__ wout, float* __restrict__ logits, int* hcnt);
 
 template <typename T>
 __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
                                                     const T* __restrict__ wr, int M, int D,
                                                     int E, int k, int32_t* __restrict__ idx,
                                                     float* __restrict__ wout,
-                                                    float* __restrict__ logits) {
+                                                    float* __restrict__ logits,
+                                                    int32_t* __restrict__ hist) {
   extern __shared__ float lg[];  // [64][E + 1]
   typedef typename Vec<T>::x8 F;
   const int lane = lane_id();
@@ -65,10 +67,23 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
   }
   __syncthreads();
 
+  int* hcnt = reinterpret_cast<int*>(lg + kRouteTok * ldl);  // [E + 1]
+  if (hist) {
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) hcnt[e] = 0;
+    __syncthreads();
+  }
   const int t = threadIdx.x;
-  if (t >= kRouteTok || tok0 + t >= M) return;
-  const int m = tok0 + t;
-  const float* l = lg + t * ldl;
+  if (t < kRouteTok && tok0 + t < M) route_token(lg + t * ldl, tok0 + t, E, k, idx, wout, logits,
+                                                 hist ? hcnt : nullptr);
+  if (hist) {
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) hist[(size_t)blockIdx.x * (E + 1) + e] = hcnt[e];
+  }
+}
+
+// Top-k and softmax of one token from its logits in LDS.
+__device__ void route_token(const float* l, int m, int E, int k, int32_t* __restrict__ idx,
+                            float* __restrict__ wout, float* __restrict__ logits, int* hcnt) {
   if (logits) {
     for (int e = 0; e < E; ++e) logits[(size_t)m * E + e] = l[e];
   }
@@ -94,14 +109,15 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
   for (int j = 0; j < k; ++j) {
     idx[(size_t)m * k + j] = chosen[j];
     wout[(size_t)m * k + j] = expf(l[chosen[j]] - mx) * inv;
+    if (hcnt) atomicAdd(&hcnt[chosen[j]], 1);
   }
 }
 
 hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M, int D, int E, int k,
-                        int32_t* idx, float* w, float* logits, hipStream_t s) {
+                        int32_t* idx, float* w, float* logits, hipStream_t s, int32_t* hist) {
   if (M == 0) return hipSuccess;
   dim3 grid((M + kRouteTok - 1) / kRouteTok), block(256);
-  size_t lds = (size_t)kRouteTok * (E + 1) * sizeof(float);
+  size_t lds = (size_t)kRouteTok * (E + 1) * sizeof(float) + (size_t)(E + 1) * sizeof(int);
   hipError_t err = hipFuncSetAttribute(
       is_bf16 ? (const void*)route_kernel<bf16> : (const void*)route_kernel<float>,
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -109,10 +125,10 @@ hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M
   prof_begin("route_topk", s);
   if (is_bf16)
     hipLaunchKernelGGL(route_kernel<bf16>, grid, block, lds, s, (const bf16*)u,
-                       (const bf16*)w_router, M, D, E, k, idx, w, logits);
+                       (const bf16*)w_router, M, D, E, k, idx, w, logits, hist);
   else
     hipLaunchKernelGGL(route_kernel<float>, grid, block, lds, s, (const float*)u,
-                       (const float*)w_router, M, D, E, k, idx, w, logits);
+                       (const float*)w_router, M, D, E, k, idx, w, logits, hist);
   prof_end(s);
   return hipGetLastError();
 }

@@ -59,13 +59,14 @@ struct ScanLds {
   static constexpr int R = KS * BT;      // pair rows per block
   static constexpr int LDN = NP + 8;     // row stride of [.][n] buffers
   static constexpr int LDR = R + 8;      // row stride of [.][r] buffers
-  static constexpr int CS = WITH_Y ? BT * LDN : 0;
-  static constexpr int BS = WITH_Y ? R * LDN : 0;
-  static constexpr int BST = NP * LDR;
-  static constexpr int XST = kP * LDR;
-  static constexpr int GM = WITH_Y ? BT * LDR : 0;
-  static constexpr int ELEMS = CS + BS + BST + XST + GM;
-  static constexpr size_t bytes = (size_t)ELEMS * sizeof(T);
+  static constexpr int CS = WITH_Y ? BT * LDN : 0;   // C~ [t][n]
+  static constexpr int BS = WITH_Y ? R * LDN : 0;    // B_hat [r][n]
+  static constexpr int HS = WITH_Y ? kP * LDN : 0;   // entering state [p][n]
+  static constexpr int BST = NP * LDR;               // B_hat^T [n][r]
+  static constexpr int XST = kP * LDR;               // X^T [p][r]
+  static constexpr int GM = WITH_Y ? BT * LDR : 0;   // masked Gram [t][r]
+  static constexpr int ELEMS = CS + BS + HS + BST + XST + GM;
+  static constexpr size_t bytes = (size_t)ELEMS * sizeof(T) + 16 * sizeof(float);
 };
 
 // Transposed [row][r] buffers store 8-element column chunks XOR-swizzled by the
@@ -87,36 +88,57 @@ struct ScanStep {
   int ch, tau, sig;
 };
 
+constexpr int kScanThreads = 512;  // 8 waves
+
 template <typename T, int NP, int KS, int BT, bool WITH_Y>
 struct ScanStage {
   static constexpr int R = KS * BT;
-  static constexpr int CUN = (BT * (NP / 8) + 255) / 256;        // C~ chunks per thread
-  static constexpr int BUN = ((R / 4) * (NP / 8) + 255) / 256;   // B_hat 4x8 units per thread
-  static constexpr int XUN = ((R / 4) * (kP / 8) + 255) / 256;   // X 4x8 units per thread
+  static constexpr int NTH = kScanThreads;
+  static constexpr int CUN = (BT * (NP / 8) + NTH - 1) / NTH;        // C~ chunks per thread
+  static constexpr int BUN = ((R / 4) * (NP / 8) + NTH - 1) / NTH;   // B_hat 4x8 units
+  static constexpr int XUN = ((R / 4) * (kP / 8) + NTH - 1) / NTH;   // X 4x8 units
   typedef typename Vec<T>::x8 F;
   F cv[WITH_Y ? CUN : 1];
   F bv[BUN][4];
   F xv[XUN][4];
 };
 
+// Work split over the 8 waves.
+//  state / carry:  WVN x WVP waves over (n, p); a wave owns NTW x PTW 16x16 tiles
+//  y / readout:    4 p-tiles x TT t-tiles; a wave owns p-tile w%4, t-tiles w/4 + 2j
+//  Gram^T:         RT x TT tiles; a wave owns tiles w + 8m (same t-tile for all m)
+template <int NP, int BT, int R>
+struct ScanSplit {
+  static constexpr int NT = NP / 16;
+  static constexpr int WVN = NT < 4 ? NT : 4;
+  static constexpr int WVP = 8 / WVN;
+  static constexpr int NTW = NT / WVN;
+  static constexpr int PTW = 4 / WVP;
+  static constexpr int TT = BT / 16, RT = R / 16;
+  static constexpr int YTW = TT / 2;                   // t-tiles per wave (y)
+  static constexpr int GTW = (RT * TT + 7) / 8;        // Gram tiles per wave
+  static constexpr int RQ = R / 32;
+};
+
 template <typename T, typename TY, int NP, int KS, int BT, bool WITH_Y>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
   typedef ScanLds<T, NP, KS, BT, WITH_Y> Lay;
   typedef ScanStage<T, NP, KS, BT, WITH_Y> Stage;
   constexpr int R = Lay::R, LDN = Lay::LDN, LDR = Lay::LDR;
-  constexpr int NT = NP / 16;               // 16-row tiles of the state
-  constexpr int RT = R / 16, TT = BT / 16;  // Gram tiles
-  constexpr int MT = (RT * TT + 3) / 4;     // Gram tiles per wave
-  constexpr int RQ = R / 32;                // 32-pair contraction steps per block
+  typedef ScanSplit<NP, BT, R> Sp;
+  constexpr int NTW = Sp::NTW, PTW = Sp::PTW, YTW = Sp::YTW, GTW = Sp::GTW, RQ = Sp::RQ;
+  constexpr int TT = Sp::TT, RT = Sp::RT;
   typedef typename Vec<T>::x8 F;
   typedef typename Vec<T>::x4 F4;
 
   extern __shared__ __align__(16) unsigned char lds_raw[];
   T* Cs = reinterpret_cast<T*>(lds_raw);
   T* Bs = Cs + Lay::CS;
-  T* BsT = Bs + Lay::BS;
+  T* Hs = Bs + Lay::BS;
+  T* BsT = Hs + Lay::HS;
   T* XsT = BsT + Lay::BST;
   T* Gm = XsT + Lay::XST;
+  float* wmax = reinterpret_cast<float*>(Gm + Lay::GM);  // [8] per-wave max |H|
 
   const int h = blockIdx.x, seg = blockIdx.y, b = blockIdx.z;
   const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
@@ -125,14 +147,18 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6;
   const int g4 = lane >> 4, c = lane & 15;
-  const int pcol = 16 * wave + c;  // this lane's state column
   const size_t NPsz = (size_t)N * kP;
   const size_t HPsz = (size_t)H * kP;
+
+  // this wave's tiles
+  const int n_t0 = (wave / Sp::WVP) * NTW;   // first n-tile of the state slice
+  const int p_t0 = (wave % Sp::WVP) * PTW;   // first p-tile of the state slice
+  const int y_pt = wave % 4;                 // y p-tile
+  const int y_t0 = wave / 4;                 // first y t-tile (then +2)
 
   const float ah = A.a[h];
   const float la = ah > 0.f ? log2f(ah) : -1e30f;
 
-  // ---- buffer resources over this sequence's streams (out of range -> 0)
   constexpr uint32_t ES = sizeof(T);
   const BufRes rB = make_rsrc(reinterpret_cast<const T*>(A.B_hat) + (size_t)b * Tlen * KS * GN,
                               (uint64_t)Tlen * KS * GN * ES);
@@ -141,20 +167,22 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
   const BufRes rC = make_rsrc(reinterpret_cast<const T*>(A.C_mix) + (size_t)b * Tlen * GN,
                               (uint64_t)Tlen * GN * ES);
 
-  // ---- per-lane decay tables for full chunks (Lc == L)
-  // carry: a^{BT-1-s} for the pair rows r = 32q + 8g + e this lane contracts
-  float cd[RQ][8];
+  // ---- decay tables for full chunks (Lc == L)
+  // carry: the transposed B_hat rows this thread stages are scaled by
+  // a^{Lc-1-s}; for a full chunk that is a^{(nb-1-sig) BT} * a^{BT-1-s_local}.
+  float cdb[Stage::BUN][4];
 #pragma unroll
-  for (int q = 0; q < RQ; ++q)
+  for (int u = 0; u < Stage::BUN; ++u) {
+    const int r0 = 4 * ((tid + kScanThreads * u) / (NP / 8));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cd[q][e] = apow(la, BT - 1 - (32 * q + 8 * g4 + e) / KS);
-  // Gram mask of a diagonal block: a^{t-s} for t >= s, else 0
-  float gmk[MT][4];
-  float al[BT / 16];  // readout decay a^{t+1} for the lane's t in block 0
+    for (int i = 0; i < 4; ++i) cdb[u][i] = apow(la, BT - 1 - (r0 + i) / KS);
+  }
+  float gmk[GTW][4];  // Gram mask of a diagonal block: a^{t-s} for t >= s, else 0
+  float al[YTW];      // readout decay a^{t+1} for the lane's t in block 0
   if (WITH_Y) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int tix = wave + 4 * m;
+    for (int m = 0; m < GTW; ++m) {
+      const int tix = wave + 8 * m;
       const int rt = tix / TT, tt = tix % TT;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -163,11 +191,11 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
       }
     }
 #pragma unroll
-    for (int tt = 0; tt < BT / 16; ++tt) al[tt] = apow(la, 16 * tt + c + 1);
+    for (int j = 0; j < YTW; ++j) al[j] = apow(la, 16 * (y_t0 + 2 * j) + c + 1);
   }
 
-  // ---- entering state of this segment
-  floatx4 Hr[NT];
+  // ---- entering state of this segment (this wave's slice, accumulator layout)
+  floatx4 Hr[NTW][PTW];
   {
     const float* src = nullptr;
     if (WITH_Y) {
@@ -179,12 +207,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
       }
     }
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni)
+    for (int a = 0; a < NTW; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = 16 * ni + 4 * g4 + i;
-        Hr[ni][i] = (src && n < N) ? src[(size_t)n * kP + pcol] : 0.f;
-      }
+      for (int pp = 0; pp < PTW; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * (n_t0 + a) + 4 * g4 + i, p = 16 * (p_t0 + pp) + c;
+          Hr[a][pp][i] = (src && n < N) ? src[(size_t)n * kP + p] : 0.f;
+        }
   }
 
   const int nc = (Tlen + L - 1) / L;
@@ -205,8 +235,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
     return s;
   };
 
-  // ---- global -> registers for one step (issued one step ahead). Full
-  // blocks take the unguarded path; only a sequence's last block is partial.
+  // ---- global -> registers for one step (issued one step ahead)
   auto load = [&](Stage& st, ScanStep s) {
     const int c0 = s.ch * L;
     const int Lc = min(L, Tlen - c0);
@@ -217,16 +246,15 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
       const uint32_t trow = (uint32_t)(c0 + s.tau * BT);
 #pragma unroll
       for (int u = 0; u < Stage::CUN; ++u) {
-        const int q = tid + 256 * u;
+        const int q = tid + kScanThreads * u;
         const int t = q / (NP / 8), n0 = 8 * (q % (NP / 8));
         const bool ok = q < BT * (NP / 8) && n0 < N && t < tlim;
-        const uint32_t off = ((trow + t) * GN + grp * N + n0) * ES;
-        st.cv[u] = load8_buf<T>(rC, ok ? off : kOOB);
+        st.cv[u] = load8_buf<T>(rC, ok ? ((trow + t) * GN + grp * N + n0) * ES : kOOB);
       }
     }
 #pragma unroll
     for (int u = 0; u < Stage::BUN; ++u) {
-      const int q = tid + 256 * u;
+      const int q = tid + kScanThreads * u;
       const int r0 = 4 * (q / (NP / 8)), n0 = 8 * (q % (NP / 8));
       const bool uok = q < (R / 4) * (NP / 8) && n0 < N;
       const uint32_t off = ((prow + r0) * GN + grp * N + n0) * ES;
@@ -236,7 +264,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
     }
 #pragma unroll
     for (int u = 0; u < Stage::XUN; ++u) {
-      const int q = tid + 256 * u;
+      const int q = tid + kScanThreads * u;
       const int r0 = 4 * (q / (kP / 8)), p0 = 8 * (q % (kP / 8));
       const bool uok = q < (R / 4) * (kP / 8);
       const uint32_t off = ((prow + r0) * (uint32_t)HPsz + h * kP + p0) * ES;
@@ -249,10 +277,12 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
   // ---- registers -> LDS
   auto store = [&](const Stage& st, ScanStep s) {
     const bool diag = s.sig == s.tau;
+    const int c0s = s.ch * L;
+    const int Lcs = min(L, Tlen - c0s);
     if (WITH_Y && s.sig == 0) {
 #pragma unroll
       for (int u = 0; u < Stage::CUN; ++u) {
-        const int q = tid + 256 * u;
+        const int q = tid + kScanThreads * u;
         if (q < BT * (NP / 8)) {
           const int t = q / (NP / 8), n0 = 8 * (q % (NP / 8));
           store8<T>(&Cs[t * LDN + n0], st.cv[u]);
@@ -261,7 +291,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
     }
 #pragma unroll
     for (int u = 0; u < Stage::BUN; ++u) {
-      const int q = tid + 256 * u;
+      const int q = tid + kScanThreads * u;
       if (q < (R / 4) * (NP / 8)) {
         const int r0 = 4 * (q / (NP / 8)), n0 = 8 * (q % (NP / 8));
         if (WITH_Y) {
@@ -269,10 +299,23 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
           for (int i = 0; i < 4; ++i) store8<T>(&Bs[(r0 + i) * LDN + n0], st.bv[u][i]);
         }
         if (diag) {
+          // rows scaled by their carry decay a^{Lc-1-s} (relative to the chunk end)
+          F dv[4];
+          if (Lcs == L) {
+            const float blk = apow(la, ((Lcs + BT - 1) / BT - 1 - s.sig) * BT);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dv[i] = st.bv[u][i] * from_f32<T>(cdb[u][i] * blk);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int d = Lcs - 1 - (s.sig * BT + (r0 + i) / KS);
+              dv[i] = st.bv[u][i] * from_f32<T>(d >= 0 ? apow(la, d) : 0.f);
+            }
+          }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int row = n0 + e;
-            F4 col = {st.bv[u][0][e], st.bv[u][1][e], st.bv[u][2][e], st.bv[u][3][e]};
+            F4 col = {dv[0][e], dv[1][e], dv[2][e], dv[3][e]};
             *reinterpret_cast<F4*>(&BsT[row * LDR + 8 * swz<R>(row, r0 >> 3) + (r0 & 7)]) = col;
           }
         }
@@ -280,7 +323,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
     }
 #pragma unroll
     for (int u = 0; u < Stage::XUN; ++u) {
-      const int q = tid + 256 * u;
+      const int q = tid + kScanThreads * u;
       if (q < (R / 4) * (kP / 8)) {
         const int r0 = 4 * (q / (kP / 8)), p0 = 8 * (q % (kP / 8));
 #pragma unroll
@@ -293,42 +336,48 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
     }
   };
 
+  // per-wave max |H| -> LDS (read after the next barrier)
+  auto publish_max = [&]() {
+    float mx = 0.f;
+#pragma unroll
+    for (int a = 0; a < NTW; ++a)
+#pragma unroll
+      for (int pp = 0; pp < PTW; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[a][pp][i]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) wmax[wave] = mx;
+  };
+
   ScanStep cur{ch0, 0, 0};
   Stage st;
   load(st, cur);
+  if (WITH_Y) publish_max();
 
-  F hfrag[NT / 2];
   float hscale = 1.f;
-  floatx4 accY[BT / 16];
+  floatx4 accY[YTW];
 
   while (cur.ch < ch1) {
     const int c0 = cur.ch * L;
     const int Lc = min(L, Tlen - c0);
     const int nb = (Lc + BT - 1) / BT;
-    const bool full_chunk = Lc == L;
     const bool diag = cur.sig == cur.tau;
+    const bool chunk_start = cur.tau == 0 && cur.sig == 0;
 
-    __syncthreads();  // every reader of the previous step's LDS data is done
+    __syncthreads();  // readers of the previous step's LDS data are done; wmax visible
     store(st, cur);
-    const ScanStep nxt = advance(cur);
-    if (nxt.ch < ch1) load(st, nxt);  // in flight during this step's compute
-    __syncthreads();
-
-    if (cur.tau == 0 && cur.sig == 0) {
+    if (chunk_start) {
       if (WITH_Y) {
-        // The entering state as a matrix-core operand. In fp16 it is first
-        // scaled by 2^-e (per wave, e >= 0 chosen from the wave's max |H|) so
-        // it stays below 2^14; the readout is multiplied back by 2^e in fp32.
+        // The entering state as an fp16 matrix-core operand [p][n], scaled by
+        // 2^-e (e >= 0 from the workgroup's max |H|) so it stays below 2^14;
+        // the readout is multiplied back by 2^e in fp32.
         float hin = 1.f;
         hscale = 1.f;
         if (sizeof(T) == 2) {
-          float mx = 0.f;
+          float mx = wmax[0];
 #pragma unroll
-          for (int ni = 0; ni < NT; ++ni)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[ni][i]));
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+          for (int w = 1; w < 8; ++w) mx = fmaxf(mx, wmax[w]);
           if (mx > 16384.f) {
             const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
             hin = ldexpf(1.f, -e);
@@ -336,109 +385,121 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
           }
         }
 #pragma unroll
-        for (int q = 0; q < NT / 2; ++q) {
+        for (int a = 0; a < NTW; ++a)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hfrag[q][i] = from_f32<T>(Hr[2 * q][i] * hin);
-            hfrag[q][4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
+          for (int pp = 0; pp < PTW; ++pp) {
+            F4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = from_f32<T>(Hr[a][pp][i] * hin);
+            *reinterpret_cast<F4*>(&Hs[(16 * (p_t0 + pp) + c) * LDN + 16 * (n_t0 + a) + 4 * g4]) = v;
           }
-        }
       }
       // The carry accumulates straight into the state: H <- a^{Lc} H first.
       const float aL = apow(la, Lc);
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni) Hr[ni] = Hr[ni] * aL;
+      for (int a = 0; a < NTW; ++a)
+#pragma unroll
+        for (int pp = 0; pp < PTW; ++pp) Hr[a][pp] = Hr[a][pp] * aL;
     }
+    const ScanStep nxt = advance(cur);
+    if (nxt.ch < ch1) load(st, nxt);  // in flight during this step's compute
+    __syncthreads();
 
     if (WITH_Y) {
       if (cur.sig == 0) {
-        // ---- readout of the entering state for block tau
+        // ---- readout of the entering state for block tau: y^T[p, t] = H^T[p, n] C~^T[n, t]
         const float ablk = (cur.tau == 0 ? 1.f : apow(la, cur.tau * BT)) * hscale;
 #pragma unroll
-        for (int tt = 0; tt < BT / 16; ++tt) {
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-          const T* crow = &Cs[(16 * tt + c) * LDN];
+        for (int j = 0; j < YTW; ++j) accY[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < NT / 2; ++q) {
-            F bf = load4x2<T>(crow + 32 * q + 4 * g4, crow + 32 * q + 16 + 4 * g4);
-            acc = mma16(hfrag[q], bf, acc);
-          }
-          accY[tt] = acc * (al[tt] * ablk);
+        for (int q = 0; q < NP / 32; ++q) {
+          F hf = load8<T>(&Hs[(16 * y_pt + c) * LDN + 32 * q + 8 * g4]);
+#pragma unroll
+          for (int j = 0; j < YTW; ++j)
+            accY[j] = mma16(hf, load8<T>(&Cs[(16 * (y_t0 + 2 * j) + c) * LDN + 32 * q + 8 * g4]), accY[j]);
         }
+#pragma unroll
+        for (int j = 0; j < YTW; ++j) accY[j] = accY[j] * (al[j] * ablk);
       }
       // ---- masked Gram^T tiles -> Gm[t][r]
       const int dblk = (cur.tau - cur.sig) * BT;
+      floatx4 gacc[GTW];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int tix = wave + 4 * m;
-        if (tix < RT * TT) {
-          const int rt = tix / TT, tt = tix % TT;
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-          const T* brow = &Bs[(16 * rt + c) * LDN + 8 * g4];
-          const T* crow = &Cs[(16 * tt + c) * LDN + 8 * g4];
+      for (int m = 0; m < GTW; ++m) gacc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+      {
+        const int tt = wave % TT;  // the same t-tile for every tile of this wave
 #pragma unroll
-          for (int q = 0; q < NP / 32; ++q) acc = mma16(load8<T>(brow + 32 * q), load8<T>(crow + 32 * q), acc);
-          F4 out;
-          if (dblk == 0) {
+        for (int q = 0; q < NP / 32; ++q) {
+          F cf = load8<T>(&Cs[(16 * tt + c) * LDN + 32 * q + 8 * g4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) out[i] = from_f32<T>(acc[i] * gmk[m][i]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              out[i] = from_f32<T>(acc[i] * apow(la, dblk + (16 * tt + c) - (16 * rt + 4 * g4 + i) / KS));
+          for (int m = 0; m < GTW; ++m) {
+            const int rt = (wave + 8 * m) / TT;
+            if (wave + 8 * m < RT * TT)
+              gacc[m] = mma16(load8<T>(&Bs[(16 * rt + c) * LDN + 32 * q + 8 * g4]), cf, gacc[m]);
           }
-          *reinterpret_cast<F4*>(&Gm[(16 * tt + c) * LDR + 16 * rt + 4 * g4]) = out;
+        }
+#pragma unroll
+        for (int m = 0; m < GTW; ++m) {
+          const int tix = wave + 8 * m;
+          if (tix < RT * TT) {
+            const int rt = tix / TT;
+            F4 out;
+            if (dblk == 0) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) out[i] = from_f32<T>(gacc[m][i] * gmk[m][i]);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                out[i] = from_f32<T>(gacc[m][i] *
+                                     apow(la, dblk + (16 * tt + c) - (16 * rt + 4 * g4 + i) / KS));
+            }
+            *reinterpret_cast<F4*>(&Gm[(16 * tt + c) * LDR + 16 * rt + 4 * g4]) = out;
+          }
         }
       }
       __syncthreads();
       // ---- y^T[p, t] += X^T[p, r] Gm[t, r]
-      F xa[RQ];
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) xa[q] = load8<T>(&XsT[pcol * LDR + 8 * swz<R>(pcol, 4 * q + g4)]);
-#pragma unroll
-      for (int tt = 0; tt < BT / 16; ++tt) {
-        const T* grow = &Gm[(16 * tt + c) * LDR + 8 * g4];
-#pragma unroll
-        for (int q = 0; q < RQ; ++q) accY[tt] = mma16(xa[q], load8<T>(grow + 32 * q), accY[tt]);
-      }
-    }
-    // ---- carry: H[n, p] += sum_r B_hat[r, n] a^{Lc-1-s} X[r, p]
-    if (diag) {
-      // decay of block sig relative to the chunk end
-      const bool tab = full_chunk;
-      const float blk = tab ? apow(la, (nb - 1 - cur.sig) * BT) : 0.f;
 #pragma unroll
       for (int q = 0; q < RQ; ++q) {
-        F xf = load8<T>(&XsT[pcol * LDR + 8 * swz<R>(pcol, 4 * q + g4)]);
-        if (tab) {
+        const int prow = 16 * y_pt + c;
+        F xa = load8<T>(&XsT[prow * LDR + 8 * swz<R>(prow, 4 * q + g4)]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xf[e] = from_f32<T>(to_f32(xf[e]) * (cd[q][e] * blk));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int d = Lc - 1 - (cur.sig * BT + (32 * q + 8 * g4 + e) / KS);
-            xf[e] = from_f32<T>(d >= 0 ? to_f32(xf[e]) * apow(la, d) : 0.f);
-          }
-        }
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni) {
-          const int row = 16 * ni + c;
-          Hr[ni] = mma16(load8<T>(&BsT[row * LDR + 8 * swz<R>(row, 4 * q + g4)]), xf, Hr[ni]);
-        }
+        for (int j = 0; j < YTW; ++j)
+          accY[j] = mma16(xa, load8<T>(&Gm[(16 * (y_t0 + 2 * j) + c) * LDR + 32 * q + 8 * g4]), accY[j]);
       }
     }
+    // ---- carry: H[n, p] += sum_r (a^{Lc-1-s} B_hat[r, n]) X[r, p]
+    if (diag) {
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        F xf[PTW];
+#pragma unroll
+        for (int pp = 0; pp < PTW; ++pp) {
+          const int prow = 16 * (p_t0 + pp) + c;
+          xf[pp] = load8<T>(&XsT[prow * LDR + 8 * swz<R>(prow, 4 * q + g4)]);
+        }
+#pragma unroll
+        for (int a = 0; a < NTW; ++a) {
+          const int row = 16 * (n_t0 + a) + c;
+          F bt = load8<T>(&BsT[row * LDR + 8 * swz<R>(row, 4 * q + g4)]);
+#pragma unroll
+          for (int pp = 0; pp < PTW; ++pp) Hr[a][pp] = mma16(bt, xf[pp], Hr[a][pp]);
+        }
+      }
+      if (WITH_Y && cur.tau == nb - 1) publish_max();  // chunk done: max for the next Hs
+    }
     if (WITH_Y && diag) {
-      // ---- store y for block tau: lane holds y[t = 16tt + c][p = 16w + 4g + i]
+      // ---- store y for block tau: lane holds y[t = 16tt + c][p = 16 y_pt + 4g + i]
       typedef typename Vec<TY>::x4 Y4;
       TY* yb = reinterpret_cast<TY*>(A.y) + ((size_t)b * Tlen + c0) * HPsz + (size_t)h * kP +
-               16 * wave + 4 * g4;
+               16 * y_pt + 4 * g4;
 #pragma unroll
-      for (int tt = 0; tt < BT / 16; ++tt) {
-        const int tl = cur.tau * BT + 16 * tt + c;
+      for (int j = 0; j < YTW; ++j) {
+        const int tl = cur.tau * BT + 16 * (y_t0 + 2 * j) + c;
         if (tl < Lc) {
           Y4 o;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[tt][i]);
+          for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[j][i]);
           *reinterpret_cast<Y4*>(yb + (size_t)tl * HPsz) = o;
         }
       }
@@ -455,12 +516,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs A) {
   }
   if (dst) {
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni)
+    for (int a = 0; a < NTW; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = 16 * ni + 4 * g4 + i;
-        if (n < N) dst[(size_t)n * kP + pcol] = Hr[ni][i];
-      }
+      for (int pp = 0; pp < PTW; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * (n_t0 + a) + 4 * g4 + i, p = 16 * (p_t0 + pp) + c;
+          if (n < N) dst[(size_t)n * kP + p] = Hr[a][pp][i];
+        }
   }
 }
 
@@ -552,7 +615,7 @@ static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStre
   if (err != hipSuccess) return err;
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
-    hipLaunchKernelGGL(k1, dim3(g.H, g.segs - 1, g.Bt), dim3(256), l1, s, args);
+    hipLaunchKernelGGL(k1, dim3(g.H, g.segs - 1, g.Bt), dim3(kScanThreads), l1, s, args);
     prof_end(s);
     const int NPsz = g.N * g.P;
     prof_begin("scan_state_pass", s);
@@ -561,7 +624,7 @@ static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStre
     prof_end(s);
   }
   prof_begin("scan_chunk_output", s);
-  hipLaunchKernelGGL(k3, dim3(g.H, g.segs, g.Bt), dim3(256), l3, s, args);
+  hipLaunchKernelGGL(k3, dim3(g.H, g.segs, g.Bt), dim3(kScanThreads), l3, s, args);
   prof_end(s);
   return hipGetLastError();
 }
