@@ -172,7 +172,8 @@ hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_ex
   dm.M = M;
   const ProjWs lay = proj_ws(dm);
   const int pairs = (int)(M * d.k);
-  const int bm = proj_bm(pairs, (int)d.E);
+  int bm = proj_bm(pairs, (int)d.E);
+  if (!d.bf16 && bm > 128) bm = 128;  // fp32 tiles of 256 x 256 do not fit LDS
   int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + lay.offsets);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);

@@ -7,7 +7,8 @@
 //
 // Grouped GEMM over active pairs only. The bucketing kernels give every expert
 // a contiguous list of (token, slot) pairs; each workgroup owns BM pairs of one
-// expert and BN = 128 of the W = H*P + 2*G*N output columns:
+// expert and BN of the W = H*P + 2*G*N output columns (256 x 256 with 8 waves
+// for large groups, smaller tiles when an expert has few rows):
 //     Z[r, c] = sum_d u[token(r), d] * W_e[c, d]
 // Both operands are contiguous along d, so global loads are 16 bytes per lane
 // and the tiles sit in LDS in [row][d] order, which is exactly the fragment
@@ -19,56 +20,79 @@
 //     c <  H*P          -> X_hat[token, slot, c]            (S)
 //     c <  H*P + G*N    -> B_hat[token, slot, .] = w * Z     (S, w folded)
 //     otherwise         -> c_part[token, slot, .] = w * Z    (fp32)
-// and a last small kernel sums c_part over the slots in slot order
-// (0..k-1, fp32) into C_mix, so C~ never depends on which workgroup ran first.
+// written as whole row segments after staging each wave's results in LDS; a
+// last small kernel sums c_part over the slots in slot order (0..k-1, fp32)
+// into C_mix, so C~ never depends on which workgroup ran first.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace swimba {
 
-constexpr int kBN = 128;
+// Tile configurations: BM pairs x BN columns per workgroup, WM x WN waves, each
+// wave computing (BM/WM) x (BN/WN) with 16x16x32 matrix-core tiles.
+template <int BM_, int BN_, int WM_, int WN_>
+struct ProjCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NTH = 64 * NW;
+  static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+};
+typedef ProjCfg<256, 256, 2, 4> ProjBig;    // large expert groups (prefill), 8 waves
+typedef ProjCfg<128, 128, 2, 2> ProjMid;
+typedef ProjCfg<64, 128, 1, 4> ProjSmall;  // few rows per expert (decode)
 
-int proj_bm(int pairs, int E) { return (pairs / (E > 0 ? E : 1)) >= 96 ? 128 : 64; }
+int proj_bm(int pairs, int E) {
+  const int per = pairs / (E > 0 ? E : 1);
+  return per >= 192 ? 256 : (per >= 96 ? 128 : 64);
+}
 
 int proj_row_tiles_max(int pairs, int E, int bm) { return (pairs + bm - 1) / bm + E; }
 
 // K-tile depth: 64 for 2-byte inputs, 32 for fp32 (same bytes per row).
 template <typename T> struct ProjK { static constexpr int BK = sizeof(T) == 2 ? 64 : 32; };
 
-template <typename T, int BM>
+template <typename T, class C>
 struct ProjLds {
   static constexpr int BK = ProjK<T>::BK;
-  static constexpr int LDK = BK + 8;  // LDS row stride in elements
-  static constexpr size_t bytes = (size_t)2 * (BM + kBN) * LDK * sizeof(T);
+  static constexpr int LDK = BK + 8;          // LDS row stride of the K tiles (elements)
+  static constexpr int RR = C::TM >= 4 ? 4 : C::TM;  // epilogue row tiles per round
+  static constexpr int EPS = C::TN * 16 + 4;  // epilogue row stride (floats)
+  static constexpr size_t main_bytes = (size_t)2 * (C::BM + C::BN) * LDK * sizeof(T);
+  static constexpr size_t epi_bytes = (size_t)C::NW * RR * 16 * EPS * sizeof(float);
+  static constexpr size_t bytes = main_bytes > epi_bytes ? main_bytes : epi_bytes;
 };
 
-template <typename T, int BM>
-__global__ __launch_bounds__(256) void proj_kernel(
+template <typename T, class C>
+__global__ __launch_bounds__(C::NTH) void proj_kernel(
     const T* __restrict__ u, const T* __restrict__ wexp, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_offsets,
     const float* __restrict__ topk_w, int M, int D, int W, int HP, int GN, int E, int k,
-    typename StreamOf<T>::type* __restrict__ X_hat, typename StreamOf<T>::type* __restrict__ B_hat,
-    float* __restrict__ c_part) {
+    int ntiles, typename StreamOf<T>::type* __restrict__ X_hat,
+    typename StreamOf<T>::type* __restrict__ B_hat, float* __restrict__ c_part) {
   typedef typename StreamOf<T>::type S;
-  constexpr int BK = ProjK<T>::BK, LDK = ProjLds<T, BM>::LDK;
+  typedef ProjLds<T, C> Lay;
+  constexpr int BM = C::BM, BN = C::BN, NTH = C::NTH, TM = C::TM, TN = C::TN;
+  constexpr int BK = Lay::BK, LDK = Lay::LDK;
   constexpr int CH = BK / 8;                 // 8-element chunks per row and K tile
-  constexpr int WAVES_M = BM / 64;           // 2 (BM=128) or 1 (BM=64)
-  constexpr int WAVES_N = 4 / WAVES_M;       // 2 or 4
-  constexpr int WN = kBN / WAVES_N;          // 64 or 32
-  constexpr int TM = 4, TN = WN / 16;        // 16x16 tiles per wave
-  constexpr int AU = BM * CH / 256;          // A chunks per thread per K tile
-  constexpr int BU = kBN * CH / 256;         // B chunks per thread per K tile
+  constexpr int AU = BM * CH / NTH;          // A chunks per thread per K tile
+  constexpr int BU = BN * CH / NTH;          // B chunks per thread per K tile
   typedef typename Vec<T>::x8 F;
 
   extern __shared__ __align__(16) unsigned char lds_raw[];
   T* As = reinterpret_cast<T*>(lds_raw);              // [2][BM][LDK]
-  T* Bs = As + 2 * BM * LDK;                          // [2][kBN][LDK]
+  T* Bs = As + 2 * BM * LDK;                          // [2][BN][LDK]
   __shared__ int rtok[BM];
   __shared__ int rslot[BM];
   __shared__ float rw[BM];
   __shared__ int sh_e, sh_row0, sh_nrows;
 
-  const int tile = blockIdx.x;
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
+  // XCD x the contiguous logical range [x * per, (x + 1) * per): its tiles
+  // share an expert's weights and, column tile fastest, a row tile of tokens.
+  const int CT = (W + BN - 1) / BN;
+  const int per = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (logical >= ntiles) return;
+  const int tile = logical / CT, ctile = logical % CT;
   if (threadIdx.x == 0) {
     int e = -1;
     if (tile < tile_offsets[E]) {
@@ -88,7 +112,7 @@ __global__ __launch_bounds__(256) void proj_kernel(
   const int e = sh_e;
   if (e < 0) return;
   const int row0 = sh_row0, nrows = sh_nrows;
-  for (int r = threadIdx.x; r < BM; r += 256) {
+  for (int r = threadIdx.x; r < BM; r += NTH) {
     if (r < nrows) {
       const int p = sorted[row0 + r];
       rtok[r] = p / k;
@@ -102,11 +126,11 @@ __global__ __launch_bounds__(256) void proj_kernel(
   }
   __syncthreads();
 
-  const int col0 = blockIdx.y * kBN;
+  const int col0 = ctile * BN;
   const T* We = wexp + (size_t)e * W * D;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wm = wave / C::WN, wn = wave % C::WN;
 
   // Per-thread byte offsets of the A (gathered tokens) and B (weight) chunks;
   // out-of-range chunks read zeros through the buffer resources.
@@ -117,14 +141,14 @@ __global__ __launch_bounds__(256) void proj_kernel(
   int ach[AU], bch[BU];
 #pragma unroll
   for (int i = 0; i < AU; ++i) {
-    const int q = threadIdx.x + 256 * i, r = q / CH;
+    const int q = threadIdx.x + NTH * i, r = q / CH;
     ach[i] = q % CH;
     const int tok = rtok[r];
     aoff[i] = tok >= 0 ? ((uint32_t)tok * D + 8 * ach[i]) * ES : kOOB;
   }
 #pragma unroll
   for (int i = 0; i < BU; ++i) {
-    const int q = threadIdx.x + 256 * i, r = q / CH;
+    const int q = threadIdx.x + NTH * i, r = q / CH;
     bch[i] = q % CH;
     const int col = col0 + r;
     boff[i] = col < W ? ((uint32_t)col * D + 8 * bch[i]) * ES : kOOB;
@@ -140,15 +164,15 @@ __global__ __launch_bounds__(256) void proj_kernel(
   };
   auto store_tile = [&](int buf) {
     T* a = As + buf * BM * LDK;
-    T* bb = Bs + buf * kBN * LDK;
+    T* bb = Bs + buf * BN * LDK;
 #pragma unroll
     for (int i = 0; i < AU; ++i) {
-      const int q = threadIdx.x + 256 * i, r = q / CH, ch = q % CH;
+      const int q = threadIdx.x + NTH * i, r = q / CH, ch = q % CH;
       store8<T>(&a[r * LDK + 8 * ch], areg[i]);
     }
 #pragma unroll
     for (int i = 0; i < BU; ++i) {
-      const int q = threadIdx.x + 256 * i, r = q / CH, ch = q % CH;
+      const int q = threadIdx.x + NTH * i, r = q / CH, ch = q % CH;
       store8<T>(&bb[r * LDK + 8 * ch], breg[i]);
     }
   };
@@ -165,46 +189,63 @@ __global__ __launch_bounds__(256) void proj_kernel(
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) load_tile((kt + 1) * BK);  // next tile in flight during compute
     __syncthreads();  // tile kt is in LDS; everyone is done with tile kt - 1
-    const T* a = As + (kt & 1) * BM * LDK;
-    const T* bb = Bs + (kt & 1) * kBN * LDK;
+    const T* a = As + (kt & 1) * BM * LDK + (wm * TM * 16 + c) * LDK + 8 * g;
+    const T* bb = Bs + (kt & 1) * BN * LDK + (wn * TN * 16 + c) * LDK + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      F af[TM], bfr[TN];
+      F bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = load8<T>(&a[(wm * 64 + i * 16 + c) * LDK + 32 * ks + 8 * g]);
+      for (int j = 0; j < TN; ++j) bfr[j] = load8<T>(bb + j * 16 * LDK + 32 * ks);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = load8<T>(&bb[(wn * WN + j * 16 + c) * LDK + 32 * ks + 8 * g]);
+      for (int i = 0; i < TM; ++i) {
+        const F af = load8<T>(a + i * 16 * LDK + 32 * ks);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mma16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mma16(af, bfr[j], acc[i][j]);
+      }
     }
     if (kt + 1 < nk) store_tile((kt + 1) & 1);
   }
 
-  // Epilogue: lane holds Z[4g + q][c] of every 16x16 tile.
+  // ---- epilogue through LDS: each wave stages RR row tiles x TN column tiles
+  // of fp32 results, then writes whole row segments (4 columns per lane).
+  constexpr int RR = Lay::RR, EPS = Lay::EPS;
+  float* ep = reinterpret_cast<float*>(lds_raw) + (size_t)wave * RR * 16 * EPS;
+  __syncthreads();  // the K tiles are no longer read
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int round = 0; round < TM / RR; ++round) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = wm * 64 + i * 16 + 4 * g + q;
+    for (int i = 0; i < RR; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ep[(16 * i + 4 * g + q) * EPS + 16 * j + c] = acc[round * RR + i][j][q];
+    __syncthreads();
+    constexpr int CPR = TN * 4;  // 4-column chunks per staged row
+    for (int it = lane; it < RR * 16 * CPR; it += 64) {
+      const int rl = it / CPR, ch = it % CPR;
+      const int r = wm * TM * 16 + round * RR * 16 + rl;
+      const int col = col0 + wn * TN * 16 + 4 * ch;
       const int tok = rtok[r];
-      if (tok < 0) continue;
+      if (tok < 0 || col >= W) continue;
       const size_t pair = (size_t)tok * k + rslot[r];
-      const float w = rw[r];
+      const floatx4 v = *reinterpret_cast<const floatx4*>(&ep[rl * EPS + 4 * ch]);
+      typedef typename Vec<S>::x4 S4;
+      if (col < HP) {
+        S4 o;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = col0 + wn * WN + j * 16 + c;
-        const float z = acc[i][j][q];
-        if (col < HP) {
-          X_hat[pair * HP + col] = from_f32<S>(z);
-        } else if (col < HP + GN) {
-          B_hat[pair * GN + (col - HP)] = from_f32<S>(w * z);
-        } else if (col < W) {
-          c_part[pair * GN + (col - HP - GN)] = w * z;
-        }
+        for (int q = 0; q < 4; ++q) o[q] = from_f32<S>(v[q]);
+        *reinterpret_cast<S4*>(&X_hat[pair * HP + col]) = o;
+      } else if (col < HP + GN) {
+        const float w = rw[r];
+        S4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = from_f32<S>(w * v[q]);
+        *reinterpret_cast<S4*>(&B_hat[pair * GN + (col - HP)]) = o;
+      } else {
+        *reinterpret_cast<floatx4*>(&c_part[pair * GN + (col - HP - GN)]) = v * rw[r];
       }
     }
+    __syncthreads();
   }
 }
 
@@ -225,6 +266,28 @@ __global__ __launch_bounds__(256) void mix_c_kernel(const float* __restrict__ c_
   for (int q = 0; q < 4; ++q) C_mix[m * GN + n + q] = from_f32<T>(s[q]);
 }
 
+template <typename T, class C>
+static hipError_t launch_proj_cfg(const ProjGeom& g, const T* u, const T* wexp,
+                                  const int32_t* sorted, const int32_t* offsets,
+                                  const int32_t* tile_offsets, const float* w,
+                                  typename StreamOf<T>::type* B_hat,
+                                  typename StreamOf<T>::type* X_hat, float* c_part,
+                                  hipStream_t s) {
+  const int pairs = g.M * g.k;
+  const int ntiles = proj_row_tiles_max(pairs, g.E, C::BM) * ((g.W + C::BN - 1) / C::BN);
+  const dim3 grid((unsigned)((ntiles + 7) / 8 * 8));  // a multiple of the 8 XCDs
+  const size_t lds = ProjLds<T, C>::bytes;
+  hipError_t err = hipFuncSetAttribute((const void*)proj_kernel<T, C>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  prof_begin("expert_project", s);
+  hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), lds, s, u, wexp, sorted, offsets,
+                     tile_offsets, w, g.M, g.D, g.W, g.HP(), g.GN(), g.E, g.k, ntiles, X_hat,
+                     B_hat, c_part);
+  prof_end(s);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
                                    const int32_t* sorted, const int32_t* offsets,
@@ -233,20 +296,22 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
                                    typename StreamOf<T>::type* X_hat, float* c_part,
                                    typename StreamOf<T>::type* C_mix, hipStream_t s) {
   typedef typename StreamOf<T>::type S;
-  const int pairs = g.M * g.k;
-  const dim3 grid(proj_row_tiles_max(pairs, g.E, bm), (g.W + kBN - 1) / kBN);
-  const size_t lds = bm == 128 ? ProjLds<T, 128>::bytes : ProjLds<T, 64>::bytes;
-  const void* kfn = bm == 128 ? (const void*)proj_kernel<T, 128> : (const void*)proj_kernel<T, 64>;
-  hipError_t err = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t err;
+  if constexpr (sizeof(T) == 2) {
+    // the 256 x 256 tile needs 2-byte K tiles to fit LDS
+    if (bm == 256)
+      err = launch_proj_cfg<T, ProjBig>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+    else if (bm == 128)
+      err = launch_proj_cfg<T, ProjMid>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+    else
+      err = launch_proj_cfg<T, ProjSmall>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+  } else {
+    if (bm >= 128)
+      err = launch_proj_cfg<T, ProjMid>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+    else
+      err = launch_proj_cfg<T, ProjSmall>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+  }
   if (err != hipSuccess) return err;
-  prof_begin("expert_project", s);
-  if (bm == 128)
-    hipLaunchKernelGGL((proj_kernel<T, 128>), grid, dim3(256), lds, s, u, wexp, sorted, offsets,
-                       tile_offsets, w, g.M, g.D, g.W, g.HP(), g.GN(), g.E, g.k, X_hat, B_hat, c_part);
-  else
-    hipLaunchKernelGGL((proj_kernel<T, 64>), grid, dim3(256), lds, s, u, wexp, sorted, offsets,
-                       tile_offsets, w, g.M, g.D, g.W, g.HP(), g.GN(), g.E, g.k, X_hat, B_hat, c_part);
-  prof_end(s);
   if (!C_mix) return hipGetLastError();
   const size_t n4 = (size_t)g.M * g.GN() / 4;
   prof_begin("mix_c", s);
