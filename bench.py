@@ -33,6 +33,66 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+CALIB_BYTES = 256 << 20     # plain device-to-device copy used to scale HBM counters
+CALIB_COPIES = 3
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "selective_ssm_parameter_amd", "csrc")
+# Kernel symbol pattern -> the name the library's profiler gives the launch.
+KERNEL_NAMES = [
+    (r"route_kernel", "route_topk"),
+    (r"bucket_count_kernel", "bucket_count"),
+    (r"bucket_place_kernel", "bucket_place"),
+    (r"proj_kernel", "expert_project"),
+    (r"mix_c_kernel", "mix_c"),
+    (r"scan_kernel.*Lb0E", "scan_segment_state"),
+    (r"scan_combine_kernel", "scan_state_pass"),
+    (r"scan_kernel.*Lb1E", "scan_chunk_output"),
+    (r"state_copy_kernel", "state_copy"),
+    (r"decode_state_kernel", "decode_state"),
+    (r"copyBuffer", "copy (runtime blit)"),
+]
+# Sources a kernel's machine code depends on (a change voids stored counters).
+KERNEL_SOURCES = {
+    "route_topk": ["route.hip"],
+    "expert_project": ["project.hip"],
+    "scan_chunk_output": ["scan.hip"],
+}
+
+
+def kernel_label(symbol):
+    import re
+    for pat, name in KERNEL_NAMES:
+        if re.search(pat, symbol):
+            return name
+    return symbol[:60]
+
+
+def source_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + ["common.hpp", "launch.hpp"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(wl_name):
+    return os.path.join(PROFILES, f"swimba_step_{wl_name}_hbm_traffic.md")
+
+
+def stored_traffic(kernel, wl_name):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary,
+    or None when there is none or the kernel's sources changed since."""
+    path = traffic_file(wl_name)
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == "traffic:" and parts[1] == kernel:
+            return int(parts[2]) if parts[3] == source_digest(kernel) else None
+    return None
+
+
 def workload(name):
     from selective_ssm_parameter_amd import synth
     return synth.WORKLOADS[name]
@@ -136,6 +196,16 @@ def run_gpu(args):
     sb.profile_enable(False)
     sb.profile_select(None)
 
+    if args.copy_calibration:
+        # A plain copy of known size, last in the process, to scale the HBM
+        # byte counters of the kernels above.
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(CALIB_COPIES):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
     tokens = wl.tokens + wl.batch
     value = tokens * args.steps / elapsed
     bound, flops, nbytes = models[dom]
@@ -144,12 +214,14 @@ def run_gpu(args):
         achieved = flops / avg_s / 1e12
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": stored_traffic(dom, wl.name),
                 "algorithmic_flops": flops, "avg_us": avg_s * 1e6}
     else:
         achieved = nbytes / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "traffic": stored_traffic(dom, wl.name),
                 "algorithmic_bytes": nbytes, "avg_us": avg_s * 1e6}
     return {
         "wl": wl, "value": value, "elapsed": elapsed, "kernels": kernels, "roofline": roof,
@@ -182,6 +254,119 @@ def cpu_baseline(wl, budget_s=20.0):
                       f"prefill only, {spent:.1f} s"}
 
 
+def find_csv(d, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        sys.exit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def summarize_trace(trace_dir, wl_name, out, command, bench_json=None):
+    """Per-kernel durations from a ``rocprofv3 --kernel-trace --stats`` run,
+    grouped by kernel and grid size (prefill and decode launch the same
+    kernels on different grids)."""
+    import csv
+    import collections
+    rows = list(csv.DictReader(open(find_csv(trace_dir, "kernel_trace.csv"))))
+    groups = collections.OrderedDict()
+    for r in rows:
+        key = (kernel_label(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"])
+               * int(r["Grid_Size_Z"]) // max(1, int(r["Workgroup_Size_X"])
+                                            * int(r["Workgroup_Size_Y"])
+                                            * int(r["Workgroup_Size_Z"])))
+        groups.setdefault(key, []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in groups.values())
+    stats = find_csv(trace_dir, "kernel_stats.csv")
+    lines = [f"# Kernel durations, bench step (prefill + decode) on workload {wl_name}", "",
+             "Command (from the repository root, after building the library):", "",
+             "    " + command, "",
+             f"Source: `{os.path.basename(stats)}` and the kernel trace of that run; "
+             "durations in microseconds, grouped by kernel and workgroup count.", "",
+             "| kernel | workgroups | launches | avg us | min us | max us | share |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for (name, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {name} | {wgs} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
+                     f"{max(v):.1f} | {100 * sum(v) / total:.1f}% |")
+    if bench_json:
+        line = [ln for ln in open(bench_json) if ln.startswith("{")][-1]
+        roof = json.loads(line)["roofline"]
+        lines += ["", f"The JSON line of the same run reports, for its dominant kernel "
+                      f"{roof['kernel']}, an average of {roof['avg_us']:.1f} us per launch "
+                      f"(HIP events on the launch stream over the timed steps) and "
+                      f"{roof['achieved']:.1f} {roof['unit']} = {100 * roof['frac']:.1f}% "
+                      f"of the {roof['peak']:.0f} {roof['unit']} peak."]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(fetch_dir, write_dir, wl_name, out, commands):
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs, each scaled by
+    what the same counter reads for the trailing copy of CALIB_BYTES."""
+    import csv
+    import collections
+
+    def per_dispatch(d, counter):
+        vals, names = collections.defaultdict(float), {}
+        for r in csv.DictReader(open(find_csv(d, "counter_collection.csv"))):
+            if r["Counter_Name"] != counter:
+                continue
+            i = int(r["Dispatch_Id"])
+            vals[i] += float(r["Counter_Value"])
+            wgs = (int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+            names[i] = (kernel_label(r["Kernel_Name"]), wgs)
+        return vals, names
+
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals, names = per_dispatch(d, counter)
+        last_lib = max(i for i, n in names.items() if not n[0].startswith("copy"))
+        calib = [i for i, n in names.items() if n[0].startswith("copy") and i > last_lib]
+        if not calib:
+            sys.exit(f"no calibration copy after the last library kernel in {d}")
+        kib = sum(vals[i] for i in calib) / CALIB_COPIES
+        scale = CALIB_BYTES / (kib * 1024.0)
+        by = collections.defaultdict(list)
+        known = {name for _, name in KERNEL_NAMES}
+        for i, n in names.items():
+            if i not in calib and n[0] in known and not n[0].startswith("copy"):
+                by[n].append(vals[i] * 1024.0 * scale)
+        res[counter] = (kib, scale, {k: sum(v) / len(v) for k, v in by.items()})
+    fk, fs, fetch = res["FETCH_SIZE"]
+    wk, ws_, write = res["WRITE_SIZE"]
+    wl = workload(wl_name)
+    models = kernel_models(wl)
+    lines = [f"# HBM traffic per launch, bench step on workload {wl_name}", "",
+             "Commands (from the repository root, after building the library):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["",
+              f"Calibration: the run ends with {CALIB_COPIES} device copies of "
+              f"{CALIB_BYTES >> 20} MiB; per copy FETCH_SIZE read {fk:.0f} KiB (scale {fs:.4f}) "
+              f"and WRITE_SIZE {wk:.0f} KiB (scale {ws_:.4f}). Counter KiB x 1024 x scale "
+              "= bytes.", "",
+              "Launches on the larger grid are the prefill's, those on the smaller one the "
+              "decode step's; the algorithmic bytes are those of the prefill launch.", "",
+              "| kernel | workgroups | read MB | written MB | traffic MB | algorithmic MB |",
+              "|---|---:|---:|---:|---:|---:|"]
+    keys = sorted(set(fetch) | set(write), key=lambda k: -(fetch.get(k, 0) + write.get(k, 0)))
+    best = {}
+    for k in keys:
+        rd, wr = fetch.get(k, 0.0), write.get(k, 0.0)
+        big = k[0] in models and k[1] == max(kk[1] for kk in keys if kk[0] == k[0])
+        alg = f"{models[k[0]][2] / 1e6:.1f}" if big else "-"
+        lines.append(f"| {k[0]} | {k[1]} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+                     f"{(rd + wr) / 1e6:.1f} | {alg} |")
+        if k[0] in KERNEL_SOURCES and (k[0] not in best or k[1] > best[k[0]][0]):
+            best[k[0]] = (k[1], rd + wr)
+    lines += ["", "Machine-readable (kernel, bytes per launch at the prefill grid, "
+              "digest of the sources the kernel is built from):", ""]
+    for k, (_, b) in sorted(best.items()):
+        lines.append(f"traffic: {k} {int(round(b))} {source_digest(k)}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,7 +374,26 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with copies of known size (scales HBM counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write a markdown summary of a rocprofv3 kernel-trace run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM traffic summary of two rocprofv3 --pmc runs")
+    ap.add_argument("--out", help="summary file to write")
+    ap.add_argument("--bench-json", help="the JSON output of the profiled bench run")
+    ap.add_argument("--command", action="append", default=[],
+                    help="the command(s) that produced the profile, for the summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.config,
+                        args.out or os.path.join(PROFILES, f"swimba_step_{args.config}_kernel_trace.md"),
+                        " ".join(args.command), args.bench_json)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config,
+                      args.out or traffic_file(args.config), args.command)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
