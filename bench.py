@@ -44,6 +44,7 @@ KERNEL_NAMES = [
     (r"bucket_place_kernel", "bucket_place"),
     (r"proj_kernel", "expert_project"),
     (r"mix_c_kernel", "mix_c"),
+    (r"scan_gram_kernel", "scan_gram"),
     (r"scan_kernel.*Lb0E", "scan_segment_state"),
     (r"scan_combine_kernel", "scan_state_pass"),
     (r"scan_kernel.*Lb1E", "scan_chunk_output"),

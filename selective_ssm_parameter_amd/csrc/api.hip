@@ -134,7 +134,7 @@ DecWs dec_ws(const Dims& d) {
 
 size_t scan_bytes(const Dims& d) {
   return scan_ws_bytes(scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
-                                 (int)d.k, (int)d.L));
+                                 (int)d.k, (int)d.L, (int)d.esize));
 }
 
 swimba_status check_ws(void* ws, size_t have, size_t need) {
@@ -323,7 +323,7 @@ swimba_status swimba_ssd_chunk_scan(const swimba_dims* dims, const void* B_hat,
   }
   if ((st = check_ws(ws, ws_bytes, scan_bytes(d))) != SWIMBA_OK) return st;
   const ScanGeom g = scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
-                               (int)d.k, (int)d.L);
+                               (int)d.k, (int)d.L, (int)d.esize);
   return hip_status(launch_scan(d.bf16, g, B_hat, X_hat, C_mix, a, h_init, y, h_final,
                                 static_cast<float*>(ws), stream),
                     "ssd_chunk_scan launch");

@@ -48,11 +48,11 @@ hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const 
 // Chunked scan.
 struct ScanGeom {
   int Bt, T, H, G, N, P, k, L;
+  int es;            // bytes per stream element (2: fp16, 4: fp32)
   int segs;          // segments per sequence
   int seg_chunks;    // chunks per segment
 };
-ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L);
-int scan_block_tokens();
+ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es);
 size_t scan_ws_bytes(const ScanGeom& g);
 hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
                        const void* C_mix, const float* a, const float* h_init, void* y,

@@ -1,0 +1,88 @@
+// LDS tile helpers for the scan: buffer-to-LDS copies of row-major tiles with an
+// XOR chunk swizzle, and K-major matrix-core fragments read back from them with
+// the gfx950 transposing LDS read.
+#pragma once
+
+#include "common.hpp"
+
+namespace swimba {
+
+// Swizzles (16-byte chunk index XOR, 2-byte element types; none for fp32).
+// Tiles read with transposing loads (X, B): a 64-lane read touches rows
+// {0..3, 8..11, 16..19, 24..27} (+4) and two adjacent chunks per row; the XOR
+// gives rows that share bank positions distinct chunk pairs.
+template <typename T, int CPR>
+__device__ __forceinline__ int swz_tr(int r) {
+  if constexpr (sizeof(T) != 2) return 0;
+  else if constexpr (CPR >= 16) return 2 * ((r & 3) | ((r >> 1) & 4));
+  else if constexpr (CPR == 8) return 2 * (((r >> 1) & 1) | ((r >> 2) & 2));
+  else return 2 * ((r >> 3) & 1);
+}
+// Tiles read by rows (C~, G): 16 consecutive rows, one chunk each.
+template <typename T, int CPR>
+__device__ __forceinline__ int swz_row(int t) {
+  if constexpr (sizeof(T) != 2) return 0;
+  else return (t / (16 / CPR)) & (CPR - 1);
+}
+
+// Buffer-to-LDS copy of a row-major tile: NROWS rows of CPR 16-byte chunks,
+// global row r at byte offset base + r * pitch, chunk c at + 16 c. Chunk c of
+// row r lands at LDS byte (r * CPR + (c ^ swz(r))) * 16 of dst. Rows >= rvalid
+// and chunks >= cvalid are read as zeros. Each instruction of a wave moves 64
+// consecutive LDS chunks; the 4 waves take turns.
+template <int NROWS, int CPR, class Swz>
+__device__ __forceinline__ void dma_tile(BufRes rs, uint32_t base, uint32_t pitch,
+                                         unsigned char* dst, int rvalid, int cvalid, int wave,
+                                         int lane, Swz swz) {
+  static_assert((NROWS * CPR) % 64 == 0, "tile must be whole 64-chunk groups");
+  constexpr int NI = NROWS * CPR / 64;
+#pragma unroll
+  for (int i0 = 0; i0 < NI; i0 += 4) {
+    const int i = i0 + wave;
+    if (i < NI) {
+      const int slot = 64 * i + lane;
+      const int r = slot / CPR, pc = slot % CPR;
+      const int lc = pc ^ swz(r);
+      const uint32_t off = (r < rvalid && lc < cvalid) ? base + r * pitch + 16 * lc : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, off, 0, 0, 0);
+    }
+  }
+}
+
+// A K-major operand fragment from a row-major [k][col] LDS tile: lane (g, c)
+// gets rows k0 + 8g .. k0 + 8g + 7 of column col0 + c. 2-byte types use two
+// transposing reads (in a 16-lane group, lane i receives element i % 4 of the
+// 4-element row pieces addressed by lanes i / 4 + 4 m, m = 0..3); fp32 reads
+// the 8 elements one by one.
+template <typename T, int CPR>
+__device__ __forceinline__ typename Vec<T>::x8 load_kmajor(const unsigned char* tile, int k0,
+                                                           int col0, int lane) {
+  typedef typename Vec<T>::x8 F;
+  const int g = lane >> 4, c = lane & 15;
+  F v;
+  if constexpr (sizeof(T) == 2) {
+    typedef short s4 __attribute__((__vector_size__(8)));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = k0 + 8 * g + 4 * hh + (c >> 2);
+      const int col = col0 + 4 * (c & 3);                 // element column of this lane's piece
+      const int ch = col >> 3, half = (col >> 2) & 1;      // 16-byte chunk, 8-byte half
+      const unsigned char* p = tile + (r * CPR + (ch ^ swz_tr<T, CPR>(r))) * 16 + 8 * half;
+      const typename Vec<T>::x4 w4 = __builtin_bit_cast(
+          typename Vec<T>::x4,
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(p)));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) v[4 * hh + m] = w4[m];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = k0 + 8 * g + j, col = col0 + c;
+      v[j] = *reinterpret_cast<const T*>(tile + r * CPR * 16 + col * (int)sizeof(T));
+    }
+  }
+  return v;
+}
+
+}  // namespace swimba

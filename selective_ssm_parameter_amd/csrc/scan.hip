@@ -10,37 +10,42 @@
 //         + sum_{r : s <= t} a^{t-s} (C~_t . B_hat_r) X_r          (intra)
 //   H'    = a^{Lc} H + sum_r a^{c0+Lc-1-s} B_hat_r X_r^T          (carry)
 // U~_t = sum_j B_hat_{t,j} X_{t,j}^T is never formed: the contraction runs over
-// the k-concatenated pair axis (k*BT rows per block of BT tokens).
+// the k-concatenated pair axis (k*BT rows per block of BT = 32 tokens).
 //
-// Work split (MI355X-first rather than the three separate SSD passes of the
-// prior art): a workgroup owns (sequence, segment of chunks, head). It walks
-// its chunks in order with the state in fp32 registers, so per-chunk states
-// never go to HBM. Segments of one sequence run in parallel; their boundary
-// states come from two small passes:
-//   pass 1: every segment but the last computes its end state from zero
-//           (the carry recurrence only) into the workspace;
-//   pass 2: per (sequence, head, element), a sequential, coalesced sweep over
-//           segments: Hin_0 = h_init, Hin_{s+1} = a^{len_s} Hin_s + S_s;
-//   pass 3: every segment recomputes its chunks from Hin_s and writes y; the
-//           last segment also writes h_final.
-//
-// Wave w of the 4 owns output columns p in [16w, 16w+16): its slice of H and of
-// the carry lives in matrix-core accumulator layout (rows n, column p), which
-// is also the A-operand layout of the readout C~ H once the contraction order
-// over n is permuted to {4g..4g+3, 16+4g..16+4g+3} per 32-step (the C~ operand
-// is read in the same permuted order). Per block pair (tau, sigma):
-//   Gram^T[r, t] = B_hat_r . C~_t          (matrix cores, K = N)
-//   Gm[t, r]     = Gram^T[r, t] a^{t-s}, zero above the diagonal (LDS table)
-//   y^T         += X^T Gm^T                 (K = pairs)
-//   carry       += B_hat^T (decay * X)      (K = pairs, diagonal block only)
+// Kernels (MI355X-first rather than the three separate SSD passes of the prior
+// art):
+//   scan_gram:   G[t, r] = C~_t . B_hat_r for every causal block pair of every
+//                chunk, once per group: it does not depend on the head, so the
+//                heads of a group share it instead of recomputing it.
+//   pass 1:      (several segments per sequence only) every segment but the
+//                last computes its end state from zero, carry recurrence only;
+//   pass 2:      per (sequence, head, element), a sequential, coalesced sweep
+//                over segments: Hin_0 = h_init, Hin_{s+1} = a^{len_s} Hin_s + S_s;
+//   pass 3:      every segment walks its chunks from Hin_s and writes y; the
+//                last segment also writes h_final.
+// A workgroup of passes 1 and 3 is 4 waves and owns (sequence, segment, head);
+// wave w owns the head columns p in [16w, 16w + 16). Its slice of the state
+// lives in fp32 matrix-core accumulators (rows n, column p) for the whole
+// segment, so per-chunk states never go to HBM or LDS: the readout C~ H takes
+// its A operand straight from those registers, with the contraction over n
+// visited in the order {4g..4g+3, 16+4g..16+4g+3} per 32-step (and the C~
+// operand read in the same order). Per block pair (tau, sigma) of a chunk:
+//   y^T[p, t]  = a^{t+1} H^T C~^T                  (sigma = 0: readout)
+//   y^T[p, t] += X^T (G o decay)^T                 (intra, K = pairs)
+//   H[n, p]   += (a^{Lc-1-s} B_hat)^T X            (carry, last block row)
+// The carry of every block of a chunk is applied in the chunk's last block
+// row, after all readouts of the chunk have used the entering state.
 #include <cstdlib>
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_tiles.hpp"
 
 namespace swimba {
 
-constexpr int kP = 64;  // head dim served by these kernels
+constexpr int kP = 64;             // head dim served by these kernels
+constexpr int kBT = 32;            // tokens per block
+constexpr int kScanThreads = 256;  // 4 waves
 
 struct ScanArgs {
   const void* B_hat;
@@ -50,152 +55,179 @@ struct ScanArgs {
   const float* h_init;
   void* y;
   float* h_final;
-  float* ws;  // [Bt, segs, H, N, P] fp32 segment states
-  int T, H, G, N, k, L, segs, seg_chunks;
+  float* ws;          // [Bt, segs, H, N, P] fp32 segment states
+  const void* gram;   // [Bt, nc, G, npairs, kBT, k*kBT] Gram tiles (stream type)
+  int T, H, G, N, k, L, segs, seg_chunks, nc, npairs;
 };
 
-template <typename T, int NP, int KS, int BT, bool WITH_Y>
+// LDS of the walk: two stages, each holding one step's row-major tiles as they
+// arrive from HBM (copied by the buffer-to-LDS path, no registers involved):
+//   X   [R][64]   pair rows of this head's X_hat      (every step)
+//   B   [R][NP]   pair rows of B_hat                   (last block row: carry)
+//   C   [BT][NP]  token rows of C~                     (sigma = 0: readout)
+//   G   [BT][R]   the Gram tile of the block pair      (every step)
+// Rows are sequences of 16-byte chunks; chunk c of row r sits at c ^ swz(r).
+template <typename T, int NP, int KS, bool WITH_Y>
 struct ScanLds {
-  static constexpr int R = KS * BT;      // pair rows per block
-  static constexpr int LDN = NP + 8;     // row stride of [.][n] buffers
-  static constexpr int LDR = R + 8;      // row stride of [.][r] buffers
-  static constexpr int CS = WITH_Y ? BT * LDN : 0;   // C~ [t][n]
-  static constexpr int BS = WITH_Y ? R * LDN : 0;    // B_hat [r][n]
-  static constexpr int HS = WITH_Y ? kP * LDN : 0;   // entering state [p][n]
-  static constexpr int BST = NP * LDR;               // B_hat^T [n][r]
-  static constexpr int XST = kP * LDR;               // X^T [p][r]
-  static constexpr int GM = WITH_Y ? BT * LDR : 0;   // masked Gram [t][r]
-  static constexpr int ELEMS = CS + BS + HS + BST + XST + GM;
-  static constexpr size_t bytes = (size_t)ELEMS * sizeof(T) + 16 * sizeof(float);
+  static constexpr int R = KS * kBT;
+  static constexpr int XROW = kP * (int)sizeof(T), BROW = NP * (int)sizeof(T);
+  static constexpr int GROW = R * (int)sizeof(T);
+  static constexpr int XB = R * XROW, BB = R * BROW;
+  static constexpr int CB = WITH_Y ? kBT * BROW : 0, GB = WITH_Y ? kBT * GROW : 0;
+  static constexpr int XO = 0, BO = XB, CO = XB + BB, GO = XB + BB + CB;
+  static constexpr int STAGE = XB + BB + CB + GB;
+  static constexpr size_t bytes = 2 * (size_t)STAGE;
 };
-
-// Transposed [row][r] buffers store 8-element column chunks XOR-swizzled by the
-// row's 8-row group, so the 4-element column writes of the staging (rows 8
-// apart) land in different banks; readers apply the same swizzle.
-template <int R>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row >> 3) & (R / 8 - 1) & 7);
-}
 
 // a^d for integer d >= 0 from la = log2(a) (la = -1e30 encodes a = 0).
 __device__ __forceinline__ float apow(float la, int d) {
   return d == 0 ? 1.f : exp2f((float)d * la);
 }
 
+// Fragments (t-tile tt, pair k-step q) of a diagonal block pair: a fragment is
+// zero when every (t, r) in it has s > t; the others get a per-lane mask.
+template <int KS>
+struct DiagFrags {
+  static constexpr int TT = kBT / 16, RQ = KS;  // k-steps of 32 pairs per block
+  static constexpr bool zero(int tt, int q) { return 16 * tt + 15 - (32 * q) / KS < 0; }
+  static constexpr int index(int tt, int q) {
+    int n = 0;
+    for (int a = 0; a < TT; ++a)
+      for (int b = 0; b < RQ; ++b) {
+        if (a == tt && b == q) return zero(a, b) ? -1 : n;
+        if (!zero(a, b)) ++n;
+      }
+    return -1;
+  }
+  static constexpr int count() {
+    int n = 0;
+    for (int a = 0; a < TT; ++a)
+      for (int b = 0; b < RQ; ++b) n += zero(a, b) ? 0 : 1;
+    return n;
+  }
+};
+
 // One step of the walk over a segment: chunk ch, output block tau, source
-// block sig (sig <= tau). Pass 1 (no output) visits (ch, sig) with tau = sig.
+// block sig (sig <= tau). Pass 1 visits (ch, sig) with tau = the last block.
 struct ScanStep {
   int ch, tau, sig;
 };
 
-constexpr int kScanThreads = 512;  // 8 waves
-
-template <typename T, int NP, int KS, int BT, bool WITH_Y>
-struct ScanStage {
-  static constexpr int R = KS * BT;
-  static constexpr int NTH = kScanThreads;
-  static constexpr int CUN = (BT * (NP / 8) + NTH - 1) / NTH;        // C~ chunks per thread
-  static constexpr int BUN = ((R / 4) * (NP / 8) + NTH - 1) / NTH;   // B_hat 4x8 units
-  static constexpr int XUN = ((R / 4) * (kP / 8) + NTH - 1) / NTH;   // X 4x8 units
-  typedef typename Vec<T>::x8 F;
-  F cv[WITH_Y ? CUN : 1];
-  F bv[BUN][4];
-  F xv[XUN][4];
-};
-
-// Work split over the 8 waves.
-//  state / carry:  WVN x WVP waves over (n, p); a wave owns NTW x PTW 16x16 tiles
-//  y / readout:    4 p-tiles x TT t-tiles; a wave owns p-tile w%4, t-tiles w/4 + 2j
-//  Gram^T:         RT x TT tiles; a wave owns tiles w + 8m (same t-tile for all m)
-template <int NP, int BT, int R>
-struct ScanSplit {
-  static constexpr int NT = NP / 16;
-  static constexpr int WVN = NT < 4 ? NT : 4;
-  static constexpr int WVP = 8 / WVN;
-  static constexpr int NTW = NT / WVN;
-  static constexpr int PTW = 4 / WVP;
-  static constexpr int TT = BT / 16, RT = R / 16;
-  static constexpr int YTW = TT / 2;                   // t-tiles per wave (y)
-  static constexpr int GTW = (RT * TT + 7) / 8;        // Gram tiles per wave
-  static constexpr int RQ = R / 32;
-};
-
-template <typename T, typename TY, int NP, int KS, int BT, bool WITH_Y>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
-  typedef ScanLds<T, NP, KS, BT, WITH_Y> Lay;
-  typedef ScanStage<T, NP, KS, BT, WITH_Y> Stage;
-  constexpr int R = Lay::R, LDN = Lay::LDN, LDR = Lay::LDR;
-  typedef ScanSplit<NP, BT, R> Sp;
-  constexpr int NTW = Sp::NTW, PTW = Sp::PTW, YTW = Sp::YTW, GTW = Sp::GTW, RQ = Sp::RQ;
-  constexpr int TT = Sp::TT, RT = Sp::RT;
+// Gram tiles G[t, r] = C~[c0 + tau*BT + t] . B_hat[(c0 + sig*BT)*k + r] (fp32
+// accumulation, stored in the stream type) for one (block pair, chunk, batch).
+template <typename T, int NP, int KS>
+__global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_hat,
+                                                        const T* __restrict__ C_mix,
+                                                        T* __restrict__ gram, int Tlen, int G,
+                                                        int N, int L, int nc, int npairs) {
+  constexpr int BT = kBT, R = KS * BT, TT = BT / 16, RT = R / 16;
+  constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
   typedef typename Vec<T>::x4 F4;
+  const int grp = blockIdx.x % G, pidx = blockIdx.x / G, ch = blockIdx.y, b = blockIdx.z;
+  int tau = 0;
+  while ((tau + 1) * (tau + 2) / 2 <= pidx) ++tau;
+  const int sig = pidx - tau * (tau + 1) / 2;
+  const int c0 = ch * L, Lc = min(L, Tlen - c0);
+  if (tau * BT >= Lc) return;  // block beyond the (last, partial) chunk
+  const int GN = G * N;
+  const BufRes rB = make_rsrc(B_hat + (size_t)b * Tlen * KS * GN, (uint64_t)Tlen * KS * GN * ES);
+  const BufRes rC = make_rsrc(C_mix + (size_t)b * Tlen * GN, (uint64_t)Tlen * GN * ES);
+  const int wave = threadIdx.x >> 6, lane = lane_id(), g4 = lane >> 4, c = lane & 15;
+  T* out = gram + ((((size_t)b * nc + ch) * G + grp) * npairs + pidx) * (size_t)(BT * R);
+  for (int tix = wave; tix < RT * TT; tix += 4) {
+    const int rt = tix / TT, tt = tix % TT;
+    const int rl = sig * BT * KS + 16 * rt + c;  // pair row within the chunk
+    const int tl = tau * BT + 16 * tt + c;       // token within the chunk
+    const uint32_t rrow = (uint32_t)(c0 * KS + rl), trow = (uint32_t)(c0 + tl);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NP / 32; ++q) {
+      const int n0 = 32 * q + 8 * g4;
+      const F af = load8_buf<T>(rB, (rl < Lc * KS && n0 < N) ? (rrow * GN + grp * N + n0) * ES : kOOB);
+      const F bf = load8_buf<T>(rC, (tl < Lc && n0 < N) ? (trow * GN + grp * N + n0) * ES : kOOB);
+      acc = mma16(af, bf, acc);
+    }
+    // lane holds G[t = 16tt + c][r = 16rt + 4g + i]
+    F4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(acc[i]);
+    *reinterpret_cast<F4*>(&out[(16 * tt + c) * R + 16 * rt + 4 * g4]) = o;
+  }
+}
 
-  extern __shared__ __align__(16) unsigned char lds_raw[];
-  T* Cs = reinterpret_cast<T*>(lds_raw);
-  T* Bs = Cs + Lay::CS;
-  T* Hs = Bs + Lay::BS;
-  T* BsT = Hs + Lay::HS;
-  T* XsT = BsT + Lay::BST;
-  T* Gm = XsT + Lay::XST;
-  float* wmax = reinterpret_cast<float*>(Gm + Lay::GM);  // [8] per-wave max |H|
+template <typename T, typename TY, int NP, int KS, bool WITH_Y>
+__global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_kernel(ScanArgs A) {
+  typedef ScanLds<T, NP, KS, WITH_Y> Lay;
+  constexpr int BT = kBT, R = Lay::R;
+  constexpr int TT = BT / 16, RQ = R / 32, NT = NP / 16, NQ = NP / 32;
+  constexpr int XC = Lay::XROW / 16, BC = Lay::BROW / 16, GC = Lay::GROW / 16;  // chunks per row
+  typedef DiagFrags<KS> DF;
+  constexpr int NDF = DF::count() > 0 ? DF::count() : 1;
+  constexpr uint32_t ES = sizeof(T);
+  typedef typename Vec<T>::x8 F;
+
+  // two stages, separate arrays: the copies into one are known not to touch the
+  // tiles being read from the other
+  __shared__ __align__(16) unsigned char stage0[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stage1[Lay::STAGE];
 
   const int h = blockIdx.x, seg = blockIdx.y, b = blockIdx.z;
   const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
   const int grp = h / (H / G);
   const int GN = G * N;
-  const int tid = threadIdx.x;
-  const int lane = lane_id(), wave = tid >> 6;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = lane >> 4, c = lane & 15;
   const size_t NPsz = (size_t)N * kP;
   const size_t HPsz = (size_t)H * kP;
-
-  // this wave's tiles
-  const int n_t0 = (wave / Sp::WVP) * NTW;   // first n-tile of the state slice
-  const int p_t0 = (wave % Sp::WVP) * PTW;   // first p-tile of the state slice
-  const int y_pt = wave % 4;                 // y p-tile
-  const int y_t0 = wave / 4;                 // first y t-tile (then +2)
+  const int prow_x = 16 * w + c;  // this lane's head column p
 
   const float ah = A.a[h];
   const float la = ah > 0.f ? log2f(ah) : -1e30f;
 
-  constexpr uint32_t ES = sizeof(T);
   const BufRes rB = make_rsrc(reinterpret_cast<const T*>(A.B_hat) + (size_t)b * Tlen * KS * GN,
                               (uint64_t)Tlen * KS * GN * ES);
   const BufRes rX = make_rsrc(reinterpret_cast<const T*>(A.X_hat) + (size_t)b * Tlen * KS * HPsz,
                               (uint64_t)Tlen * KS * HPsz * ES);
   const BufRes rC = make_rsrc(reinterpret_cast<const T*>(A.C_mix) + (size_t)b * Tlen * GN,
                               (uint64_t)Tlen * GN * ES);
+  const size_t gtile = (size_t)BT * R;
+  const BufRes rG = make_rsrc(
+      reinterpret_cast<const T*>(A.gram) + (size_t)b * A.nc * G * A.npairs * gtile,
+      WITH_Y ? (uint64_t)A.nc * G * A.npairs * gtile * ES : 0);
 
-  // ---- decay tables for full chunks (Lc == L)
-  // carry: the transposed B_hat rows this thread stages are scaled by
-  // a^{Lc-1-s}; for a full chunk that is a^{(nb-1-sig) BT} * a^{BT-1-s_local}.
-  float cdb[Stage::BUN][4];
+  // ---- per-lane decay tables (constant over the segment)
+  // er[q][j] = a^{BT-1-s} for the pair row r = 32q + 8g + j of a block (s = r / k):
+  // the carry weight of that row relative to the block end, and the row factor
+  // of the off-diagonal intra term a^{dblk + t - s} = a^{dblk-(BT-1)} a^t a^{BT-1-s}.
+  F er[RQ];
 #pragma unroll
-  for (int u = 0; u < Stage::BUN; ++u) {
-    const int r0 = 4 * ((tid + kScanThreads * u) / (NP / 8));
+  for (int q = 0; q < RQ; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cdb[u][i] = apow(la, BT - 1 - (r0 + i) / KS);
-  }
-  float gmk[GTW][4];  // Gram mask of a diagonal block: a^{t-s} for t >= s, else 0
-  float al[YTW];      // readout decay a^{t+1} for the lane's t in block 0
+    for (int j = 0; j < 8; ++j) er[q][j] = from_f32<T>(apow(la, BT - 1 - (32 * q + 8 * g4 + j) / KS));
+  float at[WITH_Y ? TT : 1];   // a^t of the lane's output token t = 16tt + c
+  F dm[WITH_Y ? NDF : 1];      // diagonal block: a^{t-s} for s <= t, else 0
   if (WITH_Y) {
 #pragma unroll
-    for (int m = 0; m < GTW; ++m) {
-      const int tix = wave + 8 * m;
-      const int rt = tix / TT, tt = tix % TT;
+    for (int tt = 0; tt < TT; ++tt) at[tt] = apow(la, 16 * tt + c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = (16 * tt + c) - (16 * rt + 4 * g4 + i) / KS;
-        gmk[m][i] = (tix < RT * TT && d >= 0) ? apow(la, d) : 0.f;
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        const int ix = DF::index(tt, q);
+        if (ix >= 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int d = 16 * tt + c - (32 * q + 8 * g4 + j) / KS;
+            dm[ix][j] = from_f32<T>(d >= 0 ? apow(la, d) : 0.f);
+          }
+        }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < YTW; ++j) al[j] = apow(la, 16 * (y_t0 + 2 * j) + c + 1);
   }
 
-  // ---- entering state of this segment (this wave's slice, accumulator layout)
-  floatx4 Hr[NTW][PTW];
+  // ---- entering state of this segment (this wave's columns, accumulator layout)
+  floatx4 Hr[NT];
   {
     const float* src = nullptr;
     if (WITH_Y) {
@@ -207,17 +239,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
       }
     }
 #pragma unroll
-    for (int a = 0; a < NTW; ++a)
+    for (int a = 0; a < NT; ++a)
 #pragma unroll
-      for (int pp = 0; pp < PTW; ++pp)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * (n_t0 + a) + 4 * g4 + i, p = 16 * (p_t0 + pp) + c;
-          Hr[a][pp][i] = (src && n < N) ? src[(size_t)n * kP + p] : 0.f;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int n = 16 * a + 4 * g4 + i;
+        Hr[a][i] = (src && n < N) ? src[(size_t)n * kP + prow_x] : 0.f;
+      }
   }
 
-  const int nc = (Tlen + L - 1) / L;
+  const int nc = A.nc;
   const int ch0 = seg * A.seg_chunks;
   const int ch1 = min(nc, ch0 + A.seg_chunks);
   if (ch0 >= ch1) return;
@@ -230,282 +260,220 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
       }
     } else {
       if (++s.sig == nblocks(s.ch)) { s.sig = 0; ++s.ch; }
-      s.tau = s.sig;
+      s.tau = s.ch < ch1 ? nblocks(s.ch) - 1 : 0;
     }
     return s;
   };
 
-  // ---- global -> registers for one step (issued one step ahead)
-  auto load = [&](Stage& st, ScanStep s) {
+  // ---- HBM -> LDS stage for one step (the tiles this step reads)
+  auto fetch = [&](unsigned char* st, ScanStep s) {
     const int c0 = s.ch * L;
     const int Lc = min(L, Tlen - c0);
+    const bool last = s.tau == (Lc + BT - 1) / BT - 1;
     const uint32_t prow = (uint32_t)(c0 + s.sig * BT) * KS;  // first pair row of block sig
     const int rlim = (Lc - s.sig * BT) * KS;                  // valid pair rows in the block
-    if (WITH_Y && s.sig == 0) {
-      const int tlim = Lc - s.tau * BT;
-      const uint32_t trow = (uint32_t)(c0 + s.tau * BT);
-#pragma unroll
-      for (int u = 0; u < Stage::CUN; ++u) {
-        const int q = tid + kScanThreads * u;
-        const int t = q / (NP / 8), n0 = 8 * (q % (NP / 8));
-        const bool ok = q < BT * (NP / 8) && n0 < N && t < tlim;
-        st.cv[u] = load8_buf<T>(rC, ok ? ((trow + t) * GN + grp * N + n0) * ES : kOOB);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < Stage::BUN; ++u) {
-      const int q = tid + kScanThreads * u;
-      const int r0 = 4 * (q / (NP / 8)), n0 = 8 * (q % (NP / 8));
-      const bool uok = q < (R / 4) * (NP / 8) && n0 < N;
-      const uint32_t off = ((prow + r0) * GN + grp * N + n0) * ES;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st.bv[u][i] = load8_buf<T>(rB, (uok && r0 + i < rlim) ? off + i * GN * ES : kOOB);
-    }
-#pragma unroll
-    for (int u = 0; u < Stage::XUN; ++u) {
-      const int q = tid + kScanThreads * u;
-      const int r0 = 4 * (q / (kP / 8)), p0 = 8 * (q % (kP / 8));
-      const bool uok = q < (R / 4) * (kP / 8);
-      const uint32_t off = ((prow + r0) * (uint32_t)HPsz + h * kP + p0) * ES;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st.xv[u][i] = load8_buf<T>(rX, (uok && r0 + i < rlim) ? off + i * (uint32_t)HPsz * ES : kOOB);
+    dma_tile<R, XC>(rX, (prow * (uint32_t)HPsz + h * kP) * ES, (uint32_t)HPsz * ES, st + Lay::XO,
+                    rlim, XC, w, lane, [](int r) { return swz_tr<T, XC>(r); });
+    if (last)
+      dma_tile<R, BC>(rB, (prow * GN + grp * N) * ES, GN * ES, st + Lay::BO, rlim,
+                      (int)(N * ES / 16), w, lane, [](int r) { return swz_tr<T, BC>(r); });
+    if (WITH_Y) {
+      if (s.sig == 0)
+        dma_tile<BT, BC>(rC, ((uint32_t)(c0 + s.tau * BT) * GN + grp * N) * ES, GN * ES,
+                         st + Lay::CO, Lc - s.tau * BT, (int)(N * ES / 16), w, lane,
+                         [](int r) { return swz_row<T, BC>(r); });
+      const int pidx = s.tau * (s.tau + 1) / 2 + s.sig;
+      const uint32_t gbase = (uint32_t)((((size_t)s.ch * G + grp) * A.npairs + pidx) * gtile);
+      dma_tile<BT, GC>(rG, gbase * ES, R * ES, st + Lay::GO, BT, GC, w, lane,
+                       [](int r) { return swz_row<T, GC>(r); });
     }
   };
 
-  // ---- registers -> LDS
-  auto store = [&](const Stage& st, ScanStep s) {
-    const bool diag = s.sig == s.tau;
-    const int c0s = s.ch * L;
-    const int Lcs = min(L, Tlen - c0s);
-    if (WITH_Y && s.sig == 0) {
-#pragma unroll
-      for (int u = 0; u < Stage::CUN; ++u) {
-        const int q = tid + kScanThreads * u;
-        if (q < BT * (NP / 8)) {
-          const int t = q / (NP / 8), n0 = 8 * (q % (NP / 8));
-          store8<T>(&Cs[t * LDN + n0], st.cv[u]);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < Stage::BUN; ++u) {
-      const int q = tid + kScanThreads * u;
-      if (q < (R / 4) * (NP / 8)) {
-        const int r0 = 4 * (q / (NP / 8)), n0 = 8 * (q % (NP / 8));
-        if (WITH_Y) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) store8<T>(&Bs[(r0 + i) * LDN + n0], st.bv[u][i]);
-        }
-        if (diag) {
-          // rows scaled by their carry decay a^{Lc-1-s} (relative to the chunk end)
-          F dv[4];
-          if (Lcs == L) {
-            const float blk = apow(la, ((Lcs + BT - 1) / BT - 1 - s.sig) * BT);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dv[i] = st.bv[u][i] * from_f32<T>(cdb[u][i] * blk);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int d = Lcs - 1 - (s.sig * BT + (r0 + i) / KS);
-              dv[i] = st.bv[u][i] * from_f32<T>(d >= 0 ? apow(la, d) : 0.f);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int row = n0 + e;
-            F4 col = {dv[0][e], dv[1][e], dv[2][e], dv[3][e]};
-            *reinterpret_cast<F4*>(&BsT[row * LDR + 8 * swz<R>(row, r0 >> 3) + (r0 & 7)]) = col;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < Stage::XUN; ++u) {
-      const int q = tid + kScanThreads * u;
-      if (q < (R / 4) * (kP / 8)) {
-        const int r0 = 4 * (q / (kP / 8)), p0 = 8 * (q % (kP / 8));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int row = p0 + e;
-          F4 col = {st.xv[u][0][e], st.xv[u][1][e], st.xv[u][2][e], st.xv[u][3][e]};
-          *reinterpret_cast<F4*>(&XsT[row * LDR + 8 * swz<R>(row, r0 >> 3) + (r0 & 7)]) = col;
-        }
-      }
-    }
-  };
+  float hin = 1.f, hscale = 1.f;
+  floatx4 accY[WITH_Y ? TT : 1];
+  bool ypend = false;
+  size_t yrow0 = 0;
+  int ylim = 0;
 
-  // per-wave max |H| -> LDS (read after the next barrier)
-  auto publish_max = [&]() {
-    float mx = 0.f;
-#pragma unroll
-    for (int a = 0; a < NTW; ++a)
-#pragma unroll
-      for (int pp = 0; pp < PTW; ++pp)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[a][pp][i]));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) wmax[wave] = mx;
-  };
-
-  ScanStep cur{ch0, 0, 0};
-  Stage st;
-  load(st, cur);
-  if (WITH_Y) publish_max();
-
-  float hscale = 1.f;
-  floatx4 accY[YTW];
-
-  while (cur.ch < ch1) {
+  // ---- compute one step from the stage at LDS byte offset st
+  auto compute = [&](const unsigned char* st, const ScanStep cur) {
+    const unsigned char* Xs = st + Lay::XO;
+    const unsigned char* Bs = st + Lay::BO;
+    const unsigned char* Cs = st + Lay::CO;
+    const unsigned char* Gs = st + Lay::GO;
     const int c0 = cur.ch * L;
     const int Lc = min(L, Tlen - c0);
     const int nb = (Lc + BT - 1) / BT;
-    const bool diag = cur.sig == cur.tau;
-    const bool chunk_start = cur.tau == 0 && cur.sig == 0;
+    const bool last = cur.tau == nb - 1;
+    const bool dg = cur.sig == cur.tau;
 
-    __syncthreads();  // readers of the previous step's LDS data are done; wmax visible
-    store(st, cur);
-    if (chunk_start) {
-      if (WITH_Y) {
-        // The entering state as an fp16 matrix-core operand [p][n], scaled by
-        // 2^-e (e >= 0 from the workgroup's max |H|) so it stays below 2^14;
-        // the readout is multiplied back by 2^e in fp32.
-        float hin = 1.f;
-        hscale = 1.f;
-        if (sizeof(T) == 2) {
-          float mx = wmax[0];
+    if (WITH_Y && cur.tau == 0 && cur.sig == 0) {
+      hin = 1.f;
+      hscale = 1.f;
+      if (sizeof(T) == 2) {
+        // The entering state as an fp16 operand, scaled by 2^-e (e >= 0 from
+        // this wave's max |H|) so it stays below 2^14; the readout is
+        // multiplied back by 2^e in fp32.
+        float mx = 0.f;
 #pragma unroll
-          for (int w = 1; w < 8; ++w) mx = fmaxf(mx, wmax[w]);
-          if (mx > 16384.f) {
-            const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
-            hin = ldexpf(1.f, -e);
-            hscale = ldexpf(1.f, e);
-          }
+        for (int a = 0; a < NT; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[a][i]));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (mx > 16384.f) {
+          const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
+          hin = ldexpf(1.f, -e);
+          hscale = ldexpf(1.f, e);
         }
-#pragma unroll
-        for (int a = 0; a < NTW; ++a)
-#pragma unroll
-          for (int pp = 0; pp < PTW; ++pp) {
-            F4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = from_f32<T>(Hr[a][pp][i] * hin);
-            *reinterpret_cast<F4*>(&Hs[(16 * (p_t0 + pp) + c) * LDN + 16 * (n_t0 + a) + 4 * g4]) = v;
-          }
       }
-      // The carry accumulates straight into the state: H <- a^{Lc} H first.
-      const float aL = apow(la, Lc);
-#pragma unroll
-      for (int a = 0; a < NTW; ++a)
-#pragma unroll
-        for (int pp = 0; pp < PTW; ++pp) Hr[a][pp] = Hr[a][pp] * aL;
     }
-    const ScanStep nxt = advance(cur);
-    if (nxt.ch < ch1) load(st, nxt);  // in flight during this step's compute
-    __syncthreads();
+
+    F xq[RQ];  // X^T fragment of this wave's columns: rows r = 32q + 8g + j
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) xq[q] = load_kmajor<T, XC>(Xs, 32 * q, 16 * w, lane);
 
     if (WITH_Y) {
       if (cur.sig == 0) {
-        // ---- readout of the entering state for block tau: y^T[p, t] = H^T[p, n] C~^T[n, t]
-        const float ablk = (cur.tau == 0 ? 1.f : apow(la, cur.tau * BT)) * hscale;
+        // ---- readout of the entering state: y^T[p, t] = H^T[p, n] C~^T[n, t]
+        const float ablk = (cur.tau == 0 ? 1.f : apow(la, cur.tau * BT)) * hscale * ah;
 #pragma unroll
-        for (int j = 0; j < YTW; ++j) accY[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < TT; ++tt) accY[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const bool scaled = hin != 1.f;
 #pragma unroll
-        for (int q = 0; q < NP / 32; ++q) {
-          F hf = load8<T>(&Hs[(16 * y_pt + c) * LDN + 32 * q + 8 * g4]);
+        for (int q = 0; q < NQ; ++q) {
+          F hf;
+          if (scaled) {
 #pragma unroll
-          for (int j = 0; j < YTW; ++j)
-            accY[j] = mma16(hf, load8<T>(&Cs[(16 * (y_t0 + 2 * j) + c) * LDN + 32 * q + 8 * g4]), accY[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < YTW; ++j) accY[j] = accY[j] * (al[j] * ablk);
-      }
-      // ---- masked Gram^T tiles -> Gm[t][r]
-      const int dblk = (cur.tau - cur.sig) * BT;
-      floatx4 gacc[GTW];
-#pragma unroll
-      for (int m = 0; m < GTW; ++m) gacc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-      {
-        const int tt = wave % TT;  // the same t-tile for every tile of this wave
-#pragma unroll
-        for (int q = 0; q < NP / 32; ++q) {
-          F cf = load8<T>(&Cs[(16 * tt + c) * LDN + 32 * q + 8 * g4]);
-#pragma unroll
-          for (int m = 0; m < GTW; ++m) {
-            const int rt = (wave + 8 * m) / TT;
-            if (wave + 8 * m < RT * TT)
-              gacc[m] = mma16(load8<T>(&Bs[(16 * rt + c) * LDN + 32 * q + 8 * g4]), cf, gacc[m]);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < GTW; ++m) {
-          const int tix = wave + 8 * m;
-          if (tix < RT * TT) {
-            const int rt = tix / TT;
-            F4 out;
-            if (dblk == 0) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) out[i] = from_f32<T>(gacc[m][i] * gmk[m][i]);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                out[i] = from_f32<T>(gacc[m][i] *
-                                     apow(la, dblk + (16 * tt + c) - (16 * rt + 4 * g4 + i) / KS));
+            for (int i = 0; i < 4; ++i) {
+              hf[i] = from_f32<T>(Hr[2 * q][i] * hin);
+              hf[4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
             }
-            *reinterpret_cast<F4*>(&Gm[(16 * tt + c) * LDR + 16 * rt + 4 * g4]) = out;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              hf[i] = from_f32<T>(Hr[2 * q][i]);
+              hf[4 + i] = from_f32<T>(Hr[2 * q + 1][i]);
+            }
+          }
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+            // C~ operand in the same n order: {32q + 4g .. +3, 32q + 16 + 4g .. +3}
+            const int t = 16 * tt + c;
+            const int n0 = 32 * q + 4 * g4;
+            const int e0 = n0 * (int)ES, e1 = (n0 + 16) * (int)ES;
+            const int sw = swz_row<T, BC>(t);
+            const T* p0 = reinterpret_cast<const T*>(Cs + (t * BC + ((e0 >> 4) ^ sw)) * 16 + (e0 & 15));
+            const T* p1 = reinterpret_cast<const T*>(Cs + (t * BC + ((e1 >> 4) ^ sw)) * 16 + (e1 & 15));
+            accY[tt] = mma16(hf, load4x2<T>(p0, p1), accY[tt]);
           }
         }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] * (at[tt] * ablk);
       }
-      __syncthreads();
-      // ---- y^T[p, t] += X^T[p, r] Gm[t, r]
+      // ---- intra-chunk: y^T[p, t] += X^T[p, r] (G o decay)[t, r]
+      auto gfrag = [&](int tt, int q) {
+        const int t = 16 * tt + c;
+        const int e0 = (32 * q + 8 * g4) * (int)ES;
+        const unsigned char* p = Gs + (t * GC + ((e0 >> 4) ^ swz_row<T, GC>(t))) * 16 + (e0 & 15);
+        return load8<T>(reinterpret_cast<const T*>(p));
+      };
+      if (dg) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int q = 0; q < RQ; ++q) {
+            const int ix = DF::index(tt, q);
+            if (ix >= 0) accY[tt] = mma16(xq[q], gfrag(tt, q) * dm[ix], accY[tt]);
+          }
+      } else {
+        floatx4 tmp[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) tmp[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {
+          const F xs = xq[q] * er[q];
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) tmp[tt] = mma16(xs, gfrag(tt, q), tmp[tt]);
+        }
+        const float u = apow(la, (cur.tau - cur.sig) * BT - (BT - 1));
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] + tmp[tt] * (u * at[tt]);
+      }
+    }
+    if (last) {
+      // The carry accumulates straight into the state: H <- a^{Lc} H first
+      // (after the readouts of this chunk, which all use the entering state).
+      if (cur.sig == 0) {
+        const float aL = apow(la, Lc);
+#pragma unroll
+        for (int a = 0; a < NT; ++a) Hr[a] = Hr[a] * aL;
+      }
+      // ---- carry: H[n, p] += sum_r B_hat[r, n] (a^{Lc-1-s} X[r, p])
+      const bool full = Lc == L;
+      const float blk = apow(la, (nb - 1 - cur.sig) * BT);
 #pragma unroll
       for (int q = 0; q < RQ; ++q) {
-        const int prow = 16 * y_pt + c;
-        F xa = load8<T>(&XsT[prow * LDR + 8 * swz<R>(prow, 4 * q + g4)]);
+        F xd;
+        if (full) {
+          xd = xq[q] * (er[q] * from_f32<T>(blk));
+        } else {
 #pragma unroll
-        for (int j = 0; j < YTW; ++j)
-          accY[j] = mma16(xa, load8<T>(&Gm[(16 * (y_t0 + 2 * j) + c) * LDR + 32 * q + 8 * g4]), accY[j]);
-      }
-    }
-    // ---- carry: H[n, p] += sum_r (a^{Lc-1-s} B_hat[r, n]) X[r, p]
-    if (diag) {
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        F xf[PTW];
-#pragma unroll
-        for (int pp = 0; pp < PTW; ++pp) {
-          const int prow = 16 * (p_t0 + pp) + c;
-          xf[pp] = load8<T>(&XsT[prow * LDR + 8 * swz<R>(prow, 4 * q + g4)]);
+          for (int j = 0; j < 8; ++j) {
+            const int d = Lc - 1 - (cur.sig * BT + (32 * q + 8 * g4 + j) / KS);
+            xd[j] = from_f32<T>(to_f32(xq[q][j]) * (d >= 0 ? apow(la, d) : 0.f));
+          }
         }
 #pragma unroll
-        for (int a = 0; a < NTW; ++a) {
-          const int row = 16 * (n_t0 + a) + c;
-          F bt = load8<T>(&BsT[row * LDR + 8 * swz<R>(row, 4 * q + g4)]);
-#pragma unroll
-          for (int pp = 0; pp < PTW; ++pp) Hr[a][pp] = mma16(bt, xf[pp], Hr[a][pp]);
-        }
-      }
-      if (WITH_Y && cur.tau == nb - 1) publish_max();  // chunk done: max for the next Hs
-    }
-    if (WITH_Y && diag) {
-      // ---- store y for block tau: lane holds y[t = 16tt + c][p = 16 y_pt + 4g + i]
-      typedef typename Vec<TY>::x4 Y4;
-      TY* yb = reinterpret_cast<TY*>(A.y) + ((size_t)b * Tlen + c0) * HPsz + (size_t)h * kP +
-               16 * y_pt + 4 * g4;
-#pragma unroll
-      for (int j = 0; j < YTW; ++j) {
-        const int tl = cur.tau * BT + 16 * (y_t0 + 2 * j) + c;
-        if (tl < Lc) {
-          Y4 o;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[j][i]);
-          *reinterpret_cast<Y4*>(yb + (size_t)tl * HPsz) = o;
-        }
+        for (int a = 0; a < NT; ++a) Hr[a] = mma16(load_kmajor<T, BC>(Bs, 32 * q, 16 * a, lane), xd, Hr[a]);
       }
     }
-    cur = nxt;
+    if (WITH_Y && dg) {
+      // y of block tau is complete; it is stored at the start of the next step
+      ypend = true;
+      yrow0 = (size_t)b * Tlen + c0 + cur.tau * BT;
+      ylim = Lc - cur.tau * BT;
+    }
+  };
+  // ---- store the pending y block: lane holds y[t = 16tt + c][p = 16w + 4g + i]
+  auto store_y = [&]() {
+    if (!WITH_Y || !ypend) return;
+    typedef typename Vec<TY>::x4 Y4;
+    TY* yb = reinterpret_cast<TY*>(A.y) + yrow0 * HPsz + (size_t)h * kP + 16 * w + 4 * g4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int tl = 16 * tt + c;
+      if (tl < ylim) {
+        Y4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[tt][i]);
+        *reinterpret_cast<Y4*>(yb + (size_t)tl * HPsz) = o;
+      }
+    }
+    ypend = false;
+  };
+
+  // ---- the walk: the copy of the next step's tiles into the other stage runs
+  // while this step computes; one barrier per step. Unrolled by two so that
+  // every access names its stage array.
+  ScanStep s0{ch0, WITH_Y ? 0 : nblocks(ch0) - 1, 0};
+  ScanStep s1 = advance(s0);
+  fetch(stage0, s0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  auto step = [&](const unsigned char* cur_st, unsigned char* next_st) {
+    store_y();
+    if (s1.ch < ch1) fetch(next_st, s1);
+    compute(cur_st, s0);
+    __builtin_amdgcn_s_waitcnt(0);  // the next stage has landed
+    __syncthreads();
+    s0 = s1;
+    if (s1.ch < ch1) s1 = advance(s1);
+    return s0.ch < ch1;
+  };
+  while (step(stage0, stage1) && step(stage1, stage0)) {
   }
+  store_y();
 
   // ---- write the end state
   float* dst = nullptr;
@@ -516,14 +484,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
   }
   if (dst) {
 #pragma unroll
-    for (int a = 0; a < NTW; ++a)
+    for (int a = 0; a < NT; ++a)
 #pragma unroll
-      for (int pp = 0; pp < PTW; ++pp)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * (n_t0 + a) + 4 * g4 + i, p = 16 * (p_t0 + pp) + c;
-          if (n < N) dst[(size_t)n * kP + p] = Hr[a][pp][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int n = 16 * a + 4 * g4 + i;
+        if (n < N) dst[(size_t)n * kP + prow_x] = Hr[a][i];
+      }
   }
 }
 
@@ -568,24 +534,24 @@ hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t
   return hipGetLastError();
 }
 
-// Tuning knobs (environment, read once): SWIMBA_SCAN_BT = 32 or 64 tokens per
-// block for fp16 streams (default 64); SWIMBA_SCAN_WGS = target number of
-// workgroups of the output pass (default 1024), which sets the segment count.
+// Tuning knob (environment, read once): SWIMBA_SCAN_WGS = target number of
+// workgroups of the output pass, which sets the segment count per sequence.
 static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   return v ? atoi(v) : dflt;
 }
-int scan_block_tokens() {
-  static const int bt = env_int("SWIMBA_SCAN_BT", 64);
-  return bt;
-}
 static int scan_target_wgs() {
-  static const int w = env_int("SWIMBA_SCAN_WGS", 1024);
-  return w > 0 ? w : 1024;
+  static const int w = env_int("SWIMBA_SCAN_WGS", 384);
+  return w > 0 ? w : 384;
 }
 
-ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L) {
-  ScanGeom g{Bt, T, H, G, N, P, k, L, 1, 1};
+static int scan_npairs(int L) {
+  const int nb = (L + kBT - 1) / kBT;
+  return nb * (nb + 1) / 2;
+}
+
+ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es) {
+  ScanGeom g{Bt, T, H, G, N, P, k, L, es, 1, 1};
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
   const int units = Bt * H;
@@ -597,22 +563,34 @@ ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L) {
   return g;
 }
 
-size_t scan_ws_bytes(const ScanGeom& g) {
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static size_t scan_state_bytes(const ScanGeom& g) {
   if (g.segs <= 1) return 0;
-  return (size_t)g.Bt * g.segs * g.H * g.N * g.P * sizeof(float);
+  return align256((size_t)g.Bt * g.segs * g.H * g.N * g.P * sizeof(float));
 }
 
-template <typename T, typename TY, int NP, int KS, int BT>
-static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStream_t s) {
-  auto k3 = scan_kernel<T, TY, NP, KS, BT, true>;
-  auto k1 = scan_kernel<T, TY, NP, KS, BT, false>;
-  const size_t l3 = ScanLds<T, NP, KS, BT, true>::bytes;
-  const size_t l1 = ScanLds<T, NP, KS, BT, false>::bytes;
-  hipError_t err = hipFuncSetAttribute((const void*)k3, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)l3);
-  if (err != hipSuccess) return err;
-  err = hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1);
-  if (err != hipSuccess) return err;
+static size_t scan_gram_bytes(const ScanGeom& g) {
+  const size_t nc = (size_t)((g.T + g.L - 1) / g.L);
+  return align256((size_t)g.Bt * nc * g.G * scan_npairs(g.L) * kBT * (g.k * kBT) * g.es);
+}
+
+size_t scan_ws_bytes(const ScanGeom& g) {
+  if (g.Bt == 0 || g.T == 0) return 0;
+  return scan_state_bytes(g) + scan_gram_bytes(g);
+}
+
+template <typename T, typename TY, int NP, int KS>
+static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s) {
+  auto k3 = scan_kernel<T, TY, NP, KS, true>;
+  auto k1 = scan_kernel<T, TY, NP, KS, false>;
+  const size_t l3 = 0, l1 = 0;  // static LDS (two stage arrays)
+  prof_begin("scan_gram", s);
+  hipLaunchKernelGGL((scan_gram_kernel<T, NP, KS>), dim3(args.npairs * g.G, args.nc, g.Bt),
+                     dim3(256), 0, s, static_cast<const T*>(args.B_hat),
+                     static_cast<const T*>(args.C_mix), static_cast<T*>(const_cast<void*>(args.gram)),
+                     g.T, g.G, g.N, g.L, args.nc, args.npairs);
+  prof_end(s);
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
     hipLaunchKernelGGL(k1, dim3(g.H, g.segs - 1, g.Bt), dim3(kScanThreads), l1, s, args);
@@ -630,18 +608,17 @@ static hipError_t launch_scan_t(const ScanGeom& g, const ScanArgs& args, hipStre
 }
 
 template <typename T, typename TY, int NP>
-static hipError_t dispatch_ks(const ScanGeom& g, const ScanArgs& a, hipStream_t s, bool bt32) {
-  if (g.k == 1)
-    return bt32 ? launch_scan_t<T, TY, NP, 1, 32>(g, a, s) : launch_scan_t<T, TY, NP, 1, 64>(g, a, s);
-  return bt32 ? launch_scan_t<T, TY, NP, 2, 32>(g, a, s) : launch_scan_t<T, TY, NP, 2, 64>(g, a, s);
+static hipError_t dispatch_ks(const ScanGeom& g, const ScanArgs& a, hipStream_t s) {
+  if (g.k == 1) return launch_scan_t<T, TY, NP, 1>(g, a, s);
+  return launch_scan_t<T, TY, NP, 2>(g, a, s);
 }
 
 template <typename T, typename TY>
-static hipError_t dispatch_np(const ScanGeom& g, const ScanArgs& a, hipStream_t s, bool bt32) {
+static hipError_t dispatch_np(const ScanGeom& g, const ScanArgs& a, hipStream_t s) {
   const int np = g.N <= 32 ? 32 : (g.N <= 64 ? 64 : 128);
-  if (np == 32) return dispatch_ks<T, TY, 32>(g, a, s, bt32);
-  if (np == 64) return dispatch_ks<T, TY, 64>(g, a, s, bt32);
-  return dispatch_ks<T, TY, 128>(g, a, s, bt32);
+  if (np == 32) return dispatch_ks<T, TY, 32>(g, a, s);
+  if (np == 64) return dispatch_ks<T, TY, 64>(g, a, s);
+  return dispatch_ks<T, TY, 128>(g, a, s);
 }
 
 hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
@@ -652,13 +629,12 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
     if (h_final) return launch_state_copy(h_init, h_final, (size_t)g.Bt * g.H * g.N * g.P, s);
     return hipSuccess;
   }
-  ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws,
-                g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks};
-  // bf16 inputs (fp16 streams) use 64-token blocks (32 when the chunk is 32);
-  // fp32 always 32, to fit LDS.
-  const bool bt32 = !is_bf16 || g.L == 32 || scan_block_tokens() == 32;
-  if (is_bf16) return dispatch_np<f16, bf16>(g, args, s, bt32);
-  return dispatch_np<float, float>(g, args, s, bt32);
+  const int nc = (g.T + g.L - 1) / g.L;
+  unsigned char* gram = reinterpret_cast<unsigned char*>(ws) + scan_state_bytes(g);
+  ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws, gram,
+                g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks, nc, scan_npairs(g.L)};
+  if (is_bf16) return dispatch_np<f16, bf16>(g, args, s);
+  return dispatch_np<float, float>(g, args, s);
 }
 
 }  // namespace swimba
