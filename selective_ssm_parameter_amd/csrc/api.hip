@@ -92,7 +92,7 @@ swimba_status check_scan_shape(const Dims& d) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct ProjWs {
-  size_t counts, offsets, tiles, sorted, cpart, total;
+  size_t counts, offsets, tiles, sorted, sortw, cpart, total;
 };
 
 ProjWs proj_ws(const Dims& d) {
@@ -104,8 +104,10 @@ ProjWs proj_ws(const Dims& d) {
   size_t off = 0;
   w.counts = off; off += align256(sizeof(int32_t) * nblk * (d.E + 1));
   w.offsets = off; off += align256(sizeof(int32_t) * (d.E + 2));
-  w.tiles = off; off += align256(sizeof(int32_t) * (d.E + 1));
+  // tile table: 4 ints per row tile, for the smallest row tile (most tiles)
+  w.tiles = off; off += align256(sizeof(int32_t) * 4 * (size_t)proj_row_tiles_max((int)pairs, (int)d.E, 64));
   w.sorted = off; off += align256(sizeof(int32_t) * pairs);
+  w.sortw = off; off += align256(sizeof(float) * pairs);
   w.cpart = off; off += align256(sizeof(float) * pairs * d.GN);
   w.total = off;
   return w;
@@ -178,13 +180,15 @@ hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_ex
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + lay.offsets);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + lay.sorted);
+  float* sortw = reinterpret_cast<float*>(ws + lay.sortw);
   float* cpart = reinterpret_cast<float*>(ws + lay.cpart);
-  hipError_t e = launch_bucket(d.bf16, idx, pairs, (int)d.E, bm, counts, nullptr, offsets, tiles,
-                               sorted, X_hat, (int)d.HP, B_hat, (int)d.GN, cpart, s,
+  const int ntiles_max = proj_row_tiles_max(pairs, (int)d.E, bm);
+  hipError_t e = launch_bucket(d.bf16, idx, w, pairs, (int)d.E, bm, ntiles_max, counts, offsets,
+                               tiles, sorted, sortw, X_hat, (int)d.HP, B_hat, (int)d.GN, cpart, s,
                                routed ? kRouteTok * (int)d.k : 0, routed);
   if (e != hipSuccess) return e;
-  return launch_project(d.bf16, proj_geom(d, M), u, w_experts, sorted, offsets, tiles, idx, w, bm,
-                        B_hat, X_hat, cpart, C_mix, s);
+  return launch_project(d.bf16, proj_geom(d, M), u, w_experts, sorted, sortw, tiles, bm, B_hat,
+                        X_hat, cpart, C_mix, s);
 }
 
 // ---------------------------------------------------------------- profiling

@@ -45,13 +45,17 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
 // blocks before its own, then places its pairs in stable order (pair id).
 // Workgroup 0 also writes the bucket offsets and the GEMM tile schedule:
 //   offsets[0..E+1]: start of each bucket and the end;
-//   tile_offsets[0..E]: prefix of ceil(count_e / bm) over real experts.
+//   tile_info[t] = {expert, first sorted row, rows} for the row tiles of bm
+//   pairs of every real expert in order, {-1, 0, 0} up to ntiles_max.
+// Next to each sorted pair id goes its top-k weight (sorted_w), so the GEMM
+// reads a tile's rows with one round trip.
 template <typename T>
 __global__ __launch_bounds__(256) void bucket_place_kernel(
-    const int32_t* __restrict__ idx, int pairs, int E, int bp, int nblk,
-    const int32_t* __restrict__ counts, int bm, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ tile_offsets, int32_t* __restrict__ sorted, T* __restrict__ X_hat,
-    int HP, T* __restrict__ B_hat, int GN, float* __restrict__ c_part) {
+    const int32_t* __restrict__ idx, const float* __restrict__ topk_w, int pairs, int E, int bp,
+    int nblk, const int32_t* __restrict__ counts, int bm, int ntiles_max,
+    int32_t* __restrict__ offsets, int4v* __restrict__ tile_info, int32_t* __restrict__ sorted,
+    float* __restrict__ sorted_w, T* __restrict__ X_hat, int HP, T* __restrict__ B_hat, int GN,
+    float* __restrict__ c_part) {
   extern __shared__ int sh[];
   const int EP = E + 1;
   int* before = sh;            // [EP] pairs of each bucket in earlier blocks (then: running base)
@@ -116,13 +120,27 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(
   if (threadIdx.x < EP) before[threadIdx.x] += excl;  // becomes the running base of this block
   if (EP > 256 && threadIdx.x == 0) before[256] += scan[255];
   __syncthreads();
-  if (blk == 0 && threadIdx.x == 0) {
-    int tiles = 0;
-    for (int e = 0; e < E; ++e) {
-      tile_offsets[e] = tiles;
-      tiles += (total[e] + bm - 1) / bm;
+  if (blk == 0) {
+    // tile prefix over experts (scan scratch is free again), then each
+    // expert's tiles written by its own thread
+    __shared__ int tprefix[257];
+    if (threadIdx.x == 0) {
+      int tiles = 0;
+      for (int e = 0; e < E; ++e) {
+        tprefix[e] = tiles;
+        tiles += (total[e] + bm - 1) / bm;
+      }
+      tprefix[E] = tiles;
     }
-    tile_offsets[E] = tiles;
+    __syncthreads();
+    if (threadIdx.x < E) {  // E <= 256: thread e holds bucket e's start in excl
+      const int e = threadIdx.x;
+      const int nt = (total[e] + bm - 1) / bm;
+      for (int j = 0; j < nt; ++j)
+        tile_info[tprefix[e] + j] = int4v{e, excl + j * bm, min(bm, total[e] - j * bm), 0};
+    }
+    for (int t = tprefix[E] + threadIdx.x; t < ntiles_max; t += blockDim.x)
+      tile_info[t] = int4v{-1, 0, 0, 0};
   }
 
   // ---- stable placement of this block's pairs
@@ -149,6 +167,7 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(
       int pos = before[bkt] + rank;
       for (int w = 0; w < wave; ++w) pos += wcnt[w * EP + bkt];
       sorted[pos] = p;
+      sorted_w[pos] = topk_w[p];
       if (bkt == E) {
         // An out-of-range expert index: this slot contributes nothing.
         for (int i = 0; i < HP; ++i) X_hat[(size_t)p * HP + i] = from_f32<T>(0.f);
@@ -167,11 +186,12 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(
   }
 }
 
-hipError_t launch_bucket(bool is_bf16, const int32_t* idx, int pairs, int E, int bm,
-                         int32_t* counts, int32_t* bases, int32_t* offsets, int32_t* tile_offsets,
-                         int32_t* sorted, void* X_hat, int HP, void* B_hat, int GN,
-                         float* c_part, hipStream_t s, int block_pairs, bool counted) {
-  (void)bases;
+hipError_t launch_bucket(bool is_bf16, const int32_t* idx, const float* topk_w, int pairs, int E,
+                         int bm, int ntiles_max, int32_t* counts, int32_t* offsets,
+                         int32_t* tile_info_i, int32_t* sorted, float* sorted_w, void* X_hat,
+                         int HP, void* B_hat, int GN, float* c_part, hipStream_t s,
+                         int block_pairs, bool counted) {
+  int4v* tile_info = reinterpret_cast<int4v*>(tile_info_i);
   const int bp = block_pairs > 0 ? block_pairs : kBucketPairs;
   const int nblk = (pairs + bp - 1) / bp;
   const size_t hl = (size_t)(E + 1) * sizeof(int);
@@ -184,13 +204,13 @@ hipError_t launch_bucket(bool is_bf16, const int32_t* idx, int pairs, int E, int
   prof_begin("bucket_place", s);
   const dim3 grid(nblk > 0 ? nblk : 1);
   if (is_bf16)
-    hipLaunchKernelGGL(bucket_place_kernel<f16>, grid, dim3(256), pl, s, idx, pairs, E, bp, nblk,
-                       counts, bm, offsets, tile_offsets, sorted, (f16*)X_hat, HP, (f16*)B_hat,
-                       GN, c_part);
+    hipLaunchKernelGGL(bucket_place_kernel<f16>, grid, dim3(256), pl, s, idx, topk_w, pairs, E, bp,
+                       nblk, counts, bm, ntiles_max, offsets, tile_info, sorted, sorted_w,
+                       (f16*)X_hat, HP, (f16*)B_hat, GN, c_part);
   else
-    hipLaunchKernelGGL(bucket_place_kernel<float>, grid, dim3(256), pl, s, idx, pairs, E, bp,
-                       nblk, counts, bm, offsets, tile_offsets, sorted, (float*)X_hat, HP,
-                       (float*)B_hat, GN, c_part);
+    hipLaunchKernelGGL(bucket_place_kernel<float>, grid, dim3(256), pl, s, idx, topk_w, pairs, E,
+                       bp, nblk, counts, bm, ntiles_max, offsets, tile_info, sorted, sorted_w,
+                       (float*)X_hat, HP, (float*)B_hat, GN, c_part);
   prof_end(s);
   return hipGetLastError();
 }

@@ -30,18 +30,19 @@ constexpr int kBucketPairs = 1024;  // pairs per bucketing block
 int bucket_blocks(int pairs);
 // block_pairs: pairs per bucketing block (0 = kBucketPairs); counted: the
 // histograms [nblk][E+1] are already in `counts` (written by the router).
-hipError_t launch_bucket(bool is_bf16, const int32_t* idx, int pairs, int E, int bm,
-                         int32_t* counts, int32_t* bases, int32_t* offsets, int32_t* tile_offsets,
-                         int32_t* sorted, void* X_hat, int HP, void* B_hat, int GN,
-                         float* c_part, hipStream_t s, int block_pairs = 0, bool counted = false);
+// tile_info: 4 ints per GEMM row tile {expert (-1: none), first sorted row, rows, 0}.
+hipError_t launch_bucket(bool is_bf16, const int32_t* idx, const float* topk_w, int pairs, int E,
+                         int bm, int ntiles_max, int32_t* counts, int32_t* offsets,
+                         int32_t* tile_info, int32_t* sorted, float* sorted_w, void* X_hat, int HP,
+                         void* B_hat, int GN, float* c_part, hipStream_t s, int block_pairs = 0,
+                         bool counted = false);
 
 // Grouped expert projection with the mix epilogue, then the slot-ordered C sum.
 int proj_row_tiles_max(int pairs, int E, int bm);
 int proj_bm(int pairs, int E);
 // C_mix == nullptr skips the slot sum (the caller consumes c_part itself).
 hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const void* w_experts,
-                          const int32_t* sorted, const int32_t* offsets,
-                          const int32_t* tile_offsets, const int32_t* idx, const float* w,
+                          const int32_t* sorted, const float* sorted_w, const int32_t* tile_info,
                           int bm, void* B_hat, void* X_hat, float* c_part, void* C_mix,
                           hipStream_t s);
 

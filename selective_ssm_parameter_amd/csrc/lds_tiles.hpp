@@ -7,22 +7,25 @@
 
 namespace swimba {
 
-// Swizzles (16-byte chunk index XOR, 2-byte element types; none for fp32).
-// Tiles read with transposing loads (X, B): a 64-lane read touches rows
-// {0..3, 8..11, 16..19, 24..27} (+4) and two adjacent chunks per row; the XOR
-// gives rows that share bank positions distinct chunk pairs.
+// Swizzles (16-byte chunk index XOR, 2-byte element types; none for fp32). Each
+// keeps the accesses of one LDS cycle on distinct banks whether a cycle serves
+// 128 bytes (8 lanes of a 16-byte read) or 256 bytes (16 lanes).
+// Tiles read with transposing loads (X, B): a 16-lane group reads two adjacent
+// chunks of 4 consecutive rows; groups g and g + 1 read rows 8 apart.
 template <typename T, int CPR>
 __device__ __forceinline__ int swz_tr(int r) {
   if constexpr (sizeof(T) != 2) return 0;
   else if constexpr (CPR >= 16) return 2 * ((r & 3) | ((r >> 1) & 4));
-  else if constexpr (CPR == 8) return 2 * (((r >> 1) & 1) | ((r >> 2) & 2));
-  else return 2 * ((r >> 3) & 1);
+  else if constexpr (CPR == 8) return 2 * ((r & 3) ^ ((r >> 3) & 1));
+  else return 2 * (((r >> 1) & 1) ^ ((r >> 3) & 1));
 }
-// Tiles read by rows (C~, G): 16 consecutive rows, one chunk each.
+// Tiles read by rows (C~, G, GEMM operands): 16 consecutive rows, one chunk each.
 template <typename T, int CPR>
 __device__ __forceinline__ int swz_row(int t) {
   if constexpr (sizeof(T) != 2) return 0;
-  else return (t / (16 / CPR)) & (CPR - 1);
+  else if constexpr (CPR >= 16) return t & 15;
+  else if constexpr (CPR == 8) return (t ^ (t >> 3)) & 7;
+  else return ((t >> 1) ^ (t >> 3)) & 3;
 }
 
 // Buffer-to-LDS copy of a row-major tile: NROWS rows of CPR 16-byte chunks,
@@ -83,6 +86,25 @@ __device__ __forceinline__ typename Vec<T>::x8 load_kmajor(const unsigned char* 
     }
   }
   return v;
+}
+
+// s_waitcnt with only the vector-memory count limited to n (0 <= n < 64): the
+// copies issued before the last n of this wave have landed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for staged loops: waits for this wave's LDS accesses only
+// (lgkmcnt), not for copies still in flight to other stages (each wave waits
+// for the stage it needs with wait_vm first); the empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace swimba

@@ -25,6 +25,7 @@
 // into C_mix, so C~ never depends on which workgroup ran first.
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_tiles.hpp"
 
 namespace swimba {
 
@@ -47,43 +48,45 @@ int proj_bm(int pairs, int E) {
 
 int proj_row_tiles_max(int pairs, int E, int bm) { return (pairs + bm - 1) / bm + E; }
 
-// K-tile depth: 64 for 2-byte inputs, 32 for fp32 (same bytes per row).
-template <typename T> struct ProjK { static constexpr int BK = sizeof(T) == 2 ? 64 : 32; };
-
+// Staged K loop: per stage, BK = 32 elements of d for the BM gathered token rows
+// (A) and the BN weight rows (B), row-major, 16-byte chunk c of row r at
+// c ^ swz_row(r). Four stages: the copies of a K tile are issued three tiles
+// ahead of its multiply.
+constexpr int kProjStages = 4;
 template <typename T, class C>
-struct ProjLds {
-  static constexpr int BK = ProjK<T>::BK;
-  static constexpr int LDK = BK + 8;          // LDS row stride of the K tiles (elements)
-  static constexpr int RR = C::TM >= 4 ? 4 : C::TM;  // epilogue row tiles per round
-  static constexpr int EPS = C::TN * 16 + 4;  // epilogue row stride (floats)
-  static constexpr size_t main_bytes = (size_t)2 * (C::BM + C::BN) * LDK * sizeof(T);
-  static constexpr size_t epi_bytes = (size_t)C::NW * RR * 16 * EPS * sizeof(float);
-  static constexpr size_t bytes = main_bytes > epi_bytes ? main_bytes : epi_bytes;
+struct ProjLay {
+  static constexpr int BK = 32;
+  static constexpr int ROWB = BK * (int)sizeof(T);  // bytes per tile row
+  static constexpr int CPR = ROWB / 16;             // chunks per row
+  static constexpr int AB = C::BM * ROWB, BB = C::BN * ROWB;
+  static constexpr int STAGE = AB + BB;
+  static constexpr int NIA = AB / 1024, NIB = BB / 1024;  // copy instructions per stage
+  static constexpr int MA = NIA / C::NW, MB = NIB / C::NW;  // ... per wave
+  static constexpr int CPW = MA + MB;
+  static_assert(NIA % C::NW == 0 && NIB % C::NW == 0, "copies split evenly over the waves");
 };
 
 template <typename T, class C>
 __global__ __launch_bounds__(C::NTH) void proj_kernel(
     const T* __restrict__ u, const T* __restrict__ wexp, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_offsets,
-    const float* __restrict__ topk_w, int M, int D, int W, int HP, int GN, int E, int k,
-    int ntiles, typename StreamOf<T>::type* __restrict__ X_hat,
+    const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
+    int HP, int GN, int k, int ntiles, typename StreamOf<T>::type* __restrict__ X_hat,
     typename StreamOf<T>::type* __restrict__ B_hat, float* __restrict__ c_part) {
   typedef typename StreamOf<T>::type S;
-  typedef ProjLds<T, C> Lay;
-  constexpr int BM = C::BM, BN = C::BN, NTH = C::NTH, TM = C::TM, TN = C::TN;
-  constexpr int BK = Lay::BK, LDK = Lay::LDK;
-  constexpr int CH = BK / 8;                 // 8-element chunks per row and K tile
-  constexpr int AU = BM * CH / NTH;          // A chunks per thread per K tile
-  constexpr int BU = BN * CH / NTH;          // B chunks per thread per K tile
+  typedef ProjLay<T, C> Lay;
+  constexpr int BM = C::BM, BN = C::BN, NTH = C::NTH, NW = C::NW, TM = C::TM, TN = C::TN;
+  constexpr int BK = Lay::BK, CPR = Lay::CPR, ROWB = Lay::ROWB, MA = Lay::MA, MB = Lay::MB;
+  constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
 
-  extern __shared__ __align__(16) unsigned char lds_raw[];
-  T* As = reinterpret_cast<T*>(lds_raw);              // [2][BM][LDK]
-  T* Bs = As + 2 * BM * LDK;                          // [2][BN][LDK]
+  // four stage arrays: copies into one are known not to touch the others
+  __shared__ __align__(16) unsigned char stg0[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stg1[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stg2[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stg3[Lay::STAGE];
   __shared__ int rtok[BM];
   __shared__ int rslot[BM];
   __shared__ float rw[BM];
-  __shared__ int sh_e, sh_row0, sh_nrows;
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
   // XCD x the contiguous logical range [x * per, (x + 1) * per): its tiles
@@ -93,31 +96,16 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
   const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (logical >= ntiles) return;
   const int tile = logical / CT, ctile = logical % CT;
-  if (threadIdx.x == 0) {
-    int e = -1;
-    if (tile < tile_offsets[E]) {
-      int lo = 0, hi = E - 1;  // last e with tile_offsets[e] <= tile
-      while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (tile_offsets[mid] <= tile) lo = mid; else hi = mid - 1;
-      }
-      e = lo;
-      const int row0 = offsets[e] + (tile - tile_offsets[e]) * BM;
-      sh_row0 = row0;
-      sh_nrows = min(BM, offsets[e + 1] - row0);
-    }
-    sh_e = e;
-  }
-  __syncthreads();
-  const int e = sh_e;
+  const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
+  const int e = ti[0];
   if (e < 0) return;
-  const int row0 = sh_row0, nrows = sh_nrows;
+  const int row0 = ti[1], nrows = ti[2];
   for (int r = threadIdx.x; r < BM; r += NTH) {
     if (r < nrows) {
       const int p = sorted[row0 + r];
       rtok[r] = p / k;
       rslot[r] = p - (p / k) * k;
-      rw[r] = topk_w[p];
+      rw[r] = sorted_w[row0 + r];
     } else {
       rtok[r] = -1;
       rslot[r] = 0;
@@ -128,124 +116,145 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
 
   const int col0 = ctile * BN;
   const T* We = wexp + (size_t)e * W * D;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // Per-thread byte offsets of the A (gathered tokens) and B (weight) chunks;
-  // out-of-range chunks read zeros through the buffer resources.
-  constexpr uint32_t ES = sizeof(T);
+  // ---- copy plan (independent of the K tile): instruction m of this wave
+  // fills LDS chunk slots 64 (wave + NW m) + lane of a tile.
   const BufRes rA = make_rsrc(u, (uint64_t)M * D * ES);
   const BufRes rW = make_rsrc(We, (uint64_t)W * D * ES);
-  uint32_t aoff[AU], boff[BU];
-  int ach[AU], bch[BU];
+  uint32_t abase[MA], bbase[MB];
+  int alc[MA], blc[MB];
 #pragma unroll
-  for (int i = 0; i < AU; ++i) {
-    const int q = threadIdx.x + NTH * i, r = q / CH;
-    ach[i] = q % CH;
+  for (int m = 0; m < MA; ++m) {
+    const int slot = 64 * (wave + NW * m) + lane;
+    const int r = slot / CPR;
+    alc[m] = (slot % CPR) ^ swz_row<T, CPR>(r);
     const int tok = rtok[r];
-    aoff[i] = tok >= 0 ? ((uint32_t)tok * D + 8 * ach[i]) * ES : kOOB;
+    abase[m] = tok >= 0 ? (uint32_t)tok * D * ES : kOOB;
   }
 #pragma unroll
-  for (int i = 0; i < BU; ++i) {
-    const int q = threadIdx.x + NTH * i, r = q / CH;
-    bch[i] = q % CH;
+  for (int m = 0; m < MB; ++m) {
+    const int slot = 64 * (wave + NW * m) + lane;
+    const int r = slot / CPR;
+    blc[m] = (slot % CPR) ^ swz_row<T, CPR>(r);
     const int col = col0 + r;
-    boff[i] = col < W ? ((uint32_t)col * D + 8 * bch[i]) * ES : kOOB;
+    bbase[m] = col < W ? (uint32_t)col * D * ES : kOOB;
   }
-  F areg[AU], breg[BU];
-  auto load_tile = [&](int k0) {
+  auto fetch = [&](unsigned char* st, int k0) {
 #pragma unroll
-    for (int i = 0; i < AU; ++i)
-      areg[i] = load8_buf<T>(rA, (aoff[i] != kOOB && k0 + 8 * ach[i] < D) ? aoff[i] + k0 * ES : kOOB);
-#pragma unroll
-    for (int i = 0; i < BU; ++i)
-      breg[i] = load8_buf<T>(rW, (boff[i] != kOOB && k0 + 8 * bch[i] < D) ? boff[i] + k0 * ES : kOOB);
-  };
-  auto store_tile = [&](int buf) {
-    T* a = As + buf * BM * LDK;
-    T* bb = Bs + buf * BN * LDK;
-#pragma unroll
-    for (int i = 0; i < AU; ++i) {
-      const int q = threadIdx.x + NTH * i, r = q / CH, ch = q % CH;
-      store8<T>(&a[r * LDK + 8 * ch], areg[i]);
+    for (int m = 0; m < MA; ++m) {
+      const int kk = k0 + alc[m] * (16 / (int)ES);
+      const uint32_t off = (abase[m] != kOOB && kk < D) ? abase[m] + kk * ES : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (__attribute__((address_space(3))) void*)(st + 1024 * (wave + NW * m)), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < BU; ++i) {
-      const int q = threadIdx.x + NTH * i, r = q / CH, ch = q % CH;
-      store8<T>(&bb[r * LDK + 8 * ch], breg[i]);
+    for (int m = 0; m < MB; ++m) {
+      const int kk = k0 + blc[m] * (16 / (int)ES);
+      const uint32_t off = (bbase[m] != kOOB && kk < D) ? bbase[m] + kk * ES : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rW, (__attribute__((address_space(3))) void*)(st + Lay::AB + 1024 * (wave + NW * m)), 16,
+          off, 0, 0, 0);
     }
   };
 
+  // ---- fragments: lane (g, c) reads row c of a 16-row tile, elements 8g .. 8g+7
+  auto frag = [&](const unsigned char* tilebase, int r) {
+    if constexpr (sizeof(T) == 2) {
+      return load8<T>(reinterpret_cast<const T*>(tilebase + r * ROWB + 16 * (g ^ swz_row<T, CPR>(r))));
+    } else {
+      return load8<T>(reinterpret_cast<const T*>(tilebase + r * ROWB + 32 * g));
+    }
+  };
+
+  // acc[i][j] holds, in lane (g, c), out[pair row 16i + c][columns 16j + 4g .. +3]
+  // of this wave's block: the weight fragment is the matrix-core A operand.
   floatx4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // Column tiles are used in pairs (2jj, 2jj + 1) covering 32 columns: row m of
+  // the pair's first matrix-core tile is column 8 (m / 4) + m % 4 and of the
+  // second 8 (m / 4) + 4 + m % 4, so lane group g ends up with the 8
+  // consecutive columns 8g .. 8g + 7 of the pair (one 16-byte store).
+  auto bcol = [&](int j) { return wn * TN * 16 + 32 * (j >> 1) + 8 * (c >> 2) + 4 * (j & 1) + (c & 3); };
+  auto compute = [&](const unsigned char* st) {
+    // all fragments of the K tile first, then the matrix-core ops
+    F bfr[TN], afr[TM];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[j] = frag(st + Lay::AB, bcol(j));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) afr[i] = frag(st, wm * TM * 16 + 16 * i + c);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mma16(bfr[j], afr[i], acc[i][j]);
+  };
+
   const int nk = (D + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);  // next tile in flight during compute
-    __syncthreads();  // tile kt is in LDS; everyone is done with tile kt - 1
-    const T* a = As + (kt & 1) * BM * LDK + (wm * TM * 16 + c) * LDK + 8 * g;
-    const T* bb = Bs + (kt & 1) * BN * LDK + (wn * TN * 16 + c) * LDK + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      F bfr[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = load8<T>(bb + j * 16 * LDK + 32 * ks);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const F af = load8<T>(a + i * 16 * LDK + 32 * ks);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mma16(af, bfr[j], acc[i][j]);
-      }
-    }
-    if (kt + 1 < nk) store_tile((kt + 1) & 1);
+  fetch(stg0, 0);
+  if (nk > 1) fetch(stg1, BK);
+  if (nk > 2) fetch(stg2, 2 * BK);
+  auto iter = [&](int kt, const unsigned char* cur, unsigned char* far) {
+    const int after = min(2, nk - 1 - kt);  // K tiles already issued after this one
+    if (after >= 2) wait_vm<2 * Lay::CPW>();
+    else if (after == 1) wait_vm<Lay::CPW>();
+    else wait_vm<0>();
+    stage_barrier();  // tile kt visible to all waves; tile kt - 1 no longer read
+    if (kt + 3 < nk) fetch(far, (kt + 3) * BK);
+    compute(cur);
+  };
+  for (int kt = 0; kt < nk; kt += kProjStages) {
+    iter(kt, stg0, stg3);
+    if (kt + 1 < nk) iter(kt + 1, stg1, stg0);
+    if (kt + 2 < nk) iter(kt + 2, stg2, stg1);
+    if (kt + 3 < nk) iter(kt + 3, stg3, stg2);
   }
 
-  // ---- epilogue through LDS: each wave stages RR row tiles x TN column tiles
-  // of fp32 results, then writes whole row segments (4 columns per lane).
-  constexpr int RR = Lay::RR, EPS = Lay::EPS;
-  float* ep = reinterpret_cast<float*>(lds_raw) + (size_t)wave * RR * 16 * EPS;
-  __syncthreads();  // the K tiles are no longer read
+  // ---- epilogue: each lane stores 8 consecutive columns of one pair row per
+  // column-tile pair (H*P and G*N are multiples of 16, so 8 columns never
+  // straddle two regions).
+  static_assert(TN % 2 == 0, "column tiles are used in pairs");
+  typedef typename Vec<S>::x8 S8;
 #pragma unroll
-  for (int round = 0; round < TM / RR; ++round) {
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * TM * 16 + 16 * i + c;
+    const int tok = rtok[r];
+    const size_t pair = (size_t)(tok < 0 ? 0 : tok) * k + rslot[r];
+    const float wv = rw[r];
 #pragma unroll
-    for (int i = 0; i < RR; ++i)
+    for (int jj = 0; jj < TN / 2; ++jj) {
+      const int cbase = __builtin_amdgcn_readfirstlane(col0 + wn * TN * 16 + 32 * jj);
+      if (cbase >= W) continue;
+      const int col = cbase + 8 * g;
+      if (col >= W) continue;
+      floatx8 v;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ep[(16 * i + 4 * g + q) * EPS + 16 * j + c] = acc[round * RR + i][j][q];
-    __syncthreads();
-    constexpr int CPR = TN * 4;  // 4-column chunks per staged row
-    for (int it = lane; it < RR * 16 * CPR; it += 64) {
-      const int rl = it / CPR, ch = it % CPR;
-      const int r = wm * TM * 16 + round * RR * 16 + rl;
-      const int col = col0 + wn * TN * 16 + 4 * ch;
-      const int tok = rtok[r];
-      if (tok < 0 || col >= W) continue;
-      const size_t pair = (size_t)tok * k + rslot[r];
-      const floatx4 v = *reinterpret_cast<const floatx4*>(&ep[rl * EPS + 4 * ch]);
-      typedef typename Vec<S>::x4 S4;
+      for (int q = 0; q < 4; ++q) {
+        v[q] = acc[i][2 * jj][q];
+        v[4 + q] = acc[i][2 * jj + 1][q];
+      }
+      if (tok < 0) continue;
       if (col < HP) {
-        S4 o;
+        S8 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = from_f32<S>(v[q]);
-        *reinterpret_cast<S4*>(&X_hat[pair * HP + col]) = o;
+        for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(v[q]);
+        store8<S>(&X_hat[pair * HP + col], o);
       } else if (col < HP + GN) {
-        const float w = rw[r];
-        S4 o;
+        S8 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = from_f32<S>(w * v[q]);
-        *reinterpret_cast<S4*>(&B_hat[pair * GN + (col - HP)]) = o;
+        for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(wv * v[q]);
+        store8<S>(&B_hat[pair * GN + (col - HP)], o);
       } else {
-        *reinterpret_cast<floatx4*>(&c_part[pair * GN + (col - HP - GN)]) = v * rw[r];
+        floatx8 o = v * wv;
+        store8<float>(&c_part[pair * GN + (col - HP - GN)], o);
       }
     }
-    __syncthreads();
   }
 }
 
@@ -268,31 +277,24 @@ __global__ __launch_bounds__(256) void mix_c_kernel(const float* __restrict__ c_
 
 template <typename T, class C>
 static hipError_t launch_proj_cfg(const ProjGeom& g, const T* u, const T* wexp,
-                                  const int32_t* sorted, const int32_t* offsets,
-                                  const int32_t* tile_offsets, const float* w,
-                                  typename StreamOf<T>::type* B_hat,
+                                  const int32_t* sorted, const float* sorted_w,
+                                  const int4v* tile_info, typename StreamOf<T>::type* B_hat,
                                   typename StreamOf<T>::type* X_hat, float* c_part,
                                   hipStream_t s) {
   const int pairs = g.M * g.k;
   const int ntiles = proj_row_tiles_max(pairs, g.E, C::BM) * ((g.W + C::BN - 1) / C::BN);
   const dim3 grid((unsigned)((ntiles + 7) / 8 * 8));  // a multiple of the 8 XCDs
-  const size_t lds = ProjLds<T, C>::bytes;
-  hipError_t err = hipFuncSetAttribute((const void*)proj_kernel<T, C>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (err != hipSuccess) return err;
   prof_begin("expert_project", s);
-  hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), lds, s, u, wexp, sorted, offsets,
-                     tile_offsets, w, g.M, g.D, g.W, g.HP(), g.GN(), g.E, g.k, ntiles, X_hat,
-                     B_hat, c_part);
+  hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, u, wexp, sorted, sorted_w,
+                     tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, ntiles, X_hat, B_hat, c_part);
   prof_end(s);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
-                                   const int32_t* sorted, const int32_t* offsets,
-                                   const int32_t* tile_offsets, const float* w, int bm,
-                                   typename StreamOf<T>::type* B_hat,
+                                   const int32_t* sorted, const float* sorted_w,
+                                   const int4v* ti, int bm, typename StreamOf<T>::type* B_hat,
                                    typename StreamOf<T>::type* X_hat, float* c_part,
                                    typename StreamOf<T>::type* C_mix, hipStream_t s) {
   typedef typename StreamOf<T>::type S;
@@ -300,16 +302,16 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
   if constexpr (sizeof(T) == 2) {
     // the 256 x 256 tile needs 2-byte K tiles to fit LDS
     if (bm == 256)
-      err = launch_proj_cfg<T, ProjBig>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+      err = launch_proj_cfg<T, ProjBig>(g, u, wexp, sorted, sorted_w, ti, B_hat, X_hat, c_part, s);
     else if (bm == 128)
-      err = launch_proj_cfg<T, ProjMid>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+      err = launch_proj_cfg<T, ProjMid>(g, u, wexp, sorted, sorted_w, ti, B_hat, X_hat, c_part, s);
     else
-      err = launch_proj_cfg<T, ProjSmall>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+      err = launch_proj_cfg<T, ProjSmall>(g, u, wexp, sorted, sorted_w, ti, B_hat, X_hat, c_part, s);
   } else {
     if (bm >= 128)
-      err = launch_proj_cfg<T, ProjMid>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+      err = launch_proj_cfg<T, ProjMid>(g, u, wexp, sorted, sorted_w, ti, B_hat, X_hat, c_part, s);
     else
-      err = launch_proj_cfg<T, ProjSmall>(g, u, wexp, sorted, offsets, tile_offsets, w, B_hat, X_hat, c_part, s);
+      err = launch_proj_cfg<T, ProjSmall>(g, u, wexp, sorted, sorted_w, ti, B_hat, X_hat, c_part, s);
   }
   if (err != hipSuccess) return err;
   if (!C_mix) return hipGetLastError();
@@ -322,18 +324,15 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
 }
 
 hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const void* w_experts,
-                          const int32_t* sorted, const int32_t* offsets,
-                          const int32_t* tile_offsets, const int32_t* /*idx*/, const float* w,
+                          const int32_t* sorted, const float* sorted_w, const int32_t* tile_info,
                           int bm, void* B_hat, void* X_hat, float* c_part, void* C_mix,
                           hipStream_t s) {
-  if (g.M == 0) return hipSuccess;
+  const int4v* ti = reinterpret_cast<const int4v*>(tile_info);
   if (is_bf16)
-    return launch_project_t<bf16>(g, (const bf16*)u, (const bf16*)w_experts, sorted, offsets,
-                                  tile_offsets, w, bm, (f16*)B_hat, (f16*)X_hat, c_part,
-                                  (f16*)C_mix, s);
-  return launch_project_t<float>(g, (const float*)u, (const float*)w_experts, sorted, offsets,
-                                 tile_offsets, w, bm, (float*)B_hat, (float*)X_hat, c_part,
-                                 (float*)C_mix, s);
+    return launch_project_t<bf16>(g, (const bf16*)u, (const bf16*)w_experts, sorted, sorted_w, ti,
+                                  bm, (f16*)B_hat, (f16*)X_hat, c_part, (f16*)C_mix, s);
+  return launch_project_t<float>(g, (const float*)u, (const float*)w_experts, sorted, sorted_w, ti,
+                                 bm, (float*)B_hat, (float*)X_hat, c_part, (float*)C_mix, s);
 }
 
 }  // namespace swimba
