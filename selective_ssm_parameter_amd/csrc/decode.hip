@@ -34,6 +34,15 @@ __global__ __launch_bounds__(256) void decode_state_kernel(
   const int h = blockIdx.x, b = blockIdx.y;
   const int grp = h / (H / G);
   const int GN = G * N;
+  const int p4 = 4 * (threadIdx.x & 15);
+  const int n0 = threadIdx.x >> 4;
+  float* hs = hstate + ((size_t)b * H + h) * (size_t)N * P;
+  // this thread's state rows, all in flight together with the staging loads
+  constexpr int NR = kDecMaxN / 16;
+  floatx4 hv[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+    if (n0 + 16 * i < N) hv[i] = *reinterpret_cast<const floatx4*>(hs + (size_t)(n0 + 16 * i) * P + p4);
   for (int q = threadIdx.x; q < k * N; q += 256) {
     const int j = q / N, n = q % N;
     sB[j][n] = to_f32(B_hat[((size_t)b * k + j) * GN + grp * N + n]);
@@ -51,18 +60,18 @@ __global__ __launch_bounds__(256) void decode_state_kernel(
   __syncthreads();
 
   const float ah = a[h];
-  const int p4 = 4 * (threadIdx.x & 15);
-  const int n0 = threadIdx.x >> 4;
-  float* hs = hstate + ((size_t)b * H + h) * (size_t)N * P;
   floatx4 xj[kDecMaxK];
   for (int j = 0; j < k; ++j) xj[j] = floatx4{sX[j][p4], sX[j][p4 + 1], sX[j][p4 + 2], sX[j][p4 + 3]};
   floatx4 yacc = {0.f, 0.f, 0.f, 0.f};
-  for (int n = n0; n < N; n += 16) {
-    floatx4* ptr = reinterpret_cast<floatx4*>(hs + (size_t)n * P + p4);
-    floatx4 v = *ptr * ah;
-    for (int j = 0; j < k; ++j) v += sB[j][n] * xj[j];
-    *ptr = v;
-    yacc += sC[n] * v;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int n = n0 + 16 * i;
+    if (n < N) {
+      floatx4 v = hv[i] * ah;
+      for (int j = 0; j < k; ++j) v += sB[j][n] * xj[j];
+      *reinterpret_cast<floatx4*>(hs + (size_t)n * P + p4) = v;
+      yacc += sC[n] * v;
+    }
   }
   red[n0][threadIdx.x & 15] = yacc;
   __syncthreads();

@@ -4,7 +4,8 @@
 // Summary section 2, Expert Routing).
 //
 // One workgroup routes 64 tokens. Wave w computes the logits of tokens
-// [16w, 16w + 16) against every expert with 16x16 matrix-core tiles: the A
+// [16w, 16w + 16) against every expert with 16x16 matrix-core tiles (a
+// workgroup with fewer tokens splits d_model over its waves instead): the A
 // operand is the token rows of u, the B operand the router rows (both are
 // contiguous along d_model, so every lane loads 16 bytes). Products of bf16
 // values are exact in fp32 and accumulate in fp32, so the logits are never
@@ -25,8 +26,8 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
                                                     int E, int k, int32_t* __restrict__ idx,
                                                     float* __restrict__ wout,
                                                     float* __restrict__ logits,
-                                                    int32_t* __restrict__ hist) {
-  extern __shared__ float lg[];  // [64][E + 1]
+                                                    int32_t* __restrict__ hist, int ksplit) {
+  extern __shared__ float lg[];  // [ksplit][64][E + 1] partial logits
   typedef typename Vec<T>::x8 F;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -34,40 +35,69 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
   const int tok0 = blockIdx.x * kRouteTok;
   const int ET = (E + 15) / 16;
   const int ldl = E + 1;
+  // Waves over (token tile, K slice): with few tokens (decode) d_model is
+  // split over the waves that would otherwise be idle (ksplit * ntt <= 4).
+  const int ntt = 4 / ksplit;
+  const int tt = wave % ntt, ks = wave / ntt;
+  const int nsteps = D / 32;
+  const int s0 = ks * nsteps / ksplit, s1 = (ks + 1) * nsteps / ksplit;
 
-  const int row = tok0 + wave * 16 + c;
-  const bool row_ok = row < M;
-  const T* urow = u + (size_t)(row_ok ? row : 0) * D + 8 * g;
+  const int row = tok0 + tt * 16 + c;
+  constexpr uint32_t ES = sizeof(T);
+  // Out-of-range rows (tokens beyond M, experts beyond E) read zeros.
+  const BufRes ru = make_rsrc(u, (uint64_t)M * D * ES);
+  const BufRes rw = make_rsrc(wr, (uint64_t)E * D * ES);
+  const uint32_t uoff = row < M ? ((uint32_t)row * D + 8 * g) * ES : kOOB;
+  float* mylg = lg + (size_t)ks * kRouteTok * ldl;
 
-  // Expert tiles are processed 4 at a time (16 accumulators per lane).
-  for (int et0 = 0; et0 < ET; et0 += 4) {
-    floatx4 acc[4];
+  // Expert tiles are processed 4 at a time (16 accumulators per lane); the K
+  // loop is unrolled so several steps' loads are in flight together.
+  if (ks < ksplit) {
+    for (int et0 = 0; et0 < ET; et0 += 4) {
+      floatx4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < D; k0 += 32) {
-      F a = row_ok ? load8<T>(urow + k0) : zero8<T>();
+      for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      uint32_t woff[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = (et0 + i) * 16 + c;
-        if (et0 + i < ET) {
-          F b = e < E ? load8<T>(wr + (size_t)e * D + k0 + 8 * g) : zero8<T>();
-          acc[i] = mma16(a, b, acc[i]);
+        woff[i] = (et0 + i < ET && e < E) ? ((uint32_t)e * D + 8 * g) * ES : kOOB;
+      }
+#pragma unroll 4
+      for (int st = s0; st < s1; ++st) {
+        const int k0 = 32 * st;
+        const F a = load8_buf<T>(ru, uoff == kOOB ? kOOB : uoff + k0 * ES);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (et0 + i < ET) {
+            const F b = load8_buf<T>(rw, woff[i] == kOOB ? kOOB : woff[i] + k0 * ES);
+            acc[i] = mma16(a, b, acc[i]);
+          }
         }
       }
-    }
-    // acc[i][q] = logit of token (16*wave + 4g + q) for expert (16*(et0+i) + c)
+      // acc[i][q] = partial logit of token (16 tt + 4g + q) for expert (16 (et0+i) + c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = (et0 + i) * 16 + c;
-      if (et0 + i < ET && e < E) {
+      for (int i = 0; i < 4; ++i) {
+        const int e = (et0 + i) * 16 + c;
+        if (et0 + i < ET && e < E) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) lg[(wave * 16 + 4 * g + q) * ldl + e] = acc[i][q];
+          for (int q = 0; q < 4; ++q) mylg[(tt * 16 + 4 * g + q) * ldl + e] = acc[i][q];
+        }
       }
     }
   }
   __syncthreads();
+  // sum the K slices in slice order (deterministic)
+  if (ksplit > 1) {
+    for (int q = threadIdx.x; q < ntt * 16 * ldl; q += blockDim.x) {
+      float sacc = lg[q];
+      for (int j = 1; j < ksplit; ++j) sacc += lg[(size_t)j * kRouteTok * ldl + q];
+      lg[q] = sacc;
+    }
+    __syncthreads();
+  }
 
-  int* hcnt = reinterpret_cast<int*>(lg + kRouteTok * ldl);  // [E + 1]
+  int* hcnt = reinterpret_cast<int*>(lg + (size_t)ksplit * kRouteTok * ldl);  // [E + 1]
   if (hist) {
     for (int e = threadIdx.x; e <= E; e += blockDim.x) hcnt[e] = 0;
     __syncthreads();
@@ -117,7 +147,11 @@ hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M
                         int32_t* idx, float* w, float* logits, hipStream_t s, int32_t* hist) {
   if (M == 0) return hipSuccess;
   dim3 grid((M + kRouteTok - 1) / kRouteTok), block(256);
-  size_t lds = (size_t)kRouteTok * (E + 1) * sizeof(float) + (size_t)(E + 1) * sizeof(int);
+  // one workgroup with at most 16 (32) tokens: d_model split 4 (2) ways, as
+  // long as the partial logits fit 64 KiB of LDS
+  int ksplit = M <= 16 ? 4 : (M <= 32 ? 2 : 1);
+  while (ksplit > 1 && (size_t)ksplit * kRouteTok * (E + 1) * sizeof(float) > 65536) ksplit /= 2;
+  size_t lds = (size_t)ksplit * kRouteTok * (E + 1) * sizeof(float) + (size_t)(E + 1) * sizeof(int);
   hipError_t err = hipFuncSetAttribute(
       is_bf16 ? (const void*)route_kernel<bf16> : (const void*)route_kernel<float>,
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -125,10 +159,10 @@ hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M
   prof_begin("route_topk", s);
   if (is_bf16)
     hipLaunchKernelGGL(route_kernel<bf16>, grid, block, lds, s, (const bf16*)u,
-                       (const bf16*)w_router, M, D, E, k, idx, w, logits, hist);
+                       (const bf16*)w_router, M, D, E, k, idx, w, logits, hist, ksplit);
   else
     hipLaunchKernelGGL(route_kernel<float>, grid, block, lds, s, (const float*)u,
-                       (const float*)w_router, M, D, E, k, idx, w, logits, hist);
+                       (const float*)w_router, M, D, E, k, idx, w, logits, hist, ksplit);
   prof_end(s);
   return hipGetLastError();
 }
