@@ -71,7 +71,7 @@ def kernel_label(symbol):
 def source_digest(kernel):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel] + ["common.hpp", "launch.hpp"]:
+    for f in KERNEL_SOURCES[kernel] + ["common.hpp", "launch.hpp", "lds_tiles.hpp"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
