@@ -50,6 +50,7 @@ hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const 
 struct ScanGeom {
   int Bt, T, H, G, N, P, k, L;
   int es;            // bytes per stream element (2: fp16, 4: fp32)
+  int bt;            // tokens per block of the scan (32 or 64)
   int segs;          // segments per sequence
   int seg_chunks;    // chunks per segment
 };

@@ -44,7 +44,6 @@
 namespace swimba {
 
 constexpr int kP = 64;             // head dim served by these kernels
-constexpr int kBT = 32;            // tokens per block
 constexpr int kScanThreads = 256;  // 4 waves
 
 struct ScanArgs {
@@ -56,7 +55,7 @@ struct ScanArgs {
   void* y;
   float* h_final;
   float* ws;          // [Bt, segs, H, N, P] fp32 segment states
-  const void* gram;   // [Bt, nc, G, npairs, kBT, k*kBT] Gram tiles (stream type)
+  const void* gram;   // [Bt, nc, G, npairs, BT, k*BT] Gram tiles (stream type)
   int T, H, G, N, k, L, segs, seg_chunks, nc, npairs;
 };
 
@@ -67,13 +66,13 @@ struct ScanArgs {
 //   C   [BT][NP]  token rows of C~                     (sigma = 0: readout)
 //   G   [BT][R]   the Gram tile of the block pair      (every step)
 // Rows are sequences of 16-byte chunks; chunk c of row r sits at c ^ swz(r).
-template <typename T, int NP, int KS, bool WITH_Y>
+template <typename T, int NP, int KS, int BT, bool WITH_Y>
 struct ScanLds {
-  static constexpr int R = KS * kBT;
+  static constexpr int R = KS * BT;
   static constexpr int XROW = kP * (int)sizeof(T), BROW = NP * (int)sizeof(T);
   static constexpr int GROW = R * (int)sizeof(T);
   static constexpr int XB = R * XROW, BB = R * BROW;
-  static constexpr int CB = WITH_Y ? kBT * BROW : 0, GB = WITH_Y ? kBT * GROW : 0;
+  static constexpr int CB = WITH_Y ? BT * BROW : 0, GB = WITH_Y ? BT * GROW : 0;
   static constexpr int XO = 0, BO = XB, CO = XB + BB, GO = XB + BB + CB;
   static constexpr int STAGE = XB + BB + CB + GB;
   static constexpr size_t bytes = 2 * (size_t)STAGE;
@@ -86,9 +85,9 @@ __device__ __forceinline__ float apow(float la, int d) {
 
 // Fragments (t-tile tt, pair k-step q) of a diagonal block pair: a fragment is
 // zero when every (t, r) in it has s > t; the others get a per-lane mask.
-template <int KS>
+template <int KS, int BT>
 struct DiagFrags {
-  static constexpr int TT = kBT / 16, RQ = KS;  // k-steps of 32 pairs per block
+  static constexpr int TT = BT / 16, RQ = KS * BT / 32;  // k-steps of 32 pairs per block
   static constexpr bool zero(int tt, int q) { return 16 * tt + 15 - (32 * q) / KS < 0; }
   static constexpr int index(int tt, int q) {
     int n = 0;
@@ -115,12 +114,12 @@ struct ScanStep {
 
 // Gram tiles G[t, r] = C~[c0 + tau*BT + t] . B_hat[(c0 + sig*BT)*k + r] (fp32
 // accumulation, stored in the stream type) for one (block pair, chunk, batch).
-template <typename T, int NP, int KS>
+template <typename T, int NP, int KS, int BT>
 __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_hat,
                                                         const T* __restrict__ C_mix,
                                                         T* __restrict__ gram, int Tlen, int G,
                                                         int N, int L, int nc, int npairs) {
-  constexpr int BT = kBT, R = KS * BT, TT = BT / 16, RT = R / 16;
+  constexpr int R = KS * BT, TT = BT / 16, RT = R / 16;
   constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
   typedef typename Vec<T>::x4 F4;
@@ -156,13 +155,13 @@ __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_
   }
 }
 
-template <typename T, typename TY, int NP, int KS, bool WITH_Y>
+template <typename T, typename TY, int NP, int KS, int BT, bool WITH_Y>
 __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_kernel(ScanArgs A) {
-  typedef ScanLds<T, NP, KS, WITH_Y> Lay;
-  constexpr int BT = kBT, R = Lay::R;
+  typedef ScanLds<T, NP, KS, BT, WITH_Y> Lay;
+  constexpr int R = Lay::R;
   constexpr int TT = BT / 16, RQ = R / 32, NT = NP / 16, NQ = NP / 32;
   constexpr int XC = Lay::XROW / 16, BC = Lay::BROW / 16, GC = Lay::GROW / 16;  // chunks per row
-  typedef DiagFrags<KS> DF;
+  typedef DiagFrags<KS, BT> DF;
   constexpr int NDF = DF::count() > 0 ? DF::count() : 1;
   constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
@@ -545,13 +544,21 @@ static int scan_target_wgs() {
   return w > 0 ? w : 384;
 }
 
-static int scan_npairs(int L) {
-  const int nb = (L + kBT - 1) / kBT;
+static int scan_npairs(int L, int bt) {
+  const int nb = (L + bt - 1) / bt;
   return nb * (nb + 1) / 2;
 }
 
+// Tokens per block. 64-token blocks (one step per 64-token chunk, two stages
+// of 80 KiB) measured slower than 32-token blocks with two workgroups per CU,
+// so the walk uses 32; the kernels stay templated on the block size.
+static int scan_block(int N, int k, int L, int es) {
+  (void)N, (void)k, (void)L, (void)es;
+  return 32;
+}
+
 ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es) {
-  ScanGeom g{Bt, T, H, G, N, P, k, L, es, 1, 1};
+  ScanGeom g{Bt, T, H, G, N, P, k, L, es, scan_block(N, k, L, es), 1, 1};
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
   const int units = Bt * H;
@@ -572,7 +579,7 @@ static size_t scan_state_bytes(const ScanGeom& g) {
 
 static size_t scan_gram_bytes(const ScanGeom& g) {
   const size_t nc = (size_t)((g.T + g.L - 1) / g.L);
-  return align256((size_t)g.Bt * nc * g.G * scan_npairs(g.L) * kBT * (g.k * kBT) * g.es);
+  return align256((size_t)g.Bt * nc * g.G * scan_npairs(g.L, g.bt) * g.bt * (g.k * g.bt) * g.es);
 }
 
 size_t scan_ws_bytes(const ScanGeom& g) {
@@ -580,13 +587,13 @@ size_t scan_ws_bytes(const ScanGeom& g) {
   return scan_state_bytes(g) + scan_gram_bytes(g);
 }
 
-template <typename T, typename TY, int NP, int KS>
+template <typename T, typename TY, int NP, int KS, int BT>
 static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s) {
-  auto k3 = scan_kernel<T, TY, NP, KS, true>;
-  auto k1 = scan_kernel<T, TY, NP, KS, false>;
+  auto k3 = scan_kernel<T, TY, NP, KS, BT, true>;
+  auto k1 = scan_kernel<T, TY, NP, KS, BT, false>;
   const size_t l3 = 0, l1 = 0;  // static LDS (two stage arrays)
   prof_begin("scan_gram", s);
-  hipLaunchKernelGGL((scan_gram_kernel<T, NP, KS>), dim3(args.npairs * g.G, args.nc, g.Bt),
+  hipLaunchKernelGGL((scan_gram_kernel<T, NP, KS, BT>), dim3(args.npairs * g.G, args.nc, g.Bt),
                      dim3(256), 0, s, static_cast<const T*>(args.B_hat),
                      static_cast<const T*>(args.C_mix), static_cast<T*>(const_cast<void*>(args.gram)),
                      g.T, g.G, g.N, g.L, args.nc, args.npairs);
@@ -607,10 +614,16 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   return hipGetLastError();
 }
 
+template <typename T, typename TY, int NP, int KS>
+static hipError_t dispatch_bt(const ScanGeom& g, const ScanArgs& a, hipStream_t s) {
+  (void)g;
+  return launch_scan_t<T, TY, NP, KS, 32>(g, a, s);
+}
+
 template <typename T, typename TY, int NP>
 static hipError_t dispatch_ks(const ScanGeom& g, const ScanArgs& a, hipStream_t s) {
-  if (g.k == 1) return launch_scan_t<T, TY, NP, 1>(g, a, s);
-  return launch_scan_t<T, TY, NP, 2>(g, a, s);
+  if (g.k == 1) return dispatch_bt<T, TY, NP, 1>(g, a, s);
+  return dispatch_bt<T, TY, NP, 2>(g, a, s);
 }
 
 template <typename T, typename TY>
@@ -632,7 +645,7 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
   const int nc = (g.T + g.L - 1) / g.L;
   unsigned char* gram = reinterpret_cast<unsigned char*>(ws) + scan_state_bytes(g);
   ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws, gram,
-                g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks, nc, scan_npairs(g.L)};
+                g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks, nc, scan_npairs(g.L, g.bt)};
   if (is_bf16) return dispatch_np<f16, bf16>(g, args, s);
   return dispatch_np<float, float>(g, args, s);
 }
