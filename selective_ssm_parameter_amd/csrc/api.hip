@@ -97,9 +97,10 @@ struct ProjWs {
 
 ProjWs proj_ws(const Dims& d) {
   const int64_t pairs = d.M * d.k;
-  // histograms: blocks of kBucketPairs pairs, or of kRouteTok tokens when the
-  // router wrote them (decode); the latter is never fewer blocks (k <= 8).
-  const int64_t nblk = std::max<int64_t>(bucket_blocks((int)pairs), (d.M + kRouteTok - 1) / kRouteTok);
+  // histograms: blocks of kBucketPairs pairs, or of the router's workgroup
+  // tokens when the router wrote them (decode)
+  const int64_t tpw = route_tokens_per_wg(d.M);
+  const int64_t nblk = std::max<int64_t>(bucket_blocks((int)pairs), (d.M + tpw - 1) / tpw);
   ProjWs w{};
   size_t off = 0;
   w.counts = off; off += align256(sizeof(int32_t) * nblk * (d.E + 1));
@@ -166,7 +167,7 @@ ProjGeom proj_geom(const Dims& d, int64_t M) {
 
 // Runs bucketing, the grouped projection and (with C_mix non-null) the
 // slot-ordered C sum for M tokens. routed: the router already wrote the
-// per-kRouteTok-token expert histograms into the workspace.
+// expert histograms of its workgroups' tokens into the workspace.
 hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_experts,
                        const int32_t* idx, const float* w, void* B_hat, void* X_hat, void* C_mix,
                        unsigned char* ws, hipStream_t s, bool routed = false) {
@@ -185,7 +186,7 @@ hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_ex
   const int ntiles_max = proj_row_tiles_max(pairs, (int)d.E, bm);
   hipError_t e = launch_bucket(d.bf16, idx, w, pairs, (int)d.E, bm, ntiles_max, counts, offsets,
                                tiles, sorted, sortw, X_hat, (int)d.HP, B_hat, (int)d.GN, cpart, s,
-                               routed ? kRouteTok * (int)d.k : 0, routed);
+                               routed ? (int)(route_tokens_per_wg(M) * d.k) : 0, routed);
   if (e != hipSuccess) return e;
   return launch_project(d.bf16, proj_geom(d, M), u, w_experts, sorted, sortw, tiles, bm, B_hat,
                         X_hat, cpart, C_mix, s);

@@ -17,87 +17,141 @@
 
 namespace swimba {
 
-constexpr int kDecMaxK = 8;
-constexpr int kDecMaxN = 128;
-
-template <typename S, typename TY>
-__global__ __launch_bounds__(256) void decode_state_kernel(
+// N (state size) and KM (a bound on k; k itself is a run-time argument) are
+// compile-time so every load is issued up front and the row loop unrolls.
+template <typename S, typename TY, int N, int KM>
+__global__ __launch_bounds__(256, 4) void decode_state_kernel(
     const S* __restrict__ B_hat, const S* __restrict__ X_hat, const float* __restrict__ c_part,
     const float* __restrict__ a, float* __restrict__ hstate, TY* __restrict__ y, int H, int G,
-    int N, int k) {
+    int k) {
   constexpr int P = 64;
-  __shared__ float sB[kDecMaxK][kDecMaxN];
-  __shared__ float sX[kDecMaxK][P];
-  __shared__ float sC[kDecMaxN];
+  constexpr int NR = N / 16;                  // state rows per thread
+  constexpr int QN = (KM * N + 255) / 256;    // B_hat / c_part staging loads per thread
+  constexpr int QP = (KM * P + 255) / 256;    // X_hat staging loads per thread
+  __shared__ float sB[KM][N];
+  __shared__ float sCp[KM][N];
+  __shared__ float sX[KM][P];
+  __shared__ float sC[N];
   __shared__ floatx4 red[16][16];
 
+  const int t = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
   const int grp = h / (H / G);
   const int GN = G * N;
-  const int p4 = 4 * (threadIdx.x & 15);
-  const int n0 = threadIdx.x >> 4;
+  const int p4 = 4 * (t & 15);
+  const int n0 = t >> 4;
   float* hs = hstate + ((size_t)b * H + h) * (size_t)N * P;
-  // this thread's state rows, all in flight together with the staging loads
-  constexpr int NR = kDecMaxN / 16;
+
+  // every HBM read of this workgroup is in flight before the first wait
   floatx4 hv[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i)
-    if (n0 + 16 * i < N) hv[i] = *reinterpret_cast<const floatx4*>(hs + (size_t)(n0 + 16 * i) * P + p4);
-  for (int q = threadIdx.x; q < k * N; q += 256) {
-    const int j = q / N, n = q % N;
-    sB[j][n] = to_f32(B_hat[((size_t)b * k + j) * GN + grp * N + n]);
+    hv[i] = *reinterpret_cast<const floatx4*>(hs + (size_t)(n0 + 16 * i) * P + p4);
+  // staging loads are unconditional (clamped index) so none waits behind a branch
+  float bq[QN], cq[QN], xq[QP];
+#pragma unroll
+  for (int r = 0; r < QN; ++r) {
+    const int q = min(t + 256 * r, k * N - 1);
+    const size_t row = ((size_t)b * k + q / N) * GN + grp * N + q % N;
+    bq[r] = to_f32(B_hat[row]);
+    cq[r] = c_part[row];
   }
-  for (int q = threadIdx.x; q < k * P; q += 256) {
-    const int j = q / P, p = q % P;
-    sX[j][p] = to_f32(X_hat[((size_t)b * k + j) * H * P + (size_t)h * P + p]);
+#pragma unroll
+  for (int r = 0; r < QP; ++r) {
+    const int q = min(t + 256 * r, k * P - 1);
+    xq[r] = to_f32(X_hat[((size_t)b * k + q / P) * H * P + (size_t)h * P + q % P]);
   }
+#pragma unroll
+  for (int r = 0; r < QN; ++r) {
+    const int q = t + 256 * r;
+    if (q < k * N) {
+      sB[q / N][q % N] = bq[r];
+      sCp[q / N][q % N] = cq[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < QP; ++r) {
+    const int q = t + 256 * r;
+    if (q < k * P) sX[q / P][q % P] = xq[r];
+  }
+  __syncthreads();
   // C~ = sum_j c_part[b, j] in slot order (fp32), rounded to the stream type
-  for (int n = threadIdx.x; n < N; n += 256) {
+  if (t < N) {
     float cs = 0.f;
-    for (int j = 0; j < k; ++j) cs += c_part[((size_t)b * k + j) * GN + grp * N + n];
-    sC[n] = to_f32(from_f32<S>(cs));
+    for (int j = 0; j < k; ++j) cs += sCp[j][t];
+    sC[t] = to_f32(from_f32<S>(cs));
   }
   __syncthreads();
 
   const float ah = a[h];
-  floatx4 xj[kDecMaxK];
-  for (int j = 0; j < k; ++j) xj[j] = floatx4{sX[j][p4], sX[j][p4 + 1], sX[j][p4 + 2], sX[j][p4 + 3]};
+  floatx4 xj[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    xj[j] = j < k ? floatx4{sX[j][p4], sX[j][p4 + 1], sX[j][p4 + 2], sX[j][p4 + 3]}
+                  : floatx4{0.f, 0.f, 0.f, 0.f};
   floatx4 yacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     const int n = n0 + 16 * i;
-    if (n < N) {
-      floatx4 v = hv[i] * ah;
-      for (int j = 0; j < k; ++j) v += sB[j][n] * xj[j];
-      *reinterpret_cast<floatx4*>(hs + (size_t)n * P + p4) = v;
-      yacc += sC[n] * v;
-    }
+    floatx4 v = hv[i] * ah;
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) v += sB[j][n] * xj[j];
+    *reinterpret_cast<floatx4*>(hs + (size_t)n * P + p4) = v;
+    yacc += sC[n] * v;
   }
-  red[n0][threadIdx.x & 15] = yacc;
+  red[n0][t & 15] = yacc;
   __syncthreads();
-  if (threadIdx.x < 16) {
-    floatx4 s = red[0][threadIdx.x];
-    for (int r = 1; r < 16; ++r) s += red[r][threadIdx.x];
-    TY* yo = y + ((size_t)b * H + h) * P + 4 * threadIdx.x;
+  if (t < 16) {
+    floatx4 s = red[0][t];
+    for (int r = 1; r < 16; ++r) s += red[r][t];
+    TY* yo = y + ((size_t)b * H + h) * P + 4 * t;
 #pragma unroll
     for (int i = 0; i < 4; ++i) yo[i] = from_f32<TY>(s[i]);
   }
 }
 
+template <int N, int KM>
+static void launch_decode_state_t(bool is_bf16, dim3 grid, const void* B_hat, const void* X_hat,
+                                  const float* c_part, const float* a, float* h, void* y, int H,
+                                  int G, int k, hipStream_t s) {
+  if (is_bf16)
+    hipLaunchKernelGGL((decode_state_kernel<f16, bf16, N, KM>), grid, dim3(256), 0, s,
+                       (const f16*)B_hat, (const f16*)X_hat, c_part, a, h, (bf16*)y, H, G, k);
+  else
+    hipLaunchKernelGGL((decode_state_kernel<float, float, N, KM>), grid, dim3(256), 0, s,
+                       (const float*)B_hat, (const float*)X_hat, c_part, a, h, (float*)y, H, G,
+                       k);
+}
+
+template <int N>
+static void launch_decode_state_n(bool is_bf16, dim3 grid, const void* B_hat, const void* X_hat,
+                                  const float* c_part, const float* a, float* h, void* y, int H,
+                                  int G, int k, hipStream_t s) {
+  if (k <= 1)
+    launch_decode_state_t<N, 1>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s);
+  else if (k <= 2)
+    launch_decode_state_t<N, 2>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s);
+  else if (k <= 4)
+    launch_decode_state_t<N, 4>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s);
+  else
+    launch_decode_state_t<N, 8>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s);
+}
+
 hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
                                const void* B_hat, const void* X_hat, const float* c_part,
                                const float* a, float* h, void* y, hipStream_t s) {
-  (void)P;
   if (Bt == 0) return hipSuccess;
+  if (P != 64 || k < 1 || k > 8 || (N != 16 && N != 32 && N != 64 && N != 128))
+    return hipErrorInvalidValue;
   prof_begin("decode_state", s);
-  if (is_bf16)
-    hipLaunchKernelGGL((decode_state_kernel<f16, bf16>), dim3(H, Bt), dim3(256), 0, s,
-                       (const f16*)B_hat, (const f16*)X_hat, c_part, a, h, (bf16*)y,
-                       H, G, N, k);
-  else
-    hipLaunchKernelGGL((decode_state_kernel<float, float>), dim3(H, Bt), dim3(256), 0, s,
-                       (const float*)B_hat, (const float*)X_hat, c_part, a, h,
-                       (float*)y, H, G, N, k);
+  const dim3 grid(H, Bt);
+  switch (N) {
+    case 16: launch_decode_state_n<16>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s); break;
+    case 32: launch_decode_state_n<32>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s); break;
+    case 64: launch_decode_state_n<64>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s); break;
+    default: launch_decode_state_n<128>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s); break;
+  }
   prof_end(s);
   return hipGetLastError();
 }

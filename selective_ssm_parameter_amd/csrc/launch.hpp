@@ -19,8 +19,12 @@ struct ProjGeom {
 };
 
 // Router: logits (fp32), softmax, top-k. With `hist` non-null it also writes
-// the expert histogram of each workgroup's kRouteTok tokens ([nblk][E+1]).
+// the expert histogram of each workgroup's route_tokens_per_wg(M) tokens
+// ([nblk][E+1]).
 constexpr int kRouteTok = 64;
+// tokens per router workgroup: 16 for up to 1024 tokens (decode batches),
+// so at least a few dozen workgroups share the router weights' reads
+inline int route_tokens_per_wg(int64_t M) { return M <= 1024 ? 16 : kRouteTok; }
 hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M, int D, int E, int k,
                         int32_t* idx, float* w, float* logits, hipStream_t s,
                         int32_t* hist = nullptr);
