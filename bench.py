@@ -4,6 +4,9 @@ One step = one pass of the whole path over one batch of synthetic input:
 route + top-k, expert projection with the mix epilogue, the chunked scan over
 the batch (prefill), then one recurrent decode step of every sequence from
 the prefill's final state. Inputs are resident in HBM before timing starts.
+The recurrent decode workload (``--config c5``: batch 256, one token per
+sequence per step, the N x P state of every head resident in HBM) times
+decode steps alone: one step = one token of every sequence.
 
 Prints ONE JSON line. ``value`` is tokens per second (prefill tokens plus the
 decoded tokens) over the timed steps. ``roofline`` describes the kernel with
@@ -42,7 +45,7 @@ KERNEL_NAMES = [
     (r"route_kernel", "route_topk"),
     (r"bucket_count_kernel", "bucket_count"),
     (r"bucket_place_kernel", "bucket_place"),
-    (r"proj_kernel", "expert_project"),
+    (r"proj_kernel|proj_skinny_kernel", "expert_project"),
     (r"mix_c_kernel", "mix_c"),
     (r"scan_gram_kernel", "scan_gram"),
     (r"scan_kernel.*Lb0E", "scan_segment_state"),
@@ -57,6 +60,7 @@ KERNEL_SOURCES = {
     "route_topk": ["route.hip"],
     "expert_project": ["project.hip"],
     "scan_chunk_output": ["scan.hip"],
+    "decode_state": ["decode.hip"],
 }
 
 
@@ -99,11 +103,18 @@ def workload(name):
     return synth.WORKLOADS[name]
 
 
+def is_decode(wl):
+    return wl.decode_steps > 0
+
+
 def kernel_models(wl):
-    """Algorithmic work per launch of each kernel, for one prefill of ``wl``.
+    """Algorithmic work per launch of each kernel, for one prefill of ``wl``
+    (one decode step for the decode workload).
 
     Returns {kernel: (bound, flops, bytes)}. Bytes count each tensor a kernel
     must read or write once; flops count multiply-adds as 2."""
+    if is_decode(wl):
+        return decode_models(wl)
     M, D, E, k = wl.tokens, wl.d_model, wl.n_experts, wl.top_k
     H, P, N, G, L = wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.chunk
     W, HP, GN = wl.width, H * P, G * N
@@ -128,6 +139,26 @@ def kernel_models(wl):
     }
 
 
+def decode_models(wl):
+    """One decode step of every sequence: the state update reads and writes
+    each head's fp32 N x P state once; the projection reads the weights of
+    every expert some token chose (all E at this batch size)."""
+    Bt, D, E, k = wl.batch, wl.d_model, wl.n_experts, wl.top_k
+    H, P, N, G = wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    W, HP, GN = wl.width, H * P, G * N
+    ei = 2 if wl.dtype == "bf16" else 4
+    es = 2 if wl.dtype == "bf16" else 4
+    pairs = Bt * k
+    state = 2 * Bt * H * N * P * 4
+    streams = pairs * (HP + GN) * es + pairs * GN * 4
+    return {
+        "route_topk": ("hbm", 2 * Bt * D * E, Bt * D * ei + E * D * ei + pairs * 8),
+        "expert_project": ("hbm", 2 * pairs * D * W,
+                           Bt * D * ei + E * W * D * ei + streams + pairs * 8),
+        "decode_state": ("hbm", 4 * pairs * H * N * P, state + streams + Bt * HP * ei),
+    }
+
+
 def run_gpu(args):
     import torch
 
@@ -143,21 +174,34 @@ def run_gpu(args):
     def up(x, t=dt):
         return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev, t)
 
-    u = up(inp["u"].reshape(wl.tokens, -1))
     wr, we, a = up(inp["w_router"]), up(inp["w_experts"]), up(inp["a"], torch.float32)
-    dims = sb.dims_of(wl)
-    buf = sb.alloc_buffers(dims, dev)
+    if not is_decode(wl):
+        u = up(inp["u"].reshape(wl.tokens, -1))
+        dims = sb.dims_of(wl)
+        buf = sb.alloc_buffers(dims, dev)
     ddims = sb.dims_of(wl, seqlen=1)
     dws, _ = sb.workspace(ddims, sb.CALL_DECODE, dev)
     u_dec = up(synth.decode_token(wl, 0))
     y_dec = torch.empty(wl.batch, wl.nheads, wl.headdim, dtype=dt, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        # prefill the batch, then decode one more token of every sequence,
-        # updating the prefill's final state in place
-        sb.forward(dims, u, wr, we, a, None, buf)
-        sb.swimba_decode_step(ddims, u_dec, wr, we, a, buf.h_final, y_dec, None, dws)
+    if is_decode(wl):
+        # decode only: the state starts from the workload's initial state and
+        # is updated in place; tokens cycle through a few seeded draws
+        h_state = up(inp["h_init"], torch.float32)
+        toks = [up(synth.decode_token(wl, i)) for i in range(8)]
+        count = [0]
+
+        def step():
+            sb.swimba_decode_step(ddims, toks[count[0] % len(toks)], wr, we, a, h_state, y_dec,
+                                  None, dws)
+            count[0] += 1
+    else:
+        def step():
+            # prefill the batch, then decode one more token of every sequence,
+            # updating the prefill's final state in place
+            sb.forward(dims, u, wr, we, a, None, buf)
+            sb.swimba_decode_step(ddims, u_dec, wr, we, a, buf.h_final, y_dec, None, dws)
 
     for _ in range(args.warmup):
         step()
@@ -170,6 +214,8 @@ def run_gpu(args):
     torch.cuda.synchronize()
     report = json.loads(sb.profile_report())
     sb.profile_enable(False)
+    if is_decode(wl):  # the library names decode launches decode_<kernel>
+        report = {n[len("decode_"):]: r for n, r in report.items() if n.startswith("decode_")}
     models = kernel_models(wl)
     kernels = {n: {"launches": r["launches"], "avg_us": 1e3 * r["ms"] / r["launches"]}
                for n, r in report.items()}
@@ -185,7 +231,7 @@ def run_gpu(args):
 
     # The timed region: the dominant kernel is bracketed by HIP events recorded
     # on the stream it runs on.
-    sb.profile_select(dom)
+    sb.profile_select(("decode_" if is_decode(wl) else "") + dom)
     sb.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -194,6 +240,8 @@ def run_gpu(args):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     rep_dom = json.loads(sb.profile_report())
+    if is_decode(wl):
+        rep_dom = {n[len("decode_"):]: r for n, r in rep_dom.items() if n.startswith("decode_")}
     sb.profile_enable(False)
     sb.profile_select(None)
 
@@ -207,7 +255,7 @@ def run_gpu(args):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    tokens = wl.tokens + wl.batch
+    tokens = wl.batch if is_decode(wl) else wl.tokens + wl.batch
     value = tokens * args.steps / elapsed
     bound, flops, nbytes = models[dom]
     avg_s = rep_dom[dom]["ms"] / rep_dom[dom]["launches"] / 1e3
@@ -230,11 +278,84 @@ def run_gpu(args):
     }
 
 
+E_SWEEP = (4, 8, 16, 32, 64)
+
+
+def e_sweep(args):
+    """Prefill tokens/s at the c3 dimensions with E experts, k = 2, for each E
+    in E_SWEEP (seed 30 + E): the recurrence has no E term and projection
+    FLOPs depend on k only, so only the weight bytes and the router grow with
+    E. Prints one JSON line per E and writes a markdown table."""
+    import torch
+
+    from selective_ssm_parameter_amd import binding as sb
+    from selective_ssm_parameter_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    rows = []
+    for E in E_SWEEP:
+        wl = synth.WORKLOADS["c3"].replace(name=f"c3_E{E}", seed=30 + E, n_experts=E)
+        inp = synth.make_inputs(wl)
+
+        def up(x, t=torch.bfloat16):
+            return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev, t)
+
+        u = up(inp["u"].reshape(wl.tokens, -1))
+        wr, we, a = up(inp["w_router"]), up(inp["w_experts"]), up(inp["a"], torch.float32)
+        del inp
+        dims = sb.dims_of(wl)
+        buf = sb.alloc_buffers(dims, dev)
+        for _ in range(args.warmup):
+            sb.forward(dims, u, wr, we, a, None, buf)
+        torch.cuda.synchronize()
+        sb.profile_select(None)
+        sb.profile_enable(True)
+        for _ in range(args.steps):
+            sb.forward(dims, u, wr, we, a, None, buf)
+        torch.cuda.synchronize()
+        report = json.loads(sb.profile_report())
+        sb.profile_enable(False)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            sb.forward(dims, u, wr, we, a, None, buf)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        kern = {n: 1e3 * r["ms"] / r["launches"] for n, r in report.items()}
+        row = {"E": E, "k": wl.top_k, "tokens_per_s": wl.tokens * args.steps / elapsed,
+               "ms_per_step": 1e3 * elapsed / args.steps, "kernels_us": kern,
+               "weight_MB": E * wl.width * wl.d_model * 2 / 1e6}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del u, wr, we, a, buf
+        torch.cuda.empty_cache()
+    if args.out:
+        base = rows[0]["tokens_per_s"]
+        names = [n for n in rows[0]["kernels_us"]]
+        lines = ["# Prefill tokens/s against the number of experts (c3 dimensions, k = 2)", "",
+                 "Command (from the repository root, after building the library):", "",
+                 "    " + (" ".join(args.command) or "python bench.py --e-sweep"), "",
+                 f"Batch 4 x T 8192 tokens, d_model 2048, 64 heads, P 64, N 128, chunk 128, "
+                 f"bf16; seed 30 + E; {args.steps} timed steps after {args.warmup} warm-up "
+                 "steps; per-kernel times from HIP events around each launch in a separate "
+                 "pass.", "",
+                 "| E | weights MB | tokens/s (M) | vs E=4 | ms/step | "
+                 + " | ".join(n + " us" for n in names) + " |",
+                 "|---:|---:|---:|---:|---:|" + "---:|" * len(names)]
+        for r in rows:
+            lines.append(f"| {r['E']} | {r['weight_MB']:.0f} | {r['tokens_per_s'] / 1e6:.2f} | "
+                         f"{r['tokens_per_s'] / base:.3f} | {r['ms_per_step']:.3f} | "
+                         + " | ".join(f"{r['kernels_us'].get(n, 0):.1f}" for n in names) + " |")
+        open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """The fp64 oracle on a bounded sample: the first rows of the batch, all
     heads, whole sequences; rows are added until ``budget_s`` is used."""
     from oracle import swimba as osw
     from selective_ssm_parameter_amd import synth
+    if is_decode(wl):
+        return cpu_baseline_decode(wl, budget_s)
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -253,6 +374,32 @@ def cpu_baseline(wl, budget_s=20.0):
     return {"value": done_tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} of {wl.batch} sequences x {wl.seqlen} tokens, all heads, "
                       f"prefill only, {spent:.1f} s"}
+
+
+def cpu_baseline_decode(wl, budget_s):
+    """The fp64 oracle's decode step on growing slices of the batch (all
+    heads, the workload's initial state) until ``budget_s`` is used."""
+    from oracle import swimba as osw
+    from selective_ssm_parameter_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    inp = synth.make_inputs(wl)
+    done, spent, step, rows = 0, 0.0, 0, 8
+    while spent < budget_s and step < wl.decode_steps:
+        u_t = synth.decode_token(wl, step)[:rows]
+        t0 = time.perf_counter()
+        osw.decode_step(u_t, inp["w_router"], inp["w_experts"], inp["a"], inp["h_init"][:rows],
+                        nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
+                        dstate=wl.dstate, top_k=wl.top_k)
+        spent += time.perf_counter() - t0
+        done += rows
+        step += 1
+    return {"value": done / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{step} decode steps of {rows} of {wl.batch} sequences, all heads, "
+                      f"{spent:.1f} s"}
 
 
 def find_csv(d, suffix):
@@ -280,7 +427,8 @@ def summarize_trace(trace_dir, wl_name, out, command, bench_json=None):
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     total = sum(sum(v) for v in groups.values())
     stats = find_csv(trace_dir, "kernel_stats.csv")
-    lines = [f"# Kernel durations, bench step (prefill + decode) on workload {wl_name}", "",
+    kind = "decode steps" if is_decode(workload(wl_name)) else "bench step (prefill + decode)"
+    lines = [f"# Kernel durations, {kind} on workload {wl_name}", "",
              "Command (from the repository root, after building the library):", "",
              "    " + command, "",
              f"Source: `{os.path.basename(stats)}` and the kernel trace of that run; "
@@ -346,8 +494,9 @@ def summarize_pmc(fetch_dir, write_dir, wl_name, out, commands):
               f"{CALIB_BYTES >> 20} MiB; per copy FETCH_SIZE read {fk:.0f} KiB (scale {fs:.4f}) "
               f"and WRITE_SIZE {wk:.0f} KiB (scale {ws_:.4f}). Counter KiB x 1024 x scale "
               "= bytes.", "",
-              "Launches on the larger grid are the prefill's, those on the smaller one the "
-              "decode step's; the algorithmic bytes are those of the prefill launch.", "",
+              ("Every launch is a decode step's." if is_decode(wl) else
+               "Launches on the larger grid are the prefill's, those on the smaller one the "
+               "decode step's; the algorithmic bytes are those of the prefill launch."), "",
               "| kernel | workgroups | read MB | written MB | traffic MB | algorithmic MB |",
               "|---|---:|---:|---:|---:|---:|"]
     keys = sorted(set(fetch) | set(write), key=lambda k: -(fetch.get(k, 0) + write.get(k, 0)))
@@ -360,7 +509,7 @@ def summarize_pmc(fetch_dir, write_dir, wl_name, out, commands):
                      f"{(rd + wr) / 1e6:.1f} | {alg} |")
         if k[0] in KERNEL_SOURCES and (k[0] not in best or k[1] > best[k[0]][0]):
             best[k[0]] = (k[1], rd + wr)
-    lines += ["", "Machine-readable (kernel, bytes per launch at the prefill grid, "
+    lines += ["", "Machine-readable (kernel, bytes per launch at the largest grid, "
               "digest of the sources the kernel is built from):", ""]
     for k, (_, b) in sorted(best.items()):
         lines.append(f"traffic: {k} {int(round(b))} {source_digest(k)}")
@@ -373,7 +522,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with copies of known size (scales HBM counters)")
@@ -382,6 +531,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary of two rocprofv3 --pmc runs")
     ap.add_argument("--out", help="summary file to write")
+    ap.add_argument("--e-sweep", action="store_true",
+                    help="prefill tokens/s at the c3 dimensions for E in 4..64 (k = 2)")
     ap.add_argument("--bench-json", help="the JSON output of the profiled bench run")
     ap.add_argument("--command", action="append", default=[],
                     help="the command(s) that produced the profile, for the summary")
@@ -398,6 +549,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.e_sweep:
+        e_sweep(args)
+        return
     r = run_gpu(args)
     wl = r["wl"]
     out = {
@@ -414,7 +568,12 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": (f"Swimba mixer prefill + 1 decode step, {wl.dtype}: batch {wl.batch}, "
+            "workload": (f"Swimba recurrent decode step, {wl.dtype}: batch {wl.batch}, "
+                         f"one token per sequence per step, d_model={wl.d_model}, "
+                         f"heads={wl.nheads}, P={wl.headdim}, N={wl.dstate} fp32 state per "
+                         f"head in HBM, E={wl.n_experts}, top-k={wl.top_k}")
+            if is_decode(wl) else
+                        (f"Swimba mixer prefill + 1 decode step, {wl.dtype}: batch {wl.batch}, "
                          f"T={wl.seqlen}, d_model={wl.d_model}, heads={wl.nheads}, "
                          f"P={wl.headdim}, N={wl.dstate}, E={wl.n_experts}, "
                          f"top-k={wl.top_k}, chunk {wl.chunk}"),

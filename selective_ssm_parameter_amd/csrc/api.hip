@@ -106,7 +106,7 @@ ProjWs proj_ws(const Dims& d) {
   w.counts = off; off += align256(sizeof(int32_t) * nblk * (d.E + 1));
   w.offsets = off; off += align256(sizeof(int32_t) * (d.E + 2));
   // tile table: 4 ints per row tile, for the smallest row tile (most tiles)
-  w.tiles = off; off += align256(sizeof(int32_t) * 4 * (size_t)proj_row_tiles_max((int)pairs, (int)d.E, 64));
+  w.tiles = off; off += align256(sizeof(int32_t) * 4 * ((size_t)proj_row_tiles_max((int)pairs, (int)d.E, 64) + 1));
   w.sorted = off; off += align256(sizeof(int32_t) * pairs);
   w.sortw = off; off += align256(sizeof(float) * pairs);
   w.cpart = off; off += align256(sizeof(float) * pairs * d.GN);

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(const int32_t* __rest
 // Workgroup 0 also writes the bucket offsets and the GEMM tile schedule:
 //   offsets[0..E+1]: start of each bucket and the end;
 //   tile_info[t] = {expert, first sorted row, rows} for the row tiles of bm
-//   pairs of every real expert in order, {-1, 0, 0} up to ntiles_max.
+//   pairs of every real expert in order, {-1, 0, 0} up to ntiles_max, and
+//   tile_info[ntiles_max] = {number of real tiles, 0, 0, 0}.
 // Next to each sorted pair id goes its top-k weight (sorted_w), so the GEMM
 // reads a tile's rows with one round trip.
 template <typename T>
@@ -141,6 +142,7 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(
     }
     for (int t = tprefix[E] + threadIdx.x; t < ntiles_max; t += blockDim.x)
       tile_info[t] = int4v{-1, 0, 0, 0};
+    if (threadIdx.x == 0) tile_info[ntiles_max] = int4v{tprefix[E], 0, 0, 0};
   }
 
   // ---- stable placement of this block's pairs

@@ -34,7 +34,8 @@ constexpr int kBucketPairs = 1024;  // pairs per bucketing block
 int bucket_blocks(int pairs);
 // block_pairs: pairs per bucketing block (0 = kBucketPairs); counted: the
 // histograms [nblk][E+1] are already in `counts` (written by the router).
-// tile_info: 4 ints per GEMM row tile {expert (-1: none), first sorted row, rows, 0}.
+// tile_info: 4 ints per GEMM row tile {expert (-1: none), first sorted row, rows, 0},
+// ntiles_max + 1 entries (the last holds the number of real tiles).
 hipError_t launch_bucket(bool is_bf16, const int32_t* idx, const float* topk_w, int pairs, int E,
                          int bm, int ntiles_max, int32_t* counts, int32_t* offsets,
                          int32_t* tile_info, int32_t* sorted, float* sorted_w, void* X_hat, int HP,

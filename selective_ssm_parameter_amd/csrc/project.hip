@@ -66,11 +66,31 @@ struct ProjLay {
   static_assert(NIA % C::NW == 0 && NIB % C::NW == 0, "copies split evenly over the waves");
 };
 
+// XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so XCD x
+// gets the contiguous logical range [x * per, (x + 1) * per) of the real
+// (row tile, column tile) units: its tiles share an expert's weights and,
+// column tile fastest, a row tile of tokens. The grid is sized for the most
+// row tiles there can be; the number that exist (written by the bucketing
+// kernel after the tile table) spreads them over all XCDs, so no XCD is left
+// with only empty slots. Returns false for a workgroup without a unit.
+__device__ __forceinline__ bool xcd_tile(const int4v* __restrict__ tile_info, int nrow_tiles,
+                                         int CT, int& tile, int& ctile) {
+  const int units = tile_info[nrow_tiles][0] * CT;
+  const int per = (units + 7) / 8;
+  const int slot = blockIdx.x / 8;
+  if (slot >= per) return false;
+  const int logical = (blockIdx.x % 8) * per + slot;
+  if (logical >= units) return false;
+  tile = logical / CT;
+  ctile = logical % CT;
+  return true;
+}
+
 template <typename T, class C>
 __global__ __launch_bounds__(C::NTH) void proj_kernel(
     const T* __restrict__ u, const T* __restrict__ wexp, const int32_t* __restrict__ sorted,
     const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
-    int HP, int GN, int k, int ntiles, typename StreamOf<T>::type* __restrict__ X_hat,
+    int HP, int GN, int k, int nrow_tiles, typename StreamOf<T>::type* __restrict__ X_hat,
     typename StreamOf<T>::type* __restrict__ B_hat, float* __restrict__ c_part) {
   typedef typename StreamOf<T>::type S;
   typedef ProjLay<T, C> Lay;
@@ -88,14 +108,9 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
   __shared__ int rslot[BM];
   __shared__ float rw[BM];
 
-  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
-  // XCD x the contiguous logical range [x * per, (x + 1) * per): its tiles
-  // share an expert's weights and, column tile fastest, a row tile of tokens.
   const int CT = (W + BN - 1) / BN;
-  const int per = gridDim.x / 8;
-  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (logical >= ntiles) return;
-  const int tile = logical / CT, ctile = logical % CT;
+  int tile, ctile;
+  if (!xcd_tile(tile_info, nrow_tiles, CT, tile, ctile)) return;
   const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
   const int e = ti[0];
   if (e < 0) return;
@@ -258,6 +273,176 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
   }
 }
 
+// Skinny variant for expert groups of at most 64 rows (decode batches, where
+// every expert has a few dozen (token, slot) pairs and the step is bound by
+// streaming all experts' weights from HBM once). The weights go from HBM
+// straight into registers in bursts: every kSkGroup K steps a wave issues the
+// next group's kSkGroup loads back to back, a whole group ahead of their use,
+// so each of its 16 columns is requested as one contiguous 512-byte run. The
+// gathered token rows (read again by every column tile, so mostly L2 hits)
+// are staged in LDS in chunks of kSkKC elements of d, double buffered,
+// written from registers one chunk ahead. Workgroup = one row tile x kSkBN
+// columns; wave w owns columns 16w .. 16w + 15 of the tile and all four
+// 16-row fragments. The epilogue is the one of proj_kernel with four
+// consecutive columns per lane.
+constexpr int kSkBN = 64;
+constexpr int kSkKC = 128;
+constexpr int kSkSteps = kSkKC / 32;   // K steps per token-row chunk
+constexpr int kSkGroup = 2 * kSkSteps;  // K steps per weight burst (two chunks)
+constexpr int kSkRowB = kSkKC * 2;      // LDS bytes per token row of a chunk
+
+__global__ __launch_bounds__(256) void proj_skinny_kernel(
+    const bf16* __restrict__ u, const bf16* __restrict__ wexp, const int32_t* __restrict__ sorted,
+    const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
+    int HP, int GN, int k, int nrow_tiles, f16* __restrict__ X_hat, f16* __restrict__ B_hat,
+    float* __restrict__ c_part) {
+  typedef bf16x8 F;
+  // chunk rows: 16-byte piece ch of row r at piece ch ^ (r % 16)
+  __shared__ __align__(16) unsigned char abuf0[64 * kSkRowB];
+  __shared__ __align__(16) unsigned char abuf1[64 * kSkRowB];
+  __shared__ int rtok[64];
+  __shared__ int rslot[64];
+  __shared__ float rw[64];
+
+  const int CT = (W + kSkBN - 1) / kSkBN;
+  int tile, ctile;
+  if (!xcd_tile(tile_info, nrow_tiles, CT, tile, ctile)) return;
+  const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
+  const int e = ti[0];
+  if (e < 0) return;
+  const int row0 = ti[1], nrows = ti[2];
+  if (threadIdx.x < 64) {
+    const int r = threadIdx.x;
+    if (r < nrows) {
+      const int p = sorted[row0 + r];
+      rtok[r] = p / k;
+      rslot[r] = p - (p / k) * k;
+      rw[r] = sorted_w[row0 + r];
+    } else {
+      rtok[r] = -1;
+      rslot[r] = 0;
+      rw[r] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int col0 = ctile * kSkBN + 16 * wave;  // W is a multiple of 16: whole waves drop out
+  const bool active = col0 < W;
+  const int nsteps = D / 32;
+  const int ngroups = (nsteps + kSkGroup - 1) / kSkGroup;
+
+  const BufRes rA = make_rsrc(u, (uint64_t)M * D * 2);
+  const BufRes rW = make_rsrc(wexp + (size_t)e * W * D, (uint64_t)W * D * 2);
+  // weights: lane (g, c) reads column col0 + c, elements 32 s + 8 g .. + 7 of
+  // K step s; steps past d read zeros
+  const uint32_t wbase = active ? ((uint32_t)(col0 + c) * D + 8 * g) * 2 : kOOB;
+  F wq[2 * kSkGroup];  // two bursts: the group in use and the next one
+  auto burst = [&](auto par, int grp) {
+    constexpr int PAR = decltype(par)::value;
+#pragma unroll
+    for (int j = 0; j < kSkGroup; ++j) {
+      const int s = kSkGroup * grp + j;
+      wq[kSkGroup * PAR + j] =
+          load8_buf<bf16>(rW, (wbase == kOOB || s >= nsteps) ? kOOB : wbase + 64u * s);
+    }
+  };
+  // token rows: thread t copies pieces q = t + 256 m of a chunk's 64 x 16 pieces
+  uint32_t abase[4];
+  int apiece[4], alds[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int q = threadIdx.x + 256 * m;
+    const int r = q >> 4, ch = q & 15;
+    apiece[m] = 8 * ch;
+    abase[m] = r < nrows ? ((uint32_t)rtok[r] * D + 8 * ch) * 2 : kOOB;
+    alds[m] = r * kSkRowB + 16 * (ch ^ (r & 15));
+  }
+  F ar[4];
+  auto aload = [&](int chunk) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const bool ok = abase[m] != kOOB && chunk * kSkKC + apiece[m] < D;
+      ar[m] = load8_buf<bf16>(rA, ok ? abase[m] + chunk * kSkRowB : kOOB);
+    }
+  };
+  auto awrite = [&](unsigned char* buf) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) *reinterpret_cast<F*>(buf + alds[m]) = ar[m];
+  };
+
+  floatx4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // the K steps of one chunk: weights from slots first .. first + 3
+  auto steps = [&](auto first, const unsigned char* buf) {
+    constexpr int S0 = decltype(first)::value;
+#pragma unroll
+    for (int j = 0; j < kSkSteps; ++j) {
+      F a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const F*>(buf + (16 * i + c) * kSkRowB + 16 * ((4 * j + g) ^ c));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mma16(wq[S0 + j], a[i], acc[i]);
+    }
+  };
+  // One group (two chunks) with its weights in slot half PAR. Token rows of
+  // the second chunk are requested before the next burst, so writing them to
+  // LDS waits for them alone; the next group's burst is waited for only at
+  // the end of this group.
+  auto group = [&](auto par, int grp) {
+    constexpr int PAR = decltype(par)::value;
+    aload(2 * grp + 1);
+    burst(std::integral_constant<int, 1 - PAR>(), grp + 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the burst's loads together
+    steps(std::integral_constant<int, kSkGroup * PAR>(), abuf0);
+    awrite(abuf1);
+    __syncthreads();  // chunk 2 grp + 1 visible; abuf0 no longer read
+    aload(2 * grp + 2);
+    steps(std::integral_constant<int, kSkGroup * PAR + kSkSteps>(), abuf1);
+    awrite(abuf0);
+    __syncthreads();  // chunk 2 grp + 2 visible; abuf1 no longer read
+  };
+  burst(std::integral_constant<int, 0>(), 0);
+  aload(0);
+  awrite(abuf0);
+  __syncthreads();
+  for (int grp = 0; grp < ngroups; grp += 2) {
+    group(std::integral_constant<int, 0>(), grp);
+    if (grp + 1 >= ngroups) break;
+    group(std::integral_constant<int, 1>(), grp + 1);
+  }
+
+  // ---- epilogue: acc[i] holds, in lane (g, c), columns col0 + 4g .. + 3 of
+  // pair row 16 i + c (H*P and G*N are multiples of 16: no region straddles)
+  if (!active) return;
+  const int col = col0 + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * i + c;
+    if (r >= nrows) continue;
+    const size_t pair = (size_t)rtok[r] * k + rslot[r];
+    const float wv = rw[r];
+    const floatx4 v = acc[i];
+    if (col < HP) {
+      f16x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = from_f32<f16>(v[q]);
+      *reinterpret_cast<f16x4*>(&X_hat[pair * HP + col]) = o;
+    } else if (col < HP + GN) {
+      f16x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = from_f32<f16>(wv * v[q]);
+      *reinterpret_cast<f16x4*>(&B_hat[pair * GN + (col - HP)]) = o;
+    } else {
+      *reinterpret_cast<floatx4*>(&c_part[pair * GN + (col - HP - GN)]) = v * wv;
+    }
+  }
+}
+
 // C_mix[m, :] = sum_{j = 0..k-1} c_part[m, j, :], in slot order, fp32.
 template <typename T>
 __global__ __launch_bounds__(256) void mix_c_kernel(const float* __restrict__ c_part, int M,
@@ -282,11 +467,12 @@ static hipError_t launch_proj_cfg(const ProjGeom& g, const T* u, const T* wexp,
                                   typename StreamOf<T>::type* X_hat, float* c_part,
                                   hipStream_t s) {
   const int pairs = g.M * g.k;
-  const int ntiles = proj_row_tiles_max(pairs, g.E, C::BM) * ((g.W + C::BN - 1) / C::BN);
+  const int nrow = proj_row_tiles_max(pairs, g.E, C::BM);
+  const int ntiles = nrow * ((g.W + C::BN - 1) / C::BN);
   const dim3 grid((unsigned)((ntiles + 7) / 8 * 8));  // a multiple of the 8 XCDs
   prof_begin("expert_project", s);
   hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, u, wexp, sorted, sorted_w,
-                     tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, ntiles, X_hat, B_hat, c_part);
+                     tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part);
   prof_end(s);
   return hipGetLastError();
 }
@@ -301,7 +487,16 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
   hipError_t err;
   if constexpr (sizeof(T) == 2) {
     // the 256 x 256 tile needs 2-byte K tiles to fit LDS
-    if (bm == 256)
+    if (bm == 64) {
+      const int nrow = proj_row_tiles_max(g.M * g.k, g.E, 64);
+      const int ntiles = nrow * ((g.W + kSkBN - 1) / kSkBN);
+      prof_begin("expert_project", s);
+      hipLaunchKernelGGL(proj_skinny_kernel, dim3((unsigned)((ntiles + 7) / 8 * 8)), dim3(256), 0,
+                         s, u, wexp, sorted, sorted_w, ti, g.M, g.D, g.W, g.HP(), g.GN(), g.k,
+                         nrow, X_hat, B_hat, c_part);
+      prof_end(s);
+      err = hipGetLastError();
+    } else if (bm == 256)
       err = launch_proj_cfg<T, ProjBig>(g, u, wexp, sorted, sorted_w, ti, B_hat, X_hat, c_part, s);
     else if (bm == 128)
       err = launch_proj_cfg<T, ProjMid>(g, u, wexp, sorted, sorted_w, ti, B_hat, X_hat, c_part, s);

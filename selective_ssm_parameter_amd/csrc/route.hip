@@ -10,18 +10,24 @@
 // operand is the token rows of u, the B operand the router rows (both are
 // contiguous along d_model, so every lane loads 16 bytes). Products of bf16
 // values are exact in fp32 and accumulate in fp32, so the logits are never
-// rounded to bf16. The logits go through LDS; one thread per token then picks
-// the top-k (strictly greater wins, so equal logits keep the lower index) and
-// evaluates the softmax over all E experts in fp32.
+// rounded to bf16. The logits go through LDS; a group of lanes per token then
+// picks the top-k (strictly greater wins, so equal logits keep the lower
+// index) and evaluates the softmax over all E experts in fp32.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace swimba {
 
-__device__ void route_token(const float* l, int m, int E, int k, int32_t* __restrict__ idx,
-                            float* __restrict__ wout, float* __restrict__ logits, int* hcnt);
+__device__ void route_tokens(const float* lg, int ldl, int tok0, int tpw, int M, int E, int k,
+                             int32_t* __restrict__ idx, float* __restrict__ wout,
+                             float* __restrict__ logits, int* hcnt);
 
-template <typename T>
+// GT: expert tiles per pass (1, 2 or 4; tiles past E read zeros). The K loop
+// issues the loads of RB steps together (A rows and every tile's router rows)
+// before their matrix-core ops, so a wave waits for memory once per batch
+// rather than once per load (8 steps of 2-byte data, 4 of fp32).
+
+template <typename T, int GT>
 __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
                                                     const T* __restrict__ wr, int M, int D,
                                                     int E, int k, int32_t* __restrict__ idx,
@@ -31,6 +37,7 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
                                                     int ksplit) {
   extern __shared__ float lg[];  // [ksplit][tpw][E + 1] partial logits
   typedef typename Vec<T>::x8 F;
+  constexpr int RB = sizeof(T) == 2 ? 8 : 4;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -46,42 +53,46 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
 
   const int row = tok0 + tt * 16 + c;
   constexpr uint32_t ES = sizeof(T);
-  // Out-of-range rows (tokens beyond M, experts beyond E) read zeros.
+  // Out-of-range rows (tokens beyond M, experts beyond E, d past the slice)
+  // read zeros.
   const BufRes ru = make_rsrc(u, (uint64_t)M * D * ES);
   const BufRes rw = make_rsrc(wr, (uint64_t)E * D * ES);
   const uint32_t uoff = row < M ? ((uint32_t)row * D + 8 * g) * ES : kOOB;
   float* mylg = lg + (size_t)ks * tpw * ldl;
 
-  // Expert tiles are processed 4 at a time (16 accumulators per lane); the K
-  // loop is unrolled so several steps' loads are in flight together.
   if (ks < ksplit && tt < ntt) {
-    for (int et0 = 0; et0 < ET; et0 += 4) {
-      floatx4 acc[4];
+    for (int et0 = 0; et0 < ET; et0 += GT) {
+      floatx4 acc[GT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-      uint32_t woff[4];
+      for (int i = 0; i < GT; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      uint32_t woff[GT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < GT; ++i) {
         const int e = (et0 + i) * 16 + c;
-        woff[i] = (et0 + i < ET && e < E) ? ((uint32_t)e * D + 8 * g) * ES : kOOB;
+        woff[i] = e < E ? ((uint32_t)e * D + 8 * g) * ES : kOOB;
       }
-#pragma unroll 4
-      for (int st = s0; st < s1; ++st) {
-        const int k0 = 32 * st;
-        const F a = load8_buf<T>(ru, uoff == kOOB ? kOOB : uoff + k0 * ES);
+      for (int st0 = s0; st0 < s1; st0 += RB) {
+        F a[RB], b[RB][GT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (et0 + i < ET) {
-            const F b = load8_buf<T>(rw, woff[i] == kOOB ? kOOB : woff[i] + k0 * ES);
-            acc[i] = mma16(a, b, acc[i]);
-          }
+        for (int q = 0; q < RB; ++q) {
+          const bool ok = st0 + q < s1;
+          const uint32_t k0 = 32u * (st0 + q) * ES;
+          a[q] = load8_buf<T>(ru, (ok && uoff != kOOB) ? uoff + k0 : kOOB);
+#pragma unroll
+          for (int i = 0; i < GT; ++i)
+            b[q][i] = load8_buf<T>(rw, (ok && woff[i] != kOOB) ? woff[i] + k0 : kOOB);
         }
+        __builtin_amdgcn_sched_barrier(0);  // all of the batch's loads before its first use
+#pragma unroll
+        for (int q = 0; q < RB; ++q)
+#pragma unroll
+          for (int i = 0; i < GT; ++i) acc[i] = mma16(a[q], b[q][i], acc[i]);
       }
       // acc[i][q] = partial logit of token (16 tt + 4g + q) for expert (16 (et0+i) + c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < GT; ++i) {
         const int e = (et0 + i) * 16 + c;
-        if (et0 + i < ET && e < E) {
+        if (e < E) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) mylg[(tt * 16 + 4 * g + q) * ldl + e] = acc[i][q];
         }
@@ -104,44 +115,81 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
     for (int e = threadIdx.x; e <= E; e += blockDim.x) hcnt[e] = 0;
     __syncthreads();
   }
-  const int t = threadIdx.x;
-  if (t < tpw && tok0 + t < M) route_token(lg + t * ldl, tok0 + t, E, k, idx, wout, logits,
-                                                 hist ? hcnt : nullptr);
+  route_tokens(lg, ldl, tok0, tpw, M, E, k, idx, wout, logits, hist ? hcnt : nullptr);
   if (hist) {
     __syncthreads();
     for (int e = threadIdx.x; e <= E; e += blockDim.x) hist[(size_t)blockIdx.x * (E + 1) + e] = hcnt[e];
   }
 }
 
-// Top-k and softmax of one token from its logits in LDS.
-__device__ void route_token(const float* l, int m, int E, int k, int32_t* __restrict__ idx,
-                            float* __restrict__ wout, float* __restrict__ logits, int* hcnt) {
-  if (logits) {
-    for (int e = 0; e < E; ++e) logits[(size_t)m * E + e] = l[e];
-  }
-  int chosen[8];
-  for (int j = 0; j < k; ++j) {
-    int bi = -1;
-    float best = 0.f;
-    for (int e = 0; e < E; ++e) {
-      bool taken = false;
-      for (int q = 0; q < j; ++q) taken |= (chosen[q] == e);
-      if (taken) continue;
-      if (bi < 0 || l[e] > best) {
-        bi = e;
-        best = l[e];
+// Top-k and softmax of the workgroup's tokens from their logits in LDS. A
+// group of sg lanes (a power of two with E <= 4 sg) shares a token: lane sl
+// holds experts sl, sl + sg, sl + 2 sg, sl + 3 sg. Each of the k rounds takes
+// the group's maximum over the experts not yet chosen (equal logits: the lower
+// expert index wins), so the choice is exactly that of a sequential scan; the
+// softmax denominator is summed over the group in a fixed butterfly order.
+__device__ void route_tokens(const float* lg, int ldl, int tok0, int tpw, int M, int E, int k,
+                             int32_t* __restrict__ idx, float* __restrict__ wout,
+                             float* __restrict__ logits, int* hcnt) {
+  constexpr int kNone = 0x7fffffff;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int sg = 1;
+  while (4 * sg < E) sg *= 2;
+  const int per_wave = 64 / sg;
+  const int sub = lane / sg, sl = lane % sg;
+  for (int t0 = wave * per_wave; t0 < tpw; t0 += 4 * per_wave) {
+    const int t = t0 + sub;
+    const int m = tok0 + t;
+    const bool valid = t < tpw && m < M;
+    const float* l = lg + (valid ? t : 0) * ldl;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = sl + sg * j;
+      v[j] = (valid && e < E) ? l[e] : -INFINITY;
+      if (logits && valid && e < E) logits[(size_t)m * E + e] = v[j];
+    }
+    int taken = 0;
+    // the group's best expert not yet taken: (value, index), ties to the lower index
+    auto best = [&](float& bv, int& be) {
+      bv = -INFINITY;
+      be = kNone;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = sl + sg * j;
+        if (!((taken >> j) & 1) && e < E && (be == kNone || v[j] > bv)) {
+          bv = v[j];
+          be = e;
+        }
+      }
+      for (int off = sg >> 1; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, sg);
+        const int oe = __shfl_xor(be, off, sg);
+        if (oe != kNone && (be == kNone || ov > bv || (ov == bv && oe < be))) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if (be != kNone && be % sg == sl) taken |= 1 << (be / sg);
+    };
+    float bv;
+    int be;
+    best(bv, be);
+    const float mx = bv;
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sl + sg * j < E) sum += expf(v[j] - mx);
+    for (int off = sg >> 1; off > 0; off >>= 1) sum += __shfl_xor(sum, off, sg);
+    const float inv = 1.f / sum;
+    for (int j = 0; j < k; ++j) {
+      if (j > 0) best(bv, be);
+      if (valid && sl == 0) {
+        idx[(size_t)m * k + j] = be;
+        wout[(size_t)m * k + j] = expf(bv - mx) * inv;
+        if (hcnt) atomicAdd(&hcnt[be], 1);
       }
     }
-    chosen[j] = bi;
-  }
-  const float mx = l[chosen[0]];
-  float sum = 0.f;
-  for (int e = 0; e < E; ++e) sum += expf(l[e] - mx);
-  const float inv = 1.f / sum;
-  for (int j = 0; j < k; ++j) {
-    idx[(size_t)m * k + j] = chosen[j];
-    wout[(size_t)m * k + j] = expf(l[chosen[j]] - mx) * inv;
-    if (hcnt) atomicAdd(&hcnt[chosen[j]], 1);
   }
 }
 
@@ -155,17 +203,31 @@ hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M
   int ksplit = 64 / tpw;
   while (ksplit > 1 && (size_t)ksplit * tpw * (E + 1) * sizeof(float) > 65536) ksplit /= 2;
   size_t lds = (size_t)ksplit * tpw * (E + 1) * sizeof(float) + (size_t)(E + 1) * sizeof(int);
-  hipError_t err = hipFuncSetAttribute(
-      is_bf16 ? (const void*)route_kernel<bf16> : (const void*)route_kernel<float>,
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int ET = (E + 15) / 16;
+  const int GT = ET >= 4 ? 4 : (ET >= 2 ? 2 : 1);
+  const void* fn;
+  if (is_bf16)
+    fn = GT == 4 ? (const void*)route_kernel<bf16, 4>
+                 : (GT == 2 ? (const void*)route_kernel<bf16, 2> : (const void*)route_kernel<bf16, 1>);
+  else
+    fn = GT == 4 ? (const void*)route_kernel<float, 4>
+                 : (GT == 2 ? (const void*)route_kernel<float, 2> : (const void*)route_kernel<float, 1>);
+  hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   prof_begin("route_topk", s);
-  if (is_bf16)
-    hipLaunchKernelGGL(route_kernel<bf16>, grid, block, lds, s, (const bf16*)u,
-                       (const bf16*)w_router, M, D, E, k, idx, w, logits, hist, tpw, ksplit);
-  else
-    hipLaunchKernelGGL(route_kernel<float>, grid, block, lds, s, (const float*)u,
-                       (const float*)w_router, M, D, E, k, idx, w, logits, hist, tpw, ksplit);
+#define SWIMBA_ROUTE(TT, G)                                                                     \
+  hipLaunchKernelGGL((route_kernel<TT, G>), grid, block, lds, s, (const TT*)u,                 \
+                     (const TT*)w_router, M, D, E, k, idx, w, logits, hist, tpw, ksplit)
+  if (is_bf16) {
+    if (GT == 4) SWIMBA_ROUTE(bf16, 4);
+    else if (GT == 2) SWIMBA_ROUTE(bf16, 2);
+    else SWIMBA_ROUTE(bf16, 1);
+  } else {
+    if (GT == 4) SWIMBA_ROUTE(float, 4);
+    else if (GT == 2) SWIMBA_ROUTE(float, 2);
+    else SWIMBA_ROUTE(float, 1);
+  }
+#undef SWIMBA_ROUTE
   prof_end(s);
   return hipGetLastError();
 }
