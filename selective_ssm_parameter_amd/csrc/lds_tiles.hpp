@@ -7,9 +7,7 @@
 
 namespace swimba {
 
-// Swizzles (16-byte chunk index XOR, 2-byte element types; none for fp32). Each
-// keeps the accesses of one LDS cycle on distinct banks whether a cycle serves
-// 128 bytes (8 lanes of a 16-byte read) or 256 bytes (16 lanes).
+// Swizzles (16-byte chunk index XOR, 2-byte element types; none for fp32).
 // Tiles read with transposing loads (X, B): a 16-lane group reads two adjacent
 // chunks of 4 consecutive rows; groups g and g + 1 read rows 8 apart.
 template <typename T, int CPR>
@@ -19,13 +17,18 @@ __device__ __forceinline__ int swz_tr(int r) {
   else if constexpr (CPR == 8) return 2 * ((r & 3) ^ ((r >> 3) & 1));
   else return 2 * (((r >> 1) & 1) ^ ((r >> 3) & 1));
 }
-// Tiles read by rows (C~, G, GEMM operands): 16 consecutive rows, one chunk each.
+// Tiles read by rows (C~, G, GEMM operands): a 16-byte read per lane, lane
+// (g, c) taking chunk g of row c of 16 rows (consecutive rows, or the GEMM's
+// weight rows 8 (c / 4) + c % 4 (+ 4)). The XOR patterns are the ones the LDS
+// bank-conflict counter of gfx950 reads as zero for these accesses (64-byte
+// rows: ((t >> 1) ^ (t >> 2)) & 3, where t & 3 and (t >> 1) ^ (t >> 3) conflict;
+// 128-byte rows: t & 7, where t ^ (t >> 3) conflicts).
 template <typename T, int CPR>
 __device__ __forceinline__ int swz_row(int t) {
   if constexpr (sizeof(T) != 2) return 0;
   else if constexpr (CPR >= 16) return t & 15;
-  else if constexpr (CPR == 8) return (t ^ (t >> 3)) & 7;
-  else return ((t >> 1) ^ (t >> 3)) & 3;
+  else if constexpr (CPR == 8) return t & 7;
+  else return ((t >> 1) ^ (t >> 2)) & 3;
 }
 
 // Buffer-to-LDS copy of a row-major tile: NROWS rows of CPR 16-byte chunks,
@@ -42,7 +45,7 @@ __device__ __forceinline__ void dma_tile(BufRes rs, uint32_t base, uint32_t pitc
 #pragma unroll
   for (int i0 = 0; i0 < NI; i0 += 4) {
     const int i = i0 + wave;
-    if (i < NI) {
+    if (NI % 4 == 0 || i < NI) {
       const int slot = 64 * i + lane;
       const int r = slot / CPR, pc = slot % CPR;
       const int lc = pc ^ swz(r);

@@ -68,21 +68,31 @@ struct ProjLay {
 
 // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so XCD x
 // gets the contiguous logical range [x * per, (x + 1) * per) of the real
-// (row tile, column tile) units: its tiles share an expert's weights and,
-// column tile fastest, a row tile of tokens. The grid is sized for the most
-// row tiles there can be; the number that exist (written by the bucketing
-// kernel after the tile table) spreads them over all XCDs, so no XCD is left
-// with only empty slots. Returns false for a workgroup without a unit.
+// (row tile, column tile) units. Units are ordered in groups of GR row tiles,
+// column tile by column tile within a group, so the workgroups one XCD runs at
+// a time share a few row tiles of tokens and a few column tiles of weights
+// (both stay in its L2 while they move along d together; GR = 1 when every
+// weight tile is read once anyway). The grid is
+// sized for the most row tiles there can be; the number that exist (written
+// by the bucketing kernel after the tile table) spreads them over all XCDs, so
+// no XCD is left with only empty slots. Returns false for a workgroup without
+// a unit.
+constexpr int kProjGroupRows = 4;
+template <int GR>
 __device__ __forceinline__ bool xcd_tile(const int4v* __restrict__ tile_info, int nrow_tiles,
                                          int CT, int& tile, int& ctile) {
-  const int units = tile_info[nrow_tiles][0] * CT;
+  const int nt = tile_info[nrow_tiles][0];
+  const int units = nt * CT;
   const int per = (units + 7) / 8;
   const int slot = blockIdx.x / 8;
   if (slot >= per) return false;
   const int logical = (blockIdx.x % 8) * per + slot;
   if (logical >= units) return false;
-  tile = logical / CT;
-  ctile = logical % CT;
+  const int group = logical / (GR * CT);
+  const int rem = logical - group * (GR * CT);
+  const int gm = min(GR, nt - group * GR);  // row tiles in this group
+  ctile = rem / gm;
+  tile = group * GR + (rem - ctile * gm);
   return true;
 }
 
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
 
   const int CT = (W + BN - 1) / BN;
   int tile, ctile;
-  if (!xcd_tile(tile_info, nrow_tiles, CT, tile, ctile)) return;
+  if (!xcd_tile<kProjGroupRows>(tile_info, nrow_tiles, CT, tile, ctile)) return;
   const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
   const int e = ti[0];
   if (e < 0) return;
@@ -211,25 +221,28 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
       for (int j = 0; j < TN; ++j) acc[i][j] = mma16(bfr[j], afr[i], acc[i][j]);
   };
 
+  // The K loop runs in whole turns of the four stages and issues every copy
+  // unconditionally (tiles past d read zeros, and multiply to nothing): with
+  // no branches in the loop the compiler's own wait counts see which stage a
+  // copy fills, and never drain all copies before reading a stage.
   const int nk = (D + BK - 1) / BK;
+  const int nk4 = (nk + kProjStages - 1) / kProjStages * kProjStages;
   fetch(stg0, 0);
-  if (nk > 1) fetch(stg1, BK);
-  if (nk > 2) fetch(stg2, 2 * BK);
+  fetch(stg1, BK);
+  fetch(stg2, 2 * BK);
   auto iter = [&](int kt, const unsigned char* cur, unsigned char* far) {
-    const int after = min(2, nk - 1 - kt);  // K tiles already issued after this one
-    if (after >= 2) wait_vm<2 * Lay::CPW>();
-    else if (after == 1) wait_vm<Lay::CPW>();
-    else wait_vm<0>();
-    stage_barrier();  // tile kt visible to all waves; tile kt - 1 no longer read
-    if (kt + 3 < nk) fetch(far, (kt + 3) * BK);
+    wait_vm<2 * Lay::CPW>();  // tile kt landed (tiles kt + 1, kt + 2 may be in flight)
+    stage_barrier();          // tile kt visible to all waves; tile kt - 1 no longer read
+    fetch(far, (kt + 3) * BK);
     compute(cur);
   };
-  for (int kt = 0; kt < nk; kt += kProjStages) {
+  for (int kt = 0; kt < nk4; kt += kProjStages) {
     iter(kt, stg0, stg3);
-    if (kt + 1 < nk) iter(kt + 1, stg1, stg0);
-    if (kt + 2 < nk) iter(kt + 2, stg2, stg1);
-    if (kt + 3 < nk) iter(kt + 3, stg3, stg2);
+    iter(kt + 1, stg1, stg0);
+    iter(kt + 2, stg2, stg1);
+    iter(kt + 3, stg3, stg2);
   }
+  wait_vm<0>();  // the copies past the end land before the workgroup's LDS is released
 
   // ---- epilogue: each lane stores 8 consecutive columns of one pair row per
   // column-tile pair (H*P and G*N are multiples of 16, so 8 columns never
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(256) void proj_skinny_kernel(
 
   const int CT = (W + kSkBN - 1) / kSkBN;
   int tile, ctile;
-  if (!xcd_tile(tile_info, nrow_tiles, CT, tile, ctile)) return;
+  if (!xcd_tile<1>(tile_info, nrow_tiles, CT, tile, ctile)) return;
   const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
   const int e = ti[0];
   if (e < 0) return;

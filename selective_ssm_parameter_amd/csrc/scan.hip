@@ -56,7 +56,7 @@ struct ScanArgs {
   float* h_final;
   float* ws;          // [Bt, segs, H, N, P] fp32 segment states
   const void* gram;   // [Bt, nc, G, npairs, BT, k*BT] Gram tiles (stream type)
-  int T, H, G, N, k, L, segs, seg_chunks, nc, npairs;
+  int T, H, G, N, k, L, segs, seg_chunks, nc, npairs, Bt;
 };
 
 // LDS of the walk: two stages, each holding one step's row-major tiles as they
@@ -171,8 +171,16 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
   __shared__ __align__(16) unsigned char stage0[Lay::STAGE];
   __shared__ __align__(16) unsigned char stage1[Lay::STAGE];
 
-  const int h = blockIdx.x, seg = blockIdx.y, b = blockIdx.z;
   const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
+  // 1-D grid over (head, segment, sequence), head fastest, dealt so that XCD x
+  // owns the contiguous range [x * per, (x + 1) * per): the heads of one
+  // (sequence, segment) share an XCD and walk its chunks together, so the
+  // B_hat, C~ and Gram tiles they all read come from that XCD's L2.
+  const int nseg = WITH_Y ? A.segs : A.segs - 1;
+  const int per = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (logical >= H * nseg * A.Bt) return;
+  const int h = logical % H, seg = (logical / H) % nseg, b = logical / (H * nseg);
   const int grp = h / (H / G);
   const int GN = G * N;
   const int lane = lane_id();
@@ -600,7 +608,8 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   prof_end(s);
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
-    hipLaunchKernelGGL(k1, dim3(g.H, g.segs - 1, g.Bt), dim3(kScanThreads), l1, s, args);
+    const int n1 = g.H * (g.segs - 1) * g.Bt;
+    hipLaunchKernelGGL(k1, dim3((unsigned)((n1 + 7) / 8 * 8)), dim3(kScanThreads), l1, s, args);
     prof_end(s);
     const int NPsz = g.N * g.P;
     prof_begin("scan_state_pass", s);
@@ -609,7 +618,8 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
     prof_end(s);
   }
   prof_begin("scan_chunk_output", s);
-  hipLaunchKernelGGL(k3, dim3(g.H, g.segs, g.Bt), dim3(kScanThreads), l3, s, args);
+  const int n3 = g.H * g.segs * g.Bt;
+  hipLaunchKernelGGL(k3, dim3((unsigned)((n3 + 7) / 8 * 8)), dim3(kScanThreads), l3, s, args);
   prof_end(s);
   return hipGetLastError();
 }
@@ -645,7 +655,8 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
   const int nc = (g.T + g.L - 1) / g.L;
   unsigned char* gram = reinterpret_cast<unsigned char*>(ws) + scan_state_bytes(g);
   ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws, gram,
-                g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks, nc, scan_npairs(g.L, g.bt)};
+                g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks, nc, scan_npairs(g.L, g.bt),
+                g.Bt};
   if (is_bf16) return dispatch_np<f16, bf16>(g, args, s);
   return dispatch_np<float, float>(g, args, s);
 }
