@@ -541,15 +541,18 @@ hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t
   return hipGetLastError();
 }
 
-// Tuning knob (environment, read once): SWIMBA_SCAN_WGS = target number of
-// workgroups of the output pass, which sets the segment count per sequence.
+// Tuning knob (environment, read once): SWIMBA_SCAN_WGS = the most workgroups
+// the output pass may have; the segment count per sequence is the largest that
+// keeps (sequences x heads x segments) within it. The default, 512, is what the
+// MI355X holds at once (two workgroups per CU): more segments than one round
+// of workgroups measured slower (a second, partial round), fewer leave CUs idle.
 static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   return v ? atoi(v) : dflt;
 }
 static int scan_target_wgs() {
-  static const int w = env_int("SWIMBA_SCAN_WGS", 384);
-  return w > 0 ? w : 384;
+  static const int w = env_int("SWIMBA_SCAN_WGS", 512);
+  return w > 0 ? w : 512;
 }
 
 static int scan_npairs(int L, int bt) {
@@ -570,7 +573,7 @@ ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int 
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
   const int units = Bt * H;
-  int want = (scan_target_wgs() + units - 1) / units;
+  int want = scan_target_wgs() / units;
   if (want > nc) want = nc;
   if (want < 1) want = 1;
   g.seg_chunks = (nc + want - 1) / want;
