@@ -30,7 +30,7 @@ hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M
                         int32_t* hist = nullptr);
 
 // Bucketing of (token, slot) pairs by expert.
-constexpr int kBucketPairs = 1024;  // pairs per bucketing block
+constexpr int kBucketPairs = 256;  // pairs per bucketing block
 int bucket_blocks(int pairs);
 // block_pairs: pairs per bucketing block (0 = kBucketPairs); counted: the
 // histograms [nblk][E+1] are already in `counts` (written by the router).
