@@ -363,6 +363,8 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
               hf[4 + i] = from_f32<T>(Hr[2 * q + 1][i]);
             }
           }
+          // the C~ fragments of every token tile first, then the matrix-core ops
+          F cf[TT];
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) {
             // C~ operand in the same n order: {32q + 4g .. +3, 32q + 16 + 4g .. +3}
@@ -372,8 +374,11 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
             const int sw = swz_row<T, BC>(t);
             const T* p0 = reinterpret_cast<const T*>(Cs + (t * BC + ((e0 >> 4) ^ sw)) * 16 + (e0 & 15));
             const T* p1 = reinterpret_cast<const T*>(Cs + (t * BC + ((e1 >> 4) ^ sw)) * 16 + (e1 & 15));
-            accY[tt] = mma16(hf, load4x2<T>(p0, p1), accY[tt]);
+            cf[tt] = load4x2<T>(p0, p1);
           }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) accY[tt] = mma16(hf, cf[tt], accY[tt]);
         }
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] * (at[tt] * ablk);
@@ -431,8 +436,18 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
             xd[j] = from_f32<T>(to_f32(xq[q][j]) * (d >= 0 ? apow(la, d) : 0.f));
           }
         }
+        // B_hat fragments four at a time: their LDS reads are all in flight
+        // before the first matrix-core op needs one
+        constexpr int CG = NT < 4 ? NT : 4;
 #pragma unroll
-        for (int a = 0; a < NT; ++a) Hr[a] = mma16(load_kmajor<T, BC>(Bs, 32 * q, 16 * a, lane), xd, Hr[a]);
+        for (int a0 = 0; a0 < NT; a0 += CG) {
+          F bf[CG];
+#pragma unroll
+          for (int i = 0; i < CG; ++i) bf[i] = load_kmajor<T, BC>(Bs, 32 * q, 16 * (a0 + i), lane);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < CG; ++i) Hr[a0 + i] = mma16(bf[i], xd, Hr[a0 + i]);
+        }
       }
     }
     if (WITH_Y && dg) {
