@@ -118,12 +118,19 @@ template <typename T, int NP, int KS, int BT>
 __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_hat,
                                                         const T* __restrict__ C_mix,
                                                         T* __restrict__ gram, int Tlen, int G,
-                                                        int N, int L, int nc, int npairs) {
+                                                        int N, int L, int nc, int npairs, int Bt) {
   constexpr int R = KS * BT, TT = BT / 16, RT = R / 16;
   constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
   typedef typename Vec<T>::x4 F4;
-  const int grp = blockIdx.x % G, pidx = blockIdx.x / G, ch = blockIdx.y, b = blockIdx.z;
+  // 1-D grid, dealt XCD-contiguously with (group, block pair) fastest: the
+  // tiles of one chunk are computed on one XCD and read its B_hat and C~ rows
+  // from that XCD's L2 once.
+  const int per = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (logical >= G * npairs * nc * Bt) return;
+  const int grp = logical % G, pidx = (logical / G) % npairs;
+  const int ch = (logical / (G * npairs)) % nc, b = logical / (G * npairs * nc);
   int tau = 0;
   while ((tau + 1) * (tau + 2) / 2 <= pidx) ++tau;
   const int sig = pidx - tau * (tau + 1) / 2;
@@ -390,23 +397,35 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
         const unsigned char* p = Gs + (t * GC + ((e0 >> 4) ^ swz_row<T, GC>(t))) * 16 + (e0 & 15);
         return load8<T>(reinterpret_cast<const T*>(p));
       };
+      // Gram fragments: all of a q-step's token tiles read before their
+      // matrix-core ops
       if (dg) {
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+        for (int q = 0; q < RQ; ++q) {
+          F gf[TT];
 #pragma unroll
-          for (int q = 0; q < RQ; ++q) {
+          for (int tt = 0; tt < TT; ++tt)
+            if (DF::index(tt, q) >= 0) gf[tt] = gfrag(tt, q);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
             const int ix = DF::index(tt, q);
-            if (ix >= 0) accY[tt] = mma16(xq[q], gfrag(tt, q) * dm[ix], accY[tt]);
+            if (ix >= 0) accY[tt] = mma16(xq[q], gf[tt] * dm[ix], accY[tt]);
           }
+        }
       } else {
         floatx4 tmp[TT];
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) tmp[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < RQ; ++q) {
+          F gf[TT];
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) gf[tt] = gfrag(tt, q);
+          __builtin_amdgcn_sched_barrier(0);
           const F xs = xq[q] * er[q];
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt) tmp[tt] = mma16(xs, gfrag(tt, q), tmp[tt]);
+          for (int tt = 0; tt < TT; ++tt) tmp[tt] = mma16(xs, gf[tt], tmp[tt]);
         }
         const float u = apow(la, (cur.tau - cur.sig) * BT - (BT - 1));
 #pragma unroll
@@ -619,10 +638,11 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   auto k1 = scan_kernel<T, TY, NP, KS, BT, false>;
   const size_t l3 = 0, l1 = 0;  // static LDS (two stage arrays)
   prof_begin("scan_gram", s);
-  hipLaunchKernelGGL((scan_gram_kernel<T, NP, KS, BT>), dim3(args.npairs * g.G, args.nc, g.Bt),
+  const int ng = args.npairs * g.G * args.nc * g.Bt;
+  hipLaunchKernelGGL((scan_gram_kernel<T, NP, KS, BT>), dim3((unsigned)((ng + 7) / 8 * 8)),
                      dim3(256), 0, s, static_cast<const T*>(args.B_hat),
                      static_cast<const T*>(args.C_mix), static_cast<T*>(const_cast<void*>(args.gram)),
-                     g.T, g.G, g.N, g.L, args.nc, args.npairs);
+                     g.T, g.G, g.N, g.L, args.nc, args.npairs, g.Bt);
   prof_end(s);
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
