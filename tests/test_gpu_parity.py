@@ -45,6 +45,11 @@ ROUTE_CASES = [
     ("bf16_e64k8", W("r3", 103, batch=1, seqlen=130, n_experts=64, top_k=8)),
     ("f32_e3k3", W("r4", 104, dtype=synth.F32, n_experts=3, top_k=3, seqlen=65)),
     ("bf16_e1k1", W("r5", 105, n_experts=1, top_k=1, seqlen=40)),
+    # 64 lanes per token (E = 256), a group size that does not divide E, and
+    # more than 1024 tokens (64-token workgroups, a partial 4-tile expert pass)
+    ("bf16_e256k8", W("r6", 107, batch=1, seqlen=96, n_experts=256, top_k=8)),
+    ("bf16_e100k5", W("r7", 108, batch=2, seqlen=150, n_experts=100, top_k=5)),
+    ("bf16_e40k3_m2048", W("r8", 109, batch=4, seqlen=512, n_experts=40, top_k=3)),
 ]
 
 
@@ -322,6 +327,9 @@ DEC_CASES = [
     ("bf16_e8k2", W("d1", 501, batch=16, seqlen=1)),
     ("bf16_e32k4", W("d2", 502, batch=40, seqlen=1, n_experts=32, top_k=4, d_model=512)),
     ("f32_g2", W("d3", 503, batch=8, seqlen=1, dtype=synth.F32, nheads=4, ngroups=2, dstate=32)),
+    # state sizes and k bounds of the other decode kernel instantiations
+    ("bf16_k1_n16", W("d4", 504, batch=24, seqlen=1, top_k=1, dstate=16, nheads=3)),
+    ("bf16_e16k8_n64", W("d5", 505, batch=20, seqlen=1, n_experts=16, top_k=8, dstate=64)),
 ]
 
 
