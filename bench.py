@@ -45,6 +45,7 @@ KERNEL_NAMES = [
     (r"route_kernel", "route_topk"),
     (r"bucket_count_kernel", "bucket_count"),
     (r"bucket_place_kernel", "bucket_place"),
+    (r"proj_kernel.*Lb1E", "output_project"),
     (r"proj_kernel|proj_skinny_kernel", "expert_project"),
     (r"mix_c_kernel", "mix_c"),
     (r"scan_gram_kernel", "scan_gram"),
@@ -349,6 +350,55 @@ def e_sweep(args):
         open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+def output_projection(args):
+    """The output projection after the recurrence on every token of the
+    workload (out = W_out y, [M, H*P] -> [M, D]): one JSON line with its
+    TFLOP/s and fraction of the matrix-core peak, and the oracle's rate on a
+    sample of rows."""
+    import torch
+
+    from oracle import swimba as osw
+    from selective_ssm_parameter_amd import binding as sb
+    from selective_ssm_parameter_amd import synth
+
+    wl = workload(args.config)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    K = wl.nheads * wl.headdim
+    inp = synth.output_projection_inputs(wl)
+    y = torch.from_numpy(inp["y"].reshape(wl.tokens, K)).to("cuda:0", dt)
+    w = torch.from_numpy(inp["w_out"]).to("cuda:0", dt)
+    out = torch.empty(wl.tokens, wl.d_model, dtype=dt, device="cuda:0")
+    dims = sb.dims_of(wl)
+    for _ in range(args.warmup):
+        sb.swimba_output_project(dims, y, w, out)
+    torch.cuda.synchronize()
+    sb.profile_select("output_project")
+    sb.profile_enable(True)
+    for _ in range(args.steps):
+        sb.swimba_output_project(dims, y, w, out)
+    torch.cuda.synchronize()
+    rep = json.loads(sb.profile_report())["output_project"]
+    sb.profile_enable(False)
+    sb.profile_select(None)
+    avg_s = rep["ms"] / rep["launches"] / 1e3
+    flops = 2 * wl.tokens * K * wl.d_model
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    rows = min(wl.tokens, 2048)
+    t0 = time.perf_counter()
+    osw.output_project(inp["y"][:rows], inp["w_out"])
+    cpu_s = time.perf_counter() - t0
+    print(json.dumps({
+        "metric": "Swimba output projection tokens/sec on 1 MI355X", "value": wl.tokens / avg_s,
+        "unit": "tokens/s", "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"output projection of {args.config}: M={wl.tokens}, "
+                               f"H*P={K} -> d_model={wl.d_model}"},
+        "roofline": {"bound": "mfma", "achieved": flops / avg_s / 1e12, "peak": peak,
+                     "unit": "TFLOP/s", "frac": flops / avg_s / 1e12 / peak,
+                     "avg_us": avg_s * 1e6, "algorithmic_flops": flops},
+        "cpu_baseline": {"value": rows / cpu_s, "unit": "tokens/s", "kind": "oracle",
+                         "sample": f"first {rows} tokens, {cpu_s:.2f} s"}}), flush=True)
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """The fp64 oracle on a bounded sample: the first rows of the batch, all
     heads, whole sequences; rows are added until ``budget_s`` is used."""
@@ -531,6 +581,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary of two rocprofv3 --pmc runs")
     ap.add_argument("--out", help="summary file to write")
+    ap.add_argument("--output-projection", action="store_true",
+                    help="time the output projection alone on the --config workload")
     ap.add_argument("--e-sweep", action="store_true",
                     help="prefill tokens/s at the c3 dimensions for E in 4..64 (k = 2)")
     ap.add_argument("--bench-json", help="the JSON output of the profiled bench run")
@@ -551,6 +603,9 @@ def main():
         sys.exit(2)
     if args.e_sweep:
         e_sweep(args)
+        return
+    if args.output_projection:
+        output_projection(args)
         return
     r = run_gpu(args)
     wl = r["wl"]

@@ -200,6 +200,22 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
                                  hipStream_t stream);
 
 /*
+ * Output projection of the mixer: the single projection that follows the
+ * recurrence (gist.science English summary, Technical Summary section 2,
+ * Architecture Details, the state-update equation "followed by a single
+ * output projection"), read as Mamba-2's projection from the H*P readout
+ * back to d_model: out[m, :] = W_out y[m, :], fp32 accumulation, out rounded
+ * to dtype. No bias.
+ *   y      [M, H*P] dtype   (the y of swimba_ssd_chunk_scan / swimba_decode_step)
+ *   w_out  [D, H*P] dtype   (D = d_model)
+ *   out    [M, D]   dtype out (must not overlap y or w_out)
+ * Uses dims.batch, seqlen, d_model, nheads, headdim and dtype (M = batch *
+ * seqlen). No workspace. Errors as for the other calls.
+ */
+swimba_status swimba_output_project(const swimba_dims* dims, const void* y, const void* w_out,
+                                    void* out, hipStream_t stream);
+
+/*
  * Per-kernel timing with HIP events, for measurement only. While enabled,
  * every kernel the library launches is bracketed by two events recorded on
  * its stream. swimba_profile_report() waits for the recorded events, writes a

@@ -22,7 +22,9 @@ identity; Theorem 3.4 equality under static routing and its bound under
 dynamic routing; a chunked fp64 solve; the BIBO bound of Theorem 3.3; dense
 brute force with explicit powers on T <= 8; the Theorem 3.5 sigmoid
 construction (tests/golden/); linearity, relabelling, causality, split and
-resume, decode == prefill; projection against an explicit triple loop.
+resume, decode == prefill; projection against an explicit triple loop; the
+output projection against an explicit double loop, the identity and a
+column selection.
 """
 from __future__ import annotations
 
@@ -183,6 +185,19 @@ def forward(u: np.ndarray, w_router: np.ndarray, w_experts: np.ndarray, a: np.nd
     B_hat, X, C_mix = mix_streams(s, r.w)
     y, hT = recurrence(B_hat, X, C_mix, a, h_init, Bt, T, heads=heads)
     return {"y": y, "h_final": hT, "routing": r, "B_hat": B_hat, "X": X, "C_mix": C_mix}
+
+
+def output_project(y: np.ndarray, w_out: np.ndarray) -> np.ndarray:
+    """The single output projection after the recurrence, in fp64.
+
+    [gist-en] Technical Summary section 2, Architecture Details: the state
+    update is followed by one output projection. Read as the map of each
+    token's H*P readout back to d_model with no bias: out_t = W_out y_t.
+    y: [M, H, P] or [M, H*P]; w_out: [D, H*P]. Returns [M, D].
+    """
+    yf = np.asarray(y, np.float64)
+    yf = yf.reshape(yf.shape[0], -1)
+    return yf @ np.asarray(w_out, np.float64).T
 
 
 def decode_step(u_t: np.ndarray, w_router: np.ndarray, w_experts: np.ndarray, a: np.ndarray,

@@ -27,7 +27,8 @@ STATUS = {
 EXPORTS = (
     "swimba_abi_version", "swimba_last_error", "swimba_workspace_size", "swimba_route_topk",
     "swimba_expert_project_mix", "swimba_ssd_chunk_scan", "swimba_decode_step",
-    "swimba_profile_enable", "swimba_profile_report", "swimba_profile_select",
+    "swimba_output_project", "swimba_profile_enable", "swimba_profile_report",
+    "swimba_profile_select",
 )
 
 
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.swimba_ssd_chunk_scan.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
     L.swimba_decode_step.restype = I32
     L.swimba_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
+    L.swimba_output_project.restype = I32
+    L.swimba_output_project.argtypes = [D, P, P, P, S]
     L.swimba_profile_enable.restype = I32
     L.swimba_profile_enable.argtypes = [I32]
     L.swimba_profile_report.restype = I32
@@ -171,6 +174,11 @@ def swimba_decode_step(dims, u, w_router, w_experts, a, h, y, topk_idx, ws, ws_b
     _check(lib().swimba_decode_step(
         ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(a), _ptr(h), _ptr(y),
         _ptr(topk_idx), _ptr(ws), nb, _stream(stream)))
+
+
+def swimba_output_project(dims, y, w_out, out, stream=None):
+    _check(lib().swimba_output_project(ctypes.byref(dims), _ptr(y), _ptr(w_out), _ptr(out),
+                                       _stream(stream)))
 
 
 def profile_enable(on: bool):

@@ -377,6 +377,26 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
   return hip_status(e, "decode_step state launch");
 }
 
+swimba_status swimba_output_project(const swimba_dims* dims, const void* y, const void* w_out,
+                                    void* out, hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if (d.D % 32 != 0) return fail(SWIMBA_ERR_UNSUPPORTED, "d_model must be a multiple of 32");
+  if (d.HP % 8 != 0) return fail(SWIMBA_ERR_UNSUPPORTED, "nheads * headdim must be a multiple of 8");
+  const int64_t in_bytes = d.bf16 ? 2 : 4;  // y, w_out and out elements
+  if (d.M * d.HP * in_bytes >= (int64_t(1) << 31) || d.D * d.HP * in_bytes >= (int64_t(1) << 31) ||
+      d.M * d.D >= (int64_t(1) << 31))
+    return fail(SWIMBA_ERR_DIMS, "problem too large for 31-bit byte offsets");
+  if (d.M == 0) return SWIMBA_OK;
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(w_out);
+  REQUIRE_PTR(out);
+  return hip_status(launch_output_project(d.bf16, (int)d.M, (int)d.HP, (int)d.D, y, w_out, out,
+                                          stream),
+                    "output_project launch");
+}
+
 swimba_status swimba_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;

@@ -68,6 +68,10 @@ hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t
 
 // Decode: in-place state update and readout for one token per sequence.
 // C~ is summed here from the per-slot fp32 parts c_part [Bt, k, G*N], in slot order.
+// Output projection out[M, N] = y[M, K] w_out[N, K]^T (out in the input type).
+hipError_t launch_output_project(bool is_bf16, int M, int K, int N, const void* y,
+                                 const void* w_out, void* out, hipStream_t s);
+
 hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
                                const void* B_hat, const void* X_hat, const float* c_part,
                                const float* a, float* h, void* y, hipStream_t s);

@@ -79,9 +79,7 @@ struct ProjLay {
 // a unit.
 constexpr int kProjGroupRows = 4;
 template <int GR>
-__device__ __forceinline__ bool xcd_tile(const int4v* __restrict__ tile_info, int nrow_tiles,
-                                         int CT, int& tile, int& ctile) {
-  const int nt = tile_info[nrow_tiles][0];
+__device__ __forceinline__ bool xcd_unit(int nt, int CT, int& tile, int& ctile) {
   const int units = nt * CT;
   const int per = (units + 7) / 8;
   const int slot = blockIdx.x / 8;
@@ -95,13 +93,22 @@ __device__ __forceinline__ bool xcd_tile(const int4v* __restrict__ tile_info, in
   tile = group * GR + (rem - ctile * gm);
   return true;
 }
+template <int GR>
+__device__ __forceinline__ bool xcd_tile(const int4v* __restrict__ tile_info, int nrow_tiles,
+                                         int CT, int& tile, int& ctile) {
+  return xcd_unit<GR>(tile_info[nrow_tiles][0], CT, tile, ctile);
+}
 
-template <typename T, class C>
+// PLAIN: the same kernel as a plain GEMM out[M, W] = u[M, D] wexp[W, D]^T (the
+// output projection): rows are u's own rows in order (nrow_tiles row tiles),
+// one weight matrix, and the epilogue writes out in TO.
+template <typename T, class C, bool PLAIN = false, typename TO = float>
 __global__ __launch_bounds__(C::NTH) void proj_kernel(
     const T* __restrict__ u, const T* __restrict__ wexp, const int32_t* __restrict__ sorted,
     const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
     int HP, int GN, int k, int nrow_tiles, typename StreamOf<T>::type* __restrict__ X_hat,
-    typename StreamOf<T>::type* __restrict__ B_hat, float* __restrict__ c_part) {
+    typename StreamOf<T>::type* __restrict__ B_hat, float* __restrict__ c_part,
+    TO* __restrict__ out) {
   typedef typename StreamOf<T>::type S;
   typedef ProjLay<T, C> Lay;
   constexpr int BM = C::BM, BN = C::BN, NTH = C::NTH, NW = C::NW, TM = C::TM, TN = C::TN;
@@ -119,18 +126,26 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
   __shared__ float rw[BM];
 
   const int CT = (W + BN - 1) / BN;
-  int tile, ctile;
-  if (!xcd_tile<kProjGroupRows>(tile_info, nrow_tiles, CT, tile, ctile)) return;
-  const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
-  const int e = ti[0];
-  if (e < 0) return;
-  const int row0 = ti[1], nrows = ti[2];
+  int tile, ctile, e, row0, nrows;
+  if constexpr (PLAIN) {
+    if (!xcd_unit<kProjGroupRows>(nrow_tiles, CT, tile, ctile)) return;
+    e = 0;
+    row0 = tile * BM;
+    nrows = min(BM, M - row0);
+  } else {
+    if (!xcd_tile<kProjGroupRows>(tile_info, nrow_tiles, CT, tile, ctile)) return;
+    const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
+    e = ti[0];
+    if (e < 0) return;
+    row0 = ti[1];
+    nrows = ti[2];
+  }
   for (int r = threadIdx.x; r < BM; r += NTH) {
     if (r < nrows) {
-      const int p = sorted[row0 + r];
+      const int p = PLAIN ? row0 + r : sorted[row0 + r];
       rtok[r] = p / k;
       rslot[r] = p - (p / k) * k;
-      rw[r] = sorted_w[row0 + r];
+      rw[r] = PLAIN ? 1.f : sorted_w[row0 + r];
     } else {
       rtok[r] = -1;
       rslot[r] = 0;
@@ -268,7 +283,12 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
         v[4 + q] = acc[i][2 * jj + 1][q];
       }
       if (tok < 0) continue;
-      if (col < HP) {
+      if constexpr (PLAIN) {
+        typename Vec<TO>::x8 o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = from_f32<TO>(v[q]);
+        store8<TO>(&out[pair * W + col], o);
+      } else if (col < HP) {
         S8 o;
 #pragma unroll
         for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(v[q]);
@@ -485,7 +505,8 @@ static hipError_t launch_proj_cfg(const ProjGeom& g, const T* u, const T* wexp,
   const dim3 grid((unsigned)((ntiles + 7) / 8 * 8));  // a multiple of the 8 XCDs
   prof_begin("expert_project", s);
   hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, u, wexp, sorted, sorted_w,
-                     tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part);
+                     tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part,
+                     (float*)nullptr);
   prof_end(s);
   return hipGetLastError();
 }
@@ -529,6 +550,41 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
                      g.M, g.k, g.GN(), C_mix);
   prof_end(s);
   return hipGetLastError();
+}
+
+// Output projection out[M, N] = y[M, K] w_out[N, K]^T (fp32 accumulation, out in
+// the input type): the expert projection's GEMM with rows in order.
+template <typename T, class C>
+static hipError_t launch_outproj_cfg(int M, int K, int N, const T* y, const T* w, T* out,
+                                     hipStream_t s) {
+  const int nrow = (M + C::BM - 1) / C::BM;
+  const int units = nrow * ((N + C::BN - 1) / C::BN);
+  prof_begin("output_project", s);
+  hipLaunchKernelGGL((proj_kernel<T, C, true, T>), dim3((unsigned)((units + 7) / 8 * 8)),
+                     dim3(C::NTH), 0, s, y, w, (const int32_t*)nullptr, (const float*)nullptr,
+                     (const int4v*)nullptr, M, K, N, 0, 0, 1, nrow,
+                     (typename StreamOf<T>::type*)nullptr, (typename StreamOf<T>::type*)nullptr,
+                     (float*)nullptr, out);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_output_project(bool is_bf16, int M, int K, int N, const void* y,
+                                 const void* w_out, void* out, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (is_bf16) {
+    const bf16* yb = static_cast<const bf16*>(y);
+    const bf16* wb = static_cast<const bf16*>(w_out);
+    bf16* ob = static_cast<bf16*>(out);
+    if (M >= 4096) return launch_outproj_cfg<bf16, ProjBig>(M, K, N, yb, wb, ob, s);
+    if (M >= 512) return launch_outproj_cfg<bf16, ProjMid>(M, K, N, yb, wb, ob, s);
+    return launch_outproj_cfg<bf16, ProjSmall>(M, K, N, yb, wb, ob, s);
+  }
+  const float* yf = static_cast<const float*>(y);
+  const float* wf = static_cast<const float*>(w_out);
+  float* of = static_cast<float*>(out);
+  if (M >= 512) return launch_outproj_cfg<float, ProjMid>(M, K, N, yf, wf, of, s);
+  return launch_outproj_cfg<float, ProjSmall>(M, K, N, yf, wf, of, s);
 }
 
 hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const void* w_experts,

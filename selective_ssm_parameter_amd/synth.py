@@ -13,6 +13,9 @@ Recipe (fixed draw order, numpy PCG64 ``default_rng(seed)``):
   4. u     ~ N(0, 1)                   shape [Bt, T, D]
   5. h_init ~ N(0, 1) * sqrt(v)        shape [Bt, H, N, P] fp32 (when asked)
 Decode steps draw their token from ``default_rng([seed, step])``.
+The output projection draws from ``default_rng([seed, 7919])``: W_out ~
+N(0, 1) * sqrt(1/(H*P)) of shape [D, H*P], then y ~ N(0, 1) of shape
+[Bt*T, H, P] (standing in for the readout that feeds it).
 
 bf16 workloads round every tensor except ``a`` and ``h_init`` to bf16 with
 round-to-nearest-even; the returned numpy arrays hold the rounded values in
@@ -126,6 +129,19 @@ def decode_token(wl: Workload, step: int, batch_rows: int | None = None) -> np.n
     if batch_rows is not None:
         u = u[:batch_rows]
     return _store(u, wl.dtype)
+
+
+def output_projection_inputs(wl: Workload, rows: int | None = None) -> dict:
+    """W_out [D, H*P] and y [M, H, P] for the output projection (same dtype
+    rule as u); ``rows`` keeps only the first rows of y."""
+    rng = np.random.default_rng([wl.seed, 7919])
+    HP = wl.nheads * wl.headdim
+    w_out = _store(rng.standard_normal((wl.d_model, HP), dtype=np.float32)
+                   * np.float32(math.sqrt(1.0 / HP)), wl.dtype)
+    y = rng.standard_normal((wl.tokens, wl.nheads, wl.headdim), dtype=np.float32)
+    if rows is not None:
+        y = y[:rows]
+    return {"w_out": w_out, "y": _store(y, wl.dtype)}
 
 
 def small(name: str, seed: int, **dims) -> Workload:

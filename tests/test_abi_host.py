@@ -41,7 +41,7 @@ def lib():
 def test_exports_every_declared_symbol():
     L = lib()
     syms = declared_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 11, syms
     for s in syms:
         assert hasattr(L, s), f"{s} declared in swimba.h but not exported"
     assert set(syms) == set(sb.EXPORTS)
@@ -130,6 +130,17 @@ def test_workspace_checks():
     st = L.swimba_decode_step(ctypes.byref(good_dims(seqlen=2)), FAKE, FAKE, FAKE, FAKE, FAKE,
                               FAKE, None, FAKE, 1 << 30, None)
     assert st == -2
+
+
+def test_output_project_argument_checks():
+    L = lib()
+    d = good_dims()
+    assert L.swimba_output_project(ctypes.byref(d), None, FAKE, FAKE, None) == -1
+    assert "y is NULL" in L.swimba_last_error().decode()
+    assert L.swimba_output_project(ctypes.byref(d), FAKE, FAKE, MISALIGNED, None) == -5
+    bad = good_dims(d_model=100)
+    assert L.swimba_output_project(ctypes.byref(bad), FAKE, FAKE, FAKE, None) == -3
+    assert L.swimba_output_project(ctypes.byref(good_dims(seqlen=0)), None, None, None, None) == 0
 
 
 def test_empty_inputs_are_no_ops():

@@ -103,3 +103,24 @@ def test_decode_full_size():
         say(f"  step {step}: y err {ey:.3e} h err {eh:.3e}")
         assert ey < TOL[wl.dtype] and eh < TOL[wl.dtype]
         h_ref = ref["h"]
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_output_project_full_size(name):
+    # every token of the workload through the output projection; the oracle
+    # checks 256 sampled tokens (rows are independent)
+    wl = synth.WORKLOADS[name]
+    K = wl.nheads * wl.headdim
+    say(f"[fullsize] output projection {name}: M={wl.tokens} K={K} D={wl.d_model}")
+    inp = synth.output_projection_inputs(wl)
+    y = dev(inp["y"].reshape(wl.tokens, K), tdt(wl))
+    w = dev(inp["w_out"], tdt(wl))
+    out = torch.empty(wl.tokens, wl.d_model, dtype=tdt(wl), device="cuda")
+    sb.swimba_output_project(sb.dims_of(wl), y, w, out)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(wl.seed).choice(wl.tokens, 256, replace=False)
+    ref = osw.output_project(inp["y"][rows], inp["w_out"])
+    got = host(out[torch.from_numpy(rows).to("cuda")])
+    err = float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref * ref)))
+    say(f"  sampled rows: err {err:.3e}")
+    assert err < TOL[wl.dtype]

@@ -333,6 +333,32 @@ DEC_CASES = [
 ]
 
 
+# ---------------------------------------------------------------- output projection
+
+OUT_CASES = [
+    ("bf16_small", W("o1", 601, batch=3, seqlen=71)),
+    ("bf16_mid_ragged", W("o2", 602, batch=2, seqlen=400, d_model=96, nheads=6)),
+    ("bf16_big", W("o3", 603, batch=3, seqlen=1400, d_model=320, nheads=8)),
+    ("f32_ragged", W("o4", 604, dtype=synth.F32, batch=2, seqlen=65, d_model=160, nheads=3)),
+]
+
+
+@pytest.mark.parametrize("name,wl", OUT_CASES, ids=[c[0] for c in OUT_CASES])
+def test_output_project(name, wl):
+    say(f"[outproj] {name} M={wl.tokens} K={wl.nheads * wl.headdim} D={wl.d_model}")
+    inp = synth.output_projection_inputs(wl)
+    dt = tdt(wl)
+    y = dev(inp["y"].reshape(wl.tokens, -1), dt)
+    w = dev(inp["w_out"], dt)
+    out = torch.full((wl.tokens, wl.d_model), float("nan"), dtype=dt, device="cuda")
+    sb.swimba_output_project(sb.dims_of(wl), y, w, out)
+    torch.cuda.synchronize()
+    ref = osw.output_project(inp["y"], inp["w_out"])
+    err = rel_err(host(out), ref)
+    say(f"[outproj] {name} rel err {err:.2e}")
+    assert err < TOL[wl.dtype]
+
+
 @pytest.mark.parametrize("name,wl", DEC_CASES, ids=[c[0] for c in DEC_CASES])
 def test_decode_steps(name, wl):
     say(f"[decode] {name}")

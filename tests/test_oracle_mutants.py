@@ -16,6 +16,7 @@ _orig_route = osw.route
 _orig_mix = osw.mix_streams
 _orig_rec = osw.recurrence
 _orig_streams = osw.expert_streams
+_orig_outproj = osw.output_project
 
 
 def mix_unweighted(streams, w):
@@ -89,6 +90,20 @@ def streams_transposed_x(u, w_experts, idx, nheads, headdim, ngroups, dstate, he
     return osw.Streams(X=s.X.reshape(M, k, P, H).transpose(0, 1, 3, 2).copy(), B=s.B, C=s.C)
 
 
+def outproj_transposed_y(y, w_out):
+    # the readout taken as [P, H] instead of [H, P]
+    yf = np.asarray(y, np.float64)
+    if yf.ndim == 3:
+        yf = yf.transpose(0, 2, 1)
+    return _orig_outproj(yf, w_out)
+
+
+def outproj_weight_transposed(y, w_out):
+    # W_out indexed [H*P, D]: reshape instead of transpose
+    w = np.asarray(w_out, np.float64)
+    return _orig_outproj(y, w.reshape(w.shape[1], w.shape[0]).T)
+
+
 MUTANTS = {
     "mix_unweighted": ("mix_streams", mix_unweighted),
     "mix_renormalised": ("mix_streams", mix_renormalised),
@@ -100,6 +115,8 @@ MUTANTS = {
     "rec_wrong_group": ("recurrence", rec_wrong_group),
     "streams_b_c_swapped": ("expert_streams", streams_b_c_swapped),
     "streams_transposed_x": ("expert_streams", streams_transposed_x),
+    "outproj_transposed_y": ("output_project", outproj_transposed_y),
+    "outproj_weight_transposed": ("output_project", outproj_weight_transposed),
 }
 
 CHECKS = [
@@ -113,6 +130,7 @@ CHECKS = [
     lambda: tp.check_brute_force(91),
     lambda: tp.check_brute_force(93, top_k=3, n_experts=3, nheads=4, ngroups=2),
     lambda: tp.check_brute_force(95, n_experts=4, top_k=2, d_model=1),
+    tp.check_output_projection,
 ]
 
 

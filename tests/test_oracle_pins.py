@@ -84,6 +84,27 @@ def check_projection_triple_loop():
             assert np.allclose(s.C[m, j].ravel(), z[H * P + G * N:], rtol=1e-14, atol=1e-14)
 
 
+def check_output_projection():
+    # explicit double loop on a tiny case
+    rng = np.random.default_rng(6)
+    M, H, P, D = 4, 2, 3, 5
+    y = rng.standard_normal((M, H, P))
+    w = rng.standard_normal((D, H * P))
+    out = osw.output_project(y, w)
+    assert out.shape == (M, D)
+    for m in range(M):
+        for d in range(D):
+            ref = sum(w[d, h * P + p] * y[m, h, p] for h in range(H) for p in range(P))
+            assert abs(out[m, d] - ref) < 1e-12
+    # the identity reproduces y (as [M, H*P]); a row selection picks columns
+    assert np.array_equal(osw.output_project(y, np.eye(H * P)), y.reshape(M, -1))
+    sel = np.zeros((2, H * P))
+    sel[0, 4] = 1.0
+    sel[1, 1] = 1.0
+    got = osw.output_project(y, sel)
+    assert np.array_equal(got[:, 0], y[:, 1, 1]) and np.array_equal(got[:, 1], y[:, 0, 1])
+
+
 def check_plain_ssm_k1_e1():
     # k = E = 1: the softmax over one logit is 1 and the layer is one SSM.
     wl = tiny(21, n_experts=1, top_k=1, seqlen=19, nheads=3, dstate=5, headdim=4, batch=2)
@@ -320,6 +341,10 @@ def test_router_sigmoid_and_ties():
 
 def test_projection_triple_loop():
     check_projection_triple_loop()
+
+
+def test_output_projection():
+    check_output_projection()
 
 
 def test_plain_ssm_k1_e1():
