@@ -273,10 +273,22 @@ def run_gpu(args):
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "traffic": stored_traffic(dom, wl.name),
                 "algorithmic_bytes": nbytes, "avg_us": avg_s * 1e6}
-    return {
+    res = {
         "wl": wl, "value": value, "elapsed": elapsed, "kernels": kernels, "roofline": roof,
         "value_without_events": tokens * args.steps / elapsed_plain,
     }
+    if is_decode(wl):
+        # Every kernel of a decode step is bound by HBM, and a kernel's time
+        # also carries the write-back of dirty lines the one before it left
+        # (the state update's writes drain while the next step's projection
+        # reads): the whole step's algorithmic bytes over the step time.
+        step_bytes = sum(m[2] for m in models.values())
+        step_s = elapsed / args.steps
+        res["step_roofline"] = {"bound": "hbm", "achieved": step_bytes / step_s / 1e9,
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": step_bytes / step_s / 1e9 / PEAK_HBM_GBS,
+                                "algorithmic_bytes": step_bytes}
+    return res
 
 
 E_SWEEP = (4, 8, 16, 32, 64)
@@ -638,6 +650,8 @@ def main():
         "kernels": r["kernels"],
         "value_without_events": r["value_without_events"],
     }
+    if "step_roofline" in r:
+        out["step_roofline"] = r["step_roofline"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
