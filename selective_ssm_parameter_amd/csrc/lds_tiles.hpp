@@ -56,6 +56,37 @@ __device__ __forceinline__ void dma_tile(BufRes rs, uint32_t base, uint32_t pitc
   }
 }
 
+// Copies of a tile whose rows and chunks are all valid: each lane's byte
+// offset within the tile is fixed (planned once), and the tile's position
+// enters as the copy's scalar offset, so a copy costs no vector arithmetic.
+// off[m] is the lane's offset for this wave's m-th instruction (instruction
+// 4m + wave of the tile, as in dma_tile).
+template <int NROWS, int CPR, class Swz>
+__device__ __forceinline__ void dma_plan(uint32_t pitch, int wave, int lane, Swz swz,
+                                         uint32_t* off) {
+  constexpr int NI = NROWS * CPR / 64;
+#pragma unroll
+  for (int i0 = 0; i0 < NI; i0 += 4) {
+    const int slot = 64 * (i0 + wave) + lane;
+    const int r = slot / CPR, pc = slot % CPR;
+    off[i0 / 4] = r * pitch + 16 * (pc ^ swz(r));
+  }
+}
+template <int NROWS, int CPR>
+__device__ __forceinline__ void dma_tile_full(BufRes rs, uint32_t base, const uint32_t* off,
+                                              unsigned char* dst, int wave) {
+  constexpr int NI = NROWS * CPR / 64;
+#pragma unroll
+  for (int i0 = 0; i0 < NI; i0 += 4) {
+    const int i = i0 + wave;
+    if (NI % 4 == 0 || i < NI) {
+      const uint32_t o = off[i0 / 4];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, o, base, 0, 0);
+    }
+  }
+}
+
 // A K-major operand fragment from a row-major [k][col] LDS tile: lane (g, c)
 // gets rows k0 + 8g .. k0 + 8g + 7 of column col0 + c. 2-byte types use two
 // transposing reads (in a 16-lane group, lane i receives element i % 4 of the

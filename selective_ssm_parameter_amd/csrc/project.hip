@@ -102,7 +102,10 @@ __device__ __forceinline__ bool xcd_tile(const int4v* __restrict__ tile_info, in
 // PLAIN: the same kernel as a plain GEMM out[M, W] = u[M, D] wexp[W, D]^T (the
 // output projection): rows are u's own rows in order (nrow_tiles row tiles),
 // one weight matrix, and the epilogue writes out in TO.
-template <typename T, class C, bool PLAIN = false, typename TO = float>
+// KFULL: d is a multiple of kProjStages K tiles, so no copy ever needs a K
+// bound: the per-lane part of every copy offset is fixed for the workgroup and
+// the K tile enters as the copy's scalar offset (no vector arithmetic per copy).
+template <typename T, class C, bool PLAIN = false, typename TO = float, bool KFULL = false>
 __global__ __launch_bounds__(C::NTH) void proj_kernel(
     const T* __restrict__ u, const T* __restrict__ wexp, const int32_t* __restrict__ sorted,
     const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
@@ -183,21 +186,48 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
     const int col = col0 + r;
     bbase[m] = col < W ? (uint32_t)col * D * ES : kOOB;
   }
+  // KFULL: lane offsets with the row and chunk folded in (rows past the group
+  // or columns past W keep an offset beyond the buffer whatever the K tile)
+  uint32_t aoff[MA], boff[MB];
+#pragma unroll
+  for (int m = 0; m < MA; ++m) aoff[m] = abase[m] != kOOB ? abase[m] + 16u * alc[m] : kOOB;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) boff[m] = bbase[m] != kOOB ? bbase[m] + 16u * blc[m] : kOOB;
   auto fetch = [&](unsigned char* st, int k0) {
+    if constexpr (KFULL) {
+      // the look-ahead of the last turn re-reads the last K tile (never used)
+      const int ks = __builtin_amdgcn_readfirstlane(min(k0, D - BK) * (int)ES);
 #pragma unroll
-    for (int m = 0; m < MA; ++m) {
-      const int kk = k0 + alc[m] * (16 / (int)ES);
-      const uint32_t off = (abase[m] != kOOB && kk < D) ? abase[m] + kk * ES : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rA, (__attribute__((address_space(3))) void*)(st + 1024 * (wave + NW * m)), 16, off, 0, 0, 0);
-    }
+      for (int m = 0; m < MA; ++m) {
+        const uint32_t off = aoff[m];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (__attribute__((address_space(3))) void*)(st + 1024 * (wave + NW * m)), 16, off,
+            ks, 0, 0);
+      }
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const int kk = k0 + blc[m] * (16 / (int)ES);
-      const uint32_t off = (bbase[m] != kOOB && kk < D) ? bbase[m] + kk * ES : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rW, (__attribute__((address_space(3))) void*)(st + Lay::AB + 1024 * (wave + NW * m)), 16,
-          off, 0, 0, 0);
+      for (int m = 0; m < MB; ++m) {
+        const uint32_t off = boff[m];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rW, (__attribute__((address_space(3))) void*)(st + Lay::AB + 1024 * (wave + NW * m)),
+            16, off, ks, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < MA; ++m) {
+        const int kk = k0 + alc[m] * (16 / (int)ES);
+        const uint32_t off = (abase[m] != kOOB && kk < D) ? abase[m] + kk * ES : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (__attribute__((address_space(3))) void*)(st + 1024 * (wave + NW * m)), 16, off, 0,
+            0, 0);
+      }
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const int kk = k0 + blc[m] * (16 / (int)ES);
+        const uint32_t off = (bbase[m] != kOOB && kk < D) ? bbase[m] + kk * ES : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rW, (__attribute__((address_space(3))) void*)(st + Lay::AB + 1024 * (wave + NW * m)),
+            16, off, 0, 0, 0);
+      }
     }
   };
 
@@ -241,7 +271,7 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
   // no branches in the loop the compiler's own wait counts see which stage a
   // copy fills, and never drain all copies before reading a stage.
   const int nk = (D + BK - 1) / BK;
-  const int nk4 = (nk + kProjStages - 1) / kProjStages * kProjStages;
+  const int nk4 = (nk + kProjStages - 1) / kProjStages * kProjStages;  // == nk when KFULL
   fetch(stg0, 0);
   fetch(stg1, BK);
   fetch(stg2, 2 * BK);
@@ -504,9 +534,14 @@ static hipError_t launch_proj_cfg(const ProjGeom& g, const T* u, const T* wexp,
   const int ntiles = nrow * ((g.W + C::BN - 1) / C::BN);
   const dim3 grid((unsigned)((ntiles + 7) / 8 * 8));  // a multiple of the 8 XCDs
   prof_begin("expert_project", s);
-  hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, u, wexp, sorted, sorted_w,
-                     tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part,
-                     (float*)nullptr);
+  if (g.D % (kProjStages * ProjLay<T, C>::BK) == 0)
+    hipLaunchKernelGGL((proj_kernel<T, C, false, float, true>), grid, dim3(C::NTH), 0, s, u, wexp,
+                       sorted, sorted_w, tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow,
+                       X_hat, B_hat, c_part, (float*)nullptr);
+  else
+    hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, u, wexp, sorted, sorted_w,
+                       tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part,
+                       (float*)nullptr);
   prof_end(s);
   return hipGetLastError();
 }
@@ -560,11 +595,16 @@ static hipError_t launch_outproj_cfg(int M, int K, int N, const T* y, const T* w
   const int nrow = (M + C::BM - 1) / C::BM;
   const int units = nrow * ((N + C::BN - 1) / C::BN);
   prof_begin("output_project", s);
-  hipLaunchKernelGGL((proj_kernel<T, C, true, T>), dim3((unsigned)((units + 7) / 8 * 8)),
-                     dim3(C::NTH), 0, s, y, w, (const int32_t*)nullptr, (const float*)nullptr,
-                     (const int4v*)nullptr, M, K, N, 0, 0, 1, nrow,
-                     (typename StreamOf<T>::type*)nullptr, (typename StreamOf<T>::type*)nullptr,
-                     (float*)nullptr, out);
+  const dim3 grid((unsigned)((units + 7) / 8 * 8));
+  typedef typename StreamOf<T>::type S;
+  if (K % (kProjStages * ProjLay<T, C>::BK) == 0)
+    hipLaunchKernelGGL((proj_kernel<T, C, true, T, true>), grid, dim3(C::NTH), 0, s, y, w,
+                       (const int32_t*)nullptr, (const float*)nullptr, (const int4v*)nullptr, M, K,
+                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out);
+  else
+    hipLaunchKernelGGL((proj_kernel<T, C, true, T>), grid, dim3(C::NTH), 0, s, y, w,
+                       (const int32_t*)nullptr, (const float*)nullptr, (const int4v*)nullptr, M, K,
+                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out);
   prof_end(s);
   return hipGetLastError();
 }

@@ -279,27 +279,53 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
     return s;
   };
 
-  // ---- HBM -> LDS stage for one step (the tiles this step reads)
+  // ---- HBM -> LDS stage for one step (the tiles this step reads). Whole
+  // tiles (every row and chunk valid: all but a sequence's last partial chunk,
+  // and N = NP) are copied from per-lane offsets planned once, with the tile
+  // position as the scalar offset; the others go through the checked copy.
+  constexpr int NXI = (R * XC / 64 + 3) / 4, NBI = (R * BC / 64 + 3) / 4;
+  constexpr int NCI = (BT * BC / 64 + 3) / 4, NGI = (BT * GC / 64 + 3) / 4;
+  uint32_t xoff[NXI], boff[NBI], coff[WITH_Y ? NCI : 1], goff[WITH_Y ? NGI : 1];
+  dma_plan<R, XC>((uint32_t)HPsz * ES, w, lane, [](int r) { return swz_tr<T, XC>(r); }, xoff);
+  dma_plan<R, BC>((uint32_t)GN * ES, w, lane, [](int r) { return swz_tr<T, BC>(r); }, boff);
+  if (WITH_Y) {
+    dma_plan<BT, BC>((uint32_t)GN * ES, w, lane, [](int r) { return swz_row<T, BC>(r); }, coff);
+    dma_plan<BT, GC>((uint32_t)R * ES, w, lane, [](int r) { return swz_row<T, GC>(r); }, goff);
+  }
+  const bool nfull = N == NP;
   auto fetch = [&](unsigned char* st, ScanStep s) {
     const int c0 = s.ch * L;
     const int Lc = min(L, Tlen - c0);
     const bool last = s.tau == (Lc + BT - 1) / BT - 1;
     const uint32_t prow = (uint32_t)(c0 + s.sig * BT) * KS;  // first pair row of block sig
     const int rlim = (Lc - s.sig * BT) * KS;                  // valid pair rows in the block
-    dma_tile<R, XC>(rX, (prow * (uint32_t)HPsz + h * kP) * ES, (uint32_t)HPsz * ES, st + Lay::XO,
-                    rlim, XC, w, lane, [](int r) { return swz_tr<T, XC>(r); });
-    if (last)
-      dma_tile<R, BC>(rB, (prow * GN + grp * N) * ES, GN * ES, st + Lay::BO, rlim,
-                      (int)(N * ES / 16), w, lane, [](int r) { return swz_tr<T, BC>(r); });
+    const bool rows_full = rlim >= R;
+    const uint32_t xb = (prow * (uint32_t)HPsz + h * kP) * ES;
+    if (rows_full)
+      dma_tile_full<R, XC>(rX, xb, xoff, st + Lay::XO, w);
+    else
+      dma_tile<R, XC>(rX, xb, (uint32_t)HPsz * ES, st + Lay::XO, rlim, XC, w, lane,
+                      [](int r) { return swz_tr<T, XC>(r); });
+    if (last) {
+      const uint32_t bb = (prow * GN + grp * N) * ES;
+      if (rows_full && nfull)
+        dma_tile_full<R, BC>(rB, bb, boff, st + Lay::BO, w);
+      else
+        dma_tile<R, BC>(rB, bb, GN * ES, st + Lay::BO, rlim, (int)(N * ES / 16), w, lane,
+                        [](int r) { return swz_tr<T, BC>(r); });
+    }
     if (WITH_Y) {
-      if (s.sig == 0)
-        dma_tile<BT, BC>(rC, ((uint32_t)(c0 + s.tau * BT) * GN + grp * N) * ES, GN * ES,
-                         st + Lay::CO, Lc - s.tau * BT, (int)(N * ES / 16), w, lane,
-                         [](int r) { return swz_row<T, BC>(r); });
+      if (s.sig == 0) {
+        const uint32_t cb = ((uint32_t)(c0 + s.tau * BT) * GN + grp * N) * ES;
+        if (Lc - s.tau * BT >= BT && nfull)
+          dma_tile_full<BT, BC>(rC, cb, coff, st + Lay::CO, w);
+        else
+          dma_tile<BT, BC>(rC, cb, GN * ES, st + Lay::CO, Lc - s.tau * BT, (int)(N * ES / 16), w,
+                           lane, [](int r) { return swz_row<T, BC>(r); });
+      }
       const int pidx = s.tau * (s.tau + 1) / 2 + s.sig;
       const uint32_t gbase = (uint32_t)((((size_t)s.ch * G + grp) * A.npairs + pidx) * gtile);
-      dma_tile<BT, GC>(rG, gbase * ES, R * ES, st + Lay::GO, BT, GC, w, lane,
-                       [](int r) { return swz_row<T, GC>(r); });
+      dma_tile_full<BT, GC>(rG, gbase * ES, goff, st + Lay::GO, w);
     }
   };
 
