@@ -16,6 +16,8 @@ Decode steps draw their token from ``default_rng([seed, step])``.
 The output projection draws from ``default_rng([seed, 7919])``: W_out ~
 N(0, 1) * sqrt(1/(H*P)) of shape [D, H*P], then y ~ N(0, 1) of shape
 [Bt*T, H, P] (standing in for the readout that feeds it).
+The expert-mixed transition draws per-expert decays from
+``default_rng([seed, 104729])``: a^(e) ~ U[lo, hi] of shape [E, H], fp32.
 
 bf16 workloads round every tensor except ``a`` and ``h_init`` to bf16 with
 round-to-nearest-even; the returned numpy arrays hold the rounded values in
@@ -142,6 +144,14 @@ def output_projection_inputs(wl: Workload, rows: int | None = None) -> dict:
     if rows is not None:
         y = y[:rows]
     return {"w_out": w_out, "y": _store(y, wl.dtype)}
+
+
+def expert_decays(wl: Workload) -> np.ndarray:
+    """Per-expert, per-head decays a^(e)_h ~ U[a_lo, a_hi] (fp32) for the
+    expert-mixed transition, [E, H], from a stream of their own so every other
+    input of the workload is unchanged."""
+    rng = np.random.default_rng([wl.seed, 104729])
+    return rng.uniform(wl.a_lo, wl.a_hi, size=(wl.n_experts, wl.nheads)).astype(np.float32)
 
 
 def small(name: str, seed: int, **dims) -> Workload:
