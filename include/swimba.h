@@ -216,6 +216,55 @@ swimba_status swimba_output_project(const swimba_dims* dims, const void* y, cons
                                     void* out, hipStream_t stream);
 
 /*
+ * Expert-mixed diagonal transition (papernotes.org notes, Limitations and
+ * outlook: the parameter-space mix extended to the transition's diagonal,
+ * keeping the contraction). Each expert e has a per-head decay a_experts[e, h]
+ * in [0, 1]; a token's decay is their convex mix over its selected experts,
+ * the routing weights renormalised over the k slots (slot order, fp32):
+ *   a[t, h] = sum_j w[t, j] a_experts[idx[t, j], h] / sum_j w[t, j]
+ * (an index outside [0, E) adds decay 0 with its weight). Equal expert decays
+ * give back the shared decay. The three calls below use it.
+ *
+ * swimba_mix_decay writes what the mixed scan consumes: per sequence b, head h
+ * and token t of a chunk starting at c0 (chunks of dims.chunk tokens),
+ *   log_decay[b, h, t] = sum_{u = c0}^{t} max(log2 a[u, h], -126)
+ * (a running log2 decay within the chunk; a zero decay counts as 2^-126).
+ *   topk_idx   [M, k] int32;  topk_w [M, k] float32 (from swimba_route_topk)
+ *   a_experts  [E, H] float32
+ *   log_decay  [Bt, H, T] float32 out
+ * No workspace. chunk must be 32, 64, 128 or 256.
+ */
+swimba_status swimba_mix_decay(const swimba_dims* dims, const int32_t* topk_idx,
+                               const float* topk_w, const float* a_experts, float* log_decay,
+                               hipStream_t stream);
+
+/*
+ * swimba_ssd_chunk_scan with the expert-mixed decay: the same recurrence with
+ * the decay of token t, h_t = a[t, h] h_{t-1} + sum_j B_hat X_hat^T, given as
+ * the log_decay of swimba_mix_decay for the same dims (same chunk). Every
+ * other argument, the workspace and the errors are those of
+ * swimba_ssd_chunk_scan.
+ *   log_decay  [Bt, H, T] float32 (may be NULL only when seqlen is 0)
+ */
+swimba_status swimba_ssd_chunk_scan_mixed(const swimba_dims* dims, const void* B_hat,
+                                          const void* X_hat, const void* C_mix,
+                                          const float* log_decay, const float* h_init, void* y,
+                                          float* h_final, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
+
+/*
+ * swimba_decode_step with the expert-mixed decay: each sequence's decay is
+ * mixed from a_experts [E, H] float32 with this step's routing. Every other
+ * argument, the workspace (SWIMBA_CALL_DECODE) and the errors are those of
+ * swimba_decode_step.
+ */
+swimba_status swimba_decode_step_mixed(const swimba_dims* dims, const void* u,
+                                       const void* w_router, const void* w_experts,
+                                       const float* a_experts, float* h, void* y,
+                                       int32_t* topk_idx, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/*
  * Per-kernel timing with HIP events, for measurement only. While enabled,
  * every kernel the library launches is bracketed by two events recorded on
  * its stream. swimba_profile_report() waits for the recorded events, writes a

@@ -28,7 +28,8 @@ EXPORTS = (
     "swimba_abi_version", "swimba_last_error", "swimba_workspace_size", "swimba_route_topk",
     "swimba_expert_project_mix", "swimba_ssd_chunk_scan", "swimba_decode_step",
     "swimba_output_project", "swimba_profile_enable", "swimba_profile_report",
-    "swimba_profile_select",
+    "swimba_profile_select", "swimba_mix_decay", "swimba_ssd_chunk_scan_mixed",
+    "swimba_decode_step_mixed",
 )
 
 
@@ -77,6 +78,12 @@ def lib() -> ctypes.CDLL:
     L.swimba_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
     L.swimba_output_project.restype = I32
     L.swimba_output_project.argtypes = [D, P, P, P, S]
+    L.swimba_mix_decay.argtypes = [D, P, P, P, P, S]
+    L.swimba_mix_decay.restype = I32
+    L.swimba_ssd_chunk_scan_mixed.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
+    L.swimba_ssd_chunk_scan_mixed.restype = I32
+    L.swimba_decode_step_mixed.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
+    L.swimba_decode_step_mixed.restype = I32
     L.swimba_profile_enable.restype = I32
     L.swimba_profile_enable.argtypes = [I32]
     L.swimba_profile_report.restype = I32
@@ -176,6 +183,27 @@ def swimba_decode_step(dims, u, w_router, w_experts, a, h, y, topk_idx, ws, ws_b
         _ptr(topk_idx), _ptr(ws), nb, _stream(stream)))
 
 
+def swimba_mix_decay(dims, topk_idx, topk_w, a_experts, log_decay, stream=None):
+    _check(lib().swimba_mix_decay(ctypes.byref(dims), _ptr(topk_idx), _ptr(topk_w),
+                                  _ptr(a_experts), _ptr(log_decay), _stream(stream)))
+
+
+def swimba_ssd_chunk_scan_mixed(dims, B_hat, X_hat, C_mix, log_decay, h_init, y, h_final, ws,
+                                ws_bytes=None, stream=None):
+    nb = (ws.numel() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check(lib().swimba_ssd_chunk_scan_mixed(
+        ctypes.byref(dims), _ptr(B_hat), _ptr(X_hat), _ptr(C_mix), _ptr(log_decay), _ptr(h_init),
+        _ptr(y), _ptr(h_final), _ptr(ws), nb, _stream(stream)))
+
+
+def swimba_decode_step_mixed(dims, u, w_router, w_experts, a_experts, h, y, topk_idx, ws,
+                             ws_bytes=None, stream=None):
+    nb = ws.numel() if ws_bytes is None else ws_bytes
+    _check(lib().swimba_decode_step_mixed(
+        ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(a_experts), _ptr(h),
+        _ptr(y), _ptr(topk_idx), _ptr(ws), nb, _stream(stream)))
+
+
 def swimba_output_project(dims, y, w_out, out, stream=None):
     _check(lib().swimba_output_project(ctypes.byref(dims), _ptr(y), _ptr(w_out), _ptr(out),
                                        _stream(stream)))
@@ -245,4 +273,21 @@ def forward(dims: Dims, u, w_router, w_experts, a, h_init=None, buf: Buffers | N
                               buf.C_mix, buf.ws_project, stream=stream)
     swimba_ssd_chunk_scan(dims, buf.B_hat, buf.X_hat, buf.C_mix, a, h_init, buf.y, buf.h_final,
                           buf.ws_scan, stream=stream)
+    return buf
+
+
+def forward_mixed(dims: Dims, u, w_router, w_experts, a_experts, h_init=None,
+                  buf: Buffers | None = None, log_decay=None, stream=None) -> Buffers:
+    """Route -> project + mix -> mixed decay -> chunked scan with it."""
+    if buf is None:
+        buf = alloc_buffers(dims, u.device)
+    if log_decay is None:
+        log_decay = torch.empty(dims.batch, dims.nheads, dims.seqlen, dtype=torch.float32,
+                                device=u.device)
+    swimba_route_topk(dims, u, w_router, buf.topk_idx, buf.topk_w, buf.logits, stream=stream)
+    swimba_expert_project_mix(dims, u, w_experts, buf.topk_idx, buf.topk_w, buf.B_hat, buf.X_hat,
+                              buf.C_mix, buf.ws_project, stream=stream)
+    swimba_mix_decay(dims, buf.topk_idx, buf.topk_w, a_experts, log_decay, stream=stream)
+    swimba_ssd_chunk_scan_mixed(dims, buf.B_hat, buf.X_hat, buf.C_mix, log_decay, h_init, buf.y,
+                                buf.h_final, buf.ws_scan, stream=stream)
     return buf

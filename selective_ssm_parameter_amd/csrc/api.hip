@@ -307,17 +307,27 @@ swimba_status swimba_expert_project_mix(const swimba_dims* dims, const void* u,
                     "expert_project_mix launch");
 }
 
-swimba_status swimba_ssd_chunk_scan(const swimba_dims* dims, const void* B_hat,
-                                    const void* X_hat, const void* C_mix, const float* a,
-                                    const float* h_init, void* y, float* h_final, void* ws,
-                                    size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The chunked scan with the shared decay a [H] (mixed false) or the
+// expert-mixed decay given as running log2 sums log_decay [Bt, H, T] (a unused).
+swimba_status scan_impl(bool mixed, const swimba_dims* dims, const void* B_hat,
+                        const void* X_hat, const void* C_mix, const float* a, const float* log_decay,
+                        const float* h_init, void* y, float* h_final, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
   Dims d;
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
   if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
   if ((st = check_scan_shape(d)) != SWIMBA_OK) return st;
   if (d.Bt == 0) return SWIMBA_OK;
-  REQUIRE_PTR(a);
+  if (mixed) {
+    if (d.T > 0) REQUIRE_PTR(log_decay);
+  } else {
+    REQUIRE_PTR(a);
+  }
   OPTIONAL_PTR(h_init);
   OPTIONAL_PTR(h_final);
   if (d.M > 0) {
@@ -330,14 +340,63 @@ swimba_status swimba_ssd_chunk_scan(const swimba_dims* dims, const void* B_hat,
   const ScanGeom g = scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
                                (int)d.k, (int)d.L, (int)d.esize);
   return hip_status(launch_scan(d.bf16, g, B_hat, X_hat, C_mix, a, h_init, y, h_final,
-                                static_cast<float*>(ws), stream),
+                                static_cast<float*>(ws), stream, log_decay),
                     "ssd_chunk_scan launch");
 }
 
-swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const void* w_router,
-                                 const void* w_experts, const float* a, float* h, void* y,
-                                 int32_t* topk_idx, void* ws, size_t ws_bytes,
-                                 hipStream_t stream) {
+}  // namespace
+
+extern "C" {
+
+swimba_status swimba_ssd_chunk_scan(const swimba_dims* dims, const void* B_hat,
+                                    const void* X_hat, const void* C_mix, const float* a,
+                                    const float* h_init, void* y, float* h_final, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  return scan_impl(false, dims, B_hat, X_hat, C_mix, a, nullptr, h_init, y, h_final, ws,
+                   ws_bytes, stream);
+}
+
+swimba_status swimba_ssd_chunk_scan_mixed(const swimba_dims* dims, const void* B_hat,
+                                          const void* X_hat, const void* C_mix,
+                                          const float* log_decay, const float* h_init, void* y,
+                                          float* h_final, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+  // with no tokens the scan only copies the state and never reads the decay;
+  // the launcher takes a non-null decay as the mixed mode
+  alignas(16) static const float kNoTokens[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* ld = log_decay;
+  if (!ld && dims && dims->seqlen == 0) ld = kNoTokens;
+  return scan_impl(true, dims, B_hat, X_hat, C_mix, nullptr, ld, h_init, y, h_final, ws,
+                   ws_bytes, stream);
+}
+
+swimba_status swimba_mix_decay(const swimba_dims* dims, const int32_t* topk_idx,
+                               const float* topk_w, const float* a_experts, float* log_decay,
+                               hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if (d.L != 32 && d.L != 64 && d.L != 128 && d.L != 256)
+    return fail(SWIMBA_ERR_UNSUPPORTED, "chunk must be 32, 64, 128 or 256");
+  if (d.M * d.H >= (int64_t(1) << 31)) return fail(SWIMBA_ERR_DIMS, "batch * seqlen * nheads too large");
+  if (d.M == 0) return SWIMBA_OK;
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(a_experts);
+  REQUIRE_PTR(log_decay);
+  return hip_status(launch_mix_decay(topk_idx, topk_w, a_experts, log_decay, (int)d.Bt,
+                                     (int)d.T, (int)d.H, (int)d.E, (int)d.k, (int)d.L, stream),
+                    "mix_decay launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+swimba_status decode_impl(bool mixed, const swimba_dims* dims, const void* u,
+                          const void* w_router, const void* w_experts, const float* a,
+                          const float* a_experts, float* h, void* y, int32_t* topk_idx, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
   Dims d;
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
@@ -347,7 +406,11 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
   REQUIRE_PTR(u);
   REQUIRE_PTR(w_router);
   REQUIRE_PTR(w_experts);
-  REQUIRE_PTR(a);
+  if (mixed) {
+    REQUIRE_PTR(a_experts);
+  } else {
+    REQUIRE_PTR(a);
+  }
   REQUIRE_PTR(h);
   REQUIRE_PTR(y);
   OPTIONAL_PTR(topk_idx);
@@ -373,8 +436,29 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
   if (e != hipSuccess) return hip_status(e, "decode_step projection launch");
   e = launch_decode_state(d.bf16, (int)d.Bt, (int)d.H, (int)d.G, (int)d.N, (int)d.P, (int)d.k,
                           bhat, xhat, reinterpret_cast<const float*>(pws + play.cpart), a, h, y,
-                          stream);
+                          stream, idx, tw, a_experts, (int)d.E);
   return hip_status(e, "decode_step state launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const void* w_router,
+                                 const void* w_experts, const float* a, float* h, void* y,
+                                 int32_t* topk_idx, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  return decode_impl(false, dims, u, w_router, w_experts, a, nullptr, h, y, topk_idx, ws,
+                     ws_bytes, stream);
+}
+
+swimba_status swimba_decode_step_mixed(const swimba_dims* dims, const void* u,
+                                       const void* w_router, const void* w_experts,
+                                       const float* a_experts, float* h, void* y,
+                                       int32_t* topk_idx, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  return decode_impl(true, dims, u, w_router, w_experts, nullptr, a_experts, h, y, topk_idx, ws,
+                     ws_bytes, stream);
 }
 
 swimba_status swimba_output_project(const swimba_dims* dims, const void* y, const void* w_out,

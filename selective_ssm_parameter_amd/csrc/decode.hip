@@ -19,11 +19,16 @@ namespace swimba {
 
 // N (state size) and KM (a bound on k; k itself is a run-time argument) are
 // compile-time so every load is issued up front and the row loop unrolls.
+// With a_experts non-null the decay is the expert-mixed one (papernotes.org
+// notes, Limitations and outlook): a = sum_j w_j a_experts[idx_j, h] / sum_j w_j
+// over the sequence's k slots, in slot order (an index outside [0, E) adds
+// decay 0 with its weight).
 template <typename S, typename TY, int N, int KM>
 __global__ __launch_bounds__(256, 4) void decode_state_kernel(
     const S* __restrict__ B_hat, const S* __restrict__ X_hat, const float* __restrict__ c_part,
     const float* __restrict__ a, float* __restrict__ hstate, TY* __restrict__ y, int H, int G,
-    int k) {
+    int k, const int32_t* __restrict__ idx, const float* __restrict__ tw,
+    const float* __restrict__ a_experts, int E) {
   constexpr int P = 64;
   constexpr int NR = N / 16;                  // state rows per thread
   constexpr int QN = (KM * N + 255) / 256;    // B_hat / c_part staging loads per thread
@@ -89,7 +94,19 @@ __global__ __launch_bounds__(256, 4) void decode_state_kernel(
   }
   __syncthreads();
 
-  const float ah = a[h];
+  float ah;
+  if (a_experts) {
+    float num = 0.f, den = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const float wj = tw[(size_t)b * k + j];
+      const int e = idx[(size_t)b * k + j];
+      num += (e >= 0 && e < E) ? wj * a_experts[(size_t)e * H + h] : 0.f;
+      den += wj;
+    }
+    ah = num / den;
+  } else {
+    ah = a[h];
+  }
   floatx4 xj[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j)
@@ -117,46 +134,57 @@ __global__ __launch_bounds__(256, 4) void decode_state_kernel(
   }
 }
 
+struct DecayMix {
+  const int32_t* idx;
+  const float* w;
+  const float* a_experts;
+  int E;
+};
+
 template <int N, int KM>
 static void launch_decode_state_t(bool is_bf16, dim3 grid, const void* B_hat, const void* X_hat,
                                   const float* c_part, const float* a, float* h, void* y, int H,
-                                  int G, int k, hipStream_t s) {
+                                  int G, int k, hipStream_t s, DecayMix m) {
   if (is_bf16)
     hipLaunchKernelGGL((decode_state_kernel<f16, bf16, N, KM>), grid, dim3(256), 0, s,
-                       (const f16*)B_hat, (const f16*)X_hat, c_part, a, h, (bf16*)y, H, G, k);
+                       (const f16*)B_hat, (const f16*)X_hat, c_part, a, h, (bf16*)y, H, G, k,
+                       m.idx, m.w, m.a_experts, m.E);
   else
     hipLaunchKernelGGL((decode_state_kernel<float, float, N, KM>), grid, dim3(256), 0, s,
                        (const float*)B_hat, (const float*)X_hat, c_part, a, h, (float*)y, H, G,
-                       k);
+                       k, m.idx, m.w, m.a_experts, m.E);
 }
 
 template <int N>
 static void launch_decode_state_n(bool is_bf16, dim3 grid, const void* B_hat, const void* X_hat,
                                   const float* c_part, const float* a, float* h, void* y, int H,
-                                  int G, int k, hipStream_t s) {
+                                  int G, int k, hipStream_t s, DecayMix m) {
   if (k <= 1)
-    launch_decode_state_t<N, 1>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s);
+    launch_decode_state_t<N, 1>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s, m);
   else if (k <= 2)
-    launch_decode_state_t<N, 2>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s);
+    launch_decode_state_t<N, 2>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s, m);
   else if (k <= 4)
-    launch_decode_state_t<N, 4>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s);
+    launch_decode_state_t<N, 4>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s, m);
   else
-    launch_decode_state_t<N, 8>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s);
+    launch_decode_state_t<N, 8>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s, m);
 }
 
 hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
                                const void* B_hat, const void* X_hat, const float* c_part,
-                               const float* a, float* h, void* y, hipStream_t s) {
+                               const float* a, float* h, void* y, hipStream_t s,
+                               const int32_t* idx, const float* w, const float* a_experts,
+                               int E) {
+  const DecayMix m{idx, w, a_experts, E};
   if (Bt == 0) return hipSuccess;
   if (P != 64 || k < 1 || k > 8 || (N != 16 && N != 32 && N != 64 && N != 128))
     return hipErrorInvalidValue;
   prof_begin("decode_state", s);
   const dim3 grid(H, Bt);
   switch (N) {
-    case 16: launch_decode_state_n<16>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s); break;
-    case 32: launch_decode_state_n<32>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s); break;
-    case 64: launch_decode_state_n<64>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s); break;
-    default: launch_decode_state_n<128>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s); break;
+    case 16: launch_decode_state_n<16>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s, m); break;
+    case 32: launch_decode_state_n<32>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s, m); break;
+    case 64: launch_decode_state_n<64>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s, m); break;
+    default: launch_decode_state_n<128>(is_bf16, grid, B_hat, X_hat, c_part, a, h, y, H, G, k, s, m); break;
   }
   prof_end(s);
   return hipGetLastError();

@@ -61,9 +61,18 @@ struct ScanGeom {
 };
 ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es);
 size_t scan_ws_bytes(const ScanGeom& g);
+// ld: the expert-mixed decay's running log2 decay [Bt, H, T] (then a is not
+// read), or nullptr for the shared decay a [H].
 hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
                        const void* C_mix, const float* a, const float* h_init, void* y,
-                       float* h_final, float* ws, hipStream_t s);
+                       float* h_final, float* ws, hipStream_t s, const float* ld = nullptr);
+
+// Expert-mixed decay: running log2 of the per-token decay within each chunk
+// of L tokens, ld [Bt, H, T], from the routing (idx, w [Bt*T, k]) and the
+// per-expert decays a_experts [E, H].
+hipError_t launch_mix_decay(const int32_t* idx, const float* w, const float* a_experts,
+                            float* ld, int Bt, int T, int H, int E, int k, int L,
+                            hipStream_t s);
 hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t s);
 
 // Decode: in-place state update and readout for one token per sequence.
@@ -72,8 +81,12 @@ hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t
 hipError_t launch_output_project(bool is_bf16, int M, int K, int N, const void* y,
                                  const void* w_out, void* out, hipStream_t s);
 
+// a_experts non-null: the expert-mixed decay, a_t = sum_j w_j a_experts[idx_j]
+// / sum_j w_j from the routing (idx, w [Bt, k]); a is then not read.
 hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
                                const void* B_hat, const void* X_hat, const float* c_part,
-                               const float* a, float* h, void* y, hipStream_t s);
+                               const float* a, float* h, void* y, hipStream_t s,
+                               const int32_t* idx = nullptr, const float* w = nullptr,
+                               const float* a_experts = nullptr, int E = 0);
 
 }  // namespace swimba

@@ -56,6 +56,8 @@ struct ScanArgs {
   float* h_final;
   float* ws;          // [Bt, segs, H, N, P] fp32 segment states
   const void* gram;   // [Bt, nc, G, npairs, BT, k*BT] Gram tiles (stream type)
+  const float* ld;    // expert-mixed decay: [Bt, H, T] running log2 decay within each
+                      // chunk (inclusive); nullptr for the shared decay a
   int T, H, G, N, k, L, segs, seg_chunks, nc, npairs, Bt;
 };
 
@@ -65,22 +67,29 @@ struct ScanArgs {
 //   B   [R][NP]   pair rows of B_hat                   (last block row: carry)
 //   C   [BT][NP]  token rows of C~                     (sigma = 0: readout)
 //   G   [BT][R]   the Gram tile of the block pair      (every step)
+//   Lam [L]       the chunk's running log2 decay        (every step; expert-mixed decay)
 // Rows are sequences of 16-byte chunks; chunk c of row r sits at c ^ swz(r).
-template <typename T, int NP, int KS, int BT, bool WITH_Y>
+template <typename T, int NP, int KS, int BT, bool WITH_Y, bool TV = false>
 struct ScanLds {
   static constexpr int R = KS * BT;
   static constexpr int XROW = kP * (int)sizeof(T), BROW = NP * (int)sizeof(T);
   static constexpr int GROW = R * (int)sizeof(T);
   static constexpr int XB = R * XROW, BB = R * BROW;
   static constexpr int CB = WITH_Y ? BT * BROW : 0, GB = WITH_Y ? BT * GROW : 0;
-  static constexpr int XO = 0, BO = XB, CO = XB + BB, GO = XB + BB + CB;
-  static constexpr int STAGE = XB + BB + CB + GB;
+  static constexpr int LB = TV ? 256 * 4 : 0;  // the chunk's running log2 decay (TV)
+  static constexpr int XO = 0, BO = XB, CO = XB + BB, GO = XB + BB + CB, LO = GO + GB;
+  static constexpr int STAGE = XB + BB + CB + GB + LB;
   static constexpr size_t bytes = 2 * (size_t)STAGE;
 };
 
 // a^d for integer d >= 0 from la = log2(a) (la = -1e30 encodes a = 0).
 __device__ __forceinline__ float apow(float la, int d) {
   return d == 0 ? 1.f : exp2f((float)d * la);
+}
+// The same with the bare hardware exp2 (no denormal range reduction: results
+// below 2^-126 may come out as zero), for the per-step factors of the walk.
+__device__ __forceinline__ float apow_step(float la, int d) {
+  return d == 0 ? 1.f : __builtin_amdgcn_exp2f((float)d * la);
 }
 
 // Fragments (t-tile tt, pair k-step q) of a diagonal block pair: a fragment is
@@ -162,9 +171,17 @@ __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_
   }
 }
 
-template <typename T, typename TY, int NP, int KS, int BT, bool WITH_Y>
+// TV: the expert-mixed decay. Every decay factor of a step is 2 to a
+// difference of the chunk's running log2 decay Lam (inclusive sums from the
+// chunk's first token), split as in the shared-decay walk into a row factor,
+// a block scalar and a column factor so that each stays <= 1:
+//   token t of block tau, pair row s of block sig < tau:
+//     prod_{u=s+1}^{t} a_u = 2^{Lam_t - Lam_send} * 2^{Lam_send - Lam_s}
+//   (send = last token of block sig), readout 2^{Lam_t}, carry to the chunk
+//   end 2^{Lam_end - Lam_send} * 2^{Lam_send - Lam_s}, H <- 2^{Lam_end} H.
+template <typename T, typename TY, int NP, int KS, int BT, bool WITH_Y, bool TV = false>
 __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_kernel(ScanArgs A) {
-  typedef ScanLds<T, NP, KS, BT, WITH_Y> Lay;
+  typedef ScanLds<T, NP, KS, BT, WITH_Y, TV> Lay;
   constexpr int R = Lay::R;
   constexpr int TT = BT / 16, RQ = R / 32, NT = NP / 16, NQ = NP / 32;
   constexpr int XC = Lay::XROW / 16, BC = Lay::BROW / 16, GC = Lay::GROW / 16;  // chunks per row
@@ -197,7 +214,7 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
   const size_t HPsz = (size_t)H * kP;
   const int prow_x = 16 * w + c;  // this lane's head column p
 
-  const float ah = A.a[h];
+  const float ah = TV ? 1.f : A.a[h];  // TV: the decay comes per token from A.ld
   const float la = ah > 0.f ? log2f(ah) : -1e30f;
 
   const BufRes rB = make_rsrc(reinterpret_cast<const T*>(A.B_hat) + (size_t)b * Tlen * KS * GN,
@@ -206,6 +223,8 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
                               (uint64_t)Tlen * KS * HPsz * ES);
   const BufRes rC = make_rsrc(reinterpret_cast<const T*>(A.C_mix) + (size_t)b * Tlen * GN,
                               (uint64_t)Tlen * GN * ES);
+  const BufRes rL = make_rsrc(TV ? A.ld + ((size_t)b * H + h) * Tlen : A.a,
+                              TV ? (uint64_t)Tlen * 4 : 0);
   const size_t gtile = (size_t)BT * R;
   const BufRes rG = make_rsrc(
       reinterpret_cast<const T*>(A.gram) + (size_t)b * A.nc * G * A.npairs * gtile,
@@ -327,6 +346,17 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
       const uint32_t gbase = (uint32_t)((((size_t)s.ch * G + grp) * A.npairs + pidx) * gtile);
       dma_tile_full<BT, GC>(rG, gbase * ES, goff, st + Lay::GO, w);
     }
+    if constexpr (TV) {
+      // every slot of the chunk's Lam is written (zeros past its last token),
+      // so no value of another chunk is left in the stage
+      if (64 * w < L) {
+        const int tl = 64 * w + lane;
+        const uint32_t off = tl < Lc ? (uint32_t)(c0 + tl) * 4u : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rL, (__attribute__((address_space(3))) void*)(st + Lay::LO + 256 * w), 4, off, 0, 0,
+            0);
+      }
+    }
   };
 
   float hin = 1.f, hscale = 1.f;
@@ -373,10 +403,32 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
 #pragma unroll
     for (int q = 0; q < RQ; ++q) xq[q] = load_kmajor<T, XC>(Xs, 32 * q, 16 * w, lane);
 
+    // TV: the step's decay factors from the chunk's running log2 decay (zero
+    // past the chunk's last token). ev[q] = 2^{Lam_send - Lam_s} for the pair
+    // rows of block sig; lt[tt] = Lam at the lane's output tokens of block tau.
+    F ev[TV ? RQ : 1];
+    float lt[TV ? TT : 1], l_send = 0.f, l_end = 0.f;
+    if constexpr (TV) {
+      const float* Ls = reinterpret_cast<const float*>(st + Lay::LO);
+      const int sig0 = cur.sig * BT, tau0 = cur.tau * BT;
+      l_send = Ls[min(sig0 + BT, Lc) - 1];
+      l_end = Ls[Lc - 1];
+#pragma unroll
+      for (int q = 0; q < RQ; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          ev[q][j] = from_f32<T>(__builtin_amdgcn_exp2f(l_send - Ls[sig0 + (32 * q + 8 * g4 + j) / KS]));
+      if (WITH_Y) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) lt[tt] = Ls[tau0 + 16 * tt + c];
+      }
+    }
+
     if (WITH_Y) {
       if (cur.sig == 0) {
         // ---- readout of the entering state: y^T[p, t] = H^T[p, n] C~^T[n, t]
-        const float ablk = (cur.tau == 0 ? 1.f : apow(la, cur.tau * BT)) * hscale * ah;
+        const float ablk =
+            TV ? hscale : (cur.tau == 0 ? 1.f : apow_step(la, cur.tau * BT)) * hscale * ah;
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) accY[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
         const bool scaled = hin != 1.f;
@@ -414,7 +466,8 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
           for (int tt = 0; tt < TT; ++tt) accY[tt] = mma16(hf, cf[tt], accY[tt]);
         }
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] * (at[tt] * ablk);
+        for (int tt = 0; tt < TT; ++tt)
+          accY[tt] = accY[tt] * ((TV ? __builtin_amdgcn_exp2f(lt[tt]) : at[tt]) * ablk);
       }
       // ---- intra-chunk: y^T[p, t] += X^T[p, r] (G o decay)[t, r]
       auto gfrag = [&](int tt, int q) {
@@ -426,6 +479,27 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
       // Gram fragments: all of a q-step's token tiles read before their
       // matrix-core ops
       if (dg) {
+        if constexpr (TV) {
+          // a^{t-s} for s <= t as 2^{Lam_t - Lam_s} (zero above the diagonal
+          // and for tokens past the chunk)
+          const float* Ls = reinterpret_cast<const float*>(st + Lay::LO);
+          const int tau0 = cur.tau * BT;
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int q = 0; q < RQ; ++q) {
+              const int ix = DF::index(tt, q);
+              if (ix >= 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                  const int t = 16 * tt + c, sj = (32 * q + 8 * g4 + j) / KS;
+                  dm[ix][j] = from_f32<T>((sj <= t && tau0 + t < Lc)
+                                              ? __builtin_amdgcn_exp2f(lt[tt] - Ls[tau0 + sj])
+                                              : 0.f);
+                }
+              }
+            }
+        }
 #pragma unroll
         for (int q = 0; q < RQ; ++q) {
           F gf[TT];
@@ -449,36 +523,37 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) gf[tt] = gfrag(tt, q);
           __builtin_amdgcn_sched_barrier(0);
-          const F xs = xq[q] * er[q];
+          const F xs = xq[q] * (TV ? ev[q] : er[q]);
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) tmp[tt] = mma16(xs, gf[tt], tmp[tt]);
         }
-        const float u = apow(la, (cur.tau - cur.sig) * BT - (BT - 1));
+        const float u = TV ? 0.f : apow_step(la, (cur.tau - cur.sig) * BT - (BT - 1));
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] + tmp[tt] * (u * at[tt]);
+        for (int tt = 0; tt < TT; ++tt)
+          accY[tt] = accY[tt] + tmp[tt] * (TV ? __builtin_amdgcn_exp2f(lt[tt] - l_send) : u * at[tt]);
       }
     }
     if (last) {
       // The carry accumulates straight into the state: H <- a^{Lc} H first
       // (after the readouts of this chunk, which all use the entering state).
       if (cur.sig == 0) {
-        const float aL = apow(la, Lc);
+        const float aL = TV ? __builtin_amdgcn_exp2f(l_end) : apow_step(la, Lc);
 #pragma unroll
         for (int a = 0; a < NT; ++a) Hr[a] = Hr[a] * aL;
       }
       // ---- carry: H[n, p] += sum_r B_hat[r, n] (a^{Lc-1-s} X[r, p])
-      const bool full = Lc == L;
-      const float blk = apow(la, (nb - 1 - cur.sig) * BT);
+      const bool full = TV || Lc == L;  // TV: ev is already relative to the valid rows
+      const float blk = TV ? __builtin_amdgcn_exp2f(l_end - l_send) : apow_step(la, (nb - 1 - cur.sig) * BT);
 #pragma unroll
       for (int q = 0; q < RQ; ++q) {
         F xd;
         if (full) {
-          xd = xq[q] * (er[q] * from_f32<T>(blk));
+          xd = xq[q] * ((TV ? ev[q] : er[q]) * from_f32<T>(blk));
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int d = Lc - 1 - (cur.sig * BT + (32 * q + 8 * g4 + j) / KS);
-            xd[j] = from_f32<T>(to_f32(xq[q][j]) * (d >= 0 ? apow(la, d) : 0.f));
+            xd[j] = from_f32<T>(to_f32(xq[q][j]) * (d >= 0 ? apow_step(la, d) : 0.f));
           }
         }
         // B_hat fragments four at a time: their LDS reads are all in flight
@@ -563,15 +638,20 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_ker
 // Pass 2: Hin_0 = h_init (or 0), Hin_{s+1} = a^{len_s} Hin_s + S_s, for every
 // (sequence, head, element), walking the segments in order. Slot s of the
 // workspace holds S_{s-1} on entry (s >= 1) and Hin_s on exit.
+// With the expert-mixed decay (ld non-null) a segment's decay is the product
+// over its chunks of 2^{Lam at the chunk's last token}, the exponents summed in
+// chunk order.
 __global__ __launch_bounds__(256) void scan_combine_kernel(const float* __restrict__ a,
                                                            const float* __restrict__ h_init,
                                                            float* __restrict__ ws, int H,
                                                            int NPsz, int T, int L, int segs,
-                                                           int seg_chunks) {
+                                                           int seg_chunks,
+                                                           const float* __restrict__ ld) {
   const int h = blockIdx.y, b = blockIdx.z;
   const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (e4 >= NPsz) return;
-  const float ah = a[h];
+  const float ah = ld ? 1.f : a[h];
+  const float* lrow = ld ? ld + ((size_t)b * H + h) * T : nullptr;
   floatx4 Hc = {0.f, 0.f, 0.f, 0.f};
   if (h_init) Hc = *reinterpret_cast<const floatx4*>(h_init + ((size_t)b * H + h) * NPsz + e4);
   float* base = ws + (size_t)b * segs * H * NPsz + (size_t)h * NPsz + e4;
@@ -581,7 +661,15 @@ __global__ __launch_bounds__(256) void scan_combine_kernel(const float* __restri
     const int t0 = s * seg_chunks * L;
     const int len = min(T, t0 + seg_chunks * L) - t0;
     floatx4* slot = reinterpret_cast<floatx4*>(base + (size_t)(s + 1) * sstride);
-    Hc = Hc * pow_int(ah, len) + *slot;
+    float dec;
+    if (lrow) {
+      float e = 0.f;
+      for (int c0 = t0; c0 < t0 + len; c0 += L) e += lrow[min(T, c0 + L) - 1];
+      dec = exp2f(e);
+    } else {
+      dec = pow_int(ah, len);
+    }
+    Hc = Hc * dec + *slot;
     *slot = Hc;
   }
 }
@@ -658,10 +746,10 @@ size_t scan_ws_bytes(const ScanGeom& g) {
   return scan_state_bytes(g) + scan_gram_bytes(g);
 }
 
-template <typename T, typename TY, int NP, int KS, int BT>
+template <typename T, typename TY, int NP, int KS, int BT, bool TV>
 static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s) {
-  auto k3 = scan_kernel<T, TY, NP, KS, BT, true>;
-  auto k1 = scan_kernel<T, TY, NP, KS, BT, false>;
+  auto k3 = scan_kernel<T, TY, NP, KS, BT, true, TV>;
+  auto k1 = scan_kernel<T, TY, NP, KS, BT, false, TV>;
   const size_t l3 = 0, l1 = 0;  // static LDS (two stage arrays)
   prof_begin("scan_gram", s);
   const int ng = args.npairs * g.G * args.nc * g.Bt;
@@ -678,7 +766,8 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
     const int NPsz = g.N * g.P;
     prof_begin("scan_state_pass", s);
     hipLaunchKernelGGL(scan_combine_kernel, dim3((NPsz / 4 + 255) / 256, g.H, g.Bt), dim3(256), 0,
-                       s, args.a, args.h_init, args.ws, g.H, NPsz, g.T, g.L, g.segs, g.seg_chunks);
+                       s, args.a, args.h_init, args.ws, g.H, NPsz, g.T, g.L, g.segs, g.seg_chunks,
+                       args.ld);
     prof_end(s);
   }
   prof_begin("scan_chunk_output", s);
@@ -690,8 +779,8 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
 
 template <typename T, typename TY, int NP, int KS>
 static hipError_t dispatch_bt(const ScanGeom& g, const ScanArgs& a, hipStream_t s) {
-  (void)g;
-  return launch_scan_t<T, TY, NP, KS, 32>(g, a, s);
+  if (a.ld) return launch_scan_t<T, TY, NP, KS, 32, true>(g, a, s);
+  return launch_scan_t<T, TY, NP, KS, 32, false>(g, a, s);
 }
 
 template <typename T, typename TY, int NP>
@@ -710,7 +799,7 @@ static hipError_t dispatch_np(const ScanGeom& g, const ScanArgs& a, hipStream_t 
 
 hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
                        const void* C_mix, const float* a, const float* h_init, void* y,
-                       float* h_final, float* ws, hipStream_t s) {
+                       float* h_final, float* ws, hipStream_t s, const float* ld) {
   if (g.Bt == 0) return hipSuccess;
   if (g.T == 0) {
     if (h_final) return launch_state_copy(h_init, h_final, (size_t)g.Bt * g.H * g.N * g.P, s);
@@ -718,7 +807,7 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
   }
   const int nc = (g.T + g.L - 1) / g.L;
   unsigned char* gram = reinterpret_cast<unsigned char*>(ws) + scan_state_bytes(g);
-  ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws, gram,
+  ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws, gram, ld,
                 g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks, nc, scan_npairs(g.L, g.bt),
                 g.Bt};
   if (is_bf16) return dispatch_np<f16, bf16>(g, args, s);

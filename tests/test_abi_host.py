@@ -41,7 +41,7 @@ def lib():
 def test_exports_every_declared_symbol():
     L = lib()
     syms = declared_symbols()
-    assert len(syms) == 11, syms
+    assert len(syms) == 14, syms
     for s in syms:
         assert hasattr(L, s), f"{s} declared in swimba.h but not exported"
     assert set(syms) == set(sb.EXPORTS)
@@ -141,6 +141,41 @@ def test_output_project_argument_checks():
     bad = good_dims(d_model=100)
     assert L.swimba_output_project(ctypes.byref(bad), FAKE, FAKE, FAKE, None) == -3
     assert L.swimba_output_project(ctypes.byref(good_dims(seqlen=0)), None, None, None, None) == 0
+
+
+def test_mixed_decay_argument_checks():
+    L = lib()
+    d = good_dims()
+    # mix_decay: pointers, chunk size, empty input
+    assert L.swimba_mix_decay(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == -1
+    assert "a_experts is NULL" in L.swimba_last_error().decode()
+    assert L.swimba_mix_decay(ctypes.byref(d), FAKE, FAKE, FAKE, MISALIGNED, None) == -5
+    assert L.swimba_mix_decay(ctypes.byref(good_dims(chunk=48)), FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert L.swimba_mix_decay(ctypes.byref(good_dims(seqlen=0)), None, None, None, None, None) == 0
+    # the mixed scan: a NULL decay is refused while there are tokens, the
+    # shared-decay checks apply as for swimba_ssd_chunk_scan
+    st = L.swimba_ssd_chunk_scan_mixed(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None,
+                                       None, 0, None)
+    assert st == -1 and "log_decay is NULL" in L.swimba_last_error().decode()
+    st = L.swimba_ssd_chunk_scan_mixed(ctypes.byref(good_dims(top_k=3)), FAKE, FAKE, FAKE, FAKE,
+                                       None, FAKE, None, None, 0, None)
+    assert st == -3
+    need = sb.swimba_workspace_size(d, sb.CALL_SCAN)
+    st = L.swimba_ssd_chunk_scan_mixed(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                       FAKE, need - 1, None)
+    assert st == -4 or need == 0
+    assert L.swimba_ssd_chunk_scan_mixed(ctypes.byref(good_dims(batch=0)), None, None, None, None,
+                                         None, None, None, None, 0, None) == 0
+    # the mixed decode step: a_experts is required, a is not read
+    dd = good_dims(seqlen=1)
+    st = L.swimba_decode_step_mixed(ctypes.byref(dd), FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                                    FAKE, 1 << 30, None)
+    assert st == -1 and "a_experts is NULL" in L.swimba_last_error().decode()
+    st = L.swimba_decode_step_mixed(ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                    None, 0, None)
+    assert st == -4
+    assert L.swimba_decode_step_mixed(ctypes.byref(good_dims(batch=0, seqlen=1)), None, None, None,
+                                      None, None, None, None, None, 0, None) == 0
 
 
 def test_empty_inputs_are_no_ops():

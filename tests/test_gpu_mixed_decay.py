@@ -1,0 +1,276 @@
+"""GPU parity of the expert-mixed diagonal transition against the fp64 oracle.
+
+The HIP path (swimba_mix_decay, swimba_ssd_chunk_scan_mixed,
+swimba_decode_step_mixed, through the C ABI) against oracle/mixed_decay.py on
+the same seeded inputs; every expected value comes from the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (TOL, check_routing, dev, host, round_stream, say, sdt, slice_err, tdt,
+                      upload, valid_prefix)
+from oracle import mixed_decay as md
+from oracle import swimba as osw
+from selective_ssm_parameter_amd import binding as sb
+from selective_ssm_parameter_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def W(name, seed, **kw):
+    base = dict(batch=2, seqlen=300, d_model=128, nheads=3, headdim=64, dstate=128, ngroups=1,
+                n_experts=4, top_k=2, chunk=64, dtype=synth.BF16, a_lo=0.9, a_hi=0.999)
+    base.update(kw)
+    return synth.small(name, seed, **base)
+
+
+def with_h0(wl, inp, scale=0.3):
+    rng = np.random.default_rng(wl.seed + 17)
+    inp = dict(inp)
+    inp["h_init"] = (rng.standard_normal((wl.batch, wl.nheads, wl.dstate, 64)) * scale).astype(np.float32)
+    return inp
+
+
+def oracle_routing_streams(wl, inp):
+    uf = inp["u"].reshape(wl.tokens, -1)
+    r = osw.route(uf, inp["w_router"], wl.top_k)
+    s = osw.expert_streams(uf, inp["w_experts"], r.idx, wl.nheads, wl.headdim, wl.ngroups,
+                           wl.dstate)
+    B_hat, X, C_mix = osw.mix_streams(s, r.w)
+    return r, B_hat, X, C_mix
+
+
+def log_decay_of(a_t, wl):
+    """The documented encoding of swimba_mix_decay: per chunk, the running sum
+    of max(log2 a, -126), laid out [Bt, H, T] (written here from its
+    definition, on the oracle's decays)."""
+    lg = np.maximum(np.log2(np.maximum(np.asarray(a_t, np.float64), 1e-300)), -126.0)
+    lg = lg.reshape(wl.batch, wl.seqlen, wl.nheads)
+    out = np.empty((wl.batch, wl.nheads, wl.seqlen))
+    for c0 in range(0, wl.seqlen, wl.chunk):
+        out[:, :, c0:c0 + wl.chunk] = np.cumsum(lg[:, c0:c0 + wl.chunk], axis=1).transpose(0, 2, 1)
+    return out
+
+
+# ---------------------------------------------------------------- mix_decay kernel
+
+MIX_CASES = [
+    ("bf16_L64_ragged", W("m1", 701, seqlen=300), None),
+    ("L32_k1", W("m2", 702, seqlen=100, chunk=32, top_k=1), None),
+    ("L128", W("m3", 703, seqlen=333, chunk=128, nheads=5), None),
+    ("L256_e8k4", W("m4", 704, seqlen=600, chunk=256, n_experts=8, top_k=4, batch=1), None),
+    ("zero_decay_expert", W("m5", 705, seqlen=200, n_experts=4, top_k=1), 0),
+]
+
+
+@pytest.mark.parametrize("name,wl,zero", MIX_CASES, ids=[c[0] for c in MIX_CASES])
+def test_mix_decay(name, wl, zero):
+    say(f"[mix_decay] {name} T={wl.seqlen} L={wl.chunk} E={wl.n_experts} k={wl.top_k}")
+    inp = synth.make_inputs(wl)
+    ae = synth.expert_decays(wl)
+    if zero is not None:
+        ae[zero] = 0.0                       # one expert that forgets everything
+    r, _, _, _ = oracle_routing_streams(wl, inp)
+    a_t = md.mix_decay(r.idx, r.w, ae)
+    ref = md.chunk_decay_products(a_t, wl.batch, wl.seqlen, wl.chunk)     # [Bt, H, T]
+    dims = sb.dims_of(wl)
+    ld = torch.full((wl.batch, wl.nheads, wl.seqlen), float("nan"), device="cuda")
+    sb.swimba_mix_decay(dims, dev(r.idx.astype(np.int32), torch.int32),
+                        dev(r.w.astype(np.float32), torch.float32), dev(ae, torch.float32), ld)
+    torch.cuda.synchronize()
+    got = np.exp2(host(ld))
+    # fp32 mixing and log2 sums: relative error of a running product of up to
+    # 256 factors, each within a few fp32 ulps; a zero decay gives 2^-126 steps
+    err = np.abs(got - ref) / np.maximum(ref, 1e-30)
+    say(f"  max rel err {err.max():.2e}")
+    assert np.all(np.isfinite(host(ld)))
+    assert err.max() < 1e-4
+    if zero is not None:
+        assert np.all(got[ref == 0] < 1e-37)
+
+
+# ---------------------------------------------------------------- mixed scan
+
+SCAN_CASES = [
+    ("c1_f32", synth.WORKLOADS["c1"], False),
+    ("bf16_L64_ragged_h0", W("x1", 711, seqlen=300), True),
+    ("bf16_L32", W("x2", 712, chunk=32, seqlen=200), True),
+    ("bf16_L128", W("x3", 713, chunk=128, seqlen=333), True),
+    ("bf16_L256", W("x4", 714, chunk=256, seqlen=600, batch=1), True),
+    ("bf16_k1_n64", W("x5", 715, top_k=1, dstate=64, seqlen=257), True),
+    ("bf16_n16_g2", W("x6", 716, dstate=16, nheads=4, ngroups=2, seqlen=130), True),
+    ("bf16_T1", W("x7", 717, seqlen=1), True),
+    ("f32_k2_n128", W("x8", 718, dtype=synth.F32, seqlen=190), True),
+    ("bf16_many_segments", W("x9", 719, batch=1, nheads=2, seqlen=4000, chunk=64), True),
+    ("bf16_wide_decays", W("x10", 720, seqlen=260, a_lo=0.3, a_hi=0.999), True),
+]
+
+
+def run_scan_mixed(wl, inp, B_hat, X, C_mix, ld_host):
+    dims = sb.dims_of(wl)
+    dt = tdt(wl)
+    st = sdt(wl)
+    y = torch.empty(wl.tokens, wl.nheads, 64, dtype=dt, device="cuda")
+    hf = torch.empty(wl.batch, wl.nheads, wl.dstate, 64, dtype=torch.float32, device="cuda")
+    ws, _ = sb.workspace(dims, sb.CALL_SCAN)
+    h_init = None if inp["h_init"] is None else dev(inp["h_init"], torch.float32)
+    sb.swimba_ssd_chunk_scan_mixed(dims, dev(B_hat, st), dev(X, st), dev(C_mix, st),
+                                   dev(ld_host, torch.float32), h_init, y, hf, ws)
+    torch.cuda.synchronize()
+    return host(y).reshape(wl.batch, wl.seqlen, wl.nheads, 64), host(hf)
+
+
+@pytest.mark.parametrize("name,wl,h0", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_ssd_chunk_scan_mixed(name, wl, h0):
+    say(f"[scan_mixed] {name} T={wl.seqlen} L={wl.chunk} N={wl.dstate} k={wl.top_k} {wl.dtype}")
+    inp = synth.make_inputs(wl)
+    if h0:
+        inp = with_h0(wl, inp)
+    ae = synth.expert_decays(wl)
+    r, B_hat, X, C_mix = oracle_routing_streams(wl, inp)
+    B_hat, X, C_mix = round_stream(B_hat, wl), round_stream(X, wl), round_stream(C_mix, wl)
+    a_t = md.mix_decay(r.idx, r.w, ae)
+    y_ref, h_ref = md.recurrence_tv(B_hat, X, C_mix, a_t, inp["h_init"], wl.batch, wl.seqlen)
+    y, hf = run_scan_mixed(wl, inp, B_hat, X, C_mix, log_decay_of(a_t, wl))
+    ey = slice_err(y, y_ref)
+    eh = slice_err(hf, h_ref, axes_slice=(0, 1))
+    say(f"  y err {ey:.3e}  h_final err {eh:.3e}")
+    assert ey < TOL[wl.dtype]
+    assert eh < TOL[wl.dtype]
+
+
+def test_equal_expert_decays_match_shared_scan():
+    # a^(e) = a for all e: the mixed scan solves the shared-decay recurrence;
+    # both the oracle and the shared-decay kernel agree with it.
+    wl = W("x11", 721, seqlen=450, batch=2)
+    inp = with_h0(wl, synth.make_inputs(wl))
+    r, B_hat, X, C_mix = oracle_routing_streams(wl, inp)
+    B_hat, X, C_mix = round_stream(B_hat, wl), round_stream(X, wl), round_stream(C_mix, wl)
+    ae = np.tile(inp["a"][None, :], (wl.n_experts, 1))
+    a_t = md.mix_decay(r.idx, r.w, ae)
+    y, hf = run_scan_mixed(wl, inp, B_hat, X, C_mix, log_decay_of(a_t, wl))
+    y_ref, h_ref = osw.recurrence(B_hat, X, C_mix, inp["a"].astype(np.float64), inp["h_init"],
+                                  wl.batch, wl.seqlen)
+    assert slice_err(y, y_ref) < TOL[wl.dtype]
+    assert slice_err(hf, h_ref, axes_slice=(0, 1)) < TOL[wl.dtype]
+    dims = sb.dims_of(wl)
+    st = sdt(wl)
+    y2 = torch.empty(wl.tokens, wl.nheads, 64, dtype=tdt(wl), device="cuda")
+    ws, _ = sb.workspace(dims, sb.CALL_SCAN)
+    sb.swimba_ssd_chunk_scan(dims, dev(B_hat, st), dev(X, st), dev(C_mix, st),
+                             dev(inp["a"], torch.float32), dev(inp["h_init"], torch.float32), y2,
+                             None, ws)
+    torch.cuda.synchronize()
+    assert slice_err(host(y2).reshape(y.shape), y) < TOL[wl.dtype]
+
+
+def test_scan_mixed_empty_sequence_copies_state():
+    wl = W("x12", 722, seqlen=0, nheads=2)
+    dims = sb.dims_of(wl)
+    rng = np.random.default_rng(5)
+    h0 = rng.standard_normal((2, 2, 128, 64)).astype(np.float32)
+    hf = torch.full((2, 2, 128, 64), 3.0, device="cuda")
+    sb.swimba_ssd_chunk_scan_mixed(dims, None, None, None, None, dev(h0, torch.float32), None, hf,
+                                   None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(hf), h0.astype(np.float64))
+
+
+# ---------------------------------------------------------------- end to end
+
+E2E_CASES = [
+    ("c1", synth.WORKLOADS["c1"]),
+    ("bf16_small", W("y1", 731, seqlen=520, batch=2)),
+    ("bf16_g2_k1", W("y2", 732, top_k=1, nheads=4, ngroups=2, dstate=64, seqlen=260)),
+]
+
+
+@pytest.mark.parametrize("name,wl", E2E_CASES, ids=[c[0] for c in E2E_CASES])
+def test_forward_mixed_end_to_end(name, wl):
+    say(f"[e2e_mixed] {name}")
+    inp = synth.make_inputs(wl)
+    ae = synth.expert_decays(wl)
+    d = upload(wl, inp)
+    dims = sb.dims_of(wl)
+    buf = sb.forward_mixed(dims, d["u"], d["w_router"], d["w_experts"], dev(ae, torch.float32),
+                           d["h_init"])
+    torch.cuda.synchronize()
+    ref = md.forward_tv(inp["u"], inp["w_router"], inp["w_experts"], ae, inp["h_init"],
+                        nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
+                        dstate=wl.dstate, top_k=wl.top_k)
+    flips = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), ref["routing"], wl)
+    lim = valid_prefix(flips, wl.batch, wl.seqlen)
+    y = host(buf.y).reshape(wl.batch, wl.seqlen, wl.nheads, 64)
+    for b in range(wl.batch):
+        e = slice_err(y[b:b + 1, :lim[b]], ref["y"][b:b + 1, :lim[b]])
+        assert e < TOL[wl.dtype], (b, e)
+        if lim[b] == wl.seqlen:
+            assert slice_err(host(buf.h_final)[b:b + 1], ref["h_final"][b:b + 1], (0, 1)) < TOL[wl.dtype]
+
+
+# ---------------------------------------------------------------- decode
+
+DEC_CASES = [
+    ("bf16_e8k2", W("z1", 741, batch=16, seqlen=1, n_experts=8)),
+    ("bf16_e32k4", W("z2", 742, batch=40, seqlen=1, n_experts=32, top_k=4, d_model=512)),
+    ("f32_g2", W("z3", 743, batch=8, seqlen=1, dtype=synth.F32, nheads=4, ngroups=2, dstate=32)),
+    ("bf16_k1_n16", W("z4", 744, batch=24, seqlen=1, top_k=1, dstate=16, nheads=3)),
+]
+
+
+@pytest.mark.parametrize("name,wl", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_decode_steps_mixed(name, wl):
+    say(f"[decode_mixed] {name}")
+    inp = with_h0(wl, synth.make_inputs(wl), scale=float(np.sqrt(0.1)))
+    ae = synth.expert_decays(wl)
+    d = upload(wl, inp)
+    dims = sb.dims_of(wl)
+    dt = tdt(wl)
+    h = d["h_init"].clone()
+    y = torch.empty(wl.batch, wl.nheads, 64, dtype=dt, device="cuda")
+    idx = torch.empty(wl.batch, wl.top_k, dtype=torch.int32, device="cuda")
+    ws, _ = sb.workspace(dims, sb.CALL_DECODE)
+    aed = dev(ae, torch.float32)
+    h_ref = inp["h_init"].astype(np.float64)
+    for step in range(5):
+        ut = synth.decode_token(wl, step)
+        sb.swimba_decode_step_mixed(dims, dev(ut, dt), d["w_router"], d["w_experts"], aed, h, y,
+                                    idx, ws)
+        torch.cuda.synchronize()
+        ref = md.decode_step_tv(ut, inp["w_router"], inp["w_experts"], ae, h_ref,
+                                nheads=wl.nheads, headdim=64, ngroups=wl.ngroups,
+                                dstate=wl.dstate, top_k=wl.top_k)
+        assert not ref["routing"].flagged.any(), "near-tie in the decode test inputs"
+        assert np.array_equal(host(idx).astype(np.int64), ref["routing"].idx)
+        assert slice_err(host(y)[:, None], ref["y"][:, None]) < TOL[wl.dtype]
+        assert slice_err(host(h), ref["h"], (0, 1)) < TOL[wl.dtype]
+        h_ref = ref["h"]
+
+
+def test_decode_mixed_matches_prefill_mixed():
+    # T mixed decode steps == one mixed prefill of T tokens
+    wl = W("z5", 745, batch=4, seqlen=12, nheads=2)
+    inp = synth.make_inputs(wl)
+    ae = synth.expert_decays(wl)
+    d = upload(wl, inp)
+    aed = dev(ae, torch.float32)
+    pre = sb.forward_mixed(sb.dims_of(wl), d["u"], d["w_router"], d["w_experts"], aed, None)
+    dims = sb.dims_of(wl, seqlen=1)
+    dt = tdt(wl)
+    h = torch.zeros(wl.batch, 2, 128, 64, device="cuda")
+    y = torch.empty(wl.batch, 2, 64, dtype=dt, device="cuda")
+    ws, _ = sb.workspace(dims, sb.CALL_DECODE)
+    u = d["u"].reshape(wl.batch, wl.seqlen, -1)
+    ys = []
+    for t in range(wl.seqlen):
+        sb.swimba_decode_step_mixed(dims, u[:, t].contiguous(), d["w_router"], d["w_experts"],
+                                    aed, h, y, None, ws)
+        ys.append(host(y).copy())
+    torch.cuda.synchronize()
+    yd = np.stack(ys, axis=1)
+    yp = host(pre.y).reshape(wl.batch, wl.seqlen, 2, 64)
+    assert slice_err(yd, yp) < TOL[wl.dtype]
+    assert slice_err(host(h), host(pre.h_final), (0, 1)) < TOL[wl.dtype]
