@@ -45,13 +45,16 @@ KERNEL_NAMES = [
     (r"route_kernel", "route_topk"),
     (r"bucket_count_kernel", "bucket_count"),
     (r"bucket_place_kernel", "bucket_place"),
-    (r"proj_kernel.*Lb1E", "output_project"),
+    # template arguments (type, tile config, PLAIN, ...): PLAIN right after the config
+    (r"proj_kernel.*EEELb1E", "output_project"),
     (r"proj_kernel|proj_skinny_kernel", "expert_project"),
     (r"mix_c_kernel", "mix_c"),
+    (r"mix_decay_kernel", "mix_decay"),
     (r"scan_gram_kernel", "scan_gram"),
-    (r"scan_kernel.*Lb0E", "scan_segment_state"),
+    # (types, NP, KS, BT, WITH_Y, TV): WITH_Y follows the block size
+    (r"scan_kernel.*Li\d+ELb0ELb[01]E", "scan_segment_state"),
     (r"scan_combine_kernel", "scan_state_pass"),
-    (r"scan_kernel.*Lb1E", "scan_chunk_output"),
+    (r"scan_kernel.*Li\d+ELb1ELb[01]E", "scan_chunk_output"),
     (r"state_copy_kernel", "state_copy"),
     (r"decode_state_kernel", "decode_state"),
     (r"copyBuffer", "copy (runtime blit)"),
@@ -62,6 +65,7 @@ KERNEL_SOURCES = {
     "expert_project": ["project.hip"],
     "scan_chunk_output": ["scan.hip"],
     "decode_state": ["decode.hip"],
+    "mix_decay": ["decay.hip"],
 }
 
 
@@ -82,14 +86,21 @@ def source_digest(kernel):
     return h.hexdigest()[:16]
 
 
-def traffic_file(wl_name):
-    return os.path.join(PROFILES, f"swimba_step_{wl_name}_hbm_traffic.md")
+def profile_key(wl_name, decay="shared"):
+    """Name of a workload's profile summaries: the expert-mixed decay runs
+    other kernels (or the same ones with other work) and has its own."""
+    return wl_name + ("_mixed" if decay == "mixed" else "")
 
 
-def stored_traffic(kernel, wl_name):
-    """HBM bytes per launch of ``kernel`` from the committed counter summary,
-    or None when there is none or the kernel's sources changed since."""
-    path = traffic_file(wl_name)
+def traffic_file(key):
+    return os.path.join(PROFILES, f"swimba_step_{key}_hbm_traffic.md")
+
+
+def stored_traffic(kernel, key):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary
+    of profile ``key``, or None when there is none or the kernel's sources
+    changed since."""
+    path = traffic_file(key)
     if kernel not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     for line in open(path):
@@ -108,14 +119,15 @@ def is_decode(wl):
     return wl.decode_steps > 0
 
 
-def kernel_models(wl):
+def kernel_models(wl, mixed=False):
     """Algorithmic work per launch of each kernel, for one prefill of ``wl``
-    (one decode step for the decode workload).
+    (one decode step for the decode workload). ``mixed``: the expert-mixed
+    decay (its mixing kernel, and the scan reading the running log2 decay).
 
     Returns {kernel: (bound, flops, bytes)}. Bytes count each tensor a kernel
     must read or write once; flops count multiply-adds as 2."""
     if is_decode(wl):
-        return decode_models(wl)
+        return decode_models(wl, mixed)
     M, D, E, k = wl.tokens, wl.d_model, wl.n_experts, wl.top_k
     H, P, N, G, L = wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.chunk
     W, HP, GN = wl.width, H * P, G * N
@@ -133,14 +145,18 @@ def kernel_models(wl):
                   + 2 * M * H * N * P                 # readout of the entering state
                   + 2 * pairs * H * N * P)            # chunk carry
     scan_bytes = pairs * (HP + GN) * es + M * GN * es + M * HP * ei
-    return {
+    models = {
         "route_topk": ("hbm", 2 * M * D * E, M * D * ei + E * D * ei + pairs * 8),
         "expert_project": ("mfma", 2 * pairs * D * W, proj_bytes),
-        "scan_chunk_output": ("hbm", scan_flops, scan_bytes),
+        "scan_chunk_output": ("hbm", scan_flops, scan_bytes + (M * H * 4 if mixed else 0)),
     }
+    if mixed:
+        # reads the routing and the expert decays, writes the running log2 decay
+        models["mix_decay"] = ("hbm", 2 * pairs * H, pairs * 8 + E * H * 4 + M * H * 4)
+    return models
 
 
-def decode_models(wl):
+def decode_models(wl, mixed=False):
     """One decode step of every sequence: the state update reads and writes
     each head's fp32 N x P state once; the projection reads the weights of
     every expert some token chose (all E at this batch size)."""
@@ -156,7 +172,8 @@ def decode_models(wl):
         "route_topk": ("hbm", 2 * Bt * D * E, Bt * D * ei + E * D * ei + pairs * 8),
         "expert_project": ("hbm", 2 * pairs * D * W,
                            Bt * D * ei + E * W * D * ei + streams + pairs * 8),
-        "decode_state": ("hbm", 4 * pairs * H * N * P, state + streams + Bt * HP * ei),
+        "decode_state": ("hbm", 4 * pairs * H * N * P,
+                         state + streams + Bt * HP * ei + (E * H * 4 + pairs * 8 if mixed else 0)),
     }
 
 
@@ -176,6 +193,8 @@ def run_gpu(args):
         return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev, t)
 
     wr, we, a = up(inp["w_router"]), up(inp["w_experts"]), up(inp["a"], torch.float32)
+    mixed = getattr(args, "decay", "shared") == "mixed"
+    a_exp = up(synth.expert_decays(wl), torch.float32) if mixed else None
     if not is_decode(wl):
         u = up(inp["u"].reshape(wl.tokens, -1))
         dims = sb.dims_of(wl)
@@ -194,15 +213,27 @@ def run_gpu(args):
         count = [0]
 
         def step():
-            sb.swimba_decode_step(ddims, toks[count[0] % len(toks)], wr, we, a, h_state, y_dec,
-                                  None, dws)
+            if mixed:
+                sb.swimba_decode_step_mixed(ddims, toks[count[0] % len(toks)], wr, we, a_exp,
+                                            h_state, y_dec, None, dws)
+            else:
+                sb.swimba_decode_step(ddims, toks[count[0] % len(toks)], wr, we, a, h_state,
+                                      y_dec, None, dws)
             count[0] += 1
     else:
+        log_decay = (torch.empty(wl.batch, wl.nheads, wl.seqlen, dtype=torch.float32, device=dev)
+                     if mixed else None)
+
         def step():
             # prefill the batch, then decode one more token of every sequence,
             # updating the prefill's final state in place
-            sb.forward(dims, u, wr, we, a, None, buf)
-            sb.swimba_decode_step(ddims, u_dec, wr, we, a, buf.h_final, y_dec, None, dws)
+            if mixed:
+                sb.forward_mixed(dims, u, wr, we, a_exp, None, buf, log_decay)
+                sb.swimba_decode_step_mixed(ddims, u_dec, wr, we, a_exp, buf.h_final, y_dec, None,
+                                            dws)
+            else:
+                sb.forward(dims, u, wr, we, a, None, buf)
+                sb.swimba_decode_step(ddims, u_dec, wr, we, a, buf.h_final, y_dec, None, dws)
 
     for _ in range(args.warmup):
         step()
@@ -217,7 +248,7 @@ def run_gpu(args):
     sb.profile_enable(False)
     if is_decode(wl):  # the library names decode launches decode_<kernel>
         report = {n[len("decode_"):]: r for n, r in report.items() if n.startswith("decode_")}
-    models = kernel_models(wl)
+    models = kernel_models(wl, mixed)
     kernels = {n: {"launches": r["launches"], "avg_us": 1e3 * r["ms"] / r["launches"]}
                for n, r in report.items()}
     dom = max((n for n in models if n in report), key=lambda n: report[n]["ms"])
@@ -265,13 +296,13 @@ def run_gpu(args):
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": stored_traffic(dom, wl.name),
+                "traffic": stored_traffic(dom, profile_key(wl.name, "mixed" if mixed else "shared")),
                 "algorithmic_flops": flops, "avg_us": avg_s * 1e6}
     else:
         achieved = nbytes / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "traffic": stored_traffic(dom, wl.name),
+                "traffic": stored_traffic(dom, profile_key(wl.name, "mixed" if mixed else "shared")),
                 "algorithmic_bytes": nbytes, "avg_us": avg_s * 1e6}
     res = {
         "wl": wl, "value": value, "elapsed": elapsed, "kernels": kernels, "roofline": roof,
@@ -411,13 +442,14 @@ def output_projection(args):
                          "sample": f"first {rows} tokens, {cpu_s:.2f} s"}}), flush=True)
 
 
-def cpu_baseline(wl, budget_s=20.0):
+def cpu_baseline(wl, budget_s=20.0, mixed=False):
     """The fp64 oracle on a bounded sample: the first rows of the batch, all
     heads, whole sequences; rows are added until ``budget_s`` is used."""
+    from oracle import mixed_decay as md
     from oracle import swimba as osw
     from selective_ssm_parameter_amd import synth
     if is_decode(wl):
-        return cpu_baseline_decode(wl, budget_s)
+        return cpu_baseline_decode(wl, budget_s, mixed)
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -427,9 +459,14 @@ def cpu_baseline(wl, budget_s=20.0):
     done_tokens, spent, rows = 0, 0.0, 0
     while rows < wl.batch and spent < budget_s:
         t0 = time.perf_counter()
-        osw.forward(inp["u"][rows:rows + 1], inp["w_router"], inp["w_experts"], inp["a"], None,
-                    nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
-                    dstate=wl.dstate, top_k=wl.top_k)
+        if mixed:
+            md.forward_tv(inp["u"][rows:rows + 1], inp["w_router"], inp["w_experts"],
+                          synth.expert_decays(wl), None, nheads=wl.nheads, headdim=wl.headdim,
+                          ngroups=wl.ngroups, dstate=wl.dstate, top_k=wl.top_k)
+        else:
+            osw.forward(inp["u"][rows:rows + 1], inp["w_router"], inp["w_experts"], inp["a"],
+                        None, nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
+                        dstate=wl.dstate, top_k=wl.top_k)
         spent += time.perf_counter() - t0
         done_tokens += wl.seqlen
         rows += 1
@@ -438,7 +475,7 @@ def cpu_baseline(wl, budget_s=20.0):
                       f"prefill only, {spent:.1f} s"}
 
 
-def cpu_baseline_decode(wl, budget_s):
+def cpu_baseline_decode(wl, budget_s, mixed=False):
     """The fp64 oracle's decode step on growing slices of the batch (all
     heads, the workload's initial state) until ``budget_s`` is used."""
     from oracle import swimba as osw
@@ -448,14 +485,21 @@ def cpu_baseline_decode(wl, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    from oracle import mixed_decay as md
     inp = synth.make_inputs(wl)
+    ae = synth.expert_decays(wl)
     done, spent, step, rows = 0, 0.0, 0, 8
     while spent < budget_s and step < wl.decode_steps:
         u_t = synth.decode_token(wl, step)[:rows]
         t0 = time.perf_counter()
-        osw.decode_step(u_t, inp["w_router"], inp["w_experts"], inp["a"], inp["h_init"][:rows],
-                        nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
-                        dstate=wl.dstate, top_k=wl.top_k)
+        if mixed:
+            md.decode_step_tv(u_t, inp["w_router"], inp["w_experts"], ae, inp["h_init"][:rows],
+                              nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
+                              dstate=wl.dstate, top_k=wl.top_k)
+        else:
+            osw.decode_step(u_t, inp["w_router"], inp["w_experts"], inp["a"],
+                            inp["h_init"][:rows], nheads=wl.nheads, headdim=wl.headdim,
+                            ngroups=wl.ngroups, dstate=wl.dstate, top_k=wl.top_k)
         spent += time.perf_counter() - t0
         done += rows
         step += 1
@@ -489,8 +533,10 @@ def summarize_trace(trace_dir, wl_name, out, command, bench_json=None):
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     total = sum(sum(v) for v in groups.values())
     stats = find_csv(trace_dir, "kernel_stats.csv")
-    kind = "decode steps" if is_decode(workload(wl_name)) else "bench step (prefill + decode)"
-    lines = [f"# Kernel durations, {kind} on workload {wl_name}", "",
+    base, mixed = wl_name.removesuffix("_mixed"), wl_name.endswith("_mixed")
+    kind = "decode steps" if is_decode(workload(base)) else "bench step (prefill + decode)"
+    what = f"workload {base}" + (", expert-mixed decay" if mixed else "")
+    lines = [f"# Kernel durations, {kind} on {what}", "",
              "Command (from the repository root, after building the library):", "",
              "    " + command, "",
              f"Source: `{os.path.basename(stats)}` and the kernel trace of that run; "
@@ -546,9 +592,11 @@ def summarize_pmc(fetch_dir, write_dir, wl_name, out, commands):
         res[counter] = (kib, scale, {k: sum(v) / len(v) for k, v in by.items()})
     fk, fs, fetch = res["FETCH_SIZE"]
     wk, ws_, write = res["WRITE_SIZE"]
-    wl = workload(wl_name)
-    models = kernel_models(wl)
-    lines = [f"# HBM traffic per launch, bench step on workload {wl_name}", "",
+    base, mixed = wl_name.removesuffix("_mixed"), wl_name.endswith("_mixed")
+    wl = workload(base)
+    models = kernel_models(wl, mixed)
+    what = f"workload {base}" + (", expert-mixed decay" if mixed else "")
+    lines = [f"# HBM traffic per launch, bench step on {what}", "",
              "Commands (from the repository root, after building the library):", ""]
     lines += ["    " + c for c in commands]
     lines += ["",
@@ -586,6 +634,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decay", default="shared", choices=["shared", "mixed"],
+                    help="mixed: the expert-mixed diagonal transition (per-expert decays "
+                         "mixed per token) instead of one shared decay per head")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with copies of known size (scales HBM counters)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -601,14 +652,15 @@ def main():
     ap.add_argument("--command", action="append", default=[],
                     help="the command(s) that produced the profile, for the summary")
     args = ap.parse_args()
+    key = profile_key(args.config, args.decay)
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.config,
-                        args.out or os.path.join(PROFILES, f"swimba_step_{args.config}_kernel_trace.md"),
+        summarize_trace(args.summarize_trace, key,
+                        args.out or os.path.join(PROFILES, f"swimba_step_{key}_kernel_trace.md"),
                         " ".join(args.command), args.bench_json)
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config,
-                      args.out or traffic_file(args.config), args.command)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], key,
+                      args.out or traffic_file(key), args.command)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -635,7 +687,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": (f"Swimba recurrent decode step, {wl.dtype}: batch {wl.batch}, "
+            "workload": ((f"Swimba recurrent decode step, {wl.dtype}: batch {wl.batch}, "
                          f"one token per sequence per step, d_model={wl.d_model}, "
                          f"heads={wl.nheads}, P={wl.headdim}, N={wl.dstate} fp32 state per "
                          f"head in HBM, E={wl.n_experts}, top-k={wl.top_k}")
@@ -643,7 +695,9 @@ def main():
                         (f"Swimba mixer prefill + 1 decode step, {wl.dtype}: batch {wl.batch}, "
                          f"T={wl.seqlen}, d_model={wl.d_model}, heads={wl.nheads}, "
                          f"P={wl.headdim}, N={wl.dstate}, E={wl.n_experts}, "
-                         f"top-k={wl.top_k}, chunk {wl.chunk}"),
+                         f"top-k={wl.top_k}, chunk {wl.chunk}"))
+            + (", expert-mixed decay (per-expert decays mixed per token)"
+               if args.decay == "mixed" else ""),
             "global_batch": wl.batch, "seq_len": wl.seqlen, "parallelism": "none",
         },
         "roofline": r["roofline"],
@@ -653,7 +707,7 @@ def main():
     if "step_roofline" in r:
         out["step_roofline"] = r["step_roofline"]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, mixed=args.decay == "mixed")
     print(json.dumps(out), flush=True)
 
 

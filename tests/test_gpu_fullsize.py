@@ -124,3 +124,67 @@ def test_output_project_full_size(name):
     err = float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref * ref)))
     say(f"  sampled rows: err {err:.3e}")
     assert err < TOL[wl.dtype]
+
+
+def test_prefill_mixed_decay_full_size():
+    # The expert-mixed decay at the c2 sizes, in the bench's launch
+    # configuration (binding.forward_mixed over the whole batch); sampled
+    # (sequence, head) pairs against the oracle one head at a time.
+    from oracle import mixed_decay as md
+    wl = synth.WORKLOADS["c2"]
+    say(f"[fullsize] c2 mixed decay: M={wl.tokens} H={wl.nheads} E={wl.n_experts}")
+    inp = synth.make_inputs(wl)
+    ae = synth.expert_decays(wl)
+    d = upload(wl, inp)
+    buf = sb.forward_mixed(sb.dims_of(wl), d["u"], d["w_router"], d["w_experts"],
+                           dev(ae, torch.float32), d["h_init"])
+    torch.cuda.synchronize()
+    M = wl.tokens
+    r = osw.route(inp["u"].reshape(M, -1), inp["w_router"], wl.top_k)
+    flips = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), r, wl)
+    lim = valid_prefix(flips, wl.batch, wl.seqlen)
+    y = buf.y.view(wl.batch, wl.seqlen, wl.nheads, 64)
+    for b, heads in [(0, [0, 11]), (5, [23])]:
+        T = int(lim[b])
+        ref = md.forward_tv(inp["u"][b:b + 1, :T], inp["w_router"], inp["w_experts"], ae, None,
+                            nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
+                            dstate=wl.dstate, top_k=wl.top_k, heads=heads)
+        e = slice_err(host(y[b:b + 1, :T][:, :, heads]), ref["y"])
+        say(f"  b={b} heads={heads} T={T}: y err {e:.3e}")
+        assert e < TOL[wl.dtype]
+        if T == wl.seqlen:
+            eh = slice_err(host(buf.h_final[b:b + 1, heads]), ref["h_final"], (0, 1))
+            assert eh < TOL[wl.dtype]
+
+
+def test_decode_mixed_decay_full_size():
+    from oracle import mixed_decay as md
+    wl = synth.WORKLOADS["c5"]
+    steps, rows = 3, [0, 128, 255]
+    say(f"[fullsize] c5 decode, mixed decay: batch {wl.batch}, {steps} steps, rows {rows}")
+    inp = synth.make_inputs(wl)
+    ae = synth.expert_decays(wl)
+    d = upload(wl, inp)
+    dims = sb.dims_of(wl)
+    dt = tdt(wl)
+    h = d["h_init"].clone()
+    y = torch.empty(wl.batch, wl.nheads, 64, dtype=dt, device="cuda")
+    idx = torch.empty(wl.batch, wl.top_k, dtype=torch.int32, device="cuda")
+    ws, _ = sb.workspace(dims, sb.CALL_DECODE)
+    aed = dev(ae, torch.float32)
+    h_ref = inp["h_init"][rows].astype(np.float64)
+    for step in range(steps):
+        ut = synth.decode_token(wl, step)
+        sb.swimba_decode_step_mixed(dims, dev(ut, dt), d["w_router"], d["w_experts"], aed, h, y,
+                                    idx, ws)
+        torch.cuda.synchronize()
+        r = osw.route(ut, inp["w_router"], wl.top_k)
+        check_routing(host(idx).astype(np.int64), None, r, wl)
+        ref = md.decode_step_tv(ut[rows], inp["w_router"], inp["w_experts"], ae, h_ref,
+                                nheads=wl.nheads, headdim=64, ngroups=1, dstate=wl.dstate,
+                                top_k=wl.top_k)
+        ey = slice_err(host(y)[rows][:, None], ref["y"][:, None])
+        eh = slice_err(host(h)[rows], ref["h"], (0, 1))
+        say(f"  step {step}: y err {ey:.3e} h err {eh:.3e}")
+        assert ey < TOL[wl.dtype] and eh < TOL[wl.dtype]
+        h_ref = ref["h"]
