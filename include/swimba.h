@@ -73,7 +73,8 @@ typedef enum swimba_call {
   SWIMBA_CALL_ROUTE = 0,
   SWIMBA_CALL_PROJECT = 1,
   SWIMBA_CALL_SCAN = 2,
-  SWIMBA_CALL_DECODE = 3
+  SWIMBA_CALL_DECODE = 3,
+  SWIMBA_CALL_SCAN_BACKWARD = 4
 } swimba_call;
 
 /*
@@ -263,6 +264,38 @@ swimba_status swimba_decode_step_mixed(const swimba_dims* dims, const void* u,
                                        const float* a_experts, float* h, void* y,
                                        int32_t* topk_idx, void* ws, size_t ws_bytes,
                                        hipStream_t stream);
+
+/*
+ * Backward of swimba_ssd_chunk_scan (papernotes.org notes, Experiments: the
+ * converted model is fine-tuned, which needs the gradients through the
+ * recurrence). For the loss l(y, h_final) with dy = dl/dy and dh_final =
+ * dl/dh_final, and g_t = dl/dh_t (g_t = C_mix_t dy_t^T + a g_{t+1}, g_T =
+ * dh_final):
+ *   dX_hat[t, j, h]  = g_t[h]^T B_hat[t, j, g]                      (P)
+ *   dB_hat[t, j, g]  = sum_{h in group g} g_t[h] X_hat[t, j, h]        (N)
+ *   dC_mix[t, g]     = sum_{h in group g} h_t[h] dy[t, h]             (N)
+ *   da[h]            = sum_t <g_t[h], h_{t-1}[h]>,   dh_init = a g_0
+ * solved in chunks of 64 tokens (32 for float32 problems) whatever
+ * dims->chunk is: local chunk states on matrix cores, a sweep over chunks for
+ * the states entering each chunk from either side, and the within-chunk
+ * quadratic forms on matrix cores (bf16 operands, or float32, fp32
+ * accumulation). Sums over heads and chunks run in a fixed order, so results
+ * are deterministic.
+ *   B_hat, X_hat, C_mix, a, h_init   as given to swimba_ssd_chunk_scan
+ *   dy        [M, H, P] dtype
+ *   dh_final  [Bt, H, N, P] float32, or NULL for zeros
+ *   dB_hat    [M, k, G, N] float32 out;  dX_hat [M, k, H, P] float32 out
+ *   dC_mix    [M, G, N] float32 out;  da [H] float32 out
+ *   dh_init   [Bt, H, N, P] float32 out, or NULL
+ *   ws        workspace of swimba_workspace_size(dims, SWIMBA_CALL_SCAN_BACKWARD)
+ * Shapes and errors as for swimba_ssd_chunk_scan (top_k <= 2).
+ */
+swimba_status swimba_ssd_chunk_scan_backward(const swimba_dims* dims, const void* B_hat,
+                                             const void* X_hat, const void* C_mix,
+                                             const float* a, const float* h_init, const void* dy,
+                                             const float* dh_final, float* dB_hat, float* dX_hat,
+                                             float* dC_mix, float* da, float* dh_init, void* ws,
+                                             size_t ws_bytes, hipStream_t stream);
 
 /*
  * Per-kernel timing with HIP events, for measurement only. While enabled,

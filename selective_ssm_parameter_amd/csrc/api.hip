@@ -262,6 +262,8 @@ size_t swimba_workspace_size(const swimba_dims* dims, int32_t call) {
     case SWIMBA_CALL_PROJECT: return d.M == 0 ? 0 : proj_ws(d).total;
     case SWIMBA_CALL_SCAN: return scan_bytes(d);
     case SWIMBA_CALL_DECODE: return d.Bt == 0 ? 0 : dec_ws(d).total;
+    case SWIMBA_CALL_SCAN_BACKWARD:
+      return d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.N);
     default: return 0;
   }
 }
@@ -368,6 +370,42 @@ swimba_status swimba_ssd_chunk_scan_mixed(const swimba_dims* dims, const void* B
   if (!ld && dims && dims->seqlen == 0) ld = kNoTokens;
   return scan_impl(true, dims, B_hat, X_hat, C_mix, nullptr, ld, h_init, y, h_final, ws,
                    ws_bytes, stream);
+}
+
+swimba_status swimba_ssd_chunk_scan_backward(const swimba_dims* dims, const void* B_hat,
+                                             const void* X_hat, const void* C_mix,
+                                             const float* a, const float* h_init, const void* dy,
+                                             const float* dh_final, float* dB_hat, float* dX_hat,
+                                             float* dC_mix, float* da, float* dh_init, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_scan_shape(d)) != SWIMBA_OK) return st;
+  if (d.M * d.HP * 4 >= (int64_t(1) << 40)) return fail(SWIMBA_ERR_DIMS, "problem too large");
+  REQUIRE_PTR(da);
+  REQUIRE_PTR(a);
+  OPTIONAL_PTR(h_init);
+  OPTIONAL_PTR(dh_final);
+  OPTIONAL_PTR(dh_init);
+  if (d.M > 0) {
+    REQUIRE_PTR(B_hat);
+    REQUIRE_PTR(X_hat);
+    REQUIRE_PTR(C_mix);
+    REQUIRE_PTR(dy);
+    REQUIRE_PTR(dB_hat);
+    REQUIRE_PTR(dX_hat);
+    REQUIRE_PTR(dC_mix);
+  }
+  const size_t need =
+      d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.N);
+  if ((st = check_ws(ws, ws_bytes, need)) != SWIMBA_OK) return st;
+  return hip_status(launch_scan_backward(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.G,
+                                         (int)d.N, (int)d.k, B_hat, X_hat, C_mix, dy, a, h_init,
+                                         dh_final, dB_hat, dX_hat, dC_mix, da, dh_init, ws,
+                                         stream),
+                    "ssd_chunk_scan_backward launch");
 }
 
 swimba_status swimba_mix_decay(const swimba_dims* dims, const int32_t* topk_idx,

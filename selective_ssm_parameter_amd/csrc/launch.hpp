@@ -83,6 +83,14 @@ hipError_t launch_output_project(bool is_bf16, int M, int K, int N, const void* 
 
 // a_experts non-null: the expert-mixed decay, a_t = sum_j w_j a_experts[idx_j]
 // / sum_j w_j from the routing (idx, w [Bt, k]); a is then not read.
+// Backward of the chunked scan (see swimba_ssd_chunk_scan_backward).
+size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int N);
+hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N, int k,
+                                const void* B_hat, const void* X_hat, const void* C_mix,
+                                const void* dy, const float* a, const float* h_init,
+                                const float* dh_final, float* dB, float* dX, float* dC, float* da,
+                                float* dh_init, void* ws, hipStream_t s);
+
 hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
                                const void* B_hat, const void* X_hat, const float* c_part,
                                const float* a, float* h, void* y, hipStream_t s,

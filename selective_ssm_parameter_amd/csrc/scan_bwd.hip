@@ -1,0 +1,476 @@
+// Backward of the single-trajectory scan (the reverse-time chunked solve).
+// (papernotes.org notes on "Swimba: Switch Mamba Model Scales State Space
+// Models", Method, key design 1: h_t = a h_{t-1} + sum_j B_hat_j X_j^T,
+// y_t = C~_t^T h_t; Experiments: the converted model is fine-tuned, which
+// needs these gradients.)
+//
+// With g_t = dl/dh_t (gradient of the loss through every later readout):
+//   g_t = C~_t dy_t^T + a g_{t+1} (+ dh_T at t = T-1)
+//   dX_j = g_t^T B_hat_j,  dB_hat_j = sum_{heads of the group} g_t X_j,
+//   dC~_t = sum_{heads} h_t dy_t,  da = sum_t <g_t, h_{t-1}>,  dh_init = a g_0.
+// Chunks of BL tokens (a fixed internal length: the result does not depend
+// on it). For chunk c = [c0, c1), entering state H_c = h_{c0-1} and F_c =
+// a g_{c1} (dh_T for the last chunk: the gradient entering from the right),
+// with local times:
+//   g_t = sum_{s >= t} a^{s-t} C~_s dy_s^T + a^{c1-1-t} F_c
+//   h_t = sum_{s <= t} a^{t-s} U_s      + a^{t-c0+1} H_c
+// so, with Gm[s, r] = C~_s . B_hat_r and D[s, r] = dy_s . X_r over the chunk's
+// (token, slot) pairs r of token t(r), masked to t(r) <= s:
+//   dX_r^T   = sum_s dy_s^T a^{s-t} Gm[s, r]     + a^{c1-1-t} F_c^T B_hat_r
+//   dB_hat_r = sum_s C~_s   a^{s-t} D[s, r]      + a^{c1-1-t} F_c X_r
+//   dC~_s    = sum_r B_hat_r a^{s-t} D[s, r]     + a^{s-c0+1} H_c dy_s
+//   da       = sum_{t(r) < s} (s-t) a^{s-t-1} Gm[s, r] D[s, r]
+//            + sum_r (c1-1-t) a^{c1-2-t} B_hat_r . (F_c X_r)
+//            + sum_s (s-c0+1) a^{s-c0} C~_s . (H_c dy_s) + Lc a^{Lc-1} <F_c, H_c>.
+// Kernels: local chunk states S_c = sum_r a^{c1-1-t} B_hat_r X_r^T and
+// R_c = sum_s a^{s-c0} C~_s dy_s^T (matrix cores); a sequential sweep per
+// state element turning S into H_c (forwards: H_{c+1} = a^{Lc} H_c + S_c) and
+// R into F_c (backwards: F_{c-1} = a R_c + a^{Lc} F_c, ending at F_{-1} =
+// dh_init) in place; per (sequence, chunk, group) the gradients above on matrix cores,
+// the heads of the group visited in order so dB_hat and dC~ are summed over
+// them in registers (deterministic); a fixed-order sum of da.
+// Matrix-core operands are fp16 (fp32 for fp32 problems) with fp32
+// accumulation and fp32 outputs: the streams are fp16 already, and dy and the
+// states are scaled per (chunk, head) by a power of two that brings their
+// largest magnitude into [1/2, 1) (exact, and undone in fp32 on the results),
+// so the gradients keep fp16's precision whatever their range.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace swimba {
+
+constexpr int kBP = 64;  // head dim
+
+struct BwdArgs {
+  const void* B_hat;    // [M, k, G, N] stream type
+  const void* X_hat;    // [M, k, H, P] stream type
+  const void* C_mix;    // [M, G, N] stream type
+  const void* dy;       // [M, H, P] dtype
+  const float* a;       // [H]
+  const float* h_init;  // [Bt, H, N, P] or null
+  const float* dh_final;
+  float* dB;            // [M, k, G, N]
+  float* dX;            // [M, k, H, P]
+  float* dC;            // [M, G, N]
+  float* da;            // [H]
+  float* dh_init;       // [Bt, H, N, P] or null
+  float* S;             // [Bt, nb, H, N, P]: S_c, then H_c
+  float* R;             // [Bt, nb, H, N, P]: R_c, then F_c
+  float* da_part;       // [Bt, nb, H]
+  int T, H, G, N, k, nb;
+};
+
+// One 16 x 16 tile D[m0.., n0..] += sum_k A(m, k) B(k, n) over k in [0, K)
+// (K a multiple of 32) from LDS: A(m, k) at A[m * am + k * ak], B(k, n) at
+// B[k * bk + n * bn]. AK1 / BK1: the contraction index is contiguous (one
+// 16-byte read per fragment), else eight element reads. Lane (g, c) gets
+// D[m0 + 4g + i][n0 + c].
+template <typename T, bool AK1, bool BK1>
+__device__ __forceinline__ floatx4 tile_mm(const T* A, int am, int ak, const T* B, int bk, int bn,
+                                           int m0, int n0, int K, floatx4 acc, int g, int c) {
+  typedef typename Vec<T>::x8 F;
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const int kk = k0 + 8 * g;
+    F fa, fb;
+    if constexpr (AK1) {
+      fa = load8<T>(A + (m0 + c) * am + kk);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fa[j] = A[(m0 + c) * am + (kk + j) * ak];
+    }
+    if constexpr (BK1) {
+      fb = load8<T>(B + kk + (n0 + c) * bn);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j] = B[(kk + j) * bk + (n0 + c) * bn];
+    }
+    acc = mma16(fa, fb, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float powi(float a, int d) {
+  float r = 1.f, b = a;
+  for (int e = d; e > 0; e >>= 1) {
+    if (e & 1) r *= b;
+    b *= b;
+  }
+  return r;
+}
+
+// Row-major LDS copy of `rows` x `cols` elements (cols a multiple of 4) from
+// global rows of stride `gstride`, converted to T; rows >= valid and columns
+// >= cvalid are zeros; each element optionally scaled by f(row).
+template <typename T, typename SRC, class F>
+__device__ __forceinline__ void load_tile(T* dst, int rows, int cols, const SRC* src,
+                                          size_t gstride, int valid, int cvalid, F f) {
+  for (int q = threadIdx.x; q < rows * cols; q += blockDim.x) {
+    const int r = q / cols, cc = q - r * cols;
+    float v = 0.f;
+    if (r < valid && cc < cvalid) v = to_f32(src[(size_t)r * gstride + cc]) * f(r);
+    dst[q] = from_f32<T>(v);
+  }
+}
+
+// load_tile with the tile scaled by the power of two 2^-e that brings its
+// largest magnitude into [1/2, 1); returns the scale (1 for an all-zero tile).
+// Every thread of the workgroup must call it (two barriers; red: 4 floats).
+template <typename T, typename SRC, class F>
+__device__ __forceinline__ float load_tile_scaled(T* dst, int rows, int cols, const SRC* src,
+                                                  size_t gstride, int valid, int cvalid, F f,
+                                                  float* red) {
+  float mx = 0.f;
+  for (int q = threadIdx.x; q < rows * cols; q += blockDim.x) {
+    const int r = q / cols, cc = q - r * cols;
+    if (r < valid && cc < cvalid) mx = fmaxf(mx, fabsf(to_f32(src[(size_t)r * gstride + cc]) * f(r)));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  const float sc = mx > 0.f ? ldexpf(1.f, -(ilogbf(mx) + 1)) : 1.f;
+  load_tile<T>(dst, rows, cols, src, gstride, valid, cvalid, [&](int r) { return f(r) * sc; });
+  return sc;
+}
+
+// ---------------------------------------------------------------- local states
+
+template <typename T, typename S, typename TY, int NP, int KS, int BL>
+__global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
+  constexpr int R = KS * BL;
+  __shared__ __align__(16) T Bs[R * NP];
+  __shared__ __align__(16) T Xd[R * kBP];
+  __shared__ __align__(16) T Cs[BL * NP];
+  __shared__ __align__(16) T Dyd[BL * kBP];
+  __shared__ float red[4];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int H = A.H, G = A.G, N = A.N, Tl = A.T;
+  const int grp = h / (H / G);
+  const int c0 = c * BL, Lc = min(BL, Tl - c0);
+  const float a = A.a[h];
+  const size_t m0 = (size_t)b * Tl + c0;  // first token row of the chunk
+  load_tile<T>(Bs, R, NP, static_cast<const S*>(A.B_hat) + (m0 * KS) * G * N + grp * N,
+               (size_t)G * N, Lc * KS, N, [](int) { return 1.f; });
+  load_tile<T>(Xd, R, kBP, static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP,
+               (size_t)H * kBP, Lc * KS, kBP, [&](int r) { return powi(a, Lc - 1 - r / KS); });
+  load_tile<T>(Cs, BL, NP, static_cast<const S*>(A.C_mix) + m0 * G * N + grp * N, (size_t)G * N,
+               Lc, N, [](int) { return 1.f; });
+  const float sdy = load_tile_scaled<T>(Dyd, BL, kBP,
+                                        static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP,
+                                        (size_t)H * kBP, Lc, kBP,
+                                        [&](int s) { return powi(a, s); }, red);
+  __syncthreads();
+  const float udy = 1.f / sdy;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, cl = lane & 15;
+  const size_t sbase = (((size_t)b * A.nb + c) * H + h) * (size_t)N * kBP;
+  constexpr int TILES = (NP / 16) * (kBP / 16);
+  for (int t = wave; t < TILES; t += 4) {
+    const int n0 = 16 * (t / (kBP / 16)), p0 = 16 * (t % (kBP / 16));
+    if (n0 >= N) continue;
+    // S[n][p] = sum_r B_hat[r][n] xd[r][p];  R[n][p] = sum_s C~[s][n] dyd[s][p]
+    floatx4 s4 = tile_mm<T, false, false>(Bs, 1, NP, Xd, kBP, 1, n0, p0, R,
+                                          floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+    floatx4 r4 = tile_mm<T, false, false>(Cs, 1, NP, Dyd, kBP, 1, n0, p0, BL,
+                                          floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 4 * g + i;
+      A.S[sbase + (size_t)n * kBP + p0 + cl] = s4[i];
+      A.R[sbase + (size_t)n * kBP + p0 + cl] = r4[i] * udy;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- state sweep
+
+// Per state element: S_c -> H_c (the state entering chunk c) in place going
+// forwards, R_c -> F_c (the gradient entering chunk c from the right) in
+// place going backwards; the backward sweep ends at F_{-1} = a g_0 = dh_init.
+template <int BL>
+__global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdArgs A) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int NPsz = A.N * kBP;
+  const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e4 >= NPsz) return;
+  const float a = A.a[h];
+  const size_t hb = ((size_t)b * A.H + h) * NPsz + e4;
+  const size_t cstride = (size_t)A.H * NPsz;
+  const size_t base = (size_t)b * A.nb * cstride + (size_t)h * NPsz + e4;
+  floatx4 st = A.h_init ? *reinterpret_cast<const floatx4*>(A.h_init + hb)
+                        : floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < A.nb; ++c) {
+    floatx4* p = reinterpret_cast<floatx4*>(A.S + base + c * cstride);
+    const floatx4 s = *p;
+    *p = st;
+    st = st * powi(a, min(BL, A.T - c * BL)) + s;
+  }
+  floatx4 gr = A.dh_final ? *reinterpret_cast<const floatx4*>(A.dh_final + hb)
+                          : floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int c = A.nb - 1; c >= 0; --c) {
+    floatx4* p = reinterpret_cast<floatx4*>(A.R + base + c * cstride);
+    const floatx4 r = *p;
+    *p = gr;
+    gr = gr * powi(a, min(BL, A.T - c * BL)) + r * a;
+  }
+  if (A.dh_init) *reinterpret_cast<floatx4*>(A.dh_init + hb) = gr;
+}
+
+// ---------------------------------------------------------------- chunk gradients
+
+template <typename T, typename S, typename TY, int NP, int KS, int BL>
+__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs A) {
+  constexpr int R = KS * BL;
+  constexpr int NBT = (NP / 16) * (R / 16);   // dB_hat tiles of the chunk
+  constexpr int NCT = (NP / 16) * (BL / 16);  // dC~ tiles
+  __shared__ __align__(16) T Bs[R * NP];      // B_hat [r][n]
+  __shared__ __align__(16) T Cs[BL * NP];     // C~ [s][n]
+  __shared__ __align__(16) T Gm[BL * R];      // C~_s . B_hat_r
+  __shared__ __align__(16) T Xs[R * kBP];     // X_r of the head
+  __shared__ __align__(16) T Dys[BL * kBP];   // dy_s of the head
+  __shared__ __align__(16) T Dm[BL * R];      // masked, decayed D
+  __shared__ __align__(16) T GmM[BL * R];     // masked, decayed Gm
+  __shared__ __align__(16) T Ss[NP * kBP];    // F_c, then H_c, of the head
+  __shared__ float red[4];
+  __shared__ float redm[4];
+
+  const int c = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
+  const int H = A.H, G = A.G, N = A.N, Tl = A.T, HG = H / G;
+  const int c0 = c * BL, Lc = min(BL, Tl - c0);
+  const size_t m0 = (size_t)b * Tl + c0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, cl = lane & 15;
+
+  load_tile<T>(Bs, R, NP, static_cast<const S*>(A.B_hat) + (m0 * KS) * G * N + grp * N,
+               (size_t)G * N, Lc * KS, N, [](int) { return 1.f; });
+  load_tile<T>(Cs, BL, NP, static_cast<const S*>(A.C_mix) + m0 * G * N + grp * N, (size_t)G * N,
+               Lc, N, [](int) { return 1.f; });
+  __syncthreads();
+  // Gm[s][r] = C~_s . B_hat_r
+  for (int t = wave; t < (BL / 16) * (R / 16); t += 4) {
+    const int s0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
+    const floatx4 v = tile_mm<T, true, true>(Cs, NP, 1, Bs, 1, NP, s0, r0, NP,
+                                             floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Gm[(s0 + 4 * g + i) * R + r0 + cl] = from_f32<T>(v[i]);
+  }
+
+  floatx4 dBa[(NBT + 3) / 4], dCa[(NCT + 3) / 4];
+#pragma unroll
+  for (int i = 0; i < (NBT + 3) / 4; ++i) dBa[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < (NCT + 3) / 4; ++i) dCa[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int hi = 0; hi < HG; ++hi) {
+    const int h = grp * HG + hi;
+    const float a = A.a[h];
+    const size_t sbase = (((size_t)b * A.nb + c) * H + h) * (size_t)N * kBP;
+    __syncthreads();  // the previous head is done with Xs, Dys, Dm, GmM, Ss
+    load_tile<T>(Xs, R, kBP, static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP,
+                 (size_t)H * kBP, Lc * KS, kBP, [](int) { return 1.f; });
+    const float sdy = load_tile_scaled<T>(Dys, BL, kBP,
+                                          static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP,
+                                          (size_t)H * kBP, Lc, kBP, [](int) { return 1.f; }, redm);
+    const float sF = load_tile_scaled<T>(Ss, NP, kBP, A.R + sbase, (size_t)kBP, N, kBP,
+                                         [](int) { return 1.f; }, redm);
+    const float udy = 1.f / sdy, uF = 1.f / sF;
+    __syncthreads();
+    float dap = 0.f;  // this lane's part of da for the head
+    // D[s][r] = dy_s . X_r; the masked, decayed D and Gm; the Gm D term of da
+    for (int t = wave; t < (BL / 16) * (R / 16); t += 4) {
+      const int s0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
+      const floatx4 v = tile_mm<T, true, true>(Dys, kBP, 1, Xs, 1, kBP, s0, r0, kBP,
+                                               floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const int r = r0 + cl, tr = r / KS;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = s0 + 4 * g + i;
+        const float gm = to_f32(Gm[s * R + r]);
+        const bool in = tr <= s && s < Lc && tr < Lc;
+        const float dec = in ? powi(a, s - tr) : 0.f;
+        if (in && tr < s) dap += (float)(s - tr) * powi(a, s - tr - 1) * gm * v[i] * udy;
+        Dm[s * R + r] = from_f32<T>(dec * v[i]);
+        GmM[s * R + r] = from_f32<T>(dec * gm);
+      }
+    }
+    __syncthreads();
+    // dX_r^T[p] = sum_s dy_s[p] GmM[s][r] + a^{Lc-1-t} (F_c^T B_hat_r)[p]
+    for (int t = wave; t < (kBP / 16) * (R / 16); t += 4) {
+      const int p0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
+      floatx4 v = tile_mm<T, false, false>(Dys, 1, kBP, GmM, R, 1, p0, r0, BL,
+                                           floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const floatx4 w = tile_mm<T, false, true>(Ss, 1, kBP, Bs, 1, NP, p0, r0, NP,
+                                                floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const int r = r0 + cl, tr = r / KS;
+      if (tr < Lc) {
+        v = v * udy + w * (powi(a, Lc - 1 - tr) * uF);
+        const size_t row = (m0 * KS + r) * H + h;  // pair row of X_hat
+        *reinterpret_cast<floatx4*>(A.dX + row * kBP + p0 + 4 * g) = v;
+      }
+    }
+    // dB_hat_r[n] += sum_s C~_s[n] Dm[s][r] + a^{Lc-1-t} (F_c X_r)[n]
+#pragma unroll
+    for (int i = 0; i < (NBT + 3) / 4; ++i) {
+      const int t = wave + 4 * i;
+      const int n0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
+      if (t >= NBT || n0 >= N) continue;
+      const floatx4 v = tile_mm<T, false, false>(Cs, 1, NP, Dm, R, 1, n0, r0, BL,
+                                                 floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const floatx4 w = tile_mm<T, true, true>(Ss, kBP, 1, Xs, 1, kBP, n0, r0, kBP,
+                                               floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const int r = r0 + cl, tr = r / KS;
+      const float sc = tr < Lc ? powi(a, Lc - 1 - tr) : 0.f;
+      const float wt = tr + 1 < Lc ? (float)(Lc - 1 - tr) * powi(a, Lc - 2 - tr) : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dap += wt * uF * w[q] * to_f32(Bs[r * NP + n0 + 4 * g + q]);
+      dBa[i] = dBa[i] + v * udy + w * (sc * uF);
+    }
+    // <F_c, H_c> in fp32, then H_c into Ss
+    float eh = 0.f;
+    for (int q = threadIdx.x; q < N * kBP; q += blockDim.x) eh += A.R[sbase + q] * A.S[sbase + q];
+    dap += eh * (float)Lc * powi(a, Lc - 1);
+    __syncthreads();  // every wave is done with F_c
+    const float sH = load_tile_scaled<T>(Ss, NP, kBP, A.S + sbase, (size_t)kBP, N, kBP,
+                                         [](int) { return 1.f; }, redm);
+    const float uHdy = 1.f / (sH * sdy);
+    __syncthreads();
+    // dC~_s[n] += sum_r B_hat_r[n] Dm[s][r] + a^{s+1} (H_c dy_s)[n]
+#pragma unroll
+    for (int i = 0; i < (NCT + 3) / 4; ++i) {
+      const int t = wave + 4 * i;
+      const int n0 = 16 * (t / (BL / 16)), s0 = 16 * (t % (BL / 16));
+      if (t >= NCT || n0 >= N) continue;
+      const floatx4 v = tile_mm<T, false, true>(Bs, 1, NP, Dm, 1, R, n0, s0, R,
+                                                floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const floatx4 w = tile_mm<T, true, true>(Ss, kBP, 1, Dys, 1, kBP, n0, s0, kBP,
+                                               floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const int s = s0 + cl;
+      const float sc = s < Lc ? powi(a, s + 1) : 0.f;
+      const float wt = s < Lc ? (float)(s + 1) * powi(a, s) : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dap += wt * uHdy * w[q] * to_f32(Cs[s * NP + n0 + 4 * g + q]);
+      dCa[i] = dCa[i] + v * udy + w * (sc * uHdy);
+    }
+    // da of this (sequence, chunk, head): wave sums, then the four waves in order
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dap += __shfl_xor(dap, off);
+    if (lane == 0) red[wave] = dap;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      A.da_part[((size_t)b * A.nb + c) * H + h] = ((red[0] + red[1]) + red[2]) + red[3];
+  }
+
+  // dB_hat and dC~ of the chunk, summed over the group's heads
+#pragma unroll
+  for (int i = 0; i < (NBT + 3) / 4; ++i) {
+    const int t = wave + 4 * i;
+    const int n0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
+    const int r = r0 + cl;
+    if (t >= NBT || n0 >= N || r / KS >= Lc) continue;
+    *reinterpret_cast<floatx4*>(A.dB + ((m0 * KS + r) * G + grp) * N + n0 + 4 * g) = dBa[i];
+  }
+#pragma unroll
+  for (int i = 0; i < (NCT + 3) / 4; ++i) {
+    const int t = wave + 4 * i;
+    const int n0 = 16 * (t / (BL / 16)), s0 = 16 * (t % (BL / 16));
+    const int s = s0 + cl;
+    if (t >= NCT || n0 >= N || s >= Lc) continue;
+    *reinterpret_cast<floatx4*>(A.dC + ((m0 + s) * G + grp) * N + n0 + 4 * g) = dCa[i];
+  }
+}
+
+// da[h] = sum over sequences and chunks in order
+__global__ void bwd_da_kernel(const float* __restrict__ part, float* __restrict__ da, int Bt,
+                              int nb, int H) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  float s = 0.f;
+  for (int b = 0; b < Bt; ++b)
+    for (int c = 0; c < nb; ++c) s += part[((size_t)b * nb + c) * H + h];
+  da[h] = s;
+}
+
+// ---------------------------------------------------------------- launch
+
+int scan_bwd_block(bool is_bf16) { return is_bf16 ? 64 : 32; }
+
+size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int N) {
+  const int BL = scan_bwd_block(is_bf16);
+  const size_t nb = (size_t)((T + BL - 1) / BL);
+  const size_t st = (size_t)Bt * nb * H * N * kBP * sizeof(float);
+  const size_t al = 255;
+  return ((st + al) & ~al) * 2 + (((size_t)Bt * nb * H * sizeof(float) + al) & ~al);
+}
+
+template <typename T, typename S, typename TY, int NP, int KS, int BL>
+static hipError_t launch_bwd_t(const BwdArgs& A, int Bt, hipStream_t s) {
+  const dim3 g1((unsigned)A.nb, (unsigned)A.H, (unsigned)Bt);
+  prof_begin("scan_bwd_local", s);
+  hipLaunchKernelGGL((bwd_local_kernel<T, S, TY, NP, KS, BL>), g1, dim3(256), 0, s, A);
+  prof_end(s);
+  prof_begin("scan_bwd_sweep", s);
+  hipLaunchKernelGGL(bwd_sweep_kernel<BL>, dim3((unsigned)((A.N * kBP / 4 + 255) / 256), A.H, Bt),
+                     dim3(256), 0, s, A);
+  prof_end(s);
+  prof_begin("scan_bwd_grad", s);
+  hipLaunchKernelGGL((bwd_grad_kernel<T, S, TY, NP, KS, BL>),
+                     dim3((unsigned)A.nb, (unsigned)A.G, (unsigned)Bt), dim3(256), 0, s, A);
+  prof_end(s);
+  prof_begin("scan_bwd_da", s);
+  hipLaunchKernelGGL(bwd_da_kernel, dim3((A.H + 63) / 64), dim3(64), 0, s, A.da_part, A.da, Bt,
+                     A.nb, A.H);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+template <typename T, typename S, typename TY, int NP>
+static hipError_t launch_bwd_np(const BwdArgs& A, int Bt, hipStream_t s) {
+  constexpr int BL = sizeof(T) == 2 ? 64 : 32;
+  if (A.k == 1) return launch_bwd_t<T, S, TY, NP, 1, BL>(A, Bt, s);
+  return launch_bwd_t<T, S, TY, NP, 2, BL>(A, Bt, s);
+}
+
+template <typename T, typename S, typename TY>
+static hipError_t launch_bwd_ty(const BwdArgs& A, int Bt, hipStream_t s) {
+  if (A.N <= 32) return launch_bwd_np<T, S, TY, 32>(A, Bt, s);
+  if (A.N <= 64) return launch_bwd_np<T, S, TY, 64>(A, Bt, s);
+  return launch_bwd_np<T, S, TY, 128>(A, Bt, s);
+}
+
+__global__ void bwd_empty_kernel(const float* __restrict__ dh_final, float* __restrict__ dh_init,
+                                 float* __restrict__ da, size_t n, int H) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (dh_init && i < n) dh_init[i] = dh_final ? dh_final[i] : 0.f;
+  if (i < (size_t)H) da[i] = 0.f;
+}
+
+hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N, int k,
+                                const void* B_hat, const void* X_hat, const void* C_mix,
+                                const void* dy, const float* a, const float* h_init,
+                                const float* dh_final, float* dB, float* dX, float* dC, float* da,
+                                float* dh_init, void* ws, hipStream_t s) {
+  if (Bt == 0) {
+    if (H > 0) hipLaunchKernelGGL(bwd_empty_kernel, dim3(1), dim3(256), 0, s, nullptr, nullptr,
+                                  da, (size_t)0, H);
+    return hipGetLastError();
+  }
+  if (T == 0) {
+    const size_t n = (size_t)Bt * H * N * kBP;
+    const size_t m = n > (size_t)H ? n : (size_t)H;
+    hipLaunchKernelGGL(bwd_empty_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s,
+                       dh_final, dh_init, da, n, H);
+    return hipGetLastError();
+  }
+  const int BL = scan_bwd_block(is_bf16);
+  const int nb = (T + BL - 1) / BL;
+  const size_t st = (size_t)Bt * nb * H * N * kBP * sizeof(float);
+  const size_t stal = (st + 255) & ~(size_t)255;
+  unsigned char* w8 = static_cast<unsigned char*>(ws);
+  BwdArgs A{B_hat, X_hat, C_mix, dy, a, h_init, dh_final, dB, dX, dC, da, dh_init,
+            reinterpret_cast<float*>(w8), reinterpret_cast<float*>(w8 + stal),
+            reinterpret_cast<float*>(w8 + 2 * stal), T, H, G, N, k, nb};
+  if (is_bf16) return launch_bwd_ty<f16, f16, bf16>(A, Bt, s);
+  return launch_bwd_ty<float, float, float>(A, Bt, s);
+}
+
+}  // namespace swimba

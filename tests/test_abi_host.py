@@ -41,7 +41,7 @@ def lib():
 def test_exports_every_declared_symbol():
     L = lib()
     syms = declared_symbols()
-    assert len(syms) == 14, syms
+    assert len(syms) == 15, syms
     for s in syms:
         assert hasattr(L, s), f"{s} declared in swimba.h but not exported"
     assert set(syms) == set(sb.EXPORTS)
