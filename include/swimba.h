@@ -74,7 +74,8 @@ typedef enum swimba_call {
   SWIMBA_CALL_PROJECT = 1,
   SWIMBA_CALL_SCAN = 2,
   SWIMBA_CALL_DECODE = 3,
-  SWIMBA_CALL_SCAN_BACKWARD = 4
+  SWIMBA_CALL_SCAN_BACKWARD = 4,
+  SWIMBA_CALL_PROJECT_BACKWARD = 5
 } swimba_call;
 
 /*
@@ -296,6 +297,40 @@ swimba_status swimba_ssd_chunk_scan_backward(const swimba_dims* dims, const void
                                              const float* dh_final, float* dB_hat, float* dX_hat,
                                              float* dC_mix, float* da, float* dh_init, void* ws,
                                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward of the router, the expert projections and the parameter-space mix
+ * (papernotes.org notes on "Swimba: Switch Mamba Model Scales State Space
+ * Models", Method, key design 1: z_j = W^(e_j) u with rows X | B | C,
+ * B_hat_j = w_j B_j, C_mix = sum_j w_j C_j, w_j = softmax(W_r u)[e_j];
+ * Experiments: fine-tuning needs these gradients). Given the gradients of
+ * the scan's inputs (from swimba_ssd_chunk_scan_backward):
+ *   dz_j      = [dX_hat_j | w_j dB_hat_j | w_j dC_mix]
+ *   dw_j      = <B_j, dB_hat_j> + <C_j, dC_mix>
+ *   dg        = pi * (dpi - <pi, dpi>),  dpi = dw scattered to the selected experts
+ *   du        = sum_j W^(e_j)^T dz_j + W_r^T dg
+ *   dW_experts[e] = sum over the (token, slot) pairs routed to e of dz_j u^T
+ *   dW_router = dg^T u
+ * The top-k set has no gradient (it is piecewise constant in the logits).
+ * The call recomputes the forward routing and projection with the forward's
+ * own kernels (same bits as swimba_route_topk + swimba_expert_project_mix),
+ * so only the primal inputs are passed. du and dW_experts are grouped GEMMs
+ * on matrix cores over the pairs sorted by expert (bf16 operands, or float32;
+ * fp32 accumulation); every sum over slots, pairs and tokens runs in a fixed
+ * order, so results are deterministic.
+ *   u, w_router, w_experts   as given to the forward calls (dtype)
+ *   dB_hat      [M, k, G, N] float32;  dX_hat [M, k, H, P] float32
+ *   dC_mix      [M, G, N] float32
+ *   du          [M, D] float32 out
+ *   dW_router   [E, D] float32 out;  dW_experts [E, W, D] float32 out
+ *               (zeros when M is 0; every other pointer may then be NULL)
+ *   ws          workspace of swimba_workspace_size(dims, SWIMBA_CALL_PROJECT_BACKWARD)
+ * Shapes and errors as for swimba_expert_project_mix.
+ */
+swimba_status swimba_expert_project_mix_backward(
+    const swimba_dims* dims, const void* u, const void* w_router, const void* w_experts,
+    const float* dB_hat, const float* dX_hat, const float* dC_mix, float* du, float* dW_router,
+    float* dW_experts, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Per-kernel timing with HIP events, for measurement only. While enabled,

@@ -17,7 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libswimba.so")
 
 F32, BF16 = 0, 1
-CALL_ROUTE, CALL_PROJECT, CALL_SCAN, CALL_DECODE, CALL_SCAN_BACKWARD = 0, 1, 2, 3, 4
+CALL_ROUTE, CALL_PROJECT, CALL_SCAN, CALL_DECODE, CALL_SCAN_BACKWARD, CALL_PROJECT_BACKWARD = (
+    0, 1, 2, 3, 4, 5)
 
 STATUS = {
     0: "SWIMBA_OK", -1: "SWIMBA_ERR_NULL", -2: "SWIMBA_ERR_DIMS", -3: "SWIMBA_ERR_UNSUPPORTED",
@@ -30,6 +31,7 @@ EXPORTS = (
     "swimba_output_project", "swimba_profile_enable", "swimba_profile_report",
     "swimba_profile_select", "swimba_mix_decay", "swimba_ssd_chunk_scan_mixed",
     "swimba_decode_step_mixed", "swimba_ssd_chunk_scan_backward",
+    "swimba_expert_project_mix_backward",
 )
 
 
@@ -86,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.swimba_decode_step_mixed.restype = I32
     L.swimba_ssd_chunk_scan_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, S]
     L.swimba_ssd_chunk_scan_backward.restype = I32
+    L.swimba_expert_project_mix_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, SZ, S]
+    L.swimba_expert_project_mix_backward.restype = I32
     L.swimba_profile_enable.restype = I32
     L.swimba_profile_enable.argtypes = [I32]
     L.swimba_profile_report.restype = I32
@@ -213,6 +217,15 @@ def swimba_ssd_chunk_scan_backward(dims, B_hat, X_hat, C_mix, a, h_init, dy, dh_
         ctypes.byref(dims), _ptr(B_hat), _ptr(X_hat), _ptr(C_mix), _ptr(a), _ptr(h_init),
         _ptr(dy), _ptr(dh_final), _ptr(dB_hat), _ptr(dX_hat), _ptr(dC_mix), _ptr(da),
         _ptr(dh_init), _ptr(ws), nb, _stream(stream)))
+
+
+def swimba_expert_project_mix_backward(dims, u, w_router, w_experts, dB_hat, dX_hat, dC_mix, du,
+                                       dW_router, dW_experts, ws, ws_bytes=None, stream=None):
+    nb = (ws.numel() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check(lib().swimba_expert_project_mix_backward(
+        ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(dB_hat), _ptr(dX_hat),
+        _ptr(dC_mix), _ptr(du), _ptr(dW_router), _ptr(dW_experts), _ptr(ws), nb,
+        _stream(stream)))
 
 
 def swimba_output_project(dims, y, w_out, out, stream=None):

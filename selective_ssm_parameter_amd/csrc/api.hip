@@ -135,6 +135,31 @@ DecWs dec_ws(const Dims& d) {
   return w;
 }
 
+// Backward of projection, mix and router: the recomputed forward (routing,
+// bucketing, weighted streams) and the backward's scratch.
+struct PbwdWs {
+  size_t idx, w, logits, proj, bhat, xhat, dz, sw, dg, dupart, dwrpart, total;
+};
+
+PbwdWs pbwd_ws(const Dims& d) {
+  PbwdWs w{};
+  size_t off = 0;
+  const int64_t pairs = d.M * d.k;
+  w.idx = off; off += align256(sizeof(int32_t) * pairs);
+  w.w = off; off += align256(sizeof(float) * pairs);
+  w.logits = off; off += align256(sizeof(float) * d.M * d.E);
+  w.proj = off; off += proj_ws(d).total;
+  w.bhat = off; off += align256(d.esize * pairs * d.GN);
+  w.xhat = off; off += align256(d.esize * pairs * d.HP);
+  w.dz = off; off += align256(d.esize * pairs * d.W);
+  w.sw = off; off += align256(sizeof(float) * pairs);
+  w.dg = off; off += align256(sizeof(float) * d.M * d.E);
+  w.dupart = off; off += align256(sizeof(float) * pairs * d.D);
+  w.dwrpart = off; off += align256(sizeof(float) * proj_bwd_splits((int)d.M) * d.E * d.D);
+  w.total = off;
+  return w;
+}
+
 size_t scan_bytes(const Dims& d) {
   return scan_ws_bytes(scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
                                  (int)d.k, (int)d.L, (int)d.esize));
@@ -264,6 +289,7 @@ size_t swimba_workspace_size(const swimba_dims* dims, int32_t call) {
     case SWIMBA_CALL_DECODE: return d.Bt == 0 ? 0 : dec_ws(d).total;
     case SWIMBA_CALL_SCAN_BACKWARD:
       return d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.N);
+    case SWIMBA_CALL_PROJECT_BACKWARD: return d.M == 0 ? 0 : pbwd_ws(d).total;
     default: return 0;
   }
 }
@@ -307,6 +333,66 @@ swimba_status swimba_expert_project_mix(const swimba_dims* dims, const void* u,
   return hip_status(run_project(d, d.M, u, w_experts, topk_idx, topk_w, B_hat, X_hat, C_mix,
                                 static_cast<unsigned char*>(ws), stream),
                     "expert_project_mix launch");
+}
+
+swimba_status swimba_expert_project_mix_backward(
+    const swimba_dims* dims, const void* u, const void* w_router, const void* w_experts,
+    const float* dB_hat, const float* dX_hat, const float* dC_mix, float* du, float* dW_router,
+    float* dW_experts, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if (d.M * d.k * d.D >= (int64_t(1) << 40) || d.M * d.k * d.W >= (int64_t(1) << 40))
+    return fail(SWIMBA_ERR_DIMS, "problem too large");
+  REQUIRE_PTR(dW_router);
+  REQUIRE_PTR(dW_experts);
+  if (d.M == 0) {
+    // no tokens: the weight gradients are zero
+    hipError_t e = launch_fill_zero(dW_router, (size_t)(d.E * d.D), stream);
+    if (e == hipSuccess) e = launch_fill_zero(dW_experts, (size_t)(d.E * d.W * d.D), stream);
+    return hip_status(e, "expert_project_mix_backward launch");
+  }
+  REQUIRE_PTR(u);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(w_experts);
+  REQUIRE_PTR(dB_hat);
+  REQUIRE_PTR(dX_hat);
+  REQUIRE_PTR(dC_mix);
+  REQUIRE_PTR(du);
+  const PbwdWs lay = pbwd_ws(d);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != SWIMBA_OK) return st;
+  unsigned char* w8 = static_cast<unsigned char*>(ws);
+  int32_t* idx = reinterpret_cast<int32_t*>(w8 + lay.idx);
+  float* tw = reinterpret_cast<float*>(w8 + lay.w);
+  float* logits = reinterpret_cast<float*>(w8 + lay.logits);
+  unsigned char* pws = w8 + lay.proj;
+  const ProjWs play = proj_ws(d);
+  // the forward's routing and weighted streams, recomputed with its own kernels
+  hipError_t e = launch_route(d.bf16, u, w_router, (int)d.M, (int)d.D, (int)d.E, (int)d.k, idx,
+                              tw, logits, stream);
+  if (e != hipSuccess) return hip_status(e, "expert_project_mix_backward route launch");
+  e = run_project(d, d.M, u, w_experts, idx, tw, w8 + lay.bhat, w8 + lay.xhat, nullptr, pws,
+                  stream);
+  if (e != hipSuccess) return hip_status(e, "expert_project_mix_backward projection launch");
+  ProjBwdArgs a{};
+  a.u = u; a.w_router = w_router; a.w_experts = w_experts;
+  a.idx = idx; a.topk_w = tw; a.dB = dB_hat; a.dX = dX_hat; a.dC = dC_mix;
+  a.du = du; a.dWr = dW_router; a.dW = dW_experts; a.logits = logits;
+  a.B_hat = w8 + lay.bhat;
+  a.c_part = reinterpret_cast<const float*>(pws + play.cpart);
+  a.sorted = reinterpret_cast<const int32_t*>(pws + play.sorted);
+  a.sorted_w = reinterpret_cast<const float*>(pws + play.sortw);
+  a.offsets = reinterpret_cast<const int32_t*>(pws + play.offsets);
+  a.dz = w8 + lay.dz;
+  a.sw = reinterpret_cast<float*>(w8 + lay.sw);
+  a.dg = reinterpret_cast<float*>(w8 + lay.dg);
+  a.du_part = reinterpret_cast<float*>(w8 + lay.dupart);
+  a.dwr_part = reinterpret_cast<float*>(w8 + lay.dwrpart);
+  a.M = (int)d.M; a.D = (int)d.D; a.E = (int)d.E; a.k = (int)d.k; a.W = (int)d.W;
+  a.HP = (int)d.HP; a.GN = (int)d.GN;
+  return hip_status(launch_project_backward(d.bf16, a, stream),
+                    "expert_project_mix_backward launch");
 }
 
 }  // extern "C"

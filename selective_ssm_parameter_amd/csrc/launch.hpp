@@ -74,15 +74,13 @@ hipError_t launch_mix_decay(const int32_t* idx, const float* w, const float* a_e
                             float* ld, int Bt, int T, int H, int E, int k, int L,
                             hipStream_t s);
 hipError_t launch_state_copy(const float* src, float* dst, size_t n, hipStream_t s);
+// dst[0 .. n) = 0 with a fill kernel (safe under stream capture).
+hipError_t launch_fill_zero(float* dst, size_t n, hipStream_t s);
 
-// Decode: in-place state update and readout for one token per sequence.
-// C~ is summed here from the per-slot fp32 parts c_part [Bt, k, G*N], in slot order.
 // Output projection out[M, N] = y[M, K] w_out[N, K]^T (out in the input type).
 hipError_t launch_output_project(bool is_bf16, int M, int K, int N, const void* y,
                                  const void* w_out, void* out, hipStream_t s);
 
-// a_experts non-null: the expert-mixed decay, a_t = sum_j w_j a_experts[idx_j]
-// / sum_j w_j from the routing (idx, w [Bt, k]); a is then not read.
 // Backward of the chunked scan (see swimba_ssd_chunk_scan_backward).
 size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int N);
 hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N, int k,
@@ -91,6 +89,43 @@ hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N
                                 const float* dh_final, float* dB, float* dX, float* dC, float* da,
                                 float* dh_init, void* ws, hipStream_t s);
 
+// Backward of the expert projections, the mix and the router (see
+// swimba_expert_project_mix_backward). The forward's routing (idx, topk_w,
+// logits), bucketing (sorted, sorted_w, offsets) and weighted streams (B_hat,
+// c_part) are recomputed by the caller; dz, sw, dg, du_part and dwr_part are
+// scratch of proj_bwd_splits(M) dW_r splits.
+struct ProjBwdArgs {
+  const void* u;          // [M, D] input type
+  const void* w_router;   // [E, D]
+  const void* w_experts;  // [E, W, D]
+  const int32_t* idx;     // [M, k]
+  const float* topk_w;    // [M, k]
+  const float* dB;        // [M, k, G*N] gradient of B_hat
+  const float* dX;        // [M, k, H*P] gradient of X_hat
+  const float* dC;        // [M, G*N] gradient of C~
+  float* du;              // [M, D]
+  float* dWr;             // [E, D]
+  float* dW;              // [E, W, D]
+  const float* logits;    // [M, E]
+  const void* B_hat;      // [M, k, G*N] stream type
+  const float* c_part;    // [M, k, G*N]
+  const int32_t* sorted;  // [M*k] pair ids grouped by expert
+  const float* sorted_w;  // [M*k]
+  const int32_t* offsets; // [E + 2]
+  void* dz;               // [M*k, W] input type, sorted order
+  float* sw;              // [M*k] w_j dw_j by pair id
+  float* dg;              // [M, E]
+  float* du_part;         // [M*k, D] by pair id
+  float* dwr_part;        // [nsplit, E, D]
+  int M, D, E, k, W, HP, GN, nsplit;
+};
+int proj_bwd_splits(int M);
+hipError_t launch_project_backward(bool is_bf16, ProjBwdArgs a, hipStream_t s);
+
+// Decode: in-place state update and readout for one token per sequence.
+// C~ is summed here from the per-slot fp32 parts c_part [Bt, k, G*N], in slot order.
+// a_experts non-null: the expert-mixed decay, a_t = sum_j w_j a_experts[idx_j]
+// / sum_j w_j from the routing (idx, w [Bt, k]); a is then not read.
 hipError_t launch_decode_state(bool is_bf16, int Bt, int H, int G, int N, int P, int k,
                                const void* B_hat, const void* X_hat, const float* c_part,
                                const float* a, float* h, void* y, hipStream_t s,

@@ -41,7 +41,7 @@ def lib():
 def test_exports_every_declared_symbol():
     L = lib()
     syms = declared_symbols()
-    assert len(syms) == 15, syms
+    assert len(syms) == 16, syms
     for s in syms:
         assert hasattr(L, s), f"{s} declared in swimba.h but not exported"
     assert set(syms) == set(sb.EXPORTS)
@@ -176,6 +176,36 @@ def test_mixed_decay_argument_checks():
     assert st == -4
     assert L.swimba_decode_step_mixed(ctypes.byref(good_dims(batch=0, seqlen=1)), None, None, None,
                                       None, None, None, None, None, 0, None) == 0
+
+
+def test_backward_argument_checks():
+    L = lib()
+    d = good_dims()
+    need = sb.swimba_workspace_size(d, sb.CALL_PROJECT_BACKWARD)
+    # at least dz ([pairs, W] bf16) and the per-pair du partials ([pairs, D] fp32)
+    pairs, Wd = 200 * 2, 4 * 64 + 2 * 32
+    assert need >= pairs * Wd * 2 + pairs * 128 * 4
+    assert sb.swimba_workspace_size(good_dims(seqlen=0), sb.CALL_PROJECT_BACKWARD) == 0
+
+    def pb(dims, u=FAKE, dwr=FAKE, dw=FAKE, du=FAKE, ws=FAKE, nb=1 << 40):
+        return L.swimba_expert_project_mix_backward(ctypes.byref(dims), u, FAKE, FAKE, FAKE, FAKE,
+                                                    FAKE, du, dwr, dw, ws, nb, None)
+
+    assert pb(d, dwr=None) == -1 and "dW_router is NULL" in L.swimba_last_error().decode()
+    assert pb(d, u=None) == -1 and "u is NULL" in L.swimba_last_error().decode()
+    assert pb(d, du=MISALIGNED) == -5
+    assert pb(d, nb=need - 1) == -4
+    assert pb(d, ws=None, nb=0) == -4
+    assert pb(good_dims(headdim=32)) == -3
+    assert pb(good_dims(top_k=5)) == -2
+    # the scan's backward: shape and pointer checks
+    st = L.swimba_ssd_chunk_scan_backward(ctypes.byref(good_dims(top_k=3)), FAKE, FAKE, FAKE, FAKE,
+                                          None, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                          1 << 40, None)
+    assert st == -3
+    st = L.swimba_ssd_chunk_scan_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                          None, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == -1 and "da is NULL" in L.swimba_last_error().decode()
 
 
 def test_empty_inputs_are_no_ops():
