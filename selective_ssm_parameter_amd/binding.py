@@ -315,3 +315,52 @@ def forward_mixed(dims: Dims, u, w_router, w_experts, a_experts, h_init=None,
     swimba_ssd_chunk_scan_mixed(dims, buf.B_hat, buf.X_hat, buf.C_mix, log_decay, h_init, buf.y,
                                 buf.h_final, buf.ws_scan, stream=stream)
     return buf
+
+
+@dataclasses.dataclass
+class Grads:
+    dB_hat: torch.Tensor
+    dX_hat: torch.Tensor
+    dC_mix: torch.Tensor
+    da: torch.Tensor
+    dh_init: torch.Tensor
+    du: torch.Tensor
+    dW_router: torch.Tensor
+    dW_experts: torch.Tensor
+    ws_scan: torch.Tensor | None
+    ws_project: torch.Tensor | None
+
+
+def alloc_grads(dims: Dims, device="cuda") -> Grads:
+    """Every output and workspace of one backward pass, allocated by torch (float32)."""
+    M = dims.batch * dims.seqlen
+    k, H, P, G, N, E, D = (dims.top_k, dims.nheads, dims.headdim, dims.ngroups, dims.dstate,
+                           dims.n_experts, dims.d_model)
+    Wd = H * P + 2 * G * N
+    f32 = torch.float32
+    ws_s, _ = workspace(dims, CALL_SCAN_BACKWARD, device)
+    ws_p, _ = workspace(dims, CALL_PROJECT_BACKWARD, device)
+    return Grads(
+        dB_hat=torch.empty(M, k, G, N, dtype=f32, device=device),
+        dX_hat=torch.empty(M, k, H, P, dtype=f32, device=device),
+        dC_mix=torch.empty(M, G, N, dtype=f32, device=device),
+        da=torch.empty(H, dtype=f32, device=device),
+        dh_init=torch.empty(dims.batch, H, N, P, dtype=f32, device=device),
+        du=torch.empty(M, D, dtype=f32, device=device),
+        dW_router=torch.empty(E, D, dtype=f32, device=device),
+        dW_experts=torch.empty(E, Wd, D, dtype=f32, device=device),
+        ws_scan=ws_s, ws_project=ws_p)
+
+
+def backward(dims: Dims, u, w_router, w_experts, a, h_init, dy, dh_final, fwd: Buffers,
+             grads: Grads | None = None, stream=None) -> Grads:
+    """Gradients of l(y, h_final) given dy and dh_final: the chunked scan's
+    backward on the forward's streams, then router, projection and mix."""
+    g = grads if grads is not None else alloc_grads(dims, u.device)
+    swimba_ssd_chunk_scan_backward(dims, fwd.B_hat, fwd.X_hat, fwd.C_mix, a, h_init, dy,
+                                   dh_final, g.dB_hat, g.dX_hat, g.dC_mix, g.da, g.dh_init,
+                                   g.ws_scan, stream=stream)
+    swimba_expert_project_mix_backward(dims, u, w_router, w_experts, g.dB_hat, g.dX_hat,
+                                       g.dC_mix, g.du, g.dW_router, g.dW_experts, g.ws_project,
+                                       stream=stream)
+    return g

@@ -130,7 +130,8 @@ __device__ __forceinline__ float load_tile_scaled(T* dst, int rows, int cols, co
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-  const float sc = mx > 0.f ? ldexpf(1.f, -(ilogbf(mx) + 1)) : 1.f;
+  // (the exponent is capped so that a subnormal maximum gives a finite scale)
+  const float sc = mx > 0.f ? ldexpf(1.f, min(-(ilogbf(mx) + 1), 126)) : 1.f;
   load_tile<T>(dst, rows, cols, src, gstride, valid, cvalid, [&](int r) { return f(r) * sc; });
   return sc;
 }

@@ -1,0 +1,229 @@
+"""The whole backward pass on the GPU (binding.backward: the chunked scan's
+backward on the forward's streams, then router, projections and mix) against
+the fp64 oracle's forward_backward, at small sizes and at the full prefill
+size the benchmark times.
+
+At the full size the oracle cannot run every head of every sequence, so the
+upstream gradient is sparse by construction: dy and dh_final are nonzero only
+on a few (sequence, head) pairs. Every other sequence's and head's gradient is
+then exactly zero (checked), and the oracle computes the rest one sequence at
+a time on those heads only. The projection's backward is also checked at full
+size with dense seeded upstream gradients, on sampled tokens and weight rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, check_routing, dev, host, run_forward, say, slice_err, tdt, upload
+from oracle import backward as ob
+from oracle import swimba as osw
+from selective_ssm_parameter_amd import binding as sb
+from selective_ssm_parameter_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def row_err(got, ref):
+    """max over rows of max_i |d_i| / max(|ref_i|, rms(ref row)); rows = last axis."""
+    got = np.asarray(got, np.float64).reshape(-1, ref.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    den = np.maximum(np.abs(ref), rms)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(got - ref) / den)) if ref.size else 0.0
+
+
+def run_chain(wl, inp, dy, dh_final):
+    d = upload(wl, inp)
+    dims = sb.dims_of(wl)
+    buf = run_forward(wl, d, logits=True)
+    dyd = dev(dy.reshape(wl.tokens, wl.nheads, wl.headdim), tdt(wl))
+    dhd = None if dh_final is None else dev(dh_final, torch.float32)
+    g = sb.backward(dims, d["u"], d["w_router"], d["w_experts"], d["a"], d["h_init"], dyd, dhd,
+                    buf)
+    torch.cuda.synchronize()
+    return buf, g
+
+
+def seeded_upstream(wl, seed_off=71):
+    rng = np.random.default_rng(wl.seed + seed_off)
+    dy = rng.standard_normal((wl.batch, wl.seqlen, wl.nheads, wl.headdim)).astype(np.float32)
+    if wl.dtype == synth.BF16:
+        dy = synth.round_bf16(dy)
+    dh = rng.standard_normal((wl.batch, wl.nheads, wl.dstate, wl.headdim)).astype(np.float32)
+    return dy, dh
+
+
+def W(name, seed, **kw):
+    base = dict(batch=2, seqlen=300, d_model=128, nheads=3, headdim=64, dstate=128, ngroups=1,
+                n_experts=4, top_k=2, chunk=64, dtype=synth.BF16, a_lo=0.9, a_hi=0.999)
+    base.update(kw)
+    return synth.small(name, seed, **base)
+
+
+SMALL = [
+    ("c1_f32", synth.WORKLOADS["c1"]),
+    ("bf16_h0", W("k1", 921, h_init_var=0.1)),
+    ("bf16_g2_n32_ragged", W("k2", 922, nheads=4, ngroups=2, dstate=32, seqlen=157, n_experts=6)),
+]
+
+
+@pytest.mark.parametrize("name,wl", SMALL, ids=[c[0] for c in SMALL])
+def test_backward_chain_small(name, wl):
+    say(f"[bwd_chain] {name} M={wl.tokens} E={wl.n_experts} k={wl.top_k} {wl.dtype}")
+    inp = synth.make_inputs(wl)
+    dy, dh = seeded_upstream(wl)
+    f64 = {k: (None if v is None else np.asarray(v, np.float64)) for k, v in inp.items()}
+    ref = ob.forward_backward(f64["u"], f64["w_router"], f64["w_experts"], f64["a"],
+                              f64["h_init"], dy.astype(np.float64), dh.astype(np.float64),
+                              nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
+                              dstate=wl.dstate, top_k=wl.top_k)
+    assert not ref["routing"].flagged.any()
+    buf, g = run_chain(wl, inp, dy, dh)
+    check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), ref["routing"], wl)
+    errs = {
+        "du": row_err(host(g.du), ref["du"].reshape(wl.tokens, -1)),
+        "dW_router": row_err(host(g.dW_router), ref["dW_router"]),
+        "dW_experts": row_err(host(g.dW_experts), ref["dW_experts"]),
+        "da": float(np.max(np.abs(host(g.da) - ref["da"])) / np.max(np.abs(ref["da"]))),
+        "dh_init": slice_err(host(g.dh_init), ref["dh_init"], (0, 1)),
+    }
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    tol = TOL[wl.dtype]
+    assert all(v < tol for v in errs.values()), errs
+
+
+def test_backward_chain_full_size():
+    """c2 at full size; dy and dh_final nonzero on heads (0, 11, 23) of
+    sequences 0 and 7 only."""
+    wl = synth.WORKLOADS["c2"]
+    seqs, heads = [0, 7], [0, 11, 23]
+    Bt, T, H, N, P, k = wl.batch, wl.seqlen, wl.nheads, wl.dstate, wl.headdim, wl.top_k
+    say(f"[bwd_chain] full size c2: M={wl.tokens} sequences {seqs} heads {heads}")
+    inp = synth.make_inputs(wl)
+    dy_all, dh_all = seeded_upstream(wl, 73)
+    dy = np.zeros_like(dy_all)
+    dh = np.zeros_like(dh_all)
+    for b in seqs:
+        dy[b][:, heads] = dy_all[b][:, heads]
+        dh[b][heads] = dh_all[b][heads]
+    buf, g = run_chain(wl, inp, dy, dh)
+    M = wl.tokens
+    u64 = np.asarray(inp["u"], np.float64).reshape(M, -1)
+    wr64 = np.asarray(inp["w_router"], np.float64)
+    we64 = np.asarray(inp["w_experts"], np.float64)
+    a64 = np.asarray(inp["a"], np.float64)
+    r = osw.route(u64, wr64, k)
+    flips = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), r, wl)
+    assert flips.size == 0
+    gB = host(g.dB_hat).reshape(Bt, T, k, 1, N)
+    gX = host(g.dX_hat).reshape(Bt, T, k, H, P)
+    gC = host(g.dC_mix).reshape(Bt, T, 1, N)
+    other = [b for b in range(Bt) if b not in seqs]
+    rest = [h for h in range(H) if h not in heads]
+    # nothing reaches the sequences and heads without an upstream gradient
+    assert np.all(gB[other] == 0) and np.all(gX[other] == 0) and np.all(gC[other] == 0)
+    assert np.all(gX[seqs][:, :, :, rest] == 0)
+    assert np.all(host(g.da)[rest] == 0)
+    assert np.all(host(g.dh_init)[other] == 0) and np.all(host(g.dh_init)[seqs][:, rest] == 0)
+    # per sequence: the oracle's recurrence backward on the selected heads
+    da_ref = np.zeros(len(heads))
+    HP = H * P
+    xrows = np.concatenate([np.arange(h * P, (h + 1) * P) for h in heads])
+    keep = np.concatenate([xrows, np.arange(HP, we64.shape[1])])
+    du_ref = np.zeros((M, wl.d_model))
+    dW_ref = np.zeros((wl.n_experts, keep.size, wl.d_model))
+    dWr_ref = np.zeros_like(wr64)
+    worst = {}
+
+    def upd(key, v):
+        worst[key] = max(worst.get(key, 0.0), v)
+
+    for b in seqs:
+        rows = slice(b * T, (b + 1) * T)
+        rb = osw.Routing(logits=r.logits[rows], pi=r.pi[rows], idx=r.idx[rows], w=r.w[rows],
+                         margin=r.margin[rows])
+        s = osw.expert_streams(u64[rows], we64, rb.idx, H, P, wl.ngroups, N, heads=heads)
+        B_hat, X, C_mix = osw.mix_streams(s, rb.w)
+        h0 = None if inp["h_init"] is None else np.asarray(inp["h_init"], np.float64)[b:b + 1, heads]
+        dB, dX, dC, da, dh0 = ob.recurrence_backward(
+            B_hat, X, C_mix, a64[heads], h0, dy[b][:, heads].astype(np.float64),
+            dh[b:b + 1, heads].astype(np.float64), 1, T)
+        da_ref += da
+        upd("dB_hat", slice_err(gB[b:b + 1].reshape(1, T * k, 1, N), dB.reshape(1, T * k, 1, N)))
+        upd("dX_hat", slice_err(gX[b:b + 1][:, :, :, heads].reshape(1, T * k, len(heads), P),
+                                dX.reshape(1, T * k, len(heads), P)))
+        upd("dC_mix", slice_err(gC[b:b + 1], dC.reshape(1, T, 1, N)))
+        upd("dh_init", slice_err(host(g.dh_init)[b:b + 1, heads], dh0, (0, 1)))
+        # router, projection and mix: only the selected heads' X rows carry a
+        # gradient, so the oracle runs on those rows of W_exp (exact for du)
+        dBs, dCs, dw = ob.mix_backward(s, rb.w, dB, dC)
+        du_p, dW = ob.project_backward(u64[rows], we64[:, keep], rb.idx, dX, dBs, dCs)
+        du_r, dWr, _ = ob.route_backward(u64[rows], wr64, rb, dw)
+        du_ref[rows] = du_p + du_r
+        dW_ref += dW
+        dWr_ref += dWr
+    upd("da", float(np.max(np.abs(host(g.da)[heads] - da_ref)) / np.max(np.abs(da_ref))))
+    gdu = host(g.du)
+    upd("du", row_err(gdu[np.r_[tuple(slice(b * T, (b + 1) * T) for b in seqs)]],
+                      du_ref[np.r_[tuple(slice(b * T, (b + 1) * T) for b in seqs)]]))
+    assert np.all(gdu.reshape(Bt, T, -1)[other] == 0)
+    gW = host(g.dW_experts)
+    upd("dW_experts", row_err(gW[:, keep], dW_ref))
+    assert np.all(np.delete(gW, keep, axis=1) == 0)
+    upd("dW_router", row_err(host(g.dW_router), dWr_ref))
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    assert all(v < TOL[wl.dtype] for v in worst.values()), worst
+
+
+def test_project_backward_full_size_dense():
+    """c2's router, projection and mix backward with dense seeded upstream
+    gradients: du on sampled tokens, dW_experts on sampled rows, dW_router
+    whole."""
+    wl = synth.WORKLOADS["c2"]
+    M, k, H, G, N, P, D, E = (wl.tokens, wl.top_k, wl.nheads, wl.ngroups, wl.dstate,
+                              wl.headdim, wl.d_model, wl.n_experts)
+    HP, GN = H * P, G * N
+    say(f"[proj_bwd] full size c2 dense: M={M} pairs={M * k}")
+    inp = synth.make_inputs(wl)
+    rng = np.random.default_rng(wl.seed + 79)
+    dB = rng.standard_normal((M, k, G, N)).astype(np.float32)
+    dX = rng.standard_normal((M, k, H, P)).astype(np.float32)
+    dC = rng.standard_normal((M, G, N)).astype(np.float32)
+    dims = sb.dims_of(wl)
+    dt = tdt(wl)
+    f32 = torch.float32
+    du = torch.empty(M, D, dtype=f32, device="cuda")
+    dWr = torch.empty(E, D, dtype=f32, device="cuda")
+    dW = torch.empty(E, HP + 2 * GN, D, dtype=f32, device="cuda")
+    ws, _ = sb.workspace(dims, sb.CALL_PROJECT_BACKWARD)
+    sb.swimba_expert_project_mix_backward(
+        dims, dev(np.reshape(inp["u"], (M, D)), dt), dev(inp["w_router"], dt),
+        dev(inp["w_experts"], dt), dev(dB, f32), dev(dX, f32), dev(dC, f32), du, dWr, dW, ws)
+    torch.cuda.synchronize()
+    u64 = np.asarray(inp["u"], np.float64).reshape(M, D)
+    wr64 = np.asarray(inp["w_router"], np.float64)
+    we64 = np.asarray(inp["w_experts"], np.float64)
+    r = osw.route(u64, wr64, k)
+    assert not r.flagged.any()
+    # B and C streams of every pair (for dw and so dg of every token)
+    s = osw.expert_streams(u64, we64, r.idx, H, P, G, N, heads=np.zeros(0, np.int64))
+    dBs, dCs, dw = ob.mix_backward(s, r.w, dB.astype(np.float64), dC.astype(np.float64))
+    du_r, dWr_ref, _ = ob.route_backward(u64, wr64, r, dw)
+    worst = {"dW_router": row_err(host(dWr), dWr_ref)}
+    # du on sampled tokens (every term of a token's du is the token's own)
+    toks = np.unique(np.r_[0, 1, 2047, 2048, 8191, rng.integers(0, M, 60), M - 1])
+    du_p, _ = ob.project_backward(u64[toks], we64, r.idx[toks], dX[toks].astype(np.float64),
+                                  dBs[toks], dCs[toks])
+    worst["du"] = row_err(host(du)[toks], du_p + du_r[toks])
+    # dW rows of head 5's X, and the first 8 rows of B and of C
+    h, n8 = 5, 8
+    keep = np.r_[np.arange(h * P, (h + 1) * P), HP + np.arange(n8), HP + GN + np.arange(n8)]
+    _, dW_sub = ob.project_backward(u64, we64[:, keep], r.idx,
+                                    dX[:, :, h:h + 1].astype(np.float64),
+                                    dBs[..., :n8], dCs[..., :n8])
+    worst["dW_experts"] = row_err(host(dW)[:, keep], dW_sub)
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    assert all(v < TOL[wl.dtype] for v in worst.values()), worst
