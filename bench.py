@@ -42,6 +42,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "selective_ssm_parameter_amd", "csrc")
 # Kernel symbol pattern -> the name the library's profiler gives the launch.
 KERNEL_NAMES = [
+    (r"pbwd_dz_kernel", "proj_bwd_dz"),
+    (r"pbwd_router_kernel", "proj_bwd_router"),
+    (r"pbwd_gemm_kernel.*Li0EEE", "proj_bwd_du"),
+    (r"pbwd_gemm_kernel.*Li1EEE", "proj_bwd_dw"),
+    (r"pbwd_du_sum_kernel", "proj_bwd_du_sum"),
+    (r"pbwd_dwr_kernel|pbwd_dwr_sum_kernel", "proj_bwd_dwr"),
+    (r"bwd_local_kernel", "scan_bwd_local"),
+    (r"bwd_sweep_kernel", "scan_bwd_sweep"),
+    (r"bwd_grad_kernel", "scan_bwd_grad"),
+    (r"bwd_da_kernel", "scan_bwd_da"),
     (r"route_kernel", "route_topk"),
     (r"bucket_count_kernel", "bucket_count"),
     (r"bucket_place_kernel", "bucket_place"),
@@ -66,6 +76,9 @@ KERNEL_SOURCES = {
     "scan_chunk_output": ["scan.hip"],
     "decode_state": ["decode.hip"],
     "mix_decay": ["decay.hip"],
+    "scan_bwd_grad": ["scan_bwd.hip"],
+    "proj_bwd_du": ["proj_bwd.hip"],
+    "proj_bwd_dw": ["proj_bwd.hip"],
 }
 
 
@@ -86,10 +99,18 @@ def source_digest(kernel):
     return h.hexdigest()[:16]
 
 
-def profile_key(wl_name, decay="shared"):
+def profile_key(wl_name, decay="shared", backward=False):
     """Name of a workload's profile summaries: the expert-mixed decay runs
-    other kernels (or the same ones with other work) and has its own."""
-    return wl_name + ("_mixed" if decay == "mixed" else "")
+    other kernels (or the same ones with other work) and has its own, and so
+    does the training step (forward + backward)."""
+    return wl_name + ("_mixed" if decay == "mixed" else "") + ("_train" if backward else "")
+
+
+def parse_key(key):
+    """(workload name, mixed, backward) of a profile key."""
+    backward = key.endswith("_train")
+    key = key.removesuffix("_train")
+    return key.removesuffix("_mixed"), key.endswith("_mixed"), backward
 
 
 def traffic_file(key):
@@ -177,6 +198,53 @@ def decode_models(wl, mixed=False):
     }
 
 
+def backward_models(wl):
+    """Algorithmic work per launch for one training step of prefill ``wl``:
+    the forward's kernels (kernel_models) and the backward's. Scan backward
+    per (chunk of L tokens, head), R = k L (token, slot) pairs, products
+    restricted to causal pairs counted at half the dense cost:
+      local:  S = B_hat^T X (2NPR), R = C~^T dy (2NPL)
+      grad:   Gm = C~ B_hat^T (LRN, once per group), D = dy X^T (LRP),
+              dX (PRL + 2PRN), dB_hat (NRL + 2NRP), dC~ (NLR + 2NLP)
+    bytes: the streams and dy read once, the two chunk-state sets [nc, H, N, P]
+    fp32 written by local, read and written by the sweep, read by grad, and
+    the fp32 gradients written once. Projection backward: two grouped GEMMs of
+    2 (pairs) W D flops each."""
+    M, D, E, k = wl.tokens, wl.d_model, wl.n_experts, wl.top_k
+    H, P, N, G = wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    W, HP, GN = wl.width, H * P, G * N
+    ei = 2 if wl.dtype == "bf16" else 4
+    es = 2 if wl.dtype == "bf16" else 4
+    pairs = M * k
+    L = 64 if wl.dtype == "bf16" else 32
+    nch = wl.batch * -(-wl.seqlen // L)          # chunks over the batch
+    R = k * L
+    states = nch * H * N * P * 4                  # one chunk-state set, fp32
+    streams = pairs * (HP + GN) * es + M * GN * es
+    dy = M * HP * ei
+    grad_flops = nch * (G * L * R * N + H * (L * R * P + P * R * L + 2 * P * R * N + N * R * L
+                                             + 2 * N * R * P + N * L * R + 2 * N * L * P))
+    models = dict(kernel_models(wl))
+    models.update({
+        "scan_bwd_local": ("hbm", nch * H * (2 * N * P * R + 2 * N * P * L),
+                           streams + dy + 2 * states),
+        "scan_bwd_sweep": ("hbm", 0, 4 * states),
+        "scan_bwd_grad": ("hbm", grad_flops,
+                          streams + dy + 2 * states + pairs * (HP + GN) * 4 + M * GN * 4),
+        "proj_bwd_dz": ("hbm", 0, pairs * (HP + GN) * 4 + M * GN * 4 + pairs * GN * (es + 4)
+                        + pairs * W * ei + pairs * 8),
+        "proj_bwd_router": ("hbm", 2 * M * E * D, M * E * 4 + pairs * 8 + E * D * ei
+                            + M * D * 4 + M * E * 4),
+        "proj_bwd_du": ("mfma", 2 * pairs * W * D, pairs * W * ei + E * W * D * ei
+                        + pairs * D * 4),
+        "proj_bwd_du_sum": ("hbm", 0, pairs * D * 4 + 2 * M * D * 4),
+        "proj_bwd_dw": ("mfma", 2 * pairs * W * D, pairs * W * ei + pairs * D * ei
+                        + E * W * D * 4),
+        "proj_bwd_dwr": ("hbm", 2 * M * E * D, M * E * 4 + M * D * ei + E * D * 4),
+    })
+    return models
+
+
 def run_gpu(args):
     import torch
 
@@ -194,6 +262,7 @@ def run_gpu(args):
 
     wr, we, a = up(inp["w_router"]), up(inp["w_experts"]), up(inp["a"], torch.float32)
     mixed = getattr(args, "decay", "shared") == "mixed"
+    backward = getattr(args, "backward", False)
     a_exp = up(synth.expert_decays(wl), torch.float32) if mixed else None
     if not is_decode(wl):
         u = up(inp["u"].reshape(wl.tokens, -1))
@@ -223,8 +292,17 @@ def run_gpu(args):
     else:
         log_decay = (torch.empty(wl.batch, wl.nheads, wl.seqlen, dtype=torch.float32, device=dev)
                      if mixed else None)
+        if backward:
+            dy = up(synth.output_gradient(wl))
+            grads = sb.alloc_grads(dims, dev)
 
         def step():
+            if backward:
+                # training step: the prefill forward, then every gradient of
+                # <dy, y> (u, W_r, W_exp, a, the initial state)
+                sb.forward(dims, u, wr, we, a, None, buf)
+                sb.backward(dims, u, wr, we, a, None, dy, None, buf, grads)
+                return
             # prefill the batch, then decode one more token of every sequence,
             # updating the prefill's final state in place
             if mixed:
@@ -248,7 +326,7 @@ def run_gpu(args):
     sb.profile_enable(False)
     if is_decode(wl):  # the library names decode launches decode_<kernel>
         report = {n[len("decode_"):]: r for n, r in report.items() if n.startswith("decode_")}
-    models = kernel_models(wl, mixed)
+    models = backward_models(wl) if backward else kernel_models(wl, mixed)
     kernels = {n: {"launches": r["launches"], "avg_us": 1e3 * r["ms"] / r["launches"]}
                for n, r in report.items()}
     dom = max((n for n in models if n in report), key=lambda n: report[n]["ms"])
@@ -287,7 +365,7 @@ def run_gpu(args):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    tokens = wl.batch if is_decode(wl) else wl.tokens + wl.batch
+    tokens = wl.batch if is_decode(wl) else wl.tokens if backward else wl.tokens + wl.batch
     value = tokens * args.steps / elapsed
     bound, flops, nbytes = models[dom]
     avg_s = rep_dom[dom]["ms"] / rep_dom[dom]["launches"] / 1e3
@@ -296,13 +374,15 @@ def run_gpu(args):
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": stored_traffic(dom, profile_key(wl.name, "mixed" if mixed else "shared")),
+                "traffic": stored_traffic(dom, profile_key(wl.name, "mixed" if mixed else "shared",
+                                                           backward)),
                 "algorithmic_flops": flops, "avg_us": avg_s * 1e6}
     else:
         achieved = nbytes / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "traffic": stored_traffic(dom, profile_key(wl.name, "mixed" if mixed else "shared")),
+                "traffic": stored_traffic(dom, profile_key(wl.name, "mixed" if mixed else "shared",
+                                                           backward)),
                 "algorithmic_bytes": nbytes, "avg_us": avg_s * 1e6}
     res = {
         "wl": wl, "value": value, "elapsed": elapsed, "kernels": kernels, "roofline": roof,
@@ -475,6 +555,36 @@ def cpu_baseline(wl, budget_s=20.0, mixed=False):
                       f"prefill only, {spent:.1f} s"}
 
 
+def cpu_baseline_backward(wl, budget_s=20.0):
+    """The fp64 oracle's forward + backward (forward_backward) on prefixes of
+    sequence 0 (128, 256, ... tokens, all heads), until ``budget_s`` is used."""
+    from oracle import backward as ob
+    from selective_ssm_parameter_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    inp = synth.make_inputs(wl)
+    dy = synth.output_gradient(wl).reshape(wl.batch, wl.seqlen, wl.nheads, wl.headdim)
+    done, spent, T, runs = 0, 0.0, 128, []
+    while spent < budget_s:
+        T = min(T, wl.seqlen)
+        t0 = time.perf_counter()
+        ob.forward_backward(inp["u"][:1, :T], inp["w_router"], inp["w_experts"], inp["a"], None,
+                            dy[:1, :T], None, nheads=wl.nheads, headdim=wl.headdim,
+                            ngroups=wl.ngroups, dstate=wl.dstate, top_k=wl.top_k)
+        spent += time.perf_counter() - t0
+        done += T
+        runs.append(T)
+        if T == wl.seqlen:
+            break
+        T *= 2
+    return {"value": done / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"forward + backward of the first {', '.join(map(str, runs))} tokens of "
+                      f"sequence 0, all heads, {spent:.1f} s"}
+
+
 def cpu_baseline_decode(wl, budget_s, mixed=False):
     """The fp64 oracle's decode step on growing slices of the batch (all
     heads, the workload's initial state) until ``budget_s`` is used."""
@@ -533,8 +643,10 @@ def summarize_trace(trace_dir, wl_name, out, command, bench_json=None):
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     total = sum(sum(v) for v in groups.values())
     stats = find_csv(trace_dir, "kernel_stats.csv")
-    base, mixed = wl_name.removesuffix("_mixed"), wl_name.endswith("_mixed")
-    kind = "decode steps" if is_decode(workload(base)) else "bench step (prefill + decode)"
+    base, mixed, backward = parse_key(wl_name)
+    kind = ("decode steps" if is_decode(workload(base)) else
+            "training step (prefill forward + backward)" if backward else
+            "bench step (prefill + decode)")
     what = f"workload {base}" + (", expert-mixed decay" if mixed else "")
     lines = [f"# Kernel durations, {kind} on {what}", "",
              "Command (from the repository root, after building the library):", "",
@@ -592,11 +704,12 @@ def summarize_pmc(fetch_dir, write_dir, wl_name, out, commands):
         res[counter] = (kib, scale, {k: sum(v) / len(v) for k, v in by.items()})
     fk, fs, fetch = res["FETCH_SIZE"]
     wk, ws_, write = res["WRITE_SIZE"]
-    base, mixed = wl_name.removesuffix("_mixed"), wl_name.endswith("_mixed")
+    base, mixed, backward = parse_key(wl_name)
     wl = workload(base)
-    models = kernel_models(wl, mixed)
+    models = backward_models(wl) if backward else kernel_models(wl, mixed)
     what = f"workload {base}" + (", expert-mixed decay" if mixed else "")
-    lines = [f"# HBM traffic per launch, bench step on {what}", "",
+    step = "training step" if backward else "bench step"
+    lines = [f"# HBM traffic per launch, {step} on {what}", "",
              "Commands (from the repository root, after building the library):", ""]
     lines += ["    " + c for c in commands]
     lines += ["",
@@ -605,6 +718,9 @@ def summarize_pmc(fetch_dir, write_dir, wl_name, out, commands):
               f"and WRITE_SIZE {wk:.0f} KiB (scale {ws_:.4f}). Counter KiB x 1024 x scale "
               "= bytes.", "",
               ("Every launch is a decode step's." if is_decode(wl) else
+               "The forward's kernels launch twice per step (the backward recomputes the "
+               "routing and the projection); the algorithmic bytes are per launch."
+               if backward else
                "Launches on the larger grid are the prefill's, those on the smaller one the "
                "decode step's; the algorithmic bytes are those of the prefill launch."), "",
               "| kernel | workgroups | read MB | written MB | traffic MB | algorithmic MB |",
@@ -637,6 +753,8 @@ def main():
     ap.add_argument("--decay", default="shared", choices=["shared", "mixed"],
                     help="mixed: the expert-mixed diagonal transition (per-expert decays "
                          "mixed per token) instead of one shared decay per head")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training step: the prefill forward and the whole backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with copies of known size (scales HBM counters)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -652,7 +770,7 @@ def main():
     ap.add_argument("--command", action="append", default=[],
                     help="the command(s) that produced the profile, for the summary")
     args = ap.parse_args()
-    key = profile_key(args.config, args.decay)
+    key = profile_key(args.config, args.decay, args.backward)
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, key,
                         args.out or os.path.join(PROFILES, f"swimba_step_{key}_kernel_trace.md"),
@@ -664,6 +782,9 @@ def main():
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if args.backward and (args.decay != "shared" or is_decode(workload(args.config))):
+        print(json.dumps({"error": "--backward times prefill workloads with the shared decay"}))
         sys.exit(2)
     if args.e_sweep:
         e_sweep(args)
@@ -687,7 +808,12 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
-            "workload": ((f"Swimba recurrent decode step, {wl.dtype}: batch {wl.batch}, "
+            "workload": ((f"Swimba mixer training step (prefill forward + backward to u, W_r, "
+                          f"W_exp, a, h_init), {wl.dtype}: batch {wl.batch}, T={wl.seqlen}, "
+                          f"d_model={wl.d_model}, heads={wl.nheads}, P={wl.headdim}, "
+                          f"N={wl.dstate}, E={wl.n_experts}, top-k={wl.top_k}, chunk {wl.chunk}")
+                         if args.backward else
+                         (f"Swimba recurrent decode step, {wl.dtype}: batch {wl.batch}, "
                          f"one token per sequence per step, d_model={wl.d_model}, "
                          f"heads={wl.nheads}, P={wl.headdim}, N={wl.dstate} fp32 state per "
                          f"head in HBM, E={wl.n_experts}, top-k={wl.top_k}")
@@ -707,7 +833,8 @@ def main():
     if "step_roofline" in r:
         out["step_roofline"] = r["step_roofline"]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, mixed=args.decay == "mixed")
+        out["cpu_baseline"] = (cpu_baseline_backward(wl) if args.backward else
+                               cpu_baseline(wl, mixed=args.decay == "mixed"))
     print(json.dumps(out), flush=True)
 
 

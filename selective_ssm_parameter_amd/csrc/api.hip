@@ -288,7 +288,7 @@ size_t swimba_workspace_size(const swimba_dims* dims, int32_t call) {
     case SWIMBA_CALL_SCAN: return scan_bytes(d);
     case SWIMBA_CALL_DECODE: return d.Bt == 0 ? 0 : dec_ws(d).total;
     case SWIMBA_CALL_SCAN_BACKWARD:
-      return d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.N);
+      return d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.k);
     case SWIMBA_CALL_PROJECT_BACKWARD: return d.M == 0 ? 0 : pbwd_ws(d).total;
     default: return 0;
   }
@@ -485,7 +485,7 @@ swimba_status swimba_ssd_chunk_scan_backward(const swimba_dims* dims, const void
     REQUIRE_PTR(dC_mix);
   }
   const size_t need =
-      d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.N);
+      d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.k);
   if ((st = check_ws(ws, ws_bytes, need)) != SWIMBA_OK) return st;
   return hip_status(launch_scan_backward(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.G,
                                          (int)d.N, (int)d.k, B_hat, X_hat, C_mix, dy, a, h_init,

@@ -82,7 +82,7 @@ hipError_t launch_output_project(bool is_bf16, int M, int K, int N, const void* 
                                  const void* w_out, void* out, hipStream_t s);
 
 // Backward of the chunked scan (see swimba_ssd_chunk_scan_backward).
-size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int N);
+size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int G, int N, int k);
 hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N, int k,
                                 const void* B_hat, const void* X_hat, const void* C_mix,
                                 const void* dy, const float* a, const float* h_init,

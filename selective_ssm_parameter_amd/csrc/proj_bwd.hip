@@ -35,18 +35,31 @@ __global__ __launch_bounds__(256) void pbwd_dz_kernel(ProjBwdArgs A) {
   const int p = A.sorted[i], m = p / A.k;
   const float wj = A.sorted_w[i];
   T* row = static_cast<T*>(A.dz) + (size_t)i * A.W;
-  for (int c = lane; c < A.W; c += 64) {
-    float v;
-    if (c < A.HP) v = A.dX[(size_t)p * A.HP + c];
-    else if (c < A.HP + A.GN) v = wj * A.dB[(size_t)p * A.GN + (c - A.HP)];
-    else v = wj * A.dC[(size_t)m * A.GN + (c - A.HP - A.GN)];
-    row[c] = from_f32<T>(v);
+  // four columns per lane (H*P and G*N are multiples of 4, so a group of
+  // four never straddles the X | B | C boundaries)
+  for (int c = 4 * lane; c < A.W; c += 256) {
+    floatx4 v;
+    if (c < A.HP) {
+      v = *reinterpret_cast<const floatx4*>(A.dX + (size_t)p * A.HP + c);
+    } else if (c < A.HP + A.GN) {
+      v = *reinterpret_cast<const floatx4*>(A.dB + (size_t)p * A.GN + (c - A.HP)) * wj;
+    } else {
+      v = *reinterpret_cast<const floatx4*>(A.dC + (size_t)m * A.GN + (c - A.HP - A.GN)) * wj;
+    }
+    typename Vec<T>::x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(v[j]);
+    *reinterpret_cast<typename Vec<T>::x4*>(row + c) = o;
   }
   float sum = 0.f;
   const S* bh = static_cast<const S*>(A.B_hat) + (size_t)p * A.GN;
-  for (int n = lane; n < A.GN; n += 64)
-    sum += to_f32(bh[n]) * A.dB[(size_t)p * A.GN + n] +
-           A.c_part[(size_t)p * A.GN + n] * A.dC[(size_t)m * A.GN + n];
+  for (int n = 4 * lane; n < A.GN; n += 256) {
+    const floatx4 db = *reinterpret_cast<const floatx4*>(A.dB + (size_t)p * A.GN + n);
+    const floatx4 cp = *reinterpret_cast<const floatx4*>(A.c_part + (size_t)p * A.GN + n);
+    const floatx4 dc = *reinterpret_cast<const floatx4*>(A.dC + (size_t)m * A.GN + n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum += to_f32(bh[n + j]) * db[j] + cp[j] * dc[j];
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
   if (lane == 0) A.sw[p] = sum;
@@ -113,7 +126,7 @@ __global__ __launch_bounds__(256) void pbwd_router_kernel(ProjBwdArgs A) {
 // ---------------------------------------------------------------- grouped GEMMs
 
 // 128 x 128 output tiles, K steps of 32, four waves of 64 x 64 each. Tiles
-// are staged through LDS as 16-byte chunks (one stage, registers in between).
+// are staged through LDS as 16-byte chunks (registers in between).
 //   MODE 0 (du): rows = one expert's sorted pairs, columns = d, K = w:
 //     A(i, w) = dz[i][w] (rows of dz, k contiguous), B(w, d) = W^(e)[w][d].
 //   MODE 1 (dW): rows = w, columns = d, K = the expert's sorted pairs:
@@ -124,14 +137,52 @@ __global__ __launch_bounds__(256) void pbwd_router_kernel(ProjBwdArgs A) {
 constexpr int kGB = 128, kGK = 32;
 
 template <typename T, int MODE>
+struct GemmTiles {
+  static constexpr int ES = sizeof(T), EPC = 16 / ES;    // bytes, elements per 16-byte chunk
+  static constexpr int ACPR = MODE == 0 ? kGK / EPC : kGB / EPC;  // chunks per LDS row
+  static constexpr int BCPR = kGB / EPC;
+  static constexpr int PT = kGB * kGK / EPC / 256;       // chunks per thread and operand
+};
+
+// Global reads of the K step at k0 into registers (zeros outside the problem).
+template <typename T, int MODE>
+__device__ __forceinline__ void pbwd_fetch(const ProjBwdArgs& A, const T* dz, const T* we,
+                                           const T* u, int r0, int nrows, int c0, int kbeg,
+                                           int klen, int k0, int4v* va, int4v* vb) {
+  typedef GemmTiles<T, MODE> G;
+#pragma unroll
+  for (int it = 0; it < G::PT; ++it) {
+    const int q = threadIdx.x + 256 * it;
+    va[it] = int4v{0, 0, 0, 0};
+    vb[it] = int4v{0, 0, 0, 0};
+    if constexpr (MODE == 0) {
+      const int r = q / G::ACPR, kk = k0 + (q % G::ACPR) * G::EPC;
+      if (r < nrows && kk < klen)
+        va[it] = *reinterpret_cast<const int4v*>(dz + (size_t)(r0 + r) * A.W + kk);
+    } else {
+      const int r = q / G::ACPR, kk = k0 + r, w = r0 + (q % G::ACPR) * G::EPC;
+      if (kk < klen && w < A.W)
+        va[it] = *reinterpret_cast<const int4v*>(dz + (size_t)(kbeg + kk) * A.W + w);
+    }
+    const int r = q / G::BCPR, kk = k0 + r, d = c0 + (q % G::BCPR) * G::EPC;
+    if (kk < klen && d < A.D) {
+      if constexpr (MODE == 0) {
+        vb[it] = *reinterpret_cast<const int4v*>(we + (size_t)kk * A.D + d);
+      } else {
+        const int tok = A.sorted[kbeg + kk] / A.k;
+        vb[it] = *reinterpret_cast<const int4v*>(u + (size_t)tok * A.D + d);
+      }
+    }
+  }
+}
+
+template <typename T, int MODE>
 __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
   typedef typename Vec<T>::x8 F;
-  constexpr int ES = sizeof(T), EPC = 16 / ES;  // bytes, elements per 16-byte chunk
-  constexpr int ACPR = MODE == 0 ? kGK / EPC : kGB / EPC;  // chunks per LDS row
-  constexpr int BCPR = kGB / EPC;
-  constexpr int NCH = kGB * kGK / EPC;  // chunks per tile
-  __shared__ __align__(16) unsigned char As[kGB * kGK * ES];
-  __shared__ __align__(16) unsigned char Bs[kGB * kGK * ES];
+  typedef GemmTiles<T, MODE> G;
+  constexpr int ACPR = G::ACPR, BCPR = G::BCPR, PT = G::PT;
+  __shared__ __align__(16) unsigned char As[kGB * kGK * G::ES];
+  __shared__ __align__(16) unsigned char Bs[kGB * kGK * G::ES];
 
   const int E = A.E, D = A.D, W = A.W;
   const int ncol = (D + kGB - 1) / kGB;
@@ -177,35 +228,17 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // MODE 1 reads the next step's chunks during this step's products (its
+  // gathered rows of u take two dependent reads); MODE 0 reads them at the
+  // top of each step, which measured faster for it.
+  constexpr bool PF = MODE == 1;
+  int4v va[PT], vb[PT];
+  if (PF) pbwd_fetch<T, MODE>(A, dz, we, u, r0, nrows, c0, kbeg, klen, 0, va, vb);
   for (int k0 = 0; k0 < klen; k0 += kGK) {
-    int4v va[NCH / 256], vb[NCH / 256];
-#pragma unroll
-    for (int it = 0; it < NCH / 256; ++it) {
-      const int q = threadIdx.x + 256 * it;
-      va[it] = int4v{0, 0, 0, 0};
-      vb[it] = int4v{0, 0, 0, 0};
-      if constexpr (MODE == 0) {
-        const int r = q / ACPR, kk = k0 + (q % ACPR) * EPC;
-        if (r < nrows && kk < klen)
-          va[it] = *reinterpret_cast<const int4v*>(dz + (size_t)(r0 + r) * W + kk);
-      } else {
-        const int r = q / ACPR, kk = k0 + r, w = r0 + (q % ACPR) * EPC;
-        if (kk < klen && w < W)
-          va[it] = *reinterpret_cast<const int4v*>(dz + (size_t)(kbeg + kk) * W + w);
-      }
-      const int r = q / BCPR, kk = k0 + r, d = c0 + (q % BCPR) * EPC;
-      if (kk < klen && d < D) {
-        if constexpr (MODE == 0) {
-          vb[it] = *reinterpret_cast<const int4v*>(we + (size_t)kk * D + d);
-        } else {
-          const int tok = A.sorted[kbeg + kk] / A.k;
-          vb[it] = *reinterpret_cast<const int4v*>(u + (size_t)tok * D + d);
-        }
-      }
-    }
+    if (!PF) pbwd_fetch<T, MODE>(A, dz, we, u, r0, nrows, c0, kbeg, klen, k0, va, vb);
     __syncthreads();  // the previous step's fragments are read
 #pragma unroll
-    for (int it = 0; it < NCH / 256; ++it) {
+    for (int it = 0; it < PT; ++it) {
       const int q = threadIdx.x + 256 * it;
       {
         const int r = q / ACPR, ch = q % ACPR;
@@ -218,25 +251,31 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
       }
     }
     __syncthreads();
-    F bf[4];
+    if (PF && k0 + kGK < klen)
+      pbwd_fetch<T, MODE>(A, dz, we, u, r0, nrows, c0, kbeg, klen, k0 + kGK, va, vb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = load_kmajor<T, BCPR>(Bs, 0, wn * 64 + 16 * j, lane);
+    for (int ks = 0; ks < kGK; ks += 32) {
+      F bf[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      F af;
-      const int row = wm * 64 + 16 * i;
-      if constexpr (MODE == 0) {
-        // lane (g, c): k = 8g .. 8g + 7 of row row + c
-        const int r = row + cl;
-        if constexpr (ES == 2)
-          af = load8<T>(reinterpret_cast<const T*>(As + (r * ACPR + (g ^ swz_row<T, ACPR>(r))) * 16));
-        else
-          af = load8<T>(reinterpret_cast<const T*>(As + r * ACPR * 16 + 32 * g));
-      } else {
-        af = load_kmajor<T, ACPR>(As, 0, row, lane);
+      for (int j = 0; j < 4; ++j) bf[j] = load_kmajor<T, BCPR>(Bs, ks, wn * 64 + 16 * j, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        F af;
+        const int row = wm * 64 + 16 * i;
+        if constexpr (MODE == 0) {
+          // lane (g, c): k = ks + 8g .. ks + 8g + 7 of row row + c
+          const int r = row + cl;
+          if constexpr (G::ES == 2)
+            af = load8<T>(reinterpret_cast<const T*>(
+                As + (r * ACPR + (((ks >> 3) + g) ^ swz_row<T, ACPR>(r))) * 16));
+          else
+            af = load8<T>(reinterpret_cast<const T*>(As + r * ACPR * 16 + (ks + 8 * g) * 4));
+        } else {
+          af = load_kmajor<T, ACPR>(As, ks, row, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma16(af, bf[j], acc[i][j]);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma16(af, bf[j], acc[i][j]);
     }
   }
 
@@ -260,40 +299,53 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
 
 // ---------------------------------------------------------------- sums
 
-// du[m] += sum_j du_part[m, j] in slot order (pairs of out-of-range experts
-// contribute nothing).
+// du[m] += sum_j du_part[m, j] in slot order, four columns per thread.
 __global__ void pbwd_du_sum_kernel(ProjBwdArgs A) {
   const size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  if (q >= (size_t)A.M * A.D) return;
-  const size_t m = q / A.D, d = q % A.D;
-  float s = A.du[q];
-  for (int j = 0; j < A.k; ++j) {
-    const int e = A.idx[m * A.k + j];
-    if (e >= 0 && e < A.E) s += A.du_part[(m * A.k + j) * A.D + d];
-  }
-  A.du[q] = s;
+  const size_t D4 = A.D / 4;
+  if (q >= (size_t)A.M * D4) return;
+  const size_t m = q / D4, d = (q % D4) * 4;
+  floatx4 s = *reinterpret_cast<const floatx4*>(A.du + m * A.D + d);
+  for (int j = 0; j < A.k; ++j)
+    s = s + *reinterpret_cast<const floatx4*>(A.du_part + (m * A.k + j) * A.D + d);
+  *reinterpret_cast<floatx4*>(A.du + m * A.D + d) = s;
 }
 
-// dW_r partials: split sp of the tokens, thread d, experts in groups of 16.
+// dW_r partials over splits of kDwrTokens tokens: block (column tile of 64,
+// split); thread (sub, c) takes column c and every fourth token of the split
+// starting at sub, 16 experts at a time; the four subs are added in order.
+constexpr int kDwrTokens = 256;
+
 template <typename T>
-__global__ __launch_bounds__(256) void pbwd_dwr_kernel(ProjBwdArgs A, int per) {
-  const int d = blockIdx.x * 256 + threadIdx.x, sp = blockIdx.y;
-  if (d >= A.D) return;
-  const int m0 = sp * per, m1 = min(A.M, m0 + per);
+__global__ __launch_bounds__(256) void pbwd_dwr_kernel(ProjBwdArgs A) {
+  __shared__ float part[4][16][64];
+  const int c = threadIdx.x & 63, sub = threadIdx.x >> 6;
+  const int d = blockIdx.x * 64 + c, sp = blockIdx.y;
+  const int m0 = sp * kDwrTokens, m1 = min(A.M, m0 + kDwrTokens);
   const T* u = static_cast<const T*>(A.u);
   for (int e0 = 0; e0 < A.E; e0 += 16) {
     float acc[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    for (int m = m0; m < m1; ++m) {
-      const float uv = to_f32(u[(size_t)m * A.D + d]);
+    if (d < A.D) {
+#pragma unroll 4
+      for (int m = m0 + sub; m < m1; m += 4) {
+        const float uv = to_f32(u[(size_t)m * A.D + d]);
+        const float* dg = A.dg + (size_t)m * A.E + e0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (e0 + q < A.E) acc[q] += A.dg[(size_t)m * A.E + e0 + q] * uv;
+        for (int q = 0; q < 16; ++q)
+          if (e0 + q < A.E) acc[q] += dg[q] * uv;
+      }
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (e0 + q < A.E) A.dwr_part[((size_t)sp * A.E + e0 + q) * A.D + d] = acc[q];
+    for (int q = 0; q < 16; ++q) part[sub][q][c] = acc[q];
+    __syncthreads();
+    for (int q = sub; q < 16; q += 4) {
+      if (e0 + q < A.E && d < A.D)
+        A.dwr_part[((size_t)sp * A.E + e0 + q) * A.D + d] =
+            ((part[0][q][c] + part[1][q][c]) + part[2][q][c]) + part[3][q][c];
+    }
+    __syncthreads();
   }
 }
 
@@ -320,8 +372,6 @@ hipError_t launch_fill_zero(float* dst, size_t n, hipStream_t s) {
 
 // ---------------------------------------------------------------- launch
 
-constexpr int kDwrTokens = 512;  // tokens per dW_r split
-
 int proj_bwd_splits(int M) { return (M + kDwrTokens - 1) / kDwrTokens; }
 
 template <typename T, typename S>
@@ -340,7 +390,7 @@ static hipError_t launch_pbwd_t(const ProjBwdArgs& A, hipStream_t s) {
   hipLaunchKernelGGL((pbwd_gemm_kernel<T, 0>), dim3((unsigned)(ntr * ncol)), dim3(256), 0, s, A);
   prof_end(s);
   prof_begin("proj_bwd_du_sum", s);
-  hipLaunchKernelGGL(pbwd_du_sum_kernel, dim3((unsigned)(((size_t)A.M * A.D + 255) / 256)),
+  hipLaunchKernelGGL(pbwd_du_sum_kernel, dim3((unsigned)(((size_t)A.M * A.D / 4 + 255) / 256)),
                      dim3(256), 0, s, A);
   prof_end(s);
   const int nwt = (A.W + kGB - 1) / kGB;
@@ -349,8 +399,8 @@ static hipError_t launch_pbwd_t(const ProjBwdArgs& A, hipStream_t s) {
                      s, A);
   prof_end(s);
   prof_begin("proj_bwd_dwr", s);
-  hipLaunchKernelGGL(pbwd_dwr_kernel<T>, dim3((unsigned)((A.D + 255) / 256), (unsigned)A.nsplit),
-                     dim3(256), 0, s, A, kDwrTokens);
+  hipLaunchKernelGGL(pbwd_dwr_kernel<T>, dim3((unsigned)((A.D + 63) / 64), (unsigned)A.nsplit),
+                     dim3(256), 0, s, A);
   hipLaunchKernelGGL(pbwd_dwr_sum_kernel, dim3((unsigned)(((size_t)A.E * A.D + 255) / 256)),
                      dim3(256), 0, s, A);
   prof_end(s);

@@ -26,9 +26,17 @@
 // R_c = sum_s a^{s-c0} C~_s dy_s^T (matrix cores); a sequential sweep per
 // state element turning S into H_c (forwards: H_{c+1} = a^{Lc} H_c + S_c) and
 // R into F_c (backwards: F_{c-1} = a R_c + a^{Lc} F_c, ending at F_{-1} =
-// dh_init) in place; per (sequence, chunk, group) the gradients above on matrix cores,
-// the heads of the group visited in order so dB_hat and dC~ are summed over
-// them in registers (deterministic); a fixed-order sum of da.
+// dh_init) in place; per (sequence, chunk, group, slice of the group's heads)
+// the gradients above on matrix cores, the slice's heads visited in order so
+// dB_hat and dC~ are summed over them in registers, then (with several
+// slices) a fixed-order sum of the slices' parts; a fixed-order sum of da.
+// Everything is deterministic.
+//
+// LDS tiles are row-major with 16-byte chunks XOR-swizzled per row (the
+// swizzle of the transposing read): a contraction along a tile row is one
+// 16-byte read per fragment, one down a tile column is the transposing read.
+// Tiles come in with 16-byte global reads, all of a thread's reads issued
+// before the first is used; powers of the decay come from a per-head table.
 // Matrix-core operands are fp16 (fp32 for fp32 problems) with fp32
 // accumulation and fp32 outputs: the streams are fp16 already, and dy and the
 // states are scaled per (chunk, head) by a power of two that brings their
@@ -36,10 +44,12 @@
 // so the gradients keep fp16's precision whatever their range.
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_tiles.hpp"
 
 namespace swimba {
 
-constexpr int kBP = 64;  // head dim
+constexpr int kBP = 64;        // head dim
+constexpr int kGradWaves = 8;  // waves of the gradient kernel
 
 struct BwdArgs {
   const void* B_hat;    // [M, k, G, N] stream type
@@ -57,36 +67,165 @@ struct BwdArgs {
   float* S;             // [Bt, nb, H, N, P]: S_c, then H_c
   float* R;             // [Bt, nb, H, N, P]: R_c, then F_c
   float* da_part;       // [Bt, nb, H]
-  int T, H, G, N, k, nb;
+  float* dBp;           // [hs, M, k, G, N] slice parts (hs > 1)
+  float* dCp;           // [hs, M, G, N]
+  int T, H, G, N, k, nb, hs;
 };
 
-// One 16 x 16 tile D[m0.., n0..] += sum_k A(m, k) B(k, n) over k in [0, K)
-// (K a multiple of 32) from LDS: A(m, k) at A[m * am + k * ak], B(k, n) at
-// B[k * bk + n * bn]. AK1 / BK1: the contraction index is contiguous (one
-// 16-byte read per fragment), else eight element reads. Lane (g, c) gets
-// D[m0 + 4g + i][n0 + c].
-template <typename T, bool AK1, bool BK1>
-__device__ __forceinline__ floatx4 tile_mm(const T* A, int am, int ak, const T* B, int bk, int bn,
-                                           int m0, int n0, int K, floatx4 acc, int g, int c) {
-  typedef typename Vec<T>::x8 F;
+// ---------------------------------------------------------------- LDS tiles
+
+template <typename T, int CPR>
+__device__ __forceinline__ int chunk_off(int r, int j) {
+  return (r * CPR + (j ^ swz_tr<T, CPR>(r))) * 16;
+}
+template <typename T, int CPR>
+__device__ __forceinline__ int elem_off(int r, int col) {
+  constexpr int EPC = 16 / (int)sizeof(T);
+  return chunk_off<T, CPR>(r, col / EPC) + (col % EPC) * (int)sizeof(T);
+}
+template <typename T, int CPR>
+__device__ __forceinline__ float lds_get(const unsigned char* t, int r, int col) {
+  return to_f32(*reinterpret_cast<const T*>(t + elem_off<T, CPR>(r, col)));
+}
+template <typename T, int CPR>
+__device__ __forceinline__ void lds_put(unsigned char* t, int r, int col, float v) {
+  *reinterpret_cast<T*>(t + elem_off<T, CPR>(r, col)) = from_f32<T>(v);
+}
+
+// Fragment along tile rows: lane (g, c) gets row r0 + c, elements
+// k0 + 8g .. k0 + 8g + 7 (k0 a multiple of 32).
+template <typename T, int CPR>
+__device__ __forceinline__ typename Vec<T>::x8 frag_row(const unsigned char* t, int r0, int k0,
+                                                        int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const typename Vec<T>::x8*>(
+        t + chunk_off<T, CPR>(r0 + c, (k0 >> 3) + g));
+  } else {
+    const int j = (k0 + 8 * g) >> 2;
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(t + chunk_off<T, CPR>(r0 + c, j));
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(t + chunk_off<T, CPR>(r0 + c, j + 1));
+    return floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// One 16 x 16 tile: acc + sum over k < K (a multiple of 32) of A(m0 + i, k)
+// B(k, n0 + j). AROW: A(m, k) = At[m][k], else At[k][m]; BROW: B(k, n) =
+// Bt[n][k], else Bt[k][n]. Lane (g, c) gets D[m0 + 4g + i][n0 + c].
+template <typename T, bool AROW, int ACPR, bool BROW, int BCPR>
+__device__ __forceinline__ floatx4 tmm(const unsigned char* At, const unsigned char* Bt, int m0,
+                                       int n0, int K, int lane) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < K; k0 += 32) {
-    const int kk = k0 + 8 * g;
-    F fa, fb;
-    if constexpr (AK1) {
-      fa = load8<T>(A + (m0 + c) * am + kk);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fa[j] = A[(m0 + c) * am + (kk + j) * ak];
-    }
-    if constexpr (BK1) {
-      fb = load8<T>(B + kk + (n0 + c) * bn);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j] = B[(kk + j) * bk + (n0 + c) * bn];
-    }
+    typename Vec<T>::x8 fa, fb;
+    if constexpr (AROW) fa = frag_row<T, ACPR>(At, m0, k0, lane);
+    else fa = load_kmajor<T, ACPR>(At, k0, m0, lane);
+    if constexpr (BROW) fb = frag_row<T, BCPR>(Bt, n0, k0, lane);
+    else fb = load_kmajor<T, BCPR>(Bt, k0, n0, lane);
     acc = mma16(fa, fb, acc);
   }
   return acc;
+}
+
+template <typename SRC> struct Raw16;
+template <> struct Raw16<f16> { typedef f16x8 type; };
+template <> struct Raw16<bf16> { typedef bf16x8 type; };
+template <> struct Raw16<float> { typedef floatx4 type; };
+
+// Global -> LDS tile of ROWS x COLS elements of T from src (row stride
+// gstride elements), each scaled by f(row) * sc; rows >= valid and columns
+// >= cvalid (a multiple of 8) are zeros. 16-byte reads, all issued first.
+template <typename T, int ROWS, int COLS, int NT, typename SRC>
+struct TileLoad {
+  static constexpr int V = 16 / (int)sizeof(SRC);  // elements per read
+  static constexpr int RPR = COLS / V;             // reads per row
+  static constexpr int NV = ROWS * RPR;
+  static constexpr int IT = (NV + NT - 1) / NT;
+  static constexpr int CPR = COLS * (int)sizeof(T) / 16;
+  typedef typename Raw16<SRC>::type RV;
+  RV raw[IT];
+
+  __device__ __forceinline__ void fetch(const SRC* src, size_t gstride, int valid, int cvalid) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int q = threadIdx.x + NT * i;
+      const int r = q / RPR, c = (q % RPR) * V;
+      raw[i] = RV{};
+      if ((NV % NT == 0 || q < NV) && r < valid && c < cvalid)
+        raw[i] = *reinterpret_cast<const RV*>(src + (size_t)r * gstride + c);
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ float absmax(F f) const {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int q = threadIdx.x + NT * i;
+      if (NV % NT != 0 && q >= NV) continue;
+      const float s = f(q / RPR);
+#pragma unroll
+      for (int j = 0; j < V; ++j) mx = fmaxf(mx, fabsf(to_f32(raw[i][j]) * s));
+    }
+    return mx;
+  }
+  template <class F>
+  __device__ __forceinline__ void store(unsigned char* tile, F f, float sc) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int q = threadIdx.x + NT * i;
+      if (NV % NT != 0 && q >= NV) continue;
+      const int r = q / RPR, c = (q % RPR) * V;
+      const float s = f(r) * sc;
+      if constexpr (sizeof(T) == 2 && V == 8) {
+        typename Vec<T>::x8 o;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = from_f32<T>(to_f32(raw[i][j]) * s);
+        *reinterpret_cast<typename Vec<T>::x8*>(tile + chunk_off<T, CPR>(r, c / 8)) = o;
+      } else if constexpr (sizeof(T) == 2) {  // fp32 source: half a chunk
+        typename Vec<T>::x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(raw[i][j] * s);
+        *reinterpret_cast<typename Vec<T>::x4*>(tile + elem_off<T, CPR>(r, c)) = o;
+      } else {  // fp32 tile
+        floatx4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = to_f32(raw[i][j]) * s;
+        *reinterpret_cast<floatx4*>(tile + chunk_off<T, CPR>(r, c / 4)) = o;
+      }
+    }
+  }
+};
+
+template <typename T, int ROWS, int COLS, int NT, typename SRC, class F>
+__device__ __forceinline__ void tile_load(unsigned char* tile, const SRC* src, size_t gstride,
+                                          int valid, int cvalid, F f) {
+  TileLoad<T, ROWS, COLS, NT, SRC> L;
+  L.fetch(src, gstride, valid, cvalid);
+  L.store(tile, f, 1.f);
+}
+
+// tile_load with the tile scaled by the power of two that brings its largest
+// magnitude into [1/2, 1) (1 for an all-zero tile; the exponent is capped so
+// a subnormal maximum still gives a finite scale). Returns the scale. Every
+// thread of the workgroup calls it (two barriers; red: NT / 64 floats).
+template <typename T, int ROWS, int COLS, int NT, typename SRC, class F>
+__device__ __forceinline__ float tile_load_scaled(unsigned char* tile, const SRC* src,
+                                                  size_t gstride, int valid, int cvalid, F f,
+                                                  float* red) {
+  TileLoad<T, ROWS, COLS, NT, SRC> L;
+  L.fetch(src, gstride, valid, cvalid);
+  float mx = L.absmax(f);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
+  const float sc = mx > 0.f ? ldexpf(1.f, min(-(ilogbf(mx) + 1), 126)) : 1.f;
+  L.store(tile, f, sc);
+  return sc;
 }
 
 __device__ __forceinline__ float powi(float a, int d) {
@@ -98,53 +237,17 @@ __device__ __forceinline__ float powi(float a, int d) {
   return r;
 }
 
-// Row-major LDS copy of `rows` x `cols` elements (cols a multiple of 4) from
-// global rows of stride `gstride`, converted to T; rows >= valid and columns
-// >= cvalid are zeros; each element optionally scaled by f(row).
-template <typename T, typename SRC, class F>
-__device__ __forceinline__ void load_tile(T* dst, int rows, int cols, const SRC* src,
-                                          size_t gstride, int valid, int cvalid, F f) {
-  for (int q = threadIdx.x; q < rows * cols; q += blockDim.x) {
-    const int r = q / cols, cc = q - r * cols;
-    float v = 0.f;
-    if (r < valid && cc < cvalid) v = to_f32(src[(size_t)r * gstride + cc]) * f(r);
-    dst[q] = from_f32<T>(v);
-  }
-}
-
-// load_tile with the tile scaled by the power of two 2^-e that brings its
-// largest magnitude into [1/2, 1); returns the scale (1 for an all-zero tile).
-// Every thread of the workgroup must call it (two barriers; red: 4 floats).
-template <typename T, typename SRC, class F>
-__device__ __forceinline__ float load_tile_scaled(T* dst, int rows, int cols, const SRC* src,
-                                                  size_t gstride, int valid, int cvalid, F f,
-                                                  float* red) {
-  float mx = 0.f;
-  for (int q = threadIdx.x; q < rows * cols; q += blockDim.x) {
-    const int r = q / cols, cc = q - r * cols;
-    if (r < valid && cc < cvalid) mx = fmaxf(mx, fabsf(to_f32(src[(size_t)r * gstride + cc]) * f(r)));
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  // (the exponent is capped so that a subnormal maximum gives a finite scale)
-  const float sc = mx > 0.f ? ldexpf(1.f, min(-(ilogbf(mx) + 1), 126)) : 1.f;
-  load_tile<T>(dst, rows, cols, src, gstride, valid, cvalid, [&](int r) { return f(r) * sc; });
-  return sc;
-}
-
 // ---------------------------------------------------------------- local states
 
 template <typename T, typename S, typename TY, int NP, int KS, int BL>
 __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
-  constexpr int R = KS * BL;
-  __shared__ __align__(16) T Bs[R * NP];
-  __shared__ __align__(16) T Xd[R * kBP];
-  __shared__ __align__(16) T Cs[BL * NP];
-  __shared__ __align__(16) T Dyd[BL * kBP];
+  constexpr int R = KS * BL, ES = sizeof(T);
+  constexpr int CB = NP * ES / 16, CX = kBP * ES / 16;
+  __shared__ __align__(16) unsigned char Bs[R * NP * ES];
+  __shared__ __align__(16) unsigned char Xd[R * kBP * ES];
+  __shared__ __align__(16) unsigned char Cs[BL * NP * ES];
+  __shared__ __align__(16) unsigned char Dyd[BL * kBP * ES];
+  __shared__ float pw[BL + 1];
   __shared__ float red[4];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int H = A.H, G = A.G, N = A.N, Tl = A.T;
@@ -152,16 +255,19 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
   const int c0 = c * BL, Lc = min(BL, Tl - c0);
   const float a = A.a[h];
   const size_t m0 = (size_t)b * Tl + c0;  // first token row of the chunk
-  load_tile<T>(Bs, R, NP, static_cast<const S*>(A.B_hat) + (m0 * KS) * G * N + grp * N,
-               (size_t)G * N, Lc * KS, N, [](int) { return 1.f; });
-  load_tile<T>(Xd, R, kBP, static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP,
-               (size_t)H * kBP, Lc * KS, kBP, [&](int r) { return powi(a, Lc - 1 - r / KS); });
-  load_tile<T>(Cs, BL, NP, static_cast<const S*>(A.C_mix) + m0 * G * N + grp * N, (size_t)G * N,
-               Lc, N, [](int) { return 1.f; });
-  const float sdy = load_tile_scaled<T>(Dyd, BL, kBP,
-                                        static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP,
-                                        (size_t)H * kBP, Lc, kBP,
-                                        [&](int s) { return powi(a, s); }, red);
+  for (int d = threadIdx.x; d <= BL; d += 256) pw[d] = powi(a, d);
+  __syncthreads();
+  const auto one = [](int) { return 1.f; };
+  tile_load<T, R, NP, 256>(Bs, static_cast<const S*>(A.B_hat) + (m0 * KS) * G * N + grp * N,
+                           (size_t)G * N, Lc * KS, N, one);
+  tile_load<T, R, kBP, 256>(Xd, static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP,
+                            (size_t)H * kBP, Lc * KS, kBP,
+                            [&](int r) { return r < Lc * KS ? pw[Lc - 1 - r / KS] : 0.f; });
+  tile_load<T, BL, NP, 256>(Cs, static_cast<const S*>(A.C_mix) + m0 * G * N + grp * N,
+                            (size_t)G * N, Lc, N, one);
+  const float sdy = tile_load_scaled<T, BL, kBP, 256>(
+      Dyd, static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP, (size_t)H * kBP, Lc, kBP,
+      [&](int s) { return s < Lc ? pw[s] : 0.f; }, red);
   __syncthreads();
   const float udy = 1.f / sdy;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, cl = lane & 15;
@@ -171,10 +277,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
     const int n0 = 16 * (t / (kBP / 16)), p0 = 16 * (t % (kBP / 16));
     if (n0 >= N) continue;
     // S[n][p] = sum_r B_hat[r][n] xd[r][p];  R[n][p] = sum_s C~[s][n] dyd[s][p]
-    floatx4 s4 = tile_mm<T, false, false>(Bs, 1, NP, Xd, kBP, 1, n0, p0, R,
-                                          floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
-    floatx4 r4 = tile_mm<T, false, false>(Cs, 1, NP, Dyd, kBP, 1, n0, p0, BL,
-                                          floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+    const floatx4 s4 = tmm<T, false, CB, false, CX>(Bs, Xd, n0, p0, R, lane);
+    const floatx4 r4 = tmm<T, false, CB, false, CX>(Cs, Dyd, n0, p0, BL, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = n0 + 4 * g + i;
@@ -221,186 +325,258 @@ __global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdArgs A) {
 // ---------------------------------------------------------------- chunk gradients
 
 template <typename T, typename S, typename TY, int NP, int KS, int BL>
-__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs A) {
-  constexpr int R = KS * BL;
-  constexpr int NBT = (NP / 16) * (R / 16);   // dB_hat tiles of the chunk
+__global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
+  constexpr int NW = kGradWaves, NT = 64 * NW;
+  constexpr int R = KS * BL, ES = sizeof(T);
+  constexpr int CB = NP * ES / 16, CX = kBP * ES / 16, CG = R * ES / 16;
+  constexpr int NGT = (BL / 16) * (R / 16);   // Gm and D tiles
+  constexpr int NXT = (kBP / 16) * (R / 16);  // dX tiles
+  constexpr int NBT = (NP / 16) * (R / 16);   // dB_hat tiles
   constexpr int NCT = (NP / 16) * (BL / 16);  // dC~ tiles
-  __shared__ __align__(16) T Bs[R * NP];      // B_hat [r][n]
-  __shared__ __align__(16) T Cs[BL * NP];     // C~ [s][n]
-  __shared__ __align__(16) T Gm[BL * R];      // C~_s . B_hat_r
-  __shared__ __align__(16) T Xs[R * kBP];     // X_r of the head
-  __shared__ __align__(16) T Dys[BL * kBP];   // dy_s of the head
-  __shared__ __align__(16) T Dm[BL * R];      // masked, decayed D
-  __shared__ __align__(16) T GmM[BL * R];     // masked, decayed Gm
-  __shared__ __align__(16) T Ss[NP * kBP];    // F_c, then H_c, of the head
-  __shared__ float red[4];
-  __shared__ float redm[4];
+  constexpr int GI = (NGT + NW - 1) / NW, BI = (NBT + NW - 1) / NW, CI = (NCT + NW - 1) / NW;
+  __shared__ __align__(16) unsigned char Bs[R * NP * ES];    // B_hat [r][n]
+  __shared__ __align__(16) unsigned char Cs[BL * NP * ES];   // C~ [s][n]
+  __shared__ __align__(16) unsigned char Xs[R * kBP * ES];   // X_r of the head [r][p]
+  __shared__ __align__(16) unsigned char Dys[BL * kBP * ES]; // dy_s of the head [s][p]
+  __shared__ __align__(16) unsigned char Dm[BL * R * ES];    // masked, decayed D [s][r]
+  __shared__ __align__(16) unsigned char GmM[BL * R * ES];   // masked, decayed Gm [s][r]
+  __shared__ __align__(16) unsigned char Ss[NP * kBP * ES];  // F_c [n][p]
+  __shared__ __align__(16) unsigned char Hs[NP * kBP * ES];  // H_c [n][p]
+  __shared__ float pw[BL + 2];                               // a^d of the head
+  __shared__ float red[NW];
+  __shared__ float redm[3][NW];
 
-  const int c = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
-  const int H = A.H, G = A.G, N = A.N, Tl = A.T, HG = H / G;
+  const int c = blockIdx.x, y = blockIdx.y, b = blockIdx.z;
+  const int H = A.H, G = A.G, N = A.N, Tl = A.T, HG = H / G, HS = A.hs, HPS = HG / HS;
+  const int grp = y / HS, slice = y % HS;
   const int c0 = c * BL, Lc = min(BL, Tl - c0);
   const size_t m0 = (size_t)b * Tl + c0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, cl = lane & 15;
+  const int lane0 = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const auto one = [](int) { return 1.f; };
 
-  load_tile<T>(Bs, R, NP, static_cast<const S*>(A.B_hat) + (m0 * KS) * G * N + grp * N,
-               (size_t)G * N, Lc * KS, N, [](int) { return 1.f; });
-  load_tile<T>(Cs, BL, NP, static_cast<const S*>(A.C_mix) + m0 * G * N + grp * N, (size_t)G * N,
-               Lc, N, [](int) { return 1.f; });
+  tile_load<T, R, NP, NT>(Bs, static_cast<const S*>(A.B_hat) + (m0 * KS) * G * N + grp * N,
+                          (size_t)G * N, Lc * KS, N, one);
+  tile_load<T, BL, NP, NT>(Cs, static_cast<const S*>(A.C_mix) + m0 * G * N + grp * N,
+                           (size_t)G * N, Lc, N, one);
   __syncthreads();
-  // Gm[s][r] = C~_s . B_hat_r
-  for (int t = wave; t < (BL / 16) * (R / 16); t += 4) {
-    const int s0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
-    const floatx4 v = tile_mm<T, true, true>(Cs, NP, 1, Bs, 1, NP, s0, r0, NP,
-                                             floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+  // Gm[s][r] = C~_s . B_hat_r: this wave's tiles, kept in registers for every head
+  floatx4 gm[GI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Gm[(s0 + 4 * g + i) * R + r0 + cl] = from_f32<T>(v[i]);
+  for (int i = 0; i < GI; ++i) {
+    const int t = wave + NW * i;
+    gm[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (t < NGT)
+      gm[i] = tmm<T, true, CB, true, CB>(Cs, Bs, 16 * (t / (R / 16)), 16 * (t % (R / 16)), NP,
+                                         lane0);
   }
 
-  floatx4 dBa[(NBT + 3) / 4], dCa[(NCT + 3) / 4];
+  floatx4 dBa[BI], dCa[CI];
 #pragma unroll
-  for (int i = 0; i < (NBT + 3) / 4; ++i) dBa[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < BI; ++i) dBa[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < (NCT + 3) / 4; ++i) dCa[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < CI; ++i) dCa[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int hi = 0; hi < HG; ++hi) {
-    const int h = grp * HG + hi;
+  for (int hi = 0; hi < HPS; ++hi) {
+    const int h = grp * HG + slice * HPS + hi;
     const float a = A.a[h];
+    // lane made opaque per head: the tiles' address arithmetic is then redone
+    // for each head instead of being held in registers across the loop
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    const int g = lane >> 4, cl = lane & 15;
     const size_t sbase = (((size_t)b * A.nb + c) * H + h) * (size_t)N * kBP;
-    __syncthreads();  // the previous head is done with Xs, Dys, Dm, GmM, Ss
-    load_tile<T>(Xs, R, kBP, static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP,
-                 (size_t)H * kBP, Lc * KS, kBP, [](int) { return 1.f; });
-    const float sdy = load_tile_scaled<T>(Dys, BL, kBP,
-                                          static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP,
-                                          (size_t)H * kBP, Lc, kBP, [](int) { return 1.f; }, redm);
-    const float sF = load_tile_scaled<T>(Ss, NP, kBP, A.R + sbase, (size_t)kBP, N, kBP,
-                                         [](int) { return 1.f; }, redm);
-    const float udy = 1.f / sdy, uF = 1.f / sF;
+    __syncthreads();  // the previous head is done with Xs, Dys, Dm, GmM, Ss, Hs, pw
+    for (int d = threadIdx.x; d < BL + 2; d += NT) pw[d] = powi(a, d);
+    // the head's tiles, every read in flight at once; dy, F_c and H_c are
+    // scaled by powers of two, and <F_c, H_c> is taken in fp32 on the way
+    TileLoad<T, R, kBP, NT, S> LX;
+    TileLoad<T, BL, kBP, NT, TY> LD;
+    TileLoad<T, NP, kBP, NT, float> LF, LH;
+    LX.fetch(static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP, (size_t)H * kBP,
+             Lc * KS, kBP);
+    LD.fetch(static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP, (size_t)H * kBP, Lc, kBP);
+    LF.fetch(A.R + sbase, (size_t)kBP, N, kBP);
+    LH.fetch(A.S + sbase, (size_t)kBP, N, kBP);
+    float eh = 0.f;
+#pragma unroll
+    for (int i = 0; i < LF.IT; ++i)
+      eh += LF.raw[i][0] * LH.raw[i][0] + LF.raw[i][1] * LH.raw[i][1] +
+            LF.raw[i][2] * LH.raw[i][2] + LF.raw[i][3] * LH.raw[i][3];
+    float mx[3] = {LD.absmax(one), LF.absmax(one), LH.absmax(one)};
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], off));
+      if (lane == 0) redm[j][wave] = mx[j];
+    }
     __syncthreads();
-    float dap = 0.f;  // this lane's part of da for the head
+    float scl[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      float m = redm[j][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) m = fmaxf(m, redm[j][w]);
+      // 2^-e brings the largest magnitude into [1/2, 1); capped for subnormals
+      scl[j] = m > 0.f ? ldexpf(1.f, min(-(ilogbf(m) + 1), 126)) : 1.f;
+    }
+    LX.store(Xs, one, 1.f);
+    LD.store(Dys, one, scl[0]);
+    LF.store(Ss, one, scl[1]);
+    LH.store(Hs, one, scl[2]);
+    const float udy = 1.f / scl[0], uF = 1.f / scl[1], uHdy = 1.f / (scl[2] * scl[0]);
+    __syncthreads();
+    float dap = eh * (float)Lc * pw[Lc - 1];  // this lane's part of da for the head
     // D[s][r] = dy_s . X_r; the masked, decayed D and Gm; the Gm D term of da
-    for (int t = wave; t < (BL / 16) * (R / 16); t += 4) {
+#pragma unroll
+    for (int i = 0; i < GI; ++i) {
+      const int t = wave + NW * i;
+      if (t >= NGT) continue;
       const int s0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
-      const floatx4 v = tile_mm<T, true, true>(Dys, kBP, 1, Xs, 1, kBP, s0, r0, kBP,
-                                               floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const floatx4 v = tmm<T, true, CX, true, CX>(Dys, Xs, s0, r0, kBP, lane);
       const int r = r0 + cl, tr = r / KS;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = s0 + 4 * g + i;
-        const float gm = to_f32(Gm[s * R + r]);
-        const bool in = tr <= s && s < Lc && tr < Lc;
-        const float dec = in ? powi(a, s - tr) : 0.f;
-        if (in && tr < s) dap += (float)(s - tr) * powi(a, s - tr - 1) * gm * v[i] * udy;
-        Dm[s * R + r] = from_f32<T>(dec * v[i]);
-        GmM[s * R + r] = from_f32<T>(dec * gm);
+      for (int q = 0; q < 4; ++q) {
+        const int s = s0 + 4 * g + q;
+        const bool in = tr <= s && s < Lc;
+        const float dec = in ? pw[s - tr] : 0.f;
+        if (in && tr < s) dap += (float)(s - tr) * pw[s - tr - 1] * gm[i][q] * v[q] * udy;
+        lds_put<T, CG>(Dm, s, r, dec * v[q]);
+        lds_put<T, CG>(GmM, s, r, dec * gm[i][q]);
       }
     }
     __syncthreads();
     // dX_r^T[p] = sum_s dy_s[p] GmM[s][r] + a^{Lc-1-t} (F_c^T B_hat_r)[p]
-    for (int t = wave; t < (kBP / 16) * (R / 16); t += 4) {
+    for (int t = wave; t < NXT; t += NW) {
       const int p0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
-      floatx4 v = tile_mm<T, false, false>(Dys, 1, kBP, GmM, R, 1, p0, r0, BL,
-                                           floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
-      const floatx4 w = tile_mm<T, false, true>(Ss, 1, kBP, Bs, 1, NP, p0, r0, NP,
-                                                floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      floatx4 v = tmm<T, false, CX, false, CG>(Dys, GmM, p0, r0, BL, lane);
+      const floatx4 w = tmm<T, false, CX, true, CB>(Ss, Bs, p0, r0, NP, lane);
       const int r = r0 + cl, tr = r / KS;
       if (tr < Lc) {
-        v = v * udy + w * (powi(a, Lc - 1 - tr) * uF);
+        v = v * udy + w * (pw[Lc - 1 - tr] * uF);
         const size_t row = (m0 * KS + r) * H + h;  // pair row of X_hat
         *reinterpret_cast<floatx4*>(A.dX + row * kBP + p0 + 4 * g) = v;
       }
     }
     // dB_hat_r[n] += sum_s C~_s[n] Dm[s][r] + a^{Lc-1-t} (F_c X_r)[n]
 #pragma unroll
-    for (int i = 0; i < (NBT + 3) / 4; ++i) {
-      const int t = wave + 4 * i;
+    for (int i = 0; i < BI; ++i) {
+      const int t = wave + NW * i;
       const int n0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
       if (t >= NBT || n0 >= N) continue;
-      const floatx4 v = tile_mm<T, false, false>(Cs, 1, NP, Dm, R, 1, n0, r0, BL,
-                                                 floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
-      const floatx4 w = tile_mm<T, true, true>(Ss, kBP, 1, Xs, 1, kBP, n0, r0, kBP,
-                                               floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const floatx4 v = tmm<T, false, CB, false, CG>(Cs, Dm, n0, r0, BL, lane);
+      const floatx4 w = tmm<T, true, CX, true, CX>(Ss, Xs, n0, r0, kBP, lane);
       const int r = r0 + cl, tr = r / KS;
-      const float sc = tr < Lc ? powi(a, Lc - 1 - tr) : 0.f;
-      const float wt = tr + 1 < Lc ? (float)(Lc - 1 - tr) * powi(a, Lc - 2 - tr) : 0.f;
+      const float sc = tr < Lc ? pw[Lc - 1 - tr] : 0.f;
+      const float wt = tr + 1 < Lc ? (float)(Lc - 1 - tr) * pw[Lc - 2 - tr] : 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dap += wt * uF * w[q] * to_f32(Bs[r * NP + n0 + 4 * g + q]);
+      for (int q = 0; q < 4; ++q) dap += wt * uF * w[q] * lds_get<T, CB>(Bs, r, n0 + 4 * g + q);
       dBa[i] = dBa[i] + v * udy + w * (sc * uF);
+      __builtin_amdgcn_sched_barrier(0);  // keep the tiles' reads from piling up in registers
     }
-    // <F_c, H_c> in fp32, then H_c into Ss
-    float eh = 0.f;
-    for (int q = threadIdx.x; q < N * kBP; q += blockDim.x) eh += A.R[sbase + q] * A.S[sbase + q];
-    dap += eh * (float)Lc * powi(a, Lc - 1);
-    __syncthreads();  // every wave is done with F_c
-    const float sH = load_tile_scaled<T>(Ss, NP, kBP, A.S + sbase, (size_t)kBP, N, kBP,
-                                         [](int) { return 1.f; }, redm);
-    const float uHdy = 1.f / (sH * sdy);
-    __syncthreads();
     // dC~_s[n] += sum_r B_hat_r[n] Dm[s][r] + a^{s+1} (H_c dy_s)[n]
 #pragma unroll
-    for (int i = 0; i < (NCT + 3) / 4; ++i) {
-      const int t = wave + 4 * i;
+    for (int i = 0; i < CI; ++i) {
+      const int t = wave + NW * i;
       const int n0 = 16 * (t / (BL / 16)), s0 = 16 * (t % (BL / 16));
       if (t >= NCT || n0 >= N) continue;
-      const floatx4 v = tile_mm<T, false, true>(Bs, 1, NP, Dm, 1, R, n0, s0, R,
-                                                floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
-      const floatx4 w = tile_mm<T, true, true>(Ss, kBP, 1, Dys, 1, kBP, n0, s0, kBP,
-                                               floatx4{0.f, 0.f, 0.f, 0.f}, g, cl);
+      const floatx4 v = tmm<T, false, CB, true, CG>(Bs, Dm, n0, s0, R, lane);
+      const floatx4 w = tmm<T, true, CX, true, CX>(Hs, Dys, n0, s0, kBP, lane);
       const int s = s0 + cl;
-      const float sc = s < Lc ? powi(a, s + 1) : 0.f;
-      const float wt = s < Lc ? (float)(s + 1) * powi(a, s) : 0.f;
+      const float sc = s < Lc ? pw[s + 1] : 0.f;
+      const float wt = s < Lc ? (float)(s + 1) * pw[s] : 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dap += wt * uHdy * w[q] * to_f32(Cs[s * NP + n0 + 4 * g + q]);
+      for (int q = 0; q < 4; ++q) dap += wt * uHdy * w[q] * lds_get<T, CB>(Cs, s, n0 + 4 * g + q);
       dCa[i] = dCa[i] + v * udy + w * (sc * uHdy);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // da of this (sequence, chunk, head): wave sums, then the four waves in order
+    // da of this (sequence, chunk, head): wave sums, then the waves in order
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dap += __shfl_xor(dap, off);
     if (lane == 0) red[wave] = dap;
     __syncthreads();
-    if (threadIdx.x == 0)
-      A.da_part[((size_t)b * A.nb + c) * H + h] = ((red[0] + red[1]) + red[2]) + red[3];
+    if (threadIdx.x == 0) {
+      float s = red[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) s += red[w];
+      A.da_part[((size_t)b * A.nb + c) * H + h] = s;
+    }
   }
 
-  // dB_hat and dC~ of the chunk, summed over the group's heads
+  // dB_hat and dC~ of the chunk, summed over the slice's heads
+  const int g = lane0 >> 4, cl = lane0 & 15;
+  float* dB = HS > 1 ? A.dBp + (size_t)slice * ((size_t)Tl * gridDim.z * KS * G * N) : A.dB;
+  float* dC = HS > 1 ? A.dCp + (size_t)slice * ((size_t)Tl * gridDim.z * G * N) : A.dC;
 #pragma unroll
-  for (int i = 0; i < (NBT + 3) / 4; ++i) {
-    const int t = wave + 4 * i;
+  for (int i = 0; i < BI; ++i) {
+    const int t = wave + NW * i;
     const int n0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
     const int r = r0 + cl;
     if (t >= NBT || n0 >= N || r / KS >= Lc) continue;
-    *reinterpret_cast<floatx4*>(A.dB + ((m0 * KS + r) * G + grp) * N + n0 + 4 * g) = dBa[i];
+    *reinterpret_cast<floatx4*>(dB + ((m0 * KS + r) * G + grp) * N + n0 + 4 * g) = dBa[i];
   }
 #pragma unroll
-  for (int i = 0; i < (NCT + 3) / 4; ++i) {
-    const int t = wave + 4 * i;
+  for (int i = 0; i < CI; ++i) {
+    const int t = wave + NW * i;
     const int n0 = 16 * (t / (BL / 16)), s0 = 16 * (t % (BL / 16));
     const int s = s0 + cl;
     if (t >= NCT || n0 >= N || s >= Lc) continue;
-    *reinterpret_cast<floatx4*>(A.dC + ((m0 + s) * G + grp) * N + n0 + 4 * g) = dCa[i];
+    *reinterpret_cast<floatx4*>(dC + ((m0 + s) * G + grp) * N + n0 + 4 * g) = dCa[i];
   }
 }
 
-// da[h] = sum over sequences and chunks in order
+// dB_hat and dC~ from the head slices' parts, slices in order (float4 units;
+// the first nb4 units are dB_hat's, the rest dC~'s).
+__global__ void bwd_slice_sum_kernel(const float* __restrict__ dBp, const float* __restrict__ dCp,
+                                     float* __restrict__ dB, float* __restrict__ dC, size_t nb4,
+                                     size_t nc4, int hs) {
+  const size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (q >= nb4 + nc4) return;
+  const bool isb = q < nb4;
+  const size_t i = isb ? q : q - nb4, n4 = isb ? nb4 : nc4;
+  const floatx4* src = reinterpret_cast<const floatx4*>(isb ? dBp : dCp);
+  floatx4 s = src[i];
+  for (int k = 1; k < hs; ++k) s = s + src[(size_t)k * n4 + i];
+  reinterpret_cast<floatx4*>(isb ? dB : dC)[i] = s;
+}
+
+// da[h] = sum over sequences and chunks: one wave per head, lane j summing
+// the parts j, j + 64, ... in order, then a fixed butterfly over the lanes.
 __global__ void bwd_da_kernel(const float* __restrict__ part, float* __restrict__ da, int Bt,
                               int nb, int H) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
+  const int h = blockIdx.x, lane = threadIdx.x;
+  const int n = Bt * nb;
   float s = 0.f;
-  for (int b = 0; b < Bt; ++b)
-    for (int c = 0; c < nb; ++c) s += part[((size_t)b * nb + c) * H + h];
-  da[h] = s;
+  for (int i = lane; i < n; i += 64) s += part[(size_t)i * H + h];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) da[h] = s;
 }
 
 // ---------------------------------------------------------------- launch
 
 int scan_bwd_block(bool is_bf16) { return is_bf16 ? 64 : 32; }
 
-size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int N) {
+// Slices of each group's heads: the fewest (a divisor of the group's heads)
+// that give the gradient kernel at least 1024 workgroups.
+int scan_bwd_slices(bool is_bf16, int Bt, int T, int H, int G) {
+  const int BL = scan_bwd_block(is_bf16);
+  const long base = (long)((T + BL - 1) / BL) * G * Bt;
+  const int HG = H / G;
+  for (int d = 1; d <= HG; ++d)
+    if (HG % d == 0 && base * d >= 1024) return d;
+  return HG;
+}
+
+size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int G, int N, int k) {
   const int BL = scan_bwd_block(is_bf16);
   const size_t nb = (size_t)((T + BL - 1) / BL);
-  const size_t st = (size_t)Bt * nb * H * N * kBP * sizeof(float);
   const size_t al = 255;
-  return ((st + al) & ~al) * 2 + (((size_t)Bt * nb * H * sizeof(float) + al) & ~al);
+  const size_t st = ((size_t)Bt * nb * H * N * kBP * sizeof(float) + al) & ~al;
+  const size_t dap = ((size_t)Bt * nb * H * sizeof(float) + al) & ~al;
+  const int hs = scan_bwd_slices(is_bf16, Bt, T, H, G);
+  const size_t M = (size_t)Bt * T;
+  const size_t parts = hs > 1 ? (size_t)hs * (M * k * G * N + M * G * N) * sizeof(float) : 0;
+  return 2 * st + dap + ((parts + al) & ~al);
 }
 
 template <typename T, typename S, typename TY, int NP, int KS, int BL>
@@ -415,10 +591,19 @@ static hipError_t launch_bwd_t(const BwdArgs& A, int Bt, hipStream_t s) {
   prof_end(s);
   prof_begin("scan_bwd_grad", s);
   hipLaunchKernelGGL((bwd_grad_kernel<T, S, TY, NP, KS, BL>),
-                     dim3((unsigned)A.nb, (unsigned)A.G, (unsigned)Bt), dim3(256), 0, s, A);
+                     dim3((unsigned)A.nb, (unsigned)(A.G * A.hs), (unsigned)Bt),
+                     dim3(64 * kGradWaves), 0, s, A);
   prof_end(s);
+  if (A.hs > 1) {
+    const size_t M = (size_t)Bt * A.T;
+    const size_t nb4 = M * A.k * A.G * A.N / 4, nc4 = M * A.G * A.N / 4;
+    prof_begin("scan_bwd_slice_sum", s);
+    hipLaunchKernelGGL(bwd_slice_sum_kernel, dim3((unsigned)((nb4 + nc4 + 255) / 256)),
+                       dim3(256), 0, s, A.dBp, A.dCp, A.dB, A.dC, nb4, nc4, A.hs);
+    prof_end(s);
+  }
   prof_begin("scan_bwd_da", s);
-  hipLaunchKernelGGL(bwd_da_kernel, dim3((A.H + 63) / 64), dim3(64), 0, s, A.da_part, A.da, Bt,
+  hipLaunchKernelGGL(bwd_da_kernel, dim3((unsigned)A.H), dim3(64), 0, s, A.da_part, A.da, Bt,
                      A.nb, A.H);
   prof_end(s);
   return hipGetLastError();
@@ -464,12 +649,17 @@ hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N
   }
   const int BL = scan_bwd_block(is_bf16);
   const int nb = (T + BL - 1) / BL;
-  const size_t st = (size_t)Bt * nb * H * N * kBP * sizeof(float);
-  const size_t stal = (st + 255) & ~(size_t)255;
+  const size_t al = 255;
+  const size_t st = ((size_t)Bt * nb * H * N * kBP * sizeof(float) + al) & ~al;
+  const size_t dap = ((size_t)Bt * nb * H * sizeof(float) + al) & ~al;
+  const int hs = scan_bwd_slices(is_bf16, Bt, T, H, G);
+  const size_t M = (size_t)Bt * T;
   unsigned char* w8 = static_cast<unsigned char*>(ws);
+  float* dBp = reinterpret_cast<float*>(w8 + 2 * st + dap);
+  float* dCp = dBp + (size_t)hs * M * k * G * N;
   BwdArgs A{B_hat, X_hat, C_mix, dy, a, h_init, dh_final, dB, dX, dC, da, dh_init,
-            reinterpret_cast<float*>(w8), reinterpret_cast<float*>(w8 + stal),
-            reinterpret_cast<float*>(w8 + 2 * stal), T, H, G, N, k, nb};
+            reinterpret_cast<float*>(w8), reinterpret_cast<float*>(w8 + st),
+            reinterpret_cast<float*>(w8 + 2 * st), dBp, dCp, T, H, G, N, k, nb, hs};
   if (is_bf16) return launch_bwd_ty<f16, f16, bf16>(A, Bt, s);
   return launch_bwd_ty<float, float, float>(A, Bt, s);
 }

@@ -146,6 +146,14 @@ def output_projection_inputs(wl: Workload, rows: int | None = None) -> dict:
     return {"w_out": w_out, "y": _store(y, wl.dtype)}
 
 
+def output_gradient(wl: Workload) -> np.ndarray:
+    """Upstream gradient dl/dy [M, H, P] of the training step (same dtype rule
+    as u), from a stream of its own so every other input is unchanged."""
+    rng = np.random.default_rng([wl.seed, 130363])
+    dy = rng.standard_normal((wl.tokens, wl.nheads, wl.headdim), dtype=np.float32)
+    return _store(dy, wl.dtype)
+
+
 def expert_decays(wl: Workload) -> np.ndarray:
     """Per-expert, per-head decays a^(e)_h ~ U[a_lo, a_hi] (fp32) for the
     expert-mixed transition, [E, H], from a stream of their own so every other
