@@ -44,10 +44,13 @@ CSRC = os.path.join(ROOT, "selective_ssm_parameter_amd", "csrc")
 KERNEL_NAMES = [
     (r"pbwd_dz_kernel", "proj_bwd_dz"),
     (r"pbwd_router_kernel", "proj_bwd_router"),
+    # (type, MODE): MODE 0 is du; the demangled name of MODE 1 varies
     (r"pbwd_gemm_kernel.*Li0EEE", "proj_bwd_du"),
-    (r"pbwd_gemm_kernel.*Li1EEE", "proj_bwd_dw"),
+    (r"pbwd_gemm_kernel", "proj_bwd_dw"),
     (r"pbwd_du_sum_kernel", "proj_bwd_du_sum"),
-    (r"pbwd_dwr_kernel|pbwd_dwr_sum_kernel", "proj_bwd_dwr"),
+    (r"pbwd_dwr_sum_kernel", "proj_bwd_dwr_sum"),
+    (r"pbwd_dwr_kernel", "proj_bwd_dwr"),
+    (r"bwd_slice_sum_kernel", "scan_bwd_slice_sum"),
     (r"bwd_local_kernel", "scan_bwd_local"),
     (r"bwd_sweep_kernel", "scan_bwd_sweep"),
     (r"bwd_grad_kernel", "scan_bwd_grad"),

@@ -186,11 +186,27 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
 
   const int E = A.E, D = A.D, W = A.W;
   const int ncol = (D + kGB - 1) / kGB;
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so XCD x
+  // takes the contiguous logical range [x per, (x + 1) per) of the units,
+  // which run row tile by row tile (all column tiles of one row tile
+  // together): an XCD's workgroups share dz rows and one expert's weights
+  // (du), or one expert's dz columns and gathered token rows (dW), in its L2.
+  int units;
+  if constexpr (MODE == 0) {
+    int nt = 0;
+    for (int q = 0; q < E; ++q) nt += (A.offsets[q + 1] - A.offsets[q] + kGB - 1) / kGB;
+    units = nt * ncol;
+  } else {
+    units = E * ((W + kGB - 1) / kGB) * ncol;
+  }
+  const int per = (units + 7) / 8, slot = blockIdx.x / 8;
+  const int logical = (blockIdx.x % 8) * per + slot;
+  if (slot >= per || logical >= units) return;
   int e = -1, r0 = 0, nrows = 0, c0 = 0;  // expert, first row, rows, first column
   int kbeg = 0, klen = 0;                  // MODE 1: the expert's sorted pair range
   if constexpr (MODE == 0) {
-    int t = blockIdx.x / ncol;
-    c0 = (blockIdx.x % ncol) * kGB;
+    int t = logical / ncol;
+    c0 = (logical % ncol) * kGB;
     for (int q = 0; q < E; ++q) {
       const int cnt = A.offsets[q + 1] - A.offsets[q];
       const int nt = (cnt + kGB - 1) / kGB;
@@ -206,11 +222,10 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
     klen = W;
   } else {
     const int nwt = (W + kGB - 1) / kGB;
-    e = blockIdx.x / (nwt * ncol);
-    const int rem = blockIdx.x % (nwt * ncol);
+    e = logical / (nwt * ncol);
+    const int rem = logical % (nwt * ncol);
     r0 = (rem / ncol) * kGB;
     c0 = (rem % ncol) * kGB;
-    if (e >= E) return;
     nrows = min(kGB, W - r0);
     kbeg = A.offsets[e];
     klen = A.offsets[e + 1] - kbeg;
@@ -387,7 +402,8 @@ static hipError_t launch_pbwd_t(const ProjBwdArgs& A, hipStream_t s) {
   // row tiles over all experts: sum_e ceil(n_e / 128) <= pairs / 128 + E
   const int ntr = pairs / kGB + A.E;
   prof_begin("proj_bwd_du", s);
-  hipLaunchKernelGGL((pbwd_gemm_kernel<T, 0>), dim3((unsigned)(ntr * ncol)), dim3(256), 0, s, A);
+  hipLaunchKernelGGL((pbwd_gemm_kernel<T, 0>), dim3((unsigned)((ntr * ncol + 7) / 8 * 8)),
+                     dim3(256), 0, s, A);
   prof_end(s);
   prof_begin("proj_bwd_du_sum", s);
   hipLaunchKernelGGL(pbwd_du_sum_kernel, dim3((unsigned)(((size_t)A.M * A.D / 4 + 255) / 256)),
@@ -395,8 +411,8 @@ static hipError_t launch_pbwd_t(const ProjBwdArgs& A, hipStream_t s) {
   prof_end(s);
   const int nwt = (A.W + kGB - 1) / kGB;
   prof_begin("proj_bwd_dw", s);
-  hipLaunchKernelGGL((pbwd_gemm_kernel<T, 1>), dim3((unsigned)(A.E * nwt * ncol)), dim3(256), 0,
-                     s, A);
+  hipLaunchKernelGGL((pbwd_gemm_kernel<T, 1>), dim3((unsigned)((A.E * nwt * ncol + 7) / 8 * 8)),
+                     dim3(256), 0, s, A);
   prof_end(s);
   prof_begin("proj_bwd_dwr", s);
   hipLaunchKernelGGL(pbwd_dwr_kernel<T>, dim3((unsigned)((A.D + 63) / 64), (unsigned)A.nsplit),
