@@ -73,6 +73,11 @@ CASES = [
     ("bf16_T1", W("b6", 806, seqlen=1), True, True),
     ("f32_k2_n128", W("b7", 807, dtype=synth.F32, seqlen=190), True, True),
     ("bf16_long", W("b8", 808, batch=1, nheads=2, seqlen=3000), True, True),
+    # one head per group: the gradient kernel writes dB_hat and dC~ itself
+    # (no head slices to sum)
+    ("bf16_groups_eq_heads", W("b11", 811, nheads=2, ngroups=2, dstate=64, seqlen=200), True, True),
+    ("f32_groups_eq_heads_k1", W("b12", 812, dtype=synth.F32, nheads=2, ngroups=2, top_k=1,
+                                 seqlen=70), True, False),
 ]
 
 
