@@ -67,16 +67,25 @@ __global__ __launch_bounds__(256) void pbwd_dz_kernel(ProjBwdArgs A) {
 
 // ---------------------------------------------------------------- router
 
-// One wave per token. With pi = softmax(logits) and q_e = pi_e dpi_e (the sum
-// of s_j over the slots routed to e), dg_e = q_e - pi_e sum_f q_f. Then du is
-// initialised with W_r^T dg, lanes over d.
+// Router gradient, 32 tokens per workgroup. Phase 1, one wave per token (8
+// per wave): pi = softmax(logits), q_e = pi_e dpi_e (the sum of s_j over the
+// slots routed to e), dg_e = q_e - pi_e sum_f q_f, into LDS and dg. Phase 2,
+// threads over d: du[t, d] = sum_e dg[t, e] W_r[e, d] for the 32 tokens, each
+// router element read once per workgroup (du is initialised here).
+constexpr int kRouterTok = 32;
+
 template <typename T>
 __global__ __launch_bounds__(256) void pbwd_router_kernel(ProjBwdArgs A) {
-  __shared__ float sdg[4][256];
+  __shared__ float sdg[kRouterTok][257];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + wave;
+  const int t0 = blockIdx.x * kRouterTok;
   const int E = A.E;
-  if (m < A.M) {
+  for (int tl = wave; tl < kRouterTok; tl += 4) {
+    const int m = t0 + tl;
+    if (m >= A.M) {
+      for (int e = lane; e < E; e += 64) sdg[tl][e] = 0.f;
+      continue;
+    }
     float pi[4], q[4];
     float mx = -INFINITY;
 #pragma unroll
@@ -108,18 +117,26 @@ __global__ __launch_bounds__(256) void pbwd_router_kernel(ProjBwdArgs A) {
       const int e = lane + 64 * r;
       if (e < E) {
         const float g = q[r] - (pi[r] / se) * sq;
-        sdg[wave][e] = g;
+        sdg[tl][e] = g;
         A.dg[(size_t)m * E + e] = g;
       }
     }
   }
   __syncthreads();
-  if (m >= A.M) return;
   const T* wr = static_cast<const T*>(A.w_router);
-  for (int d = lane; d < A.D; d += 64) {
-    float acc = 0.f;
-    for (int e = 0; e < E; ++e) acc += sdg[wave][e] * to_f32(wr[(size_t)e * A.D + d]);
-    A.du[(size_t)m * A.D + d] = acc;
+  const int nt = min(kRouterTok, A.M - t0);
+  for (int d = threadIdx.x; d < A.D; d += 256) {
+    float acc[kRouterTok];
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t) acc[t] = 0.f;
+    for (int e = 0; e < E; ++e) {
+      const float w = to_f32(wr[(size_t)e * A.D + d]);
+#pragma unroll
+      for (int t = 0; t < kRouterTok; ++t) acc[t] += sdg[t][e] * w;
+    }
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t)
+      if (t < nt) A.du[(size_t)(t0 + t) * A.D + d] = acc[t];
   }
 }
 
@@ -328,17 +345,25 @@ __global__ void pbwd_du_sum_kernel(ProjBwdArgs A) {
 
 // dW_r partials over splits of kDwrTokens tokens: block (column tile of 64,
 // split); thread (sub, c) takes column c and every fourth token of the split
-// starting at sub, 16 experts at a time; the four subs are added in order.
+// starting at sub, 16 experts at a time, with the split's router gradients
+// for those experts staged in LDS; the four subs are added in order.
 constexpr int kDwrTokens = 256;
 
 template <typename T>
 __global__ __launch_bounds__(256) void pbwd_dwr_kernel(ProjBwdArgs A) {
   __shared__ float part[4][16][64];
+  __shared__ __align__(16) float sdg[kDwrTokens][16];
   const int c = threadIdx.x & 63, sub = threadIdx.x >> 6;
   const int d = blockIdx.x * 64 + c, sp = blockIdx.y;
   const int m0 = sp * kDwrTokens, m1 = min(A.M, m0 + kDwrTokens);
   const T* u = static_cast<const T*>(A.u);
   for (int e0 = 0; e0 < A.E; e0 += 16) {
+    __syncthreads();  // the previous group's sdg and part are read
+    for (int q = threadIdx.x; q < kDwrTokens * 16; q += 256) {
+      const int t = q / 16, e = e0 + q % 16;
+      sdg[t][q % 16] = (m0 + t < m1 && e < A.E) ? A.dg[(size_t)(m0 + t) * A.E + e] : 0.f;
+    }
+    __syncthreads();
     float acc[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
@@ -346,10 +371,13 @@ __global__ __launch_bounds__(256) void pbwd_dwr_kernel(ProjBwdArgs A) {
 #pragma unroll 4
       for (int m = m0 + sub; m < m1; m += 4) {
         const float uv = to_f32(u[(size_t)m * A.D + d]);
-        const float* dg = A.dg + (size_t)m * A.E + e0;
+        const floatx4* g4 = reinterpret_cast<const floatx4*>(sdg[m - m0]);
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (e0 + q < A.E) acc[q] += dg[q] * uv;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const floatx4 gv = g4[q4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[4 * q4 + j] += gv[j] * uv;
+        }
       }
     }
 #pragma unroll
@@ -360,7 +388,6 @@ __global__ __launch_bounds__(256) void pbwd_dwr_kernel(ProjBwdArgs A) {
         A.dwr_part[((size_t)sp * A.E + e0 + q) * A.D + d] =
             ((part[0][q][c] + part[1][q][c]) + part[2][q][c]) + part[3][q][c];
     }
-    __syncthreads();
   }
 }
 
@@ -396,7 +423,8 @@ static hipError_t launch_pbwd_t(const ProjBwdArgs& A, hipStream_t s) {
   hipLaunchKernelGGL((pbwd_dz_kernel<T, S>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, A);
   prof_end(s);
   prof_begin("proj_bwd_router", s);
-  hipLaunchKernelGGL(pbwd_router_kernel<T>, dim3((unsigned)((A.M + 3) / 4)), dim3(256), 0, s, A);
+  hipLaunchKernelGGL(pbwd_router_kernel<T>, dim3((unsigned)((A.M + kRouterTok - 1) / kRouterTok)),
+                     dim3(256), 0, s, A);
   prof_end(s);
   const int ncol = (A.D + kGB - 1) / kGB;
   // row tiles over all experts: sum_e ceil(n_e / 128) <= pairs / 128 + E

@@ -26,7 +26,7 @@
 // R_c = sum_s a^{s-c0} C~_s dy_s^T (matrix cores); a sequential sweep per
 // state element turning S into H_c (forwards: H_{c+1} = a^{Lc} H_c + S_c) and
 // R into F_c (backwards: F_{c-1} = a R_c + a^{Lc} F_c, ending at F_{-1} =
-// dh_init) in place; per (sequence, chunk, group, slice of the group's heads)
+// dh_init); per (sequence, chunk, group, slice of the group's heads)
 // the gradients above on matrix cores, the slice's heads visited in order so
 // dB_hat and dC~ are summed over them in registers, then (with several
 // slices) a fixed-order sum of the slices' parts; a fixed-order sum of da.
@@ -51,6 +51,12 @@ namespace swimba {
 constexpr int kBP = 64;        // head dim
 constexpr int kGradWaves = 8;  // waves of the gradient kernel
 
+// The local chunk states S_c and R_c go to HBM in the operand type (fp16 for
+// bf16 problems), each (chunk, head) tile scaled by the power of two that
+// brings its largest magnitude into [1/2, 1); the sweep restores them and
+// sums in fp32, and writes H_c and F_c in fp32 (their rounding would be
+// amplified by the cancellation in the gradients' sums).
+
 struct BwdArgs {
   const void* B_hat;    // [M, k, G, N] stream type
   const void* X_hat;    // [M, k, H, P] stream type
@@ -64,8 +70,12 @@ struct BwdArgs {
   float* dC;            // [M, G, N]
   float* da;            // [H]
   float* dh_init;       // [Bt, H, N, P] or null
-  float* S;             // [Bt, nb, H, N, P]: S_c, then H_c
-  float* R;             // [Bt, nb, H, N, P]: R_c, then F_c
+  void* Sl;             // [Bt, nb, H, N, P] local type: S_c (scaled by 1 / S_u)
+  void* Rl;             // [Bt, nb, H, N, P] local type: R_c (scaled by 1 / R_u)
+  float* Su;            // [Bt, nb, H]: the factor that restores S_c
+  float* Ru;            // [Bt, nb, H]: the factor that restores R_c
+  float* S;             // [Bt, nb, H, N, P]: H_c (entering state of chunk c)
+  float* R;             // [Bt, nb, H, N, P]: F_c (gradient entering chunk c from the right)
   float* da_part;       // [Bt, nb, H]
   float* dBp;           // [hs, M, k, G, N] slice parts (hs > 1)
   float* dCp;           // [hs, M, G, N]
@@ -272,54 +282,154 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
   const float udy = 1.f / sdy;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, cl = lane & 15;
   const size_t sbase = (((size_t)b * A.nb + c) * H + h) * (size_t)N * kBP;
-  constexpr int TILES = (NP / 16) * (kBP / 16);
-  for (int t = wave; t < TILES; t += 4) {
+  constexpr int TILES = (NP / 16) * (kBP / 16), TI = TILES / 4;
+  // S[n][p] = sum_r B_hat[r][n] xd[r][p];  R[n][p] = sum_s C~[s][n] dyd[s][p]
+  floatx4 s4[TI], r4[TI];
+  float ms = 0.f, mr = 0.f;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int t = wave + 4 * i;
+    const int n0 = 16 * (t / (kBP / 16)), p0 = 16 * (t % (kBP / 16));
+    s4[i] = r4[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (n0 < N) {
+      s4[i] = tmm<T, false, CB, false, CX>(Bs, Xd, n0, p0, R, lane);
+      r4[i] = tmm<T, false, CB, false, CX>(Cs, Dyd, n0, p0, BL, lane) * udy;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ms = fmaxf(ms, fabsf(s4[i][q]));
+      mr = fmaxf(mr, fabsf(r4[i][q]));
+    }
+  }
+  float ss = 1.f, sr = 1.f;  // storage scales (1 for fp32 tiles)
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      ms = fmaxf(ms, __shfl_xor(ms, off));
+      mr = fmaxf(mr, __shfl_xor(mr, off));
+    }
+    __syncthreads();  // red is free again
+    if (lane == 0) {
+      red[wave] = ms;
+      pw[wave] = mr;  // the decay table is no longer read
+    }
+    __syncthreads();
+    ms = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    mr = fmaxf(fmaxf(pw[0], pw[1]), fmaxf(pw[2], pw[3]));
+    ss = ms > 0.f ? ldexpf(1.f, min(-(ilogbf(ms) + 1), 126)) : 1.f;
+    sr = mr > 0.f ? ldexpf(1.f, min(-(ilogbf(mr) + 1), 126)) : 1.f;
+  }
+  if (threadIdx.x == 0) {
+    A.Su[((size_t)b * A.nb + c) * H + h] = 1.f / ss;
+    A.Ru[((size_t)b * A.nb + c) * H + h] = 1.f / sr;
+  }
+  T* Sl = static_cast<T*>(A.Sl) + sbase;
+  T* Rl = static_cast<T*>(A.Rl) + sbase;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int t = wave + 4 * i;
     const int n0 = 16 * (t / (kBP / 16)), p0 = 16 * (t % (kBP / 16));
     if (n0 >= N) continue;
-    // S[n][p] = sum_r B_hat[r][n] xd[r][p];  R[n][p] = sum_s C~[s][n] dyd[s][p]
-    const floatx4 s4 = tmm<T, false, CB, false, CX>(Bs, Xd, n0, p0, R, lane);
-    const floatx4 r4 = tmm<T, false, CB, false, CX>(Cs, Dyd, n0, p0, BL, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 4 * g + i;
-      A.S[sbase + (size_t)n * kBP + p0 + cl] = s4[i];
-      A.R[sbase + (size_t)n * kBP + p0 + cl] = r4[i] * udy;
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + 4 * g + q;
+      Sl[(size_t)n * kBP + p0 + cl] = from_f32<T>(s4[i][q] * ss);
+      Rl[(size_t)n * kBP + p0 + cl] = from_f32<T>(r4[i][q] * sr);
     }
   }
 }
 
 // ---------------------------------------------------------------- state sweep
 
-// Per state element: S_c -> H_c (the state entering chunk c) in place going
-// forwards, R_c -> F_c (the gradient entering chunk c from the right) in
-// place going backwards; the backward sweep ends at F_{-1} = a g_0 = dh_init.
-template <int BL>
+// Per state element: the states entering each chunk, H_c going forwards
+// (H_{c+1} = a^{Lc} H_c + S_c from h_init) and F_c going backwards (F_{c-1} =
+// a R_c + a^{Lc} F_c from dh_final, ending at F_{-1} = a g_0 = dh_init). Each
+// thread owns V elements of a (sequence, head) state (16 bytes of the local
+// states, or fewer when there are few states, so that enough threads share
+// the walk) and reads those of SU chunks before it uses any (the walk over
+// chunks is serial, so the reads of several chunks are kept in flight); sums
+// in fp32.
+template <typename LT, int BL, int V>
 __global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdArgs A) {
+  constexpr int SU = V >= 4 ? 8 : 16;  // chunks whose reads are in flight together
+  typedef LT RV __attribute__((ext_vector_type(V)));
   const int h = blockIdx.y, b = blockIdx.z;
   const int NPsz = A.N * kBP;
-  const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e4 >= NPsz) return;
+  const int e0 = (blockIdx.x * 256 + threadIdx.x) * V;
+  if (e0 >= NPsz) return;
   const float a = A.a[h];
-  const size_t hb = ((size_t)b * A.H + h) * NPsz + e4;
-  const size_t cstride = (size_t)A.H * NPsz;
-  const size_t base = (size_t)b * A.nb * cstride + (size_t)h * NPsz + e4;
-  floatx4 st = A.h_init ? *reinterpret_cast<const floatx4*>(A.h_init + hb)
-                        : floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < A.nb; ++c) {
-    floatx4* p = reinterpret_cast<floatx4*>(A.S + base + c * cstride);
-    const floatx4 s = *p;
-    *p = st;
-    st = st * powi(a, min(BL, A.T - c * BL)) + s;
+  const float aL = powi(a, BL);
+  const int Tl = A.T, nb = A.nb, H = A.H;
+  const float aLast = powi(a, Tl - (nb - 1) * BL);
+  const size_t hb = ((size_t)b * H + h) * NPsz + e0;
+  const size_t cstride = (size_t)H * NPsz;
+  const size_t base = (size_t)b * nb * cstride + (size_t)h * NPsz + e0;
+  const float* Su = A.Su + (size_t)b * nb * H + h;
+  const float* Ru = A.Ru + (size_t)b * nb * H + h;
+  float st[V], gr[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    st[j] = A.h_init ? A.h_init[hb + j] : 0.f;
+    gr[j] = A.dh_final ? A.dh_final[hb + j] : 0.f;
   }
-  floatx4 gr = A.dh_final ? *reinterpret_cast<const floatx4*>(A.dh_final + hb)
-                          : floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int c = A.nb - 1; c >= 0; --c) {
-    floatx4* p = reinterpret_cast<floatx4*>(A.R + base + c * cstride);
-    const floatx4 r = *p;
-    *p = gr;
-    gr = gr * powi(a, min(BL, A.T - c * BL)) + r * a;
+  const LT* Sl = static_cast<const LT*>(A.Sl) + base;
+  const LT* Rl = static_cast<const LT*>(A.Rl) + base;
+  float* Hp = A.S + base;
+  float* Fp = A.R + base;
+  auto put = [&](float* dst, const float* v) {
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < V; j += 4)
+        *reinterpret_cast<floatx4*>(dst + j) = floatx4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j) dst[j] = v[j];
+    }
+  };
+  for (int c0 = 0; c0 < nb; c0 += SU) {
+    RV v[SU];
+    float us[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      if (c0 + u < nb) {
+        v[u] = *reinterpret_cast<const RV*>(Sl + (size_t)(c0 + u) * cstride);
+        us[u] = Su[(size_t)(c0 + u) * H];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int c = c0 + u;
+      if (c >= nb) break;
+      put(Hp + (size_t)c * cstride, st);
+      const float ac = c == nb - 1 ? aLast : aL;
+#pragma unroll
+      for (int j = 0; j < V; ++j) st[j] = st[j] * ac + to_f32(v[u][j]) * us[u];
+    }
   }
-  if (A.dh_init) *reinterpret_cast<floatx4*>(A.dh_init + hb) = gr;
+  for (int c1 = nb - 1; c1 >= 0; c1 -= SU) {
+    RV v[SU];
+    float us[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      if (c1 - u >= 0) {
+        v[u] = *reinterpret_cast<const RV*>(Rl + (size_t)(c1 - u) * cstride);
+        us[u] = Ru[(size_t)(c1 - u) * H] * a;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int c = c1 - u;
+      if (c < 0) break;
+      put(Fp + (size_t)c * cstride, gr);
+      const float ac = c == nb - 1 ? aLast : aL;
+#pragma unroll
+      for (int j = 0; j < V; ++j) gr[j] = gr[j] * ac + to_f32(v[u][j]) * us[u];
+    }
+  }
+  if (A.dh_init) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) A.dh_init[hb + j] = gr[j];
+  }
 }
 
 // ---------------------------------------------------------------- chunk gradients
@@ -400,8 +510,8 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
     float eh = 0.f;
 #pragma unroll
     for (int i = 0; i < LF.IT; ++i)
-      eh += LF.raw[i][0] * LH.raw[i][0] + LF.raw[i][1] * LH.raw[i][1] +
-            LF.raw[i][2] * LH.raw[i][2] + LF.raw[i][3] * LH.raw[i][3];
+#pragma unroll
+      for (int j = 0; j < LF.V; ++j) eh += to_f32(LF.raw[i][j]) * to_f32(LH.raw[i][j]);
     float mx[3] = {LD.absmax(one), LF.absmax(one), LH.absmax(one)};
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -567,16 +677,39 @@ int scan_bwd_slices(bool is_bf16, int Bt, int T, int H, int G) {
   return HG;
 }
 
-size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int G, int N, int k) {
+// Workspace: H_c and F_c (fp32), the local states S_c and R_c (operand type)
+// with their per-(chunk, head) factors, da's parts, and the head slices'
+// dB_hat / dC~ parts.
+struct BwdWs {
+  size_t H, F, Sl, Rl, Su, Ru, dap, parts, total;
+};
+
+static BwdWs bwd_ws(bool is_bf16, int Bt, int T, int H, int G, int N, int k) {
   const int BL = scan_bwd_block(is_bf16);
   const size_t nb = (size_t)((T + BL - 1) / BL);
   const size_t al = 255;
-  const size_t st = ((size_t)Bt * nb * H * N * kBP * sizeof(float) + al) & ~al;
-  const size_t dap = ((size_t)Bt * nb * H * sizeof(float) + al) & ~al;
+  auto up = [&](size_t x) { return (x + al) & ~al; };
+  const size_t elems = (size_t)Bt * nb * H * N * kBP;
+  const size_t les = is_bf16 ? 2 : 4;  // local-state element bytes
   const int hs = scan_bwd_slices(is_bf16, Bt, T, H, G);
   const size_t M = (size_t)Bt * T;
-  const size_t parts = hs > 1 ? (size_t)hs * (M * k * G * N + M * G * N) * sizeof(float) : 0;
-  return 2 * st + dap + ((parts + al) & ~al);
+  BwdWs w{};
+  size_t off = 0;
+  w.H = off; off += up(elems * 4);
+  w.F = off; off += up(elems * 4);
+  w.Sl = off; off += up(elems * les);
+  w.Rl = off; off += up(elems * les);
+  w.Su = off; off += up((size_t)Bt * nb * H * 4);
+  w.Ru = off; off += up((size_t)Bt * nb * H * 4);
+  w.dap = off; off += up((size_t)Bt * nb * H * 4);
+  w.parts = off;
+  off += up(hs > 1 ? (size_t)hs * (M * k * G * N + M * G * N) * sizeof(float) : 0);
+  w.total = off;
+  return w;
+}
+
+size_t scan_bwd_ws_bytes(bool is_bf16, int Bt, int T, int H, int G, int N, int k) {
+  return bwd_ws(is_bf16, Bt, T, H, G, N, k).total;
 }
 
 template <typename T, typename S, typename TY, int NP, int KS, int BL>
@@ -586,8 +719,16 @@ static hipError_t launch_bwd_t(const BwdArgs& A, int Bt, hipStream_t s) {
   hipLaunchKernelGGL((bwd_local_kernel<T, S, TY, NP, KS, BL>), g1, dim3(256), 0, s, A);
   prof_end(s);
   prof_begin("scan_bwd_sweep", s);
-  hipLaunchKernelGGL(bwd_sweep_kernel<BL>, dim3((unsigned)((A.N * kBP / 4 + 255) / 256), A.H, Bt),
-                     dim3(256), 0, s, A);
+  {
+    // 16 bytes of local state per thread, or 2 elements when that leaves
+    // fewer than 128K threads for the walk
+    constexpr int V16 = 16 / (int)sizeof(T);
+    const bool narrow = (size_t)Bt * A.H * A.N * kBP / V16 < (size_t)131072;
+    const int V = narrow ? 2 : V16;
+    const dim3 gs((unsigned)((A.N * kBP / V + 255) / 256), A.H, Bt);
+    if (narrow) hipLaunchKernelGGL((bwd_sweep_kernel<T, BL, 2>), gs, dim3(256), 0, s, A);
+    else hipLaunchKernelGGL((bwd_sweep_kernel<T, BL, V16>), gs, dim3(256), 0, s, A);
+  }
   prof_end(s);
   prof_begin("scan_bwd_grad", s);
   hipLaunchKernelGGL((bwd_grad_kernel<T, S, TY, NP, KS, BL>),
@@ -649,17 +790,17 @@ hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N
   }
   const int BL = scan_bwd_block(is_bf16);
   const int nb = (T + BL - 1) / BL;
-  const size_t al = 255;
-  const size_t st = ((size_t)Bt * nb * H * N * kBP * sizeof(float) + al) & ~al;
-  const size_t dap = ((size_t)Bt * nb * H * sizeof(float) + al) & ~al;
   const int hs = scan_bwd_slices(is_bf16, Bt, T, H, G);
+  const BwdWs w = bwd_ws(is_bf16, Bt, T, H, G, N, k);
   const size_t M = (size_t)Bt * T;
   unsigned char* w8 = static_cast<unsigned char*>(ws);
-  float* dBp = reinterpret_cast<float*>(w8 + 2 * st + dap);
+  float* dBp = reinterpret_cast<float*>(w8 + w.parts);
   float* dCp = dBp + (size_t)hs * M * k * G * N;
   BwdArgs A{B_hat, X_hat, C_mix, dy, a, h_init, dh_final, dB, dX, dC, da, dh_init,
-            reinterpret_cast<float*>(w8), reinterpret_cast<float*>(w8 + st),
-            reinterpret_cast<float*>(w8 + 2 * st), dBp, dCp, T, H, G, N, k, nb, hs};
+            w8 + w.Sl, w8 + w.Rl, reinterpret_cast<float*>(w8 + w.Su),
+            reinterpret_cast<float*>(w8 + w.Ru), reinterpret_cast<float*>(w8 + w.H),
+            reinterpret_cast<float*>(w8 + w.F), reinterpret_cast<float*>(w8 + w.dap), dBp, dCp,
+            T, H, G, N, k, nb, hs};
   if (is_bf16) return launch_bwd_ty<f16, f16, bf16>(A, Bt, s);
   return launch_bwd_ty<float, float, float>(A, Bt, s);
 }
