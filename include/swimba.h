@@ -325,7 +325,9 @@ swimba_status swimba_ssd_chunk_scan_backward(const swimba_dims* dims, const void
  *   dW_router   [E, D] float32 out;  dW_experts [E, W, D] float32 out
  *               (zeros when M is 0; every other pointer may then be NULL)
  *   ws          workspace of swimba_workspace_size(dims, SWIMBA_CALL_PROJECT_BACKWARD)
- * Shapes and errors as for swimba_expert_project_mix.
+ * Shapes and errors as for swimba_expert_project_mix; in addition
+ * M * k * (H*P + 2*G*N) and M * k * D elements of the input type must stay
+ * below 2^31 bytes (SWIMBA_ERR_DIMS).
  */
 swimba_status swimba_expert_project_mix_backward(
     const swimba_dims* dims, const void* u, const void* w_router, const void* w_experts,

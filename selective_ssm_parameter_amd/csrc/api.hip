@@ -138,7 +138,7 @@ DecWs dec_ws(const Dims& d) {
 // Backward of projection, mix and router: the recomputed forward (routing,
 // bucketing, weighted streams) and the backward's scratch.
 struct PbwdWs {
-  size_t idx, w, logits, proj, bhat, xhat, dz, sw, dg, dupart, dwrpart, total;
+  size_t idx, w, logits, proj, bhat, xhat, dz, us, sw, dg, dupart, dwrpart, total;
 };
 
 PbwdWs pbwd_ws(const Dims& d) {
@@ -152,6 +152,7 @@ PbwdWs pbwd_ws(const Dims& d) {
   w.bhat = off; off += align256(d.esize * pairs * d.GN);
   w.xhat = off; off += align256(d.esize * pairs * d.HP);
   w.dz = off; off += align256(d.esize * pairs * d.W);
+  w.us = off; off += align256(d.esize * pairs * d.D);
   w.sw = off; off += align256(sizeof(float) * pairs);
   w.dg = off; off += align256(sizeof(float) * d.M * d.E);
   w.dupart = off; off += align256(sizeof(float) * pairs * d.D);
@@ -343,8 +344,10 @@ swimba_status swimba_expert_project_mix_backward(
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
   if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
-  if (d.M * d.k * d.D >= (int64_t(1) << 40) || d.M * d.k * d.W >= (int64_t(1) << 40))
-    return fail(SWIMBA_ERR_DIMS, "problem too large");
+  // the backward GEMMs address an expert's pair rows with 32-bit byte offsets
+  if (d.M * d.k * d.D * (int64_t)d.esize >= (int64_t(1) << 31) ||
+      d.M * d.k * d.W * (int64_t)d.esize >= (int64_t(1) << 31))
+    return fail(SWIMBA_ERR_DIMS, "problem too large for 31-bit pair-row offsets");
   REQUIRE_PTR(dW_router);
   REQUIRE_PTR(dW_experts);
   if (d.M == 0) {
@@ -385,6 +388,7 @@ swimba_status swimba_expert_project_mix_backward(
   a.sorted_w = reinterpret_cast<const float*>(pws + play.sortw);
   a.offsets = reinterpret_cast<const int32_t*>(pws + play.offsets);
   a.dz = w8 + lay.dz;
+  a.us = w8 + lay.us;
   a.sw = reinterpret_cast<float*>(w8 + lay.sw);
   a.dg = reinterpret_cast<float*>(w8 + lay.dg);
   a.du_part = reinterpret_cast<float*>(w8 + lay.dupart);

@@ -113,6 +113,7 @@ struct ProjBwdArgs {
   const float* sorted_w;  // [M*k]
   const int32_t* offsets; // [E + 2]
   void* dz;               // [M*k, W] input type, sorted order
+  void* us;               // [M*k, D] input type: the pairs' token rows of u, sorted order
   float* sw;              // [M*k] w_j dw_j by pair id
   float* dg;              // [M, E]
   float* du_part;         // [M*k, D] by pair id

@@ -51,6 +51,12 @@ __global__ __launch_bounds__(256) void pbwd_dz_kernel(ProjBwdArgs A) {
     for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(v[j]);
     *reinterpret_cast<typename Vec<T>::x4*>(row + c) = o;
   }
+  // the pair's token row of u, in sorted order (the dW GEMM's B operand)
+  {
+    const int4v* src = reinterpret_cast<const int4v*>(static_cast<const T*>(A.u) + (size_t)m * A.D);
+    int4v* dst = reinterpret_cast<int4v*>(static_cast<T*>(A.us) + (size_t)i * A.D);
+    for (int q = lane; q < A.D * (int)sizeof(T) / 16; q += 64) dst[q] = src[q];
+  }
   float sum = 0.f;
   const S* bh = static_cast<const S*>(A.B_hat) + (size_t)p * A.GN;
   for (int n = 4 * lane; n < A.GN; n += 256) {
@@ -142,64 +148,43 @@ __global__ __launch_bounds__(256) void pbwd_router_kernel(ProjBwdArgs A) {
 
 // ---------------------------------------------------------------- grouped GEMMs
 
-// 128 x 128 output tiles, K steps of 32, four waves of 64 x 64 each. Tiles
-// are staged through LDS as 16-byte chunks (registers in between).
+// 128 x 128 output tiles, K steps of 32, four waves of 64 x 64 each. Tiles go
+// from HBM to LDS by buffer-to-LDS copies into a ring of four stages, issued
+// three K steps ahead of the products that read them; each lane's part of a
+// copy's offset is planned once and the K step enters as the copy's scalar
+// offset (every operand is a strided run of rows).
 //   MODE 0 (du): rows = one expert's sorted pairs, columns = d, K = w:
-//     A(i, w) = dz[i][w] (rows of dz, k contiguous), B(w, d) = W^(e)[w][d].
+//     A(i, w) = dz[i][w] (tile [row][k], read along rows),
+//     B(w, d) = W^(e)[w][d] (tile [k][col], read with the transposing read).
 //   MODE 1 (dW): rows = w, columns = d, K = the expert's sorted pairs:
-//     A(w, i) = dz[i][w] (K-major), B(i, d) = u[token of pair i][d].
-// K-major tiles ([k][row]) are read back with load_kmajor (the transposing LDS
-// read for 2-byte types) and stored with its swizzle; the k-contiguous A tile
-// of MODE 0 with the row swizzle.
-constexpr int kGB = 128, kGK = 32;
+//     A(w, i) = dz[i][w], B(i, d) = us[i][d] (both tiles [k][row]).
+// The buffer of a MODE 1 operand ends at the expert's last pair, so the rows
+// of a partial last K step read zeros; the K steps past the end of a turn of
+// the ring read zeros or are not multiplied.
+constexpr int kGB = 128, kGK = 32, kGS = 4;
 
 template <typename T, int MODE>
 struct GemmTiles {
-  static constexpr int ES = sizeof(T), EPC = 16 / ES;    // bytes, elements per 16-byte chunk
+  static constexpr int ES = sizeof(T), EPC = 16 / ES;  // bytes, elements per 16-byte chunk
   static constexpr int ACPR = MODE == 0 ? kGK / EPC : kGB / EPC;  // chunks per LDS row
-  static constexpr int BCPR = kGB / EPC;
-  static constexpr int PT = kGB * kGK / EPC / 256;       // chunks per thread and operand
+  static constexpr int AROWS = MODE == 0 ? kGB : kGK;
+  static constexpr int BCPR = kGB / EPC, BROWS = kGK;
+  static constexpr int AB = AROWS * ACPR * 16, BB = BROWS * BCPR * 16, STAGE = AB + BB;
+  static constexpr int MA = AROWS * ACPR / 256, MB = BROWS * BCPR / 256;  // copies per wave
+  static constexpr int CPW = MA + MB;
 };
-
-// Global reads of the K step at k0 into registers (zeros outside the problem).
-template <typename T, int MODE>
-__device__ __forceinline__ void pbwd_fetch(const ProjBwdArgs& A, const T* dz, const T* we,
-                                           const T* u, int r0, int nrows, int c0, int kbeg,
-                                           int klen, int k0, int4v* va, int4v* vb) {
-  typedef GemmTiles<T, MODE> G;
-#pragma unroll
-  for (int it = 0; it < G::PT; ++it) {
-    const int q = threadIdx.x + 256 * it;
-    va[it] = int4v{0, 0, 0, 0};
-    vb[it] = int4v{0, 0, 0, 0};
-    if constexpr (MODE == 0) {
-      const int r = q / G::ACPR, kk = k0 + (q % G::ACPR) * G::EPC;
-      if (r < nrows && kk < klen)
-        va[it] = *reinterpret_cast<const int4v*>(dz + (size_t)(r0 + r) * A.W + kk);
-    } else {
-      const int r = q / G::ACPR, kk = k0 + r, w = r0 + (q % G::ACPR) * G::EPC;
-      if (kk < klen && w < A.W)
-        va[it] = *reinterpret_cast<const int4v*>(dz + (size_t)(kbeg + kk) * A.W + w);
-    }
-    const int r = q / G::BCPR, kk = k0 + r, d = c0 + (q % G::BCPR) * G::EPC;
-    if (kk < klen && d < A.D) {
-      if constexpr (MODE == 0) {
-        vb[it] = *reinterpret_cast<const int4v*>(we + (size_t)kk * A.D + d);
-      } else {
-        const int tok = A.sorted[kbeg + kk] / A.k;
-        vb[it] = *reinterpret_cast<const int4v*>(u + (size_t)tok * A.D + d);
-      }
-    }
-  }
-}
 
 template <typename T, int MODE>
 __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
   typedef typename Vec<T>::x8 F;
   typedef GemmTiles<T, MODE> G;
-  constexpr int ACPR = G::ACPR, BCPR = G::BCPR, PT = G::PT;
-  __shared__ __align__(16) unsigned char As[kGB * kGK * G::ES];
-  __shared__ __align__(16) unsigned char Bs[kGB * kGK * G::ES];
+  constexpr int ACPR = G::ACPR, BCPR = G::BCPR;
+  constexpr uint32_t ES = G::ES;
+  // four stage arrays: copies into one are known not to touch the others
+  __shared__ __align__(16) unsigned char stg0[G::STAGE];
+  __shared__ __align__(16) unsigned char stg1[G::STAGE];
+  __shared__ __align__(16) unsigned char stg2[G::STAGE];
+  __shared__ __align__(16) unsigned char stg3[G::STAGE];
 
   const int E = A.E, D = A.D, W = A.W;
   const int ncol = (D + kGB - 1) / kGB;
@@ -207,7 +192,7 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
   // takes the contiguous logical range [x per, (x + 1) per) of the units,
   // which run row tile by row tile (all column tiles of one row tile
   // together): an XCD's workgroups share dz rows and one expert's weights
-  // (du), or one expert's dz columns and gathered token rows (dW), in its L2.
+  // (du), or one expert's dz and token rows (dW), in its L2.
   int units;
   if constexpr (MODE == 0) {
     int nt = 0;
@@ -248,68 +233,92 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
     klen = A.offsets[e + 1] - kbeg;
   }
   const T* dz = static_cast<const T*>(A.dz);
-  const T* we = static_cast<const T*>(A.w_experts) + (size_t)e * W * D;
-  const T* u = static_cast<const T*>(A.u);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, cl = lane & 15;
+  const int pairs = A.M * A.k;
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- operands: buffers, planned lane offsets, and the bytes one K step moves
+  BufRes rA, rB;
+  uint32_t aoff[G::MA], boff[G::MB];
+  uint32_t astep, bstep;
+  if constexpr (MODE == 0) {
+    const T* we = static_cast<const T*>(A.w_experts) + (size_t)e * W * D;
+    rA = make_rsrc(dz + (size_t)r0 * W, (uint64_t)(pairs - r0) * W * ES);
+    rB = make_rsrc(we + c0, (uint64_t)((size_t)W * D - c0) * ES);
+    dma_plan<G::AROWS, ACPR>((uint32_t)W * ES, wave, lane,
+                             [](int r) { return swz_row<T, ACPR>(r); }, aoff);
+    astep = kGK * ES;
+    bstep = kGK * (uint32_t)D * ES;
+  } else {
+    const T* us = static_cast<const T*>(A.us);
+    // (an expert without pairs gets empty buffers: every read is zero)
+    const size_t na = (size_t)klen * W, nb = (size_t)klen * D;
+    rA = make_rsrc(dz + (size_t)kbeg * W + r0, (uint64_t)(na > (size_t)r0 ? na - r0 : 0) * ES);
+    rB = make_rsrc(us + (size_t)kbeg * D + c0, (uint64_t)(nb > (size_t)c0 ? nb - c0 : 0) * ES);
+    dma_plan<G::AROWS, ACPR>((uint32_t)W * ES, wave, lane,
+                             [](int r) { return swz_tr<T, ACPR>(r); }, aoff);
+    astep = kGK * (uint32_t)W * ES;
+    bstep = kGK * (uint32_t)D * ES;
+  }
+  dma_plan<G::BROWS, BCPR>((uint32_t)D * ES, wave, lane,
+                           [](int r) { return swz_tr<T, BCPR>(r); }, boff);
+  auto fetch = [&](unsigned char* st, int kt) {
+    dma_tile_full<G::AROWS, ACPR>(rA, (uint32_t)kt * astep, aoff, st, wave);
+    dma_tile_full<G::BROWS, BCPR>(rB, (uint32_t)kt * bstep, boff, st + G::AB, wave);
+  };
+
   floatx4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  auto compute = [&](const unsigned char* st) {
+    const unsigned char* As = st;
+    const unsigned char* Bs = st + G::AB;
+    F bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = load_kmajor<T, BCPR>(Bs, 0, wn * 64 + 16 * j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      F af;
+      const int row = wm * 64 + 16 * i;
+      if constexpr (MODE == 0) {
+        // lane (g, c): k = 8g .. 8g + 7 of row row + c
+        const int r = row + cl;
+        if constexpr (ES == 2)
+          af = load8<T>(reinterpret_cast<const T*>(As + (r * ACPR + (g ^ swz_row<T, ACPR>(r))) * 16));
+        else
+          af = load8<T>(reinterpret_cast<const T*>(As + r * ACPR * 16 + 32 * g));
+      } else {
+        af = load_kmajor<T, ACPR>(As, 0, row, lane);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma16(af, bf[j], acc[i][j]);
+    }
+  };
 
-  // MODE 1 reads the next step's chunks during this step's products (its
-  // gathered rows of u take two dependent reads); MODE 0 reads them at the
-  // top of each step, which measured faster for it.
-  constexpr bool PF = MODE == 1;
-  int4v va[PT], vb[PT];
-  if (PF) pbwd_fetch<T, MODE>(A, dz, we, u, r0, nrows, c0, kbeg, klen, 0, va, vb);
-  for (int k0 = 0; k0 < klen; k0 += kGK) {
-    if (!PF) pbwd_fetch<T, MODE>(A, dz, we, u, r0, nrows, c0, kbeg, klen, k0, va, vb);
-    __syncthreads();  // the previous step's fragments are read
-#pragma unroll
-    for (int it = 0; it < PT; ++it) {
-      const int q = threadIdx.x + 256 * it;
-      {
-        const int r = q / ACPR, ch = q % ACPR;
-        const int sw = MODE == 0 ? swz_row<T, ACPR>(r) : swz_tr<T, ACPR>(r);
-        *reinterpret_cast<int4v*>(As + (r * ACPR + (ch ^ sw)) * 16) = va[it];
-      }
-      {
-        const int r = q / BCPR, ch = q % BCPR;
-        *reinterpret_cast<int4v*>(Bs + (r * BCPR + (ch ^ swz_tr<T, BCPR>(r))) * 16) = vb[it];
-      }
-    }
-    __syncthreads();
-    if (PF && k0 + kGK < klen)
-      pbwd_fetch<T, MODE>(A, dz, we, u, r0, nrows, c0, kbeg, klen, k0 + kGK, va, vb);
-#pragma unroll
-    for (int ks = 0; ks < kGK; ks += 32) {
-      F bf[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = load_kmajor<T, BCPR>(Bs, ks, wn * 64 + 16 * j, lane);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        F af;
-        const int row = wm * 64 + 16 * i;
-        if constexpr (MODE == 0) {
-          // lane (g, c): k = ks + 8g .. ks + 8g + 7 of row row + c
-          const int r = row + cl;
-          if constexpr (G::ES == 2)
-            af = load8<T>(reinterpret_cast<const T*>(
-                As + (r * ACPR + (((ks >> 3) + g) ^ swz_row<T, ACPR>(r))) * 16));
-          else
-            af = load8<T>(reinterpret_cast<const T*>(As + r * ACPR * 16 + (ks + 8 * g) * 4));
-        } else {
-          af = load_kmajor<T, ACPR>(As, ks, row, lane);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mma16(af, bf[j], acc[i][j]);
-      }
-    }
+  // whole turns of the four stages, every copy unconditional (steps past the
+  // end read zeros or are not multiplied)
+  const int nk = (klen + kGK - 1) / kGK;
+  const int nk4 = (nk + kGS - 1) / kGS * kGS;
+  fetch(stg0, 0);
+  fetch(stg1, 1);
+  fetch(stg2, 2);
+  auto iter = [&](int kt, const unsigned char* cur, unsigned char* far) {
+    wait_vm<2 * G::CPW>();  // step kt landed (steps kt + 1, kt + 2 may be in flight)
+    stage_barrier();        // step kt visible to all waves; step kt - 1 no longer read
+    fetch(far, kt + 3);
+    if (kt < nk) compute(cur);
+  };
+  for (int kt = 0; kt < nk4; kt += kGS) {
+    iter(kt, stg0, stg3);
+    iter(kt + 1, stg1, stg0);
+    iter(kt + 2, stg2, stg1);
+    iter(kt + 3, stg3, stg2);
   }
+  wait_vm<0>();  // the copies past the end land before the workgroup's LDS is released
 
   // lane (g, c) of tile (i, j) holds rows 16 i + 4 g + q, column 16 j + c
 #pragma unroll
