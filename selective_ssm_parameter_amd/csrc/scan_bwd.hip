@@ -268,16 +268,31 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
   for (int d = threadIdx.x; d <= BL; d += 256) pw[d] = powi(a, d);
   __syncthreads();
   const auto one = [](int) { return 1.f; };
-  tile_load<T, R, NP, 256>(Bs, static_cast<const S*>(A.B_hat) + (m0 * KS) * G * N + grp * N,
-                           (size_t)G * N, Lc * KS, N, one);
-  tile_load<T, R, kBP, 256>(Xd, static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP,
-                            (size_t)H * kBP, Lc * KS, kBP,
-                            [&](int r) { return r < Lc * KS ? pw[Lc - 1 - r / KS] : 0.f; });
-  tile_load<T, BL, NP, 256>(Cs, static_cast<const S*>(A.C_mix) + m0 * G * N + grp * N,
-                            (size_t)G * N, Lc, N, one);
-  const float sdy = tile_load_scaled<T, BL, kBP, 256>(
-      Dyd, static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP, (size_t)H * kBP, Lc, kBP,
-      [&](int s) { return s < Lc ? pw[s] : 0.f; }, red);
+  const auto xdec = [&](int r) { return r < Lc * KS ? pw[Lc - 1 - r / KS] : 0.f; };
+  const auto ydec = [&](int s) { return s < Lc ? pw[s] : 0.f; };
+  // every tile's reads in flight at once, then dy's scale, then the stores
+  TileLoad<T, R, NP, 256, S> LB;
+  TileLoad<T, R, kBP, 256, S> LX;
+  TileLoad<T, BL, NP, 256, S> LC;
+  TileLoad<T, BL, kBP, 256, TY> LY;
+  LB.fetch(static_cast<const S*>(A.B_hat) + (m0 * KS) * G * N + grp * N, (size_t)G * N, Lc * KS,
+           N);
+  LX.fetch(static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP, (size_t)H * kBP,
+           Lc * KS, kBP);
+  LC.fetch(static_cast<const S*>(A.C_mix) + m0 * G * N + grp * N, (size_t)G * N, Lc, N);
+  LY.fetch(static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP, (size_t)H * kBP, Lc, kBP);
+  float my = LY.absmax(ydec);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) my = fmaxf(my, __shfl_xor(my, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = my;
+  __syncthreads();
+  my = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // 2^-e brings dy's largest decayed magnitude into [1/2, 1); capped for subnormals
+  const float sdy = my > 0.f ? ldexpf(1.f, min(-(ilogbf(my) + 1), 126)) : 1.f;
+  LB.store(Bs, one, 1.f);
+  LX.store(Xd, xdec, 1.f);
+  LC.store(Cs, one, 1.f);
+  LY.store(Dyd, ydec, sdy);
   __syncthreads();
   const float udy = 1.f / sdy;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, cl = lane & 15;
