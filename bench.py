@@ -209,10 +209,12 @@ def backward_models(wl):
       local:  S = B_hat^T X (2NPR), R = C~^T dy (2NPL)
       grad:   Gm = C~ B_hat^T (LRN, once per group), D = dy X^T (LRP),
               dX (PRL + 2PRN), dB_hat (NRL + 2NRP), dC~ (NLR + 2NLP)
-    bytes: the streams and dy read once, the two chunk-state sets [nc, H, N, P]
-    fp32 written by local, read and written by the sweep, read by grad, and
-    the fp32 gradients written once. Projection backward: two grouped GEMMs of
-    2 (pairs) W D flops each."""
+    bytes: the streams and dy read once; the two local chunk-state sets
+    [nc, H, N, P] written by local in the operand type (fp16 for bf16
+    problems) and read by the sweep, which writes the entering states H_c and
+    F_c in fp32 for grad to read; the fp32 gradients written once. Projection
+    backward: two grouped GEMMs of 2 (pairs) W D flops each; the dz kernel
+    also copies each pair's token row of u into sorted order for the dW GEMM."""
     M, D, E, k = wl.tokens, wl.d_model, wl.n_experts, wl.top_k
     H, P, N, G = wl.nheads, wl.headdim, wl.dstate, wl.ngroups
     W, HP, GN = wl.width, H * P, G * N
@@ -223,6 +225,7 @@ def backward_models(wl):
     nch = wl.batch * -(-wl.seqlen // L)          # chunks over the batch
     R = k * L
     states = nch * H * N * P * 4                  # one chunk-state set, fp32
+    lstates = nch * H * N * P * es                # one local chunk-state set
     streams = pairs * (HP + GN) * es + M * GN * es
     dy = M * HP * ei
     grad_flops = nch * (G * L * R * N + H * (L * R * P + P * R * L + 2 * P * R * N + N * R * L
@@ -230,12 +233,12 @@ def backward_models(wl):
     models = dict(kernel_models(wl))
     models.update({
         "scan_bwd_local": ("hbm", nch * H * (2 * N * P * R + 2 * N * P * L),
-                           streams + dy + 2 * states),
-        "scan_bwd_sweep": ("hbm", 0, 4 * states),
+                           streams + dy + 2 * lstates),
+        "scan_bwd_sweep": ("hbm", 0, 2 * lstates + 2 * states),
         "scan_bwd_grad": ("hbm", grad_flops,
                           streams + dy + 2 * states + pairs * (HP + GN) * 4 + M * GN * 4),
         "proj_bwd_dz": ("hbm", 0, pairs * (HP + GN) * 4 + M * GN * 4 + pairs * GN * (es + 4)
-                        + pairs * W * ei + pairs * 8),
+                        + pairs * W * ei + pairs * 8 + 2 * pairs * D * ei),
         "proj_bwd_router": ("hbm", 2 * M * E * D, M * E * 4 + pairs * 8 + E * D * ei
                             + M * D * 4 + M * E * 4),
         "proj_bwd_du": ("mfma", 2 * pairs * W * D, pairs * W * ei + E * W * D * ei
