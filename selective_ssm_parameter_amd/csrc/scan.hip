@@ -698,9 +698,15 @@ static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   return v ? atoi(v) : dflt;
 }
-static int scan_target_wgs() {
-  static const int w = env_int("SWIMBA_SCAN_WGS", 512);
-  return w > 0 ? w : 512;
+// Workgroups the prefill walk aims at (segments per sequence follow from it).
+// Measured on MI355X: chunks of 64 tokens (3 block pairs each) run fastest
+// with about 1024 (8 x 2048 tokens, 24 heads: 5 segments of 7 chunks, chunk
+// output 94 -> 80 us), longer chunks with 512 (4 x 8192 tokens with L = 128
+// and 65536 tokens with L = 256 both lose 2-10 % at 384, 768 or 1024).
+static int scan_target_wgs(int L) {
+  static const int w = env_int("SWIMBA_SCAN_WGS", 0);
+  if (w > 0) return w;
+  return L <= 64 ? 1024 : 512;
 }
 
 static int scan_npairs(int L, int bt) {
@@ -721,7 +727,7 @@ ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int 
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
   const int units = Bt * H;
-  int want = scan_target_wgs() / units;
+  int want = scan_target_wgs(L) / units;
   if (want > nc) want = nc;
   if (want < 1) want = 1;
   g.seg_chunks = (nc + want - 1) / want;
