@@ -27,8 +27,8 @@ __device__ void route_tokens(const float* lg, int ldl, int tok0, int tpw, int M,
 // before their matrix-core ops, so a wave waits for memory once per batch
 // rather than once per load (8 steps of 2-byte data, 4 of fp32).
 
-template <typename T, int GT>
-__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
+template <typename T, int GT, int NW>
+__global__ __launch_bounds__(64 * NW) void route_kernel(const T* __restrict__ u,
                                                     const T* __restrict__ wr, int M, int D,
                                                     int E, int k, int32_t* __restrict__ idx,
                                                     float* __restrict__ wout,
@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u,
   const int ET = (E + 15) / 16;
   const int ldl = E + 1;
   // Waves over (token tile, K slice): with few tokens per workgroup d_model
-  // is split over the waves that would otherwise be idle (ksplit * ntt <= 4).
+  // is split over the waves that would otherwise be idle (ksplit * ntt <=
+  // the workgroup's waves).
   const int ntt = tpw / 16;
   const int tt = wave % ntt, ks = wave / ntt;
   const int nsteps = D / 32;
@@ -132,12 +133,12 @@ __device__ void route_tokens(const float* lg, int ldl, int tok0, int tpw, int M,
                              int32_t* __restrict__ idx, float* __restrict__ wout,
                              float* __restrict__ logits, int* hcnt) {
   constexpr int kNone = 0x7fffffff;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int sg = 1;
   while (4 * sg < E) sg *= 2;
   const int per_wave = 64 / sg;
   const int sub = lane / sg, sl = lane % sg;
-  for (int t0 = wave * per_wave; t0 < tpw; t0 += 4 * per_wave) {
+  for (int t0 = wave * per_wave; t0 < tpw; t0 += nw * per_wave) {
     const int t = t0 + sub;
     const int m = tok0 + t;
     const bool valid = t < tpw && m < M;
@@ -197,36 +198,45 @@ hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M
                         int32_t* idx, float* w, float* logits, hipStream_t s, int32_t* hist) {
   if (M == 0) return hipSuccess;
   const int tpw = route_tokens_per_wg(M);
-  dim3 grid((M + tpw - 1) / tpw), block(256);
-  // 16 (32) tokens per workgroup: d_model split 4 (2) ways over the waves, as
-  // long as the partial logits fit 64 KiB of LDS
-  int ksplit = 64 / tpw;
-  while (ksplit > 1 && (size_t)ksplit * tpw * (E + 1) * sizeof(float) > 65536) ksplit /= 2;
-  size_t lds = (size_t)ksplit * tpw * (E + 1) * sizeof(float) + (size_t)(E + 1) * sizeof(int);
   const int ET = (E + 15) / 16;
   const int GT = ET >= 4 ? 4 : (ET >= 2 ? 2 : 1);
+  // Decode-sized batches (16 tokens per workgroup, up to 32 experts): 16
+  // waves, d_model split 16 ways, so each wave's slice of the K loop is one
+  // batch of reads; otherwise 4 waves. The split shrinks while the partial
+  // logits would not fit 64 KiB of LDS.
+  const bool wide = tpw == 16 && GT <= 2;
+  const int nwaves = wide ? 16 : 4;
+  dim3 grid((M + tpw - 1) / tpw), block(64 * nwaves);
+  int ksplit = nwaves / (tpw / 16);
+  while (ksplit > 1 && (size_t)ksplit * tpw * (E + 1) * sizeof(float) > 65536) ksplit /= 2;
+  size_t lds = (size_t)ksplit * tpw * (E + 1) * sizeof(float) + (size_t)(E + 1) * sizeof(int);
   const void* fn;
-  if (is_bf16)
-    fn = GT == 4 ? (const void*)route_kernel<bf16, 4>
-                 : (GT == 2 ? (const void*)route_kernel<bf16, 2> : (const void*)route_kernel<bf16, 1>);
-  else
-    fn = GT == 4 ? (const void*)route_kernel<float, 4>
-                 : (GT == 2 ? (const void*)route_kernel<float, 2> : (const void*)route_kernel<float, 1>);
+#define SWIMBA_ROUTE_FN(TT)                                                                     \
+  (wide ? (GT == 2 ? (const void*)route_kernel<TT, 2, 16> : (const void*)route_kernel<TT, 1, 16>) \
+        : (GT == 4 ? (const void*)route_kernel<TT, 4, 4>                                         \
+                   : (GT == 2 ? (const void*)route_kernel<TT, 2, 4> : (const void*)route_kernel<TT, 1, 4>)))
+  if (is_bf16) fn = SWIMBA_ROUTE_FN(bf16);
+  else fn = SWIMBA_ROUTE_FN(float);
+#undef SWIMBA_ROUTE_FN
   hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   prof_begin("route_topk", s);
-#define SWIMBA_ROUTE(TT, G)                                                                     \
-  hipLaunchKernelGGL((route_kernel<TT, G>), grid, block, lds, s, (const TT*)u,                 \
+#define SWIMBA_ROUTE(TT, G, W)                                                                  \
+  hipLaunchKernelGGL((route_kernel<TT, G, W>), grid, block, lds, s, (const TT*)u,              \
                      (const TT*)w_router, M, D, E, k, idx, w, logits, hist, tpw, ksplit)
+#define SWIMBA_ROUTE_T(TT)                       \
+  if (wide) {                                    \
+    if (GT == 2) SWIMBA_ROUTE(TT, 2, 16);        \
+    else SWIMBA_ROUTE(TT, 1, 16);                \
+  } else if (GT == 4) SWIMBA_ROUTE(TT, 4, 4);    \
+  else if (GT == 2) SWIMBA_ROUTE(TT, 2, 4);      \
+  else SWIMBA_ROUTE(TT, 1, 4);
   if (is_bf16) {
-    if (GT == 4) SWIMBA_ROUTE(bf16, 4);
-    else if (GT == 2) SWIMBA_ROUTE(bf16, 2);
-    else SWIMBA_ROUTE(bf16, 1);
+    SWIMBA_ROUTE_T(bf16)
   } else {
-    if (GT == 4) SWIMBA_ROUTE(float, 4);
-    else if (GT == 2) SWIMBA_ROUTE(float, 2);
-    else SWIMBA_ROUTE(float, 1);
+    SWIMBA_ROUTE_T(float)
   }
+#undef SWIMBA_ROUTE_T
 #undef SWIMBA_ROUTE
   prof_end(s);
   return hipGetLastError();
