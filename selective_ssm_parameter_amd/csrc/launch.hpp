@@ -92,8 +92,8 @@ hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N
 // Backward of the expert projections, the mix and the router (see
 // swimba_expert_project_mix_backward). The forward's routing (idx, topk_w,
 // logits), bucketing (sorted, sorted_w, offsets) and weighted streams (B_hat,
-// c_part) are recomputed by the caller; dz, sw, dg, du_part and dwr_part are
-// scratch of proj_bwd_splits(M) dW_r splits.
+// c_part) are recomputed by the caller; dz, us, sw, dg, du_part and dwr_part
+// are scratch (dwr_part of proj_bwd_splits(M) dW_r splits).
 struct ProjBwdArgs {
   const void* u;          // [M, D] input type
   const void* w_router;   // [E, D]

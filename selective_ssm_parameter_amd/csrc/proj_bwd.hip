@@ -11,22 +11,23 @@
 //   dW^(e) = sum over the pairs of expert e of dz_j u^T,   dW_r = dg^T u
 // The top-k set is piecewise constant in the logits and has no gradient.
 // The forward routing and projection are recomputed (same kernels, so the
-// same bits); the pairs come sorted by expert from the bucketing, and
-// dz is materialised in that order so both grouped GEMMs read contiguous
-// rows. GEMM operands bf16 (fp32 for fp32 problems), fp32 accumulation, fp32
-// outputs; every sum over slots, tokens or splits runs in a fixed order.
+// same bits); the pairs come sorted by expert from the bucketing, and dz and
+// the pairs' token rows of u are materialised in that order so both grouped
+// GEMMs read contiguous rows. GEMM operands bf16 (fp32 for fp32 problems),
+// fp32 accumulation, fp32 outputs; every sum over slots, tokens or splits
+// runs in a fixed order.
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_tiles.hpp"
 
 namespace swimba {
 
-
 // ---------------------------------------------------------------- dz and dw
 
-// One wave per sorted pair: dz in sorted order, and the pair's share of the
-// router gradient s_j = w_j dw_j = <w B_j, dB_hat_j> + <w C_j, dC~> (the
-// weighted streams are what the forward keeps, so no division by w).
+// One wave per sorted pair: dz and the pair's token row of u in sorted order,
+// and the pair's share of the router gradient s_j = w_j dw_j = <w B_j,
+// dB_hat_j> + <w C_j, dC~> (the weighted streams are what the forward keeps,
+// so no division by w).
 template <typename T, typename S>
 __global__ __launch_bounds__(256) void pbwd_dz_kernel(ProjBwdArgs A) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -148,9 +149,9 @@ __global__ __launch_bounds__(256) void pbwd_router_kernel(ProjBwdArgs A) {
 
 // ---------------------------------------------------------------- grouped GEMMs
 
-// 128 x 128 output tiles, K steps of 32, four waves of 64 x 64 each. Tiles go
-// from HBM to LDS by buffer-to-LDS copies into a ring of four stages, issued
-// three K steps ahead of the products that read them; each lane's part of a
+// 128 x 128 output tiles, four waves of 64 x 64 each. Tiles go from HBM to
+// LDS by buffer-to-LDS copies into a ring of stages, issued ahead of the
+// products that read them; each lane's part of a
 // copy's offset is planned once and the K step enters as the copy's scalar
 // offset (every operand is a strided run of rows).
 //   MODE 0 (du): rows = one expert's sorted pairs, columns = d, K = w:
@@ -161,14 +162,17 @@ __global__ __launch_bounds__(256) void pbwd_router_kernel(ProjBwdArgs A) {
 // The buffer of a MODE 1 operand ends at the expert's last pair, so the rows
 // of a partial last K step read zeros; the K steps past the end of a turn of
 // the ring read zeros or are not multiplied.
-constexpr int kGB = 128, kGK = 32, kGS = 4;
+constexpr int kGB = 128;
 
+// MODE 0 takes K steps of 64 (its dz rows then arrive as 128-byte segments)
+// in a ring of two stages; MODE 1 K steps of 32 in a ring of four.
 template <typename T, int MODE>
 struct GemmTiles {
+  static constexpr int BK = MODE == 0 ? 64 : 32, NS = MODE == 0 ? 2 : 4;
   static constexpr int ES = sizeof(T), EPC = 16 / ES;  // bytes, elements per 16-byte chunk
-  static constexpr int ACPR = MODE == 0 ? kGK / EPC : kGB / EPC;  // chunks per LDS row
-  static constexpr int AROWS = MODE == 0 ? kGB : kGK;
-  static constexpr int BCPR = kGB / EPC, BROWS = kGK;
+  static constexpr int ACPR = MODE == 0 ? BK / EPC : kGB / EPC;  // chunks per LDS row
+  static constexpr int AROWS = MODE == 0 ? kGB : BK;
+  static constexpr int BCPR = kGB / EPC, BROWS = BK;
   static constexpr int AB = AROWS * ACPR * 16, BB = BROWS * BCPR * 16, STAGE = AB + BB;
   static constexpr int MA = AROWS * ACPR / 256, MB = BROWS * BCPR / 256;  // copies per wave
   static constexpr int CPW = MA + MB;
@@ -180,11 +184,12 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
   typedef GemmTiles<T, MODE> G;
   constexpr int ACPR = G::ACPR, BCPR = G::BCPR;
   constexpr uint32_t ES = G::ES;
-  // four stage arrays: copies into one are known not to touch the others
+  // stage arrays (NS of them are used): copies into one are known not to
+  // touch the others
   __shared__ __align__(16) unsigned char stg0[G::STAGE];
   __shared__ __align__(16) unsigned char stg1[G::STAGE];
-  __shared__ __align__(16) unsigned char stg2[G::STAGE];
-  __shared__ __align__(16) unsigned char stg3[G::STAGE];
+  __shared__ __align__(16) unsigned char stg2[G::NS == 4 ? G::STAGE : 16];
+  __shared__ __align__(16) unsigned char stg3[G::NS == 4 ? G::STAGE : 16];
 
   const int E = A.E, D = A.D, W = A.W;
   const int ncol = (D + kGB - 1) / kGB;
@@ -248,8 +253,8 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
     rB = make_rsrc(we + c0, (uint64_t)((size_t)W * D - c0) * ES);
     dma_plan<G::AROWS, ACPR>((uint32_t)W * ES, wave, lane,
                              [](int r) { return swz_row<T, ACPR>(r); }, aoff);
-    astep = kGK * ES;
-    bstep = kGK * (uint32_t)D * ES;
+    astep = G::BK * ES;
+    bstep = G::BK * (uint32_t)D * ES;
   } else {
     const T* us = static_cast<const T*>(A.us);
     // (an expert without pairs gets empty buffers: every read is zero)
@@ -258,8 +263,8 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
     rB = make_rsrc(us + (size_t)kbeg * D + c0, (uint64_t)(nb > (size_t)c0 ? nb - c0 : 0) * ES);
     dma_plan<G::AROWS, ACPR>((uint32_t)W * ES, wave, lane,
                              [](int r) { return swz_tr<T, ACPR>(r); }, aoff);
-    astep = kGK * (uint32_t)W * ES;
-    bstep = kGK * (uint32_t)D * ES;
+    astep = G::BK * (uint32_t)W * ES;
+    bstep = G::BK * (uint32_t)D * ES;
   }
   dma_plan<G::BROWS, BCPR>((uint32_t)D * ES, wave, lane,
                            [](int r) { return swz_tr<T, BCPR>(r); }, boff);
@@ -277,46 +282,66 @@ __global__ __launch_bounds__(256) void pbwd_gemm_kernel(ProjBwdArgs A) {
   auto compute = [&](const unsigned char* st) {
     const unsigned char* As = st;
     const unsigned char* Bs = st + G::AB;
-    F bf[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = load_kmajor<T, BCPR>(Bs, 0, wn * 64 + 16 * j, lane);
+    for (int ks = 0; ks < G::BK; ks += 32) {
+      F bf[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      F af;
-      const int row = wm * 64 + 16 * i;
-      if constexpr (MODE == 0) {
-        // lane (g, c): k = 8g .. 8g + 7 of row row + c
-        const int r = row + cl;
-        if constexpr (ES == 2)
-          af = load8<T>(reinterpret_cast<const T*>(As + (r * ACPR + (g ^ swz_row<T, ACPR>(r))) * 16));
-        else
-          af = load8<T>(reinterpret_cast<const T*>(As + r * ACPR * 16 + 32 * g));
-      } else {
-        af = load_kmajor<T, ACPR>(As, 0, row, lane);
+      for (int j = 0; j < 4; ++j) bf[j] = load_kmajor<T, BCPR>(Bs, ks, wn * 64 + 16 * j, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        F af;
+        const int row = wm * 64 + 16 * i;
+        if constexpr (MODE == 0) {
+          // lane (g, c): k = ks + 8g .. ks + 8g + 7 of row row + c
+          const int r = row + cl;
+          if constexpr (ES == 2)
+            af = load8<T>(reinterpret_cast<const T*>(
+                As + (r * ACPR + (((ks >> 3) + g) ^ swz_row<T, ACPR>(r))) * 16));
+          else
+            af = load8<T>(reinterpret_cast<const T*>(As + r * ACPR * 16 + (ks + 8 * g) * 4));
+        } else {
+          af = load_kmajor<T, ACPR>(As, ks, row, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma16(af, bf[j], acc[i][j]);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma16(af, bf[j], acc[i][j]);
     }
   };
 
-  // whole turns of the four stages, every copy unconditional (steps past the
-  // end read zeros or are not multiplied)
-  const int nk = (klen + kGK - 1) / kGK;
-  const int nk4 = (nk + kGS - 1) / kGS * kGS;
-  fetch(stg0, 0);
-  fetch(stg1, 1);
-  fetch(stg2, 2);
-  auto iter = [&](int kt, const unsigned char* cur, unsigned char* far) {
-    wait_vm<2 * G::CPW>();  // step kt landed (steps kt + 1, kt + 2 may be in flight)
-    stage_barrier();        // step kt visible to all waves; step kt - 1 no longer read
-    fetch(far, kt + 3);
-    if (kt < nk) compute(cur);
-  };
-  for (int kt = 0; kt < nk4; kt += kGS) {
-    iter(kt, stg0, stg3);
-    iter(kt + 1, stg1, stg0);
-    iter(kt + 2, stg2, stg1);
-    iter(kt + 3, stg3, stg2);
+  const int nk = (klen + G::BK - 1) / G::BK;
+  if constexpr (G::NS == 4) {
+    // whole turns of the four stages, every copy unconditional (steps past
+    // the end read zeros or are not multiplied)
+    const int nk4 = (nk + 3) / 4 * 4;
+    fetch(stg0, 0);
+    fetch(stg1, 1);
+    fetch(stg2, 2);
+    auto iter = [&](int kt, const unsigned char* cur, unsigned char* far) {
+      wait_vm<2 * G::CPW>();  // step kt landed (steps kt + 1, kt + 2 may be in flight)
+      stage_barrier();        // step kt visible to all waves; step kt - 1 no longer read
+      fetch(far, kt + 3);
+      if (kt < nk) compute(cur);
+    };
+    for (int kt = 0; kt < nk4; kt += 4) {
+      iter(kt, stg0, stg3);
+      iter(kt + 1, stg1, stg0);
+      iter(kt + 2, stg2, stg1);
+      iter(kt + 3, stg3, stg2);
+    }
+  } else {
+    // two stages: the copies of step kt + 1 run during the products of step kt
+    const int nk2 = (nk + 1) / 2 * 2;
+    fetch(stg0, 0);
+    auto iter = [&](int kt, const unsigned char* cur, unsigned char* far) {
+      wait_vm<0>();     // step kt landed
+      stage_barrier();  // step kt visible to all waves; step kt - 1 no longer read
+      fetch(far, kt + 1);
+      if (kt < nk) compute(cur);
+    };
+    for (int kt = 0; kt < nk2; kt += 2) {
+      iter(kt, stg0, stg1);
+      iter(kt + 1, stg1, stg0);
+    }
   }
   wait_vm<0>();  // the copies past the end land before the workgroup's LDS is released
 
