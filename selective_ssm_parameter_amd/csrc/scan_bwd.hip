@@ -137,6 +137,35 @@ __device__ __forceinline__ floatx4 tmm(const unsigned char* At, const unsigned c
   return acc;
 }
 
+// The NK = K / 32 fragments of one operand of a tile column (or row) block:
+// ROW: along tile rows (frag_row at row c0), else down tile columns
+// (load_kmajor at column c0).
+template <typename T, bool ROW, int CPR, int NK>
+__device__ __forceinline__ void load_frags(const unsigned char* t, int c0,
+                                           typename Vec<T>::x8* f, int lane) {
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    if constexpr (ROW) f[s] = frag_row<T, CPR>(t, c0, 32 * s, lane);
+    else f[s] = load_kmajor<T, CPR>(t, 32 * s, c0, lane);
+  }
+}
+
+// One 16 x 16 tile with the B operand's fragments given (loaded once for all
+// the tiles of a wave that share them); A as in tmm.
+template <typename T, bool AROW, int ACPR, int NK>
+__device__ __forceinline__ floatx4 tmm_b(const unsigned char* At, int m0,
+                                         const typename Vec<T>::x8* bf, int lane) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    typename Vec<T>::x8 fa;
+    if constexpr (AROW) fa = frag_row<T, ACPR>(At, m0, 32 * s, lane);
+    else fa = load_kmajor<T, ACPR>(At, 32 * s, m0, lane);
+    acc = mma16(fa, bf[s], acc);
+  }
+  return acc;
+}
+
 template <typename SRC> struct Raw16;
 template <> struct Raw16<f16> { typedef f16x8 type; };
 template <> struct Raw16<bf16> { typedef bf16x8 type; };
@@ -551,13 +580,20 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
     const float udy = 1.f / scl[0], uF = 1.f / scl[1], uHdy = 1.f / (scl[2] * scl[0]);
     __syncthreads();
     float dap = eh * (float)Lc * pw[Lc - 1];  // this lane's part of da for the head
+    // Every phase's tiles t = wave + NW i of a wave share one column block
+    // (NW is a multiple of the column blocks), so that operand's fragments
+    // are loaded once per phase.
+    static_assert(NW % (R / 16) == 0 && NW % (BL / 16) == 0, "fixed column block per wave");
+    typedef typename Vec<T>::x8 F;
     // D[s][r] = dy_s . X_r; the masked, decayed D and Gm; the Gm D term of da
+    F fx[kBP / 32];
+    load_frags<T, true, CX, kBP / 32>(Xs, 16 * (wave % (R / 16)), fx, lane);
 #pragma unroll
     for (int i = 0; i < GI; ++i) {
       const int t = wave + NW * i;
       if (t >= NGT) continue;
       const int s0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
-      const floatx4 v = tmm<T, true, CX, true, CX>(Dys, Xs, s0, r0, kBP, lane);
+      const floatx4 v = tmm_b<T, true, CX, kBP / 32>(Dys, s0, fx, lane);
       const int r = r0 + cl, tr = r / KS;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -571,10 +607,14 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
     }
     __syncthreads();
     // dX_r^T[p] = sum_s dy_s[p] GmM[s][r] + a^{Lc-1-t} (F_c^T B_hat_r)[p]
+    {
+      F fg[BL / 32], fb[NP / 32];
+      load_frags<T, false, CG, BL / 32>(GmM, 16 * (wave % (R / 16)), fg, lane);
+      load_frags<T, true, CB, NP / 32>(Bs, 16 * (wave % (R / 16)), fb, lane);
     for (int t = wave; t < NXT; t += NW) {
       const int p0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
-      floatx4 v = tmm<T, false, CX, false, CG>(Dys, GmM, p0, r0, BL, lane);
-      const floatx4 w = tmm<T, false, CX, true, CB>(Ss, Bs, p0, r0, NP, lane);
+      floatx4 v = tmm_b<T, false, CX, BL / 32>(Dys, p0, fg, lane);
+      const floatx4 w = tmm_b<T, false, CX, NP / 32>(Ss, p0, fb, lane);
       const int r = r0 + cl, tr = r / KS;
       if (tr < Lc) {
         v = v * udy + w * (pw[Lc - 1 - tr] * uF);
@@ -582,14 +622,17 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
         *reinterpret_cast<floatx4*>(A.dX + row * kBP + p0 + 4 * g) = v;
       }
     }
+    }
     // dB_hat_r[n] += sum_s C~_s[n] Dm[s][r] + a^{Lc-1-t} (F_c X_r)[n]
+    F fd[BL / 32];
+    load_frags<T, false, CG, BL / 32>(Dm, 16 * (wave % (R / 16)), fd, lane);
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       const int t = wave + NW * i;
       const int n0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
       if (t >= NBT || n0 >= N) continue;
-      const floatx4 v = tmm<T, false, CB, false, CG>(Cs, Dm, n0, r0, BL, lane);
-      const floatx4 w = tmm<T, true, CX, true, CX>(Ss, Xs, n0, r0, kBP, lane);
+      const floatx4 v = tmm_b<T, false, CB, BL / 32>(Cs, n0, fd, lane);
+      const floatx4 w = tmm_b<T, true, CX, kBP / 32>(Ss, n0, fx, lane);
       const int r = r0 + cl, tr = r / KS;
       const float sc = tr < Lc ? pw[Lc - 1 - tr] : 0.f;
       const float wt = tr + 1 < Lc ? (float)(Lc - 1 - tr) * pw[Lc - 2 - tr] : 0.f;
@@ -599,13 +642,16 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
       __builtin_amdgcn_sched_barrier(0);  // keep the tiles' reads from piling up in registers
     }
     // dC~_s[n] += sum_r B_hat_r[n] Dm[s][r] + a^{s+1} (H_c dy_s)[n]
+    F fm[R / 32], fy[kBP / 32];
+    load_frags<T, true, CG, R / 32>(Dm, 16 * (wave % (BL / 16)), fm, lane);
+    load_frags<T, true, CX, kBP / 32>(Dys, 16 * (wave % (BL / 16)), fy, lane);
 #pragma unroll
     for (int i = 0; i < CI; ++i) {
       const int t = wave + NW * i;
       const int n0 = 16 * (t / (BL / 16)), s0 = 16 * (t % (BL / 16));
       if (t >= NCT || n0 >= N) continue;
-      const floatx4 v = tmm<T, false, CB, true, CG>(Bs, Dm, n0, s0, R, lane);
-      const floatx4 w = tmm<T, true, CX, true, CX>(Hs, Dys, n0, s0, kBP, lane);
+      const floatx4 v = tmm_b<T, false, CB, R / 32>(Bs, n0, fm, lane);
+      const floatx4 w = tmm_b<T, true, CX, kBP / 32>(Hs, n0, fy, lane);
       const int s = s0 + cl;
       const float sc = s < Lc ? pw[s + 1] : 0.f;
       const float wt = s < Lc ? (float)(s + 1) * pw[s] : 0.f;
