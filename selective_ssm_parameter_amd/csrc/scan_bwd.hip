@@ -328,16 +328,22 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
   const size_t sbase = (((size_t)b * A.nb + c) * H + h) * (size_t)N * kBP;
   constexpr int TILES = (NP / 16) * (kBP / 16), TI = TILES / 4;
   // S[n][p] = sum_r B_hat[r][n] xd[r][p];  R[n][p] = sum_s C~[s][n] dyd[s][p]
+  // (wave w owns column block p0 = 16 w of every tile it computes, so the
+  // xd and dyd fragments are read once)
+  typedef typename Vec<T>::x8 F;
+  F fx[R / 32], fy[BL / 32];
+  load_frags<T, false, CX, R / 32>(Xd, 16 * wave, fx, lane);
+  load_frags<T, false, CX, BL / 32>(Dyd, 16 * wave, fy, lane);
   floatx4 s4[TI], r4[TI];
   float ms = 0.f, mr = 0.f;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     const int t = wave + 4 * i;
-    const int n0 = 16 * (t / (kBP / 16)), p0 = 16 * (t % (kBP / 16));
+    const int n0 = 16 * (t / (kBP / 16));
     s4[i] = r4[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (n0 < N) {
-      s4[i] = tmm<T, false, CB, false, CX>(Bs, Xd, n0, p0, R, lane);
-      r4[i] = tmm<T, false, CB, false, CX>(Cs, Dyd, n0, p0, BL, lane) * udy;
+      s4[i] = tmm_b<T, false, CB, R / 32>(Bs, n0, fx, lane);
+      r4[i] = tmm_b<T, false, CB, BL / 32>(Cs, n0, fy, lane) * udy;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
