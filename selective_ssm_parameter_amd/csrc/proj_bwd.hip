@@ -378,21 +378,42 @@ __global__ void pbwd_du_sum_kernel(ProjBwdArgs A) {
 }
 
 // dW_r partials over splits of kDwrTokens tokens: block (column tile of 64,
-// split); thread (sub, c) takes column c and every fourth token of the split
-// starting at sub, 16 experts at a time, with the split's router gradients
-// for those experts staged in LDS; the four subs are added in order.
+// split). The split's u columns (all their 16-byte reads in flight at once)
+// and, 16 experts at a time, its router gradients are staged in LDS; thread
+// (sub, c) takes column c and every fourth token of the split starting at
+// sub; the four subs are added in order.
 constexpr int kDwrTokens = 256;
 
 template <typename T>
 __global__ __launch_bounds__(256) void pbwd_dwr_kernel(ProjBwdArgs A) {
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  constexpr int CPT = 64 / EPC;              // chunks per token row of the tile
+  constexpr int IT = kDwrTokens * CPT / 256; // chunks per thread
   __shared__ float part[4][16][64];
   __shared__ __align__(16) float sdg[kDwrTokens][16];
+  __shared__ __align__(16) T su[kDwrTokens][64];
   const int c = threadIdx.x & 63, sub = threadIdx.x >> 6;
-  const int d = blockIdx.x * 64 + c, sp = blockIdx.y;
+  const int d0 = blockIdx.x * 64, d = d0 + c, sp = blockIdx.y;
   const int m0 = sp * kDwrTokens, m1 = min(A.M, m0 + kDwrTokens);
   const T* u = static_cast<const T*>(A.u);
+  {
+    int4v v[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int q = threadIdx.x + 256 * i;
+      const int t = q / CPT, cc = (q % CPT) * EPC;
+      v[i] = int4v{0, 0, 0, 0};
+      if (m0 + t < m1 && d0 + cc < A.D)
+        v[i] = *reinterpret_cast<const int4v*>(u + (size_t)(m0 + t) * A.D + d0 + cc);
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int q = threadIdx.x + 256 * i;
+      *reinterpret_cast<int4v*>(&su[q / CPT][(q % CPT) * EPC]) = v[i];
+    }
+  }
   for (int e0 = 0; e0 < A.E; e0 += 16) {
-    __syncthreads();  // the previous group's sdg and part are read
+    __syncthreads();  // su is written; the previous group's sdg and part are read
     for (int q = threadIdx.x; q < kDwrTokens * 16; q += 256) {
       const int t = q / 16, e = e0 + q % 16;
       sdg[t][q % 16] = (m0 + t < m1 && e < A.E) ? A.dg[(size_t)(m0 + t) * A.E + e] : 0.f;
@@ -401,17 +422,15 @@ __global__ __launch_bounds__(256) void pbwd_dwr_kernel(ProjBwdArgs A) {
     float acc[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    if (d < A.D) {
 #pragma unroll 4
-      for (int m = m0 + sub; m < m1; m += 4) {
-        const float uv = to_f32(u[(size_t)m * A.D + d]);
-        const floatx4* g4 = reinterpret_cast<const floatx4*>(sdg[m - m0]);
+    for (int t = sub; t < m1 - m0; t += 4) {
+      const float uv = to_f32(su[t][c]);
+      const floatx4* g4 = reinterpret_cast<const floatx4*>(sdg[t]);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const floatx4 gv = g4[q4];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const floatx4 gv = g4[q4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[4 * q4 + j] += gv[j] * uv;
-        }
+        for (int j = 0; j < 4; ++j) acc[4 * q4 + j] += gv[j] * uv;
       }
     }
 #pragma unroll
@@ -425,11 +444,22 @@ __global__ __launch_bounds__(256) void pbwd_dwr_kernel(ProjBwdArgs A) {
   }
 }
 
-__global__ void pbwd_dwr_sum_kernel(ProjBwdArgs A) {
+// dW_r = the splits' partials added in split order; the reads of 16 splits
+// are issued together (64-thread workgroups, so that many CUs share the sum).
+__global__ __launch_bounds__(64) void pbwd_dwr_sum_kernel(ProjBwdArgs A) {
   const size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  if (q >= (size_t)A.E * A.D) return;
+  const size_t ED = (size_t)A.E * A.D;
+  if (q >= ED) return;
   float s = 0.f;
-  for (int sp = 0; sp < A.nsplit; ++sp) s += A.dwr_part[(size_t)sp * A.E * A.D + q];
+  int sp = 0;
+  for (; sp + 16 <= A.nsplit; sp += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = A.dwr_part[(size_t)(sp + j) * ED + q];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += v[j];
+  }
+  for (; sp < A.nsplit; ++sp) s += A.dwr_part[(size_t)sp * ED + q];
   A.dWr[q] = s;
 }
 
@@ -479,8 +509,8 @@ static hipError_t launch_pbwd_t(const ProjBwdArgs& A, hipStream_t s) {
   prof_begin("proj_bwd_dwr", s);
   hipLaunchKernelGGL(pbwd_dwr_kernel<T>, dim3((unsigned)((A.D + 63) / 64), (unsigned)A.nsplit),
                      dim3(256), 0, s, A);
-  hipLaunchKernelGGL(pbwd_dwr_sum_kernel, dim3((unsigned)(((size_t)A.E * A.D + 255) / 256)),
-                     dim3(256), 0, s, A);
+  hipLaunchKernelGGL(pbwd_dwr_sum_kernel, dim3((unsigned)(((size_t)A.E * A.D + 63) / 64)),
+                     dim3(64), 0, s, A);
   prof_end(s);
   return hipGetLastError();
 }
