@@ -74,11 +74,14 @@ __global__ __launch_bounds__(256) void pbwd_dz_kernel(ProjBwdArgs A) {
 
 // ---------------------------------------------------------------- router
 
-// Router gradient, 32 tokens per workgroup. Phase 1, one wave per token (8
-// per wave): pi = softmax(logits), q_e = pi_e dpi_e (the sum of s_j over the
-// slots routed to e), dg_e = q_e - pi_e sum_f q_f, into LDS and dg. Phase 2,
-// threads over d: du[t, d] = sum_e dg[t, e] W_r[e, d] for the 32 tokens, each
-// router element read once per workgroup (du is initialised here).
+// Router gradient, 32 tokens per workgroup. Phase 1, a group of sg lanes
+// per token (sg a power of two with E <= 4 sg; lane l of a group holds
+// experts l, l + sg, l + 2 sg, l + 3 sg), so a wave covers 64 / sg tokens per
+// pass: pi = softmax(logits), q_e = pi_e dpi_e (the sum of s_j over the slots
+// routed to e), dg_e = q_e - pi_e sum_f q_f, into LDS and dg; the group's sums
+// run in a fixed butterfly order. Phase 2, threads over d: du[t, d] =
+// sum_e dg[t, e] W_r[e, d] for the 32 tokens, each router element read once
+// per workgroup (du is initialised here).
 constexpr int kRouterTok = 32;
 
 template <typename T>
@@ -87,45 +90,43 @@ __global__ __launch_bounds__(256) void pbwd_router_kernel(ProjBwdArgs A) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * kRouterTok;
   const int E = A.E;
-  for (int tl = wave; tl < kRouterTok; tl += 4) {
+  int sg = 1;
+  while (4 * sg < E) sg *= 2;
+  const int tpp = 64 / sg, sl = lane % sg;
+  for (int tl = wave * tpp + lane / sg; tl < kRouterTok; tl += 4 * tpp) {
     const int m = t0 + tl;
-    if (m >= A.M) {
-      for (int e = lane; e < E; e += 64) sdg[tl][e] = 0.f;
-      continue;
-    }
+    const bool ok = m < A.M;
     float pi[4], q[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int e = lane + 64 * r;
-      pi[r] = e < E ? A.logits[(size_t)m * E + e] : -INFINITY;
+      const int e = sl + sg * r;
+      pi[r] = (ok && e < E) ? A.logits[(size_t)m * E + e] : -INFINITY;
       mx = fmaxf(mx, pi[r]);
       q[r] = 0.f;
-      if (e < E)
+      if (ok && e < E)
         for (int j = 0; j < A.k; ++j)
           if (A.idx[(size_t)m * A.k + j] == e) q[r] += A.sw[(size_t)m * A.k + j];
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    for (int off = sg >> 1; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, sg));
     float se = 0.f, sq = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pi[r] = lane + 64 * r < E ? expf(pi[r] - mx) : 0.f;
+      pi[r] = (ok && sl + sg * r < E) ? expf(pi[r] - mx) : 0.f;
       se += pi[r];
       sq += q[r];
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      se += __shfl_xor(se, off);
-      sq += __shfl_xor(sq, off);
+    for (int off = sg >> 1; off > 0; off >>= 1) {
+      se += __shfl_xor(se, off, sg);
+      sq += __shfl_xor(sq, off, sg);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int e = lane + 64 * r;
+      const int e = sl + sg * r;
       if (e < E) {
-        const float g = q[r] - (pi[r] / se) * sq;
+        const float g = ok ? q[r] - (pi[r] / se) * sq : 0.f;
         sdg[tl][e] = g;
-        A.dg[(size_t)m * E + e] = g;
+        if (ok) A.dg[(size_t)m * E + e] = g;
       }
     }
   }
