@@ -299,15 +299,18 @@ def run_gpu(args):
         log_decay = (torch.empty(wl.batch, wl.nheads, wl.seqlen, dtype=torch.float32, device=dev)
                      if mixed else None)
         if backward:
+            # the forward keeps its routing (with logits), B_hat and projection
+            # workspace for the backward, which reuses them
             dy = up(synth.output_gradient(wl))
-            grads = sb.alloc_grads(dims, dev)
+            buf = sb.alloc_buffers(dims, dev, logits=True)
+            grads = sb.alloc_grads(dims, dev, saved=True)
 
         def step():
             if backward:
                 # training step: the prefill forward, then every gradient of
                 # <dy, y> (u, W_r, W_exp, a, the initial state)
                 sb.forward(dims, u, wr, we, a, None, buf)
-                sb.backward(dims, u, wr, we, a, None, dy, None, buf, grads)
+                sb.backward(dims, u, wr, we, a, None, dy, None, buf, grads, saved=True)
                 return
             # prefill the batch, then decode one more token of every sequence,
             # updating the prefill's final state in place

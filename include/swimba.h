@@ -75,7 +75,8 @@ typedef enum swimba_call {
   SWIMBA_CALL_SCAN = 2,
   SWIMBA_CALL_DECODE = 3,
   SWIMBA_CALL_SCAN_BACKWARD = 4,
-  SWIMBA_CALL_PROJECT_BACKWARD = 5
+  SWIMBA_CALL_PROJECT_BACKWARD = 5,
+  SWIMBA_CALL_PROJECT_BACKWARD_SAVED = 6
 } swimba_call;
 
 /*
@@ -333,6 +334,28 @@ swimba_status swimba_expert_project_mix_backward(
     const swimba_dims* dims, const void* u, const void* w_router, const void* w_experts,
     const float* dB_hat, const float* dX_hat, const float* dC_mix, float* du, float* dW_router,
     float* dW_experts, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * swimba_expert_project_mix_backward without recomputing the forward: the
+ * routing, the weighted streams and the bucketing come from the forward
+ * calls (the reserve-space pattern of training libraries). Results are
+ * bitwise those of swimba_expert_project_mix_backward on the same inputs.
+ *   topk_idx, topk_w, logits   the outputs of swimba_route_topk for u (logits
+ *                              is then required)
+ *   B_hat       the B_hat output of swimba_expert_project_mix for that routing
+ *   fwd_ws      the workspace of that swimba_expert_project_mix call, not
+ *               written since (it holds the expert-sorted pair lists and the
+ *               per-slot C parts); fwd_ws_bytes as passed to it
+ *   ws          workspace of swimba_workspace_size(dims, SWIMBA_CALL_PROJECT_BACKWARD_SAVED)
+ * Every other argument, shape and error as for
+ * swimba_expert_project_mix_backward.
+ */
+swimba_status swimba_expert_project_mix_backward_saved(
+    const swimba_dims* dims, const void* u, const void* w_router, const void* w_experts,
+    const int32_t* topk_idx, const float* topk_w, const float* logits, const void* B_hat,
+    const void* fwd_ws, size_t fwd_ws_bytes, const float* dB_hat, const float* dX_hat,
+    const float* dC_mix, float* du, float* dW_router, float* dW_experts, void* ws,
+    size_t ws_bytes, hipStream_t stream);
 
 /*
  * Per-kernel timing with HIP events, for measurement only. While enabled,

@@ -17,8 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libswimba.so")
 
 F32, BF16 = 0, 1
-CALL_ROUTE, CALL_PROJECT, CALL_SCAN, CALL_DECODE, CALL_SCAN_BACKWARD, CALL_PROJECT_BACKWARD = (
-    0, 1, 2, 3, 4, 5)
+(CALL_ROUTE, CALL_PROJECT, CALL_SCAN, CALL_DECODE, CALL_SCAN_BACKWARD, CALL_PROJECT_BACKWARD,
+ CALL_PROJECT_BACKWARD_SAVED) = (0, 1, 2, 3, 4, 5, 6)
 
 STATUS = {
     0: "SWIMBA_OK", -1: "SWIMBA_ERR_NULL", -2: "SWIMBA_ERR_DIMS", -3: "SWIMBA_ERR_UNSUPPORTED",
@@ -31,7 +31,7 @@ EXPORTS = (
     "swimba_output_project", "swimba_profile_enable", "swimba_profile_report",
     "swimba_profile_select", "swimba_mix_decay", "swimba_ssd_chunk_scan_mixed",
     "swimba_decode_step_mixed", "swimba_ssd_chunk_scan_backward",
-    "swimba_expert_project_mix_backward",
+    "swimba_expert_project_mix_backward", "swimba_expert_project_mix_backward_saved",
 )
 
 
@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
     L.swimba_ssd_chunk_scan_backward.restype = I32
     L.swimba_expert_project_mix_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, SZ, S]
     L.swimba_expert_project_mix_backward.restype = I32
+    L.swimba_expert_project_mix_backward_saved.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P, P,
+                                                           P, P, P, P, P, SZ, S]
+    L.swimba_expert_project_mix_backward_saved.restype = I32
     L.swimba_profile_enable.restype = I32
     L.swimba_profile_enable.argtypes = [I32]
     L.swimba_profile_report.restype = I32
@@ -228,6 +231,19 @@ def swimba_expert_project_mix_backward(dims, u, w_router, w_experts, dB_hat, dX_
         _stream(stream)))
 
 
+def swimba_expert_project_mix_backward_saved(dims, u, w_router, w_experts, topk_idx, topk_w,
+                                             logits, B_hat, fwd_ws, dB_hat, dX_hat, dC_mix, du,
+                                             dW_router, dW_experts, ws, fwd_ws_bytes=None,
+                                             ws_bytes=None, stream=None):
+    fnb = (fwd_ws.numel() if fwd_ws is not None else 0) if fwd_ws_bytes is None else fwd_ws_bytes
+    nb = (ws.numel() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check(lib().swimba_expert_project_mix_backward_saved(
+        ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(logits), _ptr(B_hat), _ptr(fwd_ws), fnb, _ptr(dB_hat), _ptr(dX_hat),
+        _ptr(dC_mix), _ptr(du), _ptr(dW_router), _ptr(dW_experts), _ptr(ws), nb,
+        _stream(stream)))
+
+
 def swimba_output_project(dims, y, w_out, out, stream=None):
     _check(lib().swimba_output_project(ctypes.byref(dims), _ptr(y), _ptr(w_out), _ptr(out),
                                        _stream(stream)))
@@ -331,15 +347,17 @@ class Grads:
     ws_project: torch.Tensor | None
 
 
-def alloc_grads(dims: Dims, device="cuda") -> Grads:
-    """Every output and workspace of one backward pass, allocated by torch (float32)."""
+def alloc_grads(dims: Dims, device="cuda", saved=False) -> Grads:
+    """Every output and workspace of one backward pass, allocated by torch
+    (float32); saved: the workspace of the call that reuses the forward."""
     M = dims.batch * dims.seqlen
     k, H, P, G, N, E, D = (dims.top_k, dims.nheads, dims.headdim, dims.ngroups, dims.dstate,
                            dims.n_experts, dims.d_model)
     Wd = H * P + 2 * G * N
     f32 = torch.float32
     ws_s, _ = workspace(dims, CALL_SCAN_BACKWARD, device)
-    ws_p, _ = workspace(dims, CALL_PROJECT_BACKWARD, device)
+    ws_p, _ = workspace(dims, CALL_PROJECT_BACKWARD_SAVED if saved else CALL_PROJECT_BACKWARD,
+                        device)
     return Grads(
         dB_hat=torch.empty(M, k, G, N, dtype=f32, device=device),
         dX_hat=torch.empty(M, k, H, P, dtype=f32, device=device),
@@ -353,14 +371,23 @@ def alloc_grads(dims: Dims, device="cuda") -> Grads:
 
 
 def backward(dims: Dims, u, w_router, w_experts, a, h_init, dy, dh_final, fwd: Buffers,
-             grads: Grads | None = None, stream=None) -> Grads:
+             grads: Grads | None = None, stream=None, saved=False) -> Grads:
     """Gradients of l(y, h_final) given dy and dh_final: the chunked scan's
-    backward on the forward's streams, then router, projection and mix."""
-    g = grads if grads is not None else alloc_grads(dims, u.device)
+    backward on the forward's streams, then router, projection and mix. With
+    saved, the latter reuses the forward's routing, B_hat and projection
+    workspace (fwd must hold logits, and grads come from alloc_grads(saved=True))
+    instead of recomputing them."""
+    g = grads if grads is not None else alloc_grads(dims, u.device, saved)
     swimba_ssd_chunk_scan_backward(dims, fwd.B_hat, fwd.X_hat, fwd.C_mix, a, h_init, dy,
                                    dh_final, g.dB_hat, g.dX_hat, g.dC_mix, g.da, g.dh_init,
                                    g.ws_scan, stream=stream)
-    swimba_expert_project_mix_backward(dims, u, w_router, w_experts, g.dB_hat, g.dX_hat,
-                                       g.dC_mix, g.du, g.dW_router, g.dW_experts, g.ws_project,
-                                       stream=stream)
+    if saved:
+        swimba_expert_project_mix_backward_saved(
+            dims, u, w_router, w_experts, fwd.topk_idx, fwd.topk_w, fwd.logits, fwd.B_hat,
+            fwd.ws_project, g.dB_hat, g.dX_hat, g.dC_mix, g.du, g.dW_router, g.dW_experts,
+            g.ws_project, stream=stream)
+    else:
+        swimba_expert_project_mix_backward(dims, u, w_router, w_experts, g.dB_hat, g.dX_hat,
+                                           g.dC_mix, g.du, g.dW_router, g.dW_experts,
+                                           g.ws_project, stream=stream)
     return g

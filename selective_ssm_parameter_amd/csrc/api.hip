@@ -141,16 +141,20 @@ struct PbwdWs {
   size_t idx, w, logits, proj, bhat, xhat, dz, us, sw, dg, dupart, dwrpart, total;
 };
 
-PbwdWs pbwd_ws(const Dims& d) {
+// saved: the forward's routing, B_hat and projection workspace are passed in
+// (swimba_expert_project_mix_backward_saved), so none of them is recomputed.
+PbwdWs pbwd_ws(const Dims& d, bool saved = false) {
   PbwdWs w{};
   size_t off = 0;
   const int64_t pairs = d.M * d.k;
-  w.idx = off; off += align256(sizeof(int32_t) * pairs);
-  w.w = off; off += align256(sizeof(float) * pairs);
-  w.logits = off; off += align256(sizeof(float) * d.M * d.E);
-  w.proj = off; off += proj_ws(d).total;
-  w.bhat = off; off += align256(d.esize * pairs * d.GN);
-  w.xhat = off; off += align256(d.esize * pairs * d.HP);
+  if (!saved) {
+    w.idx = off; off += align256(sizeof(int32_t) * pairs);
+    w.w = off; off += align256(sizeof(float) * pairs);
+    w.logits = off; off += align256(sizeof(float) * d.M * d.E);
+    w.proj = off; off += proj_ws(d).total;
+    w.bhat = off; off += align256(d.esize * pairs * d.GN);
+    w.xhat = off; off += align256(d.esize * pairs * d.HP);
+  }
   w.dz = off; off += align256(d.esize * pairs * d.W);
   w.us = off; off += align256(d.esize * pairs * d.D);
   w.sw = off; off += align256(sizeof(float) * pairs);
@@ -291,6 +295,7 @@ size_t swimba_workspace_size(const swimba_dims* dims, int32_t call) {
     case SWIMBA_CALL_SCAN_BACKWARD:
       return d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.k);
     case SWIMBA_CALL_PROJECT_BACKWARD: return d.M == 0 ? 0 : pbwd_ws(d).total;
+    case SWIMBA_CALL_PROJECT_BACKWARD_SAVED: return d.M == 0 ? 0 : pbwd_ws(d, true).total;
     default: return 0;
   }
 }
@@ -336,10 +341,20 @@ swimba_status swimba_expert_project_mix(const swimba_dims* dims, const void* u,
                     "expert_project_mix launch");
 }
 
-swimba_status swimba_expert_project_mix_backward(
-    const swimba_dims* dims, const void* u, const void* w_router, const void* w_experts,
-    const float* dB_hat, const float* dX_hat, const float* dC_mix, float* du, float* dW_router,
-    float* dW_experts, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward of router, projections and mix. saved == false: the forward's
+// routing and projection are recomputed into the workspace; saved == true:
+// they come from the caller (the router's outputs, the forward's B_hat and
+// the workspace of the swimba_expert_project_mix call that produced it).
+swimba_status pbwd_impl(bool saved, const swimba_dims* dims, const void* u, const void* w_router,
+                        const void* w_experts, const int32_t* topk_idx, const float* topk_w,
+                        const float* logits, const void* B_hat, const void* fwd_ws,
+                        size_t fwd_ws_bytes, const float* dB_hat, const float* dX_hat,
+                        const float* dC_mix, float* du, float* dW_router, float* dW_experts,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
   Dims d;
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
@@ -363,26 +378,47 @@ swimba_status swimba_expert_project_mix_backward(
   REQUIRE_PTR(dX_hat);
   REQUIRE_PTR(dC_mix);
   REQUIRE_PTR(du);
-  const PbwdWs lay = pbwd_ws(d);
+  const ProjWs play = proj_ws(d);
+  if (saved) {
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(B_hat);
+    if ((st = check_ws(const_cast<void*>(fwd_ws), fwd_ws_bytes, play.total)) != SWIMBA_OK) {
+      g_err = "forward " + g_err;
+      return st;
+    }
+  }
+  const PbwdWs lay = pbwd_ws(d, saved);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != SWIMBA_OK) return st;
   unsigned char* w8 = static_cast<unsigned char*>(ws);
-  int32_t* idx = reinterpret_cast<int32_t*>(w8 + lay.idx);
-  float* tw = reinterpret_cast<float*>(w8 + lay.w);
-  float* logits = reinterpret_cast<float*>(w8 + lay.logits);
-  unsigned char* pws = w8 + lay.proj;
-  const ProjWs play = proj_ws(d);
-  // the forward's routing and weighted streams, recomputed with its own kernels
-  hipError_t e = launch_route(d.bf16, u, w_router, (int)d.M, (int)d.D, (int)d.E, (int)d.k, idx,
-                              tw, logits, stream);
-  if (e != hipSuccess) return hip_status(e, "expert_project_mix_backward route launch");
-  e = run_project(d, d.M, u, w_experts, idx, tw, w8 + lay.bhat, w8 + lay.xhat, nullptr, pws,
-                  stream);
-  if (e != hipSuccess) return hip_status(e, "expert_project_mix_backward projection launch");
+  const int32_t* idx = topk_idx;
+  const float* tw = topk_w;
+  const float* lg = logits;
+  const void* bhat = B_hat;
+  const unsigned char* pws = static_cast<const unsigned char*>(fwd_ws);
+  if (!saved) {
+    // the forward's routing and weighted streams, recomputed with its own kernels
+    int32_t* ridx = reinterpret_cast<int32_t*>(w8 + lay.idx);
+    float* rw = reinterpret_cast<float*>(w8 + lay.w);
+    float* rlg = reinterpret_cast<float*>(w8 + lay.logits);
+    hipError_t e = launch_route(d.bf16, u, w_router, (int)d.M, (int)d.D, (int)d.E, (int)d.k,
+                                ridx, rw, rlg, stream);
+    if (e != hipSuccess) return hip_status(e, "expert_project_mix_backward route launch");
+    e = run_project(d, d.M, u, w_experts, ridx, rw, w8 + lay.bhat, w8 + lay.xhat, nullptr,
+                    w8 + lay.proj, stream);
+    if (e != hipSuccess) return hip_status(e, "expert_project_mix_backward projection launch");
+    idx = ridx;
+    tw = rw;
+    lg = rlg;
+    bhat = w8 + lay.bhat;
+    pws = w8 + lay.proj;
+  }
   ProjBwdArgs a{};
   a.u = u; a.w_router = w_router; a.w_experts = w_experts;
   a.idx = idx; a.topk_w = tw; a.dB = dB_hat; a.dX = dX_hat; a.dC = dC_mix;
-  a.du = du; a.dWr = dW_router; a.dW = dW_experts; a.logits = logits;
-  a.B_hat = w8 + lay.bhat;
+  a.du = du; a.dWr = dW_router; a.dW = dW_experts; a.logits = lg;
+  a.B_hat = bhat;
   a.c_part = reinterpret_cast<const float*>(pws + play.cpart);
   a.sorted = reinterpret_cast<const int32_t*>(pws + play.sorted);
   a.sorted_w = reinterpret_cast<const float*>(pws + play.sortw);
@@ -397,6 +433,30 @@ swimba_status swimba_expert_project_mix_backward(
   a.HP = (int)d.HP; a.GN = (int)d.GN;
   return hip_status(launch_project_backward(d.bf16, a, stream),
                     "expert_project_mix_backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+swimba_status swimba_expert_project_mix_backward(
+    const swimba_dims* dims, const void* u, const void* w_router, const void* w_experts,
+    const float* dB_hat, const float* dX_hat, const float* dC_mix, float* du, float* dW_router,
+    float* dW_experts, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return pbwd_impl(false, dims, u, w_router, w_experts, nullptr, nullptr, nullptr, nullptr,
+                   nullptr, 0, dB_hat, dX_hat, dC_mix, du, dW_router, dW_experts, ws, ws_bytes,
+                   stream);
+}
+
+swimba_status swimba_expert_project_mix_backward_saved(
+    const swimba_dims* dims, const void* u, const void* w_router, const void* w_experts,
+    const int32_t* topk_idx, const float* topk_w, const float* logits, const void* B_hat,
+    const void* fwd_ws, size_t fwd_ws_bytes, const float* dB_hat, const float* dX_hat,
+    const float* dC_mix, float* du, float* dW_router, float* dW_experts, void* ws,
+    size_t ws_bytes, hipStream_t stream) {
+  return pbwd_impl(true, dims, u, w_router, w_experts, topk_idx, topk_w, logits, B_hat, fwd_ws,
+                   fwd_ws_bytes, dB_hat, dX_hat, dC_mix, du, dW_router, dW_experts, ws,
+                   ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -41,7 +41,7 @@ def lib():
 def test_exports_every_declared_symbol():
     L = lib()
     syms = declared_symbols()
-    assert len(syms) == 16, syms
+    assert len(syms) == 17, syms
     for s in syms:
         assert hasattr(L, s), f"{s} declared in swimba.h but not exported"
     assert set(syms) == set(sb.EXPORTS)
@@ -198,6 +198,22 @@ def test_backward_argument_checks():
     assert pb(d, ws=None, nb=0) == -4
     assert pb(good_dims(headdim=32)) == -3
     assert pb(good_dims(top_k=5)) == -2
+    # the variant that reuses the forward: its own workspace, the forward's
+    # projection workspace and the routing outputs are checked too
+    need_s = sb.swimba_workspace_size(d, sb.CALL_PROJECT_BACKWARD_SAVED)
+    fwd_need = sb.swimba_workspace_size(d, sb.CALL_PROJECT)
+    assert 0 < need_s < need
+
+    def pbs(dims, logits=FAKE, fws=FAKE, fnb=1 << 40, ws=FAKE, nb=1 << 40):
+        return L.swimba_expert_project_mix_backward_saved(
+            ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, logits, FAKE, fws, fnb, FAKE, FAKE,
+            FAKE, FAKE, FAKE, FAKE, ws, nb, None)
+
+    assert pbs(d, logits=None) == -1 and "logits is NULL" in L.swimba_last_error().decode()
+    assert pbs(d, fnb=fwd_need - 1) == -4
+    assert "forward workspace" in L.swimba_last_error().decode()
+    assert pbs(d, nb=need_s - 1) == -4
+    assert pbs(good_dims(top_k=5)) == -2
     # the scan's backward: shape and pointer checks
     st = L.swimba_ssd_chunk_scan_backward(ctypes.byref(good_dims(top_k=3)), FAKE, FAKE, FAKE, FAKE,
                                           None, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE,

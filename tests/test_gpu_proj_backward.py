@@ -133,3 +133,40 @@ def test_project_backward_no_tokens():
                                           None)
     torch.cuda.synchronize()
     assert np.all(host(dWr) == 0) and np.all(host(dW) == 0)
+
+
+def test_project_backward_saved_forward_is_bitwise_equal():
+    """The variant that takes the forward's routing, B_hat and projection
+    workspace returns bitwise what the recomputing call returns."""
+    wl = W("q10", 910, n_experts=8, seqlen=333)
+    inp = synth.make_inputs(wl)
+    dB, dX, dC = upstream(wl)
+    dims = sb.dims_of(wl)
+    dt = tdt(wl)
+    M, D, E = wl.tokens, wl.d_model, wl.n_experts
+    Wd = wl.nheads * wl.headdim + 2 * wl.ngroups * wl.dstate
+    u = dev(np.reshape(inp["u"], (M, D)), dt)
+    wr, we = dev(inp["w_router"], dt), dev(inp["w_experts"], dt)
+    buf = sb.alloc_buffers(dims, "cuda", logits=True)
+    sb.swimba_route_topk(dims, u, wr, buf.topk_idx, buf.topk_w, buf.logits)
+    sb.swimba_expert_project_mix(dims, u, we, buf.topk_idx, buf.topk_w, buf.B_hat, buf.X_hat,
+                                 buf.C_mix, buf.ws_project)
+    f32 = torch.float32
+    outs = []
+    for saved in (False, True):
+        du = torch.full((M, D), float("nan"), dtype=f32, device="cuda")
+        dWr = torch.full((E, D), float("nan"), dtype=f32, device="cuda")
+        dW = torch.full((E, Wd, D), float("nan"), dtype=f32, device="cuda")
+        args = (dev(dB, f32), dev(dX, f32), dev(dC, f32), du, dWr, dW)
+        if saved:
+            ws, _ = sb.workspace(dims, sb.CALL_PROJECT_BACKWARD_SAVED)
+            sb.swimba_expert_project_mix_backward_saved(dims, u, wr, we, buf.topk_idx, buf.topk_w,
+                                                        buf.logits, buf.B_hat, buf.ws_project,
+                                                        *args, ws)
+        else:
+            ws, _ = sb.workspace(dims, sb.CALL_PROJECT_BACKWARD)
+            sb.swimba_expert_project_mix_backward(dims, u, wr, we, *args, ws)
+        torch.cuda.synchronize()
+        outs.append([host(du), host(dWr), host(dW)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
