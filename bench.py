@@ -212,7 +212,8 @@ def backward_models(wl):
     bytes: the streams and dy read once; the two local chunk-state sets
     [nc, H, N, P] written by local in the operand type (fp16 for bf16
     problems) and read by the sweep, which writes the entering states H_c and
-    F_c in fp32 for grad to read; the fp32 gradients written once. Projection
+    F_c for grad to read in the same type (fp16 rows with one fp32 factor per
+    row of P for bf16 problems); the fp32 gradients written once. Projection
     backward: two grouped GEMMs of 2 (pairs) W D flops each; the dz kernel
     also copies each pair's token row of u into sorted order for the dW GEMM."""
     M, D, E, k = wl.tokens, wl.d_model, wl.n_experts, wl.top_k
@@ -224,7 +225,7 @@ def backward_models(wl):
     L = 64 if wl.dtype == "bf16" else 32
     nch = wl.batch * -(-wl.seqlen // L)          # chunks over the batch
     R = k * L
-    states = nch * H * N * P * 4                  # one chunk-state set, fp32
+    states = nch * H * N * (P * es + (4 if es == 2 else 0))  # one entering-state set
     lstates = nch * H * N * P * es                # one local chunk-state set
     streams = pairs * (HP + GN) * es + M * GN * es
     dy = M * HP * ei

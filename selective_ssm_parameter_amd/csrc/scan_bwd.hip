@@ -74,8 +74,11 @@ struct BwdArgs {
   void* Rl;             // [Bt, nb, H, N, P] local type: R_c (scaled by 1 / R_u)
   float* Su;            // [Bt, nb, H]: the factor that restores S_c
   float* Ru;            // [Bt, nb, H]: the factor that restores R_c
-  float* S;             // [Bt, nb, H, N, P]: H_c (entering state of chunk c)
-  float* R;             // [Bt, nb, H, N, P]: F_c (gradient entering chunk c from the right)
+  void* S;              // [Bt, nb, H, N, P] local type: H_c (entering state of chunk c)
+  void* R;              // [Bt, nb, H, N, P] local type: F_c (gradient entering chunk c
+                        // from the right); fp16 rows are scaled by 1 / Hu, 1 / Fu
+  float* Hu;            // [Bt, nb, H, N]: the factor that restores row n of H_c (fp16 only)
+  float* Fu;            // [Bt, nb, H, N]: the factor that restores row n of F_c (fp16 only)
   float* da_part;       // [Bt, nb, H]
   float* dBp;           // [hs, M, k, G, N] slice parts (hs > 1)
   float* dCp;           // [hs, M, G, N]
@@ -194,27 +197,37 @@ struct TileLoad {
         raw[i] = *reinterpret_cast<const RV*>(src + (size_t)r * gstride + c);
     }
   }
+  // absmax and store take the factor of read i of this thread, row r, as
+  // f(i, r); absmax and store take it per row.
   template <class F>
-  __device__ __forceinline__ float absmax(F f) const {
+  __device__ __forceinline__ float absmax_ir(F f) const {
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int q = threadIdx.x + NT * i;
       if (NV % NT != 0 && q >= NV) continue;
-      const float s = f(q / RPR);
+      const float s = f(i, q / RPR);
 #pragma unroll
       for (int j = 0; j < V; ++j) mx = fmaxf(mx, fabsf(to_f32(raw[i][j]) * s));
     }
     return mx;
   }
   template <class F>
+  __device__ __forceinline__ float absmax(F f) const {
+    return absmax_ir([&](int, int r) { return f(r); });
+  }
+  template <class F>
   __device__ __forceinline__ void store(unsigned char* tile, F f, float sc) const {
+    store_ir(tile, [&](int, int r) { return f(r); }, sc);
+  }
+  template <class F>
+  __device__ __forceinline__ void store_ir(unsigned char* tile, F f, float sc) const {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int q = threadIdx.x + NT * i;
       if (NV % NT != 0 && q >= NV) continue;
       const int r = q / RPR, c = (q % RPR) * V;
-      const float s = f(r) * sc;
+      const float s = f(i, r) * sc;
       if constexpr (sizeof(T) == 2 && V == 8) {
         typename Vec<T>::x8 o;
 #pragma unroll
@@ -391,6 +404,28 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
 
 // ---------------------------------------------------------------- state sweep
 
+// DPP move of x from the lane that control word CTRL names (all rows and banks).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// Largest x over each aligned group of G lanes (G a power of two up to 32),
+// every lane of the group receiving it. Within 16 lanes the steps are DPP
+// moves (quad permutations [1,0,3,2] and [2,3,0,1], then the half-row and row
+// mirrors, each pairing a block of lanes whose maximum is already known with
+// its neighbour); only the step between the two 16-lane rows of a 32-lane
+// group goes through the cross-lane permute.
+template <int G>
+__device__ __forceinline__ float group_max(float m) {
+  static_assert(G >= 1 && G <= 32 && (G & (G - 1)) == 0, "power-of-two group up to 32 lanes");
+  if constexpr (G >= 2) m = fmaxf(m, dpp_f<0xB1>(m));
+  if constexpr (G >= 4) m = fmaxf(m, dpp_f<0x4E>(m));
+  if constexpr (G >= 8) m = fmaxf(m, dpp_f<0x141>(m));
+  if constexpr (G >= 16) m = fmaxf(m, dpp_f<0x140>(m));
+  if constexpr (G >= 32) m = fmaxf(m, __shfl_xor(m, 16));
+  return m;
+}
+
 // Per state element: the states entering each chunk, H_c going forwards
 // (H_{c+1} = a^{Lc} H_c + S_c from h_init) and F_c going backwards (F_{c-1} =
 // a R_c + a^{Lc} F_c from dh_final, ending at F_{-1} = a g_0 = dh_init). Each
@@ -398,7 +433,9 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(BwdArgs A) {
 // states, or fewer when there are few states, so that enough threads share
 // the walk) and reads those of SU chunks before it uses any (the walk over
 // chunks is serial, so the reads of several chunks are kept in flight); sums
-// in fp32.
+// in fp32. H_c and F_c are written in the local states' type, fp16 rows of
+// kBP elements each with its own power-of-two factor: the gradient kernel
+// rounds them to fp16 tiles for the matrix cores in any case.
 template <typename LT, int BL, int V>
 __global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdArgs A) {
   constexpr int SU = V >= 4 ? 8 : 16;  // chunks whose reads are in flight together
@@ -424,16 +461,35 @@ __global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdArgs A) {
   }
   const LT* Sl = static_cast<const LT*>(A.Sl) + base;
   const LT* Rl = static_cast<const LT*>(A.Rl) + base;
-  float* Hp = A.S + base;
-  float* Fp = A.R + base;
-  auto put = [&](float* dst, const float* v) {
-    if constexpr (V % 4 == 0) {
+  LT* Hp = static_cast<LT*>(A.S) + base;
+  LT* Fp = static_cast<LT*>(A.R) + base;
+  // row n of the state: factors at ((b nb + c) H + h) N + n
+  const size_t ubase = ((size_t)b * nb * H + h) * A.N + e0 / kBP;
+  const size_t ustride = (size_t)H * A.N;
+  auto put = [&](LT* dst, float* uf, const float* v) {
+    if constexpr (sizeof(LT) == 4) {
+      if constexpr (V % 4 == 0) {
 #pragma unroll
-      for (int j = 0; j < V; j += 4)
-        *reinterpret_cast<floatx4*>(dst + j) = floatx4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+        for (int j = 0; j < V; j += 4)
+          *reinterpret_cast<floatx4*>(dst + j) = floatx4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+      } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) dst[j] = v[j];
+      }
     } else {
+      // fp16: the row (the kBP / V lanes holding it, all in one wave) is
+      // scaled by the power of two that brings its largest magnitude into
+      // [1/2, 1); the factor that restores it goes beside the state
+      float m = 0.f;
 #pragma unroll
-      for (int j = 0; j < V; ++j) dst[j] = v[j];
+      for (int j = 0; j < V; ++j) m = fmaxf(m, fabsf(v[j]));
+      m = group_max<kBP / V>(m);
+      const float sc = m > 0.f ? ldexpf(1.f, min(-(ilogbf(m) + 1), 126)) : 1.f;
+      RV o;
+#pragma unroll
+      for (int j = 0; j < V; ++j) o[j] = from_f32<LT>(v[j] * sc);
+      *reinterpret_cast<RV*>(dst) = o;
+      if (e0 % kBP == 0) *uf = 1.f / sc;
     }
   };
   for (int c0 = 0; c0 < nb; c0 += SU) {
@@ -450,7 +506,7 @@ __global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdArgs A) {
     for (int u = 0; u < SU; ++u) {
       const int c = c0 + u;
       if (c >= nb) break;
-      put(Hp + (size_t)c * cstride, st);
+      put(Hp + (size_t)c * cstride, A.Hu + ubase + (size_t)c * ustride, st);
       const float ac = c == nb - 1 ? aLast : aL;
 #pragma unroll
       for (int j = 0; j < V; ++j) st[j] = st[j] * ac + to_f32(v[u][j]) * us[u];
@@ -470,7 +526,7 @@ __global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdArgs A) {
     for (int u = 0; u < SU; ++u) {
       const int c = c1 - u;
       if (c < 0) break;
-      put(Fp + (size_t)c * cstride, gr);
+      put(Fp + (size_t)c * cstride, A.Fu + ubase + (size_t)c * ustride, gr);
       const float ac = c == nb - 1 ? aLast : aL;
 #pragma unroll
       for (int j = 0; j < V; ++j) gr[j] = gr[j] * ac + to_f32(v[u][j]) * us[u];
@@ -551,18 +607,37 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
     // scaled by powers of two, and <F_c, H_c> is taken in fp32 on the way
     TileLoad<T, R, kBP, NT, S> LX;
     TileLoad<T, BL, kBP, NT, TY> LD;
-    TileLoad<T, NP, kBP, NT, float> LF, LH;
+    TileLoad<T, NP, kBP, NT, T> LF, LH;
     LX.fetch(static_cast<const S*>(A.X_hat) + (m0 * KS) * H * kBP + h * kBP, (size_t)H * kBP,
              Lc * KS, kBP);
     LD.fetch(static_cast<const TY*>(A.dy) + m0 * H * kBP + h * kBP, (size_t)H * kBP, Lc, kBP);
-    LF.fetch(A.R + sbase, (size_t)kBP, N, kBP);
-    LH.fetch(A.S + sbase, (size_t)kBP, N, kBP);
+    LF.fetch(static_cast<const T*>(A.R) + sbase, (size_t)kBP, N, kBP);
+    LH.fetch(static_cast<const T*>(A.S) + sbase, (size_t)kBP, N, kBP);
+    // fp16 states: the factor of each read's row (1 for fp32 states)
+    float fu[LF.IT], hu[LF.IT];
+#pragma unroll
+    for (int i = 0; i < LF.IT; ++i) {
+      fu[i] = hu[i] = 1.f;
+      if constexpr (sizeof(T) == 2) {
+        const int r = (threadIdx.x + NT * i) / LF.RPR;
+        if (r < N) {
+          const size_t ui = sbase / kBP + r;  // ((b nb + c) H + h) N + r
+          fu[i] = A.Fu[ui];
+          hu[i] = A.Hu[ui];
+        }
+      }
+    }
+    auto fsc = [&](int i, int) { return fu[i]; };
+    auto hsc = [&](int i, int) { return hu[i]; };
     float eh = 0.f;
 #pragma unroll
-    for (int i = 0; i < LF.IT; ++i)
+    for (int i = 0; i < LF.IT; ++i) {
+      float e = 0.f;
 #pragma unroll
-      for (int j = 0; j < LF.V; ++j) eh += to_f32(LF.raw[i][j]) * to_f32(LH.raw[i][j]);
-    float mx[3] = {LD.absmax(one), LF.absmax(one), LH.absmax(one)};
+      for (int j = 0; j < LF.V; ++j) e += to_f32(LF.raw[i][j]) * to_f32(LH.raw[i][j]);
+      eh += e * (fu[i] * hu[i]);
+    }
+    float mx[3] = {LD.absmax(one), LF.absmax_ir(fsc), LH.absmax_ir(hsc)};
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
 #pragma unroll
@@ -581,8 +656,8 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
     }
     LX.store(Xs, one, 1.f);
     LD.store(Dys, one, scl[0]);
-    LF.store(Ss, one, scl[1]);
-    LH.store(Hs, one, scl[2]);
+    LF.store_ir(Ss, fsc, scl[1]);
+    LH.store_ir(Hs, hsc, scl[2]);
     const float udy = 1.f / scl[0], uF = 1.f / scl[1], uHdy = 1.f / (scl[2] * scl[0]);
     __syncthreads();
     float dap = eh * (float)Lc * pw[Lc - 1];  // this lane's part of da for the head
@@ -748,7 +823,7 @@ int scan_bwd_slices(bool is_bf16, int Bt, int T, int H, int G) {
 // with their per-(chunk, head) factors, da's parts, and the head slices'
 // dB_hat / dC~ parts.
 struct BwdWs {
-  size_t H, F, Sl, Rl, Su, Ru, dap, parts, total;
+  size_t H, F, Hu, Fu, Sl, Rl, Su, Ru, dap, parts, total;
 };
 
 static BwdWs bwd_ws(bool is_bf16, int Bt, int T, int H, int G, int N, int k) {
@@ -762,8 +837,10 @@ static BwdWs bwd_ws(bool is_bf16, int Bt, int T, int H, int G, int N, int k) {
   const size_t M = (size_t)Bt * T;
   BwdWs w{};
   size_t off = 0;
-  w.H = off; off += up(elems * 4);
-  w.F = off; off += up(elems * 4);
+  w.H = off; off += up(elems * les);
+  w.F = off; off += up(elems * les);
+  w.Hu = off; off += up((size_t)Bt * nb * H * N * 4);
+  w.Fu = off; off += up((size_t)Bt * nb * H * N * 4);
   w.Sl = off; off += up(elems * les);
   w.Rl = off; off += up(elems * les);
   w.Su = off; off += up((size_t)Bt * nb * H * 4);
@@ -865,8 +942,9 @@ hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N
   float* dCp = dBp + (size_t)hs * M * k * G * N;
   BwdArgs A{B_hat, X_hat, C_mix, dy, a, h_init, dh_final, dB, dX, dC, da, dh_init,
             w8 + w.Sl, w8 + w.Rl, reinterpret_cast<float*>(w8 + w.Su),
-            reinterpret_cast<float*>(w8 + w.Ru), reinterpret_cast<float*>(w8 + w.H),
-            reinterpret_cast<float*>(w8 + w.F), reinterpret_cast<float*>(w8 + w.dap), dBp, dCp,
+            reinterpret_cast<float*>(w8 + w.Ru), w8 + w.H, w8 + w.F,
+            reinterpret_cast<float*>(w8 + w.Hu), reinterpret_cast<float*>(w8 + w.Fu),
+            reinterpret_cast<float*>(w8 + w.dap), dBp, dCp,
             T, H, G, N, k, nb, hs};
   if (is_bf16) return launch_bwd_ty<f16, f16, bf16>(A, Bt, s);
   return launch_bwd_ty<float, float, float>(A, Bt, s);
