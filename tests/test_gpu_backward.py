@@ -128,3 +128,46 @@ def test_scan_backward_empty_sequence():
     # no tokens: h_final = h_init, so dh_init = dh_final, and da = 0
     assert np.array_equal(host(dh0), dhT.astype(np.float64))
     assert np.all(host(da) == 0)
+
+
+GRADED = [
+    # (name, workload): the small shape takes the two-element sweep, the
+    # second has enough states (Bt H N P / 8 >= 131072) for the 8-element one
+    ("narrow", W("b13", 813, seqlen=300)),
+    ("wide", W("b14", 814, batch=4, nheads=32, seqlen=130)),
+]
+
+
+@pytest.mark.parametrize("name,wl", GRADED, ids=[g[0] for g in GRADED])
+def test_scan_backward_rows_over_many_binades(name, wl):
+    """The entering states are stored as fp16 rows, each under its own
+    power-of-two factor. Rows of h_init and dh_final set 2^-10 .. 2^10 apart
+    (two different patterns over the state rows) give neighbouring rows
+    different factors, so a factor written or read for the wrong row, or a
+    row maximum taken over the wrong lanes, shows as a large error. (Wider
+    spreads approach the bar for another reason: the matrix-core tiles built
+    from the states share one power-of-two scale per tile, so rows far below
+    the tile's largest fall into fp16's subnormal range; 2^-20 .. 2^20 gave
+    1.7e-2 in dC~, with fp32 states as well.)"""
+    say(f"[scan_bwd graded] {name} Bt={wl.batch} H={wl.nheads} T={wl.seqlen}")
+    inp = synth.make_inputs(wl)
+    B_hat, X, C_mix = streams(wl, inp)
+    dy, h_init, dh_final = grads_in(wl, True, True)
+    n = np.arange(wl.dstate)
+    h_init = (h_init * (2.0 ** ((n % 21) - 10))[None, None, :, None]).astype(np.float32)
+    dh_final = (dh_final * (2.0 ** (((7 * n) % 21) - 10))[None, None, :, None]).astype(np.float32)
+    a = inp["a"]
+    ref = ob.recurrence_backward(B_hat, X, C_mix, a.astype(np.float64), h_init, dy, dh_final,
+                                 wl.batch, wl.seqlen)
+    got = run_backward(wl, B_hat, X, C_mix, a, dy, h_init, dh_final)
+    Bt, T, k, H, G, N = wl.batch, wl.seqlen, wl.top_k, wl.nheads, wl.ngroups, wl.dstate
+    tol = TOL[wl.dtype]
+    for g in got:
+        assert np.all(np.isfinite(g))
+    e_dB = slice_err(got[0].reshape(Bt, T * k, G, N), ref[0].reshape(Bt, T * k, G, N))
+    e_dX = slice_err(got[1].reshape(Bt, T * k, H, 64), ref[1].reshape(Bt, T * k, H, 64))
+    e_dC = slice_err(got[2].reshape(Bt, T, G, N), ref[2].reshape(Bt, T, G, N))
+    e_da = float(np.max(np.abs(got[3] - ref[3])) / max(np.max(np.abs(ref[3])), 1e-30))
+    e_dh = slice_err(got[4], ref[4], (0, 1))
+    say(f"  dB {e_dB:.2e} dX {e_dX:.2e} dC {e_dC:.2e} da {e_da:.2e} dh_init {e_dh:.2e}")
+    assert e_dB < tol and e_dX < tol and e_dC < tol and e_dh < tol and e_da < tol
