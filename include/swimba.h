@@ -280,9 +280,12 @@ swimba_status swimba_decode_step_mixed(const swimba_dims* dims, const void* u,
  * solved in chunks of 64 tokens (32 for float32 problems) whatever
  * dims->chunk is: local chunk states on matrix cores, a sweep over chunks for
  * the states entering each chunk from either side, and the within-chunk
- * quadratic forms on matrix cores (bf16 operands, or float32, fp32
- * accumulation). Sums over heads and chunks run in a fixed order, so results
- * are deterministic.
+ * quadratic forms on matrix cores (for bf16 problems fp16 operands, dy and
+ * the states under power-of-two scales; float32 operands for float32
+ * problems; fp32 accumulation). For bf16 problems the chunk states cross HBM
+ * in the workspace as fp16 (rows of P elements for the entering states),
+ * each under a power-of-two factor; the sweep sums in fp32. Sums over heads
+ * and chunks run in a fixed order, so results are deterministic.
  *   B_hat, X_hat, C_mix, a, h_init   as given to swimba_ssd_chunk_scan
  *   dy        [M, H, P] dtype
  *   dh_final  [Bt, H, N, P] float32, or NULL for zeros
