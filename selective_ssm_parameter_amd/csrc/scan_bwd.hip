@@ -409,20 +409,21 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
-// Largest x over each aligned group of G lanes (G a power of two up to 32),
+// Largest x over each aligned group of G lanes (G a power of two up to 64),
 // every lane of the group receiving it. Within 16 lanes the steps are DPP
 // moves (quad permutations [1,0,3,2] and [2,3,0,1], then the half-row and row
 // mirrors, each pairing a block of lanes whose maximum is already known with
-// its neighbour); only the step between the two 16-lane rows of a 32-lane
-// group goes through the cross-lane permute.
+// its neighbour); only the steps between 16-lane rows go through the
+// cross-lane permute.
 template <int G>
 __device__ __forceinline__ float group_max(float m) {
-  static_assert(G >= 1 && G <= 32 && (G & (G - 1)) == 0, "power-of-two group up to 32 lanes");
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "power-of-two group up to 64 lanes");
   if constexpr (G >= 2) m = fmaxf(m, dpp_f<0xB1>(m));
   if constexpr (G >= 4) m = fmaxf(m, dpp_f<0x4E>(m));
   if constexpr (G >= 8) m = fmaxf(m, dpp_f<0x141>(m));
   if constexpr (G >= 16) m = fmaxf(m, dpp_f<0x140>(m));
   if constexpr (G >= 32) m = fmaxf(m, __shfl_xor(m, 16));
+  if constexpr (G >= 64) m = fmaxf(m, __shfl_xor(m, 32));
   return m;
 }
 
@@ -864,13 +865,13 @@ static hipError_t launch_bwd_t(const BwdArgs& A, int Bt, hipStream_t s) {
   prof_end(s);
   prof_begin("scan_bwd_sweep", s);
   {
-    // 16 bytes of local state per thread, or 2 elements when that leaves
+    // 16 bytes of local state per thread, or 4 elements when that leaves
     // fewer than 128K threads for the walk
     constexpr int V16 = 16 / (int)sizeof(T);
     const bool narrow = (size_t)Bt * A.H * A.N * kBP / V16 < (size_t)131072;
-    const int V = narrow ? 2 : V16;
+    const int V = narrow ? 4 : V16;
     const dim3 gs((unsigned)((A.N * kBP / V + 255) / 256), A.H, Bt);
-    if (narrow) hipLaunchKernelGGL((bwd_sweep_kernel<T, BL, 2>), gs, dim3(256), 0, s, A);
+    if (narrow) hipLaunchKernelGGL((bwd_sweep_kernel<T, BL, 4>), gs, dim3(256), 0, s, A);
     else hipLaunchKernelGGL((bwd_sweep_kernel<T, BL, V16>), gs, dim3(256), 0, s, A);
   }
   prof_end(s);

@@ -131,7 +131,7 @@ def test_scan_backward_empty_sequence():
 
 
 GRADED = [
-    # (name, workload): the small shape takes the two-element sweep, the
+    # (name, workload): the small shape takes the four-element sweep, the
     # second has enough states (Bt H N P / 8 >= 131072) for the 8-element one
     ("narrow", W("b13", 813, seqlen=300)),
     ("wide", W("b14", 814, batch=4, nheads=32, seqlen=130)),
