@@ -96,11 +96,14 @@ def forward_tv(u: np.ndarray, w_router: np.ndarray, w_experts: np.ndarray,
 
 def decode_step_tv(u_t: np.ndarray, w_router: np.ndarray, w_experts: np.ndarray,
                    a_experts: np.ndarray, h: np.ndarray, *, nheads: int, headdim: int,
-                   ngroups: int, dstate: int, top_k: int) -> dict:
+                   ngroups: int, dstate: int, top_k: int, heads=None, routing=None) -> dict:
     """One recurrent decode step with the expert-mixed decay ([notes] Method,
-    key design 1, recurrent form). u_t: [Bt, D]; h: [Bt, H, N, P]."""
+    key design 1, recurrent form). u_t: [Bt, D]; h: [Bt, H, N, P] over all
+    heads; ``heads`` and ``routing`` as for ``forward_tv`` (y and the new
+    state are then over those heads)."""
     out = forward_tv(u_t[:, None, :], w_router, w_experts, a_experts, h, nheads=nheads,
-                     headdim=headdim, ngroups=ngroups, dstate=dstate, top_k=top_k)
+                     headdim=headdim, ngroups=ngroups, dstate=dstate, top_k=top_k,
+                     heads=heads, routing=routing)
     return {"y": out["y"][:, 0], "h": out["h_final"], "routing": out["routing"],
             "a_t": out["a_t"]}
 

@@ -85,6 +85,57 @@ def route(u: np.ndarray, w_router: np.ndarray, top_k: int) -> Routing:
     return Routing(logits=g, pi=pi, idx=idx.astype(np.int64), w=w, margin=margin)
 
 
+def tie_alternatives(routing: Routing, m: int) -> list:
+    """Every ordered top-k selection of token m that a near-tie leaves open.
+
+    The top-k set of [notes] Method, key design 1 is decided by the logits;
+    where two of the leading logits lie within TIE_MARGIN of each other, a
+    computation in another precision may order them either way, and both
+    orders are correct. The fp64 logits are sorted (descending, exact ties to
+    the lower index) and split into runs whose consecutive gaps are below the
+    margin; any order that permutes experts inside a run is a valid order,
+    and its first k entries a valid selection. Returns the distinct
+    selections (tuples of expert ids), the unperturbed one first.
+    """
+    import itertools
+
+    g = routing.logits[m]
+    k = routing.idx.shape[1]
+    order = list(np.argsort(-g, kind="stable"))
+    runs, cur = [], [order[0]]
+    for e in order[1:]:
+        if g[cur[-1]] - g[e] < TIE_MARGIN:
+            cur.append(e)
+        else:
+            runs.append(cur)
+            cur = [e]
+    runs.append(cur)
+    # only runs that start among the first k positions can change the selection
+    pos, lead = 0, []
+    for r in runs:
+        if pos >= k:
+            break
+        lead.append(r)
+        pos += len(r)
+    out, seen = [], set()
+    for perm in itertools.product(*[itertools.permutations(r) for r in lead]):
+        sel = tuple(int(e) for e in itertools.chain(*perm))[:k]
+        if sel not in seen:
+            seen.add(sel)
+            out.append(sel)
+    return out
+
+
+def with_selection(routing: Routing, m: int, sel) -> Routing:
+    """The routing with token m's ordered selection replaced by ``sel`` (one
+    of ``tie_alternatives(routing, m)``); its weights are pi at ``sel``."""
+    idx = routing.idx.copy()
+    idx[m] = np.asarray(sel, dtype=np.int64)
+    w = routing.w.copy()
+    w[m] = routing.pi[m, idx[m]]
+    return Routing(logits=routing.logits, pi=routing.pi, idx=idx, w=w, margin=routing.margin)
+
+
 def expert_streams(u: np.ndarray, w_experts: np.ndarray, idx: np.ndarray,
                    nheads: int, headdim: int, ngroups: int, dstate: int,
                    heads=None) -> Streams:
@@ -202,11 +253,12 @@ def output_project(y: np.ndarray, w_out: np.ndarray) -> np.ndarray:
 
 def decode_step(u_t: np.ndarray, w_router: np.ndarray, w_experts: np.ndarray, a: np.ndarray,
                 h: np.ndarray, *, nheads: int, headdim: int, ngroups: int, dstate: int,
-                top_k: int, heads=None) -> dict:
+                top_k: int, heads=None, routing: Routing | None = None) -> dict:
     """One recurrent decode step: the same recurrence for a single token.
 
     [notes] Method, key design 1 (recurrent form); [notes] key findings, vLLM
     decoding. u_t: [Bt, D]; h: [Bt, H, N, P] (or the heads in ``heads``).
+    ``routing`` as for ``forward``.
     """
     Bt = u_t.shape[0]
     h_full = h
@@ -214,5 +266,6 @@ def decode_step(u_t: np.ndarray, w_router: np.ndarray, w_experts: np.ndarray, a:
         h_full = np.zeros((Bt, nheads) + h.shape[2:])
         h_full[:, np.asarray(heads)] = h
     out = forward(u_t[:, None, :], w_router, w_experts, a, h_full, nheads=nheads,
-                  headdim=headdim, ngroups=ngroups, dstate=dstate, top_k=top_k, heads=heads)
+                  headdim=headdim, ngroups=ngroups, dstate=dstate, top_k=top_k, heads=heads,
+                  routing=routing)
     return {"y": out["y"][:, 0], "h": out["h_final"], "routing": out["routing"]}

@@ -67,6 +67,52 @@ def check_router_sigmoid_and_ties():
     assert r.w[0, 0] == pytest.approx(math.exp(1.0) / sum(math.exp(v) for v in (0.25, 1, 0.5, 0)))
 
 
+def check_tie_alternatives():
+    # Exact and near ties leave the order of the tied experts open; nothing
+    # else. Logits are set by a one-column router on u = 1.
+    def alts(logits, k):
+        r = osw.route(np.array([[1.0]]), np.array(logits, np.float64)[:, None], k)
+        return r, osw.tie_alternatives(r, 0)
+
+    # no near tie: only the oracle's own selection
+    r, a = alts([0.3, 1.0, 0.7, 0.1], 2)
+    assert a == [(1, 2)]
+    # a near tie between rank 1 and rank 2 (the last selected slot and the
+    # first unselected expert): either may take the slot
+    r, a = alts([0.3, 1.0, 0.7, 0.7 - 4e-6], 2)
+    assert r.flagged[0] and a == [(1, 2), (1, 3)]
+    # a near tie between the two selected experts: both orders, same set
+    r, a = alts([0.3, 1.0, 1.0 - 3e-6, 0.1], 2)
+    assert a == [(1, 2), (2, 1)]
+    # a gap just above the margin is decided
+    r, a = alts([0.3, 1.0, 1.0 - 2e-5, 0.1], 2)
+    assert not r.flagged[0] and a == [(1, 2)]
+    # a tie below the selected slots changes nothing
+    r, a = alts([0.3, 1.0, 0.8, 0.3 - 1e-6], 2)
+    assert a == [(1, 2)]
+    # three exact ties with one slot left: each may take it (lower index first)
+    r, a = alts([0.5, 1.0, 0.5, 0.5], 2)
+    assert a[0] == (1, 0) and sorted(a) == [(1, 0), (1, 2), (1, 3)]
+    # every alternative is k distinct experts whose logits match the oracle's
+    # ranks within the margin, and with_selection takes pi at the selection
+    rng = np.random.default_rng(17)
+    for _ in range(200):
+        E, k = int(rng.integers(2, 7)), int(rng.integers(1, 4))
+        k = min(k, E)
+        g = rng.standard_normal(E)
+        g[rng.integers(0, E)] = g[rng.integers(0, E)] + rng.choice([0.0, 3e-6, 5e-5])
+        r, a = alts(g, k)
+        assert a[0] == tuple(r.idx[0])
+        for sel in a:
+            assert len(set(sel)) == k
+            assert np.all(np.abs(r.logits[0, list(sel)] - r.logits[0, r.idx[0]]) < k * osw.TIE_MARGIN)
+            r2 = osw.with_selection(r, 0, sel)
+            assert tuple(r2.idx[0]) == sel and np.array_equal(r2.w[0], r.pi[0, list(sel)])
+            assert tuple(r.idx[0]) == a[0]  # the original routing is untouched
+        if not r.flagged[0]:
+            assert a == [tuple(r.idx[0])]
+
+
 def check_projection_triple_loop():
     rng = np.random.default_rng(5)
     M, D, E, H, P, G, N, k = 5, 4, 3, 2, 2, 1, 3, 2
@@ -337,6 +383,10 @@ def check_head_subset():
 
 def test_router_sigmoid_and_ties():
     check_router_sigmoid_and_ties()
+
+
+def test_tie_alternatives():
+    check_tie_alternatives()
 
 
 def test_projection_triple_loop():
