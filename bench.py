@@ -1,18 +1,22 @@
 """Throughput of the Swimba mixer hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-route + top-k, expert projection with the mix epilogue, the chunked scan over
-the batch (prefill), then one recurrent decode step of every sequence from
-the prefill's final state. Inputs are resident in HBM before timing starts.
+route + top-k, expert projection with the mix epilogue, and the chunked scan
+over the batch (prefill). The default workload is the largest prefill
+(batch 4 x 8192 tokens, d_model 2048, 64 heads, E = 16, k = 2, chunk 128).
+Inputs are resident in HBM before timing starts.
 The recurrent decode workload (``--config c5``: batch 256, one token per
 sequence per step, the N x P state of every head resident in HBM) times
 decode steps alone: one step = one token of every sequence.
 
-Prints ONE JSON line. ``value`` is tokens per second (prefill tokens plus the
-decoded tokens) over the timed steps. ``roofline`` describes the kernel with
-the largest share of the step (found in an untimed pass with events around
-every kernel); inside the timed region the library records a HIP event pair
-around each launch of that kernel only, on the stream it runs on.
+Prints ONE JSON line. ``value`` is tokens per second over the timed steps.
+``roofline`` describes the kernel with the largest share of the step (found
+in an untimed pass with events around every kernel); ``roofline_scan`` the
+scan's chunk-output kernel (the intra-chunk and readout work); inside the
+timed region the library records a HIP event pair around each launch of
+those kernels only, on the stream they run on. ``scan_pipeline`` sums the
+scan's kernels (from the untimed pass) against the bytes the scan must move
+at least: its input streams once and y once.
 ``cpu_baseline`` is the fp64 oracle timed on a bounded sample of the same
 workload on this host's cores.
 """
@@ -276,9 +280,9 @@ def run_gpu(args):
         dims = sb.dims_of(wl)
         buf = sb.alloc_buffers(dims, dev)
     ddims = sb.dims_of(wl, seqlen=1)
-    dws, _ = sb.workspace(ddims, sb.CALL_DECODE, dev)
-    u_dec = up(synth.decode_token(wl, 0))
-    y_dec = torch.empty(wl.batch, wl.nheads, wl.headdim, dtype=dt, device=dev)
+    if is_decode(wl):
+        dws, _ = sb.workspace(ddims, sb.CALL_DECODE, dev)
+        y_dec = torch.empty(wl.batch, wl.nheads, wl.headdim, dtype=dt, device=dev)
     stream = torch.cuda.current_stream()
 
     if is_decode(wl):
@@ -313,15 +317,11 @@ def run_gpu(args):
                 sb.forward(dims, u, wr, we, a, None, buf)
                 sb.backward(dims, u, wr, we, a, None, dy, None, buf, grads, saved=True)
                 return
-            # prefill the batch, then decode one more token of every sequence,
-            # updating the prefill's final state in place
+            # prefill the batch
             if mixed:
                 sb.forward_mixed(dims, u, wr, we, a_exp, None, buf, log_decay)
-                sb.swimba_decode_step_mixed(ddims, u_dec, wr, we, a_exp, buf.h_final, y_dec, None,
-                                            dws)
             else:
                 sb.forward(dims, u, wr, we, a, None, buf)
-                sb.swimba_decode_step(ddims, u_dec, wr, we, a, buf.h_final, y_dec, None, dws)
 
     for _ in range(args.warmup):
         step()
@@ -349,9 +349,10 @@ def run_gpu(args):
     torch.cuda.synchronize()
     elapsed_plain = time.perf_counter() - t0
 
-    # The timed region: the dominant kernel is bracketed by HIP events recorded
-    # on the stream it runs on.
-    sb.profile_select(("decode_" if is_decode(wl) else "") + dom)
+    # The timed region: the dominant kernel (and the scan's chunk output) are
+    # bracketed by HIP events recorded on the stream they run on.
+    timed = [dom] + ([SCAN_KERNEL] if SCAN_KERNEL in report and SCAN_KERNEL != dom else [])
+    sb.profile_select(",".join(("decode_" if is_decode(wl) else "") + n for n in timed))
     sb.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -375,29 +376,44 @@ def run_gpu(args):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    tokens = wl.batch if is_decode(wl) else wl.tokens if backward else wl.tokens + wl.batch
+    tokens = wl.batch if is_decode(wl) else wl.tokens
     value = tokens * args.steps / elapsed
-    bound, flops, nbytes = models[dom]
-    avg_s = rep_dom[dom]["ms"] / rep_dom[dom]["launches"] / 1e3
-    if bound == "mfma":
-        achieved = flops / avg_s / 1e12
-        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
-        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": stored_traffic(dom, profile_key(wl.name, "mixed" if mixed else "shared",
-                                                           backward)),
-                "algorithmic_flops": flops, "avg_us": avg_s * 1e6}
-    else:
+    key = profile_key(wl.name, "mixed" if mixed else "shared", backward)
+
+    def roofline(name):
+        bound, flops, nbytes = models[name]
+        avg_s = rep_dom[name]["ms"] / rep_dom[name]["launches"] / 1e3
+        if bound == "mfma":
+            achieved = flops / avg_s / 1e12
+            peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+            return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": peak,
+                    "unit": "TFLOP/s", "frac": achieved / peak,
+                    "traffic": stored_traffic(name, key),
+                    "algorithmic_flops": flops, "avg_us": avg_s * 1e6}
         achieved = nbytes / avg_s / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+        return {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "traffic": stored_traffic(dom, profile_key(wl.name, "mixed" if mixed else "shared",
-                                                           backward)),
-                "algorithmic_bytes": nbytes, "avg_us": avg_s * 1e6}
+                "traffic": stored_traffic(name, key),
+                "algorithmic_bytes": nbytes, "avg_us": avg_s * 1e6,
+                "algorithmic_flops": flops,
+                "mfma_frac": flops / avg_s / 1e12 / PEAK_BF16_TFLOPS}
+
     res = {
-        "wl": wl, "value": value, "elapsed": elapsed, "kernels": kernels, "roofline": roof,
+        "wl": wl, "value": value, "elapsed": elapsed, "kernels": kernels,
+        "roofline": roofline(dom),
         "value_without_events": tokens * args.steps / elapsed_plain,
     }
+    if len(timed) > 1:
+        res["roofline_scan"] = roofline(SCAN_KERNEL)
+    if not is_decode(wl) and not backward:
+        # the scan's kernels together against the bytes it must move at least
+        names = [n for n in SCAN_PIPELINE if n in kernels]
+        us = sum(kernels[n]["avg_us"] for n in names)
+        nbytes = models[SCAN_KERNEL][2]
+        res["scan_pipeline"] = {"kernels": names, "avg_us": us, "bound": "hbm",
+                                "algorithmic_bytes": nbytes,
+                                "achieved": nbytes / us / 1e3, "unit": "GB/s",
+                                "frac": nbytes / us / 1e3 / PEAK_HBM_GBS}
     if is_decode(wl):
         # Every kernel of a decode step is bound by HBM, and a kernel's time
         # also carries the write-back of dirty lines the one before it left
@@ -412,6 +428,8 @@ def run_gpu(args):
     return res
 
 
+SCAN_KERNEL = "scan_chunk_output"
+SCAN_PIPELINE = ("scan_gram", "scan_segment_state", "scan_state_pass", "scan_chunk_output")
 E_SWEEP = (4, 8, 16, 32, 64)
 
 
@@ -656,7 +674,7 @@ def summarize_trace(trace_dir, wl_name, out, command, bench_json=None):
     base, mixed, backward = parse_key(wl_name)
     kind = ("decode steps" if is_decode(workload(base)) else
             "training step (prefill forward + backward)" if backward else
-            "bench step (prefill + decode)")
+            "bench step (prefill)")
     what = f"workload {base}" + (", expert-mixed decay" if mixed else "")
     lines = [f"# Kernel durations, {kind} on {what}", "",
              "Command (from the repository root, after building the library):", "",
@@ -731,8 +749,7 @@ def summarize_pmc(fetch_dir, write_dir, wl_name, out, commands):
                "The forward's kernels launch twice per step (the backward recomputes the "
                "routing and the projection); the algorithmic bytes are per launch."
                if backward else
-               "Launches on the larger grid are the prefill's, those on the smaller one the "
-               "decode step's; the algorithmic bytes are those of the prefill launch."), "",
+               "Every launch is the prefill's; the algorithmic bytes are per launch."), "",
               "| kernel | workgroups | read MB | written MB | traffic MB | algorithmic MB |",
               "|---|---:|---:|---:|---:|---:|"]
     keys = sorted(set(fetch) | set(write), key=lambda k: -(fetch.get(k, 0) + write.get(k, 0)))
@@ -758,7 +775,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decay", default="shared", choices=["shared", "mixed"],
                     help="mixed: the expert-mixed diagonal transition (per-expert decays "
@@ -828,7 +845,7 @@ def main():
                          f"heads={wl.nheads}, P={wl.headdim}, N={wl.dstate} fp32 state per "
                          f"head in HBM, E={wl.n_experts}, top-k={wl.top_k}")
             if is_decode(wl) else
-                        (f"Swimba mixer prefill + 1 decode step, {wl.dtype}: batch {wl.batch}, "
+                        (f"Swimba mixer prefill (forward), {wl.dtype}: batch {wl.batch}, "
                          f"T={wl.seqlen}, d_model={wl.d_model}, heads={wl.nheads}, "
                          f"P={wl.headdim}, N={wl.dstate}, E={wl.n_experts}, "
                          f"top-k={wl.top_k}, chunk {wl.chunk}"))
@@ -840,8 +857,9 @@ def main():
         "kernels": r["kernels"],
         "value_without_events": r["value_without_events"],
     }
-    if "step_roofline" in r:
-        out["step_roofline"] = r["step_roofline"]
+    for extra in ("roofline_scan", "scan_pipeline", "step_roofline"):
+        if extra in r:
+            out[extra] = r[extra]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_backward(wl) if args.backward else
                                cpu_baseline(wl, mixed=args.decay == "mixed"))

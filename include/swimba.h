@@ -370,8 +370,9 @@ swimba_status swimba_expert_project_mix_backward_saved(
  */
 swimba_status swimba_profile_enable(int32_t on);
 int32_t swimba_profile_report(char* buf, size_t cap);
-/* Restrict the timing to kernels of this name (host string, copied); NULL or
- * "" records every kernel. Decode-step kernels carry the prefix "decode_". */
+/* Restrict the timing to kernels of these names (host string, copied: one
+ * name or several separated by commas); NULL or "" records every kernel.
+ * Decode-step kernels carry the prefix "decode_". */
 swimba_status swimba_profile_select(const char* kernel);
 
 #ifdef __cplusplus

@@ -231,7 +231,7 @@ struct ProfRec {
 
 std::mutex g_prof_mu;
 bool g_prof_on = false;
-std::string g_prof_only;  // record only this kernel name (empty: all)
+std::vector<std::string> g_prof_only;  // record only these kernel names (empty: all)
 thread_local const char* g_prof_prefix = "";  // "decode_" inside swimba_decode_step
 bool g_prof_open = false;                      // a begin without its end yet
 std::vector<ProfRec> g_prof_recs;
@@ -256,7 +256,9 @@ void prof_begin(const char* name, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
   std::string full = std::string(g_prof_prefix) + name;
-  if (!g_prof_only.empty() && full != g_prof_only) return;
+  if (!g_prof_only.empty() &&
+      std::find(g_prof_only.begin(), g_prof_only.end(), full) == g_prof_only.end())
+    return;
   ProfRec r{full, prof_event(), prof_event()};
   if (!r.start || !r.stop) return;
   g_prof_open = true;
@@ -677,7 +679,15 @@ swimba_status swimba_profile_enable(int32_t on) {
 
 swimba_status swimba_profile_select(const char* kernel) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_only = kernel ? kernel : "";
+  g_prof_only.clear();
+  const std::string list = kernel ? kernel : "";
+  size_t pos = 0;
+  while (pos < list.size()) {
+    size_t end = list.find(',', pos);
+    if (end == std::string::npos) end = list.size();
+    if (end > pos) g_prof_only.emplace_back(list.substr(pos, end - pos));
+    pos = end + 1;
+  }
   return SWIMBA_OK;
 }
 

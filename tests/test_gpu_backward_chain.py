@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, check_routing, dev, host, run_forward, say, slice_err, tdt, upload
+from gpu_util import (F32_TINY, TOL, check_routing, dev, host, run_forward, say, slice_err, sub_routing, tdt,
+                      upload)
 from oracle import backward as ob
 from oracle import swimba as osw
 from selective_ssm_parameter_amd import binding as sb
@@ -96,34 +97,40 @@ def test_backward_chain_small(name, wl):
 
 
 FULL = [
-    # workload, sequences, heads, tokens of dy per sequence (None: all)
-    ("c2", [0, 7], [0, 11, 23], None),
-    # 4 x 8192 tokens: two head slices of 32; the prefix avoids the near-tie
-    # tokens of sequences 0 and 1 (flips after it cannot reach any gradient)
-    ("c3", [0, 2], [0, 31, 63], 2048),
+    # workload, sequences, heads, tokens [t0, t1) of dy per sequence (None: all),
+    # whether dh_final is nonzero on those heads
+    ("c2", [0, 7], [0, 11, 23], None, True),
+    # 4 x 8192 tokens: two head slices of 32
+    ("c3", [0, 2], [0, 31, 63], (0, 2048), False),
     # 1 x 65536 tokens, 1024 chunks: one head slice, the narrow sweep
-    ("c4", [0], [0, 17, 31], 4096),
+    ("c4", [0], [0, 17, 31], (0, 4096), False),
+    # the same with dy on the last 4096 tokens and dh_final nonzero: both
+    # walks of the sweep then carry states over all 1024 chunks
+    ("c4_tail", [0], [0, 17, 31], (65536 - 4096, 65536), True),
 ]
 
 
-@pytest.mark.parametrize("name,seqs,heads,prefix", FULL, ids=[f[0] for f in FULL])
-def test_backward_chain_full_size(name, seqs, heads, prefix):
-    """The whole backward at a full workload size; dy (and dh_final when dy
-    covers whole sequences) nonzero on a few heads of a few sequences, on the
-    first `prefix` tokens only: every other gradient is then exactly zero, and
-    the oracle runs those heads over the prefix alone."""
-    wl = synth.WORKLOADS[name]
+@pytest.mark.parametrize("name,seqs,heads,span,with_dh", FULL, ids=[f[0] for f in FULL])
+def test_backward_chain_full_size(name, seqs, heads, span, with_dh):
+    """The whole backward at a full workload size; dy nonzero on a few heads
+    of a few sequences over the tokens of ``span``, dh_final nonzero on those
+    heads when ``with_dh``: a gradient then reaches only tokens before the
+    span's end (every token when dh_final is nonzero), and every other
+    gradient is exactly zero. The oracle runs those heads over the tokens a
+    gradient reaches."""
+    wl = synth.WORKLOADS[name.split("_")[0]]
     Bt, T, H, N, P, k = wl.batch, wl.seqlen, wl.nheads, wl.dstate, wl.headdim, wl.top_k
-    Tp = T if prefix is None else prefix
+    t0, t1 = (0, T) if span is None else span
+    Tp = T if with_dh else t1          # tokens a gradient reaches
     say(f"[bwd_chain] full size {name}: M={wl.tokens} sequences {seqs} heads {heads} "
-        f"tokens {Tp}")
+        f"dy tokens [{t0}, {t1}) dh_final {'on' if with_dh else 'off'}")
     inp = synth.make_inputs(wl)
     dy_all, dh_all = seeded_upstream(wl, 73)
     dy = np.zeros_like(dy_all)
     dh = np.zeros_like(dh_all)
     for b in seqs:
-        dy[b][:Tp][:, heads] = dy_all[b][:Tp][:, heads]
-        if prefix is None:
+        dy[b][t0:t1][:, heads] = dy_all[b][t0:t1][:, heads]
+        if with_dh:
             dh[b][heads] = dh_all[b][heads]
     buf, g = run_chain(wl, inp, dy, dh)
     M = wl.tokens
@@ -132,9 +139,9 @@ def test_backward_chain_full_size(name, seqs, heads, prefix):
     we64 = np.asarray(inp["w_experts"], np.float64)
     a64 = np.asarray(inp["a"], np.float64)
     r = osw.route(u64, wr64, k)
-    flips = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), r, wl)
-    for m in flips:  # a flip may only sit where no gradient reaches
-        assert m // T not in seqs or m % T >= Tp, f"near-tie flip at token {m} inside the checked span"
+    # the oracle's routing with its own alternative at any near-tie the GPU
+    # ordered the other way
+    r = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), r, wl)
     gB = host(g.dB_hat).reshape(Bt, T, k, 1, N)
     gX = host(g.dX_hat).reshape(Bt, T, k, H, P)
     gC = host(g.dC_mix).reshape(Bt, T, 1, N)
@@ -160,8 +167,7 @@ def test_backward_chain_full_size(name, seqs, heads, prefix):
 
     for b in seqs:
         rows = slice(b * T, b * T + Tp)
-        rb = osw.Routing(logits=r.logits[rows], pi=r.pi[rows], idx=r.idx[rows], w=r.w[rows],
-                         margin=r.margin[rows])
+        rb = sub_routing(r, rows)
         s = osw.expert_streams(u64[rows], we64, rb.idx, H, P, wl.ngroups, N, heads=heads)
         B_hat, X, C_mix = osw.mix_streams(s, rb.w)
         h0 = None if inp["h_init"] is None else np.asarray(inp["h_init"], np.float64)[b:b + 1, heads]
@@ -173,7 +179,10 @@ def test_backward_chain_full_size(name, seqs, heads, prefix):
         upd("dX_hat", slice_err(gX[b:b + 1, :Tp][:, :, :, heads].reshape(1, Tp * k, len(heads), P),
                                 dX.reshape(1, Tp * k, len(heads), P)))
         upd("dC_mix", slice_err(gC[b:b + 1, :Tp], dC.reshape(1, Tp, 1, N)))
-        upd("dh_init", slice_err(host(g.dh_init)[b:b + 1, heads], dh0, (0, 1)))
+        # over 65536 tokens the slowest-decaying heads leave dh_init far below
+        # fp32's normal range (a^65536 ~ 1e-97 at a = 0.9966): compared with
+        # the fp32 floor
+        upd("dh_init", slice_err(host(g.dh_init)[b:b + 1, heads], dh0, (0, 1), floor=F32_TINY))
         # router, projection and mix: only the selected heads' X rows carry a
         # gradient, so the oracle runs on those rows of W_exp (exact for du)
         dBs, dCs, dw = ob.mix_backward(s, rb.w, dB, dC)

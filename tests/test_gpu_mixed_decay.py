@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from gpu_util import (TOL, check_routing, dev, host, round_stream, say, sdt, slice_err, tdt,
-                      upload, valid_prefix)
+                      upload)
 from oracle import mixed_decay as md
 from oracle import swimba as osw
 from selective_ssm_parameter_amd import binding as sb
@@ -201,14 +201,17 @@ def test_forward_mixed_end_to_end(name, wl):
     ref = md.forward_tv(inp["u"], inp["w_router"], inp["w_experts"], ae, inp["h_init"],
                         nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
                         dstate=wl.dstate, top_k=wl.top_k)
-    flips = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), ref["routing"], wl)
-    lim = valid_prefix(flips, wl.batch, wl.seqlen)
+    r = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), ref["routing"], wl)
+    if r is not ref["routing"]:
+        # the oracle's alternative selection at near-ties the GPU ordered the other way
+        ref = md.forward_tv(inp["u"], inp["w_router"], inp["w_experts"], ae, inp["h_init"],
+                            nheads=wl.nheads, headdim=wl.headdim, ngroups=wl.ngroups,
+                            dstate=wl.dstate, top_k=wl.top_k, routing=r)
     y = host(buf.y).reshape(wl.batch, wl.seqlen, wl.nheads, 64)
     for b in range(wl.batch):
-        e = slice_err(y[b:b + 1, :lim[b]], ref["y"][b:b + 1, :lim[b]])
+        e = slice_err(y[b:b + 1], ref["y"][b:b + 1])
         assert e < TOL[wl.dtype], (b, e)
-        if lim[b] == wl.seqlen:
-            assert slice_err(host(buf.h_final)[b:b + 1], ref["h_final"][b:b + 1], (0, 1)) < TOL[wl.dtype]
+        assert slice_err(host(buf.h_final)[b:b + 1], ref["h_final"][b:b + 1], (0, 1)) < TOL[wl.dtype]
 
 
 # ---------------------------------------------------------------- decode

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from gpu_util import (STREAM_TOL, TOL, check_routing, dev, host, oracle_forward, rel_err,
-                      round_stream, run_forward, say, sdt, slice_err, tdt, upload, valid_prefix)
+                      round_stream, run_forward, say, sdt, slice_err, tdt, upload)
 from oracle import swimba as osw
 from selective_ssm_parameter_amd import binding as sb
 from selective_ssm_parameter_amd import synth
@@ -285,14 +285,14 @@ def test_forward_end_to_end(name, wl):
     inp = synth.make_inputs(wl)
     buf = run_forward(wl, upload(wl, inp))
     ref = oracle_forward(wl, inp)
-    flips = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), ref["routing"], wl)
-    lim = valid_prefix(flips, wl.batch, wl.seqlen)
+    r = check_routing(host(buf.topk_idx).astype(np.int64), host(buf.topk_w), ref["routing"], wl)
+    if r is not ref["routing"]:
+        ref = oracle_forward(wl, inp, routing=r)   # the oracle's alternative at near-ties
     y = host(buf.y).reshape(wl.batch, wl.seqlen, wl.nheads, 64)
     for b in range(wl.batch):
-        e = slice_err(y[b:b + 1, :lim[b]], ref["y"][b:b + 1, :lim[b]])
+        e = slice_err(y[b:b + 1], ref["y"][b:b + 1])
         assert e < TOL[wl.dtype], (b, e)
-        if lim[b] == wl.seqlen:
-            assert slice_err(host(buf.h_final)[b:b + 1], ref["h_final"][b:b + 1], (0, 1)) < TOL[wl.dtype]
+        assert slice_err(host(buf.h_final)[b:b + 1], ref["h_final"][b:b + 1], (0, 1)) < TOL[wl.dtype]
 
 
 def test_forward_is_deterministic():
