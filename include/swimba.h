@@ -203,6 +203,25 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
                                  hipStream_t stream);
 
 /*
+ * swimba_decode_step for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same kernels and the same results, with the
+ * workspace in a static scratch array of 32 MiB per device that the library
+ * holds until the process ends (its address is looked up on the first call
+ * on each device; the calling thread's current device must own `stream`).
+ * Dims whose decode workspace (swimba_workspace_size(dims,
+ * SWIMBA_CALL_DECODE)) exceeds 32 MiB return SWIMBA_ERR_WORKSPACE before any
+ * launch. Every call on one device shares that scratch: calls that overlap
+ * on one device (other streams, other threads) race and must be serialised
+ * by the caller. Allocates nothing (no hipMalloc, no hipFree). Arguments and
+ * errors otherwise as for swimba_decode_step.
+ */
+swimba_status swimba_decode_step_noalloc(const swimba_dims* dims, const void* u,
+                                         const void* w_router, const void* w_experts,
+                                         const float* a, float* h, void* y, int32_t* topk_idx,
+                                         hipStream_t stream);
+
+/*
  * Output projection of the mixer: the single projection that follows the
  * recurrence (gist.science English summary, Technical Summary section 2,
  * Architecture Details, the state-update equation "followed by a single

@@ -30,7 +30,7 @@ EXPORTS = (
     "swimba_expert_project_mix", "swimba_ssd_chunk_scan", "swimba_decode_step",
     "swimba_output_project", "swimba_profile_enable", "swimba_profile_report",
     "swimba_profile_select", "swimba_mix_decay", "swimba_ssd_chunk_scan_mixed",
-    "swimba_decode_step_mixed", "swimba_ssd_chunk_scan_backward",
+    "swimba_decode_step_mixed", "swimba_decode_step_noalloc", "swimba_ssd_chunk_scan_backward",
     "swimba_expert_project_mix_backward", "swimba_expert_project_mix_backward_saved",
 )
 
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.swimba_mix_decay.restype = I32
     L.swimba_ssd_chunk_scan_mixed.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
     L.swimba_ssd_chunk_scan_mixed.restype = I32
+    L.swimba_decode_step_noalloc.restype = I32
+    L.swimba_decode_step_noalloc.argtypes = [D, P, P, P, P, P, P, P, S]
     L.swimba_decode_step_mixed.argtypes = [D, P, P, P, P, P, P, P, P, SZ, S]
     L.swimba_decode_step_mixed.restype = I32
     L.swimba_ssd_chunk_scan_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, S]
@@ -190,6 +192,12 @@ def swimba_decode_step(dims, u, w_router, w_experts, a, h, y, topk_idx, ws, ws_b
     _check(lib().swimba_decode_step(
         ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(a), _ptr(h), _ptr(y),
         _ptr(topk_idx), _ptr(ws), nb, _stream(stream)))
+
+
+def swimba_decode_step_noalloc(dims, u, w_router, w_experts, a, h, y, topk_idx, stream=None):
+    _check(lib().swimba_decode_step_noalloc(
+        ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(a), _ptr(h), _ptr(y),
+        _ptr(topk_idx), _stream(stream)))
 
 
 def swimba_mix_decay(dims, topk_idx, topk_w, a_experts, log_decay, stream=None):

@@ -15,6 +15,10 @@
 
 using namespace swimba;
 
+// Scratch of swimba_decode_step_noalloc (see scratch_ptr below).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_err;
@@ -583,10 +587,40 @@ swimba_status swimba_mix_decay(const swimba_dims* dims, const int32_t* topk_idx,
 
 namespace {
 
+// Scratch of swimba_decode_step_noalloc: the decode workspace (routing,
+// streams, bucketing, per-slot C parts) of one call, in a file-scope device
+// array instead of caller memory. Each device holds its own copy for the life
+// of the process; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in). Nothing in it needs to start at zero: every byte a
+// decode step reads was written earlier in the same step.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device.
+swimba_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SWIMBA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SWIMBA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SWIMBA_OK;
+}
+
+// noalloc: the workspace is the device's static scratch (ws is ignored).
 swimba_status decode_impl(bool mixed, const swimba_dims* dims, const void* u,
                           const void* w_router, const void* w_experts, const float* a,
                           const float* a_experts, float* h, void* y, int32_t* topk_idx, void* ws,
-                          size_t ws_bytes, hipStream_t stream) {
+                          size_t ws_bytes, hipStream_t stream, bool noalloc = false) {
   Dims d;
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
@@ -605,7 +639,17 @@ swimba_status decode_impl(bool mixed, const swimba_dims* dims, const void* u,
   REQUIRE_PTR(y);
   OPTIONAL_PTR(topk_idx);
   const DecWs lay = dec_ws(d);
-  if ((st = check_ws(ws, ws_bytes, lay.total)) != SWIMBA_OK) return st;
+  if (noalloc) {
+    if (lay.total > kScratchBytes)
+      return fail(SWIMBA_ERR_WORKSPACE,
+                  "decode_step_noalloc: these dims need %zu bytes of scratch; the static "
+                  "scratch holds %zu (use swimba_decode_step with a workspace)",
+                  lay.total, kScratchBytes);
+    if ((st = scratch_ptr(&ws)) != SWIMBA_OK) return st;
+    ws_bytes = kScratchBytes;
+  } else if ((st = check_ws(ws, ws_bytes, lay.total)) != SWIMBA_OK) {
+    return st;
+  }
   struct PrefixGuard {
     PrefixGuard() { g_prof_prefix = "decode_"; }
     ~PrefixGuard() { g_prof_prefix = ""; }
@@ -640,6 +684,14 @@ swimba_status swimba_decode_step(const swimba_dims* dims, const void* u, const v
                                  hipStream_t stream) {
   return decode_impl(false, dims, u, w_router, w_experts, a, nullptr, h, y, topk_idx, ws,
                      ws_bytes, stream);
+}
+
+swimba_status swimba_decode_step_noalloc(const swimba_dims* dims, const void* u,
+                                         const void* w_router, const void* w_experts,
+                                         const float* a, float* h, void* y, int32_t* topk_idx,
+                                         hipStream_t stream) {
+  return decode_impl(false, dims, u, w_router, w_experts, a, nullptr, h, y, topk_idx, nullptr, 0,
+                     stream, true);
 }
 
 swimba_status swimba_decode_step_mixed(const swimba_dims* dims, const void* u,
