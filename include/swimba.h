@@ -88,6 +88,13 @@ typedef enum swimba_call {
  *   headdim == 64; dstate in {16, 32, 64, 128}; d_model % 32 == 0;
  *   n_experts <= 256; top_k <= 8 (the prefill scan: top_k <= 2);
  *   chunk in {32, 64, 128, 256} for the scan.
+ * Sizes the kernels can address (else SWIMBA_ERR_DIMS, before any launch;
+ * 4 GiB here means 0xFFFFFFF0 bytes): u at most 4 GiB in every call that
+ * reads it; w_router and each expert's [W, D] weight matrix at most 4 GiB;
+ * in the scans, one sequence's B_hat and X_hat (T * k * G*N and T * k * H*P
+ * stream elements) and its intra-chunk Gram tiles at most 4 GiB (a longer
+ * sequence is scanned in pieces, the state handed on through h_final and
+ * h_init).
  */
 typedef struct swimba_dims {
   int32_t batch;      /* Bt: independent sequences */

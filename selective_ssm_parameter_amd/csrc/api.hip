@@ -84,6 +84,40 @@ swimba_status check_kernel_shape(const Dims& d) {
   return SWIMBA_OK;
 }
 
+// The kernels address HBM through buffer resources with 32-bit byte offsets
+// (records of at most 0xFFFFFFF0 bytes): the token rows of u, the router and
+// each expert's weight matrix as a whole, and the scan's streams of one
+// sequence. Larger tensors are rejected here instead of being read wrongly.
+constexpr int64_t kMaxRecord = 0xFFFFFFF0ll;
+
+swimba_status check_records(const Dims& d, bool router, bool experts) {
+  const int64_t ein = d.bf16 ? 2 : 4;  // u and weight elements
+  if (d.M * d.D * ein > kMaxRecord)
+    return fail(SWIMBA_ERR_DIMS, "u is %lld bytes; the kernels address at most 4 GiB of it",
+                (long long)(d.M * d.D * ein));
+  if (router && d.E * d.D * ein > kMaxRecord)
+    return fail(SWIMBA_ERR_DIMS, "w_router is larger than 4 GiB");
+  if (experts && d.W * d.D * ein > kMaxRecord)
+    return fail(SWIMBA_ERR_DIMS, "one expert's weights (%lld bytes) exceed 4 GiB",
+                (long long)(d.W * d.D * ein));
+  return SWIMBA_OK;
+}
+
+// Per sequence, the scan addresses B_hat, X_hat, C_mix and its Gram tiles
+// with 32-bit byte offsets.
+swimba_status check_scan_records(const Dims& d) {
+  const int64_t es = (int64_t)d.esize;
+  const int64_t nc = (d.T + d.L - 1) / d.L;
+  const int64_t nb = (d.L + 31) / 32;
+  const int64_t gram = nc * d.G * (nb * (nb + 1) / 2) * 32 * (32 * d.k) * es;
+  if (d.T * d.k * d.HP * es > kMaxRecord || d.T * d.k * d.GN * es > kMaxRecord || gram > kMaxRecord)
+    return fail(SWIMBA_ERR_DIMS,
+                "one sequence's X_hat (%lld bytes) or Gram tiles (%lld bytes) exceed 4 GiB; "
+                "split the sequence and pass the state on (h_final -> h_init)",
+                (long long)(d.T * d.k * d.HP * es), (long long)gram);
+  return SWIMBA_OK;
+}
+
 swimba_status check_scan_shape(const Dims& d) {
   if (d.k > 2) return fail(SWIMBA_ERR_UNSUPPORTED, "the prefill scan supports top_k <= 2");
   if (d.L != 32 && d.L != 64 && d.L != 128 && d.L != 256)
@@ -313,6 +347,7 @@ swimba_status swimba_route_topk(const swimba_dims* dims, const void* u, const vo
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
   if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_records(d, true, false)) != SWIMBA_OK) return st;
   if (d.M == 0) return SWIMBA_OK;
   REQUIRE_PTR(u);
   REQUIRE_PTR(w_router);
@@ -333,6 +368,7 @@ swimba_status swimba_expert_project_mix(const swimba_dims* dims, const void* u,
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
   if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_records(d, false, true)) != SWIMBA_OK) return st;
   if (d.M == 0) return SWIMBA_OK;
   REQUIRE_PTR(u);
   REQUIRE_PTR(w_experts);
@@ -365,6 +401,7 @@ swimba_status pbwd_impl(bool saved, const swimba_dims* dims, const void* u, cons
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
   if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_records(d, true, true)) != SWIMBA_OK) return st;
   // the backward GEMMs address an expert's pair rows with 32-bit byte offsets
   if (d.M * d.k * d.D * (int64_t)d.esize >= (int64_t(1) << 31) ||
       d.M * d.k * d.W * (int64_t)d.esize >= (int64_t(1) << 31))
@@ -480,6 +517,7 @@ swimba_status scan_impl(bool mixed, const swimba_dims* dims, const void* B_hat,
   if (st != SWIMBA_OK) return st;
   if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
   if ((st = check_scan_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_scan_records(d)) != SWIMBA_OK) return st;
   if (d.Bt == 0) return SWIMBA_OK;
   if (mixed) {
     if (d.T > 0) REQUIRE_PTR(log_decay);
@@ -626,6 +664,7 @@ swimba_status decode_impl(bool mixed, const swimba_dims* dims, const void* u,
   if (st != SWIMBA_OK) return st;
   if (d.T != 1) return fail(SWIMBA_ERR_DIMS, "decode_step needs seqlen == 1");
   if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_records(d, true, true)) != SWIMBA_OK) return st;
   if (d.Bt == 0) return SWIMBA_OK;
   REQUIRE_PTR(u);
   REQUIRE_PTR(w_router);

@@ -54,8 +54,10 @@ constexpr int kGradWaves = 8;  // waves of the gradient kernel
 // The local chunk states S_c and R_c go to HBM in the operand type (fp16 for
 // bf16 problems), each (chunk, head) tile scaled by the power of two that
 // brings its largest magnitude into [1/2, 1); the sweep restores them and
-// sums in fp32, and writes H_c and F_c in fp32 (their rounding would be
-// amplified by the cancellation in the gradients' sums).
+// sums in fp32, and writes H_c and F_c in the same type: for bf16 problems
+// fp16 rows of P elements, each row with its own power-of-two factor (the
+// gradient kernel rounds them to fp16 tiles under a power-of-two scale
+// anyway); fp32 for fp32 problems.
 
 struct BwdArgs {
   const void* B_hat;    // [M, k, G, N] stream type
@@ -820,9 +822,10 @@ int scan_bwd_slices(bool is_bf16, int Bt, int T, int H, int G) {
   return HG;
 }
 
-// Workspace: H_c and F_c (fp32), the local states S_c and R_c (operand type)
-// with their per-(chunk, head) factors, da's parts, and the head slices'
-// dB_hat / dC~ parts.
+// Workspace: H_c and F_c in the local-state type (fp16 rows for bf16 problems)
+// with one fp32 factor per row of P elements (Hu, Fu), the local states S_c
+// and R_c (same type) with their per-(chunk, head) factors, da's parts, and
+// the head slices' dB_hat / dC~ parts.
 struct BwdWs {
   size_t H, F, Hu, Fu, Sl, Rl, Su, Ru, dap, parts, total;
 };
@@ -922,8 +925,9 @@ hipError_t launch_scan_backward(bool is_bf16, int Bt, int T, int H, int G, int N
                                 const float* dh_final, float* dB, float* dX, float* dC, float* da,
                                 float* dh_init, void* ws, hipStream_t s) {
   if (Bt == 0) {
-    if (H > 0) hipLaunchKernelGGL(bwd_empty_kernel, dim3(1), dim3(256), 0, s, nullptr, nullptr,
-                                  da, (size_t)0, H);
+    if (H > 0)
+      hipLaunchKernelGGL(bwd_empty_kernel, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, s,
+                         nullptr, nullptr, da, (size_t)0, H);
     return hipGetLastError();
   }
   if (T == 0) {

@@ -101,6 +101,35 @@ def test_unsupported_shapes():
     assert "chunk" in L.swimba_last_error().decode()
 
 
+def test_sizes_beyond_32bit_offsets():
+    # tensors the kernels would address past their 4 GiB buffer records are
+    # rejected before any launch (the pointers are never touched)
+    L = lib()
+    big_u = good_dims(batch=1, seqlen=1 << 21, d_model=1024)      # u: 4 GiB of bf16
+    assert call_route(big_u) == -2
+    assert "u is" in L.swimba_last_error().decode()
+    st = L.swimba_expert_project_mix(ctypes.byref(big_u), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 1 << 40, None)
+    assert st == -2
+    # one expert's weights: W = 64*64 + 2*128 rows of d_model 2^18 fp32 values (4.6 GB)
+    big_w = good_dims(batch=1, seqlen=4, nheads=64, dstate=128, d_model=1 << 18, dtype="f32")
+    st = L.swimba_expert_project_mix(ctypes.byref(big_w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 1 << 40, None)
+    assert st == -2 and "expert" in L.swimba_last_error().decode()
+    dd = good_dims(batch=2, seqlen=1, nheads=64, dstate=128, d_model=1 << 18, dtype="f32")
+    st = L.swimba_decode_step(ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                              1 << 40, None)
+    assert st == -2
+    # one sequence of X_hat: 2^20 tokens x 2 slots x 32 heads x 64 fp16 = 8 GiB
+    long_seq = good_dims(batch=1, seqlen=1 << 20, nheads=32, dstate=128, chunk=256)
+    st = L.swimba_ssd_chunk_scan(ctypes.byref(long_seq), FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                 FAKE, 1 << 40, None)
+    assert st == -2 and "h_final -> h_init" in L.swimba_last_error().decode()
+    # the same tokens over 4 sequences fit
+    ok_seq = good_dims(batch=4, seqlen=1 << 18, nheads=32, dstate=128, chunk=256)
+    assert sb.swimba_workspace_size(ok_seq, sb.CALL_SCAN) > 0
+
+
 def test_null_and_misaligned_pointers():
     lib()
     assert call_route(good_dims(), u=None) == -1

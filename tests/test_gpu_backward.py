@@ -130,6 +130,19 @@ def test_scan_backward_empty_sequence():
     assert np.all(host(da) == 0)
 
 
+def test_scan_backward_no_sequences_many_heads():
+    # batch 0 with more heads than one 256-thread block covers: every da[h]
+    # is written (zero), none is left as it was
+    wl = W("b11", 811, batch=0, seqlen=100, nheads=300)
+    dims = sb.dims_of(wl)
+    da = torch.full((300,), 7.0, device="cuda")
+    a = dev(np.full(300, 0.9), torch.float32)
+    sb.swimba_ssd_chunk_scan_backward(dims, None, None, None, a, None, None, None, None, None, None,
+                                      da, None, None)
+    torch.cuda.synchronize()
+    assert np.all(host(da) == 0)
+
+
 GRADED = [
     # (name, workload): the small shape takes the four-element sweep, the
     # second has enough states (Bt H N P / 8 >= 131072) for the 8-element one
