@@ -86,7 +86,8 @@ typedef enum swimba_call {
  *   n_experts >= 1, 1 <= top_k <= n_experts, chunk >= 1, dtype in swimba_dtype.
  * Shapes with a kernel (else SWIMBA_ERR_UNSUPPORTED):
  *   headdim == 64; dstate in {16, 32, 64, 128}; d_model % 32 == 0;
- *   n_experts <= 256; top_k <= 8 (the prefill scan: top_k <= 2);
+ *   n_experts <= 256; top_k <= 8 (the prefill scans: top_k <= 4 for bf16,
+ *   <= 2 for fp32; the scan backward: top_k <= 2);
  *   chunk in {32, 64, 128, 256} for the scan.
  * Sizes the kernels can address (else SWIMBA_ERR_DIMS, before any launch;
  * 4 GiB here means 0xFFFFFFF0 bytes): u at most 4 GiB in every call that
@@ -319,7 +320,7 @@ swimba_status swimba_decode_step_mixed(const swimba_dims* dims, const void* u,
  *   dC_mix    [M, G, N] float32 out;  da [H] float32 out
  *   dh_init   [Bt, H, N, P] float32 out, or NULL
  *   ws        workspace of swimba_workspace_size(dims, SWIMBA_CALL_SCAN_BACKWARD)
- * Shapes and errors as for swimba_ssd_chunk_scan (top_k <= 2).
+ * Shapes and errors as for swimba_ssd_chunk_scan, with top_k <= 2.
  */
 swimba_status swimba_ssd_chunk_scan_backward(const swimba_dims* dims, const void* B_hat,
                                              const void* X_hat, const void* C_mix,

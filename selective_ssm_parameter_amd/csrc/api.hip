@@ -118,8 +118,11 @@ swimba_status check_scan_records(const Dims& d) {
   return SWIMBA_OK;
 }
 
-swimba_status check_scan_shape(const Dims& d) {
-  if (d.k > 2) return fail(SWIMBA_ERR_UNSUPPORTED, "the prefill scan supports top_k <= 2");
+// kmax: the scans take top_k <= 4, the scan backward top_k <= 2.
+swimba_status check_scan_shape(const Dims& d, int kmax = 4) {
+  if (!d.bf16 && kmax > 2) kmax = 2;  // fp32 streams: two LDS stages fit for k <= 2 only
+  if (d.k > kmax)
+    return fail(SWIMBA_ERR_UNSUPPORTED, "this scan supports top_k <= %d for this dtype", kmax);
   if (d.L != 32 && d.L != 64 && d.L != 128 && d.L != 256)
     return fail(SWIMBA_ERR_UNSUPPORTED, "chunk must be 32, 64, 128 or 256");
   return SWIMBA_OK;
@@ -576,7 +579,7 @@ swimba_status swimba_ssd_chunk_scan_backward(const swimba_dims* dims, const void
   swimba_status st = read_dims(dims, d);
   if (st != SWIMBA_OK) return st;
   if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
-  if ((st = check_scan_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_scan_shape(d, 2)) != SWIMBA_OK) return st;
   if (d.M * d.HP * 4 >= (int64_t(1) << 40)) return fail(SWIMBA_ERR_DIMS, "problem too large");
   REQUIRE_PTR(da);
   REQUIRE_PTR(a);

@@ -180,7 +180,8 @@ __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_
 //   (send = last token of block sig), readout 2^{Lam_t}, carry to the chunk
 //   end 2^{Lam_end - Lam_send} * 2^{Lam_send - Lam_s}, H <- 2^{Lam_end} H.
 template <typename T, typename TY, int NP, int KS, int BT, bool WITH_Y, bool TV = false>
-__global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 ? 2 : 1) void scan_kernel(ScanArgs A) {
+// Two workgroups per CU where their LDS fits (2-byte streams, k <= 2).
+__global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 && KS <= 2 ? 2 : 1) void scan_kernel(ScanArgs A) {
   typedef ScanLds<T, NP, KS, BT, WITH_Y, TV> Lay;
   constexpr int R = Lay::R;
   constexpr int TT = BT / 16, RQ = R / 32, NT = NP / 16, NQ = NP / 32;
@@ -792,6 +793,11 @@ static hipError_t dispatch_bt(const ScanGeom& g, const ScanArgs& a, hipStream_t 
 template <typename T, typename TY, int NP>
 static hipError_t dispatch_ks(const ScanGeom& g, const ScanArgs& a, hipStream_t s) {
   if (g.k == 1) return dispatch_bt<T, TY, NP, 1>(g, a, s);
+  if constexpr (sizeof(T) == 2) {
+    // 2-byte streams: k = 3 and 4 fit two stages in LDS (fp32 ones do not)
+    if (g.k == 3) return dispatch_bt<T, TY, NP, 3>(g, a, s);
+    if (g.k == 4) return dispatch_bt<T, TY, NP, 4>(g, a, s);
+  }
   return dispatch_bt<T, TY, NP, 2>(g, a, s);
 }
 

@@ -92,9 +92,10 @@ def test_unsupported_shapes():
     assert call_route(good_dims(dstate=48)) == -3
     assert call_route(good_dims(d_model=100)) == -3
     assert call_route(good_dims(n_experts=300, top_k=2)) == -3
-    # the scan: top_k > 2 and odd chunk sizes
+    # the scan: top_k > 4 (> 2 for fp32) and odd chunk sizes
     L = sb.lib()
-    for d in (good_dims(n_experts=4, top_k=3), good_dims(chunk=48)):
+    for d in (good_dims(n_experts=8, top_k=5), good_dims(n_experts=4, top_k=3, dtype="f32"),
+              good_dims(chunk=48)):
         st = L.swimba_ssd_chunk_scan(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
                                      None, 0, None)
         assert st == -3
@@ -186,7 +187,7 @@ def test_mixed_decay_argument_checks():
     st = L.swimba_ssd_chunk_scan_mixed(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None,
                                        None, 0, None)
     assert st == -1 and "log_decay is NULL" in L.swimba_last_error().decode()
-    st = L.swimba_ssd_chunk_scan_mixed(ctypes.byref(good_dims(top_k=3)), FAKE, FAKE, FAKE, FAKE,
+    st = L.swimba_ssd_chunk_scan_mixed(ctypes.byref(good_dims(top_k=5, n_experts=8)), FAKE, FAKE, FAKE, FAKE,
                                        None, FAKE, None, None, 0, None)
     assert st == -3
     need = sb.swimba_workspace_size(d, sb.CALL_SCAN)

@@ -185,6 +185,7 @@ E2E_CASES = [
     ("c1", synth.WORKLOADS["c1"]),
     ("bf16_small", W("y1", 731, seqlen=520, batch=2)),
     ("bf16_g2_k1", W("y2", 732, top_k=1, nheads=4, ngroups=2, dstate=64, seqlen=260)),
+    ("bf16_e16_k4", W("y3", 733, top_k=4, n_experts=16, seqlen=230, chunk=128)),
 ]
 
 

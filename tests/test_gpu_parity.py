@@ -175,6 +175,13 @@ SCAN_CASES = [
     ("f32_k2_n128", W("s9", 309, dtype=synth.F32, seqlen=190), True),
     ("f32_k1_n64_L64", W("s10", 310, dtype=synth.F32, top_k=1, dstate=64, chunk=64, seqlen=100), False),
     ("bf16_many_segments", W("s11", 311, batch=1, nheads=2, seqlen=4000, chunk=64), True),
+    # top-k 3 and 4: 96 and 128 (token, slot) pairs per 32-token block
+    ("bf16_k3_L64_ragged", W("s15", 315, top_k=3, seqlen=301), True),
+    ("bf16_k3_n64_L128", W("s16", 316, top_k=3, dstate=64, chunk=128, seqlen=290), True),
+    ("bf16_k4_L128", W("s17", 317, top_k=4, chunk=128, seqlen=333), True),
+    ("bf16_k4_n32_L32_g2", W("s18", 318, top_k=4, dstate=32, chunk=32, ngroups=2, seqlen=150), True),
+    ("bf16_k4_L256_segments", W("s19", 319, top_k=4, chunk=256, batch=1, nheads=2, seqlen=3000), True),
+    ("bf16_k4_n16_short", W("s20", 320, top_k=4, dstate=16, seqlen=7, batch=3), False),
 ]
 
 
@@ -276,6 +283,8 @@ E2E_CASES = [
     ("c1", synth.WORKLOADS["c1"]),
     ("bf16_small", W("e1", 401, seqlen=520, batch=2)),
     ("bf16_g2_k1", W("e2", 402, top_k=1, nheads=4, ngroups=2, dstate=64, seqlen=260)),
+    ("bf16_e16_k3", W("e5", 405, top_k=3, n_experts=16, seqlen=300, chunk=128)),
+    ("bf16_e32_k4", W("e6", 406, top_k=4, n_experts=32, seqlen=270, batch=2)),
 ]
 
 
