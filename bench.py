@@ -73,6 +73,8 @@ KERNEL_NAMES = [
     (r"scan_combine_kernel", "scan_state_pass"),
     (r"scan_kernel.*Li\d+ELb1ELb[01]E", "scan_chunk_output"),
     (r"state_copy_kernel", "state_copy"),
+    (r"sep_scatter_kernel", "sep_scatter"),
+    (r"sep_sum_kernel", "sep_sum"),
     (r"decode_state_kernel", "decode_state"),
     (r"copyBuffer", "copy (runtime blit)"),
 ]
@@ -501,6 +503,96 @@ def e_sweep(args):
         open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+SEP_POINTS = [(2, 2), (4, 2), (8, 2), (16, 2), (32, 2), (8, 1), (8, 4)]
+
+
+def separated_sweep(args):
+    """Prefill tokens/s of the MoE over separated SSMs (one state trajectory
+    per expert) beside Swimba's single trajectory, at the c2 dimensions
+    (batch 8 x 2048 tokens, d_model 768, 24 heads, chunk 64) for each
+    (E, k) in SEP_POINTS (seed 40 + E + 100 k). One JSON line per point and a
+    markdown table: the separated layer's cost grows with E (its E
+    trajectories are all scanned), Swimba's does not."""
+    import torch
+
+    from selective_ssm_parameter_amd import binding as sb
+    from selective_ssm_parameter_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    rows = []
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        sb.profile_select(None)
+        sb.profile_enable(True)
+        fn()
+        torch.cuda.synchronize()
+        rep = json.loads(sb.profile_report())
+        sb.profile_enable(False)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps, {n: 1e3 * r["ms"] / r["launches"]
+                                                    for n, r in rep.items()}
+
+    for E, k in SEP_POINTS:
+        wl = synth.WORKLOADS["c2"].replace(name=f"c2_E{E}_k{k}", seed=40 + E + 100 * k,
+                                           n_experts=E, top_k=k)
+        inp = synth.make_inputs(wl)
+
+        def up(x, t=torch.bfloat16):
+            return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev, t)
+
+        u = up(inp["u"].reshape(wl.tokens, -1))
+        wr, we, a = up(inp["w_router"]), up(inp["w_experts"]), up(inp["a"], torch.float32)
+        del inp
+        dims = sb.dims_of(wl)
+        buf = sb.alloc_buffers(dims, dev)
+        sbuf = sb.alloc_separated(dims, dev)
+        t_mix, k_mix = timed(lambda: sb.forward(dims, u, wr, we, a, None, buf), args.steps,
+                             args.warmup)
+        t_sep, k_sep = timed(lambda: sb.separated_forward(dims, u, wr, we, a, None, sbuf),
+                             args.steps, args.warmup)
+        row = {"E": E, "k": k, "swimba_tokens_per_s": wl.tokens / t_mix,
+               "separated_tokens_per_s": wl.tokens / t_sep, "swimba_ms": 1e3 * t_mix,
+               "separated_ms": 1e3 * t_sep, "swimba_kernels_us": k_mix,
+               "separated_kernels_us": k_sep,
+               "state_MB": {"swimba": wl.batch * wl.nheads * wl.dstate * wl.headdim * 4 / 1e6,
+                            "separated": E * wl.batch * wl.nheads * wl.dstate * wl.headdim
+                            * 4 / 1e6}}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del u, wr, we, a, buf, sbuf
+        torch.cuda.empty_cache()
+    if args.out:
+        lines = ["# Separated-SSM MoE against Swimba: prefill tokens/s against E and k "
+                 "(c2 dimensions)", "",
+                 "Command (from the repository root, after building the library):", "",
+                 "    " + (" ".join(args.command) or "python bench.py --separated"), "",
+                 "Batch 8 x T 2048 tokens, d_model 768, 24 heads, P 64, N 128, chunk 64, bf16; "
+                 "seed 40 + E + 100 k. Swimba: one state trajectory per head (route, project + "
+                 "mix, scan). Separated: one trajectory per expert and head (route, the same "
+                 "projection of the selected pairs, per-expert streams, Bt x E scans of k = 1, "
+                 f"the sum over experts). {args.steps} timed steps after {args.warmup} warm-up "
+                 "steps each; per-kernel times from HIP events in one extra pass.", "",
+                 "| E | k | Swimba tokens/s (M) | separated tokens/s (M) | separated / Swimba "
+                 "time | Swimba scan us | separated scan us | state MB (Swimba / separated) |",
+                 "|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        scan = ("scan_gram", "scan_segment_state", "scan_state_pass", "scan_chunk_output")
+        for r in rows:
+            sm = sum(r["swimba_kernels_us"].get(n, 0) for n in scan)
+            ss = sum(r["separated_kernels_us"].get(n, 0) for n in scan)
+            lines.append(f"| {r['E']} | {r['k']} | {r['swimba_tokens_per_s'] / 1e6:.2f} | "
+                         f"{r['separated_tokens_per_s'] / 1e6:.2f} | "
+                         f"{r['separated_ms'] / r['swimba_ms']:.2f} | {sm:.1f} | {ss:.1f} | "
+                         f"{r['state_MB']['swimba']:.0f} / {r['state_MB']['separated']:.0f} |")
+        open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def output_projection(args):
     """The output projection after the recurrence on every token of the
     workload (out = W_out y, [M, H*P] -> [M, D]): one JSON line with its
@@ -793,6 +885,9 @@ def main():
                     help="time the output projection alone on the --config workload")
     ap.add_argument("--e-sweep", action="store_true",
                     help="prefill tokens/s at the c3 dimensions for E in 4..64 (k = 2)")
+    ap.add_argument("--separated", action="store_true",
+                    help="tokens/s of the MoE over separated SSMs beside Swimba's, at the c2 "
+                         "dimensions for several E and k")
     ap.add_argument("--bench-json", help="the JSON output of the profiled bench run")
     ap.add_argument("--command", action="append", default=[],
                     help="the command(s) that produced the profile, for the summary")
@@ -815,6 +910,9 @@ def main():
         sys.exit(2)
     if args.e_sweep:
         e_sweep(args)
+        return
+    if args.separated:
+        separated_sweep(args)
         return
     if args.output_projection:
         output_projection(args)

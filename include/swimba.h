@@ -76,7 +76,8 @@ typedef enum swimba_call {
   SWIMBA_CALL_DECODE = 3,
   SWIMBA_CALL_SCAN_BACKWARD = 4,
   SWIMBA_CALL_PROJECT_BACKWARD = 5,
-  SWIMBA_CALL_PROJECT_BACKWARD_SAVED = 6
+  SWIMBA_CALL_PROJECT_BACKWARD_SAVED = 6,
+  SWIMBA_CALL_SEPARATED = 7
 } swimba_call;
 
 /*
@@ -386,6 +387,36 @@ swimba_status swimba_expert_project_mix_backward_saved(
     const void* fwd_ws, size_t fwd_ws_bytes, const float* dB_hat, const float* dX_hat,
     const float* dC_mix, float* du, float* dW_router, float* dW_experts, void* ws,
     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * MoE over separated SSMs, the design Swimba is compared against
+ * (papernotes.org notes, research background and motivation: one state
+ * trajectory per expert, each expert's recursion advanced at every step, so
+ * state memory and recurrence work grow with E; Method, key design 2,
+ * Theorem 3.4: the output is the routing-weighted sum of the experts'
+ * readouts of their own states). With the same router and expert
+ * projections as the Swimba calls, for every expert e and head h:
+ *   h^(e)_t = a_h h^(e)_{t-1} + [e in K_t] B^(e)_t X^(e)_t^T     (N x P, fp32)
+ *   y_t     = sum_{e in K_t} pi_{t,e} C^(e)_t^T h^(e)_t
+ * (an unselected expert injects nothing; its state still decays). Solved as
+ * Bt * E chunked scans of k = 1 over per-expert streams (zeros where the
+ * expert is not selected) in the workspace, whose fp32 outputs are summed
+ * over the experts in order.
+ *   u, w_router, w_experts   as for swimba_route_topk / swimba_expert_project_mix
+ *   a         [H] float32
+ *   h_init    [Bt, E, H, N, P] float32, or NULL for zeros
+ *   y         [M, H, P] dtype out
+ *   h_final   [Bt, E, H, N, P] float32 out, or NULL (may alias h_init)
+ *   topk_idx  [M, k] int32 out, or NULL
+ *   ws        workspace of swimba_workspace_size(dims, SWIMBA_CALL_SEPARATED)
+ * Shapes and errors as for the Swimba calls; the per-expert scans take
+ * dims.chunk, and the size limits of the scan apply to each trajectory.
+ */
+swimba_status swimba_separated_forward(const swimba_dims* dims, const void* u,
+                                       const void* w_router, const void* w_experts,
+                                       const float* a, const float* h_init, void* y,
+                                       float* h_final, int32_t* topk_idx, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
 
 /*
  * Per-kernel timing with HIP events, for measurement only. While enabled,

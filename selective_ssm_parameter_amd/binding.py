@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libswimba.so")
 
 F32, BF16 = 0, 1
 (CALL_ROUTE, CALL_PROJECT, CALL_SCAN, CALL_DECODE, CALL_SCAN_BACKWARD, CALL_PROJECT_BACKWARD,
- CALL_PROJECT_BACKWARD_SAVED) = (0, 1, 2, 3, 4, 5, 6)
+ CALL_PROJECT_BACKWARD_SAVED, CALL_SEPARATED) = (0, 1, 2, 3, 4, 5, 6, 7)
 
 STATUS = {
     0: "SWIMBA_OK", -1: "SWIMBA_ERR_NULL", -2: "SWIMBA_ERR_DIMS", -3: "SWIMBA_ERR_UNSUPPORTED",
@@ -32,6 +32,7 @@ EXPORTS = (
     "swimba_profile_select", "swimba_mix_decay", "swimba_ssd_chunk_scan_mixed",
     "swimba_decode_step_mixed", "swimba_decode_step_noalloc", "swimba_ssd_chunk_scan_backward",
     "swimba_expert_project_mix_backward", "swimba_expert_project_mix_backward_saved",
+    "swimba_separated_forward",
 )
 
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.swimba_expert_project_mix_backward_saved.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P, P,
                                                            P, P, P, P, P, SZ, S]
     L.swimba_expert_project_mix_backward_saved.restype = I32
+    L.swimba_separated_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, SZ, S]
+    L.swimba_separated_forward.restype = I32
     L.swimba_profile_enable.restype = I32
     L.swimba_profile_enable.argtypes = [I32]
     L.swimba_profile_report.restype = I32
@@ -198,6 +201,14 @@ def swimba_decode_step_noalloc(dims, u, w_router, w_experts, a, h, y, topk_idx, 
     _check(lib().swimba_decode_step_noalloc(
         ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(a), _ptr(h), _ptr(y),
         _ptr(topk_idx), _stream(stream)))
+
+
+def swimba_separated_forward(dims, u, w_router, w_experts, a, h_init, y, h_final, topk_idx, ws,
+                             ws_bytes=None, stream=None):
+    nb = (ws.numel() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check(lib().swimba_separated_forward(
+        ctypes.byref(dims), _ptr(u), _ptr(w_router), _ptr(w_experts), _ptr(a), _ptr(h_init),
+        _ptr(y), _ptr(h_final), _ptr(topk_idx), _ptr(ws), nb, _stream(stream)))
 
 
 def swimba_mix_decay(dims, topk_idx, topk_w, a_experts, log_decay, stream=None):
@@ -399,3 +410,33 @@ def backward(dims: Dims, u, w_router, w_experts, a, h_init, dy, dh_final, fwd: B
                                            g.dC_mix, g.du, g.dW_router, g.dW_experts,
                                            g.ws_project, stream=stream)
     return g
+
+
+@dataclasses.dataclass
+class SeparatedBuffers:
+    topk_idx: torch.Tensor
+    y: torch.Tensor
+    h_final: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc_separated(dims: Dims, device="cuda") -> SeparatedBuffers:
+    """Outputs and workspace of one separated-SSM forward, allocated by torch."""
+    M = dims.batch * dims.seqlen
+    H, P, N, E = dims.nheads, dims.headdim, dims.dstate, dims.n_experts
+    ws, _ = workspace(dims, CALL_SEPARATED, device)
+    return SeparatedBuffers(
+        topk_idx=torch.empty(M, dims.top_k, dtype=torch.int32, device=device),
+        y=torch.empty(M, H, P, dtype=torch_dtype(dims), device=device),
+        h_final=torch.empty(dims.batch, E, H, N, P, dtype=torch.float32, device=device),
+        ws=ws)
+
+
+def separated_forward(dims: Dims, u, w_router, w_experts, a, h_init=None,
+                      buf: SeparatedBuffers | None = None, stream=None) -> SeparatedBuffers:
+    """The MoE over separated SSMs (one trajectory per expert), on the current stream."""
+    if buf is None:
+        buf = alloc_separated(dims, u.device)
+    swimba_separated_forward(dims, u, w_router, w_experts, a, h_init, buf.y, buf.h_final,
+                             buf.topk_idx, buf.ws, stream=stream)
+    return buf

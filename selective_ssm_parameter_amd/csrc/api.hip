@@ -206,6 +206,41 @@ PbwdWs pbwd_ws(const Dims& d, bool saved = false) {
   return w;
 }
 
+// Separated-SSM MoE: the routing, the projection of the selected pairs, the
+// per-expert dense streams of the Bt * E trajectories, their fp32 outputs and
+// the scan's own workspace for them.
+Dims sep_dims(const Dims& d) {
+  Dims s = d;
+  s.Bt = d.Bt * d.E;
+  s.k = 1;
+  s.M = s.Bt * d.T;
+  return s;
+}
+
+size_t scan_bytes(const Dims& d);
+
+struct SepWs {
+  size_t idx, w, proj, xhat, bhat, xs, bs, cs, yp, scan, total;
+};
+
+SepWs sep_ws(const Dims& d) {
+  SepWs w{};
+  size_t off = 0;
+  const int64_t pairs = d.M * d.k, rows = d.Bt * d.E * d.T;
+  w.idx = off; off += align256(sizeof(int32_t) * pairs);
+  w.w = off; off += align256(sizeof(float) * pairs);
+  w.proj = off; off += proj_ws(d).total;
+  w.xhat = off; off += align256(d.esize * pairs * d.HP);
+  w.bhat = off; off += align256(d.esize * pairs * d.GN);
+  w.xs = off; off += align256(d.esize * rows * d.HP);
+  w.bs = off; off += align256(d.esize * rows * d.GN);
+  w.cs = off; off += align256(d.esize * rows * d.GN);
+  w.yp = off; off += align256(sizeof(float) * rows * d.HP);
+  w.scan = off; off += scan_bytes(sep_dims(d));
+  w.total = off;
+  return w;
+}
+
 size_t scan_bytes(const Dims& d) {
   return scan_ws_bytes(scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
                                  (int)d.k, (int)d.L, (int)d.esize));
@@ -229,8 +264,9 @@ swimba_status check_ws(void* ws, size_t have, size_t need) {
     if ((p) && !aligned16(p)) return fail(SWIMBA_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
   } while (0)
 
-ProjGeom proj_geom(const Dims& d, int64_t M) {
+ProjGeom proj_geom(const Dims& d, int64_t M, bool bw_one = false) {
   ProjGeom g;
+  g.bw_one = bw_one ? 1 : 0;
   g.M = (int)M; g.D = (int)d.D; g.H = (int)d.H; g.P = (int)d.P; g.G = (int)d.G; g.N = (int)d.N;
   g.E = (int)d.E; g.k = (int)d.k; g.W = (int)d.W;
   return g;
@@ -241,7 +277,7 @@ ProjGeom proj_geom(const Dims& d, int64_t M) {
 // expert histograms of its workgroups' tokens into the workspace.
 hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_experts,
                        const int32_t* idx, const float* w, void* B_hat, void* X_hat, void* C_mix,
-                       unsigned char* ws, hipStream_t s, bool routed = false) {
+                       unsigned char* ws, hipStream_t s, bool routed = false, bool bw_one = false) {
   Dims dm = d;
   dm.M = M;
   const ProjWs lay = proj_ws(dm);
@@ -259,8 +295,8 @@ hipError_t run_project(const Dims& d, int64_t M, const void* u, const void* w_ex
                                tiles, sorted, sortw, X_hat, (int)d.HP, B_hat, (int)d.GN, cpart, s,
                                routed ? (int)(route_tokens_per_wg(M) * d.k) : 0, routed);
   if (e != hipSuccess) return e;
-  return launch_project(d.bf16, proj_geom(d, M), u, w_experts, sorted, sortw, tiles, bm, B_hat,
-                        X_hat, cpart, C_mix, s);
+  return launch_project(d.bf16, proj_geom(d, M, bw_one), u, w_experts, sorted, sortw, tiles, bm,
+                        B_hat, X_hat, cpart, C_mix, s);
 }
 
 // ---------------------------------------------------------------- profiling
@@ -339,6 +375,7 @@ size_t swimba_workspace_size(const swimba_dims* dims, int32_t call) {
       return d.M == 0 ? 0 : scan_bwd_ws_bytes(d.bf16, (int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.k);
     case SWIMBA_CALL_PROJECT_BACKWARD: return d.M == 0 ? 0 : pbwd_ws(d).total;
     case SWIMBA_CALL_PROJECT_BACKWARD_SAVED: return d.M == 0 ? 0 : pbwd_ws(d, true).total;
+    case SWIMBA_CALL_SEPARATED: return d.M == 0 ? 0 : sep_ws(d).total;
     default: return 0;
   }
 }
@@ -743,6 +780,62 @@ swimba_status swimba_decode_step_mixed(const swimba_dims* dims, const void* u,
                                        hipStream_t stream) {
   return decode_impl(true, dims, u, w_router, w_experts, nullptr, a_experts, h, y, topk_idx, ws,
                      ws_bytes, stream);
+}
+
+swimba_status swimba_separated_forward(const swimba_dims* dims, const void* u,
+                                       const void* w_router, const void* w_experts,
+                                       const float* a, const float* h_init, void* y,
+                                       float* h_final, int32_t* topk_idx, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  Dims d;
+  swimba_status st = read_dims(dims, d);
+  if (st != SWIMBA_OK) return st;
+  if ((st = check_kernel_shape(d)) != SWIMBA_OK) return st;
+  if ((st = check_records(d, true, true)) != SWIMBA_OK) return st;
+  const Dims ds = sep_dims(d);
+  if (ds.Bt > INT32_MAX || ds.M * d.HP >= (int64_t(1) << 40))
+    return fail(SWIMBA_ERR_DIMS, "batch * n_experts trajectories too large");
+  if ((st = check_scan_shape(ds)) != SWIMBA_OK) return st;
+  if ((st = check_scan_records(ds)) != SWIMBA_OK) return st;
+  if (d.Bt == 0) return SWIMBA_OK;
+  REQUIRE_PTR(a);
+  OPTIONAL_PTR(h_init);
+  OPTIONAL_PTR(h_final);
+  const ScanGeom g = scan_geom((int)ds.Bt, (int)ds.T, (int)ds.H, (int)ds.G, (int)ds.N, (int)ds.P,
+                               1, (int)ds.L, (int)ds.esize);
+  if (d.M == 0)  // no tokens: the states pass through unchanged
+    return hip_status(launch_scan(d.bf16, g, nullptr, nullptr, nullptr, a, h_init, nullptr,
+                                  h_final, nullptr, stream),
+                      "separated_forward launch");
+  REQUIRE_PTR(u);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(w_experts);
+  REQUIRE_PTR(y);
+  OPTIONAL_PTR(topk_idx);
+  const SepWs lay = sep_ws(d);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != SWIMBA_OK) return st;
+  unsigned char* w8 = static_cast<unsigned char*>(ws);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w8 + lay.idx);
+  float* tw = reinterpret_cast<float*>(w8 + lay.w);
+  hipError_t e = launch_route(d.bf16, u, w_router, (int)d.M, (int)d.D, (int)d.E, (int)d.k, idx,
+                              tw, nullptr, stream);
+  if (e != hipSuccess) return hip_status(e, "separated_forward route launch");
+  // the selected pairs' X, B (unweighted) and pi * C parts
+  e = run_project(d, d.M, u, w_experts, idx, tw, w8 + lay.bhat, w8 + lay.xhat, nullptr,
+                  w8 + lay.proj, stream, false, true);
+  if (e != hipSuccess) return hip_status(e, "separated_forward projection launch");
+  const ProjWs play = proj_ws(d);
+  e = launch_sep_scatter(d.bf16, idx, w8 + lay.xhat, w8 + lay.bhat,
+                         reinterpret_cast<const float*>(w8 + lay.proj + play.cpart), (int)d.Bt,
+                         (int)d.T, (int)d.E, (int)d.k, (int)d.HP, (int)d.GN, w8 + lay.xs,
+                         w8 + lay.bs, w8 + lay.cs, stream);
+  if (e != hipSuccess) return hip_status(e, "separated_forward scatter launch");
+  float* yp = reinterpret_cast<float*>(w8 + lay.yp);
+  e = launch_scan(d.bf16, g, w8 + lay.bs, w8 + lay.xs, w8 + lay.cs, a, h_init, yp, h_final,
+                  reinterpret_cast<float*>(w8 + lay.scan), stream, nullptr, true);
+  if (e != hipSuccess) return hip_status(e, "separated_forward scan launch");
+  return hip_status(launch_sep_sum(d.bf16, yp, (int)d.Bt, (int)d.T, (int)d.E, (int)d.HP, y, stream),
+                    "separated_forward sum launch");
 }
 
 swimba_status swimba_output_project(const swimba_dims* dims, const void* y, const void* w_out,

@@ -14,6 +14,7 @@ void prof_end(hipStream_t s);
 
 struct ProjGeom {
   int M, D, H, P, G, N, E, k, W;
+  int bw_one = 0;  // B_hat without the routing weight (the separated-SSM layout)
   int HP() const { return H * P; }
   int GN() const { return G * N; }
 };
@@ -63,9 +64,21 @@ ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int 
 size_t scan_ws_bytes(const ScanGeom& g);
 // ld: the expert-mixed decay's running log2 decay [Bt, H, T] (then a is not
 // read), or nullptr for the shared decay a [H].
+// y_f32: fp32 y for bf16 problems (k = 1 and the shared decay only).
 hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
                        const void* C_mix, const float* a, const float* h_init, void* y,
-                       float* h_final, float* ws, hipStream_t s, const float* ld = nullptr);
+                       float* h_final, float* ws, hipStream_t s, const float* ld = nullptr,
+                       bool y_f32 = false);
+
+// Separated-SSM MoE (one trajectory per expert): per-expert dense streams of
+// the Bt * E sequences (row (b E + e) T + t) from the selected pairs' X_hat,
+// unweighted B_hat and weighted C parts, zeros where the expert is not
+// selected; and y = the sum over experts of the trajectories' fp32 outputs.
+hipError_t launch_sep_scatter(bool is_bf16, const int32_t* idx, const void* X_hat,
+                              const void* B_hat, const float* c_part, int Bt, int T, int E, int k,
+                              int HP, int GN, void* Xs, void* Bs, void* Cs, hipStream_t s);
+hipError_t launch_sep_sum(bool is_bf16, const float* yp, int Bt, int T, int E, int HP, void* y,
+                          hipStream_t s);
 
 // Expert-mixed decay: running log2 of the per-token decay within each chunk
 // of L tokens, ld [Bt, H, T], from the routing (idx, w [Bt*T, k]) and the

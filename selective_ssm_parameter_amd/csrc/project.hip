@@ -111,7 +111,7 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
     const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
     int HP, int GN, int k, int nrow_tiles, typename StreamOf<T>::type* __restrict__ X_hat,
     typename StreamOf<T>::type* __restrict__ B_hat, float* __restrict__ c_part,
-    TO* __restrict__ out) {
+    TO* __restrict__ out, int bw_one) {
   typedef typename StreamOf<T>::type S;
   typedef ProjLay<T, C> Lay;
   constexpr int BM = C::BM, BN = C::BN, NTH = C::NTH, NW = C::NW, TM = C::TM, TN = C::TN;
@@ -325,8 +325,9 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
         store8<S>(&X_hat[pair * HP + col], o);
       } else if (col < HP + GN) {
         S8 o;
+        const float wb = bw_one ? 1.f : wv;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(wv * v[q]);
+        for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(wb * v[q]);
         store8<S>(&B_hat[pair * GN + (col - HP)], o);
       } else {
         floatx8 o = v * wv;
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(256) void proj_skinny_kernel(
     const bf16* __restrict__ u, const bf16* __restrict__ wexp, const int32_t* __restrict__ sorted,
     const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
     int HP, int GN, int k, int nrow_tiles, f16* __restrict__ X_hat, f16* __restrict__ B_hat,
-    float* __restrict__ c_part) {
+    float* __restrict__ c_part, int bw_one) {
   typedef bf16x8 F;
   // chunk rows: 16-byte piece ch of row r at piece ch ^ (r % 16)
   __shared__ __align__(16) unsigned char abuf0[64 * kSkRowB];
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(256) void proj_skinny_kernel(
     } else if (col < HP + GN) {
       f16x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = from_f32<f16>(wv * v[q]);
+      for (int q = 0; q < 4; ++q) o[q] = from_f32<f16>((bw_one ? 1.f : wv) * v[q]);
       *reinterpret_cast<f16x4*>(&B_hat[pair * GN + (col - HP)]) = o;
     } else {
       *reinterpret_cast<floatx4*>(&c_part[pair * GN + (col - HP - GN)]) = v * wv;
@@ -537,11 +538,11 @@ static hipError_t launch_proj_cfg(const ProjGeom& g, const T* u, const T* wexp,
   if (g.D % (kProjStages * ProjLay<T, C>::BK) == 0)
     hipLaunchKernelGGL((proj_kernel<T, C, false, float, true>), grid, dim3(C::NTH), 0, s, u, wexp,
                        sorted, sorted_w, tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow,
-                       X_hat, B_hat, c_part, (float*)nullptr);
+                       X_hat, B_hat, c_part, (float*)nullptr, g.bw_one);
   else
     hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, u, wexp, sorted, sorted_w,
                        tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part,
-                       (float*)nullptr);
+                       (float*)nullptr, g.bw_one);
   prof_end(s);
   return hipGetLastError();
 }
@@ -562,7 +563,7 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
       prof_begin("expert_project", s);
       hipLaunchKernelGGL(proj_skinny_kernel, dim3((unsigned)((ntiles + 7) / 8 * 8)), dim3(256), 0,
                          s, u, wexp, sorted, sorted_w, ti, g.M, g.D, g.W, g.HP(), g.GN(), g.k,
-                         nrow, X_hat, B_hat, c_part);
+                         nrow, X_hat, B_hat, c_part, g.bw_one);
       prof_end(s);
       err = hipGetLastError();
     } else if (bm == 256)
@@ -600,11 +601,11 @@ static hipError_t launch_outproj_cfg(int M, int K, int N, const T* y, const T* w
   if (K % (kProjStages * ProjLay<T, C>::BK) == 0)
     hipLaunchKernelGGL((proj_kernel<T, C, true, T, true>), grid, dim3(C::NTH), 0, s, y, w,
                        (const int32_t*)nullptr, (const float*)nullptr, (const int4v*)nullptr, M, K,
-                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out);
+                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out, 0);
   else
     hipLaunchKernelGGL((proj_kernel<T, C, true, T>), grid, dim3(C::NTH), 0, s, y, w,
                        (const int32_t*)nullptr, (const float*)nullptr, (const int4v*)nullptr, M, K,
-                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out);
+                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out, 0);
   prof_end(s);
   return hipGetLastError();
 }

@@ -811,7 +811,7 @@ static hipError_t dispatch_np(const ScanGeom& g, const ScanArgs& a, hipStream_t 
 
 hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const void* X_hat,
                        const void* C_mix, const float* a, const float* h_init, void* y,
-                       float* h_final, float* ws, hipStream_t s, const float* ld) {
+                       float* h_final, float* ws, hipStream_t s, const float* ld, bool y_f32) {
   if (g.Bt == 0) return hipSuccess;
   if (g.T == 0) {
     if (h_final) return launch_state_copy(h_init, h_final, (size_t)g.Bt * g.H * g.N * g.P, s);
@@ -822,6 +822,15 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
   ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws, gram, ld,
                 g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks, nc, scan_npairs(g.L, g.bt),
                 g.Bt};
+  if (is_bf16 && y_f32) {
+    // fp16 streams with an fp32 y (the separated-SSM trajectories, summed
+    // over experts afterwards): shared decay, one slot per token
+    if (g.k != 1 || ld) return hipErrorInvalidValue;
+    const int np = g.N <= 32 ? 32 : (g.N <= 64 ? 64 : 128);
+    if (np == 32) return launch_scan_t<f16, float, 32, 1, 32, false>(g, args, s);
+    if (np == 64) return launch_scan_t<f16, float, 64, 1, 32, false>(g, args, s);
+    return launch_scan_t<f16, float, 128, 1, 32, false>(g, args, s);
+  }
   if (is_bf16) return dispatch_np<f16, bf16>(g, args, s);
   return dispatch_np<float, float>(g, args, s);
 }
