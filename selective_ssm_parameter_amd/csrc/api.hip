@@ -241,9 +241,13 @@ SepWs sep_ws(const Dims& d) {
   return w;
 }
 
+// The shared-decay and the expert-mixed scans may walk different segment
+// counts; one workspace query (SWIMBA_CALL_SCAN) serves both.
 size_t scan_bytes(const Dims& d) {
-  return scan_ws_bytes(scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
-                                 (int)d.k, (int)d.L, (int)d.esize));
+  return std::max(scan_ws_bytes(scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N,
+                                          (int)d.P, (int)d.k, (int)d.L, (int)d.esize, false)),
+                  scan_ws_bytes(scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N,
+                                          (int)d.P, (int)d.k, (int)d.L, (int)d.esize, true)));
 }
 
 swimba_status check_ws(void* ws, size_t have, size_t need) {
@@ -574,7 +578,7 @@ swimba_status scan_impl(bool mixed, const swimba_dims* dims, const void* B_hat,
   }
   if ((st = check_ws(ws, ws_bytes, scan_bytes(d))) != SWIMBA_OK) return st;
   const ScanGeom g = scan_geom((int)d.Bt, (int)d.T, (int)d.H, (int)d.G, (int)d.N, (int)d.P,
-                               (int)d.k, (int)d.L, (int)d.esize);
+                               (int)d.k, (int)d.L, (int)d.esize, mixed);
   return hip_status(launch_scan(d.bf16, g, B_hat, X_hat, C_mix, a, h_init, y, h_final,
                                 static_cast<float*>(ws), stream, log_decay),
                     "ssd_chunk_scan launch");

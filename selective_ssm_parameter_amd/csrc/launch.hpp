@@ -59,8 +59,11 @@ struct ScanGeom {
   int bt;            // tokens per block of the scan (32 or 64)
   int segs;          // segments per sequence
   int seg_chunks;    // chunks per segment
+  int walk2;         // the output pass walks two heads per workgroup
 };
-ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es);
+// tv: the expert-mixed decay (its output pass walks one head per workgroup).
+ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es,
+                   bool tv = false);
 size_t scan_ws_bytes(const ScanGeom& g);
 // ld: the expert-mixed decay's running log2 decay [Bt, H, T] (then a is not
 // read), or nullptr for the shared decay a [H].

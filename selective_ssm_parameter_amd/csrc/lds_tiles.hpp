@@ -87,6 +87,79 @@ __device__ __forceinline__ void dma_tile_full(BufRes rs, uint32_t base, const ui
   }
 }
 
+// Copies of a tile shared by NWV waves in which every wave issues the same
+// number of instructions (dma_count), so that a wave can wait for a tile with
+// a fixed vector-memory count: instruction m of wave w moves the tile's
+// 64-chunk group m NWV + w; when the group count NI is not a multiple of NWV,
+// the waves past the last group repeat one already moved (the same bytes to
+// the same LDS place).
+template <int NROWS, int CPR, int NWV>
+constexpr int dma_count() {
+  return (NROWS * CPR / 64 + NWV - 1) / NWV;
+}
+template <int NROWS, int CPR, int NWV>
+__device__ __forceinline__ int dma_group(int m, int wave) {
+  constexpr int NI = NROWS * CPR / 64;
+  const int i = m * NWV + wave;
+  return i < NI ? i : i % NI;
+}
+template <int NROWS, int CPR, int NWV, class Swz>
+__device__ __forceinline__ void dma_plan_n(uint32_t pitch, int wave, int lane, Swz swz,
+                                           uint32_t* off) {
+  static_assert((NROWS * CPR) % 64 == 0, "tile must be whole 64-chunk groups");
+#pragma unroll
+  for (int m = 0; m < dma_count<NROWS, CPR, NWV>(); ++m) {
+    const int slot = 64 * dma_group<NROWS, CPR, NWV>(m, wave) + lane;
+    const int r = slot / CPR, pc = slot % CPR;
+    off[m] = r * pitch + 16 * (pc ^ swz(r));
+  }
+}
+// Every row and chunk valid: per-lane offsets from dma_plan_n, the tile's
+// position as the scalar offset.
+template <int NROWS, int CPR, int NWV>
+__device__ __forceinline__ void dma_tile_full_n(BufRes rs, uint32_t base, const uint32_t* off,
+                                                unsigned char* dst, int wave) {
+#pragma unroll
+  for (int m = 0; m < dma_count<NROWS, CPR, NWV>(); ++m) {
+    const int i = dma_group<NROWS, CPR, NWV>(m, wave);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, off[m], base, 0, 0);
+  }
+}
+// Rows >= rvalid and chunks >= cvalid read as zeros; the same instruction
+// count as dma_tile_full_n.
+template <int NROWS, int CPR, int NWV, class Swz>
+__device__ __forceinline__ void dma_tile_n(BufRes rs, uint32_t base, uint32_t pitch,
+                                           unsigned char* dst, int rvalid, int cvalid, int wave,
+                                           int lane, Swz swz) {
+#pragma unroll
+  for (int m = 0; m < dma_count<NROWS, CPR, NWV>(); ++m) {
+    const int i = dma_group<NROWS, CPR, NWV>(m, wave);
+    const int slot = 64 * i + lane;
+    const int r = slot / CPR, pc = slot % CPR;
+    const int lc = pc ^ swz(r);
+    const uint32_t off = (r < rvalid && lc < cvalid) ? base + r * pitch + 16 * lc : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, off, 0, 0, 0);
+  }
+}
+
+// dma_tile_full_n with a row limit: the copy of instruction m reads zeros
+// unless row[m] < rvalid (row[m]: the tile row, in the caller's numbering, of
+// this lane's chunk; off[m] its offset within the tile).
+template <int NROWS, int CPR, int NWV>
+__device__ __forceinline__ void dma_rows_n(BufRes rs, uint32_t base, const uint32_t* off,
+                                           const int* row, int rvalid, unsigned char* dst,
+                                           int wave) {
+#pragma unroll
+  for (int m = 0; m < dma_count<NROWS, CPR, NWV>(); ++m) {
+    const int i = dma_group<NROWS, CPR, NWV>(m, wave);
+    const uint32_t o = row[m] < rvalid ? off[m] + base : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, o, 0, 0, 0);
+  }
+}
+
 // A K-major operand fragment from a row-major [k][col] LDS tile: lane (g, c)
 // gets rows k0 + 8g .. k0 + 8g + 7 of column col0 + c. 2-byte types use two
 // transposing reads (in a 16-lane group, lane i receives element i % 4 of the

@@ -636,6 +636,431 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 && KS <= 2 ? 2 : 1) vo
   }
 }
 
+// The output walk with two heads per workgroup (8 waves) and a ring of three
+// LDS stages: the copies of step s + 2 are issued while step s computes, so
+// every tile has two steps to arrive (with one head per workgroup and two
+// stages, a step's compute was shorter than the HBM latency of the next
+// step's X tile, and the walk waited on it). The two heads share one group's
+// B_hat, C~ and Gram tiles, copied once into the stage for both; each head's
+// X tile is copied by its own four waves. Per chunk, the entering state's
+// fp16 operand of the readout is formed once (it does not change until the
+// chunk's carry). The arithmetic is that of scan_kernel (pass 3).
+// N copies that read nothing (an offset past the buffer) and write 4-byte
+// zeros into `sink` (256 bytes of LDS): they keep a wave's count of copies in
+// flight fixed when a step needs fewer tiles.
+template <int N>
+__device__ __forceinline__ void dma_dummies(BufRes rs, unsigned char* sink) {
+#pragma unroll
+  for (int m = 0; m < N; ++m) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sink),
+                                             4, kOOB, 0, 0, 0);
+  }
+}
+
+template <typename T, int NP, int KS, int BT>
+struct Walk2Lds {
+  static constexpr int HPW = 2;  // heads per workgroup
+  static constexpr int R = KS * BT;
+  static constexpr int XROW = kP * (int)sizeof(T), BROW = NP * (int)sizeof(T);
+  static constexpr int GROW = R * (int)sizeof(T);
+  static constexpr int XB = R * XROW, BB = R * BROW, CB = BT * BROW, GB = BT * GROW;
+  static constexpr int XO = 0, BO = HPW * XB, CO = BO + BB, GO = CO + CB;
+  static constexpr int STAGE = GO + GB;
+};
+constexpr int kWalk2Threads = 512;
+
+template <typename T, typename TY, int NP, int KS, int BT>
+__global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A) {
+  typedef Walk2Lds<T, NP, KS, BT> Lay;
+  constexpr int R = Lay::R;
+  constexpr int TT = BT / 16, RQ = R / 32, NT = NP / 16, NQ = NP / 32;
+  constexpr int XC = Lay::XROW / 16, BC = Lay::BROW / 16, GC = Lay::GROW / 16;
+  typedef DiagFrags<KS, BT> DF;
+  constexpr int NDF = DF::count() > 0 ? DF::count() : 1;
+  constexpr uint32_t ES = sizeof(T);
+  typedef typename Vec<T>::x8 F;
+  // copy instructions per wave and tile (X by the head's 4 waves, the shared
+  // tiles by all 8)
+  constexpr int CX = dma_count<2 * R, XC, 8>(), CBn = dma_count<R, BC, 8>();
+  constexpr int CCn = dma_count<BT, BC, 8>(), CG = dma_count<BT, GC, 8>();
+
+  __shared__ __align__(16) unsigned char stage0[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stage1[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stage2[Lay::STAGE];
+
+  const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
+  const int HU = H / 2;
+  // (head pair, segment, sequence), head pair fastest, XCD-contiguous as in
+  // scan_kernel
+  const int per = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (logical >= HU * A.segs * A.Bt) return;
+  const int hp = logical % HU, seg = (logical / HU) % A.segs, b = logical / (HU * A.segs);
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hw = w >> 2, wc = w & 3;  // head of the pair, column block of the head
+  const int h = 2 * hp + hw;
+  const int grp = h / (H / G);
+  const int GN = G * N;
+  const int g4 = lane >> 4, c = lane & 15;
+  const size_t NPsz = (size_t)N * kP;
+  const size_t HPsz = (size_t)H * kP;
+  const int prow_x = 16 * wc + c;  // this lane's head column p
+
+  const float ah = A.a[h];
+  const float la = ah > 0.f ? log2f(ah) : -1e30f;
+
+  const BufRes rB = make_rsrc(reinterpret_cast<const T*>(A.B_hat) + (size_t)b * Tlen * KS * GN,
+                              (uint64_t)Tlen * KS * GN * ES);
+  const BufRes rX = make_rsrc(reinterpret_cast<const T*>(A.X_hat) + (size_t)b * Tlen * KS * HPsz,
+                              (uint64_t)Tlen * KS * HPsz * ES);
+  const BufRes rC = make_rsrc(reinterpret_cast<const T*>(A.C_mix) + (size_t)b * Tlen * GN,
+                              (uint64_t)Tlen * GN * ES);
+  const size_t gtile = (size_t)BT * R;
+  const BufRes rG = make_rsrc(
+      reinterpret_cast<const T*>(A.gram) + (size_t)b * A.nc * G * A.npairs * gtile,
+      (uint64_t)A.nc * G * A.npairs * gtile * ES);
+
+  // ---- per-lane decay tables of this wave's head (as in scan_kernel)
+  F er[RQ];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) er[q][j] = from_f32<T>(apow(la, BT - 1 - (32 * q + 8 * g4 + j) / KS));
+  float at[TT];
+  F dm[NDF];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) at[tt] = apow(la, 16 * tt + c);
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int ix = DF::index(tt, q);
+      if (ix >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int d = 16 * tt + c - (32 * q + 8 * g4 + j) / KS;
+          dm[ix][j] = from_f32<T>(d >= 0 ? apow(la, d) : 0.f);
+        }
+      }
+    }
+
+  // ---- entering state of this segment (this wave's columns)
+  floatx4 Hr[NT];
+  {
+    const float* src = nullptr;
+    if (A.segs == 1) {
+      src = A.h_init;
+      if (src) src += ((size_t)b * H + h) * NPsz;
+    } else {
+      src = A.ws + (((size_t)b * A.segs + seg) * H + h) * NPsz;
+    }
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 16 * a + 4 * g4 + i;
+        Hr[a][i] = (src && n < N) ? src[(size_t)n * kP + prow_x] : 0.f;
+      }
+  }
+
+  const int nc = A.nc;
+  const int ch0 = seg * A.seg_chunks;
+  const int ch1 = min(nc, ch0 + A.seg_chunks);
+  if (ch0 >= ch1) return;
+  auto nblocks = [&](int ch) { return (min(L, Tlen - ch * L) + BT - 1) / BT; };
+  auto advance = [&](ScanStep s) {
+    if (++s.sig > s.tau) {
+      s.sig = 0;
+      if (++s.tau == nblocks(s.ch)) { s.tau = 0; ++s.ch; }
+    }
+    return s;
+  };
+
+  // ---- copies of one step into a stage
+  // X: the two heads' tiles as one tile of 2R rows copied by all 8 waves
+  // (row r of head r / R at global row r % R, the head's columns kP * ES
+  // further), so the copies' LDS addresses do not depend on the wave's head
+  uint32_t xoff[CX], boff[CBn], coff[CCn], goff[CG];
+  int xrow[CX];
+#pragma unroll
+  for (int m = 0; m < CX; ++m) {
+    const int slot = 64 * dma_group<2 * R, XC, 8>(m, w) + lane;
+    const int r = slot / XC, pc = slot % XC, rr = r % R;
+    xrow[m] = rr;
+    xoff[m] = rr * (uint32_t)HPsz * ES + (r / R) * kP * ES + 16 * (pc ^ swz_tr<T, XC>(rr));
+  }
+  dma_plan_n<R, BC, 8>((uint32_t)GN * ES, w, lane, [](int r) { return swz_tr<T, BC>(r); }, boff);
+  dma_plan_n<BT, BC, 8>((uint32_t)GN * ES, w, lane, [](int r) { return swz_row<T, BC>(r); }, coff);
+  dma_plan_n<BT, GC, 8>((uint32_t)R * ES, w, lane, [](int r) { return swz_row<T, GC>(r); }, goff);
+  const bool nfull = N == NP;
+  // Every step issues the same number of copy instructions per wave (NCOPY):
+  // tiles a step does not need are replaced by copies that read nothing (an
+  // offset past the buffer) and write 4-byte zeros into a small sink, so the
+  // wait for a stage is one fixed count and the compiler's own wait model
+  // stays exact (with per-step counts it waited for every copy in flight).
+  constexpr int NCOPY = CX + CG + CCn + CBn;
+  __shared__ __align__(16) unsigned char sink[256];
+
+  auto fetch = [&](unsigned char* st, ScanStep s) {
+    const int c0 = s.ch * L;
+    const int Lc = min(L, Tlen - c0);
+    const bool last = s.tau == (Lc + BT - 1) / BT - 1;
+    const uint32_t prow = (uint32_t)(c0 + s.sig * BT) * KS;
+    const int rlim = (Lc - s.sig * BT) * KS;
+    const bool rows_full = rlim >= R;
+    const uint32_t xb = (prow * (uint32_t)HPsz + 2 * hp * kP) * ES;
+    if (rows_full)
+      dma_tile_full_n<2 * R, XC, 8>(rX, xb, xoff, st + Lay::XO, w);
+    else
+      dma_rows_n<2 * R, XC, 8>(rX, xb, xoff, xrow, rlim, st + Lay::XO, w);
+    const int pidx = s.tau * (s.tau + 1) / 2 + s.sig;
+    const uint32_t gbase = (uint32_t)((((size_t)s.ch * G + grp) * A.npairs + pidx) * gtile);
+    dma_tile_full_n<BT, GC, 8>(rG, gbase * ES, goff, st + Lay::GO, w);
+    if (s.sig == 0) {
+      const uint32_t cb = ((uint32_t)(c0 + s.tau * BT) * GN + grp * N) * ES;
+      if (Lc - s.tau * BT >= BT && nfull)
+        dma_tile_full_n<BT, BC, 8>(rC, cb, coff, st + Lay::CO, w);
+      else
+        dma_tile_n<BT, BC, 8>(rC, cb, GN * ES, st + Lay::CO, Lc - s.tau * BT, (int)(N * ES / 16),
+                              w, lane, [](int r) { return swz_row<T, BC>(r); });
+    } else {
+      dma_dummies<CCn>(rX, sink);
+    }
+    if (last) {
+      const uint32_t bb = (prow * GN + grp * N) * ES;
+      if (rows_full && nfull)
+        dma_tile_full_n<R, BC, 8>(rB, bb, boff, st + Lay::BO, w);
+      else
+        dma_tile_n<R, BC, 8>(rB, bb, GN * ES, st + Lay::BO, rlim, (int)(N * ES / 16), w, lane,
+                             [](int r) { return swz_tr<T, BC>(r); });
+    } else {
+      dma_dummies<CBn>(rX, sink);
+    }
+  };
+
+  float hscale = 1.f;
+  F hf[NQ];  // the entering state of the chunk as fp16 operands (scaled by 1/hscale)
+  floatx4 accY[TT];
+  bool ypend = false;
+  size_t yrow0 = 0;
+  int ylim = 0;
+
+  auto compute = [&](const unsigned char* st, const ScanStep cur) {
+    const unsigned char* Xs = st + Lay::XO + hw * Lay::XB;
+    const unsigned char* Bs = st + Lay::BO;
+    const unsigned char* Cs = st + Lay::CO;
+    const unsigned char* Gs = st + Lay::GO;
+    const int c0 = cur.ch * L;
+    const int Lc = min(L, Tlen - c0);
+    const int nb = (Lc + BT - 1) / BT;
+    const bool last = cur.tau == nb - 1;
+    const bool dg = cur.sig == cur.tau;
+
+    if (cur.tau == 0 && cur.sig == 0) {
+      // the chunk's entering state as fp16 operands, scaled by 2^-e (e >= 0
+      // from this wave's max |H|) so they stay below 2^14; the readout is
+      // multiplied back by 2^e in fp32
+      float hin = 1.f;
+      hscale = 1.f;
+      if (sizeof(T) == 2) {
+        float mx = 0.f;
+#pragma unroll
+        for (int a = 0; a < NT; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[a][i]));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (mx > 16384.f) {
+          const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
+          hin = ldexpf(1.f, -e);
+          hscale = ldexpf(1.f, e);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hf[q][i] = from_f32<T>(Hr[2 * q][i] * hin);
+          hf[q][4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
+        }
+    }
+
+    F xq[RQ];  // X^T fragment of this wave's columns: rows r = 32q + 8g + j
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) xq[q] = load_kmajor<T, XC>(Xs, 32 * q, 16 * wc, lane);
+
+    if (cur.sig == 0) {
+      // ---- readout of the entering state: y^T[p, t] = H^T[p, n] C~^T[n, t]
+      const float ablk = (cur.tau == 0 ? 1.f : apow_step(la, cur.tau * BT)) * hscale * ah;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) accY[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        F cf[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          // C~ operand in the state's n order: {32q + 4g .. +3, 32q + 16 + 4g .. +3}
+          const int t = 16 * tt + c;
+          const int n0 = 32 * q + 4 * g4;
+          const int e0 = n0 * (int)ES, e1 = (n0 + 16) * (int)ES;
+          const int sw = swz_row<T, BC>(t);
+          const T* p0 = reinterpret_cast<const T*>(Cs + (t * BC + ((e0 >> 4) ^ sw)) * 16 + (e0 & 15));
+          const T* p1 = reinterpret_cast<const T*>(Cs + (t * BC + ((e1 >> 4) ^ sw)) * 16 + (e1 & 15));
+          cf[tt] = load4x2<T>(p0, p1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) accY[tt] = mma16(hf[q], cf[tt], accY[tt]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] * (at[tt] * ablk);
+    }
+    // ---- intra-chunk: y^T[p, t] += X^T[p, r] (G o decay)[t, r]
+    auto gfrag = [&](int tt, int q) {
+      const int t = 16 * tt + c;
+      const int e0 = (32 * q + 8 * g4) * (int)ES;
+      const unsigned char* p = Gs + (t * GC + ((e0 >> 4) ^ swz_row<T, GC>(t))) * 16 + (e0 & 15);
+      return load8<T>(reinterpret_cast<const T*>(p));
+    };
+    if (dg) {
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        F gf[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          if (DF::index(tt, q) >= 0) gf[tt] = gfrag(tt, q);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const int ix = DF::index(tt, q);
+          if (ix >= 0) accY[tt] = mma16(xq[q], gf[tt] * dm[ix], accY[tt]);
+        }
+      }
+    } else {
+      floatx4 tmp[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) tmp[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        F gf[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) gf[tt] = gfrag(tt, q);
+        __builtin_amdgcn_sched_barrier(0);
+        const F xs = xq[q] * er[q];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) tmp[tt] = mma16(xs, gf[tt], tmp[tt]);
+      }
+      const float u = apow_step(la, (cur.tau - cur.sig) * BT - (BT - 1));
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] + tmp[tt] * (u * at[tt]);
+    }
+    if (last) {
+      // the carry accumulates straight into the state: H <- a^{Lc} H first
+      // (every readout of this chunk used the fp16 copy taken at its start)
+      if (cur.sig == 0) {
+        const float aL = apow_step(la, Lc);
+#pragma unroll
+        for (int a = 0; a < NT; ++a) Hr[a] = Hr[a] * aL;
+      }
+      // ---- carry: H[n, p] += sum_r B_hat[r, n] (a^{Lc-1-s} X[r, p])
+      const bool full = Lc == L;
+      const float blk = apow_step(la, (nb - 1 - cur.sig) * BT);
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        F xd;
+        if (full) {
+          xd = xq[q] * (er[q] * from_f32<T>(blk));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int d = Lc - 1 - (cur.sig * BT + (32 * q + 8 * g4 + j) / KS);
+            xd[j] = from_f32<T>(to_f32(xq[q][j]) * (d >= 0 ? apow_step(la, d) : 0.f));
+          }
+        }
+        constexpr int CGR = NT < 4 ? NT : 4;
+#pragma unroll
+        for (int a0 = 0; a0 < NT; a0 += CGR) {
+          F bf[CGR];
+#pragma unroll
+          for (int i = 0; i < CGR; ++i) bf[i] = load_kmajor<T, BC>(Bs, 32 * q, 16 * (a0 + i), lane);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < CGR; ++i) Hr[a0 + i] = mma16(bf[i], xd, Hr[a0 + i]);
+        }
+      }
+    }
+    if (dg) {
+      // y of block tau is complete; it is stored at the start of the next step
+      ypend = true;
+      yrow0 = (size_t)b * Tlen + c0 + cur.tau * BT;
+      ylim = Lc - cur.tau * BT;
+    }
+  };
+  auto store_y = [&]() {
+    if (!ypend) return;
+    typedef typename Vec<TY>::x4 Y4;
+    TY* yb = reinterpret_cast<TY*>(A.y) + yrow0 * HPsz + (size_t)h * kP + 16 * wc + 4 * g4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int tl = 16 * tt + c;
+      if (tl < ylim) {
+        Y4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[tt][i]);
+        *reinterpret_cast<Y4*>(yb + (size_t)tl * HPsz) = o;
+      }
+    }
+    ypend = false;
+  };
+
+  // ---- the walk: step s computes from stage s % 3 while the copies of step
+  // s + 2 go into stage (s + 2) % 3 (the one step s - 1 read); one barrier per
+  // step. Unrolled by three so that every access names its stage array.
+  ScanStep s0{ch0, 0, 0};
+  ScanStep s1 = advance(s0);
+  ScanStep s2 = s1.ch < ch1 ? advance(s1) : s1;
+  fetch(stage0, s0);
+  if (s1.ch < ch1)
+    fetch(stage1, s1);
+  else
+    dma_dummies<NCOPY>(rX, sink);
+  // Both first stages complete before the walk starts: the compiler's own
+  // wait model then knows every stage's copies at the loop head (with only
+  // step 0's stage waited for here it waited for every copy in flight before
+  // the first read of each turn of the loop).
+  wait_vm<0>();
+  stage_barrier();
+  auto step = [&](const unsigned char* cur_st, unsigned char* far_st) {
+    store_y();
+    if (s2.ch < ch1)
+      fetch(far_st, s2);
+    else
+      dma_dummies<NCOPY>(rX, sink);
+    compute(cur_st, s0);
+    wait_vm<NCOPY>();  // the next step's copies have landed
+    stage_barrier();
+    s0 = s1;
+    s1 = s2;
+    if (s2.ch < ch1) s2 = advance(s2);
+    return s0.ch < ch1;
+  };
+  while (step(stage0, stage2) && step(stage1, stage0) && step(stage2, stage1)) {
+  }
+  store_y();
+
+  if (seg == A.segs - 1 && A.h_final) {
+    float* dst = A.h_final + ((size_t)b * H + h) * NPsz;
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 16 * a + 4 * g4 + i;
+        if (n < N) dst[(size_t)n * kP + prow_x] = Hr[a][i];
+      }
+  }
+}
+
 // Pass 2: Hin_0 = h_init (or 0), Hin_{s+1} = a^{len_s} Hin_s + S_s, for every
 // (sequence, head, element), walking the segments in order. Slot s of the
 // workspace holds S_{s-1} on entry (s >= 1) and Hin_s on exit.
@@ -723,12 +1148,30 @@ static int scan_block(int N, int k, int L, int es) {
   return 32;
 }
 
-ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es) {
-  ScanGeom g{Bt, T, H, G, N, P, k, L, es, scan_block(N, k, L, es), 1, 1};
+// The two-head walk serves 2-byte streams with k <= 2 and the shared decay,
+// when the heads of a group pair up (H / G even), for chunks of 128 and 256
+// tokens (10 and 36 block pairs per chunk, where sharing the Gram, C~ and
+// B_hat tiles between two heads pays: measured on MI355X, 4 x 8192 tokens,
+// 64 heads, L = 128: 415 -> 402 us; 65536 tokens, 32 heads, L = 256: 812 ->
+// 546 us; with 64-token chunks, 8 x 2048 tokens, 24 heads, it was slower,
+// 80 -> 88 us). It holds one workgroup per CU: it aims at one round of 256.
+static bool walk2_eligible(int H, int G, int k, int es, bool tv, int L) {
+  return es == 2 && k <= 2 && !tv && (H / G) % 2 == 0 && L >= 128;
+}
+static int walk2_target_wgs(int L) {
+  static const int w = env_int("SWIMBA_SCAN_WGS", 0);
+  if (w > 0) return w;
+  (void)L;
+  return 256;
+}
+
+ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es, bool tv) {
+  ScanGeom g{Bt, T, H, G, N, P, k, L, es, scan_block(N, k, L, es), 1, 1, 0};
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
-  const int units = Bt * H;
-  int want = scan_target_wgs(L) / units;
+  g.walk2 = walk2_eligible(H, G, k, es, tv, L) ? 1 : 0;
+  const int units = g.walk2 ? Bt * (H / 2) : Bt * H;
+  int want = (g.walk2 ? walk2_target_wgs(L) : scan_target_wgs(L)) / units;
   if (want > nc) want = nc;
   if (want < 1) want = 1;
   g.seg_chunks = (nc + want - 1) / want;
@@ -778,6 +1221,15 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
     prof_end(s);
   }
   prof_begin("scan_chunk_output", s);
+  if constexpr (sizeof(T) == 2 && KS <= 2 && !TV) {
+    if (g.walk2) {
+      const int n3 = (g.H / 2) * g.segs * g.Bt;
+      hipLaunchKernelGGL((scan_walk2_kernel<T, TY, NP, KS, BT>), dim3((unsigned)((n3 + 7) / 8 * 8)),
+                         dim3(kWalk2Threads), 0, s, args);
+      prof_end(s);
+      return hipGetLastError();
+    }
+  }
   const int n3 = g.H * g.segs * g.Bt;
   hipLaunchKernelGGL(k3, dim3((unsigned)((n3 + 7) / 8 * 8)), dim3(kScanThreads), l3, s, args);
   prof_end(s);

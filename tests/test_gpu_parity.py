@@ -182,6 +182,13 @@ SCAN_CASES = [
     ("bf16_k4_n32_L32_g2", W("s18", 318, top_k=4, dstate=32, chunk=32, ngroups=2, seqlen=150), True),
     ("bf16_k4_L256_segments", W("s19", 319, top_k=4, chunk=256, batch=1, nheads=2, seqlen=3000), True),
     ("bf16_k4_n16_short", W("s20", 320, top_k=4, dstate=16, seqlen=7, batch=3), False),
+    # the two-head walk (chunks of 128 and 256 tokens): k = 1, N = 64, two
+    # groups with N = 32, a sequence shorter than one chunk, an odd number of
+    # heads per group (which keeps one head per workgroup)
+    ("bf16_k1_n64_L128_pairs", W("s21", 321, top_k=1, dstate=64, chunk=128, seqlen=517), True),
+    ("bf16_n32_g2_L256_pairs", W("s22", 322, dstate=32, ngroups=2, chunk=256, seqlen=700), True),
+    ("bf16_n16_L128_short_pairs", W("s23", 323, dstate=16, chunk=128, seqlen=40, batch=3), True),
+    ("bf16_h6_g2_L128_odd", W("s24", 324, nheads=6, ngroups=2, dstate=64, chunk=128, seqlen=300), True),
 ]
 
 
