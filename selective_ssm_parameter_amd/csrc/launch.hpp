@@ -60,6 +60,7 @@ struct ScanGeom {
   int segs;          // segments per sequence
   int seg_chunks;    // chunks per segment
   int walk2;         // the output pass walks two heads per workgroup
+  int sub;           // pass 1 walks each segment in `sub` pieces
 };
 // tv: the expert-mixed decay (its output pass walks one head per workgroup).
 ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es,

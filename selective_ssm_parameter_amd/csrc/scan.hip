@@ -59,6 +59,7 @@ struct ScanArgs {
   const float* ld;    // expert-mixed decay: [Bt, H, T] running log2 decay within each
                       // chunk (inclusive); nullptr for the shared decay a
   int T, H, G, N, k, L, segs, seg_chunks, nc, npairs, Bt;
+  int sub;  // pass 1 splits each segment into `sub` pieces of seg_chunks / sub chunks
 };
 
 // LDS of the walk: two stages, each holding one step's row-major tiles as they
@@ -201,7 +202,11 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 && KS <= 2 ? 2 : 1) vo
   // owns the contiguous range [x * per, (x + 1) * per): the heads of one
   // (sequence, segment) share an XCD and walk its chunks together, so the
   // B_hat, C~ and Gram tiles they all read come from that XCD's L2.
-  const int nseg = WITH_Y ? A.segs : A.segs - 1;
+  // pass 1 walks the pieces of every segment but the last (sub per segment),
+  // pass 3 the segments; the workspace holds one state slot per piece
+  // boundary (slot 0: h_init), segment s entering at slot s * sub
+  const int nseg = WITH_Y ? A.segs : (A.segs - 1) * A.sub;
+  const int nslot = (A.segs - 1) * A.sub + 1;
   const int per = gridDim.x / 8;
   const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (logical >= H * nseg * A.Bt) return;
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 && KS <= 2 ? 2 : 1) vo
         src = A.h_init;
         if (src) src += ((size_t)b * H + h) * NPsz;
       } else {
-        src = A.ws + (((size_t)b * A.segs + seg) * H + h) * NPsz;
+        src = A.ws + (((size_t)b * nslot + seg * A.sub) * H + h) * NPsz;
       }
     }
 #pragma unroll
@@ -282,8 +287,9 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 && KS <= 2 ? 2 : 1) vo
   }
 
   const int nc = A.nc;
-  const int ch0 = seg * A.seg_chunks;
-  const int ch1 = min(nc, ch0 + A.seg_chunks);
+  const int span = WITH_Y ? A.seg_chunks : A.seg_chunks / A.sub;  // chunks walked
+  const int ch0 = seg * span;
+  const int ch1 = min(nc, ch0 + span);
   if (ch0 >= ch1) return;
   auto nblocks = [&](int ch) { return (min(L, Tlen - ch * L) + BT - 1) / BT; };
   auto advance = [&](ScanStep s) {
@@ -621,7 +627,7 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 && KS <= 2 ? 2 : 1) vo
   // ---- write the end state
   float* dst = nullptr;
   if (!WITH_Y) {
-    dst = A.ws + (((size_t)b * A.segs + seg + 1) * H + h) * NPsz;  // slot s+1 holds S_s
+    dst = A.ws + (((size_t)b * nslot + seg + 1) * H + h) * NPsz;  // slot j+1 holds S_j
   } else if (seg == A.segs - 1 && A.h_final) {
     dst = A.h_final + ((size_t)b * H + h) * NPsz;
   }
@@ -753,7 +759,7 @@ __global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A
       src = A.h_init;
       if (src) src += ((size_t)b * H + h) * NPsz;
     } else {
-      src = A.ws + (((size_t)b * A.segs + seg) * H + h) * NPsz;
+      src = A.ws + (((size_t)b * ((A.segs - 1) * A.sub + 1) + seg * A.sub) * H + h) * NPsz;
     }
 #pragma unroll
     for (int a = 0; a < NT; ++a)
@@ -1062,8 +1068,9 @@ __global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A
 }
 
 // Pass 2: Hin_0 = h_init (or 0), Hin_{s+1} = a^{len_s} Hin_s + S_s, for every
-// (sequence, head, element), walking the segments in order. Slot s of the
-// workspace holds S_{s-1} on entry (s >= 1) and Hin_s on exit.
+// (sequence, head, element), walking the pieces of pass 1 in order (`segs`
+// slots here, pieces of `seg_chunks` chunks). Slot s of the workspace holds
+// S_{s-1} on entry (s >= 1) and Hin_s on exit.
 // With the expert-mixed decay (ld non-null) a segment's decay is the product
 // over its chunks of 2^{Lam at the chunk's last token}, the exponents summed in
 // chunk order.
@@ -1165,8 +1172,31 @@ static int walk2_target_wgs(int L) {
   return 256;
 }
 
+// Pass 1 (the carry-only walk to each segment's end state) runs one head per
+// workgroup; with few segments it leaves CUs idle (4 x 8192 tokens, 64 heads,
+// two segments: 256 workgroups). It splits every segment into equal pieces
+// (a divisor of its chunk count), as many as bring it closest to 512
+// workgroups, and the combine then sweeps the pieces. Measured on MI355X:
+// 4 x 8192 tokens, 64 heads: 2 pieces took pass 1 + combine from 128 to 95 us
+// (4 pieces: 123 us); 65536 tokens, 32 heads (480 workgroups already): 2
+// pieces were slower (168 -> 202 us).
+static int scan_pieces(int units1, int seg_chunks) {
+  static const int forced = env_int("SWIMBA_SCAN_SUB", 0);
+  if (units1 <= 0) return 1;
+  int best = 1;
+  for (int m = 1; m <= seg_chunks; ++m) {
+    if (seg_chunks % m) continue;
+    if (forced > 0) {
+      if (m >= forced) return m;
+      continue;
+    }
+    if (std::abs(units1 * m - 512) < std::abs(units1 * best - 512)) best = m;
+  }
+  return forced > 0 ? seg_chunks : best;
+}
+
 ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es, bool tv) {
-  ScanGeom g{Bt, T, H, G, N, P, k, L, es, scan_block(N, k, L, es), 1, 1, 0};
+  ScanGeom g{Bt, T, H, G, N, P, k, L, es, scan_block(N, k, L, es), 1, 1, 0, 1};
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
   g.walk2 = walk2_eligible(H, G, k, es, tv, L) ? 1 : 0;
@@ -1176,6 +1206,7 @@ ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int 
   if (want < 1) want = 1;
   g.seg_chunks = (nc + want - 1) / want;
   g.segs = (nc + g.seg_chunks - 1) / g.seg_chunks;
+  g.sub = scan_pieces(Bt * H * (g.segs - 1), g.seg_chunks);
   return g;
 }
 
@@ -1183,7 +1214,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static size_t scan_state_bytes(const ScanGeom& g) {
   if (g.segs <= 1) return 0;
-  return align256((size_t)g.Bt * g.segs * g.H * g.N * g.P * sizeof(float));
+  const size_t nslot = (size_t)(g.segs - 1) * g.sub + 1;
+  return align256((size_t)g.Bt * nslot * g.H * g.N * g.P * sizeof(float));
 }
 
 static size_t scan_gram_bytes(const ScanGeom& g) {
@@ -1210,14 +1242,14 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   prof_end(s);
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
-    const int n1 = g.H * (g.segs - 1) * g.Bt;
+    const int n1 = g.H * (g.segs - 1) * g.sub * g.Bt;
     hipLaunchKernelGGL(k1, dim3((unsigned)((n1 + 7) / 8 * 8)), dim3(kScanThreads), l1, s, args);
     prof_end(s);
     const int NPsz = g.N * g.P;
     prof_begin("scan_state_pass", s);
     hipLaunchKernelGGL(scan_combine_kernel, dim3((NPsz / 4 + 255) / 256, g.H, g.Bt), dim3(256), 0,
-                       s, args.a, args.h_init, args.ws, g.H, NPsz, g.T, g.L, g.segs, g.seg_chunks,
-                       args.ld);
+                       s, args.a, args.h_init, args.ws, g.H, NPsz, g.T, g.L,
+                       (g.segs - 1) * g.sub + 1, g.seg_chunks / g.sub, args.ld);
     prof_end(s);
   }
   prof_begin("scan_chunk_output", s);
@@ -1273,7 +1305,7 @@ hipError_t launch_scan(bool is_bf16, const ScanGeom& g, const void* B_hat, const
   unsigned char* gram = reinterpret_cast<unsigned char*>(ws) + scan_state_bytes(g);
   ScanArgs args{B_hat, X_hat, C_mix, a, h_init, y, h_final, ws, gram, ld,
                 g.T, g.H, g.G, g.N, g.k, g.L, g.segs, g.seg_chunks, nc, scan_npairs(g.L, g.bt),
-                g.Bt};
+                g.Bt, g.sub};
   if (is_bf16 && y_f32) {
     // fp16 streams with an fp32 y (the separated-SSM trajectories, summed
     // over experts afterwards): shared decay, one slot per token
