@@ -123,6 +123,97 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const T* __restrict__ u,
   }
 }
 
+// Prefill-sized batches: a workgroup routes 64 tokens with 4 waves that split
+// d_model four ways, every wave computing all 64 tokens (four token tiles)
+// against GT expert tiles for its quarter of d_model, so each router-row
+// fragment serves four token tiles (with 16 tokens per wave over all of
+// d_model, every wave read all of W_r: at E = 64 and d_model 2048, four times
+// the bytes of u). The partial logits are summed in LDS in slice order. The
+// loads of RB K steps are issued together before their matrix-core ops.
+template <typename T, int GT, int RB>
+__global__ __launch_bounds__(256) void route_big_kernel(const T* __restrict__ u,
+                                                        const T* __restrict__ wr, int M, int D,
+                                                        int E, int k, int32_t* __restrict__ idx,
+                                                        float* __restrict__ wout,
+                                                        float* __restrict__ logits) {
+  constexpr int TPW = 64, TM = 4, KS = 4;
+  extern __shared__ float lg[];  // [KS][TPW][E + 1] partial logits
+  typedef typename Vec<T>::x8 F;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int tok0 = blockIdx.x * TPW;
+  const int ET = (E + 15) / 16;
+  const int ldl = E + 1;
+  const int nsteps = D / 32;
+  const int s0 = wave * nsteps / KS, s1 = (wave + 1) * nsteps / KS;
+  constexpr uint32_t ES = sizeof(T);
+  const BufRes ru = make_rsrc(u, (uint64_t)M * D * ES);
+  const BufRes rw = make_rsrc(wr, (uint64_t)E * D * ES);
+  float* mylg = lg + (size_t)wave * TPW * ldl;
+  uint32_t uoff[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = tok0 + i * 16 + c;
+    uoff[i] = row < M ? ((uint32_t)row * D + 8 * g) * ES : kOOB;
+  }
+  for (int et0 = 0; et0 < ET; et0 += GT) {
+    floatx4 acc[TM][GT];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < GT; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    uint32_t woff[GT];
+#pragma unroll
+    for (int j = 0; j < GT; ++j) {
+      const int e = (et0 + j) * 16 + c;
+      woff[j] = e < E ? ((uint32_t)e * D + 8 * g) * ES : kOOB;
+    }
+    for (int st0 = s0; st0 < s1; st0 += RB) {
+      F a[RB][TM], b[RB][GT];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const bool ok = st0 + q < s1;
+        const uint32_t k0 = 32u * (st0 + q) * ES;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          a[q][i] = load8_buf<T>(ru, (ok && uoff[i] != kOOB) ? uoff[i] + k0 : kOOB);
+#pragma unroll
+        for (int j = 0; j < GT; ++j)
+          b[q][j] = load8_buf<T>(rw, (ok && woff[j] != kOOB) ? woff[j] + k0 : kOOB);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // all of the batch's loads before its first use
+#pragma unroll
+      for (int q = 0; q < RB; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < GT; ++j) acc[i][j] = mma16(a[q][i], b[q][j], acc[i][j]);
+    }
+    // acc[i][j][q] = partial logit of token 16 i + 4g + q for expert 16 (et0 + j) + c
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < GT; ++j) {
+        const int e = (et0 + j) * 16 + c;
+        if (e < E) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) mylg[(i * 16 + 4 * g + q) * ldl + e] = acc[i][j][q];
+        }
+      }
+  }
+  __syncthreads();
+  // the slices' partial logits summed in slice order (deterministic)
+  for (int q = threadIdx.x; q < TPW * ldl; q += blockDim.x) {
+    float sacc = lg[q];
+#pragma unroll
+    for (int j = 1; j < KS; ++j) sacc += lg[(size_t)j * TPW * ldl + q];
+    lg[q] = sacc;
+  }
+  __syncthreads();
+  route_tokens(lg, ldl, tok0, TPW, M, E, k, idx, wout, logits, nullptr);
+}
+
 // Top-k and softmax of the workgroup's tokens from their logits in LDS. A
 // group of sg lanes (a power of two with E <= 4 sg) shares a token: lane sl
 // holds experts sl, sl + sg, sl + 2 sg, sl + 3 sg. Each of the k rounds takes
@@ -197,6 +288,39 @@ __device__ void route_tokens(const float* lg, int ldl, int tok0, int tpw, int M,
 hipError_t launch_route(bool is_bf16, const void* u, const void* w_router, int M, int D, int E, int k,
                         int32_t* idx, float* w, float* logits, hipStream_t s, int32_t* hist) {
   if (M == 0) return hipSuccess;
+  if (!hist && M > 1024 && E <= 64) {
+    // prefill: 64 tokens per workgroup, d_model split over the 4 waves
+    const size_t lds = (size_t)4 * 64 * (E + 1) * sizeof(float);
+    const dim3 grid((M + 63) / 64);
+    const int ET = (E + 15) / 16;
+    const void* fn;
+    if (is_bf16)
+      fn = ET > 2 ? (const void*)route_big_kernel<bf16, 4, 2>
+                  : (ET > 1 ? (const void*)route_big_kernel<bf16, 2, 2>
+                            : (const void*)route_big_kernel<bf16, 1, 2>);
+    else
+      fn = ET > 2 ? (const void*)route_big_kernel<float, 4, 1>
+                  : (ET > 1 ? (const void*)route_big_kernel<float, 2, 1>
+                            : (const void*)route_big_kernel<float, 1, 1>);
+    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    prof_begin("route_topk", s);
+#define SWIMBA_ROUTE_BIG(TT, G, RBQ)                                                           \
+  hipLaunchKernelGGL((route_big_kernel<TT, G, RBQ>), grid, dim3(256), lds, s, (const TT*)u,   \
+                     (const TT*)w_router, M, D, E, k, idx, w, logits)
+    if (is_bf16) {
+      if (ET > 2) SWIMBA_ROUTE_BIG(bf16, 4, 2);
+      else if (ET > 1) SWIMBA_ROUTE_BIG(bf16, 2, 2);
+      else SWIMBA_ROUTE_BIG(bf16, 1, 2);
+    } else {
+      if (ET > 2) SWIMBA_ROUTE_BIG(float, 4, 1);
+      else if (ET > 1) SWIMBA_ROUTE_BIG(float, 2, 1);
+      else SWIMBA_ROUTE_BIG(float, 1, 1);
+    }
+#undef SWIMBA_ROUTE_BIG
+    prof_end(s);
+    return hipGetLastError();
+  }
   const int tpw = route_tokens_per_wg(M);
   const int ET = (E + 15) / 16;
   const int GT = ET >= 4 ? 4 : (ET >= 2 ? 2 : 1);

@@ -50,6 +50,13 @@ ROUTE_CASES = [
     ("bf16_e256k8", W("r6", 107, batch=1, seqlen=96, n_experts=256, top_k=8)),
     ("bf16_e100k5", W("r7", 108, batch=2, seqlen=150, n_experts=100, top_k=5)),
     ("bf16_e40k3_m2048", W("r8", 109, batch=4, seqlen=512, n_experts=40, top_k=3)),
+    # prefill-sized batches (more than 1024 tokens): d_model split over the
+    # workgroup's waves; ragged token counts, one to four expert tiles, fp32,
+    # a d_model that splits unevenly
+    ("bf16_e16k2_m3000", W("r9", 110, batch=3, seqlen=1000, n_experts=16)),
+    ("bf16_e8k2_m2050", W("r10", 111, batch=2, seqlen=1025, n_experts=8)),
+    ("f32_e24k2_m1100", W("r11", 112, dtype=synth.F32, batch=1, seqlen=1100, n_experts=24)),
+    ("bf16_e64k2_m1280_d384", W("r12", 113, batch=1, seqlen=1280, n_experts=64, d_model=384)),
 ]
 
 
