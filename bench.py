@@ -59,7 +59,7 @@ KERNEL_NAMES = [
     (r"bwd_sweep_kernel", "scan_bwd_sweep"),
     (r"bwd_grad_kernel", "scan_bwd_grad"),
     (r"bwd_da_kernel", "scan_bwd_da"),
-    (r"route_kernel", "route_topk"),
+    (r"route_kernel|route_big_kernel", "route_topk"),
     (r"bucket_count_kernel", "bucket_count"),
     (r"bucket_place_kernel", "bucket_place"),
     # template arguments (type, tile config, PLAIN, ...): PLAIN right after the config
@@ -71,7 +71,7 @@ KERNEL_NAMES = [
     # (types, NP, KS, BT, WITH_Y, TV): WITH_Y follows the block size
     (r"scan_kernel.*Li\d+ELb0ELb[01]E", "scan_segment_state"),
     (r"scan_combine_kernel", "scan_state_pass"),
-    (r"scan_kernel.*Li\d+ELb1ELb[01]E", "scan_chunk_output"),
+    (r"scan_kernel.*Li\d+ELb1ELb[01]E|scan_walk2_kernel", "scan_chunk_output"),
     (r"state_copy_kernel", "state_copy"),
     (r"sep_scatter_kernel", "sep_scatter"),
     (r"sep_sum_kernel", "sep_sum"),
@@ -503,6 +503,102 @@ def e_sweep(args):
         open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+def library_gemm(args):
+    """The fused expert projection beside the vendor GEMM library (hipBLASLt,
+    through torch.mm) on the same shapes, for c2, c3 and c4: the library's
+    dense GEMM of all (token, slot) rows against one expert's weights (the
+    same FLOPs with no routing, gather or mix), and one library GEMM per
+    expert over an equal share of the rows (the unfused grouped form). Writes
+    a markdown table; a context for the projection's roofline fraction."""
+    import torch
+
+    from selective_ssm_parameter_amd import binding as sb
+    from selective_ssm_parameter_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / args.steps
+
+    rows = []
+    for name in ("c2", "c3", "c4"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make_inputs(wl)
+
+        def up(x, t=torch.bfloat16):
+            return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev, t)
+
+        u = up(inp["u"].reshape(wl.tokens, -1))
+        wr, we, a = up(inp["w_router"]), up(inp["w_experts"]), up(inp["a"], torch.float32)
+        del inp
+        dims = sb.dims_of(wl)
+        buf = sb.alloc_buffers(dims, dev)
+        for _ in range(args.warmup):
+            sb.forward(dims, u, wr, we, a, None, buf)
+        torch.cuda.synchronize()
+        sb.profile_select("expert_project")
+        sb.profile_enable(True)
+        for _ in range(args.steps):
+            sb.forward(dims, u, wr, we, a, None, buf)
+        torch.cuda.synchronize()
+        rep = json.loads(sb.profile_report())["expert_project"]
+        sb.profile_enable(False)
+        sb.profile_select(None)
+        ours = 1e3 * rep["ms"] / rep["launches"]
+        del buf
+        R, D, W, E = wl.tokens * wl.top_k, wl.d_model, wl.width, wl.n_experts
+        A = torch.randn(R, D, device=dev, dtype=torch.bfloat16)
+        out = torch.empty(R, W, device=dev, dtype=torch.bfloat16)
+        dense = timed(lambda: torch.mm(A, we[0].t(), out=out))
+        share = R // E
+        parts = [(A[e * share:(e + 1) * share], out[e * share:(e + 1) * share]) for e in range(E)]
+
+        def grouped():
+            for e, (ae, oe) in enumerate(parts):
+                torch.mm(ae, we[e].t(), out=oe)
+        per_expert = timed(grouped)
+        flops = 2.0 * R * D * W
+        row = {"workload": name, "rows": R, "d_model": D, "width": W, "E": E,
+               "fused_us": ours, "library_dense_us": dense, "library_per_expert_us": per_expert,
+               "fused_frac": flops / ours / 1e6 / PEAK_BF16_TFLOPS,
+               "dense_frac": flops / dense / 1e6 / PEAK_BF16_TFLOPS,
+               "per_expert_frac": flops * (share * E / R) / per_expert / 1e6 / PEAK_BF16_TFLOPS}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del u, wr, we, a, A, out, parts
+        torch.cuda.empty_cache()
+    if args.out:
+        lines = ["# Expert projection beside the vendor GEMM library", "",
+                 "Command (from the repository root, after building the library):", "",
+                 "    " + (" ".join(args.command) or "python bench.py --library-gemm"), "",
+                 "fused: `expert_project` of a prefill step (routing gather, the w-weighted "
+                 "B and C epilogue and the stream writes included), HIP events around each "
+                 "launch. library dense: one `torch.mm` (hipBLASLt) of all k M rows against "
+                 "one expert's [W, d_model] weights, bf16 out. library per expert: one "
+                 "`torch.mm` per expert over M k / E rows each. Fractions of the 2500 "
+                 f"TFLOP/s dense bf16 peak; {args.steps} timed calls after {args.warmup} "
+                 "warm-up calls.", "",
+                 "| workload | rows k M | d_model | W | E | fused us | frac | library dense us "
+                 "| frac | library per expert us | frac |",
+                 "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for r in rows:
+            lines.append(f"| {r['workload']} | {r['rows']} | {r['d_model']} | {r['width']} | "
+                         f"{r['E']} | {r['fused_us']:.1f} | {r['fused_frac']:.3f} | "
+                         f"{r['library_dense_us']:.1f} | {r['dense_frac']:.3f} | "
+                         f"{r['library_per_expert_us']:.1f} | {r['per_expert_frac']:.3f} |")
+        open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 SEP_POINTS = [(2, 2), (4, 2), (8, 2), (16, 2), (32, 2), (8, 1), (8, 4)]
 
 
@@ -862,6 +958,84 @@ def summarize_pmc(fetch_dir, write_dir, wl_name, out, commands):
     print("\n".join(lines))
 
 
+# Counter passes of the SQ summary (each within one rocprofv3 --pmc run's
+# hardware limits: at most 8 SQ, 2 TA and 2 GRBM counters).
+SQ_PASSES = [
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 "
+    "SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAVES GRBM_GUI_ACTIVE",
+    "SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT "
+    "SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA "
+    "TA_TA_BUSY GRBM_GUI_ACTIVE",
+]
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def summarize_sq(dirs, wl_name, out, commands):
+    """Matrix-core and issue counters per kernel from rocprofv3 --pmc runs of
+    the SQ_PASSES sets: per-dispatch averages, and the derived figures
+    (MFMA busy per SIMD, the clock the run held, instruction mix per wave,
+    issue stalls, LDS read rate, texture-unit busy)."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(list)
+    for d in dirs:
+        seen = set()
+        for r in csv.DictReader(open(find_csv(d, "counter_collection.csv"))):
+            lab = kernel_label(r["Kernel_Name"])
+            wgs = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+            key = (lab, wgs)
+            vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            did = (d, r["Dispatch_Id"])
+            if did not in seen:
+                seen.add(did)
+                durs[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    mean = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    base, mixed, backward = parse_key(wl_name)
+    lines = [f"# Matrix-core and issue counters per kernel, bench step (prefill) on workload "
+             f"{base}", "", "Commands (from the repository root, after building the library):",
+             ""] + ["    " + c for c in commands] + [
+        "", "Per-dispatch averages over the profiled steps. Derived: clock = GRBM_GUI_ACTIVE "
+        f"per XCD / duration (kernels of 50 us or more); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles x {N_SIMD} "
+        "SIMDs); MFMA TFLOP/s = 512 x (MOPS_BF16 + MOPS_F16) / duration; issue stall = "
+        "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave-cycles waiting to issue); LDS read B/clk/CU "
+        f"= 64 x SQ_INSTS_LDS_LOAD_BANDWIDTH / (GUI cycles x {N_CU}); TA busy = TA_TA_BUSY / "
+        f"(GUI cycles x {N_CU}). Durations come from the counter runs (kernels serialised).",
+        "", "| kernel | WGs | us | clock GHz | MFMA busy | MFMA TFLOP/s | MFMA / wave | "
+        "VALU / wave | SALU / wave | LDS / wave | issue stall | LDS-wait share | "
+        "LDS read B/clk/CU | LDS bank-conflict cycles | TA busy |",
+        "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    order = sorted(mean, key=lambda k: -sum(durs[k]) / max(1, len(durs[k])))
+    for key in order:
+        m = mean[key]
+        dur = sum(durs[key]) / len(durs[key])
+        gui = m.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        if dur < 2.0 or gui <= 0:
+            continue
+        waves = max(1.0, m.get("SQ_WAVES", 1.0))
+
+        def g(c, f=lambda x: x, fmt="{:.3g}"):
+            return fmt.format(f(m[c])) if c in m else "-"
+        mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + m.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        wc = m.get("SQ_WAVE_CYCLES", 0.0)
+        lines.append(
+            f"| {key[0]} | {key[1]} | {dur:.1f} | "
+            + (f"{gui / dur / 1e3:.2f}" if dur >= 50 else "-") + " | "
+            + g("SQ_VALU_MFMA_BUSY_CYCLES", lambda x: 100 * x / (gui * N_SIMD), "{:.1f}%") + " | "
+            + f"{512 * mops / dur / 1e6:.0f} | "
+            + g("SQ_INSTS_MFMA", lambda x: x / waves, "{:.0f}") + " | "
+            + g("SQ_INSTS_VALU", lambda x: x / waves, "{:.0f}") + " | "
+            + g("SQ_INSTS_SALU", lambda x: x / waves, "{:.0f}") + " | "
+            + g("SQ_INSTS_LDS", lambda x: x / waves, "{:.0f}") + " | "
+            + (g("SQ_WAIT_INST_ANY", lambda x: 100 * x / wc, "{:.0f}%") if wc else "-") + " | "
+            + (g("SQ_WAIT_INST_LDS", lambda x: 100 * x / wc, "{:.0f}%") if wc else "-") + " | "
+            + g("SQ_INSTS_LDS_LOAD_BANDWIDTH", lambda x: 64 * x / (gui * N_CU), "{:.1f}") + " | "
+            + g("SQ_LDS_BANK_CONFLICT", lambda x: x, "{:.3g}") + " | "
+            + g("TA_TA_BUSY", lambda x: 100 * x / (gui * N_CU), "{:.0f}%") + " |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -880,6 +1054,9 @@ def main():
                     help="write a markdown summary of a rocprofv3 kernel-trace run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary of two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
+                    help="write the matrix-core / issue counter summary of rocprofv3 --pmc "
+                         "runs of the SQ_PASSES counter sets")
     ap.add_argument("--out", help="summary file to write")
     ap.add_argument("--output-projection", action="store_true",
                     help="time the output projection alone on the --config workload")
@@ -888,6 +1065,9 @@ def main():
     ap.add_argument("--separated", action="store_true",
                     help="tokens/s of the MoE over separated SSMs beside Swimba's, at the c2 "
                          "dimensions for several E and k")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="the expert projection beside hipBLASLt (torch.mm) on the c2, c3 and "
+                         "c4 shapes")
     ap.add_argument("--bench-json", help="the JSON output of the profiled bench run")
     ap.add_argument("--command", action="append", default=[],
                     help="the command(s) that produced the profile, for the summary")
@@ -897,6 +1077,11 @@ def main():
         summarize_trace(args.summarize_trace, key,
                         args.out or os.path.join(PROFILES, f"swimba_step_{key}_kernel_trace.md"),
                         " ".join(args.command), args.bench_json)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, key,
+                     args.out or os.path.join(PROFILES, f"swimba_step_{key}_sq_counters.md"),
+                     args.command)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], key,
@@ -916,6 +1101,9 @@ def main():
         return
     if args.output_projection:
         output_projection(args)
+        return
+    if args.library_gemm:
+        library_gemm(args)
         return
     r = run_gpu(args)
     wl = r["wl"]

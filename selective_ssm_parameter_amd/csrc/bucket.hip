@@ -71,15 +71,29 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(
   for (int e = threadIdx.x; e < EP; e += blockDim.x) { before[e] = 0; total[e] = 0; }
   for (int e = threadIdx.x; e < 4 * EP; e += blockDim.x) wcnt[e] = 0;
   __syncthreads();
+  // bucket e's counts of blocks b0, b0 + step, ...: loads issued 8 at a time
+  // (a thread walks nblk / nparts blocks; one load in flight at a time made
+  // this loop's latency grow with E)
+  auto column = [&](int e, int b0, int step, int& sb, int& st) {
+    for (int b = b0; b < nblk; b += 8 * step) {
+      int v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int bq = b + q * step;
+        v[q] = bq < nblk ? counts[(size_t)bq * EP + e] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        st += v[q];
+        sb += b + q * step < blk ? v[q] : 0;
+      }
+    }
+  };
   {
     const int part = threadIdx.x / EP, e = threadIdx.x % EP;
     if (part < nparts) {
       int sb = 0, st = 0;
-      for (int b = part; b < nblk; b += nparts) {
-        const int v = counts[(size_t)b * EP + e];
-        st += v;
-        sb += b < blk ? v : 0;
-      }
+      column(e, part, nparts, sb, st);
       atomicAdd(&before[e], sb);
       atomicAdd(&total[e], st);
     }
@@ -87,11 +101,7 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(
       for (int e2 = threadIdx.x; e2 < EP; e2 += blockDim.x) {
         if (e2 < 256) continue;
         int sb = 0, st = 0;
-        for (int b = 0; b < nblk; ++b) {
-          const int v = counts[(size_t)b * EP + e2];
-          st += v;
-          sb += b < blk ? v : 0;
-        }
+        column(e2, 0, 1, sb, st);
         before[e2] = sb;
         total[e2] = st;
       }

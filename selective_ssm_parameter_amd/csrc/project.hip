@@ -77,9 +77,19 @@ struct ProjLay {
 // by the bucketing kernel after the tile table) spreads them over all XCDs, so
 // no XCD is left with only empty slots. Returns false for a workgroup without
 // a unit.
+// GR (environment SWIMBA_PROJ_GR, read once; default 4) matters little on
+// MI355X: 4 x 8192 tokens, E = 16: GR 1, 2, 4, 8, 16 took 1158, 1134, 1129,
+// 1140, 1149 us; 65536 tokens, E = 8: GR 4 636 us, GR 8 613 us.
 constexpr int kProjGroupRows = 4;
-template <int GR>
-__device__ __forceinline__ bool xcd_unit(int nt, int CT, int& tile, int& ctile) {
+static int proj_group_rows() {
+  static const int g = [] {
+    const char* v = getenv("SWIMBA_PROJ_GR");
+    const int x = v ? atoi(v) : 0;
+    return x > 0 ? x : kProjGroupRows;
+  }();
+  return g;
+}
+__device__ __forceinline__ bool xcd_unit(int GR, int nt, int CT, int& tile, int& ctile) {
   const int units = nt * CT;
   const int per = (units + 7) / 8;
   const int slot = blockIdx.x / 8;
@@ -93,10 +103,9 @@ __device__ __forceinline__ bool xcd_unit(int nt, int CT, int& tile, int& ctile) 
   tile = group * GR + (rem - ctile * gm);
   return true;
 }
-template <int GR>
-__device__ __forceinline__ bool xcd_tile(const int4v* __restrict__ tile_info, int nrow_tiles,
-                                         int CT, int& tile, int& ctile) {
-  return xcd_unit<GR>(tile_info[nrow_tiles][0], CT, tile, ctile);
+__device__ __forceinline__ bool xcd_tile(int GR, const int4v* __restrict__ tile_info,
+                                         int nrow_tiles, int CT, int& tile, int& ctile) {
+  return xcd_unit(GR, tile_info[nrow_tiles][0], CT, tile, ctile);
 }
 
 // PLAIN: the same kernel as a plain GEMM out[M, W] = u[M, D] wexp[W, D]^T (the
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
     const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
     int HP, int GN, int k, int nrow_tiles, typename StreamOf<T>::type* __restrict__ X_hat,
     typename StreamOf<T>::type* __restrict__ B_hat, float* __restrict__ c_part,
-    TO* __restrict__ out, int bw_one) {
+    TO* __restrict__ out, int bw_one, int gr) {
   typedef typename StreamOf<T>::type S;
   typedef ProjLay<T, C> Lay;
   constexpr int BM = C::BM, BN = C::BN, NTH = C::NTH, NW = C::NW, TM = C::TM, TN = C::TN;
@@ -131,12 +140,12 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
   const int CT = (W + BN - 1) / BN;
   int tile, ctile, e, row0, nrows;
   if constexpr (PLAIN) {
-    if (!xcd_unit<kProjGroupRows>(nrow_tiles, CT, tile, ctile)) return;
+    if (!xcd_unit(gr, nrow_tiles, CT, tile, ctile)) return;
     e = 0;
     row0 = tile * BM;
     nrows = min(BM, M - row0);
   } else {
-    if (!xcd_tile<kProjGroupRows>(tile_info, nrow_tiles, CT, tile, ctile)) return;
+    if (!xcd_tile(gr, tile_info, nrow_tiles, CT, tile, ctile)) return;
     const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
     e = ti[0];
     if (e < 0) return;
@@ -370,7 +379,7 @@ __global__ __launch_bounds__(256) void proj_skinny_kernel(
 
   const int CT = (W + kSkBN - 1) / kSkBN;
   int tile, ctile;
-  if (!xcd_tile<1>(tile_info, nrow_tiles, CT, tile, ctile)) return;
+  if (!xcd_tile(1, tile_info, nrow_tiles, CT, tile, ctile)) return;
   const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
   const int e = ti[0];
   if (e < 0) return;
@@ -538,11 +547,11 @@ static hipError_t launch_proj_cfg(const ProjGeom& g, const T* u, const T* wexp,
   if (g.D % (kProjStages * ProjLay<T, C>::BK) == 0)
     hipLaunchKernelGGL((proj_kernel<T, C, false, float, true>), grid, dim3(C::NTH), 0, s, u, wexp,
                        sorted, sorted_w, tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow,
-                       X_hat, B_hat, c_part, (float*)nullptr, g.bw_one);
+                       X_hat, B_hat, c_part, (float*)nullptr, g.bw_one, proj_group_rows());
   else
     hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, u, wexp, sorted, sorted_w,
                        tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part,
-                       (float*)nullptr, g.bw_one);
+                       (float*)nullptr, g.bw_one, proj_group_rows());
   prof_end(s);
   return hipGetLastError();
 }
@@ -601,11 +610,13 @@ static hipError_t launch_outproj_cfg(int M, int K, int N, const T* y, const T* w
   if (K % (kProjStages * ProjLay<T, C>::BK) == 0)
     hipLaunchKernelGGL((proj_kernel<T, C, true, T, true>), grid, dim3(C::NTH), 0, s, y, w,
                        (const int32_t*)nullptr, (const float*)nullptr, (const int4v*)nullptr, M, K,
-                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out, 0);
+                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out, 0,
+                       proj_group_rows());
   else
     hipLaunchKernelGGL((proj_kernel<T, C, true, T>), grid, dim3(C::NTH), 0, s, y, w,
                        (const int32_t*)nullptr, (const float*)nullptr, (const int4v*)nullptr, M, K,
-                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out, 0);
+                       N, 0, 0, 1, nrow, (S*)nullptr, (S*)nullptr, (float*)nullptr, out, 0,
+                       proj_group_rows());
   prof_end(s);
   return hipGetLastError();
 }
