@@ -746,10 +746,19 @@ swimba_status decode_impl(bool mixed, const swimba_dims* dims, const void* u,
   d1.M = d.Bt;
   const ProjWs play = proj_ws(d1);
   unsigned char* pws = w8 + lay.proj;
+  // bf16 batches whose experts get a few dozen pairs each: the skinny
+  // projection finds every expert's pairs in idx itself (no bucketing launch)
+  const int pairs = (int)(d.Bt * d.k);
+  const bool direct = d.bf16 && proj_bm(pairs, (int)d.E) == 64 && pairs <= proj_direct_max_pairs();
   hipError_t e = launch_route(d.bf16, u, w_router, (int)d.Bt, (int)d.D, (int)d.E, (int)d.k, idx,
-                              tw, nullptr, stream, reinterpret_cast<int32_t*>(pws + play.counts));
+                              tw, nullptr, stream,
+                              direct ? nullptr : reinterpret_cast<int32_t*>(pws + play.counts));
   if (e != hipSuccess) return hip_status(e, "decode_step route launch");
-  e = run_project(d, d.Bt, u, w_experts, idx, tw, bhat, xhat, nullptr, pws, stream, true);
+  if (direct)
+    e = launch_project_direct(proj_geom(d, d.Bt), u, w_experts, idx, tw, bhat, xhat,
+                              reinterpret_cast<float*>(pws + play.cpart), stream);
+  else
+    e = run_project(d, d.Bt, u, w_experts, idx, tw, bhat, xhat, nullptr, pws, stream, true);
   if (e != hipSuccess) return hip_status(e, "decode_step projection launch");
   e = launch_decode_state(d.bf16, (int)d.Bt, (int)d.H, (int)d.G, (int)d.N, (int)d.P, (int)d.k,
                           bhat, xhat, reinterpret_cast<const float*>(pws + play.cpart), a, h, y,

@@ -47,6 +47,13 @@ hipError_t launch_bucket(bool is_bf16, const int32_t* idx, const float* topk_w, 
 int proj_row_tiles_max(int pairs, int E, int bm);
 int proj_bm(int pairs, int E);
 // C_mix == nullptr skips the slot sum (the caller consumes c_part itself).
+// Decode batches (bf16, at most proj_direct_max_pairs() pairs): the skinny
+// projection with every workgroup finding its expert's pairs in idx itself,
+// with no bucketing launch before it.
+int proj_direct_max_pairs();
+hipError_t launch_project_direct(const ProjGeom& g, const void* u, const void* w_experts,
+                                 const int32_t* idx, const float* topk_w, void* B_hat,
+                                 void* X_hat, float* c_part, hipStream_t s);
 hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const void* w_experts,
                           const int32_t* sorted, const float* sorted_w, const int32_t* tile_info,
                           int bm, void* B_hat, void* X_hat, float* c_part, void* C_mix,

@@ -364,11 +364,22 @@ constexpr int kSkSteps = kSkKC / 32;   // K steps per token-row chunk
 constexpr int kSkGroup = 2 * kSkSteps;  // K steps per weight burst (two chunks)
 constexpr int kSkRowB = kSkKC * 2;      // LDS bytes per token row of a chunk
 
-__global__ __launch_bounds__(256) void proj_skinny_kernel(
+// DIRECT (decode batches of at most kSkDirectPairs pairs): no bucketing
+// launch. A workgroup owns one expert and kSkBN columns; it finds its
+// expert's pairs itself by reading the router's idx (all of it, a few KiB
+// from L2), in pair order (wave ballots, then wave order), and walks them in
+// row tiles of 64. Otherwise a workgroup owns one row tile of the bucketing
+// kernel's schedule.
+constexpr int kSkDirectPairs = 4096;
+int proj_direct_max_pairs() { return kSkDirectPairs; }
+
+template <bool DIRECT>
+__global__ __launch_bounds__(256, 3) void proj_skinny_kernel(
     const bf16* __restrict__ u, const bf16* __restrict__ wexp, const int32_t* __restrict__ sorted,
     const float* __restrict__ sorted_w, const int4v* __restrict__ tile_info, int M, int D, int W,
     int HP, int GN, int k, int nrow_tiles, f16* __restrict__ X_hat, f16* __restrict__ B_hat,
-    float* __restrict__ c_part, int bw_one) {
+    float* __restrict__ c_part, int bw_one, const int32_t* __restrict__ idx,
+    const float* __restrict__ topk_w, int E) {
   typedef bf16x8 F;
   // chunk rows: 16-byte piece ch of row r at piece ch ^ (r % 16)
   __shared__ __align__(16) unsigned char abuf0[64 * kSkRowB];
@@ -376,42 +387,105 @@ __global__ __launch_bounds__(256) void proj_skinny_kernel(
   __shared__ int rtok[64];
   __shared__ int rslot[64];
   __shared__ float rw[64];
+  constexpr int NPL = DIRECT ? kSkDirectPairs : 1;
+  __shared__ int plist[NPL];  // DIRECT: the expert's pair ids, ascending
+  __shared__ int wcnt[16];
 
   const int CT = (W + kSkBN - 1) / kSkBN;
-  int tile, ctile;
-  if (!xcd_tile(1, tile_info, nrow_tiles, CT, tile, ctile)) return;
-  const int4v ti = tile_info[tile];  // {expert, first sorted row, rows}
-  const int e = ti[0];
-  if (e < 0) return;
-  const int row0 = ti[1], nrows = ti[2];
-  if (threadIdx.x < 64) {
-    const int r = threadIdx.x;
-    if (r < nrows) {
-      const int p = sorted[row0 + r];
-      rtok[r] = p / k;
-      rslot[r] = p - (p / k) * k;
-      rw[r] = sorted_w[row0 + r];
-    } else {
-      rtok[r] = -1;
-      rslot[r] = 0;
-      rw[r] = 0.f;
-    }
-  }
-  __syncthreads();
-
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int ctile, e, nrt, total = 0;
+  int4v ti = int4v{0, 0, 0, 0};
+  if constexpr (DIRECT) {
+    if (!xcd_unit(1, E, CT, e, ctile)) return;
+    // rounds of 1024 pairs: p = r0 + 256 i + threadIdx.x, the round's four
+    // loads issued before their first use
+    const int pairs = M * k;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    int run = 0;
+    for (int r0 = 0; r0 < pairs; r0 += 1024) {
+      int hit[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = r0 + 256 * i + threadIdx.x;
+        hit[i] = p < pairs ? idx[p] : -1;
+      }
+      uint64_t bal[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bal[i] = __ballot(hit[i] == e);
+        if (lane == 0) wcnt[4 * i + wave] = __popcll(bal[i]);
+      }
+      __syncthreads();
+      // rank = hits of earlier rounds and quarters, earlier waves of this
+      // quarter, earlier lanes of this wave
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int before = run;
+        for (int w2 = 0; w2 < wave; ++w2) before += wcnt[4 * i + w2];
+        if (hit[i] == e) plist[before + __popcll(bal[i] & below)] = r0 + 256 * i + threadIdx.x;
+        run += wcnt[4 * i] + wcnt[4 * i + 1] + wcnt[4 * i + 2] + wcnt[4 * i + 3];
+      }
+      __syncthreads();  // wcnt is rewritten by the next round
+    }
+    total = run;
+    nrt = (total + 63) / 64;
+  } else {
+    int tile;
+    if (!xcd_tile(1, tile_info, nrow_tiles, CT, tile, ctile)) return;
+    ti = tile_info[tile];  // {expert, first sorted row, rows}
+    e = ti[0];
+    if (e < 0) return;
+    nrt = 1;
+  }
+
   const int g = lane >> 4, c = lane & 15;
   const int col0 = ctile * kSkBN + 16 * wave;  // W is a multiple of 16: whole waves drop out
   const bool active = col0 < W;
   const int nsteps = D / 32;
   const int ngroups = (nsteps + kSkGroup - 1) / kSkGroup;
-
   const BufRes rA = make_rsrc(u, (uint64_t)M * D * 2);
   const BufRes rW = make_rsrc(wexp + (size_t)e * W * D, (uint64_t)W * D * 2);
   // weights: lane (g, c) reads column col0 + c, elements 32 s + 8 g .. + 7 of
   // K step s; steps past d read zeros
   const uint32_t wbase = active ? ((uint32_t)(col0 + c) * D + 8 * g) * 2 : kOOB;
+
+  for (int rt = 0; rt < nrt; ++rt) {
+  int nrows;
+  if constexpr (DIRECT) {
+    nrows = min(64, total - 64 * rt);
+    if (threadIdx.x < 64) {
+      const int r = threadIdx.x;
+      if (r < nrows) {
+        const int p = plist[64 * rt + r];
+        rtok[r] = p / k;
+        rslot[r] = p - (p / k) * k;
+        rw[r] = topk_w[p];
+      } else {
+        rtok[r] = -1;
+        rslot[r] = 0;
+        rw[r] = 0.f;
+      }
+    }
+  } else {
+    const int row0 = ti[1];
+    nrows = ti[2];
+    if (threadIdx.x < 64) {
+      const int r = threadIdx.x;
+      if (r < nrows) {
+        const int p = sorted[row0 + r];
+        rtok[r] = p / k;
+        rslot[r] = p - (p / k) * k;
+        rw[r] = sorted_w[row0 + r];
+      } else {
+        rtok[r] = -1;
+        rslot[r] = 0;
+        rw[r] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
   F wq[2 * kSkGroup];  // two bursts: the group in use and the next one
   auto burst = [&](auto par, int grp) {
     constexpr int PAR = decltype(par)::value;
@@ -491,28 +565,31 @@ __global__ __launch_bounds__(256) void proj_skinny_kernel(
 
   // ---- epilogue: acc[i] holds, in lane (g, c), columns col0 + 4g .. + 3 of
   // pair row 16 i + c (H*P and G*N are multiples of 16: no region straddles)
-  if (!active) return;
-  const int col = col0 + 4 * g;
+  if (active) {
+    const int col = col0 + 4 * g;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * i + c;
-    if (r >= nrows) continue;
-    const size_t pair = (size_t)rtok[r] * k + rslot[r];
-    const float wv = rw[r];
-    const floatx4 v = acc[i];
-    if (col < HP) {
-      f16x4 o;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * i + c;
+      if (r >= nrows) continue;
+      const size_t pair = (size_t)rtok[r] * k + rslot[r];
+      const float wv = rw[r];
+      const floatx4 v = acc[i];
+      if (col < HP) {
+        f16x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = from_f32<f16>(v[q]);
-      *reinterpret_cast<f16x4*>(&X_hat[pair * HP + col]) = o;
-    } else if (col < HP + GN) {
-      f16x4 o;
+        for (int q = 0; q < 4; ++q) o[q] = from_f32<f16>(v[q]);
+        *reinterpret_cast<f16x4*>(&X_hat[pair * HP + col]) = o;
+      } else if (col < HP + GN) {
+        f16x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = from_f32<f16>((bw_one ? 1.f : wv) * v[q]);
-      *reinterpret_cast<f16x4*>(&B_hat[pair * GN + (col - HP)]) = o;
-    } else {
-      *reinterpret_cast<floatx4*>(&c_part[pair * GN + (col - HP - GN)]) = v * wv;
+        for (int q = 0; q < 4; ++q) o[q] = from_f32<f16>((bw_one ? 1.f : wv) * v[q]);
+        *reinterpret_cast<f16x4*>(&B_hat[pair * GN + (col - HP)]) = o;
+      } else {
+        *reinterpret_cast<floatx4*>(&c_part[pair * GN + (col - HP - GN)]) = v * wv;
+      }
     }
+  }
+  __syncthreads();  // the next row tile rewrites the row table and both chunk buffers
   }
 }
 
@@ -570,9 +647,10 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
       const int nrow = proj_row_tiles_max(g.M * g.k, g.E, 64);
       const int ntiles = nrow * ((g.W + kSkBN - 1) / kSkBN);
       prof_begin("expert_project", s);
-      hipLaunchKernelGGL(proj_skinny_kernel, dim3((unsigned)((ntiles + 7) / 8 * 8)), dim3(256), 0,
-                         s, u, wexp, sorted, sorted_w, ti, g.M, g.D, g.W, g.HP(), g.GN(), g.k,
-                         nrow, X_hat, B_hat, c_part, g.bw_one);
+      hipLaunchKernelGGL(proj_skinny_kernel<false>, dim3((unsigned)((ntiles + 7) / 8 * 8)),
+                         dim3(256), 0, s, u, wexp, sorted, sorted_w, ti, g.M, g.D, g.W, g.HP(),
+                         g.GN(), g.k, nrow, X_hat, B_hat, c_part, g.bw_one,
+                         (const int32_t*)nullptr, (const float*)nullptr, g.E);
       prof_end(s);
       err = hipGetLastError();
     } else if (bm == 256)
@@ -637,6 +715,20 @@ hipError_t launch_output_project(bool is_bf16, int M, int K, int N, const void* 
   float* of = static_cast<float*>(out);
   if (M >= 512) return launch_outproj_cfg<float, ProjMid>(M, K, N, yf, wf, of, s);
   return launch_outproj_cfg<float, ProjSmall>(M, K, N, yf, wf, of, s);
+}
+
+hipError_t launch_project_direct(const ProjGeom& g, const void* u, const void* w_experts,
+                                 const int32_t* idx, const float* topk_w, void* B_hat,
+                                 void* X_hat, float* c_part, hipStream_t s) {
+  if (g.M == 0) return hipSuccess;
+  const int units = g.E * ((g.W + kSkBN - 1) / kSkBN);
+  prof_begin("expert_project", s);
+  hipLaunchKernelGGL(proj_skinny_kernel<true>, dim3((unsigned)((units + 7) / 8 * 8)), dim3(256),
+                     0, s, (const bf16*)u, (const bf16*)w_experts, (const int32_t*)nullptr,
+                     (const float*)nullptr, (const int4v*)nullptr, g.M, g.D, g.W, g.HP(), g.GN(),
+                     g.k, 0, (f16*)X_hat, (f16*)B_hat, c_part, g.bw_one, idx, topk_w, g.E);
+  prof_end(s);
+  return hipGetLastError();
 }
 
 hipError_t launch_project(bool is_bf16, const ProjGeom& g, const void* u, const void* w_experts,
