@@ -450,7 +450,21 @@ __global__ __launch_bounds__(256, 3) void proj_skinny_kernel(
   // K step s; steps past d read zeros
   const uint32_t wbase = active ? ((uint32_t)(col0 + c) * D + 8 * g) * 2 : kOOB;
 
+  F wq[2 * kSkGroup];  // two bursts: the group in use and the next one
+  auto burst = [&](auto par, int grp) {
+    constexpr int PAR = decltype(par)::value;
+#pragma unroll
+    for (int j = 0; j < kSkGroup; ++j) {
+      const int s = kSkGroup * grp + j;
+      wq[kSkGroup * PAR + j] =
+          load8_buf<bf16>(rW, (wbase == kOOB || s >= nsteps) ? kOOB : wbase + 64u * s);
+    }
+  };
+
   for (int rt = 0; rt < nrt; ++rt) {
+  // the row tile's first weight burst does not depend on its rows: it is in
+  // flight while the row table is filled
+  burst(std::integral_constant<int, 0>(), 0);
   int nrows;
   if constexpr (DIRECT) {
     nrows = min(64, total - 64 * rt);
@@ -486,16 +500,6 @@ __global__ __launch_bounds__(256, 3) void proj_skinny_kernel(
   }
   __syncthreads();
 
-  F wq[2 * kSkGroup];  // two bursts: the group in use and the next one
-  auto burst = [&](auto par, int grp) {
-    constexpr int PAR = decltype(par)::value;
-#pragma unroll
-    for (int j = 0; j < kSkGroup; ++j) {
-      const int s = kSkGroup * grp + j;
-      wq[kSkGroup * PAR + j] =
-          load8_buf<bf16>(rW, (wbase == kOOB || s >= nsteps) ? kOOB : wbase + 64u * s);
-    }
-  };
   // token rows: thread t copies pieces q = t + 256 m of a chunk's 64 x 16 pieces
   uint32_t abase[4];
   int apiece[4], alds[4];
@@ -553,7 +557,6 @@ __global__ __launch_bounds__(256, 3) void proj_skinny_kernel(
     awrite(abuf0);
     __syncthreads();  // chunk 2 grp + 2 visible; abuf1 no longer read
   };
-  burst(std::integral_constant<int, 0>(), 0);
   aload(0);
   awrite(abuf0);
   __syncthreads();
