@@ -37,6 +37,8 @@
 // row, after all readouts of the chunk have used the entering state.
 #include <cstdlib>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_tiles.hpp"
@@ -128,7 +130,8 @@ template <typename T, int NP, int KS, int BT>
 __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_hat,
                                                         const T* __restrict__ C_mix,
                                                         T* __restrict__ gram, int Tlen, int G,
-                                                        int N, int L, int nc, int npairs, int Bt) {
+                                                        int N, int L, int nc, int npairs, int Bt,
+                                                        int subb) {
   constexpr int R = KS * BT, TT = BT / 16, RT = R / 16;
   constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
@@ -146,6 +149,8 @@ __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_
   const int sig = pidx - tau * (tau + 1) / 2;
   const int c0 = ch * L, Lc = min(L, Tlen - c0);
   if (tau * BT >= Lc) return;  // block beyond the (last, partial) chunk
+  // subb > 0: the walk reads only pairs within sub-chunks of subb blocks
+  if (subb > 0 && tau / subb != sig / subb) return;
   const int GN = G * N;
   const BufRes rB = make_rsrc(B_hat + (size_t)b * Tlen * KS * GN, (uint64_t)Tlen * KS * GN * ES);
   const BufRes rC = make_rsrc(C_mix + (size_t)b * Tlen * GN, (uint64_t)Tlen * GN * ES);
@@ -642,15 +647,6 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 && KS <= 2 ? 2 : 1) vo
   }
 }
 
-// The output walk with two heads per workgroup (8 waves) and a ring of three
-// LDS stages: the copies of step s + 2 are issued while step s computes, so
-// every tile has two steps to arrive (with one head per workgroup and two
-// stages, a step's compute was shorter than the HBM latency of the next
-// step's X tile, and the walk waited on it). The two heads share one group's
-// B_hat, C~ and Gram tiles, copied once into the stage for both; each head's
-// X tile is copied by its own four waves. Per chunk, the entering state's
-// fp16 operand of the readout is formed once (it does not change until the
-// chunk's carry). The arithmetic is that of scan_kernel (pass 3).
 // N copies that read nothing (an offset past the buffer) and write 4-byte
 // zeros into `sink` (256 bytes of LDS): they keep a wave's count of copies in
 // flight fixed when a step needs fewer tiles.
@@ -663,21 +659,87 @@ __device__ __forceinline__ void dma_dummies(BufRes rs, unsigned char* sink) {
   }
 }
 
-template <typename T, int NP, int KS, int BT>
-struct Walk2Lds {
-  static constexpr int HPW = 2;  // heads per workgroup
+// The output walk by source block, two heads per workgroup (8 waves; the
+// heads share one copy of the group's B_hat, C~ and Gram tiles). A chunk is
+// walked in sub-chunks of NBM blocks of BT tokens (kRowsSub = 64 tokens; the
+// SSD decomposition is exact for any chunk length, and the Gram kernel then
+// computes only the block pairs inside sub-chunks). Step sig of a sub-chunk
+// brings block sig's X_hat rows (both heads), B_hat rows, C~ rows and the
+// Gram tiles (tau, sig) of the blocks tau >= sig, and computes
+//   the readout of block sig from the sub-chunk's entering state,
+//   the intra term of block sig into every y block tau >= sig (the
+//     accumulators of the sub-chunk's blocks stay in registers),
+//   the carry of block sig into the state;
+// y block sig is then complete. Against a walk over block pairs: one step per
+// block instead of one per block pair, each X_hat and B_hat block copied once,
+// and, since every block's carry goes into the state anyway, block pairs
+// across sub-chunks cost one readout each instead of an intra term (per 128
+// tokens and wave 116 matrix-core ops instead of 136). The steps of a
+// sub-chunk are unrolled with sig a compile-time constant, so every
+// accumulator index is one (a run-time block index made the compiler move the
+// accumulators to scratch), and with NBM even the LDS stage of every step is
+// fixed too. Two stages: the copies of the next step are in flight while a
+// step computes. 128-token sub-chunks (10 block pairs per 4 steps, twice the
+// accumulators) spilled registers and ran at half the speed.
+constexpr int kRowsSub = 64;
+constexpr int kRowsThreads = 512;
+// load_kmajor with each read's lane offset made opaque to the optimiser, so
+// the LDS address is one step from the tile base: the LDS lowering gives an
+// access its alias scope only within a few address steps of the variable,
+// and a transposing read without one is taken to alias every copy in flight
+// (the compiler then waits for all of them before it)
+template <typename T, int CPR>
+__device__ __forceinline__ typename Vec<T>::x8 load_kmajor_flat(const unsigned char* tile, int k0,
+                                                                int col0, int lane) {
+  typedef typename Vec<T>::x8 F;
+  static_assert(sizeof(T) == 2, "2-byte streams");
+  typedef short s4 __attribute__((__vector_size__(8)));
+  const int g = lane >> 4, c = lane & 15;
+  F v;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = k0 + 8 * g + 4 * hh + (c >> 2);
+    const int col = col0 + 4 * (c & 3);
+    const int ch = col >> 3, half = (col >> 2) & 1;
+    int off = (r * CPR + (ch ^ swz_tr<T, CPR>(r))) * 16 + 8 * half;
+    asm("" : "+v"(off));
+    const typename Vec<T>::x4 w4 = __builtin_bit_cast(
+        typename Vec<T>::x4,
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(tile + off)));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) v[4 * hh + m] = w4[m];
+  }
+  return v;
+}
+// f(integral_constant<int, I>) for I = I0 .. N-1
+template <int I, int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <typename T, int NP, int KS, int BT, int NBM>
+struct RowsLds {
+  static constexpr int HPW = 2;
   static constexpr int R = KS * BT;
   static constexpr int XROW = kP * (int)sizeof(T), BROW = NP * (int)sizeof(T);
   static constexpr int GROW = R * (int)sizeof(T);
   static constexpr int XB = R * XROW, BB = R * BROW, CB = BT * BROW, GB = BT * GROW;
   static constexpr int XO = 0, BO = HPW * XB, CO = BO + BB, GO = CO + CB;
-  static constexpr int STAGE = GO + GB;
+  static constexpr int STAGE = GO + NBM * GB;
 };
-constexpr int kWalk2Threads = 512;
 
-template <typename T, typename TY, int NP, int KS, int BT>
-__global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A) {
-  typedef Walk2Lds<T, NP, KS, BT> Lay;
+// (chunk, sub-chunk) of the walk by source block
+struct SubChunk {
+  int ch, half;
+};
+
+template <typename T, typename TY, int NP, int KS, int BT, int NBM>
+__global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) {
+  static_assert(NBM % 2 == 0, "an even number of steps per sub-chunk keeps each step's stage fixed");
+  typedef RowsLds<T, NP, KS, BT, NBM> Lay;
   constexpr int R = Lay::R;
   constexpr int TT = BT / 16, RQ = R / 32, NT = NP / 16, NQ = NP / 32;
   constexpr int XC = Lay::XROW / 16, BC = Lay::BROW / 16, GC = Lay::GROW / 16;
@@ -685,19 +747,21 @@ __global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A
   constexpr int NDF = DF::count() > 0 ? DF::count() : 1;
   constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
-  // copy instructions per wave and tile (X by the head's 4 waves, the shared
-  // tiles by all 8)
   constexpr int CX = dma_count<2 * R, XC, 8>(), CBn = dma_count<R, BC, 8>();
-  constexpr int CCn = dma_count<BT, BC, 8>(), CG = dma_count<BT, GC, 8>();
+  // the step's Gram tiles as one stack of NBM tiles (NBM * BT rows)
+  constexpr int CCn = dma_count<BT, BC, 8>(), CGA = dma_count<NBM * BT, GC, 8>();
+  constexpr int NCOPY = CX + CBn + CCn + CGA;
+  constexpr int S = NBM * BT;  // sub-chunk length
 
   __shared__ __align__(16) unsigned char stage0[Lay::STAGE];
   __shared__ __align__(16) unsigned char stage1[Lay::STAGE];
-  __shared__ __align__(16) unsigned char stage2[Lay::STAGE];
+  __shared__ __align__(16) unsigned char sink[256];
+  // each wave's fp16 copy of the sub-chunk's entering state (the readout's
+  // operand), kept in LDS rather than in registers
+  __shared__ __align__(16) unsigned char hfl[8 * NQ * 64 * 16];
 
   const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
   const int HU = H / 2;
-  // (head pair, segment, sequence), head pair fastest, XCD-contiguous as in
-  // scan_kernel
   const int per = gridDim.x / 8;
   const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (logical >= HU * A.segs * A.Bt) return;
@@ -711,7 +775,7 @@ __global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A
   const int g4 = lane >> 4, c = lane & 15;
   const size_t NPsz = (size_t)N * kP;
   const size_t HPsz = (size_t)H * kP;
-  const int prow_x = 16 * wc + c;  // this lane's head column p
+  const int prow_x = 16 * wc + c;
 
   const float ah = A.a[h];
   const float la = ah > 0.f ? log2f(ah) : -1e30f;
@@ -727,7 +791,7 @@ __global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A
       reinterpret_cast<const T*>(A.gram) + (size_t)b * A.nc * G * A.npairs * gtile,
       (uint64_t)A.nc * G * A.npairs * gtile * ES);
 
-  // ---- per-lane decay tables of this wave's head (as in scan_kernel)
+  // ---- per-lane decay tables (as in scan_kernel)
   F er[RQ];
 #pragma unroll
   for (int q = 0; q < RQ; ++q)
@@ -774,20 +838,19 @@ __global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A
   const int ch0 = seg * A.seg_chunks;
   const int ch1 = min(nc, ch0 + A.seg_chunks);
   if (ch0 >= ch1) return;
-  auto nblocks = [&](int ch) { return (min(L, Tlen - ch * L) + BT - 1) / BT; };
-  auto advance = [&](ScanStep s) {
-    if (++s.sig > s.tau) {
-      s.sig = 0;
-      if (++s.tau == nblocks(s.ch)) { s.tau = 0; ++s.ch; }
+  auto chunk_len = [&](int ch) { return min(L, Tlen - ch * L); };
+  auto sub_len = [&](const SubChunk& u) { return min(S, chunk_len(u.ch) - u.half * S); };
+  auto next_sub = [&](SubChunk u) {
+    if (++u.half == (chunk_len(u.ch) + S - 1) / S) {
+      u.half = 0;
+      ++u.ch;
     }
-    return s;
+    return u;
   };
 
-  // ---- copies of one step into a stage
-  // X: the two heads' tiles as one tile of 2R rows copied by all 8 waves
-  // (row r of head r / R at global row r % R, the head's columns kP * ES
-  // further), so the copies' LDS addresses do not depend on the wave's head
-  uint32_t xoff[CX], boff[CBn], coff[CCn], goff[CG];
+  // ---- copies of one step into a stage (every wave takes its share of each
+  // tile; X of both heads as one tile of 2R rows, as in the two-head walk)
+  uint32_t xoff[CX], boff[CBn], coff[CCn];
   int xrow[CX];
 #pragma unroll
   for (int m = 0; m < CX; ++m) {
@@ -798,212 +861,90 @@ __global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A
   }
   dma_plan_n<R, BC, 8>((uint32_t)GN * ES, w, lane, [](int r) { return swz_tr<T, BC>(r); }, boff);
   dma_plan_n<BT, BC, 8>((uint32_t)GN * ES, w, lane, [](int r) { return swz_row<T, BC>(r); }, coff);
-  dma_plan_n<BT, GC, 8>((uint32_t)R * ES, w, lane, [](int r) { return swz_row<T, GC>(r); }, goff);
+  // Gram stack: instruction m of this wave moves rows of tile gtau[m] only (8
+  // rows of a 32-row tile per 64 chunks), so a tile's position in HBM goes in
+  // the scalar offset; the lane's offset within its tile is fixed
+  uint32_t gaoff[CGA];
+  int gtau[CGA];
+#pragma unroll
+  for (int m = 0; m < CGA; ++m) {
+    const int slot = 64 * dma_group<NBM * BT, GC, 8>(m, w) + lane;
+    const int r = slot / GC, pc = slot % GC, rr = r % BT;
+    gtau[m] = r / BT;
+    gaoff[m] = rr * (uint32_t)R * ES + 16 * (pc ^ swz_row<T, GC>(rr));
+  }
   const bool nfull = N == NP;
-  // Every step issues the same number of copy instructions per wave (NCOPY):
-  // tiles a step does not need are replaced by copies that read nothing (an
-  // offset past the buffer) and write 4-byte zeros into a small sink, so the
-  // wait for a stage is one fixed count and the compiler's own wait model
-  // stays exact (with per-step counts it waited for every copy in flight).
-  constexpr int NCOPY = CX + CG + CCn + CBn;
-  __shared__ __align__(16) unsigned char sink[256];
 
-  auto fetch = [&](unsigned char* st, ScanStep s) {
-    const int c0 = s.ch * L;
-    const int Lc = min(L, Tlen - c0);
-    const bool last = s.tau == (Lc + BT - 1) / BT - 1;
-    const uint32_t prow = (uint32_t)(c0 + s.sig * BT) * KS;
-    const int rlim = (Lc - s.sig * BT) * KS;
+  // copies of step sig of sub-chunk u into a stage
+  auto fetch = [&](unsigned char* st, const SubChunk& u, int sig) {
+    const int c0 = u.ch * L + u.half * S;
+    const int Ls = sub_len(u);
+    const int nbs = (Ls + BT - 1) / BT;
+    const uint32_t prow = (uint32_t)(c0 + sig * BT) * KS;
+    const int rlim = (Ls - sig * BT) * KS;
     const bool rows_full = rlim >= R;
     const uint32_t xb = (prow * (uint32_t)HPsz + 2 * hp * kP) * ES;
     if (rows_full)
       dma_tile_full_n<2 * R, XC, 8>(rX, xb, xoff, st + Lay::XO, w);
     else
       dma_rows_n<2 * R, XC, 8>(rX, xb, xoff, xrow, rlim, st + Lay::XO, w);
-    const int pidx = s.tau * (s.tau + 1) / 2 + s.sig;
-    const uint32_t gbase = (uint32_t)((((size_t)s.ch * G + grp) * A.npairs + pidx) * gtile);
-    dma_tile_full_n<BT, GC, 8>(rG, gbase * ES, goff, st + Lay::GO, w);
-    if (s.sig == 0) {
-      const uint32_t cb = ((uint32_t)(c0 + s.tau * BT) * GN + grp * N) * ES;
-      if (Lc - s.tau * BT >= BT && nfull)
-        dma_tile_full_n<BT, BC, 8>(rC, cb, coff, st + Lay::CO, w);
-      else
-        dma_tile_n<BT, BC, 8>(rC, cb, GN * ES, st + Lay::CO, Lc - s.tau * BT, (int)(N * ES / 16),
-                              w, lane, [](int r) { return swz_row<T, BC>(r); });
-    } else {
-      dma_dummies<CCn>(rX, sink);
-    }
-    if (last) {
-      const uint32_t bb = (prow * GN + grp * N) * ES;
-      if (rows_full && nfull)
-        dma_tile_full_n<R, BC, 8>(rB, bb, boff, st + Lay::BO, w);
-      else
-        dma_tile_n<R, BC, 8>(rB, bb, GN * ES, st + Lay::BO, rlim, (int)(N * ES / 16), w, lane,
-                             [](int r) { return swz_tr<T, BC>(r); });
-    } else {
-      dma_dummies<CBn>(rX, sink);
+    const uint32_t bb = (prow * GN + grp * N) * ES;
+    if (rows_full && nfull)
+      dma_tile_full_n<R, BC, 8>(rB, bb, boff, st + Lay::BO, w);
+    else
+      dma_tile_n<R, BC, 8>(rB, bb, GN * ES, st + Lay::BO, rlim, (int)(N * ES / 16), w, lane,
+                           [](int r) { return swz_tr<T, BC>(r); });
+    const uint32_t cb = ((uint32_t)(c0 + sig * BT) * GN + grp * N) * ES;
+    if (Ls - sig * BT >= BT && nfull)
+      dma_tile_full_n<BT, BC, 8>(rC, cb, coff, st + Lay::CO, w);
+    else
+      dma_tile_n<BT, BC, 8>(rC, cb, GN * ES, st + Lay::CO, Ls - sig * BT, (int)(N * ES / 16), w,
+                            lane, [](int r) { return swz_row<T, BC>(r); });
+    // Gram tiles (tau, sig) in the chunk's block numbering into slot tau of
+    // the stack; the slots of blocks before sig or past the sub-chunk read
+    // zeros (never used)
+    const int tb = u.half * NBM;
+#pragma unroll
+    for (int m = 0; m < CGA; ++m) {
+      const int tau = __builtin_amdgcn_readfirstlane(gtau[m]);
+      uint32_t vo = kOOB, so = 0;
+      if (tau >= sig && tau < nbs) {
+        const int tc = tb + tau, sc = tb + sig;
+        const int pidx = tc * (tc + 1) / 2 + sc;
+        so = (uint32_t)((((size_t)u.ch * G + grp) * A.npairs + pidx) * gtile) * ES;
+        vo = gaoff[m];
+      }
+      const int gi = dma_group<NBM * BT, GC, 8>(m, w);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rG, (__attribute__((address_space(3))) void*)(st + Lay::GO + 1024 * gi), 16, vo,
+          __builtin_amdgcn_readfirstlane(so), 0, 0);
     }
   };
 
   float hscale = 1.f;
-  F hf[NQ];  // the entering state of the chunk as fp16 operands (scaled by 1/hscale)
-  floatx4 accY[TT];
-  bool ypend = false;
+  floatx4 accY[NBM][TT];
+  // fragment q of this wave's fp16 entering state (scaled by 1/hscale)
+  const int hfo = w * NQ * 64 * 16 + 16 * lane;
+  // fragment q's address, one step from hfl (see load_kmajor_flat)
+  auto hfq = [&](int q) {
+    int o = hfo + q * 64 * 16;
+    asm("" : "+v"(o));
+    return hfl + o;
+  };
+
+  auto gfrag = [&](const unsigned char* Gt, int tt, int q) {
+    const int t = 16 * tt + c;
+    const int e0 = (32 * q + 8 * g4) * (int)ES;
+    return load8<T>(reinterpret_cast<const T*>(
+        Gt + (t * GC + ((e0 >> 4) ^ swz_row<T, GC>(t))) * 16 + (e0 & 15)));
+  };
+
+  bool ypend = false;  // y block of the previous step waiting to be stored
   size_t yrow0 = 0;
   int ylim = 0;
-
-  auto compute = [&](const unsigned char* st, const ScanStep cur) {
-    const unsigned char* Xs = st + Lay::XO + hw * Lay::XB;
-    const unsigned char* Bs = st + Lay::BO;
-    const unsigned char* Cs = st + Lay::CO;
-    const unsigned char* Gs = st + Lay::GO;
-    const int c0 = cur.ch * L;
-    const int Lc = min(L, Tlen - c0);
-    const int nb = (Lc + BT - 1) / BT;
-    const bool last = cur.tau == nb - 1;
-    const bool dg = cur.sig == cur.tau;
-
-    if (cur.tau == 0 && cur.sig == 0) {
-      // the chunk's entering state as fp16 operands, scaled by 2^-e (e >= 0
-      // from this wave's max |H|) so they stay below 2^14; the readout is
-      // multiplied back by 2^e in fp32
-      float hin = 1.f;
-      hscale = 1.f;
-      if (sizeof(T) == 2) {
-        float mx = 0.f;
-#pragma unroll
-        for (int a = 0; a < NT; ++a)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[a][i]));
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        if (mx > 16384.f) {
-          const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
-          hin = ldexpf(1.f, -e);
-          hscale = ldexpf(1.f, e);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hf[q][i] = from_f32<T>(Hr[2 * q][i] * hin);
-          hf[q][4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
-        }
-    }
-
-    F xq[RQ];  // X^T fragment of this wave's columns: rows r = 32q + 8g + j
-#pragma unroll
-    for (int q = 0; q < RQ; ++q) xq[q] = load_kmajor<T, XC>(Xs, 32 * q, 16 * wc, lane);
-
-    if (cur.sig == 0) {
-      // ---- readout of the entering state: y^T[p, t] = H^T[p, n] C~^T[n, t]
-      const float ablk = (cur.tau == 0 ? 1.f : apow_step(la, cur.tau * BT)) * hscale * ah;
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) accY[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        F cf[TT];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          // C~ operand in the state's n order: {32q + 4g .. +3, 32q + 16 + 4g .. +3}
-          const int t = 16 * tt + c;
-          const int n0 = 32 * q + 4 * g4;
-          const int e0 = n0 * (int)ES, e1 = (n0 + 16) * (int)ES;
-          const int sw = swz_row<T, BC>(t);
-          const T* p0 = reinterpret_cast<const T*>(Cs + (t * BC + ((e0 >> 4) ^ sw)) * 16 + (e0 & 15));
-          const T* p1 = reinterpret_cast<const T*>(Cs + (t * BC + ((e1 >> 4) ^ sw)) * 16 + (e1 & 15));
-          cf[tt] = load4x2<T>(p0, p1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) accY[tt] = mma16(hf[q], cf[tt], accY[tt]);
-      }
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] * (at[tt] * ablk);
-    }
-    // ---- intra-chunk: y^T[p, t] += X^T[p, r] (G o decay)[t, r]
-    auto gfrag = [&](int tt, int q) {
-      const int t = 16 * tt + c;
-      const int e0 = (32 * q + 8 * g4) * (int)ES;
-      const unsigned char* p = Gs + (t * GC + ((e0 >> 4) ^ swz_row<T, GC>(t))) * 16 + (e0 & 15);
-      return load8<T>(reinterpret_cast<const T*>(p));
-    };
-    if (dg) {
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        F gf[TT];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-          if (DF::index(tt, q) >= 0) gf[tt] = gfrag(tt, q);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          const int ix = DF::index(tt, q);
-          if (ix >= 0) accY[tt] = mma16(xq[q], gf[tt] * dm[ix], accY[tt]);
-        }
-      }
-    } else {
-      floatx4 tmp[TT];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) tmp[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        F gf[TT];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) gf[tt] = gfrag(tt, q);
-        __builtin_amdgcn_sched_barrier(0);
-        const F xs = xq[q] * er[q];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) tmp[tt] = mma16(xs, gf[tt], tmp[tt]);
-      }
-      const float u = apow_step(la, (cur.tau - cur.sig) * BT - (BT - 1));
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) accY[tt] = accY[tt] + tmp[tt] * (u * at[tt]);
-    }
-    if (last) {
-      // the carry accumulates straight into the state: H <- a^{Lc} H first
-      // (every readout of this chunk used the fp16 copy taken at its start)
-      if (cur.sig == 0) {
-        const float aL = apow_step(la, Lc);
-#pragma unroll
-        for (int a = 0; a < NT; ++a) Hr[a] = Hr[a] * aL;
-      }
-      // ---- carry: H[n, p] += sum_r B_hat[r, n] (a^{Lc-1-s} X[r, p])
-      const bool full = Lc == L;
-      const float blk = apow_step(la, (nb - 1 - cur.sig) * BT);
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        F xd;
-        if (full) {
-          xd = xq[q] * (er[q] * from_f32<T>(blk));
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int d = Lc - 1 - (cur.sig * BT + (32 * q + 8 * g4 + j) / KS);
-            xd[j] = from_f32<T>(to_f32(xq[q][j]) * (d >= 0 ? apow_step(la, d) : 0.f));
-          }
-        }
-        constexpr int CGR = NT < 4 ? NT : 4;
-#pragma unroll
-        for (int a0 = 0; a0 < NT; a0 += CGR) {
-          F bf[CGR];
-#pragma unroll
-          for (int i = 0; i < CGR; ++i) bf[i] = load_kmajor<T, BC>(Bs, 32 * q, 16 * (a0 + i), lane);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int i = 0; i < CGR; ++i) Hr[a0 + i] = mma16(bf[i], xd, Hr[a0 + i]);
-        }
-      }
-    }
-    if (dg) {
-      // y of block tau is complete; it is stored at the start of the next step
-      ypend = true;
-      yrow0 = (size_t)b * Tlen + c0 + cur.tau * BT;
-      ylim = Lc - cur.tau * BT;
-    }
-  };
-  auto store_y = [&]() {
+  // y block bl (a compile-time constant) of the previous step
+  auto store_y = [&](auto blc) {
+    constexpr int bl = decltype(blc)::value;
     if (!ypend) return;
     typedef typename Vec<TY>::x4 Y4;
     TY* yb = reinterpret_cast<TY*>(A.y) + yrow0 * HPsz + (size_t)h * kP + 16 * wc + 4 * g4;
@@ -1013,47 +954,208 @@ __global__ __launch_bounds__(kWalk2Threads, 1) void scan_walk2_kernel(ScanArgs A
       if (tl < ylim) {
         Y4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[tt][i]);
+        for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[bl][tt][i]);
         *reinterpret_cast<Y4*>(yb + (size_t)tl * HPsz) = o;
       }
     }
     ypend = false;
   };
 
-  // ---- the walk: step s computes from stage s % 3 while the copies of step
-  // s + 2 go into stage (s + 2) % 3 (the one step s - 1 read); one barrier per
-  // step. Unrolled by three so that every access names its stage array.
-  ScanStep s0{ch0, 0, 0};
-  ScanStep s1 = advance(s0);
-  ScanStep s2 = s1.ch < ch1 ? advance(s1) : s1;
-  fetch(stage0, s0);
-  if (s1.ch < ch1)
-    fetch(stage1, s1);
-  else
-    dma_dummies<NCOPY>(rX, sink);
-  // Both first stages complete before the walk starts: the compiler's own
-  // wait model then knows every stage's copies at the loop head (with only
-  // step 0's stage waited for here it waited for every copy in flight before
-  // the first read of each turn of the loop).
+  // step sig (a compile-time constant) of sub-chunk u from stage st; last:
+  // no step follows in this walk
+  auto compute = [&](const unsigned char* st, const SubChunk& u, auto sigc, bool last) {
+    constexpr int sig = decltype(sigc)::value;
+    const unsigned char* Xs = st + Lay::XO + hw * Lay::XB;
+    const unsigned char* Bs = st + Lay::BO;
+    const unsigned char* Cs = st + Lay::CO;
+    const unsigned char* Gs = st + Lay::GO;
+    const int c0 = u.ch * L + u.half * S;
+    const int Ls = sub_len(u);
+    const int nbs = (Ls + BT - 1) / BT;
+
+    if constexpr (sig == 0) {
+      // the sub-chunk's entering state as fp16 operands, scaled by 2^-e (e >= 0
+      // from this wave's max |H|) so they stay below 2^14
+      float hin = 1.f;
+      hscale = 1.f;
+      if (sizeof(T) == 2) {
+        float mx = 0.f;
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[a][i]));
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (mx > 16384.f) {
+          const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
+          hin = ldexpf(1.f, -e);
+          hscale = ldexpf(1.f, e);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        F hq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hq[i] = from_f32<T>(Hr[2 * q][i] * hin);
+          hq[4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
+        }
+        *reinterpret_cast<F*>(hfq(q)) = hq;
+      }
+#pragma unroll
+      for (int tb = 0; tb < NBM; ++tb) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) accY[tb][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+
+    F xq[RQ];  // X^T fragments of this wave's columns
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) xq[q] = load_kmajor_flat<T, XC>(Xs, 32 * q, 16 * wc, lane);
+
+    // ---- readout of block sig: y^T[p, t] = H^T[p, n] C~^T[n, t]
+    {
+      floatx4 ro[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) ro[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        F cf[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const int t = 16 * tt + c;
+          const int n0 = 32 * q + 4 * g4;
+          const int e0 = n0 * (int)ES, e1 = (n0 + 16) * (int)ES;
+          const int sw = swz_row<T, BC>(t);
+          const T* p0 = reinterpret_cast<const T*>(Cs + (t * BC + ((e0 >> 4) ^ sw)) * 16 + (e0 & 15));
+          const T* p1 = reinterpret_cast<const T*>(Cs + (t * BC + ((e1 >> 4) ^ sw)) * 16 + (e1 & 15));
+          cf[tt] = load4x2<T>(p0, p1);
+        }
+        const F hq = *reinterpret_cast<const F*>(hfq(q));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) ro[tt] = mma16(hq, cf[tt], ro[tt]);
+      }
+      const float ablk = (sig == 0 ? 1.f : apow_step(la, sig * BT)) * hscale * ah;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) accY[sig][tt] = accY[sig][tt] + ro[tt] * (at[tt] * ablk);
+    }
+    // ---- intra term of the diagonal block pair (sig, sig)
+    {
+      const unsigned char* Gd = Gs + sig * Lay::GB;
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        F gf[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          if (DF::index(tt, q) >= 0) gf[tt] = gfrag(Gd, tt, q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const int ix = DF::index(tt, q);
+          if (ix >= 0) accY[sig][tt] = mma16(xq[q], gf[tt] * dm[ix], accY[sig][tt]);
+        }
+      }
+    }
+    // ---- intra terms of block sig in the later blocks tau of the sub-chunk
+    static_for<sig + 1, NBM>([&](auto tauc) {
+      constexpr int tau = decltype(tauc)::value;
+      if (tau < nbs) {
+        const unsigned char* Gt = Gs + tau * Lay::GB;
+        floatx4 tmp[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) tmp[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {
+          F gf[TT];
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) gf[tt] = gfrag(Gt, tt, q);
+          __builtin_amdgcn_sched_barrier(0);
+          const F xs = xq[q] * er[q];
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) tmp[tt] = mma16(xs, gf[tt], tmp[tt]);
+        }
+        const float uf = apow_step(la, (tau - sig) * BT - (BT - 1));
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) accY[tau][tt] = accY[tau][tt] + tmp[tt] * (uf * at[tt]);
+      }
+    });
+
+    // ---- carry of block sig: H <- a^{Ls} H at the sub-chunk's first step
+    // (every readout of the sub-chunk uses the fp16 copy taken there), then
+    // H[n, p] += sum_r B_hat[r, n] (a^{Ls-1-s} X[r, p])
+    if constexpr (sig == 0) {
+      const float aL = apow_step(la, Ls);
+#pragma unroll
+      for (int a = 0; a < NT; ++a) Hr[a] = Hr[a] * aL;
+    }
+    const bool full = Ls == nbs * BT;
+    const float blk = apow_step(la, (nbs - 1 - sig) * BT);
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      F xd;
+      if (full) {
+        xd = xq[q] * (er[q] * from_f32<T>(blk));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int d = Ls - 1 - (sig * BT + (32 * q + 8 * g4 + j) / KS);
+          xd[j] = from_f32<T>(to_f32(xq[q][j]) * (d >= 0 ? apow_step(la, d) : 0.f));
+        }
+      }
+      constexpr int CGR = NT < 4 ? NT : 4;
+#pragma unroll
+      for (int a0 = 0; a0 < NT; a0 += CGR) {
+        F bf[CGR];
+#pragma unroll
+        for (int i = 0; i < CGR; ++i) bf[i] = load_kmajor_flat<T, BC>(Bs, 32 * q, 16 * (a0 + i), lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < CGR; ++i) Hr[a0 + i] = mma16(bf[i], xd, Hr[a0 + i]);
+      }
+    }
+
+    // ---- y block sig is complete: stored at the start of the next step
+    // (before its copies), or now when no step follows
+    ypend = true;
+    yrow0 = (size_t)b * Tlen + c0 + sig * BT;
+    ylim = Ls - sig * BT;
+    if (last) store_y(sigc);
+  };
+
+  // ---- the walk: sub-chunk by sub-chunk, its NBM steps unrolled; step sig
+  // computes from stage sig % 2 while the copies of the next step go into the
+  // other; one barrier per step
+  SubChunk cur{ch0, 0};
+  fetch(stage0, cur, 0);
   wait_vm<0>();
   stage_barrier();
-  auto step = [&](const unsigned char* cur_st, unsigned char* far_st) {
-    store_y();
-    if (s2.ch < ch1)
-      fetch(far_st, s2);
-    else
-      dma_dummies<NCOPY>(rX, sink);
-    compute(cur_st, s0);
-    wait_vm<NCOPY>();  // the next step's copies have landed
-    stage_barrier();
-    s0 = s1;
-    s1 = s2;
-    if (s2.ch < ch1) s2 = advance(s2);
-    return s0.ch < ch1;
-  };
-  while (step(stage0, stage2) && step(stage1, stage0) && step(stage2, stage1)) {
+  while (cur.ch < ch1) {
+    const SubChunk nxt = next_sub(cur);
+    const int nbs = (sub_len(cur) + BT - 1) / BT;
+    static_for<0, NBM>([&](auto sigc) {
+      constexpr int sig = decltype(sigc)::value;
+      unsigned char* cst = sig % 2 == 0 ? stage0 : stage1;
+      unsigned char* nst = sig % 2 == 0 ? stage1 : stage0;
+      // (a sub-chunk shorter than NBM blocks ends the sequence: its missing
+      // steps only wait, so that on every path no copy is in flight at a
+      // step's start and the compiler's wait model stays exact)
+      store_y(std::integral_constant<int, (sig + NBM - 1) % NBM>());
+      const bool more = sig + 1 < nbs || (sig + 1 == nbs && nxt.ch < ch1);
+      if (sig + 1 < nbs)
+        fetch(nst, cur, sig + 1);
+      else if (sig + 1 == nbs && nxt.ch < ch1)
+        fetch(nst, nxt, 0);
+      else
+        dma_dummies<NCOPY>(rX, sink);
+      if (sig < nbs) compute(cst, cur, sigc, !more);
+      wait_vm<0>();  // the next step's copies have landed
+      stage_barrier();
+    });
+    cur = nxt;
   }
-  store_y();
 
   if (seg == A.segs - 1 && A.h_final) {
     float* dst = A.h_final + ((size_t)b * H + h) * NPsz;
@@ -1155,17 +1257,23 @@ static int scan_block(int N, int k, int L, int es) {
   return 32;
 }
 
-// The two-head walk serves 2-byte streams with k <= 2 and the shared decay,
-// when the heads of a group pair up (H / G even), for chunks of 128 and 256
-// tokens (10 and 36 block pairs per chunk, where sharing the Gram, C~ and
-// B_hat tiles between two heads pays: measured on MI355X, 4 x 8192 tokens,
-// 64 heads, L = 128: 415 -> 402 us; 65536 tokens, 32 heads, L = 256: 812 ->
-// 546 us; with 64-token chunks, 8 x 2048 tokens, 24 heads, it was slower,
-// 80 -> 88 us). It holds one workgroup per CU: it aims at one round of 256.
-static bool walk2_eligible(int H, int G, int k, int es, bool tv, int L) {
-  return es == 2 && k <= 2 && !tv && (H / G) % 2 == 0 && L >= 128;
+// The walk by source block (scan_rows_kernel, two heads per workgroup)
+// serves 2-byte streams with k <= 2 and the shared decay when the heads of a
+// group pair up (H / G even), for chunks of 128 and 256 tokens. Measured on
+// MI355X against the walk by block pair it replaced (itself two heads per
+// workgroup): 4 x 8192 tokens, 64 heads, L = 128: chunk output 398 -> 356 us;
+// 65536 tokens, 32 heads, L = 256: 550 -> 350 us; with 64-token chunks (8 x
+// 2048 tokens, 24 heads) it was slower than one head per workgroup (82 -> 90
+// us), which those keep. SWIMBA_SCAN_WALK = 0 or 1 forces one or the other
+// where eligible.
+static int scan_walk(int H, int G, int k, int es, bool tv, int L) {
+  static const int forced = env_int("SWIMBA_SCAN_WALK", -1);
+  const bool two = es == 2 && k <= 2 && !tv && (H / G) % 2 == 0 && L >= 64;
+  if (forced == 0) return 0;
+  if (forced == 1 && two) return 1;
+  return two && L >= 128 ? 1 : 0;
 }
-static int walk2_target_wgs(int L) {
+static int walk_target_wgs(int L) {
   static const int w = env_int("SWIMBA_SCAN_WGS", 0);
   if (w > 0) return w;
   (void)L;
@@ -1199,9 +1307,9 @@ ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int 
   ScanGeom g{Bt, T, H, G, N, P, k, L, es, scan_block(N, k, L, es), 1, 1, 0, 1};
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
-  g.walk2 = walk2_eligible(H, G, k, es, tv, L) ? 1 : 0;
-  const int units = g.walk2 ? Bt * (H / 2) : Bt * H;
-  int want = (g.walk2 ? walk2_target_wgs(L) : scan_target_wgs(L)) / units;
+  g.walk = scan_walk(H, G, k, es, tv, L);
+  const int units = g.walk ? Bt * (H / 2) : Bt * H;
+  int want = (g.walk ? walk_target_wgs(L) : scan_target_wgs(L)) / units;
   if (want > nc) want = nc;
   if (want < 1) want = 1;
   g.seg_chunks = (nc + want - 1) / want;
@@ -1238,7 +1346,8 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   hipLaunchKernelGGL((scan_gram_kernel<T, NP, KS, BT>), dim3((unsigned)((ng + 7) / 8 * 8)),
                      dim3(256), 0, s, static_cast<const T*>(args.B_hat),
                      static_cast<const T*>(args.C_mix), static_cast<T*>(const_cast<void*>(args.gram)),
-                     g.T, g.G, g.N, g.L, args.nc, args.npairs, g.Bt);
+                     g.T, g.G, g.N, g.L, args.nc, args.npairs, g.Bt,
+                     (sizeof(T) == 2 && KS <= 2 && !TV && g.walk == 1) ? kRowsSub / BT : 0);
   prof_end(s);
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
@@ -1254,10 +1363,10 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   }
   prof_begin("scan_chunk_output", s);
   if constexpr (sizeof(T) == 2 && KS <= 2 && !TV) {
-    if (g.walk2) {
+    if (g.walk == 1) {
       const int n3 = (g.H / 2) * g.segs * g.Bt;
-      hipLaunchKernelGGL((scan_walk2_kernel<T, TY, NP, KS, BT>), dim3((unsigned)((n3 + 7) / 8 * 8)),
-                         dim3(kWalk2Threads), 0, s, args);
+      hipLaunchKernelGGL((scan_rows_kernel<T, TY, NP, KS, BT, kRowsSub / BT>),
+                         dim3((unsigned)((n3 + 7) / 8 * 8)), dim3(kRowsThreads), 0, s, args);
       prof_end(s);
       return hipGetLastError();
     }
