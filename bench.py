@@ -69,7 +69,7 @@ KERNEL_NAMES = [
     (r"mix_decay_kernel", "mix_decay"),
     (r"scan_gram_kernel", "scan_gram"),
     # (types, NP, KS, BT, WITH_Y, TV): WITH_Y follows the block size
-    (r"scan_kernel.*Li\d+ELb0ELb[01]E", "scan_segment_state"),
+    (r"scan_kernel.*Li\d+ELb0ELb[01]E|scan_carry_kernel", "scan_segment_state"),
     (r"scan_combine_kernel", "scan_state_pass"),
     (r"scan_kernel.*Li\d+ELb1ELb[01]E|scan_walk2_kernel|scan_rows_kernel", "scan_chunk_output"),
     (r"state_copy_kernel", "state_copy"),

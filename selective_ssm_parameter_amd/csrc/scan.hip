@@ -1169,6 +1169,196 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
   }
 }
 
+// Pass 1 with two heads per workgroup (8 waves; the heads share one copy of
+// the group's B_hat rows): the carry-only walk over the chunks of one piece of
+// a segment, one step per 32-token block (its X_hat rows for both heads and
+// its B_hat rows), H <- a^{Lc} H at a chunk's first block and
+// H += B_hat^T (a^{Lc-1-s} X_hat) for every block, from a zero state; the
+// piece's end state goes to its workspace slot. Three LDS stages with a fixed
+// number of copies per step, so the copies of step s + 2 are in flight while
+// step s computes and a stage is waited for with one count.
+constexpr int kCarryThreads = 512;
+template <typename T, int NP, int KS, int BT>
+struct CarryLds {
+  static constexpr int R = KS * BT;
+  static constexpr int XROW = kP * (int)sizeof(T), BROW = NP * (int)sizeof(T);
+  static constexpr int XB = R * XROW, BB = R * BROW;
+  static constexpr int XO = 0, BO = 2 * XB;
+  static constexpr int STAGE = BO + BB;
+};
+
+template <typename T, int NP, int KS, int BT>
+__global__ __launch_bounds__(kCarryThreads, 1) void scan_carry_kernel(ScanArgs A) {
+  typedef CarryLds<T, NP, KS, BT> Lay;
+  constexpr int R = Lay::R, RQ = R / 32, NT = NP / 16;
+  constexpr int XC = Lay::XROW / 16, BC = Lay::BROW / 16;
+  constexpr uint32_t ES = sizeof(T);
+  typedef typename Vec<T>::x8 F;
+  constexpr int CX = dma_count<2 * R, XC, 8>(), CBn = dma_count<R, BC, 8>();
+  constexpr int NCOPY = CX + CBn;
+
+  __shared__ __align__(16) unsigned char stage0[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stage1[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stage2[Lay::STAGE];
+  __shared__ __align__(16) unsigned char sink[256];
+
+  const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
+  const int HU = H / 2;
+  const int nseg = (A.segs - 1) * A.sub;  // pieces
+  const int nslot = nseg + 1;
+  const int per = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (logical >= HU * nseg * A.Bt) return;
+  const int hp = logical % HU, seg = (logical / HU) % nseg, b = logical / (HU * nseg);
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hw = w >> 2, wc = w & 3;
+  const int h = 2 * hp + hw;
+  const int grp = h / (H / G);
+  const int GN = G * N;
+  const int g4 = lane >> 4, c = lane & 15;
+  const size_t NPsz = (size_t)N * kP;
+  const size_t HPsz = (size_t)H * kP;
+  const int prow_x = 16 * wc + c;
+  const float la = A.a[h] > 0.f ? log2f(A.a[h]) : -1e30f;
+
+  const BufRes rB = make_rsrc(reinterpret_cast<const T*>(A.B_hat) + (size_t)b * Tlen * KS * GN,
+                              (uint64_t)Tlen * KS * GN * ES);
+  const BufRes rX = make_rsrc(reinterpret_cast<const T*>(A.X_hat) + (size_t)b * Tlen * KS * HPsz,
+                              (uint64_t)Tlen * KS * HPsz * ES);
+
+  F er[RQ];  // a^{BT-1-s} of the pair row r = 32q + 8g + j of a block (s = r / k)
+#pragma unroll
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) er[q][j] = from_f32<T>(apow(la, BT - 1 - (32 * q + 8 * g4 + j) / KS));
+
+  floatx4 Hr[NT];
+#pragma unroll
+  for (int a = 0; a < NT; ++a) Hr[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int span = A.seg_chunks / A.sub;
+  const int ch0 = seg * span;
+  const int ch1 = min(A.nc, ch0 + span);
+  if (ch0 >= ch1) return;
+  auto nblocks = [&](int ch) { return (min(L, Tlen - ch * L) + BT - 1) / BT; };
+  struct Blk {
+    int ch, sig;
+  };
+  auto advance = [&](Blk s) {
+    if (++s.sig == nblocks(s.ch)) {
+      s.sig = 0;
+      ++s.ch;
+    }
+    return s;
+  };
+
+  uint32_t xoff[CX], boff[CBn];
+  int xrow[CX];
+#pragma unroll
+  for (int m = 0; m < CX; ++m) {
+    const int slot = 64 * dma_group<2 * R, XC, 8>(m, w) + lane;
+    const int r = slot / XC, pc = slot % XC, rr = r % R;
+    xrow[m] = rr;
+    xoff[m] = rr * (uint32_t)HPsz * ES + (r / R) * kP * ES + 16 * (pc ^ swz_tr<T, XC>(rr));
+  }
+  dma_plan_n<R, BC, 8>((uint32_t)GN * ES, w, lane, [](int r) { return swz_tr<T, BC>(r); }, boff);
+  const bool nfull = N == NP;
+  auto fetch = [&](unsigned char* st, Blk s) {
+    const int c0 = s.ch * L;
+    const int Lc = min(L, Tlen - c0);
+    const uint32_t prow = (uint32_t)(c0 + s.sig * BT) * KS;
+    const int rlim = (Lc - s.sig * BT) * KS;
+    const bool rows_full = rlim >= R;
+    const uint32_t xb = (prow * (uint32_t)HPsz + 2 * hp * kP) * ES;
+    if (rows_full)
+      dma_tile_full_n<2 * R, XC, 8>(rX, xb, xoff, st + Lay::XO, w);
+    else
+      dma_rows_n<2 * R, XC, 8>(rX, xb, xoff, xrow, rlim, st + Lay::XO, w);
+    const uint32_t bb = (prow * GN + grp * N) * ES;
+    if (rows_full && nfull)
+      dma_tile_full_n<R, BC, 8>(rB, bb, boff, st + Lay::BO, w);
+    else
+      dma_tile_n<R, BC, 8>(rB, bb, GN * ES, st + Lay::BO, rlim, (int)(N * ES / 16), w, lane,
+                           [](int r) { return swz_tr<T, BC>(r); });
+  };
+  auto compute = [&](const unsigned char* st, Blk cur) {
+    const unsigned char* Xs = st + Lay::XO + hw * Lay::XB;
+    const unsigned char* Bs = st + Lay::BO;
+    const int Lc = min(L, Tlen - cur.ch * L);
+    const int nb = (Lc + BT - 1) / BT;
+    if (cur.sig == 0) {
+      const float aL = apow_step(la, Lc);
+#pragma unroll
+      for (int a = 0; a < NT; ++a) Hr[a] = Hr[a] * aL;
+    }
+    const bool full = Lc == nb * BT;
+    const float blk = apow_step(la, (nb - 1 - cur.sig) * BT);
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const F xq = load_kmajor_flat<T, XC>(Xs, 32 * q, 16 * wc, lane);
+      F xd;
+      if (full) {
+        xd = xq * (er[q] * from_f32<T>(blk));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int d = Lc - 1 - (cur.sig * BT + (32 * q + 8 * g4 + j) / KS);
+          xd[j] = from_f32<T>(to_f32(xq[j]) * (d >= 0 ? apow_step(la, d) : 0.f));
+        }
+      }
+      constexpr int CGR = NT < 4 ? NT : 4;
+#pragma unroll
+      for (int a0 = 0; a0 < NT; a0 += CGR) {
+        F bf[CGR];
+#pragma unroll
+        for (int i = 0; i < CGR; ++i) bf[i] = load_kmajor_flat<T, BC>(Bs, 32 * q, 16 * (a0 + i), lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < CGR; ++i) Hr[a0 + i] = mma16(bf[i], xd, Hr[a0 + i]);
+      }
+    }
+  };
+
+  // ---- the walk: step s computes from stage s % 3 while the copies of step
+  // s + 2 go into stage (s + 2) % 3; one barrier per step
+  Blk s0{ch0, 0};
+  Blk s1 = advance(s0);
+  Blk s2 = s1.ch < ch1 ? advance(s1) : s1;
+  fetch(stage0, s0);
+  if (s1.ch < ch1)
+    fetch(stage1, s1);
+  else
+    dma_dummies<NCOPY>(rX, sink);
+  wait_vm<0>();
+  stage_barrier();
+  auto step = [&](const unsigned char* cur_st, unsigned char* far_st) {
+    if (s2.ch < ch1)
+      fetch(far_st, s2);
+    else
+      dma_dummies<NCOPY>(rX, sink);
+    compute(cur_st, s0);
+    wait_vm<NCOPY>();  // the next step's copies have landed
+    stage_barrier();
+    s0 = s1;
+    s1 = s2;
+    if (s2.ch < ch1) s2 = advance(s2);
+    return s0.ch < ch1;
+  };
+  while (step(stage0, stage2) && step(stage1, stage0) && step(stage2, stage1)) {
+  }
+  wait_vm<0>();  // the copies past the end land before the workgroup's LDS is released
+
+  float* dst = A.ws + (((size_t)b * nslot + seg + 1) * H + h) * NPsz;  // slot j+1 holds S_j
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = 16 * a + 4 * g4 + i;
+      if (n < N) dst[(size_t)n * kP + prow_x] = Hr[a][i];
+    }
+}
+
 // Pass 2: Hin_0 = h_init (or 0), Hin_{s+1} = a^{len_s} Hin_s + S_s, for every
 // (sequence, head, element), walking the pieces of pass 1 in order (`segs`
 // slots here, pieces of `seg_chunks` chunks). Slot s of the workspace holds
@@ -1303,6 +1493,17 @@ static int scan_pieces(int units1, int seg_chunks) {
   return forced > 0 ? seg_chunks : best;
 }
 
+// Pass 1 with two heads per workgroup (scan_carry_kernel) goes with the
+// two-head output walk (2-byte streams, k <= 2, the shared decay, heads of a
+// group in pairs, chunks of 128+ tokens). Measured on MI355X: 4 x 8192
+// tokens, 64 heads: 84 -> 75 us; 65536 tokens, 32 heads: 156 -> 136 us; with
+// 64-token chunks (8 x 2048 tokens, 24 heads: 384 workgroups, one per CU) it
+// was slower, 28 -> 40 us. SWIMBA_SCAN_CARRY = 0 keeps one head per workgroup.
+static bool carry_two(const ScanGeom& g) {
+  static const int on = env_int("SWIMBA_SCAN_CARRY", 1);
+  return on > 0 && g.walk == 1;
+}
+
 ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int es, bool tv) {
   ScanGeom g{Bt, T, H, G, N, P, k, L, es, scan_block(N, k, L, es), 1, 1, 0, 1};
   const int nc = (T + L - 1) / L;
@@ -1351,8 +1552,19 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   prof_end(s);
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
-    const int n1 = g.H * (g.segs - 1) * g.sub * g.Bt;
-    hipLaunchKernelGGL(k1, dim3((unsigned)((n1 + 7) / 8 * 8)), dim3(kScanThreads), l1, s, args);
+    bool done = false;
+    if constexpr (sizeof(T) == 2 && KS <= 2 && !TV) {
+      if (carry_two(g)) {
+        const int n1 = (g.H / 2) * (g.segs - 1) * g.sub * g.Bt;
+        hipLaunchKernelGGL((scan_carry_kernel<T, NP, KS, BT>), dim3((unsigned)((n1 + 7) / 8 * 8)),
+                           dim3(kCarryThreads), 0, s, args);
+        done = true;
+      }
+    }
+    if (!done) {
+      const int n1 = g.H * (g.segs - 1) * g.sub * g.Bt;
+      hipLaunchKernelGGL(k1, dim3((unsigned)((n1 + 7) / 8 * 8)), dim3(kScanThreads), l1, s, args);
+    }
     prof_end(s);
     const int NPsz = g.N * g.P;
     prof_begin("scan_state_pass", s);
