@@ -932,6 +932,41 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
     return hfl + o;
   };
 
+  // the entering state of the next sub-chunk as fp16 operands in hfl, scaled
+  // by 2^-e (e >= 0 from this wave's max |H|) so they stay below 2^14. Called
+  // where no copy is in flight (after a step's wait), so that the writes to
+  // hfl wait for nothing; the wave-wide maximum is formed only when some lane
+  // holds a value past the bound.
+  auto stash_state = [&]() {
+    float hin = 1.f;
+    hscale = 1.f;
+    if (sizeof(T) == 2) {
+      float mx = 0.f;
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[a][i]));
+      }
+      if (__ballot(mx > 16384.f)) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
+        hin = ldexpf(1.f, -e);
+        hscale = ldexpf(1.f, e);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      F hq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hq[i] = from_f32<T>(Hr[2 * q][i] * hin);
+        hq[4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
+      }
+      *reinterpret_cast<F*>(hfq(q)) = hq;
+    }
+  };
+
   auto gfrag = [&](const unsigned char* Gt, int tt, int q) {
     const int t = 16 * tt + c;
     const int e0 = (32 * q + 8 * g4) * (int)ES;
@@ -974,35 +1009,6 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
     const int nbs = (Ls + BT - 1) / BT;
 
     if constexpr (sig == 0) {
-      // the sub-chunk's entering state as fp16 operands, scaled by 2^-e (e >= 0
-      // from this wave's max |H|) so they stay below 2^14
-      float hin = 1.f;
-      hscale = 1.f;
-      if (sizeof(T) == 2) {
-        float mx = 0.f;
-#pragma unroll
-        for (int a = 0; a < NT; ++a) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Hr[a][i]));
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        if (mx > 16384.f) {
-          const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
-          hin = ldexpf(1.f, -e);
-          hscale = ldexpf(1.f, e);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        F hq;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hq[i] = from_f32<T>(Hr[2 * q][i] * hin);
-          hq[4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
-        }
-        *reinterpret_cast<F*>(hfq(q)) = hq;
-      }
 #pragma unroll
       for (int tb = 0; tb < NBM; ++tb) {
 #pragma unroll
@@ -1131,6 +1137,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
   SubChunk cur{ch0, 0};
   fetch(stage0, cur, 0);
   wait_vm<0>();
+  stash_state();
   stage_barrier();
   while (cur.ch < ch1) {
     const SubChunk nxt = next_sub(cur);
@@ -1152,6 +1159,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
         dma_dummies<NCOPY>(rX, sink);
       if (sig < nbs) compute(cst, cur, sigc, !more);
       wait_vm<0>();  // the next step's copies have landed
+      if constexpr (sig == NBM - 1) stash_state();
       stage_barrier();
     });
     cur = nxt;
