@@ -66,7 +66,7 @@ struct ScanGeom {
   int bt;            // tokens per block of the scan (32 or 64)
   int segs;          // segments per sequence
   int seg_chunks;    // chunks per segment
-  int walk;          // output walk: 0 one head per workgroup, 1 two heads by source block
+  int walk;          // output walk: 0 one head per workgroup, 1 two heads, one block per step
   int sub;           // pass 1 walks each segment in `sub` pieces
 };
 // tv: the expert-mixed decay (its output pass walks one head per workgroup).

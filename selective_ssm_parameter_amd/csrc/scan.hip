@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_
                                                         const T* __restrict__ C_mix,
                                                         T* __restrict__ gram, int Tlen, int G,
                                                         int N, int L, int nc, int npairs, int Bt,
-                                                        int subb) {
+                                                        int diag) {
   constexpr int R = KS * BT, TT = BT / 16, RT = R / 16;
   constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
@@ -139,18 +139,24 @@ __global__ __launch_bounds__(256) void scan_gram_kernel(const T* __restrict__ B_
   // 1-D grid, dealt XCD-contiguously with (group, block pair) fastest: the
   // tiles of one chunk are computed on one XCD and read its B_hat and C~ rows
   // from that XCD's L2 once.
+  // diag: only the diagonal pairs (tau, tau), for the walk one block per step
+  const int npw = diag ? L / BT : npairs;  // pairs computed per chunk
   const int per = gridDim.x / 8;
   const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (logical >= G * npairs * nc * Bt) return;
-  const int grp = logical % G, pidx = (logical / G) % npairs;
-  const int ch = (logical / (G * npairs)) % nc, b = logical / (G * npairs * nc);
-  int tau = 0;
-  while ((tau + 1) * (tau + 2) / 2 <= pidx) ++tau;
-  const int sig = pidx - tau * (tau + 1) / 2;
+  if (logical >= G * npw * nc * Bt) return;
+  const int grp = logical % G, ip = (logical / G) % npw;
+  const int ch = (logical / (G * npw)) % nc, b = logical / (G * npw * nc);
+  int tau = 0, sig = 0, pidx = 0;
+  if (diag) {
+    tau = sig = ip;
+    pidx = ip * (ip + 1) / 2 + ip;
+  } else {
+    pidx = ip;
+    while ((tau + 1) * (tau + 2) / 2 <= pidx) ++tau;
+    sig = pidx - tau * (tau + 1) / 2;
+  }
   const int c0 = ch * L, Lc = min(L, Tlen - c0);
   if (tau * BT >= Lc) return;  // block beyond the (last, partial) chunk
-  // subb > 0: the walk reads only pairs within sub-chunks of subb blocks
-  if (subb > 0 && tau / subb != sig / subb) return;
   const int GN = G * N;
   const BufRes rB = make_rsrc(B_hat + (size_t)b * Tlen * KS * GN, (uint64_t)Tlen * KS * GN * ES);
   const BufRes rC = make_rsrc(C_mix + (size_t)b * Tlen * GN, (uint64_t)Tlen * GN * ES);
@@ -659,30 +665,7 @@ __device__ __forceinline__ void dma_dummies(BufRes rs, unsigned char* sink) {
   }
 }
 
-// The output walk by source block, two heads per workgroup (8 waves; the
-// heads share one copy of the group's B_hat, C~ and Gram tiles). A chunk is
-// walked in sub-chunks of NBM blocks of BT tokens (kRowsSub = 64 tokens; the
-// SSD decomposition is exact for any chunk length, and the Gram kernel then
-// computes only the block pairs inside sub-chunks). Step sig of a sub-chunk
-// brings block sig's X_hat rows (both heads), B_hat rows, C~ rows and the
-// Gram tiles (tau, sig) of the blocks tau >= sig, and computes
-//   the readout of block sig from the sub-chunk's entering state,
-//   the intra term of block sig into every y block tau >= sig (the
-//     accumulators of the sub-chunk's blocks stay in registers),
-//   the carry of block sig into the state;
-// y block sig is then complete. Against a walk over block pairs: one step per
-// block instead of one per block pair, each X_hat and B_hat block copied once,
-// and, since every block's carry goes into the state anyway, block pairs
-// across sub-chunks cost one readout each instead of an intra term (per 128
-// tokens and wave 116 matrix-core ops instead of 136). The steps of a
-// sub-chunk are unrolled with sig a compile-time constant, so every
-// accumulator index is one (a run-time block index made the compiler move the
-// accumulators to scratch), and with NBM even the LDS stage of every step is
-// fixed too. Two stages: the copies of the next step are in flight while a
-// step computes. 128-token sub-chunks (10 block pairs per 4 steps, twice the
-// accumulators) spilled registers and ran at half the speed.
-constexpr int kRowsSub = 64;
-constexpr int kRowsThreads = 512;
+constexpr int kBlockThreads = 512;
 // load_kmajor with each read's lane offset made opaque to the optimiser, so
 // the LDS address is one step from the tile base: the LDS lowering gives an
 // access its alias scope only within a few address steps of the variable,
@@ -711,35 +694,34 @@ __device__ __forceinline__ typename Vec<T>::x8 load_kmajor_flat(const unsigned c
   }
   return v;
 }
-// f(integral_constant<int, I>) for I = I0 .. N-1
-template <int I, int N, class Fn>
-__device__ __forceinline__ void static_for(Fn&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>());
-    static_for<I + 1, N>(f);
-  }
-}
 
-template <typename T, int NP, int KS, int BT, int NBM>
-struct RowsLds {
-  static constexpr int HPW = 2;
+// The output walk one 32-token block per step, two heads per workgroup (8
+// waves; the heads share one copy of the group's B_hat, C~ and Gram tiles).
+// Every block is its own sub-chunk: the SSD split is exact for any chunk
+// length, so block sig's tokens take the cross-block part of y from the state
+// after the carry of block sig - 1, and only the diagonal Gram tiles are
+// needed. Step s copies block s's X_hat rows (both heads), B_hat rows, C~ rows
+// and its diagonal Gram tile, and computes
+//   y^T[p, t]  = a^{t+1} H^T C~^T + X^T (G o decay)^T     (readout + intra)
+//   H         <- a^{Ls} H + B_hat^T (a^{Ls-1-s} X)         (carry)
+// with the readout's fp16 operand converted from the state registers at the
+// step's start. Against walking 64-token sub-chunks: no fp16 copy of the
+// state in LDS (its writes and reads), no cross-block intra term, half the
+// Gram tiles, and the LDS left free holds a third stage, so the copies of
+// step s + 2 are in flight while step s computes.
+template <typename T, int NP, int KS, int BT>
+struct BlockLds {
   static constexpr int R = KS * BT;
   static constexpr int XROW = kP * (int)sizeof(T), BROW = NP * (int)sizeof(T);
   static constexpr int GROW = R * (int)sizeof(T);
   static constexpr int XB = R * XROW, BB = R * BROW, CB = BT * BROW, GB = BT * GROW;
-  static constexpr int XO = 0, BO = HPW * XB, CO = BO + BB, GO = CO + CB;
-  static constexpr int STAGE = GO + NBM * GB;
+  static constexpr int XO = 0, BO = 2 * XB, CO = BO + BB, GO = CO + CB;
+  static constexpr int STAGE = GO + GB;
 };
 
-// (chunk, sub-chunk) of the walk by source block
-struct SubChunk {
-  int ch, half;
-};
-
-template <typename T, typename TY, int NP, int KS, int BT, int NBM>
-__global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) {
-  static_assert(NBM % 2 == 0, "an even number of steps per sub-chunk keeps each step's stage fixed");
-  typedef RowsLds<T, NP, KS, BT, NBM> Lay;
+template <typename T, typename TY, int NP, int KS, int BT>
+__global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A) {
+  typedef BlockLds<T, NP, KS, BT> Lay;
   constexpr int R = Lay::R;
   constexpr int TT = BT / 16, RQ = R / 32, NT = NP / 16, NQ = NP / 32;
   constexpr int XC = Lay::XROW / 16, BC = Lay::BROW / 16, GC = Lay::GROW / 16;
@@ -748,17 +730,13 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
   constexpr uint32_t ES = sizeof(T);
   typedef typename Vec<T>::x8 F;
   constexpr int CX = dma_count<2 * R, XC, 8>(), CBn = dma_count<R, BC, 8>();
-  // the step's Gram tiles as one stack of NBM tiles (NBM * BT rows)
-  constexpr int CCn = dma_count<BT, BC, 8>(), CGA = dma_count<NBM * BT, GC, 8>();
-  constexpr int NCOPY = CX + CBn + CCn + CGA;
-  constexpr int S = NBM * BT;  // sub-chunk length
+  constexpr int CCn = dma_count<BT, BC, 8>(), CG = dma_count<BT, GC, 8>();
+  constexpr int NCOPY = CX + CBn + CCn + CG;
 
   __shared__ __align__(16) unsigned char stage0[Lay::STAGE];
   __shared__ __align__(16) unsigned char stage1[Lay::STAGE];
+  __shared__ __align__(16) unsigned char stage2[Lay::STAGE];
   __shared__ __align__(16) unsigned char sink[256];
-  // each wave's fp16 copy of the sub-chunk's entering state (the readout's
-  // operand), kept in LDS rather than in registers
-  __shared__ __align__(16) unsigned char hfl[8 * NQ * 64 * 16];
 
   const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
   const int HU = H / 2;
@@ -791,7 +769,8 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
       reinterpret_cast<const T*>(A.gram) + (size_t)b * A.nc * G * A.npairs * gtile,
       (uint64_t)A.nc * G * A.npairs * gtile * ES);
 
-  // ---- per-lane decay tables (as in scan_kernel)
+  // ---- per-lane decay tables: carry a^{BT-1-s} of pair row r = 32q + 8 g4 + j
+  // (s = r / k), readout a^t of token t = 16 tt + c, diagonal block a^{t-s}
   F er[RQ];
 #pragma unroll
   for (int q = 0; q < RQ; ++q)
@@ -800,7 +779,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
   float at[TT];
   F dm[NDF];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) at[tt] = apow(la, 16 * tt + c);
+  for (int tt = 0; tt < TT; ++tt) at[tt] = apow(la, 16 * tt + c) * ah;
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -814,6 +793,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
         }
       }
     }
+  const float aBT = apow(la, BT);
 
   // ---- entering state of this segment (this wave's columns)
   floatx4 Hr[NT];
@@ -838,19 +818,21 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
   const int ch0 = seg * A.seg_chunks;
   const int ch1 = min(nc, ch0 + A.seg_chunks);
   if (ch0 >= ch1) return;
-  auto chunk_len = [&](int ch) { return min(L, Tlen - ch * L); };
-  auto sub_len = [&](const SubChunk& u) { return min(S, chunk_len(u.ch) - u.half * S); };
-  auto next_sub = [&](SubChunk u) {
-    if (++u.half == (chunk_len(u.ch) + S - 1) / S) {
-      u.half = 0;
-      ++u.ch;
+  struct Blk {
+    int ch, sig;
+  };
+  auto nblocks = [&](int ch) { return (min(L, Tlen - ch * L) + BT - 1) / BT; };
+  auto advance = [&](Blk s) {
+    if (++s.sig == nblocks(s.ch)) {
+      s.sig = 0;
+      ++s.ch;
     }
-    return u;
+    return s;
   };
 
   // ---- copies of one step into a stage (every wave takes its share of each
-  // tile; X of both heads as one tile of 2R rows, as in the two-head walk)
-  uint32_t xoff[CX], boff[CBn], coff[CCn];
+  // tile; X of both heads as one tile of 2R rows)
+  uint32_t xoff[CX], boff[CBn], coff[CCn], goff[CG];
   int xrow[CX];
 #pragma unroll
   for (int m = 0; m < CX; ++m) {
@@ -861,27 +843,14 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
   }
   dma_plan_n<R, BC, 8>((uint32_t)GN * ES, w, lane, [](int r) { return swz_tr<T, BC>(r); }, boff);
   dma_plan_n<BT, BC, 8>((uint32_t)GN * ES, w, lane, [](int r) { return swz_row<T, BC>(r); }, coff);
-  // Gram stack: instruction m of this wave moves rows of tile gtau[m] only (8
-  // rows of a 32-row tile per 64 chunks), so a tile's position in HBM goes in
-  // the scalar offset; the lane's offset within its tile is fixed
-  uint32_t gaoff[CGA];
-  int gtau[CGA];
-#pragma unroll
-  for (int m = 0; m < CGA; ++m) {
-    const int slot = 64 * dma_group<NBM * BT, GC, 8>(m, w) + lane;
-    const int r = slot / GC, pc = slot % GC, rr = r % BT;
-    gtau[m] = r / BT;
-    gaoff[m] = rr * (uint32_t)R * ES + 16 * (pc ^ swz_row<T, GC>(rr));
-  }
+  dma_plan_n<BT, GC, 8>((uint32_t)R * ES, w, lane, [](int r) { return swz_row<T, GC>(r); }, goff);
   const bool nfull = N == NP;
 
-  // copies of step sig of sub-chunk u into a stage
-  auto fetch = [&](unsigned char* st, const SubChunk& u, int sig) {
-    const int c0 = u.ch * L + u.half * S;
-    const int Ls = sub_len(u);
-    const int nbs = (Ls + BT - 1) / BT;
-    const uint32_t prow = (uint32_t)(c0 + sig * BT) * KS;
-    const int rlim = (Ls - sig * BT) * KS;
+  auto fetch = [&](unsigned char* st, Blk s) {
+    const int c0 = s.ch * L + s.sig * BT;  // the block's first token
+    const int Ls = min(BT, Tlen - c0);
+    const uint32_t prow = (uint32_t)c0 * KS;
+    const int rlim = Ls * KS;
     const bool rows_full = rlim >= R;
     const uint32_t xb = (prow * (uint32_t)HPsz + 2 * hp * kP) * ES;
     if (rows_full)
@@ -894,52 +863,58 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
     else
       dma_tile_n<R, BC, 8>(rB, bb, GN * ES, st + Lay::BO, rlim, (int)(N * ES / 16), w, lane,
                            [](int r) { return swz_tr<T, BC>(r); });
-    const uint32_t cb = ((uint32_t)(c0 + sig * BT) * GN + grp * N) * ES;
-    if (Ls - sig * BT >= BT && nfull)
+    const uint32_t cb = ((uint32_t)c0 * GN + grp * N) * ES;
+    if (Ls >= BT && nfull)
       dma_tile_full_n<BT, BC, 8>(rC, cb, coff, st + Lay::CO, w);
     else
-      dma_tile_n<BT, BC, 8>(rC, cb, GN * ES, st + Lay::CO, Ls - sig * BT, (int)(N * ES / 16), w,
-                            lane, [](int r) { return swz_row<T, BC>(r); });
-    // Gram tiles (tau, sig) in the chunk's block numbering into slot tau of
-    // the stack; the slots of blocks before sig or past the sub-chunk read
-    // zeros (never used)
-    const int tb = u.half * NBM;
+      dma_tile_n<BT, BC, 8>(rC, cb, GN * ES, st + Lay::CO, Ls, (int)(N * ES / 16), w, lane,
+                            [](int r) { return swz_row<T, BC>(r); });
+    // the diagonal Gram tile (sig, sig) of chunk ch
+    const int pidx = s.sig * (s.sig + 1) / 2 + s.sig;
+    const uint32_t gb = (uint32_t)((((size_t)s.ch * G + grp) * A.npairs + pidx) * gtile * ES);
+    dma_tile_full_n<BT, GC, 8>(rG, gb, goff, st + Lay::GO, w);
+  };
+
+  floatx4 accY[TT];
+  bool ypend = false;  // y of the previous step waiting to be stored
+  size_t yrow0 = 0;
+  int ylim = 0;
+  auto store_y = [&]() {
+    if (!ypend) return;
+    typedef typename Vec<TY>::x4 Y4;
+    TY* yb = reinterpret_cast<TY*>(A.y) + yrow0 * HPsz + (size_t)h * kP + 16 * wc + 4 * g4;
 #pragma unroll
-    for (int m = 0; m < CGA; ++m) {
-      const int tau = __builtin_amdgcn_readfirstlane(gtau[m]);
-      uint32_t vo = kOOB, so = 0;
-      if (tau >= sig && tau < nbs) {
-        const int tc = tb + tau, sc = tb + sig;
-        const int pidx = tc * (tc + 1) / 2 + sc;
-        so = (uint32_t)((((size_t)u.ch * G + grp) * A.npairs + pidx) * gtile) * ES;
-        vo = gaoff[m];
+    for (int tt = 0; tt < TT; ++tt) {
+      const int tl = 16 * tt + c;
+      if (tl < ylim) {
+        Y4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[tt][i]);
+        *reinterpret_cast<Y4*>(yb + (size_t)tl * HPsz) = o;
       }
-      const int gi = dma_group<NBM * BT, GC, 8>(m, w);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rG, (__attribute__((address_space(3))) void*)(st + Lay::GO + 1024 * gi), 16, vo,
-          __builtin_amdgcn_readfirstlane(so), 0, 0);
     }
+    ypend = false;
   };
 
-  float hscale = 1.f;
-  floatx4 accY[NBM][TT];
-  // fragment q of this wave's fp16 entering state (scaled by 1/hscale)
-  const int hfo = w * NQ * 64 * 16 + 16 * lane;
-  // fragment q's address, one step from hfl (see load_kmajor_flat)
-  auto hfq = [&](int q) {
-    int o = hfo + q * 64 * 16;
-    asm("" : "+v"(o));
-    return hfl + o;
+  auto gfrag = [&](const unsigned char* Gt, int tt, int q) {
+    const int t = 16 * tt + c;
+    const int e0 = (32 * q + 8 * g4) * (int)ES;
+    return load8<T>(reinterpret_cast<const T*>(
+        Gt + (t * GC + ((e0 >> 4) ^ swz_row<T, GC>(t))) * 16 + (e0 & 15)));
   };
 
-  // the entering state of the next sub-chunk as fp16 operands in hfl, scaled
-  // by 2^-e (e >= 0 from this wave's max |H|) so they stay below 2^14. Called
-  // where no copy is in flight (after a step's wait), so that the writes to
-  // hfl wait for nothing; the wave-wide maximum is formed only when some lane
-  // holds a value past the bound.
-  auto stash_state = [&]() {
-    float hin = 1.f;
-    hscale = 1.f;
+  auto compute = [&](const unsigned char* st, Blk s) {
+    const unsigned char* Xs = st + Lay::XO + hw * Lay::XB;
+    const unsigned char* Bs = st + Lay::BO;
+    const unsigned char* Cs = st + Lay::CO;
+    const unsigned char* Gd = st + Lay::GO;
+    const int c0 = s.ch * L + s.sig * BT;
+    const int Ls = min(BT, Tlen - c0);
+
+    // ---- the block's entering state as fp16 operands, scaled by 2^-e (e >= 0
+    // from this wave's max |H|) so they stay below 2^14; the wave-wide maximum
+    // is formed only when some lane holds a value past the bound
+    float hin = 1.f, hscale = 1.f;
     if (sizeof(T) == 2) {
       float mx = 0.f;
 #pragma unroll
@@ -955,72 +930,13 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
         hscale = ldexpf(1.f, e);
       }
     }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      F hq;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hq[i] = from_f32<T>(Hr[2 * q][i] * hin);
-        hq[4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
-      }
-      *reinterpret_cast<F*>(hfq(q)) = hq;
-    }
-  };
-
-  auto gfrag = [&](const unsigned char* Gt, int tt, int q) {
-    const int t = 16 * tt + c;
-    const int e0 = (32 * q + 8 * g4) * (int)ES;
-    return load8<T>(reinterpret_cast<const T*>(
-        Gt + (t * GC + ((e0 >> 4) ^ swz_row<T, GC>(t))) * 16 + (e0 & 15)));
-  };
-
-  bool ypend = false;  // y block of the previous step waiting to be stored
-  size_t yrow0 = 0;
-  int ylim = 0;
-  // y block bl (a compile-time constant) of the previous step
-  auto store_y = [&](auto blc) {
-    constexpr int bl = decltype(blc)::value;
-    if (!ypend) return;
-    typedef typename Vec<TY>::x4 Y4;
-    TY* yb = reinterpret_cast<TY*>(A.y) + yrow0 * HPsz + (size_t)h * kP + 16 * wc + 4 * g4;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int tl = 16 * tt + c;
-      if (tl < ylim) {
-        Y4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = from_f32<TY>(accY[bl][tt][i]);
-        *reinterpret_cast<Y4*>(yb + (size_t)tl * HPsz) = o;
-      }
-    }
-    ypend = false;
-  };
-
-  // step sig (a compile-time constant) of sub-chunk u from stage st; last:
-  // no step follows in this walk
-  auto compute = [&](const unsigned char* st, const SubChunk& u, auto sigc, bool last) {
-    constexpr int sig = decltype(sigc)::value;
-    const unsigned char* Xs = st + Lay::XO + hw * Lay::XB;
-    const unsigned char* Bs = st + Lay::BO;
-    const unsigned char* Cs = st + Lay::CO;
-    const unsigned char* Gs = st + Lay::GO;
-    const int c0 = u.ch * L + u.half * S;
-    const int Ls = sub_len(u);
-    const int nbs = (Ls + BT - 1) / BT;
-
-    if constexpr (sig == 0) {
-#pragma unroll
-      for (int tb = 0; tb < NBM; ++tb) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) accY[tb][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
 
     F xq[RQ];  // X^T fragments of this wave's columns
 #pragma unroll
     for (int q = 0; q < RQ; ++q) xq[q] = load_kmajor_flat<T, XC>(Xs, 32 * q, 16 * wc, lane);
 
-    // ---- readout of block sig: y^T[p, t] = H^T[p, n] C~^T[n, t]
+    // ---- readout: y^T[p, t] = H^T[p, n] C~^T[n, t], n visited in the order
+    // {4 g4 .. 4 g4 + 3, 16 + 4 g4 .. 16 + 4 g4 + 3} per 32 (the accumulator's)
     {
       floatx4 ro[TT];
 #pragma unroll
@@ -1038,76 +954,47 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
           const T* p1 = reinterpret_cast<const T*>(Cs + (t * BC + ((e1 >> 4) ^ sw)) * 16 + (e1 & 15));
           cf[tt] = load4x2<T>(p0, p1);
         }
-        const F hq = *reinterpret_cast<const F*>(hfq(q));
-        __builtin_amdgcn_sched_barrier(0);
+        F hq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hq[i] = from_f32<T>(Hr[2 * q][i] * hin);
+          hq[4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
+        }
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) ro[tt] = mma16(hq, cf[tt], ro[tt]);
       }
-      const float ablk = (sig == 0 ? 1.f : apow_step(la, sig * BT)) * hscale * ah;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) accY[sig][tt] = accY[sig][tt] + ro[tt] * (at[tt] * ablk);
+      for (int tt = 0; tt < TT; ++tt) accY[tt] = ro[tt] * (at[tt] * hscale);
     }
-    // ---- intra term of the diagonal block pair (sig, sig)
-    {
-      const unsigned char* Gd = Gs + sig * Lay::GB;
+    // ---- intra term of the block
 #pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        F gf[TT];
+    for (int q = 0; q < RQ; ++q) {
+      F gf[TT];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          if (DF::index(tt, q) >= 0) gf[tt] = gfrag(Gd, tt, q);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int tt = 0; tt < TT; ++tt) {
+        if (DF::index(tt, q) >= 0) gf[tt] = gfrag(Gd, tt, q);
+      }
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          const int ix = DF::index(tt, q);
-          if (ix >= 0) accY[sig][tt] = mma16(xq[q], gf[tt] * dm[ix], accY[sig][tt]);
-        }
+      for (int tt = 0; tt < TT; ++tt) {
+        const int ix = DF::index(tt, q);
+        if (ix >= 0) accY[tt] = mma16(xq[q], gf[tt] * dm[ix], accY[tt]);
       }
     }
-    // ---- intra terms of block sig in the later blocks tau of the sub-chunk
-    static_for<sig + 1, NBM>([&](auto tauc) {
-      constexpr int tau = decltype(tauc)::value;
-      if (tau < nbs) {
-        const unsigned char* Gt = Gs + tau * Lay::GB;
-        floatx4 tmp[TT];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) tmp[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < RQ; ++q) {
-          F gf[TT];
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt) gf[tt] = gfrag(Gt, tt, q);
-          __builtin_amdgcn_sched_barrier(0);
-          const F xs = xq[q] * er[q];
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt) tmp[tt] = mma16(xs, gf[tt], tmp[tt]);
-        }
-        const float uf = apow_step(la, (tau - sig) * BT - (BT - 1));
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) accY[tau][tt] = accY[tau][tt] + tmp[tt] * (uf * at[tt]);
-      }
-    });
 
-    // ---- carry of block sig: H <- a^{Ls} H at the sub-chunk's first step
-    // (every readout of the sub-chunk uses the fp16 copy taken there), then
-    // H[n, p] += sum_r B_hat[r, n] (a^{Ls-1-s} X[r, p])
-    if constexpr (sig == 0) {
-      const float aL = apow_step(la, Ls);
+    // ---- carry: H <- a^{Ls} H + sum_r B_hat[r, n] (a^{Ls-1-s} X[r, p])
+    const bool full = Ls == BT;
+    const float aL = full ? aBT : apow_step(la, Ls);
 #pragma unroll
-      for (int a = 0; a < NT; ++a) Hr[a] = Hr[a] * aL;
-    }
-    const bool full = Ls == nbs * BT;
-    const float blk = apow_step(la, (nbs - 1 - sig) * BT);
+    for (int a = 0; a < NT; ++a) Hr[a] = Hr[a] * aL;
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
       F xd;
       if (full) {
-        xd = xq[q] * (er[q] * from_f32<T>(blk));
+        xd = xq[q] * er[q];
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int d = Ls - 1 - (sig * BT + (32 * q + 8 * g4 + j) / KS);
+          const int d = Ls - 1 - (32 * q + 8 * g4 + j) / KS;
           xd[j] = from_f32<T>(to_f32(xq[q][j]) * (d >= 0 ? apow_step(la, d) : 0.f));
         }
       }
@@ -1122,48 +1009,41 @@ __global__ __launch_bounds__(kRowsThreads, 1) void scan_rows_kernel(ScanArgs A) 
         for (int i = 0; i < CGR; ++i) Hr[a0 + i] = mma16(bf[i], xd, Hr[a0 + i]);
       }
     }
-
-    // ---- y block sig is complete: stored at the start of the next step
-    // (before its copies), or now when no step follows
     ypend = true;
-    yrow0 = (size_t)b * Tlen + c0 + sig * BT;
-    ylim = Ls - sig * BT;
-    if (last) store_y(sigc);
+    yrow0 = (size_t)b * Tlen + c0;
+    ylim = Ls;
   };
 
-  // ---- the walk: sub-chunk by sub-chunk, its NBM steps unrolled; step sig
-  // computes from stage sig % 2 while the copies of the next step go into the
-  // other; one barrier per step
-  SubChunk cur{ch0, 0};
-  fetch(stage0, cur, 0);
+  // ---- the walk: step s computes from stage s % 3 while the copies of step
+  // s + 2 go into stage (s + 2) % 3; one barrier per step
+  Blk s0{ch0, 0};
+  Blk s1 = advance(s0);
+  Blk s2 = s1.ch < ch1 ? advance(s1) : s1;
+  fetch(stage0, s0);
+  if (s1.ch < ch1)
+    fetch(stage1, s1);
+  else
+    dma_dummies<NCOPY>(rX, sink);
   wait_vm<0>();
-  stash_state();
   stage_barrier();
-  while (cur.ch < ch1) {
-    const SubChunk nxt = next_sub(cur);
-    const int nbs = (sub_len(cur) + BT - 1) / BT;
-    static_for<0, NBM>([&](auto sigc) {
-      constexpr int sig = decltype(sigc)::value;
-      unsigned char* cst = sig % 2 == 0 ? stage0 : stage1;
-      unsigned char* nst = sig % 2 == 0 ? stage1 : stage0;
-      // (a sub-chunk shorter than NBM blocks ends the sequence: its missing
-      // steps only wait, so that on every path no copy is in flight at a
-      // step's start and the compiler's wait model stays exact)
-      store_y(std::integral_constant<int, (sig + NBM - 1) % NBM>());
-      const bool more = sig + 1 < nbs || (sig + 1 == nbs && nxt.ch < ch1);
-      if (sig + 1 < nbs)
-        fetch(nst, cur, sig + 1);
-      else if (sig + 1 == nbs && nxt.ch < ch1)
-        fetch(nst, nxt, 0);
-      else
-        dma_dummies<NCOPY>(rX, sink);
-      if (sig < nbs) compute(cst, cur, sigc, !more);
-      wait_vm<0>();  // the next step's copies have landed
-      if constexpr (sig == NBM - 1) stash_state();
-      stage_barrier();
-    });
-    cur = nxt;
+  auto step = [&](const unsigned char* cur_st, unsigned char* far_st) {
+    store_y();  // the previous block's y, before this step's copies
+    if (s2.ch < ch1)
+      fetch(far_st, s2);
+    else
+      dma_dummies<NCOPY>(rX, sink);
+    compute(cur_st, s0);
+    wait_vm<NCOPY>();  // the next step's copies have landed
+    stage_barrier();
+    s0 = s1;
+    s1 = s2;
+    if (s2.ch < ch1) s2 = advance(s2);
+    return s0.ch < ch1;
+  };
+  while (step(stage0, stage2) && step(stage1, stage0) && step(stage2, stage1)) {
   }
+  store_y();
+  wait_vm<0>();  // the copies past the end land before the workgroup's LDS is released
 
   if (seg == A.segs - 1 && A.h_final) {
     float* dst = A.h_final + ((size_t)b * H + h) * NPsz;
@@ -1455,21 +1335,19 @@ static int scan_block(int N, int k, int L, int es) {
   return 32;
 }
 
-// The walk by source block (scan_rows_kernel, two heads per workgroup)
+// The walk one block per step (scan_block_kernel, two heads per workgroup)
 // serves 2-byte streams with k <= 2 and the shared decay when the heads of a
-// group pair up (H / G even), for chunks of 128 and 256 tokens. Measured on
-// MI355X against the walk by block pair it replaced (itself two heads per
-// workgroup): 4 x 8192 tokens, 64 heads, L = 128: chunk output 398 -> 356 us;
-// 65536 tokens, 32 heads, L = 256: 550 -> 350 us; with 64-token chunks (8 x
-// 2048 tokens, 24 heads) it was slower than one head per workgroup (82 -> 90
-// us), which those keep. SWIMBA_SCAN_WALK = 0 or 1 forces one or the other
-// where eligible.
-static int scan_walk(int H, int G, int k, int es, bool tv, int L) {
+// group pair up (H / G even). Measured on MI355X against the walks it
+// replaced: 4 x 8192 tokens, 64 heads, L = 128: chunk output 323 -> 300 us
+// (a walk of 64-token sub-chunks by source block, whose fp16 copy of the
+// entering state lived in LDS); 65536 tokens, 32 heads, L = 256: 319 -> 296
+// us; 8 x 2048 tokens, 24 heads, L = 64: 81 -> 78 us (one head per
+// workgroup). SWIMBA_SCAN_WALK = 0 forces one head per workgroup.
+static int scan_walk(int H, int G, int k, int es, bool tv) {
   static const int forced = env_int("SWIMBA_SCAN_WALK", -1);
-  const bool two = es == 2 && k <= 2 && !tv && (H / G) % 2 == 0 && L >= 64;
+  const bool two = es == 2 && k <= 2 && !tv && (H / G) % 2 == 0;
   if (forced == 0) return 0;
-  if (forced == 1 && two) return 1;
-  return two && L >= 128 ? 1 : 0;
+  return two ? 1 : 0;
 }
 static int walk_target_wgs(int L) {
   static const int w = env_int("SWIMBA_SCAN_WGS", 0);
@@ -1503,10 +1381,9 @@ static int scan_pieces(int units1, int seg_chunks) {
 
 // Pass 1 with two heads per workgroup (scan_carry_kernel) goes with the
 // two-head output walk (2-byte streams, k <= 2, the shared decay, heads of a
-// group in pairs, chunks of 128+ tokens). Measured on MI355X: 4 x 8192
-// tokens, 64 heads: 84 -> 75 us; 65536 tokens, 32 heads: 156 -> 136 us; with
-// 64-token chunks (8 x 2048 tokens, 24 heads: 384 workgroups, one per CU) it
-// was slower, 28 -> 40 us. SWIMBA_SCAN_CARRY = 0 keeps one head per workgroup.
+// group in pairs). Measured on MI355X: 4 x 8192 tokens, 64 heads: 84 -> 75
+// us; 65536 tokens, 32 heads: 156 -> 136 us; 8 x 2048 tokens, 24 heads, L =
+// 64: 29 -> 25 us. SWIMBA_SCAN_CARRY = 0 keeps one head per workgroup.
 static bool carry_two(const ScanGeom& g) {
   static const int on = env_int("SWIMBA_SCAN_CARRY", 1);
   return on > 0 && g.walk == 1;
@@ -1516,7 +1393,7 @@ ScanGeom scan_geom(int Bt, int T, int H, int G, int N, int P, int k, int L, int 
   ScanGeom g{Bt, T, H, G, N, P, k, L, es, scan_block(N, k, L, es), 1, 1, 0, 1};
   const int nc = (T + L - 1) / L;
   if (nc <= 0) return g;
-  g.walk = scan_walk(H, G, k, es, tv, L);
+  g.walk = scan_walk(H, G, k, es, tv);
   const int units = g.walk ? Bt * (H / 2) : Bt * H;
   int want = (g.walk ? walk_target_wgs(L) : scan_target_wgs(L)) / units;
   if (want > nc) want = nc;
@@ -1551,12 +1428,13 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   auto k1 = scan_kernel<T, TY, NP, KS, BT, false, TV>;
   const size_t l3 = 0, l1 = 0;  // static LDS (two stage arrays)
   prof_begin("scan_gram", s);
-  const int ng = args.npairs * g.G * args.nc * g.Bt;
+  const int diag = (sizeof(T) == 2 && KS <= 2 && !TV && g.walk == 1) ? 1 : 0;
+  const int ng = (diag ? g.L / BT : args.npairs) * g.G * args.nc * g.Bt;
   hipLaunchKernelGGL((scan_gram_kernel<T, NP, KS, BT>), dim3((unsigned)((ng + 7) / 8 * 8)),
                      dim3(256), 0, s, static_cast<const T*>(args.B_hat),
                      static_cast<const T*>(args.C_mix), static_cast<T*>(const_cast<void*>(args.gram)),
                      g.T, g.G, g.N, g.L, args.nc, args.npairs, g.Bt,
-                     (sizeof(T) == 2 && KS <= 2 && !TV && g.walk == 1) ? kRowsSub / BT : 0);
+                     diag);
   prof_end(s);
   if (g.segs > 1) {
     prof_begin("scan_segment_state", s);
@@ -1585,8 +1463,8 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
   if constexpr (sizeof(T) == 2 && KS <= 2 && !TV) {
     if (g.walk == 1) {
       const int n3 = (g.H / 2) * g.segs * g.Bt;
-      hipLaunchKernelGGL((scan_rows_kernel<T, TY, NP, KS, BT, kRowsSub / BT>),
-                         dim3((unsigned)((n3 + 7) / 8 * 8)), dim3(kRowsThreads), 0, s, args);
+      hipLaunchKernelGGL((scan_block_kernel<T, TY, NP, KS, BT>), dim3((unsigned)((n3 + 7) / 8 * 8)),
+                         dim3(kBlockThreads), 0, s, args);
       prof_end(s);
       return hipGetLastError();
     }
