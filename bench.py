@@ -71,7 +71,7 @@ KERNEL_NAMES = [
     # (types, NP, KS, BT, WITH_Y, TV): WITH_Y follows the block size
     (r"scan_kernel.*Li\d+ELb0ELb[01]E|scan_carry_kernel", "scan_segment_state"),
     (r"scan_combine_kernel", "scan_state_pass"),
-    (r"scan_kernel.*Li\d+ELb1ELb[01]E|scan_rows_kernel", "scan_chunk_output"),
+    (r"scan_kernel.*Li\d+ELb1ELb[01]E|scan_block_kernel", "scan_chunk_output"),
     (r"state_copy_kernel", "state_copy"),
     (r"sep_scatter_kernel", "sep_scatter"),
     (r"sep_sum_kernel", "sep_sum"),

@@ -262,15 +262,36 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
   // second 8 (m / 4) + 4 + m % 4, so lane group g ends up with the 8
   // consecutive columns 8g .. 8g + 7 of the pair (one 16-byte store).
   auto bcol = [&](int j) { return wn * TN * 16 + 32 * (j >> 1) + 8 * (c >> 2) + 4 * (j & 1) + (c & 3); };
+  // The matrix-core ops of the last DEF fragment rows of K tile kt are issued
+  // after the reads of tile kt + 1 (past its barrier), so that they cover the
+  // wait for those reads: 1-2 % at c3 and c4 (4 x 8192 and 65536 tokens),
+  // bit-identical results.
+  constexpr int DEF = TM > 1 ? 1 : 0;
+  F bfr[TN], afr[TM];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bfr[j] = zero8<T>();
+#pragma unroll
+  for (int i = 0; i < TM; ++i) afr[i] = zero8<T>();
+  auto mma_tail = [&]() {
+#pragma unroll
+    for (int i = TM - DEF; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mma16(bfr[j], afr[i], acc[i][j]);
+  };
   auto compute = [&](const unsigned char* st) {
-    // all fragments of the K tile first, then the matrix-core ops
-    F bfr[TN], afr[TM];
+    F nb[TN], na[TM];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[j] = frag(st + Lay::AB, bcol(j));
+    for (int j = 0; j < TN; ++j) nb[j] = frag(st + Lay::AB, bcol(j));
 #pragma unroll
-    for (int i = 0; i < TM; ++i) afr[i] = frag(st, wm * TM * 16 + 16 * i + c);
+    for (int i = 0; i < TM; ++i) na[i] = frag(st, wm * TM * 16 + 16 * i + c);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_tail();
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j) bfr[j] = nb[j];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) afr[i] = na[i];
+#pragma unroll
+    for (int i = 0; i < TM - DEF; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mma16(bfr[j], afr[i], acc[i][j]);
   };
@@ -296,6 +317,7 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
     iter(kt + 2, stg2, stg1);
     iter(kt + 3, stg3, stg2);
   }
+  mma_tail();
   wait_vm<0>();  // the copies past the end land before the workgroup's LDS is released
 
   // ---- epilogue: each lane stores 8 consecutive columns of one pair row per
