@@ -354,6 +354,21 @@ void prof_end(hipStream_t s) {
   hipEventRecord(g_prof_recs.back().stop, s);
 }
 
+void prof_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  std::string full = std::string(g_prof_prefix) + name;
+  if (!g_prof_only.empty() &&
+      std::find(g_prof_only.begin(), g_prof_only.end(), full) == g_prof_only.end())
+    return;
+  ProfRec r{full, prof_event(), prof_event()};
+  if (!r.start || !r.stop) return;
+  g_prof_recs.push_back(r);
+  *start = r.start;
+  *stop = r.stop;
+}
+
 }  // namespace swimba
 
 // ---------------------------------------------------------------- C ABI

@@ -2,6 +2,7 @@
 // its launch(es); arguments are validated by the API layer before any call.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -11,6 +12,12 @@ namespace swimba {
 // Optional per-kernel timing (see swimba_profile_enable in the public header).
 void prof_begin(const char* name, hipStream_t s);  // no-op unless profiling is on
 void prof_end(hipStream_t s);
+// One kernel timed under `name`: when profiling selects it, *start and *stop
+// are events for the kernel's launch (hipExtLaunchKernelGGL), which takes the
+// kernel's own start and end times, so no event packet goes between kernels
+// (each such packet held the stream for several microseconds); otherwise both
+// are null, and the launch behaves as a plain one.
+void prof_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
 struct ProjGeom {
   int M, D, H, P, G, N, E, k, W;

@@ -645,16 +645,17 @@ static hipError_t launch_proj_cfg(const ProjGeom& g, const T* u, const T* wexp,
   const int nrow = proj_row_tiles_max(pairs, g.E, C::BM);
   const int ntiles = nrow * ((g.W + C::BN - 1) / C::BN);
   const dim3 grid((unsigned)((ntiles + 7) / 8 * 8));  // a multiple of the 8 XCDs
-  prof_begin("expert_project", s);
+  hipEvent_t e0, e1;
+  prof_kernel("expert_project", &e0, &e1);
   if (g.D % (kProjStages * ProjLay<T, C>::BK) == 0)
-    hipLaunchKernelGGL((proj_kernel<T, C, false, float, true>), grid, dim3(C::NTH), 0, s, u, wexp,
-                       sorted, sorted_w, tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow,
-                       X_hat, B_hat, c_part, (float*)nullptr, g.bw_one, proj_group_rows());
+    hipExtLaunchKernelGGL((proj_kernel<T, C, false, float, true>), grid, dim3(C::NTH), 0, s, e0, e1,
+                          0, u, wexp, sorted, sorted_w, tile_info, g.M, g.D, g.W, g.HP(), g.GN(),
+                          g.k, nrow, X_hat, B_hat, c_part, (float*)nullptr, g.bw_one,
+                          proj_group_rows());
   else
-    hipLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, u, wexp, sorted, sorted_w,
-                       tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part,
-                       (float*)nullptr, g.bw_one, proj_group_rows());
-  prof_end(s);
+    hipExtLaunchKernelGGL((proj_kernel<T, C>), grid, dim3(C::NTH), 0, s, e0, e1, 0, u, wexp, sorted,
+                          sorted_w, tile_info, g.M, g.D, g.W, g.HP(), g.GN(), g.k, nrow, X_hat,
+                          B_hat, c_part, (float*)nullptr, g.bw_one, proj_group_rows());
   return hipGetLastError();
 }
 
@@ -671,12 +672,12 @@ static hipError_t launch_project_t(const ProjGeom& g, const T* u, const T* wexp,
     if (bm == 64) {
       const int nrow = proj_row_tiles_max(g.M * g.k, g.E, 64);
       const int ntiles = nrow * ((g.W + kSkBN - 1) / kSkBN);
-      prof_begin("expert_project", s);
-      hipLaunchKernelGGL(proj_skinny_kernel<false>, dim3((unsigned)((ntiles + 7) / 8 * 8)),
-                         dim3(256), 0, s, u, wexp, sorted, sorted_w, ti, g.M, g.D, g.W, g.HP(),
-                         g.GN(), g.k, nrow, X_hat, B_hat, c_part, g.bw_one,
-                         (const int32_t*)nullptr, (const float*)nullptr, g.E);
-      prof_end(s);
+      hipEvent_t e0, e1;
+      prof_kernel("expert_project", &e0, &e1);
+      hipExtLaunchKernelGGL(proj_skinny_kernel<false>, dim3((unsigned)((ntiles + 7) / 8 * 8)),
+                            dim3(256), 0, s, e0, e1, 0, u, wexp, sorted, sorted_w, ti, g.M, g.D,
+                            g.W, g.HP(), g.GN(), g.k, nrow, X_hat, B_hat, c_part, g.bw_one,
+                            (const int32_t*)nullptr, (const float*)nullptr, g.E);
       err = hipGetLastError();
     } else if (bm == 256)
       err = launch_proj_cfg<T, ProjBig>(g, u, wexp, sorted, sorted_w, ti, B_hat, X_hat, c_part, s);
@@ -747,12 +748,13 @@ hipError_t launch_project_direct(const ProjGeom& g, const void* u, const void* w
                                  void* X_hat, float* c_part, hipStream_t s) {
   if (g.M == 0) return hipSuccess;
   const int units = g.E * ((g.W + kSkBN - 1) / kSkBN);
-  prof_begin("expert_project", s);
-  hipLaunchKernelGGL(proj_skinny_kernel<true>, dim3((unsigned)((units + 7) / 8 * 8)), dim3(256),
-                     0, s, (const bf16*)u, (const bf16*)w_experts, (const int32_t*)nullptr,
-                     (const float*)nullptr, (const int4v*)nullptr, g.M, g.D, g.W, g.HP(), g.GN(),
-                     g.k, 0, (f16*)X_hat, (f16*)B_hat, c_part, g.bw_one, idx, topk_w, g.E);
-  prof_end(s);
+  hipEvent_t e0, e1;
+  prof_kernel("expert_project", &e0, &e1);
+  hipExtLaunchKernelGGL(proj_skinny_kernel<true>, dim3((unsigned)((units + 7) / 8 * 8)), dim3(256),
+                        0, s, e0, e1, 0, (const bf16*)u, (const bf16*)w_experts,
+                        (const int32_t*)nullptr, (const float*)nullptr, (const int4v*)nullptr, g.M,
+                        g.D, g.W, g.HP(), g.GN(), g.k, 0, (f16*)X_hat, (f16*)B_hat, c_part,
+                        g.bw_one, idx, topk_w, g.E);
   return hipGetLastError();
 }
 

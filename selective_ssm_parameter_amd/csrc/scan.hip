@@ -1459,19 +1459,20 @@ static hipError_t launch_scan_t(const ScanGeom& g, ScanArgs args, hipStream_t s)
                        (g.segs - 1) * g.sub + 1, g.seg_chunks / g.sub, args.ld);
     prof_end(s);
   }
-  prof_begin("scan_chunk_output", s);
+  hipEvent_t e0, e1;
+  prof_kernel("scan_chunk_output", &e0, &e1);
   if constexpr (sizeof(T) == 2 && KS <= 2 && !TV) {
     if (g.walk == 1) {
       const int n3 = (g.H / 2) * g.segs * g.Bt;
-      hipLaunchKernelGGL((scan_block_kernel<T, TY, NP, KS, BT>), dim3((unsigned)((n3 + 7) / 8 * 8)),
-                         dim3(kBlockThreads), 0, s, args);
-      prof_end(s);
+      hipExtLaunchKernelGGL((scan_block_kernel<T, TY, NP, KS, BT>),
+                            dim3((unsigned)((n3 + 7) / 8 * 8)), dim3(kBlockThreads), 0, s, e0, e1,
+                            0, args);
       return hipGetLastError();
     }
   }
   const int n3 = g.H * g.segs * g.Bt;
-  hipLaunchKernelGGL(k3, dim3((unsigned)((n3 + 7) / 8 * 8)), dim3(kScanThreads), l3, s, args);
-  prof_end(s);
+  hipExtLaunchKernelGGL(k3, dim3((unsigned)((n3 + 7) / 8 * 8)), dim3(kScanThreads), l3, s, e0, e1,
+                        0, args);
   return hipGetLastError();
 }
 
