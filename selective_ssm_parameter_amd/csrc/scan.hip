@@ -14,8 +14,8 @@
 //
 // Kernels (MI355X-first rather than the three separate SSD passes of the prior
 // art):
-//   scan_gram:   G[t, r] = C~_t . B_hat_r for every causal block pair of every
-//                chunk, once per group: it does not depend on the head, so the
+//   scan_gram:   G[t, r] = C~_t . B_hat_r for the block pairs the output walk
+//                reads, once per group: it does not depend on the head, so the
 //                heads of a group share it instead of recomputing it.
 //   pass 1:      (several segments per sequence only) every segment but the
 //                last computes its end state from zero, carry recurrence only;
@@ -23,7 +23,13 @@
 //                over segments: Hin_0 = h_init, Hin_{s+1} = a^{len_s} Hin_s + S_s;
 //   pass 3:      every segment walks its chunks from Hin_s and writes y; the
 //                last segment also writes h_final.
-// A workgroup of passes 1 and 3 is 4 waves and owns (sequence, segment, head);
+// Passes 1 and 3 have two forms. For 2-byte streams, k <= 2 and the shared
+// decay (the prefill hot path), two heads of a group share a workgroup of 8
+// waves and walk one 32-token block per step (scan_carry_kernel,
+// scan_block_kernel, described at their definitions). Otherwise (fp32
+// streams, k = 3 or 4, the expert-mixed decay, an odd number of heads per
+// group) scan_kernel below walks one head per workgroup:
+// a workgroup of passes 1 and 3 is 4 waves and owns (sequence, segment, head);
 // wave w owns the head columns p in [16w, 16w + 16). Its slice of the state
 // lives in fp32 matrix-core accumulators (rows n, column p) for the whole
 // segment, so per-chunk states never go to HBM or LDS: the readout C~ H takes
