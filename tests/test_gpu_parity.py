@@ -237,6 +237,41 @@ def test_ssd_chunk_scan(name, wl, h0):
     assert eh < TOL[wl.dtype]
 
 
+# An entering state far above 2^14: the walks convert the state to an fp16
+# readout operand only after scaling it by a power of two, found per block
+# from the state's largest value; these cases take that branch in every block
+# (the two-head block walk with k = 2, the one-head walk with k = 4).
+BIG_STATE_CASES = [
+    ("bf16_L128_pairs_big_h0", W("s25", 325, chunk=128, seqlen=300)),
+    ("bf16_k4_L64_big_h0", W("s26", 326, top_k=4, chunk=64, seqlen=200)),
+]
+
+
+@pytest.mark.parametrize("name,wl", BIG_STATE_CASES, ids=[c[0] for c in BIG_STATE_CASES])
+def test_scan_large_state(name, wl):
+    say(f"[scan big state] {name} T={wl.seqlen} L={wl.chunk} k={wl.top_k}")
+    inp = with_h0(wl, synth.make_inputs(wl), scale=3e4)
+    assert np.max(np.abs(inp["h_init"])) > 4 * 16384
+    B_hat, X, C_mix = oracle_streams(wl, inp)
+    B_hat, X, C_mix = round_stream(B_hat, wl), round_stream(X, wl), round_stream(C_mix, wl)
+    y_ref, h_ref = osw.recurrence(B_hat, X, C_mix, inp["a"].astype(np.float64), inp["h_init"],
+                                  wl.batch, wl.seqlen)
+    dims = sb.dims_of(wl)
+    y = torch.empty(wl.tokens, wl.nheads, 64, dtype=tdt(wl), device="cuda")
+    hf = torch.empty(wl.batch, wl.nheads, wl.dstate, 64, dtype=torch.float32, device="cuda")
+    ws, _ = sb.workspace(dims, sb.CALL_SCAN)
+    st = sdt(wl)
+    sb.swimba_ssd_chunk_scan(dims, dev(B_hat, st), dev(X, st), dev(C_mix, st),
+                             dev(inp["a"], torch.float32), dev(inp["h_init"], torch.float32), y,
+                             hf, ws)
+    torch.cuda.synchronize()
+    ey = slice_err(host(y).reshape(wl.batch, wl.seqlen, wl.nheads, 64), y_ref)
+    eh = slice_err(host(hf), h_ref, axes_slice=(0, 1))
+    say(f"  y err {ey:.3e}  h_final err {eh:.3e}")
+    assert ey < TOL[wl.dtype]
+    assert eh < TOL[wl.dtype]
+
+
 def test_scan_h_final_aliases_h_init():
     wl = W("s12", 312, seqlen=700, batch=2, nheads=2)
     inp = with_h0(wl, synth.make_inputs(wl))
