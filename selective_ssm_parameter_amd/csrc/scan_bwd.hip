@@ -98,13 +98,34 @@ __device__ __forceinline__ int elem_off(int r, int col) {
   constexpr int EPC = 16 / (int)sizeof(T);
   return chunk_off<T, CPR>(r, col / EPC) + (col % EPC) * (int)sizeof(T);
 }
+// Elements col .. col + 3 of row r (col a multiple of 4: one 8-byte piece of a
+// 16-byte chunk for 2-byte types, a whole chunk for fp32), as fp32.
 template <typename T, int CPR>
-__device__ __forceinline__ float lds_get(const unsigned char* t, int r, int col) {
-  return to_f32(*reinterpret_cast<const T*>(t + elem_off<T, CPR>(r, col)));
+__device__ __forceinline__ floatx4 lds_get4(const unsigned char* t, int r, int col) {
+  floatx4 v;
+  if constexpr (sizeof(T) == 2) {
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    const T4 x = *reinterpret_cast<const T4*>(t + elem_off<T, CPR>(r, col));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = to_f32(x[q]);
+  } else {
+    v = *reinterpret_cast<const floatx4*>(t + elem_off<T, CPR>(r, col));
+  }
+  return v;
 }
+// Elements col .. col + 3 of row r (col a multiple of 4) from fp32 values:
+// one 8-byte write for 2-byte types, one 16-byte write for fp32.
 template <typename T, int CPR>
-__device__ __forceinline__ void lds_put(unsigned char* t, int r, int col, float v) {
-  *reinterpret_cast<T*>(t + elem_off<T, CPR>(r, col)) = from_f32<T>(v);
+__device__ __forceinline__ void lds_put4(unsigned char* t, int r, int col, floatx4 v) {
+  if constexpr (sizeof(T) == 2) {
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    T4 x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = from_f32<T>(v[q]);
+    *reinterpret_cast<T4*>(t + elem_off<T, CPR>(r, col)) = x;
+  } else {
+    *reinterpret_cast<floatx4*>(t + elem_off<T, CPR>(r, col)) = v;
+  }
 }
 
 // Fragment along tile rows: lane (g, c) gets row r0 + c, elements
@@ -547,7 +568,7 @@ template <typename T, typename S, typename TY, int NP, int KS, int BL>
 __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
   constexpr int NW = kGradWaves, NT = 64 * NW;
   constexpr int R = KS * BL, ES = sizeof(T);
-  constexpr int CB = NP * ES / 16, CX = kBP * ES / 16, CG = R * ES / 16;
+  constexpr int CB = NP * ES / 16, CX = kBP * ES / 16, CG = R * ES / 16, CD = BL * ES / 16;
   constexpr int NGT = (BL / 16) * (R / 16);   // Gm and D tiles
   constexpr int NXT = (kBP / 16) * (R / 16);  // dX tiles
   constexpr int NBT = (NP / 16) * (R / 16);   // dB_hat tiles
@@ -557,8 +578,8 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
   __shared__ __align__(16) unsigned char Cs[BL * NP * ES];   // C~ [s][n]
   __shared__ __align__(16) unsigned char Xs[R * kBP * ES];   // X_r of the head [r][p]
   __shared__ __align__(16) unsigned char Dys[BL * kBP * ES]; // dy_s of the head [s][p]
-  __shared__ __align__(16) unsigned char Dm[BL * R * ES];    // masked, decayed D [s][r]
-  __shared__ __align__(16) unsigned char GmM[BL * R * ES];   // masked, decayed Gm [s][r]
+  __shared__ __align__(16) unsigned char Dm[R * BL * ES];    // masked, decayed D [r][s]
+  __shared__ __align__(16) unsigned char GmM[R * BL * ES];   // masked, decayed Gm [r][s]
   __shared__ __align__(16) unsigned char Ss[NP * kBP * ES];  // F_c [n][p]
   __shared__ __align__(16) unsigned char Hs[NP * kBP * ES];  // H_c [n][p]
   __shared__ float pw[BL + 2];                               // a^d of the head
@@ -679,21 +700,24 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
       const int s0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
       const floatx4 v = tmm_b<T, true, CX, kBP / 32>(Dys, s0, fx, lane);
       const int r = r0 + cl, tr = r / KS;
+      floatx4 dv, dg;  // this lane's 4 consecutive s of row r, stored [r][s]
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int s = s0 + 4 * g + q;
         const bool in = tr <= s && s < Lc;
         const float dec = in ? pw[s - tr] : 0.f;
         if (in && tr < s) dap += (float)(s - tr) * pw[s - tr - 1] * gm[i][q] * v[q] * udy;
-        lds_put<T, CG>(Dm, s, r, dec * v[q]);
-        lds_put<T, CG>(GmM, s, r, dec * gm[i][q]);
+        dv[q] = dec * v[q];
+        dg[q] = dec * gm[i][q];
       }
+      lds_put4<T, CD>(Dm, r, s0 + 4 * g, dv);
+      lds_put4<T, CD>(GmM, r, s0 + 4 * g, dg);
     }
     __syncthreads();
-    // dX_r^T[p] = sum_s dy_s[p] GmM[s][r] + a^{Lc-1-t} (F_c^T B_hat_r)[p]
+    // dX_r^T[p] = sum_s dy_s[p] GmM(s, r) + a^{Lc-1-t} (F_c^T B_hat_r)[p]
     {
       F fg[BL / 32], fb[NP / 32];
-      load_frags<T, false, CG, BL / 32>(GmM, 16 * (wave % (R / 16)), fg, lane);
+      load_frags<T, true, CD, BL / 32>(GmM, 16 * (wave % (R / 16)), fg, lane);
       load_frags<T, true, CB, NP / 32>(Bs, 16 * (wave % (R / 16)), fb, lane);
     for (int t = wave; t < NXT; t += NW) {
       const int p0 = 16 * (t / (R / 16)), r0 = 16 * (t % (R / 16));
@@ -707,9 +731,9 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
       }
     }
     }
-    // dB_hat_r[n] += sum_s C~_s[n] Dm[s][r] + a^{Lc-1-t} (F_c X_r)[n]
+    // dB_hat_r[n] += sum_s C~_s[n] Dm(s, r) + a^{Lc-1-t} (F_c X_r)[n]
     F fd[BL / 32];
-    load_frags<T, false, CG, BL / 32>(Dm, 16 * (wave % (R / 16)), fd, lane);
+    load_frags<T, true, CD, BL / 32>(Dm, 16 * (wave % (R / 16)), fd, lane);
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       const int t = wave + NW * i;
@@ -720,14 +744,15 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
       const int r = r0 + cl, tr = r / KS;
       const float sc = tr < Lc ? pw[Lc - 1 - tr] : 0.f;
       const float wt = tr + 1 < Lc ? (float)(Lc - 1 - tr) * pw[Lc - 2 - tr] : 0.f;
+      const floatx4 bq = lds_get4<T, CB>(Bs, r, n0 + 4 * g);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dap += wt * uF * w[q] * lds_get<T, CB>(Bs, r, n0 + 4 * g + q);
+      for (int q = 0; q < 4; ++q) dap += wt * uF * w[q] * bq[q];
       dBa[i] = dBa[i] + v * udy + w * (sc * uF);
       __builtin_amdgcn_sched_barrier(0);  // keep the tiles' reads from piling up in registers
     }
-    // dC~_s[n] += sum_r B_hat_r[n] Dm[s][r] + a^{s+1} (H_c dy_s)[n]
+    // dC~_s[n] += sum_r B_hat_r[n] Dm(s, r) + a^{s+1} (H_c dy_s)[n]
     F fm[R / 32], fy[kBP / 32];
-    load_frags<T, true, CG, R / 32>(Dm, 16 * (wave % (BL / 16)), fm, lane);
+    load_frags<T, false, CD, R / 32>(Dm, 16 * (wave % (BL / 16)), fm, lane);
     load_frags<T, true, CX, kBP / 32>(Dys, 16 * (wave % (BL / 16)), fy, lane);
 #pragma unroll
     for (int i = 0; i < CI; ++i) {
@@ -739,8 +764,9 @@ __global__ __launch_bounds__(64 * kGradWaves) void bwd_grad_kernel(BwdArgs A) {
       const int s = s0 + cl;
       const float sc = s < Lc ? pw[s + 1] : 0.f;
       const float wt = s < Lc ? (float)(s + 1) * pw[s] : 0.f;
+      const floatx4 cq = lds_get4<T, CB>(Cs, s, n0 + 4 * g);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dap += wt * uHdy * w[q] * lds_get<T, CB>(Cs, s, n0 + 4 * g + q);
+      for (int q = 0; q < 4; ++q) dap += wt * uHdy * w[q] * cq[q];
       dCa[i] = dCa[i] + v * udy + w * (sc * uHdy);
       __builtin_amdgcn_sched_barrier(0);
     }
