@@ -701,6 +701,38 @@ __device__ __forceinline__ typename Vec<T>::x8 load_kmajor_flat(const unsigned c
   return v;
 }
 
+// Byte offset within a tile of lane `lane`'s half hh of the K-major fragment
+// that load_kmajor_flat reads at k0 = 0 and column col0. The swizzle depends on
+// the row's low three bits only, so the read at k0 (a multiple of 32) lies
+// k0 * CPR * 16 bytes further on.
+template <typename T, int CPR>
+__device__ __forceinline__ int kmajor_off(int col0, int hh, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int r = 8 * g + 4 * hh + (c >> 2);
+  const int col = col0 + 4 * (c & 3);
+  const int ch = col >> 3, half = (col >> 2) & 1;
+  return (r * CPR + (ch ^ swz_tr<T, CPR>(r))) * 16 + 8 * half;
+}
+// The fragment at lane offsets off[0], off[1] (made opaque once, where they
+// are planned, so that each read is one address step from its stage array and
+// keeps the array's alias scope) plus kb bytes (a constant).
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x8 load_kmajor_at(const unsigned char* stage,
+                                                              const int (&off)[2], int kb) {
+  typedef typename Vec<T>::x8 F;
+  typedef short s4 __attribute__((__vector_size__(8)));
+  F v;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const typename Vec<T>::x4 w4 = __builtin_bit_cast(
+        typename Vec<T>::x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                 (__attribute__((address_space(3))) s4*)(stage + off[hh] + kb)));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) v[4 * hh + m] = w4[m];
+  }
+  return v;
+}
+
 // The output walk one 32-token block per step, two heads per workgroup (8
 // waves; the heads share one copy of the group's B_hat, C~ and Gram tiles).
 // Every block is its own sub-chunk: the SSD split is exact for any chunk
@@ -760,6 +792,35 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
   const size_t NPsz = (size_t)N * kP;
   const size_t HPsz = (size_t)H * kP;
   const int prow_x = 16 * wc + c;
+  // lane offsets of the transposing reads within a stage: this wave's X
+  // columns of its head, and the B_hat columns of each 16-wide n tile
+  int xo[2], bo[NT][2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    xo[hh] = Lay::XO + hw * Lay::XB + kmajor_off<T, XC>(16 * wc, hh, lane);
+    asm("" : "+v"(xo[hh]));
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      bo[a][hh] = Lay::BO + kmajor_off<T, BC>(16 * a, hh, lane);
+      asm("" : "+v"(bo[a][hh]));
+    }
+  }
+  // lane offsets of the readout's C~ reads within a stage: token t = 16 tt + c,
+  // n0 = 32 q + 4 g4 and n0 + 16, four elements each (one opaque offset per
+  // read, so that the two tiles' reads are not merged into one whose halves
+  // then have to be moved into place)
+  int co[TT][NQ][2];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int t = 16 * tt + c;
+        const int e0 = (32 * q + 16 * m + 4 * g4) * (int)ES;
+        co[tt][q][m] = Lay::CO + (t * BC + ((e0 >> 4) ^ swz_row<T, BC>(t))) * 16 + (e0 & 15);
+        asm("" : "+v"(co[tt][q][m]));
+      }
 
   const float ah = A.a[h];
   const float la = ah > 0.f ? log2f(ah) : -1e30f;
@@ -910,16 +971,14 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
   };
 
   auto compute = [&](const unsigned char* st, Blk s) {
-    const unsigned char* Xs = st + Lay::XO + hw * Lay::XB;
-    const unsigned char* Bs = st + Lay::BO;
-    const unsigned char* Cs = st + Lay::CO;
     const unsigned char* Gd = st + Lay::GO;
     const int c0 = s.ch * L + s.sig * BT;
     const int Ls = min(BT, Tlen - c0);
 
-    // ---- the block's entering state as fp16 operands, scaled by 2^-e (e >= 0
-    // from this wave's max |H|) so they stay below 2^14; the wave-wide maximum
-    // is formed only when some lane holds a value past the bound
+    // ---- the block's entering state as fp16 operands; past 2^14 (found from
+    // this wave's max |H| with one ballot) they are scaled by 2^-e, e >= 0, and
+    // the readout by 2^e
+    bool scaled = false;
     float hin = 1.f, hscale = 1.f;
     if (sizeof(T) == 2) {
       float mx = 0.f;
@@ -934,16 +993,18 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
         const int e = (int)ceilf(log2f(mx * (1.f / 16384.f)));
         hin = ldexpf(1.f, -e);
         hscale = ldexpf(1.f, e);
+        scaled = true;
       }
     }
 
     F xq[RQ];  // X^T fragments of this wave's columns
 #pragma unroll
-    for (int q = 0; q < RQ; ++q) xq[q] = load_kmajor_flat<T, XC>(Xs, 32 * q, 16 * wc, lane);
+    for (int q = 0; q < RQ; ++q) xq[q] = load_kmajor_at<T>(st, xo, 32 * q * XC * 16);
 
     // ---- readout: y^T[p, t] = H^T[p, n] C~^T[n, t], n visited in the order
     // {4 g4 .. 4 g4 + 3, 16 + 4 g4 .. 16 + 4 g4 + 3} per 32 (the accumulator's)
-    {
+    auto readout = [&](auto scale_tag) {
+      constexpr bool SC = decltype(scale_tag)::value;
       floatx4 ro[TT];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) ro[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -951,27 +1012,25 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
       for (int q = 0; q < NQ; ++q) {
         F cf[TT];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          const int t = 16 * tt + c;
-          const int n0 = 32 * q + 4 * g4;
-          const int e0 = n0 * (int)ES, e1 = (n0 + 16) * (int)ES;
-          const int sw = swz_row<T, BC>(t);
-          const T* p0 = reinterpret_cast<const T*>(Cs + (t * BC + ((e0 >> 4) ^ sw)) * 16 + (e0 & 15));
-          const T* p1 = reinterpret_cast<const T*>(Cs + (t * BC + ((e1 >> 4) ^ sw)) * 16 + (e1 & 15));
-          cf[tt] = load4x2<T>(p0, p1);
-        }
+        for (int tt = 0; tt < TT; ++tt)
+          cf[tt] = load4x2<T>(reinterpret_cast<const T*>(st + co[tt][q][0]),
+                              reinterpret_cast<const T*>(st + co[tt][q][1]));
         F hq;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          hq[i] = from_f32<T>(Hr[2 * q][i] * hin);
-          hq[4 + i] = from_f32<T>(Hr[2 * q + 1][i] * hin);
+          hq[i] = from_f32<T>(SC ? Hr[2 * q][i] * hin : Hr[2 * q][i]);
+          hq[4 + i] = from_f32<T>(SC ? Hr[2 * q + 1][i] * hin : Hr[2 * q + 1][i]);
         }
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) ro[tt] = mma16(hq, cf[tt], ro[tt]);
       }
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) accY[tt] = ro[tt] * (at[tt] * hscale);
-    }
+      for (int tt = 0; tt < TT; ++tt) accY[tt] = ro[tt] * (SC ? at[tt] * hscale : at[tt]);
+    };
+    if (scaled)
+      readout(std::true_type{});
+    else
+      readout(std::false_type{});
     // ---- intra term of the block
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
@@ -1009,7 +1068,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
       // slower)
       F bf[NT];
 #pragma unroll
-      for (int a = 0; a < NT; ++a) bf[a] = load_kmajor_flat<T, BC>(Bs, 32 * q, 16 * a, lane);
+      for (int a = 0; a < NT; ++a) bf[a] = load_kmajor_at<T>(st, bo[a], 32 * q * BC * 16);
 #pragma unroll
       for (int a = 0; a < NT; ++a) Hr[a] = mma16(bf[a], xd, Hr[a]);
     }
