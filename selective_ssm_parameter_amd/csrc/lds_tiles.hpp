@@ -126,6 +126,24 @@ __device__ __forceinline__ void dma_tile_full_n(BufRes rs, uint32_t base, const 
         rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, off[m], base, 0, 0);
   }
 }
+// dma_tile_full_n with this wave's LDS position given as a byte offset wl =
+// 1024 * dma_group(0, wave) that the caller recomputes at each use (through an
+// empty volatile asm): the compiler then forms every copy's LDS address from
+// it inside the loop instead of keeping one scalar register per copy and stage
+// live across the whole walk.
+template <int NROWS, int CPR, int NWV>
+__device__ __forceinline__ void dma_tile_full_w(BufRes rs, uint32_t base, const uint32_t* off,
+                                                unsigned char* dst, int wl) {
+  constexpr int NI = NROWS * CPR / 64, NC = dma_count<NROWS, CPR, NWV>();
+  static_assert(NI % NWV == 0 || NC == 1, "group m of a wave lies NWV groups after group m - 1");
+#pragma unroll
+  for (int m = 0; m < NC; ++m) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(dst + wl + 1024 * NWV * m), 16, off[m], base,
+        0, 0);
+  }
+}
+
 // Rows >= rvalid and chunks >= cvalid read as zeros; the same instruction
 // count as dma_tile_full_n.
 template <int NROWS, int CPR, int NWV, class Swz>

@@ -881,21 +881,13 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
       }
   }
 
-  const int nc = A.nc;
-  const int ch0 = seg * A.seg_chunks;
-  const int ch1 = min(nc, ch0 + A.seg_chunks);
-  if (ch0 >= ch1) return;
-  struct Blk {
-    int ch, sig;
-  };
-  auto nblocks = [&](int ch) { return (min(L, Tlen - ch * L) + BT - 1) / BT; };
-  auto advance = [&](Blk s) {
-    if (++s.sig == nblocks(s.ch)) {
-      s.sig = 0;
-      ++s.ch;
-    }
-    return s;
-  };
+  // the walk goes over the segment's 32-token blocks by their index in the
+  // sequence: chunk lengths are multiples of BT, so block j starts at token
+  // j * BT, belongs to chunk j / LB and is block j % LB of it
+  const int LB = L / BT;
+  const int j0 = seg * A.seg_chunks * LB;
+  const int j1 = min((Tlen + BT - 1) / BT, (seg + 1) * A.seg_chunks * LB);
+  if (j0 >= j1) return;
 
   // ---- copies of one step into a stage (every wave takes its share of each
   // tile; X of both heads as one tile of 2R rows)
@@ -913,33 +905,38 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
   dma_plan_n<BT, GC, 8>((uint32_t)R * ES, w, lane, [](int r) { return swz_row<T, GC>(r); }, goff);
   const bool nfull = N == NP;
 
-  auto fetch = [&](unsigned char* st, Blk s) {
-    const int c0 = s.ch * L + s.sig * BT;  // the block's first token
-    const int Ls = min(BT, Tlen - c0);
+  auto fetch = [&](unsigned char* st, int jb) {
+    const int c0 = jb * BT;  // the block's first token
+    const int ch = jb / LB, sig = jb - ch * LB;
     const uint32_t prow = (uint32_t)c0 * KS;
-    const int rlim = Ls * KS;
-    const bool rows_full = rlim >= R;
     const uint32_t xb = (prow * (uint32_t)HPsz + 2 * hp * kP) * ES;
-    if (rows_full)
-      dma_tile_full_n<2 * R, XC, 8>(rX, xb, xoff, st + Lay::XO, w);
-    else
-      dma_rows_n<2 * R, XC, 8>(rX, xb, xoff, xrow, rlim, st + Lay::XO, w);
     const uint32_t bb = (prow * GN + grp * N) * ES;
-    if (rows_full && nfull)
-      dma_tile_full_n<R, BC, 8>(rB, bb, boff, st + Lay::BO, w);
-    else
+    const uint32_t cb = ((uint32_t)c0 * GN + grp * N) * ES;
+    if (c0 + BT <= Tlen && nfull) {  // a whole block: every row and chunk valid
+      int wx = 1024 * dma_group<2 * R, XC, 8>(0, w), wb = 1024 * dma_group<R, BC, 8>(0, w);
+      int wcc = 1024 * dma_group<BT, BC, 8>(0, w);
+      asm volatile("" : "+s"(wx), "+s"(wb), "+s"(wcc));
+      dma_tile_full_w<2 * R, XC, 8>(rX, xb, xoff, st + Lay::XO, wx);
+      dma_tile_full_w<R, BC, 8>(rB, bb, boff, st + Lay::BO, wb);
+      dma_tile_full_w<BT, BC, 8>(rC, cb, coff, st + Lay::CO, wcc);
+    } else {
+      const int Ls = min(BT, Tlen - c0);
+      const int rlim = Ls * KS;
+      if (rlim >= R)
+        dma_tile_full_n<2 * R, XC, 8>(rX, xb, xoff, st + Lay::XO, w);
+      else
+        dma_rows_n<2 * R, XC, 8>(rX, xb, xoff, xrow, rlim, st + Lay::XO, w);
       dma_tile_n<R, BC, 8>(rB, bb, GN * ES, st + Lay::BO, rlim, (int)(N * ES / 16), w, lane,
                            [](int r) { return swz_tr<T, BC>(r); });
-    const uint32_t cb = ((uint32_t)c0 * GN + grp * N) * ES;
-    if (Ls >= BT && nfull)
-      dma_tile_full_n<BT, BC, 8>(rC, cb, coff, st + Lay::CO, w);
-    else
       dma_tile_n<BT, BC, 8>(rC, cb, GN * ES, st + Lay::CO, Ls, (int)(N * ES / 16), w, lane,
                             [](int r) { return swz_row<T, BC>(r); });
+    }
     // the diagonal Gram tile (sig, sig) of chunk ch
-    const int pidx = s.sig * (s.sig + 1) / 2 + s.sig;
-    const uint32_t gb = (uint32_t)((((size_t)s.ch * G + grp) * A.npairs + pidx) * gtile * ES);
-    dma_tile_full_n<BT, GC, 8>(rG, gb, goff, st + Lay::GO, w);
+    const int pidx = sig * (sig + 1) / 2 + sig;
+    const uint32_t gb = (uint32_t)((((size_t)ch * G + grp) * A.npairs + pidx) * gtile * ES);
+    int wg = 1024 * dma_group<BT, GC, 8>(0, w);
+    asm volatile("" : "+s"(wg));
+    dma_tile_full_w<BT, GC, 8>(rG, gb, goff, st + Lay::GO, wg);
   };
 
   floatx4 accY[TT];
@@ -970,9 +967,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
         Gt + (t * GC + ((e0 >> 4) ^ swz_row<T, GC>(t))) * 16 + (e0 & 15)));
   };
 
-  auto compute = [&](const unsigned char* st, Blk s) {
+  auto compute = [&](const unsigned char* st, int jb) {
     const unsigned char* Gd = st + Lay::GO;
-    const int c0 = s.ch * L + s.sig * BT;
+    const int c0 = jb * BT;
     const int Ls = min(BT, Tlen - c0);
 
     // ---- the block's entering state as fp16 operands; past 2^14 (found from
@@ -1079,29 +1076,24 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
 
   // ---- the walk: step s computes from stage s % 3 while the copies of step
   // s + 2 go into stage (s + 2) % 3; one barrier per step
-  Blk s0{ch0, 0};
-  Blk s1 = advance(s0);
-  Blk s2 = s1.ch < ch1 ? advance(s1) : s1;
-  fetch(stage0, s0);
-  if (s1.ch < ch1)
-    fetch(stage1, s1);
+  int jc = j0;
+  fetch(stage0, jc);
+  if (jc + 1 < j1)
+    fetch(stage1, jc + 1);
   else
     dma_dummies<NCOPY>(rX, sink);
   wait_vm<0>();
   stage_barrier();
   auto step = [&](const unsigned char* cur_st, unsigned char* far_st) {
     store_y();  // the previous block's y, before this step's copies
-    if (s2.ch < ch1)
-      fetch(far_st, s2);
+    if (jc + 2 < j1)
+      fetch(far_st, jc + 2);
     else
       dma_dummies<NCOPY>(rX, sink);
-    compute(cur_st, s0);
+    compute(cur_st, jc);
     wait_vm<NCOPY>();  // the next step's copies have landed
     stage_barrier();
-    s0 = s1;
-    s1 = s2;
-    if (s2.ch < ch1) s2 = advance(s2);
-    return s0.ch < ch1;
+    return ++jc < j1;
   };
   while (step(stage0, stage2) && step(stage1, stage0) && step(stage2, stage1)) {
   }
