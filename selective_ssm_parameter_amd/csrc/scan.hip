@@ -884,7 +884,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
   // the walk goes over the segment's 32-token blocks by their index in the
   // sequence: chunk lengths are multiples of BT, so block j starts at token
   // j * BT, belongs to chunk j / LB and is block j % LB of it
-  const int LB = L / BT;
+  const int LB = L / BT;  // 1, 2, 4 or 8
+  const int lbs = __builtin_ctz((unsigned)LB);
   const int j0 = seg * A.seg_chunks * LB;
   const int j1 = min((Tlen + BT - 1) / BT, (seg + 1) * A.seg_chunks * LB);
   if (j0 >= j1) return;
@@ -905,9 +906,12 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
   dma_plan_n<BT, GC, 8>((uint32_t)R * ES, w, lane, [](int r) { return swz_row<T, GC>(r); }, goff);
   const bool nfull = N == NP;
 
+  const uint32_t gpair = (uint32_t)(gtile * ES);                     // one Gram tile
+  const uint32_t gbase = (uint32_t)grp * (uint32_t)A.npairs * gpair;  // this group's
+  const uint32_t gchunk = (uint32_t)G * (uint32_t)A.npairs * gpair;   // one chunk's
   auto fetch = [&](unsigned char* st, int jb) {
     const int c0 = jb * BT;  // the block's first token
-    const int ch = jb / LB, sig = jb - ch * LB;
+    const int ch = jb >> lbs, sig = jb & (LB - 1);
     const uint32_t prow = (uint32_t)c0 * KS;
     const uint32_t xb = (prow * (uint32_t)HPsz + 2 * hp * kP) * ES;
     const uint32_t bb = (prow * GN + grp * N) * ES;
@@ -931,9 +935,10 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
       dma_tile_n<BT, BC, 8>(rC, cb, GN * ES, st + Lay::CO, Ls, (int)(N * ES / 16), w, lane,
                             [](int r) { return swz_row<T, BC>(r); });
     }
-    // the diagonal Gram tile (sig, sig) of chunk ch
-    const int pidx = sig * (sig + 1) / 2 + sig;
-    const uint32_t gb = (uint32_t)((((size_t)ch * G + grp) * A.npairs + pidx) * gtile * ES);
+    // the diagonal Gram tile (sig, sig) of chunk ch: pair index sig (sig + 3) / 2
+    // (32-bit offsets: the Gram buffer of a sequence is below 4 GiB)
+    const uint32_t pidx = ((uint32_t)sig * (uint32_t)(sig + 3)) >> 1;
+    const uint32_t gb = (uint32_t)ch * gchunk + gbase + pidx * gpair;
     int wg = 1024 * dma_group<BT, GC, 8>(0, w);
     asm volatile("" : "+s"(wg));
     dma_tile_full_w<BT, GC, 8>(rG, gb, goff, st + Lay::GO, wg);
