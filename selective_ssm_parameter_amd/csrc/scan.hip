@@ -672,39 +672,12 @@ __device__ __forceinline__ void dma_dummies(BufRes rs, unsigned char* sink) {
 }
 
 constexpr int kBlockThreads = 512;
-// load_kmajor with each read's lane offset made opaque to the optimiser, so
-// the LDS address is one step from the tile base: the LDS lowering gives an
-// access its alias scope only within a few address steps of the variable,
-// and a transposing read without one is taken to alias every copy in flight
-// (the compiler then waits for all of them before it)
-template <typename T, int CPR>
-__device__ __forceinline__ typename Vec<T>::x8 load_kmajor_flat(const unsigned char* tile, int k0,
-                                                                int col0, int lane) {
-  typedef typename Vec<T>::x8 F;
-  static_assert(sizeof(T) == 2, "2-byte streams");
-  typedef short s4 __attribute__((__vector_size__(8)));
-  const int g = lane >> 4, c = lane & 15;
-  F v;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int r = k0 + 8 * g + 4 * hh + (c >> 2);
-    const int col = col0 + 4 * (c & 3);
-    const int ch = col >> 3, half = (col >> 2) & 1;
-    int off = (r * CPR + (ch ^ swz_tr<T, CPR>(r))) * 16 + 8 * half;
-    asm("" : "+v"(off));
-    const typename Vec<T>::x4 w4 = __builtin_bit_cast(
-        typename Vec<T>::x4,
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(tile + off)));
-#pragma unroll
-    for (int m = 0; m < 4; ++m) v[4 * hh + m] = w4[m];
-  }
-  return v;
-}
-
-// Byte offset within a tile of lane `lane`'s half hh of the K-major fragment
-// that load_kmajor_flat reads at k0 = 0 and column col0. The swizzle depends on
-// the row's low three bits only, so the read at k0 (a multiple of 32) lies
-// k0 * CPR * 16 bytes further on.
+// K-major fragments of 2-byte tiles with planned lane offsets: lane (g, c)
+// gets rows k0 + 8g .. k0 + 8g + 7 of column col0 + c through two transposing
+// reads (as load_kmajor). kmajor_off is the byte offset within the tile of
+// the lane's half hh at k0 = 0; the swizzle depends on the row's low four bits
+// only, so the read at k0 (a multiple of 32) lies k0 * CPR * 16 bytes further
+// on.
 template <typename T, int CPR>
 __device__ __forceinline__ int kmajor_off(int col0, int hh, int lane) {
   const int g = lane >> 4, c = lane & 15;
@@ -713,9 +686,12 @@ __device__ __forceinline__ int kmajor_off(int col0, int hh, int lane) {
   const int ch = col >> 3, half = (col >> 2) & 1;
   return (r * CPR + (ch ^ swz_tr<T, CPR>(r))) * 16 + 8 * half;
 }
-// The fragment at lane offsets off[0], off[1] (made opaque once, where they
-// are planned, so that each read is one address step from its stage array and
-// keeps the array's alias scope) plus kb bytes (a constant).
+// The fragment at lane offsets off[0], off[1] plus kb bytes (a constant). The
+// offsets are made opaque to the optimiser once, where they are planned, so
+// that each read's LDS address is one step from its stage array: the LDS
+// lowering gives an access its alias scope only within a few address steps of
+// the variable, and a transposing read without one is taken to alias every
+// buffer-to-LDS copy in flight (the compiler then waits for all of them first).
 template <typename T>
 __device__ __forceinline__ typename Vec<T>::x8 load_kmajor_at(const unsigned char* stage,
                                                               const int (&off)[2], int kb) {
@@ -1169,6 +1145,19 @@ __global__ __launch_bounds__(kCarryThreads, 1) void scan_carry_kernel(ScanArgs A
   const size_t HPsz = (size_t)H * kP;
   const int prow_x = 16 * wc + c;
   const float la = A.a[h] > 0.f ? log2f(A.a[h]) : -1e30f;
+  // lane offsets of the transposing reads within a stage (planned once, as in
+  // the output walk)
+  int xo[2], bo[NT][2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    xo[hh] = Lay::XO + hw * Lay::XB + kmajor_off<T, XC>(16 * wc, hh, lane);
+    asm("" : "+v"(xo[hh]));
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      bo[a][hh] = Lay::BO + kmajor_off<T, BC>(16 * a, hh, lane);
+      asm("" : "+v"(bo[a][hh]));
+    }
+  }
 
   const BufRes rB = make_rsrc(reinterpret_cast<const T*>(A.B_hat) + (size_t)b * Tlen * KS * GN,
                               (uint64_t)Tlen * KS * GN * ES);
@@ -1231,8 +1220,6 @@ __global__ __launch_bounds__(kCarryThreads, 1) void scan_carry_kernel(ScanArgs A
                            [](int r) { return swz_tr<T, BC>(r); });
   };
   auto compute = [&](const unsigned char* st, Blk cur) {
-    const unsigned char* Xs = st + Lay::XO + hw * Lay::XB;
-    const unsigned char* Bs = st + Lay::BO;
     const int Lc = min(L, Tlen - cur.ch * L);
     const int nb = (Lc + BT - 1) / BT;
     if (cur.sig == 0) {
@@ -1244,7 +1231,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void scan_carry_kernel(ScanArgs A
     const float blk = apow_step(la, (nb - 1 - cur.sig) * BT);
 #pragma unroll
     for (int q = 0; q < RQ; ++q) {
-      const F xq = load_kmajor_flat<T, XC>(Xs, 32 * q, 16 * wc, lane);
+      const F xq = load_kmajor_at<T>(st, xo, 32 * q * XC * 16);
       F xd;
       if (full) {
         xd = xq * (er[q] * from_f32<T>(blk));
@@ -1260,7 +1247,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void scan_carry_kernel(ScanArgs A
       for (int a0 = 0; a0 < NT; a0 += CGR) {
         F bf[CGR];
 #pragma unroll
-        for (int i = 0; i < CGR; ++i) bf[i] = load_kmajor_flat<T, BC>(Bs, 32 * q, 16 * (a0 + i), lane);
+        for (int i = 0; i < CGR; ++i) bf[i] = load_kmajor_at<T>(st, bo[a0 + i], 32 * q * BC * 16);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < CGR; ++i) Hr[a0 + i] = mma16(bf[i], xd, Hr[a0 + i]);
