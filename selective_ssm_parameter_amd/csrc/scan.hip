@@ -660,14 +660,20 @@ __global__ __launch_bounds__(kScanThreads, sizeof(T) == 2 && KS <= 2 ? 2 : 1) vo
 }
 
 // N copies that read nothing (an offset past the buffer) and write 4-byte
-// zeros into `sink` (256 bytes of LDS): they keep a wave's count of copies in
-// flight fixed when a step needs fewer tiles.
+// zeros into `sink` (kSinkBytes of LDS): they keep a wave's count of copies in
+// flight fixed when a step needs fewer tiles, so that a fixed vmcnt wait still
+// covers the previous step's copies. Each goes to its own 256 bytes of the
+// sink: identical calls were merged into one by the compiler, which left the
+// wait short by N - 1 and let a walk's last two steps read tiles still in
+// flight.
+constexpr int kSinkBytes = 2048;
 template <int N>
 __device__ __forceinline__ void dma_dummies(BufRes rs, unsigned char* sink) {
+  static_assert(N * 256 <= kSinkBytes, "one 256-byte sink slot per dummy copy");
 #pragma unroll
   for (int m = 0; m < N; ++m) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sink),
-                                             4, kOOB, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(sink + 256 * m), 4, kOOB, 0, 0, 0);
   }
 }
 
@@ -750,7 +756,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void scan_block_kernel(ScanArgs A
   __shared__ __align__(16) unsigned char stage0[Lay::STAGE];
   __shared__ __align__(16) unsigned char stage1[Lay::STAGE];
   __shared__ __align__(16) unsigned char stage2[Lay::STAGE];
-  __shared__ __align__(16) unsigned char sink[256];
+  __shared__ __align__(16) unsigned char sink[kSinkBytes];
 
   const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
   const int HU = H / 2;
@@ -1124,7 +1130,7 @@ __global__ __launch_bounds__(kCarryThreads, 1) void scan_carry_kernel(ScanArgs A
   __shared__ __align__(16) unsigned char stage0[Lay::STAGE];
   __shared__ __align__(16) unsigned char stage1[Lay::STAGE];
   __shared__ __align__(16) unsigned char stage2[Lay::STAGE];
-  __shared__ __align__(16) unsigned char sink[256];
+  __shared__ __align__(16) unsigned char sink[kSinkBytes];
 
   const int H = A.H, G = A.G, N = A.N, L = A.L, Tlen = A.T;
   const int HU = H / 2;
