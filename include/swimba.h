@@ -91,12 +91,13 @@ typedef enum swimba_call {
  *   <= 2 for fp32; the scan backward: top_k <= 2);
  *   chunk in {32, 64, 128, 256} for the scan.
  * Sizes the kernels can address (else SWIMBA_ERR_DIMS, before any launch;
- * 4 GiB here means 0xFFFFFFF0 bytes): u at most 4 GiB in every call that
- * reads it; w_router and each expert's [W, D] weight matrix at most 4 GiB;
- * in the scans, one sequence's B_hat and X_hat (T * k * G*N and T * k * H*P
- * stream elements) and its intra-chunk Gram tiles at most 4 GiB (a longer
- * sequence is scanned in pieces, the state handed on through h_final and
- * h_init).
+ * 2 GiB here means 0x7FFFFFF0 bytes, so that the byte offset 2^31 the kernels
+ * give to loads that must read zeros lies past every buffer): u at most 2 GiB
+ * in every call that reads it; w_router and each expert's [W, D] weight
+ * matrix at most 2 GiB; in the scans, one sequence's B_hat and X_hat
+ * (T * k * G*N and T * k * H*P stream elements) and its intra-chunk Gram
+ * tiles at most 2 GiB (a longer sequence is scanned in pieces, the state
+ * handed on through h_final and h_init).
  */
 typedef struct swimba_dims {
   int32_t batch;      /* Bt: independent sequences */

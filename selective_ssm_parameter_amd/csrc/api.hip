@@ -84,21 +84,23 @@ swimba_status check_kernel_shape(const Dims& d) {
   return SWIMBA_OK;
 }
 
-// The kernels address HBM through buffer resources with 32-bit byte offsets
-// (records of at most 0xFFFFFFF0 bytes): the token rows of u, the router and
-// each expert's weight matrix as a whole, and the scan's streams of one
-// sequence. Larger tensors are rejected here instead of being read wrongly.
-constexpr int64_t kMaxRecord = 0xFFFFFFF0ll;
+// The kernels address HBM through buffer resources with 32-bit byte offsets:
+// the token rows of u, the router and each expert's weight matrix as a whole,
+// and the scan's streams of one sequence. Rows, columns and K steps a load must
+// not read take the offset 2^31 (kOOB), which returns zeros only while it lies
+// past the record, so records stay below 2^31 bytes (0x7FFFFFF0, "2 GiB"
+// below). Larger tensors are rejected here instead of being read wrongly.
+constexpr int64_t kMaxRecord = 0x7FFFFFF0ll;
 
 swimba_status check_records(const Dims& d, bool router, bool experts) {
   const int64_t ein = d.bf16 ? 2 : 4;  // u and weight elements
   if (d.M * d.D * ein > kMaxRecord)
-    return fail(SWIMBA_ERR_DIMS, "u is %lld bytes; the kernels address at most 4 GiB of it",
+    return fail(SWIMBA_ERR_DIMS, "u is %lld bytes; the kernels address at most 2 GiB of it",
                 (long long)(d.M * d.D * ein));
   if (router && d.E * d.D * ein > kMaxRecord)
-    return fail(SWIMBA_ERR_DIMS, "w_router is larger than 4 GiB");
+    return fail(SWIMBA_ERR_DIMS, "w_router is larger than 2 GiB");
   if (experts && d.W * d.D * ein > kMaxRecord)
-    return fail(SWIMBA_ERR_DIMS, "one expert's weights (%lld bytes) exceed 4 GiB",
+    return fail(SWIMBA_ERR_DIMS, "one expert's weights (%lld bytes) exceed 2 GiB",
                 (long long)(d.W * d.D * ein));
   return SWIMBA_OK;
 }
@@ -112,7 +114,7 @@ swimba_status check_scan_records(const Dims& d) {
   const int64_t gram = nc * d.G * (nb * (nb + 1) / 2) * 32 * (32 * d.k) * es;
   if (d.T * d.k * d.HP * es > kMaxRecord || d.T * d.k * d.GN * es > kMaxRecord || gram > kMaxRecord)
     return fail(SWIMBA_ERR_DIMS,
-                "one sequence's X_hat (%lld bytes) or Gram tiles (%lld bytes) exceed 4 GiB; "
+                "one sequence's X_hat (%lld bytes) or Gram tiles (%lld bytes) exceed 2 GiB; "
                 "split the sequence and pass the state on (h_final -> h_init)",
                 (long long)(d.T * d.k * d.HP * es), (long long)gram);
   return SWIMBA_OK;

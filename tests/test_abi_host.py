@@ -103,12 +103,17 @@ def test_unsupported_shapes():
 
 
 def test_sizes_beyond_32bit_offsets():
-    # tensors the kernels would address past their 4 GiB buffer records are
+    # tensors the kernels would address past their 2 GiB buffer records are
     # rejected before any launch (the pointers are never touched)
     L = lib()
     big_u = good_dims(batch=1, seqlen=1 << 21, d_model=1024)      # u: 4 GiB of bf16
     assert call_route(big_u) == -2
     assert "u is" in L.swimba_last_error().decode()
+    # 3 GiB: within 32-bit offsets, but the zero-reading offset 2^31 would lie
+    # inside the record
+    mid_u = good_dims(batch=3, seqlen=1 << 19, d_model=1024)
+    assert call_route(mid_u) == -2
+    assert "2 GiB" in L.swimba_last_error().decode()
     st = L.swimba_expert_project_mix(ctypes.byref(big_u), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                      FAKE, FAKE, 1 << 40, None)
     assert st == -2
@@ -126,8 +131,13 @@ def test_sizes_beyond_32bit_offsets():
     st = L.swimba_ssd_chunk_scan(ctypes.byref(long_seq), FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
                                  FAKE, 1 << 40, None)
     assert st == -2 and "h_final -> h_init" in L.swimba_last_error().decode()
-    # the same tokens over 4 sequences fit
-    ok_seq = good_dims(batch=4, seqlen=1 << 18, nheads=32, dstate=128, chunk=256)
+    # 2 GiB in one sequence is past the limit; the same tokens over 8
+    # sequences fit
+    two = good_dims(batch=4, seqlen=1 << 18, nheads=32, dstate=128, chunk=256)
+    st = L.swimba_ssd_chunk_scan(ctypes.byref(two), FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                 FAKE, 1 << 40, None)
+    assert st == -2
+    ok_seq = good_dims(batch=8, seqlen=1 << 17, nheads=32, dstate=128, chunk=256)
     assert sb.swimba_workspace_size(ok_seq, sb.CALL_SCAN) > 0
 
 
