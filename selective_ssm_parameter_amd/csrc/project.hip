@@ -23,6 +23,8 @@
 // written as whole row segments after staging each wave's results in LDS; a
 // last small kernel sums c_part over the slots in slot order (0..k-1, fp32)
 // into C_mix, so C~ never depends on which workgroup ran first.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_tiles.hpp"
@@ -202,12 +204,15 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
   for (int m = 0; m < MA; ++m) aoff[m] = abase[m] != kOOB ? abase[m] + 16u * alc[m] : kOOB;
 #pragma unroll
   for (int m = 0; m < MB; ++m) boff[m] = bbase[m] != kOOB ? bbase[m] + 16u * blc[m] : kOOB;
-  auto fetch = [&](unsigned char* st, int k0) {
+  // MAV: the A copies of the tile's rows (MA, or MA / 2 for a half tile: the
+  // copies m < MA / 2 cover rows 0 .. BM / 2 - 1)
+  auto fetch = [&](unsigned char* st, int k0, auto mav_tag) {
+    constexpr int MAV = decltype(mav_tag)::value;
     if constexpr (KFULL) {
       // the look-ahead of the last turn re-reads the last K tile (never used)
       const int ks = __builtin_amdgcn_readfirstlane(min(k0, D - BK) * (int)ES);
 #pragma unroll
-      for (int m = 0; m < MA; ++m) {
+      for (int m = 0; m < MAV; ++m) {
         const uint32_t off = aoff[m];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rA, (__attribute__((address_space(3))) void*)(st + 1024 * (wave + NW * m)), 16, off,
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < MA; ++m) {
+      for (int m = 0; m < MAV; ++m) {
         const int kk = k0 + alc[m] * (16 / (int)ES);
         const uint32_t off = (abase[m] != kOOB && kk < D) ? abase[m] + kk * ES : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -249,122 +254,141 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
     }
   };
 
-  // acc[i][j] holds, in lane (g, c), out[pair row 16i + c][columns 16j + 4g .. +3]
-  // of this wave's block: the weight fragment is the matrix-core A operand.
-  floatx4 acc[TM][TN];
+  // The K loop and epilogue for TMV fragment rows per wave: TM, or TM / 2 for
+  // a half tile (an expert's last row tile with at most BM / 2 rows, where
+  // the waves' rows are BM / 2 / WM apart and only the first half of the A
+  // copies is issued), so that a short tail costs about half a tile.
+  auto run = [&](auto tmv_tag) {
+    constexpr int TMV = decltype(tmv_tag)::value;
+    constexpr int MAV = MA * TMV / TM;
+    const std::integral_constant<int, MAV> mav{};
+    // acc[i][j] holds, in lane (g, c), out[pair row 16i + c][columns 16j + 4g .. +3]
+    // of this wave's block: the weight fragment is the matrix-core A operand.
+    floatx4 acc[TMV][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TMV; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Column tiles are used in pairs (2jj, 2jj + 1) covering 32 columns: row m of
-  // the pair's first matrix-core tile is column 8 (m / 4) + m % 4 and of the
-  // second 8 (m / 4) + 4 + m % 4, so lane group g ends up with the 8
-  // consecutive columns 8g .. 8g + 7 of the pair (one 16-byte store).
-  auto bcol = [&](int j) { return wn * TN * 16 + 32 * (j >> 1) + 8 * (c >> 2) + 4 * (j & 1) + (c & 3); };
-  // The matrix-core ops of the last DEF fragment rows of K tile kt are issued
-  // after the reads of tile kt + 1 (past its barrier), so that they cover the
-  // wait for those reads: 1-2 % at c3 and c4 (4 x 8192 and 65536 tokens),
-  // bit-identical results.
-  constexpr int DEF = TM > 1 ? 1 : 0;
-  F bfr[TN], afr[TM];
+    // Column tiles are used in pairs (2jj, 2jj + 1) covering 32 columns: row m of
+    // the pair's first matrix-core tile is column 8 (m / 4) + m % 4 and of the
+    // second 8 (m / 4) + 4 + m % 4, so lane group g ends up with the 8
+    // consecutive columns 8g .. 8g + 7 of the pair (one 16-byte store).
+    auto bcol = [&](int j) {
+      return wn * TN * 16 + 32 * (j >> 1) + 8 * (c >> 2) + 4 * (j & 1) + (c & 3);
+    };
+    // The matrix-core ops of the last DEF fragment rows of K tile kt are issued
+    // after the reads of tile kt + 1 (past its barrier), so that they cover the
+    // wait for those reads: 1-2 % at c3 and c4 (4 x 8192 and 65536 tokens),
+    // bit-identical results.
+    constexpr int DEF = TMV > 1 ? 1 : 0;
+    F bfr[TN], afr[TMV];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) bfr[j] = zero8<T>();
+    for (int j = 0; j < TN; ++j) bfr[j] = zero8<T>();
 #pragma unroll
-  for (int i = 0; i < TM; ++i) afr[i] = zero8<T>();
-  auto mma_tail = [&]() {
+    for (int i = 0; i < TMV; ++i) afr[i] = zero8<T>();
+    auto mma_tail = [&]() {
 #pragma unroll
-    for (int i = TM - DEF; i < TM; ++i)
+      for (int i = TMV - DEF; i < TMV; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mma16(bfr[j], afr[i], acc[i][j]);
-  };
-  auto compute = [&](const unsigned char* st) {
-    F nb[TN], na[TM];
+        for (int j = 0; j < TN; ++j) acc[i][j] = mma16(bfr[j], afr[i], acc[i][j]);
+    };
+    auto compute = [&](const unsigned char* st) {
+      F nb[TN], na[TMV];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) nb[j] = frag(st + Lay::AB, bcol(j));
+      for (int j = 0; j < TN; ++j) nb[j] = frag(st + Lay::AB, bcol(j));
 #pragma unroll
-    for (int i = 0; i < TM; ++i) na[i] = frag(st, wm * TM * 16 + 16 * i + c);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < TMV; ++i) na[i] = frag(st, wm * TMV * 16 + 16 * i + c);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_tail();
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = nb[j];
+#pragma unroll
+      for (int i = 0; i < TMV; ++i) afr[i] = na[i];
+#pragma unroll
+      for (int i = 0; i < TMV - DEF; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mma16(bfr[j], afr[i], acc[i][j]);
+    };
+
+    // The K loop runs in whole turns of the four stages and issues every copy
+    // unconditionally (tiles past d read zeros, and multiply to nothing): with
+    // no branches in the loop the compiler's own wait counts see which stage a
+    // copy fills, and never drain all copies before reading a stage.
+    const int nk = (D + BK - 1) / BK;
+    const int nk4 = (nk + kProjStages - 1) / kProjStages * kProjStages;  // == nk when KFULL
+    fetch(stg0, 0, mav);
+    fetch(stg1, BK, mav);
+    fetch(stg2, 2 * BK, mav);
+    auto iter = [&](int kt, const unsigned char* cur, unsigned char* far) {
+      wait_vm<2 * (MAV + MB)>();  // tile kt landed (tiles kt + 1, kt + 2 may be in flight)
+      stage_barrier();          // tile kt visible to all waves; tile kt - 1 no longer read
+      fetch(far, (kt + 3) * BK, mav);
+      compute(cur);
+    };
+    for (int kt = 0; kt < nk4; kt += kProjStages) {
+      iter(kt, stg0, stg3);
+      iter(kt + 1, stg1, stg0);
+      iter(kt + 2, stg2, stg1);
+      iter(kt + 3, stg3, stg2);
+    }
     mma_tail();
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[j] = nb[j];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) afr[i] = na[i];
-#pragma unroll
-    for (int i = 0; i < TM - DEF; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mma16(bfr[j], afr[i], acc[i][j]);
-  };
+    wait_vm<0>();  // the copies past the end land before the workgroup's LDS is released
 
-  // The K loop runs in whole turns of the four stages and issues every copy
-  // unconditionally (tiles past d read zeros, and multiply to nothing): with
-  // no branches in the loop the compiler's own wait counts see which stage a
-  // copy fills, and never drain all copies before reading a stage.
-  const int nk = (D + BK - 1) / BK;
-  const int nk4 = (nk + kProjStages - 1) / kProjStages * kProjStages;  // == nk when KFULL
-  fetch(stg0, 0);
-  fetch(stg1, BK);
-  fetch(stg2, 2 * BK);
-  auto iter = [&](int kt, const unsigned char* cur, unsigned char* far) {
-    wait_vm<2 * Lay::CPW>();  // tile kt landed (tiles kt + 1, kt + 2 may be in flight)
-    stage_barrier();          // tile kt visible to all waves; tile kt - 1 no longer read
-    fetch(far, (kt + 3) * BK);
-    compute(cur);
-  };
-  for (int kt = 0; kt < nk4; kt += kProjStages) {
-    iter(kt, stg0, stg3);
-    iter(kt + 1, stg1, stg0);
-    iter(kt + 2, stg2, stg1);
-    iter(kt + 3, stg3, stg2);
-  }
-  mma_tail();
-  wait_vm<0>();  // the copies past the end land before the workgroup's LDS is released
-
-  // ---- epilogue: each lane stores 8 consecutive columns of one pair row per
-  // column-tile pair (H*P and G*N are multiples of 16, so 8 columns never
-  // straddle two regions).
-  static_assert(TN % 2 == 0, "column tiles are used in pairs");
-  typedef typename Vec<S>::x8 S8;
+    // ---- epilogue: each lane stores 8 consecutive columns of one pair row per
+    // column-tile pair (H*P and G*N are multiples of 16, so 8 columns never
+    // straddle two regions).
+    static_assert(TN % 2 == 0, "column tiles are used in pairs");
+    typedef typename Vec<S>::x8 S8;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = wm * TM * 16 + 16 * i + c;
-    const int tok = rtok[r];
-    const size_t pair = (size_t)(tok < 0 ? 0 : tok) * k + rslot[r];
-    const float wv = rw[r];
+    for (int i = 0; i < TMV; ++i) {
+      const int r = wm * TMV * 16 + 16 * i + c;
+      const int tok = rtok[r];
+      const size_t pair = (size_t)(tok < 0 ? 0 : tok) * k + rslot[r];
+      const float wv = rw[r];
 #pragma unroll
-    for (int jj = 0; jj < TN / 2; ++jj) {
-      const int cbase = __builtin_amdgcn_readfirstlane(col0 + wn * TN * 16 + 32 * jj);
-      if (cbase >= W) continue;
-      const int col = cbase + 8 * g;
-      if (col >= W) continue;
-      floatx8 v;
+      for (int jj = 0; jj < TN / 2; ++jj) {
+        const int cbase = __builtin_amdgcn_readfirstlane(col0 + wn * TN * 16 + 32 * jj);
+        if (cbase >= W) continue;
+        const int col = cbase + 8 * g;
+        if (col >= W) continue;
+        floatx8 v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q] = acc[i][2 * jj][q];
-        v[4 + q] = acc[i][2 * jj + 1][q];
-      }
-      if (tok < 0) continue;
-      if constexpr (PLAIN) {
-        typename Vec<TO>::x8 o;
+        for (int q = 0; q < 4; ++q) {
+          v[q] = acc[i][2 * jj][q];
+          v[4 + q] = acc[i][2 * jj + 1][q];
+        }
+        if (tok < 0) continue;
+        if constexpr (PLAIN) {
+          typename Vec<TO>::x8 o;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = from_f32<TO>(v[q]);
-        store8<TO>(&out[pair * W + col], o);
-      } else if (col < HP) {
-        S8 o;
+          for (int q = 0; q < 8; ++q) o[q] = from_f32<TO>(v[q]);
+          store8<TO>(&out[pair * W + col], o);
+        } else if (col < HP) {
+          S8 o;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(v[q]);
-        store8<S>(&X_hat[pair * HP + col], o);
-      } else if (col < HP + GN) {
-        S8 o;
-        const float wb = bw_one ? 1.f : wv;
+          for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(v[q]);
+          store8<S>(&X_hat[pair * HP + col], o);
+        } else if (col < HP + GN) {
+          S8 o;
+          const float wb = bw_one ? 1.f : wv;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(wb * v[q]);
-        store8<S>(&B_hat[pair * GN + (col - HP)], o);
-      } else {
-        floatx8 o = v * wv;
-        store8<float>(&c_part[pair * GN + (col - HP - GN)], o);
+          for (int q = 0; q < 8; ++q) o[q] = from_f32<S>(wb * v[q]);
+          store8<S>(&B_hat[pair * GN + (col - HP)], o);
+        } else {
+          floatx8 o = v * wv;
+          store8<float>(&c_part[pair * GN + (col - HP - GN)], o);
+        }
       }
     }
+  };
+  if constexpr (!PLAIN && TM % 2 == 0 && MA % 2 == 0) {
+    if (nrows <= BM / 2)
+      run(std::integral_constant<int, TM / 2>{});
+    else
+      run(std::integral_constant<int, TM>{});
+  } else {
+    run(std::integral_constant<int, TM>{});
   }
 }
 

@@ -108,6 +108,9 @@ PROJ_CASES = [
                          d_model=384, n_experts=5)),
     ("bf16_decode_shape", W("p3", 203, batch=96, seqlen=1, n_experts=32, top_k=4, dstate=128)),
     ("f32_k1_n16", W("p4", 204, dtype=synth.F32, top_k=1, dstate=16, nheads=3, seqlen=130)),
+    # 256-row tiles; the experts' last tiles hold 143, 124, 91 and 154 rows, so
+    # two of them run as half tiles (at most 128 rows) and two as whole ones
+    ("bf16_big_tile_tails", W("p6", 206, seqlen=640, n_experts=4)),
 ]
 
 
