@@ -254,13 +254,15 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
     }
   };
 
-  // The K loop and epilogue for TMV fragment rows per wave: TM, or TM / 2 for
-  // a half tile (an expert's last row tile with at most BM / 2 rows, where
-  // the waves' rows are BM / 2 / WM apart and only the first half of the A
-  // copies is issued), so that a short tail costs about half a tile.
+  // The K loop and epilogue for TMV fragment rows per wave: TM, or TM / 2 or
+  // TM / 4 for a half or quarter tile (an expert's last row tile with at most
+  // BM / 2 or BM / 4 rows: the waves' rows are 16 TMV apart and only the A
+  // copies of the first BM / 2 rows are issued, rows past the tile's reading
+  // zeros), so that a short tail costs about half or a quarter of a tile.
   auto run = [&](auto tmv_tag) {
     constexpr int TMV = decltype(tmv_tag)::value;
-    constexpr int MAV = MA * TMV / TM;
+    constexpr int MAV = MA * TMV / TM > 0 ? MA * TMV / TM : 1;
+    static_assert(MAV * (BM / MA) >= C::WM * TMV * 16, "the A copies cover the rows computed");
     const std::integral_constant<int, MAV> mav{};
     // acc[i][j] holds, in lane (g, c), out[pair row 16i + c][columns 16j + 4g .. +3]
     // of this wave's block: the weight fragment is the matrix-core A operand.
@@ -382,7 +384,14 @@ __global__ __launch_bounds__(C::NTH) void proj_kernel(
       }
     }
   };
-  if constexpr (!PLAIN && TM % 2 == 0 && MA % 2 == 0) {
+  if constexpr (!PLAIN && TM % 4 == 0 && MA % 2 == 0) {
+    if (nrows <= BM / 4)
+      run(std::integral_constant<int, TM / 4>{});
+    else if (nrows <= BM / 2)
+      run(std::integral_constant<int, TM / 2>{});
+    else
+      run(std::integral_constant<int, TM>{});
+  } else if constexpr (!PLAIN && TM % 2 == 0 && MA % 2 == 0) {
     if (nrows <= BM / 2)
       run(std::integral_constant<int, TM / 2>{});
     else

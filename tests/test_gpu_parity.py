@@ -111,6 +111,9 @@ PROJ_CASES = [
     # 256-row tiles; the experts' last tiles hold 143, 124, 91 and 154 rows, so
     # two of them run as half tiles (at most 128 rows) and two as whole ones
     ("bf16_big_tile_tails", W("p6", 206, seqlen=640, n_experts=4)),
+    # last tiles of 105, 84, 48 and 115 rows: three half tiles and a quarter
+    # tile (at most 64 rows)
+    ("bf16_big_tile_short_tails", W("p7", 206, seqlen=600, n_experts=4)),
 ]
 
 
