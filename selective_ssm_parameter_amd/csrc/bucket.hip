@@ -71,19 +71,20 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(
   for (int e = threadIdx.x; e < EP; e += blockDim.x) { before[e] = 0; total[e] = 0; }
   for (int e = threadIdx.x; e < 4 * EP; e += blockDim.x) wcnt[e] = 0;
   __syncthreads();
-  // bucket e's counts of blocks b0, b0 + step, ...: loads issued 8 at a time
-  // (a thread walks nblk / nparts blocks; one load in flight at a time made
-  // this loop's latency grow with E)
+  // bucket e's counts of blocks b0, b0 + step, ...: loads issued kColumnLoads
+  // at a time (a thread walks nblk / nparts blocks, more as E grows; one load
+  // in flight at a time made this loop's latency grow with E)
+  constexpr int kColumnLoads = 16;
   auto column = [&](int e, int b0, int step, int& sb, int& st) {
-    for (int b = b0; b < nblk; b += 8 * step) {
-      int v[8];
+    for (int b = b0; b < nblk; b += kColumnLoads * step) {
+      int v[kColumnLoads];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kColumnLoads; ++q) {
         const int bq = b + q * step;
         v[q] = bq < nblk ? counts[(size_t)bq * EP + e] : 0;
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kColumnLoads; ++q) {
         st += v[q];
         sb += b + q * step < blk ? v[q] : 0;
       }
